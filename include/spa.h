@@ -1,0 +1,308 @@
+/*
+ * spa.h - C ABI of the MI355X (gfx950) spatially pipelined MoE decode layer.
+ *
+ * The library runs one GPT-OSS-style MoE transformer decode layer - the
+ * operator chain drawn in Figure 3 of "SubGPU Pipelining: Intra-GPU
+ * Fine-Grained Spatial Parallelism for LLM Inference" (Andoorveedu et al.,
+ * arXiv:2611.14904): RMSNorm, Q/KV projection, attention, output projection,
+ * Add+Norm, router gating, top-k dispatch, expert up, SwiGLU, expert down,
+ * combine - and repeats it over layers that alternate sliding-window and full
+ * attention (its section 5.1). It executes a decode iteration either
+ * temporally (every kernel on all CUs, section 5.1 "Temporal") or as the
+ * paper's two-stage spatial pipeline (sections 3.1-3.2): the layer is cut
+ * into two contiguous segments bound to disjoint CU pools, and microbatches
+ * stream through them with event-ordered hand-offs.
+ *
+ * Conventions
+ *   - Every tensor argument is a device pointer to caller-owned memory
+ *     (allocated by the caller, e.g. with PyTorch); the library never frees
+ *     it. The library owns only the objects it creates: contexts, CU pools
+ *     (with their streams) and pipelines.
+ *   - Compute calls are asynchronous: they enqueue work on the given HIP
+ *     stream (NULL = the null stream) and return. Device faults surface at
+ *     the caller's next synchronisation.
+ *   - Errors are status codes (spa_status < 0). Arguments are validated on
+ *     the host before anything is launched; on error nothing is enqueued and
+ *     spa_last_error() describes the problem (thread-local string, valid
+ *     until the next call on the same thread).
+ *   - Data-dependent errors found on the device (a KV length beyond its
+ *     cache capacity) set bits in the workspace error word; read them with
+ *     spa_workspace_errors().
+ *   - Results are deterministic: every reduction runs in a fixed order, and
+ *     launch shapes depend only on tensor shapes, so the spatial pipeline and
+ *     the temporal schedule with the same microbatch count give identical
+ *     bits.
+ *   - Objects are not thread-safe; use one per thread or serialise.
+ *
+ * Tensor layouts (row-major; all offsets in elements)
+ *   x         [B][H] fp32 residual stream, updated in place by a layer.
+ *   wqkv      [(Hq + 2 Hkv) D][H]    rows: q heads, then k heads, then v heads.
+ *   wo        [H][Hq D]
+ *   wr        [E][H] fp32 (router)
+ *   wgu       [E_res][2I][H]  rows 0..I-1 gate, I..2I-1 up (per expert).
+ *   wd        [E_res][H][I]
+ *   wgu_scale [E_res][2I], wd_scale [E_res][H] fp32 (E4M3 experts only):
+ *             dequantised weight = code value * scale of its row.
+ *   sinks     [Hq] fp32 attention sink logits; gamma1, gamma2 [H] fp32.
+ *   KV cache, per layer, D = 64, dtype kv_dtype:
+ *     full layers (packed): the region of (sequence s, KV head g) starts at
+ *       (kv_off[s] * Hkv + g * kv_cap[s]) * D and holds kv_cap[s] positions
+ *       (kv_cap a multiple of 32, kv_len[s] <= kv_cap[s]; regions of
+ *       different sequences must not overlap);
+ *     sliding layers (ring): region (s * Hkv + g) * W * D holds W slots,
+ *       position p in slot p % W (W a multiple of 32);
+ *     K of slot t at region + t*D + d; V at region + (t/32)*32*D + d*32 +
+ *     vslot(t%32), vslot(p) = 8*((p%16)/4) + 4*(p/16) + p%4 (d-major 32-slot
+ *     blocks). Use spa_kv_write / spa_kv_read instead of computing offsets.
+ *   A decode step of sequence s attends positions [0, L) (full) or
+ *   [max(0, L-W), L) (sliding), L = kv_len[s], and writes its own K/V at L-1.
+ */
+#ifndef SPA_H
+#define SPA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int spa_status;
+#define SPA_OK 0
+#define SPA_EINVAL (-1)        /* bad argument (shape, pointer, alignment, config) */
+#define SPA_EHIP (-2)          /* a HIP runtime call failed */
+#define SPA_EWORKSPACE (-3)    /* workspace smaller than spa_workspace_query() */
+#define SPA_EUNSUPPORTED (-4)  /* valid but not implemented (shape / dtype combination) */
+#define SPA_EMASK (-5)         /* CU mask empty, overlapping, or not honoured by the hardware */
+
+typedef enum { SPA_F32 = 0, SPA_BF16 = 1, SPA_E4M3 = 2 } spa_dtype;
+typedef enum { SPA_SLIDING = 0, SPA_FULL = 1 } spa_layer_kind;
+
+/* Model shapes. Constraints: head_dim == 64; Hq % Hkv == 0, Hq/Hkv <= 16;
+ * H % 64 == 0; inter % 32 == 0; window % 32 == 0; H, inter, Hq*D multiples
+ * of the weight k-step (32 bf16 / 16 fp32 / 64 e4m3 elements);
+ * E <= 256; 1 <= top_k <= min(E, 8); 1 <= n_resident <= E.
+ * dense_dtype: F32 or BF16 (wqkv, wo); expert_dtype: F32, BF16 or E4M3;
+ * kv_dtype: F32 or BF16 and equal to dense_dtype. */
+typedef struct spa_model_desc {
+  int32_t hidden;        /* H */
+  int32_t n_q_heads;     /* Hq */
+  int32_t n_kv_heads;    /* Hkv */
+  int32_t head_dim;      /* D */
+  int32_t n_experts;     /* E: router width */
+  int32_t n_resident;    /* E_res: experts held here; router pick t runs expert t % E_res */
+  int32_t top_k;         /* k */
+  int32_t inter;         /* I: expert intermediate width */
+  int32_t window;        /* W: sliding-window length */
+  int32_t n_layers;
+  float eps;             /* RMSNorm epsilon */
+  int32_t dense_dtype;
+  int32_t expert_dtype;
+  int32_t kv_dtype;
+} spa_model_desc;
+
+/* One layer's parameters and KV cache (device pointers). */
+typedef struct spa_layer {
+  int32_t kind;          /* spa_layer_kind */
+  const void* wqkv;
+  const void* wo;
+  const float* wr;
+  const void* wgu;
+  const void* wd;
+  const float* wgu_scale;   /* E4M3 experts only, else NULL */
+  const float* wd_scale;
+  const float* gamma1;
+  const float* gamma2;
+  const float* sinks;
+  void* k_cache;
+  void* v_cache;
+} spa_layer;
+
+/* The decode batch: B sequences, one decoded token each. */
+typedef struct spa_batch {
+  int32_t batch;              /* B */
+  int32_t max_kv_len;         /* host upper bound of kv_len[] (sizes the attention grid) */
+  const int32_t* kv_len;      /* device [B]: L (positions incl. the decoded token) */
+  const int64_t* kv_off;      /* device [B]: full-layer region start, in positions */
+  const int32_t* kv_cap;      /* device [B]: full-layer region capacity (multiple of 32) */
+  float* x;                   /* device [B][H] fp32, in/out */
+  int32_t* topk_out;          /* optional device [n_layers][B][k]: router picks per layer */
+} spa_batch;
+
+/* Router / dispatch buffers of B tokens (device). */
+typedef struct spa_route_bufs {
+  int32_t* topk_idx;   /* [B][k] router picks 0..E-1, by logit descending, ties to lower index */
+  float* topk_w;       /* [B][k] softmax over the k picked logits */
+  int32_t* offsets;    /* [E_res + 1] exclusive prefix sum of rows per resident expert */
+  int32_t* row_tok;    /* [B*k] dispatch row -> token */
+  int32_t* row_slot;   /* [B*k] dispatch row -> pick index */
+  int32_t* inv;        /* [B][k] (token, pick) -> dispatch row */
+} spa_route_bufs;
+
+typedef struct spa_ctx spa_ctx;
+typedef struct spa_pool spa_pool;
+typedef struct spa_pipeline spa_pipeline;
+
+/* ---------------------------------------------------------------- context */
+spa_status spa_init(int hip_device, spa_ctx** out);
+spa_status spa_shutdown(spa_ctx* ctx);
+const char* spa_last_error(void);
+/* number of CUs of the device (hipDeviceProp_t::multiProcessorCount) */
+spa_status spa_device_cus(spa_ctx* ctx, int32_t* n_cus);
+
+/* -------------------------------------------------------------- workspace */
+/* Bytes of workspace a call with these shapes needs: n_micro microbatches of
+ * batch/n_micro tokens each (n_micro = 1 for the single-op calls). */
+spa_status spa_workspace_query(const spa_model_desc* m, int32_t batch, int32_t max_kv_len, int32_t n_micro,
+                               size_t* bytes);
+/* Prepare a fresh workspace (clears its counters); enqueued on `stream`. */
+spa_status spa_workspace_init(spa_ctx* ctx, const spa_model_desc* m, int32_t batch, int32_t max_kv_len,
+                              int32_t n_micro, void* ws, size_t ws_bytes, void* stream);
+/* Device error bits found so far (1: a kv_len outside its cache); synchronises `stream`. */
+spa_status spa_workspace_errors(spa_ctx* ctx, const void* ws, size_t ws_bytes, void* stream, int32_t* bits);
+
+/* -------------------------------------------------------------- KV cache */
+/* Write (write = 1) or read (write = 0) n cache rows: row r is position pos[r]
+ * of sequence seq[r], all KV heads: rows [n][Hkv][D] in kv_dtype. seq/pos are
+ * device arrays. kind selects the layer layout (spa_layer_kind). */
+spa_status spa_kv_io(spa_ctx* ctx, const spa_model_desc* m, int32_t kind, void* k_cache, void* v_cache,
+                     const spa_batch* b, const int32_t* seq, const int32_t* pos, int32_t n, void* k_rows,
+                     void* v_rows, int32_t write, void* stream);
+
+/* -------------------------------------------------------- single operators
+ * Each acts on tokens [tok0, tok0 + n_tok) of the batch and uses `ws`
+ * (>= spa_workspace_query(m, n_tok, max_kv_len, 1) bytes). */
+
+/* Row sum-of-squares partials of x [n_tok][H]: ss [H/64][n_tok] (the RMSNorm
+ * statistic consumed by the projections). */
+spa_status spa_row_sumsq(spa_ctx* ctx, const spa_model_desc* m, const float* x, int32_t n_tok, float* ss,
+                         void* stream);
+
+/* Figure 3 "RMSNorm, Q proj, KV proj": xn = RMSNorm(x) gamma1 (bf16 when
+ * dense_dtype is BF16); [q | k | v] = xn Wqkv^T; q -> q_out [n_tok][Hq*D]
+ * (kv_dtype), k and v -> the layer's cache at position kv_len[s] - 1. */
+spa_status spa_qkv_append(spa_ctx* ctx, const spa_model_desc* m, const spa_layer* l, const spa_batch* b,
+                          int32_t tok0, int32_t n_tok, const float* ss_x, void* q_out, void* ws, size_t ws_bytes,
+                          void* stream);
+
+/* Figure 3 "FMHA" (section 5.1: sliding or full): grouped-query decode
+ * attention with sinks over the cached window; q [n_tok][Hq*D] and o_out
+ * [n_tok][Hq*D] in kv_dtype. Split-KV over 256-position chunks. */
+spa_status spa_decode_attn(spa_ctx* ctx, const spa_model_desc* m, const spa_layer* l, const spa_batch* b,
+                           int32_t tok0, int32_t n_tok, const void* q, void* o_out, void* ws, size_t ws_bytes,
+                           void* stream);
+
+/* Figure 3 "Output proj, Add+Norm": h = x + o Wo^T (h_out [n_tok][H] fp32)
+ * and the row sum-of-squares partials of h (ss_h [H/64][n_tok]). */
+spa_status spa_out_proj(spa_ctx* ctx, const spa_model_desc* m, const spa_layer* l, const float* x, const void* o,
+                        int32_t n_tok, float* h_out, float* ss_h, void* ws, size_t ws_bytes, void* stream);
+
+/* Figure 3 "Router gating, TopK dispatch": hn = RMSNorm(h) gamma2 (fp32);
+ * logits = hn Wr^T (fp32); top-k + softmax over the picks; permutation of
+ * (token, pick) rows grouped by resident expert (pick t -> expert t % E_res),
+ * (token, pick) ascending inside an expert. */
+spa_status spa_moe_route(spa_ctx* ctx, const spa_model_desc* m, const spa_layer* l, const float* h,
+                         const float* ss_h, int32_t n_tok, float* logits_out, const spa_route_bufs* r,
+                         int32_t* topk_rec, void* ws, size_t ws_bytes, void* stream);
+
+/* Figure 3 "Expert up (BMM), SwiGLU, Expert down": for each dispatch row,
+ * z = silu(hn Wg^T) * (hn Wu^T) and y = z Wd^T (y_out [n_tok*k][H] fp32). */
+spa_status spa_moe_expert(spa_ctx* ctx, const spa_model_desc* m, const spa_layer* l, const float* h,
+                          const float* ss_h, int32_t n_tok, const spa_route_bufs* r, float* y_out, void* ws,
+                          size_t ws_bytes, void* stream);
+
+/* Figure 3 "Combine": x_out = h + sum over picks (in pick order) of w * y,
+ * and the row sum-of-squares partials of x_out (ss_out [H/64][n_tok]). */
+spa_status spa_moe_combine(spa_ctx* ctx, const spa_model_desc* m, const float* h, const float* y,
+                           const spa_route_bufs* r, int32_t n_tok, float* x_out, float* ss_out, void* stream);
+
+/* One whole layer, temporal, on tokens [tok0, tok0 + n_tok): updates x in
+ * place, appends K/V, optionally records the router picks. */
+spa_status spa_layer_forward(spa_ctx* ctx, const spa_model_desc* m, const spa_layer* l, int32_t layer_index,
+                             const spa_batch* b, int32_t tok0, int32_t n_tok, void* ws, size_t ws_bytes,
+                             void* stream);
+
+/* ------------------------------------------------------ decode iteration */
+/* Temporal execution (section 5.1 "Temporal"): the n_layers layers in order,
+ * each kernel on the whole device, the batch split into n_micro equal
+ * microbatches processed one after another on `stream`. */
+spa_status spa_temporal_run(spa_ctx* ctx, const spa_model_desc* m, const spa_layer* layers, const spa_batch* b,
+                            int32_t n_micro, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------- CU pools
+ * The HIP analogue of an SM partition (section 2.4 of the paper): a pool is
+ * a set of CUs with its own stream(s) whose kernels may only run on those
+ * CUs (hipExtStreamCreateWithCUMask). Masks are given in the runtime's CU
+ * mask bit order (bit i of word i/32). */
+spa_status spa_pool_create_mask(spa_ctx* ctx, const uint32_t* cu_mask, int32_t n_words, spa_pool** out);
+/* A pool of n_cus CUs spread evenly over the XCDs; `first` selects which CUs
+ * of each XCD (pools built with disjoint [first, first + n_cus/n_xcd) ranges
+ * are disjoint). n_cus must be a multiple of the XCD count. */
+spa_status spa_pool_create_split(spa_ctx* ctx, int32_t first_per_xcd, int32_t n_cus, spa_pool** out);
+spa_status spa_pool_mask(spa_pool* p, uint32_t* mask_out, int32_t n_words);
+spa_status spa_pool_stream(spa_pool* p, void** hip_stream);
+/* Placement probe: launch many short workgroups on the pool's stream and
+ * report the distinct hardware CUs (XCC, SE, SH, CU ids packed as
+ * xcc << 16 | se << 8 | sh << 4 | cu) they ran on, up to max_ids entries. */
+spa_status spa_pool_probe(spa_pool* p, int32_t n_blocks, uint32_t* ids_out, int32_t max_ids, int32_t* n_ids);
+spa_status spa_pool_destroy(spa_pool* p);
+
+/* --------------------------------------------------------- the pipeline
+ * theta = (D = 2 stages, w = 0, cut, CU split, microbatch count) of section
+ * 3.1. Stage A holds the segment up to the cut, stage B the rest:
+ *   cut 0: A = Norm+QKV, attention, output projection (+ residual) | B = router ... combine
+ *   cut 1: A = Norm+QKV, attention, output projection, router       | B = experts, combine
+ * Microbatch mu is the contiguous token slice [mu*B/m, (mu+1)*B/m). Tasks are
+ * dispatched region-major, then microbatch (a topological order of the data
+ * edges, section 3.2); each stage runs its tasks in that order (stage FIFO);
+ * A(l, mu) waits for B(l-1, mu) and B(l, mu) for A(l, mu) through events. */
+typedef struct spa_pipeline_cfg {
+  int32_t cut;        /* 0 or 1 */
+  int32_t n_micro;    /* m, divides the batch */
+} spa_pipeline_cfg;
+
+spa_status spa_pipeline_create(spa_ctx* ctx, const spa_model_desc* m, const spa_pipeline_cfg* cfg, spa_pool* stage_a,
+                               spa_pool* stage_b, spa_pipeline** out);
+/* Run one decode iteration; joins `caller_stream` at both ends (the pipeline
+ * starts after work already queued there, and work queued there afterwards
+ * starts after the iteration). */
+spa_status spa_pipeline_run(spa_pipeline* p, const spa_layer* layers, const spa_batch* b, void* ws, size_t ws_bytes,
+                            void* caller_stream);
+/* Per-kernel timing: when enabled, every launch of kernel class `cls`
+ * (0 = full-layer attention, 1 = sliding attention, 2 = QKV, 3 = output
+ * projection, 4 = router, 5 = expert gate/up, 6 = expert down, 7 = combine)
+ * is bracketed by events; spa_pipeline_timing returns the mean duration (ms)
+ * over the launches since enabling, and the count. */
+spa_status spa_pipeline_time_kernel(spa_pipeline* p, int32_t cls, int32_t enable);
+spa_status spa_pipeline_timing(spa_pipeline* p, double* mean_ms, int32_t* count);
+spa_status spa_pipeline_destroy(spa_pipeline* p);
+
+/* ------------------------------------------------- schedule model (host)
+ * Equations 1, 4 and 5 of the paper: binding of segment k (1-based) of K
+ * with boundary reuse w, and the max-plus makespan of n_regions x n_micro x
+ * K segment tasks with durations tau[(l * n_micro + mu) * K + (k - 1)] in the
+ * region-major dispatch order. */
+int32_t spa_sched_binding(int32_t k, int32_t K, int32_t w);
+spa_status spa_sched_makespan(int32_t n_regions, int32_t n_micro, int32_t K, int32_t w, const double* tau,
+                              double* makespan, double* start_out, double* end_out);
+/* Equation 7's counts: contiguous cut-and-binding choices of an n_ops chain
+ * for n_stages (K = D and K = D + 1), and ordered full-budget allocations of
+ * n_units to n_stages in positive multiples of quantum. */
+spa_status spa_sched_counts(int32_t n_ops, int32_t n_stages, int32_t n_units, int32_t quantum, int64_t* cut_choices,
+                            int64_t* allocations);
+
+/* Section 4.2, Algorithm 2 (pairwise-line refinement): improve an
+ * allocation p[n_stages] (positive multiples of quantum, at least p_min,
+ * summing to total) by moving quanta between one donor and one receiver
+ * stage per pass. objective(p, user) returns the value to minimise.
+ * pass_limit <= 0 means no limit. */
+typedef double (*spa_objective_fn)(const int32_t* p, int32_t n_stages, void* user);
+spa_status spa_refine_allocation(int32_t n_stages, int32_t total, int32_t quantum, int32_t p_min, int32_t* p,
+                                 spa_objective_fn objective, void* user, int32_t pass_limit, double* best,
+                                 int32_t* n_evals);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPA_H */

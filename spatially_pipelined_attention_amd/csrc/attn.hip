@@ -1,0 +1,384 @@
+// Grouped-query decode attention with sinks on gfx950 (the "FMHA" operator of
+// Figure 3 of the SubGPU Pipelining paper; full and sliding-window layers as
+// in its section 5.1).
+//
+// Work item = (sequence, KV head, chunk of `chunk` cached positions). The 4
+// waves of a workgroup take 32-position blocks of the chunk round-robin:
+//   * S^T[pos][head] = K Q^T on MFMA: the K block streams from HBM straight
+//     into A-operand registers (16 B per lane per 16x32 tile half), all query
+//     heads of the KV group ride in the 16 B-operand columns;
+//   * online softmax in base 2, one head per lane column, running max shared
+//     by the 4 lanes that hold the column;
+//   * O^T[d][head] += V^T P^T on MFMA: V is cached d-major inside each
+//     32-position block (positions interleaved by v_slot) so the A operand is
+//     again one contiguous 16 B load, and the lane's own probabilities are
+//     exactly its B operand;
+//   * the 4 wave states merge through LDS; a chunk's (m, l, o) partial goes
+//     to workspace and the last chunk of a (sequence, KV head) to arrive
+//     (integer counter) merges all chunks in chunk order together with the
+//     sink logit: M = max(sink, m_c), Z = 2^(sink-M) + sum l_c 2^(m_c-M),
+//     o = sum o_c 2^(m_c-M) / Z.
+// Cache layouts (element offsets, D = 64):
+//   packed (full layers):  region(seq, g) = (kv_off[seq] * Hkv + g * cap[seq]) * D
+//   ring (sliding layers): region(seq, g) = (seq * Hkv + g) * W * D, slot = pos % W
+//   K at region + slot * D + d
+//   V at region + (slot / 32) * 32 * D + d * 32 + v_slot(slot % 32)
+#include "common.h"
+#include "kernels.h"
+
+namespace spa {
+
+constexpr int kD = 64;
+
+struct KvLoc {
+  long long base;
+  int n_valid;
+  bool ok;
+};
+
+__device__ __forceinline__ KvLoc kv_locate(const AttnArgs& a, int seq, int g) {
+  KvLoc r;
+  const int L = a.kv_len[seq];
+  if (a.kv_kind == KV_RING) {
+    r.base = ((long long)seq * a.n_kv_heads + g) * a.window * kD;
+    r.n_valid = min(L, a.window);
+    r.ok = L >= 1;
+  } else {
+    const int cap = a.kv_cap[seq];
+    r.base = (a.kv_off[seq] * a.n_kv_heads + (long long)g * cap) * kD;
+    r.n_valid = L;
+    r.ok = L >= 1 && L <= cap;
+  }
+  return r;
+}
+
+template <int KVT>
+struct BlockRegs;
+
+template <>
+struct BlockRegs<DT_BF16> {
+  u32x4 k[2][2];   // [tile][d half]
+  u32x4 v[4];      // [d tile]
+};
+
+template <>
+struct BlockRegs<DT_F32> {
+  u32x4 k[2][4];   // [tile][d quarter]
+  u32x4 v[4][2];   // [d tile][slot half]
+};
+
+template <int KVT>
+__device__ __forceinline__ void load_block(BlockRegs<KVT>& br, const char* kreg, const char* vreg, int blk, int lane,
+                                           bool stream) {
+  const int p16 = lane & 15, q4 = lane >> 4;
+  if constexpr (KVT == DT_BF16) {
+    const char* kb = kreg + ((long long)blk * 32 * kD) * 2;
+    const char* vb = vreg + ((long long)blk * 32 * kD) * 2;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const char* p = kb + ((16 * t + p16) * kD + 32 * h + 8 * q4) * 2;
+        br.k[t][h] = stream ? ld16_stream(p) : ld16(p);
+      }
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+      const char* p = vb + ((16 * dt + p16) * 32 + 8 * q4) * 2;
+      br.v[dt] = stream ? ld16_stream(p) : ld16(p);
+    }
+  } else {
+    const char* kb = kreg + ((long long)blk * 32 * kD) * 4;
+    const char* vb = vreg + ((long long)blk * 32 * kD) * 4;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc) {
+        const char* p = kb + ((16 * t + p16) * kD + 16 * cc + 4 * q4) * 4;
+        br.k[t][cc] = stream ? ld16_stream(p) : ld16(p);
+      }
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const char* p = vb + ((16 * dt + p16) * 32 + 8 * q4 + 4 * hh) * 4;
+        br.v[dt][hh] = stream ? ld16_stream(p) : ld16(p);
+      }
+  }
+}
+
+template <int KVT>
+struct QRegs;
+template <>
+struct QRegs<DT_BF16> { u32x4 q[2]; };
+template <>
+struct QRegs<DT_F32> { u32x4 q[4]; };
+
+// One 32-position block: scores, online softmax update, PV accumulation.
+template <int KVT>
+__device__ __forceinline__ void attend_block(const BlockRegs<KVT>& br, const QRegs<KVT>& qr, int blk, int n_valid,
+                                             float scale_log2, float& m_run, float& l_run, f32x4 (&acc)[4],
+                                             int lane) {
+  const int q4 = lane >> 4;
+  f32x4 s[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    s[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if constexpr (KVT == DT_BF16) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        s[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bitcast<bf16x8>(br.k[t][h]), bitcast<bf16x8>(qr.q[h]), s[t],
+                                                      0, 0, 0);
+    } else {
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc)
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          s[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(br.k[t][cc][u]), __uint_as_float(qr.q[cc][u]),
+                                                     s[t], 0, 0, 0);
+    }
+  }
+  // scale + mask; this lane holds positions 16t + 4q4 + r of head (lane & 15)
+  const int pos0 = blk * 32;
+  float bmax = -INFINITY;
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int pos = pos0 + 16 * t + 4 * q4 + r;
+      float v = s[t][r] * scale_log2;
+      v = pos < n_valid ? v : -INFINITY;
+      s[t][r] = v;
+      bmax = fmaxf(bmax, v);
+    }
+  bmax = fmaxf(bmax, __shfl_xor(bmax, 16, 64));
+  bmax = fmaxf(bmax, __shfl_xor(bmax, 32, 64));
+  const float m_new = fmaxf(m_run, bmax);
+  const float alpha = exp2f(m_run - m_new);   // m_run = -inf on the first block -> 0
+  m_run = m_new;
+  float p[2][4];
+  float psum = 0.f;
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      p[t][r] = exp2f(s[t][r] - m_new);
+      psum += p[t][r];
+    }
+  l_run = l_run * alpha + psum;
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) acc[dt] *= alpha;
+
+  // zero V of masked positions in a partial last block
+  const bool partial = pos0 + 32 > n_valid;
+  if constexpr (KVT == DT_BF16) {
+    u32x4 pf = {pack_bf16x2(p[0][0], p[0][1]), pack_bf16x2(p[0][2], p[0][3]), pack_bf16x2(p[1][0], p[1][1]),
+                pack_bf16x2(p[1][2], p[1][3])};
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+      u32x4 vv = br.v[dt];
+      if (partial) {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          // word w holds slots 8q4 + 2w, 8q4 + 2w + 1
+          int u0 = 2 * w, u1 = 2 * w + 1;
+          int pa = pos0 + (u0 < 4 ? 4 * q4 + u0 : 16 + 4 * q4 + u0 - 4);
+          int pb = pos0 + (u1 < 4 ? 4 * q4 + u1 : 16 + 4 * q4 + u1 - 4);
+          uint32_t m = (pa < n_valid ? 0x0000ffffu : 0u) | (pb < n_valid ? 0xffff0000u : 0u);
+          vv[w] &= m;
+        }
+      }
+      acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bitcast<bf16x8>(vv), bitcast<bf16x8>(pf), acc[dt], 0, 0, 0);
+    }
+  } else {
+    float pv[8] = {p[0][0], p[0][1], p[0][2], p[0][3], p[1][0], p[1][1], p[1][2], p[1][3]};
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        float vv = __uint_as_float(br.v[dt][u >> 2][u & 3]);
+        if (partial) {
+          int pp = pos0 + (u < 4 ? 4 * q4 + u : 16 + 4 * q4 + u - 4);
+          vv = pp < n_valid ? vv : 0.f;
+        }
+        acc[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(vv, pv[u], acc[dt], 0, 0, 0);
+      }
+  }
+}
+
+template <int KVT>
+__global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
+  __shared__ float s_m[4][16];
+  __shared__ float s_l[4][16];
+  __shared__ float s_o[4][kD][17];
+  __shared__ int s_flag;
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int seq = a.tok0 + b;
+  const int G = a.n_q_heads / a.n_kv_heads;
+  const KvLoc loc = kv_locate(a, seq, g);
+  if (!loc.ok) {
+    if (c == 0 && tid == 0 && a.err) atomicOr(a.err, ERR_KV_LEN);
+    return;
+  }
+  const int n_chunks = (loc.n_valid + a.chunk - 1) / a.chunk;
+  if (n_chunks > a.max_chunks) {   // kv_len above the planned maximum: refuse, never read past the plan
+    if (c == 0 && tid == 0 && a.err) atomicOr(a.err, ERR_KV_LEN);
+    return;
+  }
+  if (c >= n_chunks) return;
+
+  constexpr int esz = KVT == DT_BF16 ? 2 : 4;
+  const char* kreg = (const char*)a.k_cache + loc.base * esz;
+  const char* vreg = (const char*)a.v_cache + loc.base * esz;
+
+  // query fragment: head (lane & 15) of this group
+  const int hl = lane & 15, q4 = lane >> 4;
+  const bool hvalid = hl < G;
+  const char* qrow = (const char*)a.q + ((long long)b * a.n_q_heads + g * G + (hvalid ? hl : 0)) * kD * esz;
+  QRegs<KVT> qr;
+  if constexpr (KVT == DT_BF16) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) qr.q[h] = hvalid ? ld16(qrow + (32 * h + 8 * q4) * 2) : u32x4{0u, 0u, 0u, 0u};
+  } else {
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc) qr.q[cc] = hvalid ? ld16(qrow + (16 * cc + 4 * q4) * 4) : u32x4{0u, 0u, 0u, 0u};
+  }
+
+  const int bpc = a.chunk / 32;
+  const int blk0 = c * bpc;
+  const int blk_end = min(blk0 + bpc, (loc.n_valid + 31) / 32);
+  float m_run = -INFINITY, l_run = 0.f;
+  f32x4 acc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const bool stream = a.stream_kv != 0;
+  int j = blk0 + wave;
+  if (j < blk_end) {
+    BlockRegs<KVT> cur, nxt;
+    load_block<KVT>(cur, kreg, vreg, j, lane, stream);
+    for (;;) {
+      const bool more = j + 4 < blk_end;
+      if (more) load_block<KVT>(nxt, kreg, vreg, j + 4, lane, stream);
+      attend_block<KVT>(cur, qr, j, loc.n_valid, a.scale_log2, m_run, l_run, acc, lane);
+      if (!more) break;
+      j += 4;
+      cur = nxt;
+    }
+  }
+  l_run += __shfl_xor(l_run, 16, 64);
+  l_run += __shfl_xor(l_run, 32, 64);
+
+  // wave states -> LDS (O^T: lane holds d = 16 dt + 4 q4 + r of head hl)
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) s_o[wave][16 * dt + 4 * q4 + r][hl] = acc[dt][r];
+  if (q4 == 0) {
+    s_m[wave][hl] = m_run;
+    s_l[wave][hl] = l_run;
+  }
+  __syncthreads();
+
+  // merge the 4 waves: thread -> (head, d) pairs
+  const int GD = G * kD;
+  const long long pbase = (((long long)b * a.n_kv_heads + g) * a.max_chunks) * G * (kD + 2);
+  float mrg_o[4], mrg_m[4], mrg_l[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int idx = tid + 256 * i;
+    mrg_o[i] = 0.f;
+    mrg_m[i] = -INFINITY;
+    mrg_l[i] = 0.f;
+    if (idx < GD) {
+      const int h = idx >> 6, d = idx & 63;
+      float M = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) M = fmaxf(M, s_m[w][h]);
+      float l = 0.f, o = 0.f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const float mw = s_m[w][h];
+        const float f = mw == -INFINITY ? 0.f : exp2f(mw - M);
+        l += f * s_l[w][h];
+        o += f * s_o[w][d][h];
+      }
+      mrg_o[i] = o;
+      mrg_m[i] = M;
+      mrg_l[i] = l;
+    }
+  }
+
+  bool last = true;
+  if (n_chunks > 1) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int idx = tid + 256 * i;
+      if (idx < GD) {
+        const int h = idx >> 6, d = idx & 63;
+        float* pp = a.part + pbase + ((long long)c * G + h) * (kD + 2);
+        pp[d] = mrg_o[i];
+        if (d == 0) {
+          pp[kD] = mrg_m[i];
+          pp[kD + 1] = mrg_l[i];
+        }
+      }
+    }
+    __threadfence();
+    __syncthreads();
+    if (tid == 0) {
+      int* ctr = a.ctr + (long long)b * a.n_kv_heads + g;
+      int old = atomicAdd(ctr, 1);
+      int l = old == n_chunks - 1;
+      if (l) atomicExch(ctr, 0);
+      s_flag = l;
+    }
+    __syncthreads();
+    last = s_flag != 0;
+    if (last) __threadfence();
+  }
+  if (!last) return;
+
+  // final merge over chunks (fixed chunk order) with the sink
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int idx = tid + 256 * i;
+    if (idx >= GD) continue;
+    const int h = idx >> 6, d = idx & 63;
+    const int hq = g * G + h;
+    const float sink = a.sinks[hq] * kLog2e;
+    float M = sink, Z, o;
+    if (n_chunks == 1) {
+      M = fmaxf(M, mrg_m[i]);
+      const float f = mrg_m[i] == -INFINITY ? 0.f : exp2f(mrg_m[i] - M);
+      Z = exp2f(sink - M) + f * mrg_l[i];
+      o = f * mrg_o[i];
+    } else {
+      const float* pp = a.part + pbase + (long long)h * (kD + 2);
+      const long long cstride = (long long)G * (kD + 2);
+      for (int cc = 0; cc < n_chunks; ++cc) M = fmaxf(M, pp[cc * cstride + kD]);
+      Z = exp2f(sink - M);
+      o = 0.f;
+      for (int cc = 0; cc < n_chunks; ++cc) {
+        const float mc = pp[cc * cstride + kD];
+        const float f = mc == -INFINITY ? 0.f : exp2f(mc - M);
+        Z += f * pp[cc * cstride + kD + 1];
+        o += f * pp[cc * cstride + d];
+      }
+    }
+    const float out = o / Z;
+    const long long oi = ((long long)b * a.n_q_heads + hq) * kD + d;
+    if constexpr (KVT == DT_BF16) ((uint16_t*)a.o)[oi] = f32_to_bf16(out);
+    else ((float*)a.o)[oi] = out;
+  }
+}
+
+hipError_t launch_attn(const AttnArgs& a, hipStream_t st) {
+  dim3 grid(a.max_chunks, a.n_kv_heads, a.n_tok);
+  if (a.kv_dtype == DT_BF16) hipLaunchKernelGGL(k_attn<DT_BF16>, grid, dim3(256), 0, st, a);
+  else hipLaunchKernelGGL(k_attn<DT_F32>, grid, dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace spa

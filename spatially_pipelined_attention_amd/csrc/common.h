@@ -1,0 +1,89 @@
+// Shared device helpers for the gfx950 kernels (CDNA4, wave64).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace spa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// fp32 -> bf16, round to nearest even; NaN stays NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+}
+
+// Barrier that orders LDS only: outstanding global loads stay in flight.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+template <typename T>
+__device__ __forceinline__ T wave_sum(T v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+__device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+__device__ __forceinline__ u32x4 ld16_stream(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+__device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+
+template <typename T, typename S>
+__device__ __forceinline__ T bitcast(S s) {
+  static_assert(sizeof(T) == sizeof(S), "bitcast size");
+  return __builtin_bit_cast(T, s);
+}
+
+// Position p of a 32-position KV block -> storage slot inside the block's
+// d-major V tile. Two 16-position halves are interleaved in runs of four so
+// that one lane's eight MFMA k-slots (positions 4q..4q+3 of both halves) are
+// one contiguous 16-byte run.
+__host__ __device__ __forceinline__ int v_slot(int p) {
+  return 8 * ((p & 15) >> 2) + 4 * (p >> 4) + (p & 3);
+}
+
+// OCP E4M3 value of a finite float already in [-448, 448]: round to nearest
+// even on 3 mantissa bits (quantum 2^-9 below 2^-6).
+__device__ __forceinline__ uint8_t f32_to_e4m3(float f) {
+  uint32_t u = __float_as_uint(f);
+  uint8_t sign = (uint8_t)((u >> 24) & 0x80u);
+  float a = fabsf(f);
+  if (a >= 448.0f) return sign | 0x7Eu;
+  int e = (int)((__float_as_uint(a) >> 23) & 0xff) - 127;   // a == 0 gives -127
+  if (e < -6) e = -6;
+  float q = __uint_as_float((uint32_t)(e - 3 + 127) << 23);  // 2^(e-3)
+  float n = __builtin_rintf(a / q);                            // ties to even
+  float v = n * q;
+  if (v >= 448.0f) return sign | 0x7Eu;
+  if (v == 0.0f) return sign;
+  int ev = (int)((__float_as_uint(v) >> 23) & 0xff) - 127;
+  if (ev < -6) return sign | (uint8_t)(int)(v * 512.0f);      // subnormal: mant * 2^-9
+  int mant = (int)(v / __uint_as_float((uint32_t)(ev - 3 + 127) << 23)) - 8;
+  return sign | (uint8_t)(((ev + 7) << 3) | mant);
+}
+
+}  // namespace spa

@@ -1,0 +1,112 @@
+// Host-side internals shared by the C ABI translation units.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <string>
+#include <vector>
+
+#include "kernels.h"
+#include "spa.h"
+
+struct spa_ctx {
+  int device = 0;
+  int n_cus = 0;
+  int n_xcd = 8;
+  hipDeviceProp_t prop{};
+};
+
+namespace spa {
+
+void set_error(const std::string& msg);
+spa_status fail(spa_status code, const std::string& msg);
+spa_status hip_fail(hipError_t e, const char* what);
+
+#define SPA_HIP(call)                                   \
+  do {                                                  \
+    hipError_t _e = (call);                             \
+    if (_e != hipSuccess) return ::spa::hip_fail(_e, #call); \
+  } while (0)
+
+// Kernel classes (timing hooks and split heuristics).
+enum KClass : int {
+  KC_ATTN_FULL = 0, KC_ATTN_SLIDING = 1, KC_QKV = 2, KC_OPROJ = 3,
+  KC_ROUTER = 4, KC_GATEUP = 5, KC_DOWN = 6, KC_COMBINE = 7, KC_COUNT = 8
+};
+
+constexpr int kAttnChunk = 256;
+
+// Byte layout of one microbatch slot of the workspace.
+struct SlotLayout {
+  size_t ss_x, ss_h, q, o, h, logits;
+  size_t topk_idx, topk_w, offsets, row_tok, row_slot, inv;
+  size_t hq8, hq8_scale, z, z8, z8_scale, y;
+  size_t attn_part, gemm_part, attn_ctr, gemm_ctr, done_ctr;
+  size_t bytes;
+};
+
+struct WsLayout {
+  size_t err;           // int32 error word (shared by all slots)
+  size_t slot0;         // first slot
+  size_t slot_bytes;
+  int n_slots;
+  int n_tok;            // tokens per slot
+  int max_chunks;
+  size_t total;
+  SlotLayout s;
+  // counters region of a slot (relative), cleared on init
+  size_t ctr_begin, ctr_end;
+};
+
+struct GemmPlan {
+  int n_tiles, n_groups, S, rb_stride, ks;
+};
+
+spa_status validate_model(const spa_model_desc* m);
+WsLayout ws_layout(const spa_model_desc* m, int n_tok, int max_kv_len, int n_micro);
+int max_chunks_for(int max_kv_len, const spa_model_desc* m);
+GemmPlan plan_gemm(int kclass, const spa_model_desc* m, int n_tok, int n_cus);
+
+// Per-slot device pointers resolved from a workspace base.
+struct Slot {
+  char* base;
+  int* err;
+  float* ss_x;
+  float* ss_h;
+  void* q;
+  void* o;
+  float* h;
+  float* logits;
+  spa_route_bufs route;
+  uint8_t* hq8;
+  float* hq8_scale;
+  void* z;
+  uint8_t* z8;
+  float* z8_scale;
+  float* y;
+  float* attn_part;
+  float* gemm_part;
+  int* attn_ctr;
+  int* gemm_ctr;
+  int* done_ctr;
+};
+
+Slot slot_ptrs(const WsLayout& L, void* ws, int slot);
+
+// Timing hook: called around each kernel launch of a class (may be null).
+struct TimingHook {
+  int cls = -1;
+  std::vector<hipEvent_t>* evs = nullptr;   // pairs (start, stop)
+  std::vector<hipEvent_t>* pool = nullptr;  // free events
+};
+
+// The layer's pieces on one slot (tokens [tok0, tok0+n_tok)); enqueue on st.
+spa_status run_segment_a(spa_ctx* ctx, const spa_model_desc* m, const spa_layer* l, int layer_index,
+                         const spa_batch* b, int tok0, int n_tok, const WsLayout& W, const Slot& s, bool with_router,
+                         bool first_layer, hipStream_t st, TimingHook* th);
+spa_status run_segment_b(spa_ctx* ctx, const spa_model_desc* m, const spa_layer* l, int layer_index,
+                         const spa_batch* b, int tok0, int n_tok, const WsLayout& W, const Slot& s, bool with_router,
+                         hipStream_t st, TimingHook* th);
+spa_status clear_counters(const WsLayout& W, void* ws, hipStream_t st);
+
+}  // namespace spa

@@ -1,0 +1,290 @@
+// CU pools and the two-stage spatial pipeline (sections 3.1-3.2 and 5.3.2 of
+// the SubGPU Pipelining paper, realised with CU-masked HIP streams and
+// events instead of Green Contexts).
+#include <string.h>
+
+#include <algorithm>
+#include <set>
+#include <string>
+#include <vector>
+
+#include <hip/hip_ext.h>
+
+#include "host.h"
+
+using namespace spa;
+
+struct spa_pool {
+  spa_ctx* ctx = nullptr;
+  std::vector<uint32_t> mask;
+  hipStream_t stream = nullptr;
+  unsigned* probe_buf = nullptr;
+};
+
+struct spa_pipeline {
+  spa_ctx* ctx = nullptr;
+  spa_model_desc m{};
+  spa_pipeline_cfg cfg{};
+  spa_pool* a = nullptr;   // null: temporal (everything on the caller stream)
+  spa_pool* b = nullptr;
+  std::vector<hipEvent_t> evA, evB;   // [layer][micro]
+  hipEvent_t ev_start = nullptr, ev_end_a = nullptr, ev_end_b = nullptr;
+  int timed_cls = -1;
+  std::vector<hipEvent_t> tevs, tpool;
+  double t_sum_ms = 0.0;
+  int t_count = 0;
+};
+
+static spa_status make_pool(spa_ctx* ctx, const std::vector<uint32_t>& mask, spa_pool** out) {
+  int nbits = 0;
+  for (size_t w = 0; w < mask.size(); ++w) {
+    for (int bit = 0; bit < 32; ++bit) {
+      if (mask[w] >> bit & 1u) {
+        if ((int)(w * 32 + bit) >= ctx->n_cus) return fail(SPA_EMASK, "CU mask names a CU beyond the device");
+        ++nbits;
+      }
+    }
+  }
+  if (nbits == 0) return fail(SPA_EMASK, "CU mask is empty");
+  spa_pool* p = new spa_pool();
+  p->ctx = ctx;
+  p->mask = mask;
+  hipError_t e = hipSetDevice(ctx->device);
+  if (e == hipSuccess) e = hipExtStreamCreateWithCUMask(&p->stream, (uint32_t)mask.size(), mask.data());
+  if (e != hipSuccess) {
+    delete p;
+    return hip_fail(e, "hipExtStreamCreateWithCUMask");
+  }
+  *out = p;
+  return SPA_OK;
+}
+
+extern "C" {
+
+spa_status spa_pool_create_mask(spa_ctx* ctx, const uint32_t* cu_mask, int32_t n_words, spa_pool** out) {
+  if (!ctx || !cu_mask || !out || n_words < 1) return fail(SPA_EINVAL, "bad argument");
+  std::vector<uint32_t> m(cu_mask, cu_mask + n_words);
+  return make_pool(ctx, m, out);
+}
+
+spa_status spa_pool_create_split(spa_ctx* ctx, int32_t first_per_xcd, int32_t n_cus, spa_pool** out) {
+  if (!ctx || !out) return fail(SPA_EINVAL, "bad argument");
+  const int nx = ctx->n_xcd;
+  const int per_xcd = ctx->n_cus / nx;
+  if (n_cus < nx || n_cus % nx) return fail(SPA_EINVAL, "n_cus must be a positive multiple of the XCD count");
+  const int take = n_cus / nx;
+  if (first_per_xcd < 0 || first_per_xcd + take > per_xcd) return fail(SPA_EINVAL, "CU range beyond an XCD");
+  // runtime CU mask bit i belongs to XCD i % n_xcd (mask bits are dealt to
+  // the XCDs round-robin); its index inside the XCD is i / n_xcd
+  std::vector<uint32_t> mask((ctx->n_cus + 31) / 32, 0u);
+  for (int x = 0; x < nx; ++x)
+    for (int j = first_per_xcd; j < first_per_xcd + take; ++j) {
+      int bit = j * nx + x;
+      mask[bit / 32] |= 1u << (bit % 32);
+    }
+  return make_pool(ctx, mask, out);
+}
+
+spa_status spa_pool_mask(spa_pool* p, uint32_t* mask_out, int32_t n_words) {
+  if (!p || !mask_out) return fail(SPA_EINVAL, "bad argument");
+  for (int i = 0; i < n_words; ++i) mask_out[i] = i < (int)p->mask.size() ? p->mask[i] : 0u;
+  return SPA_OK;
+}
+
+spa_status spa_pool_stream(spa_pool* p, void** s) {
+  if (!p || !s) return fail(SPA_EINVAL, "bad argument");
+  *s = (void*)p->stream;
+  return SPA_OK;
+}
+
+spa_status spa_pool_probe(spa_pool* p, int32_t n_blocks, uint32_t* ids_out, int32_t max_ids, int32_t* n_ids) {
+  if (!p || !ids_out || !n_ids || n_blocks < 1 || n_blocks > (1 << 20)) return fail(SPA_EINVAL, "bad argument");
+  unsigned* buf = nullptr;
+  SPA_HIP(hipMalloc(&buf, sizeof(unsigned) * 2 * n_blocks));
+  std::vector<unsigned> h(2 * (size_t)n_blocks);
+  hipError_t e = launch_probe(buf, n_blocks, 20000, p->stream);
+  if (e == hipSuccess) e = hipMemcpyAsync(h.data(), buf, h.size() * sizeof(unsigned), hipMemcpyDeviceToHost, p->stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(p->stream);
+  (void)hipFree(buf);
+  if (e != hipSuccess) return hip_fail(e, "probe");
+  std::set<uint32_t> ids;
+  for (int i = 0; i < n_blocks; ++i) {
+    unsigned xcc = h[2 * i] & 0xF, hw = h[2 * i + 1];
+    unsigned cu = (hw >> 8) & 0xF, sh = (hw >> 12) & 1, se = (hw >> 13) & 7;
+    ids.insert((xcc << 16) | (se << 8) | (sh << 4) | cu);
+  }
+  int n = 0;
+  for (uint32_t v : ids) {
+    if (n < max_ids) ids_out[n] = v;
+    ++n;
+  }
+  *n_ids = n;
+  return SPA_OK;
+}
+
+spa_status spa_pool_destroy(spa_pool* p) {
+  if (!p) return SPA_OK;
+  if (p->stream) (void)hipStreamDestroy(p->stream);
+  delete p;
+  return SPA_OK;
+}
+
+spa_status spa_pipeline_create(spa_ctx* ctx, const spa_model_desc* m, const spa_pipeline_cfg* cfg, spa_pool* stage_a,
+                               spa_pool* stage_b, spa_pipeline** out) {
+  if (!ctx || !cfg || !out) return fail(SPA_EINVAL, "bad argument");
+  spa_status rc = validate_model(m);
+  if (rc) return rc;
+  if (cfg->cut != 0 && cfg->cut != 1) return fail(SPA_EINVAL, "cut must be 0 or 1");
+  if (cfg->n_micro < 1) return fail(SPA_EINVAL, "n_micro must be >= 1");
+  if ((stage_a == nullptr) != (stage_b == nullptr)) return fail(SPA_EINVAL, "give both pools or neither");
+  if (stage_a) {
+    if (stage_a == stage_b) return fail(SPA_EMASK, "the two stages need distinct pools");
+    size_t nw = std::max(stage_a->mask.size(), stage_b->mask.size());
+    for (size_t w = 0; w < nw; ++w) {
+      uint32_t ma = w < stage_a->mask.size() ? stage_a->mask[w] : 0u;
+      uint32_t mb = w < stage_b->mask.size() ? stage_b->mask[w] : 0u;
+      if (ma & mb) return fail(SPA_EMASK, "stage CU pools overlap");
+    }
+  }
+  spa_pipeline* p = new spa_pipeline();
+  p->ctx = ctx;
+  p->m = *m;
+  p->cfg = *cfg;
+  p->a = stage_a;
+  p->b = stage_b;
+  const size_t n_ev = (size_t)m->n_layers * cfg->n_micro;
+  p->evA.resize(n_ev, nullptr);
+  p->evB.resize(n_ev, nullptr);
+  hipError_t e = hipSuccess;
+  for (size_t i = 0; i < n_ev && e == hipSuccess; ++i) {
+    e = hipEventCreateWithFlags(&p->evA[i], hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&p->evB[i], hipEventDisableTiming);
+  }
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&p->ev_start, hipEventDisableTiming);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&p->ev_end_a, hipEventDisableTiming);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&p->ev_end_b, hipEventDisableTiming);
+  if (e != hipSuccess) {
+    spa_pipeline_destroy(p);
+    return hip_fail(e, "hipEventCreate");
+  }
+  *out = p;
+  return SPA_OK;
+}
+
+static void harvest_timing(spa_pipeline* p) {
+  // pairs (start, stop) in launch order; all complete once the caller synchronised
+  for (size_t i = 0; i + 1 < p->tevs.size(); i += 2) {
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, p->tevs[i], p->tevs[i + 1]) == hipSuccess) {
+      p->t_sum_ms += ms;
+      p->t_count += 1;
+    }
+    p->tpool.push_back(p->tevs[i]);
+    p->tpool.push_back(p->tevs[i + 1]);
+  }
+  p->tevs.clear();
+}
+
+spa_status spa_pipeline_run(spa_pipeline* p, const spa_layer* layers, const spa_batch* b, void* ws, size_t ws_bytes,
+                            void* caller_stream) {
+  if (!p || !layers || !b) return fail(SPA_EINVAL, "bad argument");
+  const spa_model_desc* m = &p->m;
+  const int n_micro = p->cfg.n_micro;
+  if (b->batch < 1 || b->batch % n_micro) return fail(SPA_EINVAL, "n_micro must divide the batch");
+  if (!b->x || !b->kv_len || !b->kv_off || !b->kv_cap || b->max_kv_len < 1) return fail(SPA_EINVAL, "bad batch");
+  if (b->batch * m->top_k > 4096 * n_micro) return fail(SPA_EUNSUPPORTED, "microbatch * top_k above 4096");
+  for (int i = 0; i < m->n_layers; ++i) {
+    const spa_layer* l = &layers[i];
+    if (!l->wqkv || !l->wo || !l->wr || !l->wgu || !l->wd || !l->gamma1 || !l->gamma2 || !l->sinks || !l->k_cache ||
+        !l->v_cache || (l->kind != SPA_FULL && l->kind != SPA_SLIDING))
+      return fail(SPA_EINVAL, "incomplete layer " + std::to_string(i));
+    if (m->expert_dtype == SPA_E4M3 && (!l->wgu_scale || !l->wd_scale))
+      return fail(SPA_EINVAL, "E4M3 experts need scales");
+  }
+  const int bm = b->batch / n_micro;
+  if (!ws || (((uintptr_t)ws) & 255)) return fail(SPA_EINVAL, "workspace NULL or not 256-byte aligned");
+  WsLayout W = ws_layout(m, bm, b->max_kv_len, n_micro);
+  if (ws_bytes < W.total) return fail(SPA_EWORKSPACE, "workspace too small: need " + std::to_string(W.total));
+
+  hipStream_t cs = (hipStream_t)caller_stream;
+  if (!p->tevs.empty()) harvest_timing(p);
+  TimingHook th;
+  th.cls = p->timed_cls;
+  th.evs = &p->tevs;
+  th.pool = &p->tpool;
+  TimingHook* thp = p->timed_cls >= 0 ? &th : nullptr;
+
+  spa_status rc = clear_counters(W, ws, cs);
+  if (rc) return rc;
+  const bool temporal = p->a == nullptr;
+  const bool router_in_a = p->cfg.cut == 1;
+  hipStream_t sa = temporal ? cs : p->a->stream;
+  hipStream_t sb = temporal ? cs : p->b->stream;
+  if (!temporal) {
+    SPA_HIP(hipEventRecord(p->ev_start, cs));
+    SPA_HIP(hipStreamWaitEvent(sa, p->ev_start, 0));
+    SPA_HIP(hipStreamWaitEvent(sb, p->ev_start, 0));
+  }
+  for (int l = 0; l < m->n_layers; ++l) {
+    for (int mu = 0; mu < n_micro; ++mu) {
+      Slot s = slot_ptrs(W, ws, mu);
+      const size_t ei = (size_t)l * n_micro + mu;
+      if (!temporal && l > 0) SPA_HIP(hipStreamWaitEvent(sa, p->evB[ei - n_micro], 0));
+      rc = run_segment_a(p->ctx, m, &layers[l], l, b, mu * bm, bm, W, s, router_in_a, l == 0, sa, thp);
+      if (rc) return rc;
+      if (!temporal) {
+        SPA_HIP(hipEventRecord(p->evA[ei], sa));
+        SPA_HIP(hipStreamWaitEvent(sb, p->evA[ei], 0));
+      }
+      rc = run_segment_b(p->ctx, m, &layers[l], l, b, mu * bm, bm, W, s, router_in_a, sb, thp);
+      if (rc) return rc;
+      if (!temporal) SPA_HIP(hipEventRecord(p->evB[ei], sb));
+    }
+  }
+  if (!temporal) {
+    SPA_HIP(hipEventRecord(p->ev_end_a, sa));
+    SPA_HIP(hipEventRecord(p->ev_end_b, sb));
+    SPA_HIP(hipStreamWaitEvent(cs, p->ev_end_a, 0));
+    SPA_HIP(hipStreamWaitEvent(cs, p->ev_end_b, 0));
+  }
+  return SPA_OK;
+}
+
+spa_status spa_pipeline_time_kernel(spa_pipeline* p, int32_t cls, int32_t enable) {
+  if (!p || cls < 0 || cls >= KC_COUNT) return fail(SPA_EINVAL, "bad argument");
+  if (!p->tevs.empty()) {
+    SPA_HIP(hipDeviceSynchronize());
+    harvest_timing(p);
+  }
+  p->timed_cls = enable ? cls : -1;
+  p->t_sum_ms = 0.0;
+  p->t_count = 0;
+  return SPA_OK;
+}
+
+spa_status spa_pipeline_timing(spa_pipeline* p, double* mean_ms, int32_t* count) {
+  if (!p || !mean_ms || !count) return fail(SPA_EINVAL, "bad argument");
+  SPA_HIP(hipDeviceSynchronize());
+  harvest_timing(p);
+  *count = p->t_count;
+  *mean_ms = p->t_count ? p->t_sum_ms / p->t_count : 0.0;
+  return SPA_OK;
+}
+
+spa_status spa_pipeline_destroy(spa_pipeline* p) {
+  if (!p) return SPA_OK;
+  (void)hipDeviceSynchronize();
+  for (hipEvent_t e : p->evA)
+    if (e) (void)hipEventDestroy(e);
+  for (hipEvent_t e : p->evB)
+    if (e) (void)hipEventDestroy(e);
+  for (hipEvent_t e : p->tevs) (void)hipEventDestroy(e);
+  for (hipEvent_t e : p->tpool) (void)hipEventDestroy(e);
+  if (p->ev_start) (void)hipEventDestroy(p->ev_start);
+  if (p->ev_end_a) (void)hipEventDestroy(p->ev_end_a);
+  if (p->ev_end_b) (void)hipEventDestroy(p->ev_end_b);
+  delete p;
+  return SPA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,164 @@
+"""GPU parity of every step of one decode layer against the CPU oracle.
+
+Inputs come from the seeded generator; the HIP path runs all tokens of the
+batch and the oracle a sample of them (tokens are independent, so the sample
+is exact). Stages with oracle inputs injected isolate one kernel each; the
+chained run covers the whole layer.
+"""
+import numpy as np
+import pytest
+import torch
+
+from tests import harness as hz
+
+pytestmark = pytest.mark.gpu
+
+CASES = {
+    # workload, sampled tokens
+    "tiny_fp32": [0, 1, 2, 3],
+    "gptoss_layer_full": [0, 5, 17, 63],
+}
+
+
+def _f(t):
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+@pytest.fixture(scope="module", params=list(CASES))
+def setup(request):
+    from spatially_pipelined_attention_amd import binding as B, synth
+    from spatially_pipelined_attention_amd.workload import DeviceWorkload
+    name = request.param
+    wl = synth.WORKLOADS[name]
+    toks = CASES[name]
+    print(f"\n[setup] {name}: tokens {toks}", flush=True)
+    resample, margins = hz.resample_for_margins(wl, toks)
+    x_out, picks, mg, recs = hz.run_oracle(wl, toks, resample, keep_records=True)
+    dw = DeviceWorkload(wl, resample)
+    ctx = B.spa_init(0)
+    return dict(name=name, wl=wl, toks=toks, rec=recs[0], dw=dw, ctx=ctx, B=B, x_ref=x_out)
+
+
+def _bufs(s, n):
+    wl, dw = s["wl"], s["dw"]
+    dev = dw.dev
+    kvt = torch.bfloat16 if wl.kv_dtype == "bf16" else torch.float32
+    H, QD, k = wl.hidden, wl.n_q_heads * wl.head_dim, wl.top_k
+    return dict(
+        ss_x=torch.zeros((H // 64, n), dtype=torch.float32, device=dev),
+        ss_h=torch.zeros((H // 64, n), dtype=torch.float32, device=dev),
+        q=torch.zeros((n, QD), dtype=kvt, device=dev),
+        o=torch.zeros((n, QD), dtype=kvt, device=dev),
+        h=torch.zeros((n, H), dtype=torch.float32, device=dev),
+        logits=torch.zeros((n, wl.n_experts), dtype=torch.float32, device=dev),
+        topk_idx=torch.zeros((n, k), dtype=torch.int32, device=dev),
+        topk_w=torch.zeros((n, k), dtype=torch.float32, device=dev),
+        offsets=torch.zeros(wl.n_resident + 1, dtype=torch.int32, device=dev),
+        row_tok=torch.zeros(n * k, dtype=torch.int32, device=dev),
+        row_slot=torch.zeros(n * k, dtype=torch.int32, device=dev),
+        inv=torch.zeros((n, k), dtype=torch.int32, device=dev),
+        y=torch.zeros((n * k, H), dtype=torch.float32, device=dev),
+        xo=torch.zeros((n, H), dtype=torch.float32, device=dev),
+        ss_o=torch.zeros((H // 64, n), dtype=torch.float32, device=dev),
+    )
+
+
+def _route(B, b):
+    return B.spa_route_bufs(b["topk_idx"].data_ptr(), b["topk_w"].data_ptr(), b["offsets"].data_ptr(),
+                            b["row_tok"].data_ptr(), b["row_slot"].data_ptr(), b["inv"].data_ptr())
+
+
+def test_steps_chained_and_isolated(setup):
+    s = setup
+    B, wl, dw, ctx, rec, toks = s["B"], s["wl"], s["dw"], s["ctx"], s["rec"], s["toks"]
+    tol = hz.tol_of(wl)
+    n = wl.batch
+    m = dw.m
+    lay = dw.layers_c[0]
+    bf = _bufs(s, n)
+    ws = dw.workspace(n_tok=n)
+    dw.reset_x()
+    print(f"[{s['name']}] qkv", flush=True)
+    B.spa_row_sumsq(ctx, m, dw.x, n, bf["ss_x"])
+    B.spa_qkv_append(ctx, m, lay, dw.batch, 0, n, bf["ss_x"], bf["q"], ws)
+    torch.cuda.synchronize()
+    q = _f(bf["q"]).reshape(n, wl.n_q_heads, wl.head_dim)
+    hz.assert_close_rms(q[toks], rec.q, tol, "q")
+    L = dw.L
+    kk, vv = dw.read_kv(0, toks, [int(L[b]) - 1 for b in toks])
+    hz.assert_close_rms(kk, rec.k_new, tol, "k_new")
+    hz.assert_close_rms(vv, rec.v_new, tol, "v_new")
+
+    # attention, isolated: oracle q and new K/V injected for the sampled tokens
+    print(f"[{s['name']}] attention", flush=True)
+    kvt = bf["q"].dtype
+    qi = bf["q"].view(n, wl.n_q_heads, wl.head_dim)
+    qi[toks] = torch.as_tensor(rec.q, dtype=torch.float32, device=dw.dev).to(kvt)
+    kr = torch.as_tensor(rec.k_new, dtype=torch.float32, device=dw.dev).to(kvt).contiguous()
+    vr = torch.as_tensor(rec.v_new, dtype=torch.float32, device=dw.dev).to(kvt).contiguous()
+    t0 = dw.layers_t[0]
+    B.spa_kv_io(ctx, m, t0["kind"], t0["k_cache"], t0["v_cache"], dw._io_batch(),
+                torch.as_tensor(np.array(toks, np.int32), device=dw.dev),
+                torch.as_tensor(np.array([int(L[b]) - 1 for b in toks], np.int32), device=dw.dev), len(toks), kr, vr, 1)
+    B.spa_decode_attn(ctx, m, lay, dw.batch, 0, n, bf["q"], bf["o"], ws)
+    torch.cuda.synchronize()
+    o = _f(bf["o"]).reshape(n, wl.n_q_heads, wl.head_dim)
+    hz.assert_close_rms(o[toks], rec.o, tol, "attention o")
+
+    # output projection + residual (GPU o of every token)
+    print(f"[{s['name']}] out proj", flush=True)
+    B.spa_out_proj(ctx, m, lay, dw.x, bf["o"], n, bf["h"], bf["ss_h"], ws)
+    torch.cuda.synchronize()
+    h = _f(bf["h"])
+    hz.assert_close_rms(h[toks], rec.h, tol, "h")
+    ss = _f(bf["ss_h"]).sum(axis=0)
+    np.testing.assert_allclose(ss[toks], (rec.h ** 2).sum(axis=1), rtol=5e-2 if tol > 1e-3 else 1e-4)
+
+    # router, isolated: oracle h injected
+    print(f"[{s['name']}] route", flush=True)
+    bf["h"][toks] = torch.as_tensor(rec.h, dtype=torch.float32, device=dw.dev)
+    B.spa_row_sumsq(ctx, m, bf["h"], n, bf["ss_h"])
+    route = _route(B, bf)
+    B.spa_moe_route(ctx, m, lay, bf["h"], bf["ss_h"], n, bf["logits"], route, None, ws)
+    torch.cuda.synchronize()
+    lg = _f(bf["logits"])
+    np.testing.assert_allclose(lg[toks], rec.logits, rtol=1e-4, atol=1e-4 * np.abs(rec.logits).max())
+    idx = bf["topk_idx"].cpu().numpy()
+    np.testing.assert_array_equal(idx[toks], rec.topk)
+    np.testing.assert_allclose(bf["topk_w"].cpu().numpy()[toks], rec.weights, rtol=1e-4, atol=1e-6)
+    # permutation invariants over all tokens (bit-exact integer work)
+    from oracle.layer import permutation
+    grp = idx.astype(np.int64) % wl.n_resident
+    counts, offs, rt, rs, inv = permutation(grp, wl.n_resident)
+    np.testing.assert_array_equal(bf["offsets"].cpu().numpy(), offs)
+    np.testing.assert_array_equal(bf["row_tok"].cpu().numpy(), rt)
+    np.testing.assert_array_equal(bf["row_slot"].cpu().numpy(), rs)
+    np.testing.assert_array_equal(bf["inv"].cpu().numpy(), inv)
+
+    # experts, isolated on the injected h
+    print(f"[{s['name']}] experts", flush=True)
+    B.spa_moe_expert(ctx, m, lay, bf["h"], bf["ss_h"], n, route, bf["y"], ws)
+    torch.cuda.synchronize()
+    y = _f(bf["y"])
+    invn = bf["inv"].cpu().numpy()
+    ysel = np.stack([y[invn[b]] for b in toks])       # [tokens][k][H]
+    hz.assert_close_rms(ysel, rec.y, tol, "expert y")
+
+    # combine
+    print(f"[{s['name']}] combine", flush=True)
+    B.spa_moe_combine(ctx, m, bf["h"], bf["y"], route, n, bf["xo"], bf["ss_o"])
+    torch.cuda.synchronize()
+    hz.assert_close_rms(_f(bf["xo"])[toks], rec.x_next, tol, "x_next (combine)")
+    assert B.spa_workspace_errors(ctx, ws) == 0
+
+
+def test_layer_forward_matches_oracle(setup):
+    s = setup
+    B, wl, dw, ctx, toks = s["B"], s["wl"], s["dw"], s["ctx"], s["toks"]
+    dw.reset_x()
+    ws = dw.workspace(n_tok=wl.batch)
+    B.spa_layer_forward(ctx, dw.m, dw.layers_c[0], 0, dw.batch, 0, wl.batch, ws)
+    torch.cuda.synchronize()
+    hz.assert_close_rms(_f(dw.x)[toks], s["x_ref"], hz.tol_of(wl), "layer output")
+    np.testing.assert_array_equal(dw.topk[0].cpu().numpy()[toks], s["rec"].topk)
+    assert B.spa_workspace_errors(ctx, ws) == 0
