@@ -173,48 +173,52 @@ spa_status spa_kv_io(spa_ctx* ctx, const spa_model_desc* m, int32_t kind, void* 
  * Each acts on tokens [tok0, tok0 + n_tok) of the batch and uses `ws`
  * (>= spa_workspace_query(m, n_tok, max_kv_len, 1) bytes). */
 
-/* Row sum-of-squares partials of x [n_tok][H]: ss [H/64][n_tok] (the RMSNorm
- * statistic consumed by the projections). */
-spa_status spa_row_sumsq(spa_ctx* ctx, const spa_model_desc* m, const float* x, int32_t n_tok, float* ss,
-                         void* stream);
+/* RMSNorm (Figure 3 "RMSNorm"): xn = x * gamma / sqrt(mean(x^2) + eps) per
+ * row of x [n_tok][H] fp32; xn_out [n_tok][H] in dense_dtype (the
+ * projection input). */
+spa_status spa_rms_norm(spa_ctx* ctx, const spa_model_desc* m, const float* x, const float* gamma, int32_t n_tok,
+                        void* xn_out, void* stream);
 
-/* Figure 3 "RMSNorm, Q proj, KV proj": xn = RMSNorm(x) gamma1 (bf16 when
- * dense_dtype is BF16); [q | k | v] = xn Wqkv^T; q -> q_out [n_tok][Hq*D]
- * (kv_dtype), k and v -> the layer's cache at position kv_len[s] - 1. */
+/* Figure 3 "Q proj, KV proj": [q | k | v] = xn Wqkv^T from the normalised
+ * rows xn [n_tok][H] (dense_dtype); q -> q_out [n_tok][Hq*D] (kv_dtype), k and
+ * v -> the layer's cache at position kv_len[s] - 1 of sequence s = tok0 + row. */
 spa_status spa_qkv_append(spa_ctx* ctx, const spa_model_desc* m, const spa_layer* l, const spa_batch* b,
-                          int32_t tok0, int32_t n_tok, const float* ss_x, void* q_out, void* ws, size_t ws_bytes,
+                          int32_t tok0, int32_t n_tok, const void* xn, void* q_out, void* ws, size_t ws_bytes,
                           void* stream);
 
 /* Figure 3 "FMHA" (section 5.1: sliding or full): grouped-query decode
  * attention with sinks over the cached window; q [n_tok][Hq*D] and o_out
- * [n_tok][Hq*D] in kv_dtype. Split-KV over 256-position chunks. */
+ * [n_tok][Hq*D] in kv_dtype. Split-KV over 512-position chunks. */
 spa_status spa_decode_attn(spa_ctx* ctx, const spa_model_desc* m, const spa_layer* l, const spa_batch* b,
                            int32_t tok0, int32_t n_tok, const void* q, void* o_out, void* ws, size_t ws_bytes,
                            void* stream);
 
 /* Figure 3 "Output proj, Add+Norm": h = x + o Wo^T (h_out [n_tok][H] fp32)
- * and the row sum-of-squares partials of h (ss_h [H/64][n_tok]). */
+ * and hn = RMSNorm(h) gamma2 (hn_out [n_tok][H] fp32). */
 spa_status spa_out_proj(spa_ctx* ctx, const spa_model_desc* m, const spa_layer* l, const float* x, const void* o,
-                        int32_t n_tok, float* h_out, float* ss_h, void* ws, size_t ws_bytes, void* stream);
+                        int32_t n_tok, float* h_out, float* hn_out, void* ws, size_t ws_bytes, void* stream);
 
-/* Figure 3 "Router gating, TopK dispatch": hn = RMSNorm(h) gamma2 (fp32);
- * logits = hn Wr^T (fp32); top-k + softmax over the picks; permutation of
- * (token, pick) rows grouped by resident expert (pick t -> expert t % E_res),
+/* Figure 3 "Router gating, TopK dispatch": logits = hn Wr^T (fp32, hn
+ * [n_tok][H] fp32); top-k + softmax over the picks; permutation of (token,
+ * pick) rows grouped by resident expert (pick t -> expert t % E_res),
  * (token, pick) ascending inside an expert. */
-spa_status spa_moe_route(spa_ctx* ctx, const spa_model_desc* m, const spa_layer* l, const float* h,
-                         const float* ss_h, int32_t n_tok, float* logits_out, const spa_route_bufs* r,
-                         int32_t* topk_rec, void* ws, size_t ws_bytes, void* stream);
+spa_status spa_moe_route(spa_ctx* ctx, const spa_model_desc* m, const spa_layer* l, const float* hn, int32_t n_tok,
+                         float* logits_out, const spa_route_bufs* r, int32_t* topk_rec, void* ws, size_t ws_bytes,
+                         void* stream);
 
 /* Figure 3 "Expert up (BMM), SwiGLU, Expert down": for each dispatch row,
- * z = silu(hn Wg^T) * (hn Wu^T) and y = z Wd^T (y_out [n_tok*k][H] fp32). */
-spa_status spa_moe_expert(spa_ctx* ctx, const spa_model_desc* m, const spa_layer* l, const float* h,
-                          const float* ss_h, int32_t n_tok, const spa_route_bufs* r, float* y_out, void* ws,
-                          size_t ws_bytes, void* stream);
+ * with x = hn of its token in the expert input format (bf16, or per-row
+ * power-of-two-scaled E4M3): z = silu(x Wg^T) * (x Wu^T), y = z Wd^T
+ * (y_out [n_tok*k][H] fp32, dispatch row order). */
+spa_status spa_moe_expert(spa_ctx* ctx, const spa_model_desc* m, const spa_layer* l, const float* hn, int32_t n_tok,
+                          const spa_route_bufs* r, float* y_out, void* ws, size_t ws_bytes, void* stream);
 
-/* Figure 3 "Combine": x_out = h + sum over picks (in pick order) of w * y,
- * and the row sum-of-squares partials of x_out (ss_out [H/64][n_tok]). */
+/* Figure 3 "Combine": x_out = h + sum over picks (in pick order) of w * y;
+ * when gamma_next is given, also xn_out = RMSNorm(x_out) gamma_next (the next
+ * layer's projection input, dense_dtype). */
 spa_status spa_moe_combine(spa_ctx* ctx, const spa_model_desc* m, const float* h, const float* y,
-                           const spa_route_bufs* r, int32_t n_tok, float* x_out, float* ss_out, void* stream);
+                           const spa_route_bufs* r, int32_t n_tok, float* x_out, const float* gamma_next, void* xn_out,
+                           void* stream);
 
 /* One whole layer, temporal, on tokens [tok0, tok0 + n_tok): updates x in
  * place, appends K/V, optionally records the router picks. */

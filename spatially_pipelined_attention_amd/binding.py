@@ -73,17 +73,17 @@ _PROTOS = {
     "spa_workspace_init": [_P, C.POINTER(spa_model_desc), _I, _I, _I, _P, C.c_size_t, _P],
     "spa_workspace_errors": [_P, _P, C.c_size_t, _P, C.POINTER(C.c_int32)],
     "spa_kv_io": [_P, C.POINTER(spa_model_desc), _I, _P, _P, C.POINTER(spa_batch), _P, _P, _I, _P, _P, _I, _P],
-    "spa_row_sumsq": [_P, C.POINTER(spa_model_desc), _P, _I, _P, _P],
+    "spa_rms_norm": [_P, C.POINTER(spa_model_desc), _P, _P, _I, _P, _P],
     "spa_qkv_append": [_P, C.POINTER(spa_model_desc), C.POINTER(spa_layer), C.POINTER(spa_batch), _I, _I, _P, _P,
                        _P, C.c_size_t, _P],
     "spa_decode_attn": [_P, C.POINTER(spa_model_desc), C.POINTER(spa_layer), C.POINTER(spa_batch), _I, _I, _P, _P,
                         _P, C.c_size_t, _P],
     "spa_out_proj": [_P, C.POINTER(spa_model_desc), C.POINTER(spa_layer), _P, _P, _I, _P, _P, _P, C.c_size_t, _P],
-    "spa_moe_route": [_P, C.POINTER(spa_model_desc), C.POINTER(spa_layer), _P, _P, _I, _P,
+    "spa_moe_route": [_P, C.POINTER(spa_model_desc), C.POINTER(spa_layer), _P, _I, _P,
                       C.POINTER(spa_route_bufs), _P, _P, C.c_size_t, _P],
-    "spa_moe_expert": [_P, C.POINTER(spa_model_desc), C.POINTER(spa_layer), _P, _P, _I, C.POINTER(spa_route_bufs),
+    "spa_moe_expert": [_P, C.POINTER(spa_model_desc), C.POINTER(spa_layer), _P, _I, C.POINTER(spa_route_bufs),
                        _P, _P, C.c_size_t, _P],
-    "spa_moe_combine": [_P, C.POINTER(spa_model_desc), _P, _P, C.POINTER(spa_route_bufs), _I, _P, _P, _P],
+    "spa_moe_combine": [_P, C.POINTER(spa_model_desc), _P, _P, C.POINTER(spa_route_bufs), _I, _P, _P, _P, _P],
     "spa_layer_forward": [_P, C.POINTER(spa_model_desc), C.POINTER(spa_layer), _I, C.POINTER(spa_batch), _I, _I, _P,
                           C.c_size_t, _P],
     "spa_temporal_run": [_P, C.POINTER(spa_model_desc), C.POINTER(spa_layer), C.POINTER(spa_batch), _I, _P,
@@ -197,12 +197,12 @@ def _ws(ws):
     return ptr(ws), ws.numel() * ws.element_size()
 
 
-def spa_row_sumsq(ctx, m, x, n_tok, ss, stream=None):
-    _check(lib().spa_row_sumsq(ctx, C.byref(m), ptr(x), n_tok, ptr(ss), stream_handle(stream)))
+def spa_rms_norm(ctx, m, x, gamma, n_tok, xn_out, stream=None):
+    _check(lib().spa_rms_norm(ctx, C.byref(m), ptr(x), ptr(gamma), n_tok, ptr(xn_out), stream_handle(stream)))
 
 
-def spa_qkv_append(ctx, m, layer, batch, tok0, n_tok, ss_x, q_out, ws, stream=None):
-    _check(lib().spa_qkv_append(ctx, C.byref(m), C.byref(layer), C.byref(batch), tok0, n_tok, ptr(ss_x), ptr(q_out),
+def spa_qkv_append(ctx, m, layer, batch, tok0, n_tok, xn, q_out, ws, stream=None):
+    _check(lib().spa_qkv_append(ctx, C.byref(m), C.byref(layer), C.byref(batch), tok0, n_tok, ptr(xn), ptr(q_out),
                                 *_ws(ws), stream_handle(stream)))
 
 
@@ -211,24 +211,24 @@ def spa_decode_attn(ctx, m, layer, batch, tok0, n_tok, q, o_out, ws, stream=None
                                  *_ws(ws), stream_handle(stream)))
 
 
-def spa_out_proj(ctx, m, layer, x, o, n_tok, h_out, ss_h, ws, stream=None):
-    _check(lib().spa_out_proj(ctx, C.byref(m), C.byref(layer), ptr(x), ptr(o), n_tok, ptr(h_out), ptr(ss_h), *_ws(ws),
-                              stream_handle(stream)))
+def spa_out_proj(ctx, m, layer, x, o, n_tok, h_out, hn_out, ws, stream=None):
+    _check(lib().spa_out_proj(ctx, C.byref(m), C.byref(layer), ptr(x), ptr(o), n_tok, ptr(h_out), ptr(hn_out),
+                              *_ws(ws), stream_handle(stream)))
 
 
-def spa_moe_route(ctx, m, layer, h, ss_h, n_tok, logits_out, route: spa_route_bufs, topk_rec, ws, stream=None):
-    _check(lib().spa_moe_route(ctx, C.byref(m), C.byref(layer), ptr(h), ptr(ss_h), n_tok, ptr(logits_out),
-                               C.byref(route), ptr(topk_rec), *_ws(ws), stream_handle(stream)))
+def spa_moe_route(ctx, m, layer, hn, n_tok, logits_out, route: spa_route_bufs, topk_rec, ws, stream=None):
+    _check(lib().spa_moe_route(ctx, C.byref(m), C.byref(layer), ptr(hn), n_tok, ptr(logits_out), C.byref(route),
+                               ptr(topk_rec), *_ws(ws), stream_handle(stream)))
 
 
-def spa_moe_expert(ctx, m, layer, h, ss_h, n_tok, route: spa_route_bufs, y_out, ws, stream=None):
-    _check(lib().spa_moe_expert(ctx, C.byref(m), C.byref(layer), ptr(h), ptr(ss_h), n_tok, C.byref(route), ptr(y_out),
+def spa_moe_expert(ctx, m, layer, hn, n_tok, route: spa_route_bufs, y_out, ws, stream=None):
+    _check(lib().spa_moe_expert(ctx, C.byref(m), C.byref(layer), ptr(hn), n_tok, C.byref(route), ptr(y_out),
                                 *_ws(ws), stream_handle(stream)))
 
 
-def spa_moe_combine(ctx, m, h, y, route: spa_route_bufs, n_tok, x_out, ss_out, stream=None):
-    _check(lib().spa_moe_combine(ctx, C.byref(m), ptr(h), ptr(y), C.byref(route), n_tok, ptr(x_out), ptr(ss_out),
-                                 stream_handle(stream)))
+def spa_moe_combine(ctx, m, h, y, route: spa_route_bufs, n_tok, x_out, gamma_next=None, xn_out=None, stream=None):
+    _check(lib().spa_moe_combine(ctx, C.byref(m), ptr(h), ptr(y), C.byref(route), n_tok, ptr(x_out), ptr(gamma_next),
+                                 ptr(xn_out), stream_handle(stream)))
 
 
 def spa_layer_forward(ctx, m, layer, layer_index, batch, tok0, n_tok, ws, stream=None):

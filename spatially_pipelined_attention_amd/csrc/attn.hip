@@ -13,11 +13,13 @@
 //     32-position block (positions interleaved by v_slot) so the A operand is
 //     again one contiguous 16 B load, and the lane's own probabilities are
 //     exactly its B operand;
-//   * the 4 wave states merge through LDS; a chunk's (m, l, o) partial goes
-//     to workspace and the last chunk of a (sequence, KV head) to arrive
-//     (integer counter) merges all chunks in chunk order together with the
-//     sink logit: M = max(sink, m_c), Z = 2^(sink-M) + sum l_c 2^(m_c-M),
-//     o = sum o_c 2^(m_c-M) / Z.
+//   * each wave keeps two blocks of K/V in registers and always consumes the
+//     older one first, so the next block's loads stay in flight;
+//   * the 4 wave states merge through LDS; when the whole window fits one
+//     chunk the sink is applied and o written at once, otherwise the chunk's
+//     (m, l, o) partial goes to workspace and k_attn_merge combines the chunks
+//     in chunk order together with the sink logit:
+//     M = max(sink, m_c), Z = 2^(sink-M) + sum l_c 2^(m_c-M), o = sum o_c 2^(m_c-M) / Z.
 // Cache layouts (element offsets, D = 64):
 //   packed (full layers):  region(seq, g) = (kv_off[seq] * Hkv + g * cap[seq]) * D
 //   ring (sliding layers): region(seq, g) = (seq * Hkv + g) * W * D, slot = pos % W
@@ -210,9 +212,9 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
   __shared__ float s_m[4][16];
   __shared__ float s_l[4][16];
   __shared__ float s_o[4][kD][17];
-  __shared__ int s_flag;
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: scalar control flow
   const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int seq = a.tok0 + b;
   const int G = a.n_q_heads / a.n_kv_heads;
@@ -245,27 +247,35 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
     for (int cc = 0; cc < 4; ++cc) qr.q[cc] = hvalid ? ld16(qrow + (16 * cc + 4 * q4) * 4) : u32x4{0u, 0u, 0u, 0u};
   }
 
+  // this wave's blocks: blk0 + wave + 4i, i < nbw
   const int bpc = a.chunk / 32;
-  const int blk0 = c * bpc;
-  const int blk_end = min(blk0 + bpc, (loc.n_valid + 31) / 32);
+  const int blk0 = c * bpc + wave;
+  const int blk_end = min(c * bpc + bpc, (loc.n_valid + 31) / 32);
+  const int nbw = blk_end > blk0 ? (blk_end - blk0 + 3) / 4 : 0;
   float m_run = -INFINITY, l_run = 0.f;
   f32x4 acc[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const bool stream = a.stream_kv != 0;
-  int j = blk0 + wave;
-  if (j < blk_end) {
-    BlockRegs<KVT> cur, nxt;
-    load_block<KVT>(cur, kreg, vreg, j, lane, stream);
-    for (;;) {
-      const bool more = j + 4 < blk_end;
-      if (more) load_block<KVT>(nxt, kreg, vreg, j + 4, lane, stream);
-      attend_block<KVT>(cur, qr, j, loc.n_valid, a.scale_log2, m_run, l_run, acc, lane);
-      if (!more) break;
-      j += 4;
-      cur = nxt;
+  if (nbw > 0) {
+    // Two register sets; the older one is always consumed first so the
+    // other's loads stay in flight while it is used. The steady-state body is
+    // straight-line; a block index past this wave's last block is clamped for
+    // the load (a re-read of data it just loaded) and fully masked by position.
+    const int last = blk0 + 4 * (nbw - 1);
+    BlockRegs<KVT> A, B;
+    load_block<KVT>(A, kreg, vreg, blk0, lane, stream);
+    load_block<KVT>(B, kreg, vreg, min(blk0 + 4, last), lane, stream);
+    int i = 0;
+    for (; i + 2 < nbw; i += 2) {
+      attend_block<KVT>(A, qr, blk0 + 4 * i, loc.n_valid, a.scale_log2, m_run, l_run, acc, lane);
+      load_block<KVT>(A, kreg, vreg, blk0 + 4 * (i + 2), lane, stream);
+      attend_block<KVT>(B, qr, blk0 + 4 * (i + 1), loc.n_valid, a.scale_log2, m_run, l_run, acc, lane);
+      load_block<KVT>(B, kreg, vreg, min(blk0 + 4 * (i + 3), last), lane, stream);
     }
+    attend_block<KVT>(A, qr, blk0 + 4 * i, loc.n_valid, a.scale_log2, m_run, l_run, acc, lane);
+    if (i + 1 < nbw) attend_block<KVT>(B, qr, blk0 + 4 * (i + 1), loc.n_valid, a.scale_log2, m_run, l_run, acc, lane);
   }
   l_run += __shfl_xor(l_run, 16, 64);
   l_run += __shfl_xor(l_run, 32, 64);
@@ -281,90 +291,90 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
   }
   __syncthreads();
 
-  // merge the 4 waves: thread -> (head, d) pairs
+  // merge the 4 waves (fixed order); thread -> (head, d) pairs
   const int GD = G * kD;
   const long long pbase = (((long long)b * a.n_kv_heads + g) * a.max_chunks) * G * (kD + 2);
-  float mrg_o[4], mrg_m[4], mrg_l[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int idx = tid + 256 * i;
-    mrg_o[i] = 0.f;
-    mrg_m[i] = -INFINITY;
-    mrg_l[i] = 0.f;
-    if (idx < GD) {
-      const int h = idx >> 6, d = idx & 63;
-      float M = -INFINITY;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) M = fmaxf(M, s_m[w][h]);
-      float l = 0.f, o = 0.f;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const float mw = s_m[w][h];
-        const float f = mw == -INFINITY ? 0.f : exp2f(mw - M);
-        l += f * s_l[w][h];
-        o += f * s_o[w][d][h];
-      }
-      mrg_o[i] = o;
-      mrg_m[i] = M;
-      mrg_l[i] = l;
-    }
-  }
-
-  bool last = true;
-  if (n_chunks > 1) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int idx = tid + 256 * i;
-      if (idx < GD) {
-        const int h = idx >> 6, d = idx & 63;
-        float* pp = a.part + pbase + ((long long)c * G + h) * (kD + 2);
-        pp[d] = mrg_o[i];
-        if (d == 0) {
-          pp[kD] = mrg_m[i];
-          pp[kD + 1] = mrg_l[i];
-        }
-      }
-    }
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) {
-      int* ctr = a.ctr + (long long)b * a.n_kv_heads + g;
-      int old = atomicAdd(ctr, 1);
-      int l = old == n_chunks - 1;
-      if (l) atomicExch(ctr, 0);
-      s_flag = l;
-    }
-    __syncthreads();
-    last = s_flag != 0;
-    if (last) __threadfence();
-  }
-  if (!last) return;
-
-  // final merge over chunks (fixed chunk order) with the sink
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int idx = tid + 256 * i;
     if (idx >= GD) continue;
     const int h = idx >> 6, d = idx & 63;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, s_m[w][h]);
+    float l = 0.f, o = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float mw = s_m[w][h];
+      const float f = mw == -INFINITY ? 0.f : exp2f(mw - M);
+      l += f * s_l[w][h];
+      o += f * s_o[w][d][h];
+    }
+    if (n_chunks == 1) {
+      // the whole window was in this chunk: finish with the sink here
+      const int hq = g * G + h;
+      const float sink = a.sinks[hq] * kLog2e;
+      const float MM = fmaxf(M, sink);
+      const float f = M == -INFINITY ? 0.f : exp2f(M - MM);
+      const float Z = exp2f(sink - MM) + f * l;
+      const float out = f * o / Z;
+      const long long oi = ((long long)b * a.n_q_heads + hq) * kD + d;
+      if constexpr (KVT == DT_BF16) ((uint16_t*)a.o)[oi] = f32_to_bf16(out);
+      else ((float*)a.o)[oi] = out;
+    } else {
+      float* pp = a.part + pbase + ((long long)c * G + h) * (kD + 2);
+      pp[d] = o;
+      if (d == 0) {
+        pp[kD] = M;
+        pp[kD + 1] = l;
+      }
+    }
+  }
+}
+
+// Merge the chunk partials of one (sequence, KV head) in chunk order with the
+// sink: M = max(sink, m_c), Z = 2^(sink-M) + sum l_c 2^(m_c-M), o = sum o_c 2^(m_c-M) / Z.
+template <int KVT>
+__global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
+  const int g = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const int seq = a.tok0 + b;
+  const int G = a.n_q_heads / a.n_kv_heads;
+  const KvLoc loc = kv_locate(a, seq, g);
+  if (!loc.ok) return;
+  const int n_chunks = (loc.n_valid + a.chunk - 1) / a.chunk;
+  if (n_chunks <= 1 || n_chunks > a.max_chunks) return;
+  const long long pbase = (((long long)b * a.n_kv_heads + g) * a.max_chunks) * G * (kD + 2);
+  const long long cstride = (long long)G * (kD + 2);
+  constexpr int U = 16;   // chunk states loaded together (clamped, masked)
+  for (int idx = tid; idx < G * kD; idx += 256) {
+    const int h = idx >> 6, d = idx & 63;
     const int hq = g * G + h;
     const float sink = a.sinks[hq] * kLog2e;
-    float M = sink, Z, o;
-    if (n_chunks == 1) {
-      M = fmaxf(M, mrg_m[i]);
-      const float f = mrg_m[i] == -INFINITY ? 0.f : exp2f(mrg_m[i] - M);
-      Z = exp2f(sink - M) + f * mrg_l[i];
-      o = f * mrg_o[i];
-    } else {
-      const float* pp = a.part + pbase + (long long)h * (kD + 2);
-      const long long cstride = (long long)G * (kD + 2);
-      for (int cc = 0; cc < n_chunks; ++cc) M = fmaxf(M, pp[cc * cstride + kD]);
-      Z = exp2f(sink - M);
-      o = 0.f;
-      for (int cc = 0; cc < n_chunks; ++cc) {
-        const float mc = pp[cc * cstride + kD];
-        const float f = mc == -INFINITY ? 0.f : exp2f(mc - M);
-        Z += f * pp[cc * cstride + kD + 1];
-        o += f * pp[cc * cstride + d];
+    const float* pp = a.part + pbase + (long long)h * (kD + 2);
+    float M = sink;
+    for (int c0 = 0; c0 < n_chunks; c0 += U) {
+      float mv[U];
+#pragma unroll
+      for (int i = 0; i < U; ++i) mv[i] = pp[min(c0 + i, n_chunks - 1) * cstride + kD];
+#pragma unroll
+      for (int i = 0; i < U; ++i) M = fmaxf(M, mv[i]);   // clamped repeats do not change a max
+    }
+    float Z = exp2f(sink - M), o = 0.f;
+    for (int c0 = 0; c0 < n_chunks; c0 += U) {
+      float mv[U], lv[U], ov[U];
+#pragma unroll
+      for (int i = 0; i < U; ++i) {
+        const float* q = pp + min(c0 + i, n_chunks - 1) * cstride;
+        mv[i] = q[kD];
+        lv[i] = q[kD + 1];
+        ov[i] = q[d];
+      }
+#pragma unroll
+      for (int i = 0; i < U; ++i) {
+        if (c0 + i >= n_chunks) break;
+        const float f = mv[i] == -INFINITY ? 0.f : exp2f(mv[i] - M);
+        Z += f * lv[i];
+        o += f * ov[i];
       }
     }
     const float out = o / Z;
@@ -378,6 +388,13 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t st) {
   dim3 grid(a.max_chunks, a.n_kv_heads, a.n_tok);
   if (a.kv_dtype == DT_BF16) hipLaunchKernelGGL(k_attn<DT_BF16>, grid, dim3(256), 0, st, a);
   else hipLaunchKernelGGL(k_attn<DT_F32>, grid, dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_merge(const AttnArgs& a, hipStream_t st) {
+  dim3 grid(a.n_kv_heads, a.n_tok);
+  if (a.kv_dtype == DT_BF16) hipLaunchKernelGGL(k_attn_merge<DT_BF16>, grid, dim3(256), 0, st, a);
+  else hipLaunchKernelGGL(k_attn_merge<DT_F32>, grid, dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

@@ -53,6 +53,7 @@ spa_status validate_model(const spa_model_desc* m) {
   if (m->hidden % kse || m->inter % kse)
     return fail(SPA_EUNSUPPORTED, "hidden and inter must be multiples of the expert k-step");
   if (m->hidden % 16) return fail(SPA_EUNSUPPORTED, "hidden must be a multiple of 16 (router)");
+  if (m->hidden > 4096) return fail(SPA_EUNSUPPORTED, "hidden above 4096 (row kernels hold 4 columns per thread)");
   return SPA_OK;
 }
 
@@ -61,17 +62,20 @@ int max_chunks_for(int max_kv_len, const spa_model_desc* m) {
   return (l + kAttnChunk - 1) / kAttnChunk;
 }
 
+// Launch shapes depend only on tensor shapes (never on the CU pool), so a
+// microbatch computes the same bits in every schedule.
 GemmPlan plan_gemm(int kc, const spa_model_desc* m, int n_tok, int n_cus) {
   GemmPlan p{};
-  int N = 0, K = 0, groups = 1, rows = n_tok;
+  int K = 0, groups = 1, rows = n_tok;
+  p.epi = EPI_PARTIAL;
   switch (kc) {
-    case KC_QKV: N = (m->n_q_heads + 2 * m->n_kv_heads) * m->head_dim; K = m->hidden; p.ks = ks_of(m->dense_dtype);
-      p.n_tiles = N / 64; break;
-    case KC_OPROJ: N = m->hidden; K = m->n_q_heads * m->head_dim; p.ks = ks_of(m->dense_dtype); p.n_tiles = N / 64; break;
-    case KC_ROUTER: N = m->n_experts; K = m->hidden; p.ks = 16; p.n_tiles = (N + 63) / 64; break;
-    case KC_GATEUP: N = m->inter; K = m->hidden; p.ks = ks_of(m->expert_dtype); p.n_tiles = N / 32;
-      groups = m->n_resident; rows = n_tok * m->top_k; break;
-    case KC_DOWN: N = m->hidden; K = m->inter; p.ks = ks_of(m->expert_dtype); p.n_tiles = N / 64;
+    case KC_QKV: K = m->hidden; p.ks = ks_of(m->dense_dtype);
+      p.n_tiles = (m->n_q_heads + 2 * m->n_kv_heads) * m->head_dim / 64; break;
+    case KC_OPROJ: K = m->n_q_heads * m->head_dim; p.ks = ks_of(m->dense_dtype); p.n_tiles = m->hidden / 64; break;
+    case KC_ROUTER: K = m->hidden; p.ks = 16; p.n_tiles = (m->n_experts + 63) / 64; break;
+    case KC_GATEUP: K = m->hidden; p.ks = ks_of(m->expert_dtype); p.n_tiles = m->inter / 32;
+      groups = m->n_resident; rows = n_tok * m->top_k; p.epi = EPI_SWIGLU; break;
+    case KC_DOWN: K = m->inter; p.ks = ks_of(m->expert_dtype); p.n_tiles = m->hidden / 64;
       groups = m->n_resident; rows = n_tok * m->top_k; break;
     default: break;
   }
@@ -80,9 +84,21 @@ GemmPlan plan_gemm(int kc, const spa_model_desc* m, int n_tok, int n_cus) {
   const int nks = K / p.ks;
   const int target = std::max(256, (n_cus * 5) / 4);
   int S = (target + p.n_tiles * groups - 1) / (p.n_tiles * groups);
-  S = std::min(S, std::max(1, nks / 8));
+  S = std::min(S, std::max(1, nks / 16));
+  S = std::min(S, 16);   // the finish kernels sum at most 16 splits
+  if (p.epi == EPI_SWIGLU) S = 1;
   p.S = std::max(1, S);
+  if (kc == KC_DOWN && p.S == 1) p.epi = EPI_STORE;
   return p;
+}
+
+static size_t gemm_part_floats(const spa_model_desc* m, int n_tok) {
+  size_t mx = 0;
+  for (int kc : {KC_QKV, KC_OPROJ, KC_ROUTER, KC_GATEUP, KC_DOWN}) {
+    GemmPlan p = plan_gemm(kc, m, n_tok, 1024);   // S never exceeds this device-independent bound
+    if (p.epi == EPI_PARTIAL) mx = std::max(mx, (size_t)p.n_groups * p.n_tiles * p.rb_stride * p.S * 4096);
+  }
+  return mx;
 }
 
 WsLayout ws_layout(const spa_model_desc* m, int n_tok, int max_kv_len, int n_micro) {
@@ -90,40 +106,21 @@ WsLayout ws_layout(const spa_model_desc* m, int n_tok, int max_kv_len, int n_mic
   const int H = m->hidden, Hq = m->n_q_heads, Hkv = m->n_kv_heads, D = m->head_dim;
   const int G = Hq / Hkv, k = m->top_k, E = m->n_experts, Er = m->n_resident, I = m->inter;
   const int R = n_tok * k;
-  const int nbh = H / 64;
-  const size_t kv_esz = esz_of(m->kv_dtype);
-  const bool fp8 = m->expert_dtype == SPA_E4M3;
+  const size_t kv_esz = esz_of(m->kv_dtype), dn_esz = esz_of(m->dense_dtype);
+  const bool fp8 = m->expert_dtype == SPA_E4M3, ebf = m->expert_dtype == SPA_BF16;
   L.n_slots = n_micro;
   L.n_tok = n_tok;
   L.max_chunks = max_chunks_for(max_kv_len, m);
-
-  // counters of one slot
-  size_t gemm_ctr_n = 0, gemm_part_n = 0;
-  for (int kc : {KC_QKV, KC_OPROJ, KC_ROUTER, KC_GATEUP, KC_DOWN}) {
-    GemmPlan p = plan_gemm(kc, m, n_tok, 1024);   // upper bound on S for any device
-    size_t tiles = (size_t)p.n_groups * p.n_tiles * p.rb_stride;
-    gemm_ctr_n = std::max(gemm_ctr_n, tiles);
-  }
-  // partials sized for the S actually used on this device are computed at
-  // run time; reserve for the largest S any plan can give (nks / 8 bound)
-  for (int kc : {KC_QKV, KC_OPROJ, KC_ROUTER, KC_GATEUP, KC_DOWN}) {
-    GemmPlan p = plan_gemm(kc, m, n_tok, 1024);
-    if (p.S > 1) gemm_part_n = std::max(gemm_part_n, (size_t)p.n_groups * p.n_tiles * p.rb_stride * p.S * 4096);
-  }
-
   SlotLayout& s = L.s;
   size_t o = 0;
-  // --- counters first (cleared together) ---
-  s.attn_ctr = o; o = align256(o + (size_t)n_tok * Hkv * 4);
-  s.gemm_ctr = o; o = align256(o + gemm_ctr_n * 5 * 4);   // one region per GEMM class
-  s.done_ctr = o; o = align256(o + 64);
-  const size_t ctr_bytes = o;
-  // --- data ---
-  s.ss_x = o; o = align256(o + (size_t)nbh * n_tok * 4);
-  s.ss_h = o; o = align256(o + (size_t)nbh * n_tok * 4);
+  s.xn = o; o = align256(o + (size_t)n_tok * H * dn_esz);
   s.q = o; o = align256(o + (size_t)n_tok * Hq * D * kv_esz);
   s.o = o; o = align256(o + (size_t)n_tok * Hq * D * kv_esz);
   s.h = o; o = align256(o + (size_t)n_tok * H * 4);
+  s.hn_f32 = o; o = align256(o + (size_t)n_tok * H * 4);
+  s.hn_bf16 = o; o = align256(o + (ebf ? (size_t)n_tok * H * 2 : 0));
+  s.hn8 = o; o = align256(o + (fp8 ? (size_t)n_tok * H : 0));
+  s.hn8_scale = o; o = align256(o + (fp8 ? (size_t)n_tok * 4 : 0));
   s.logits = o; o = align256(o + (size_t)n_tok * E * 4);
   s.topk_idx = o; o = align256(o + (size_t)R * 4);
   s.topk_w = o; o = align256(o + (size_t)R * 4);
@@ -131,22 +128,17 @@ WsLayout ws_layout(const spa_model_desc* m, int n_tok, int max_kv_len, int n_mic
   s.row_tok = o; o = align256(o + (size_t)R * 4);
   s.row_slot = o; o = align256(o + (size_t)R * 4);
   s.inv = o; o = align256(o + (size_t)R * 4);
-  s.hq8 = o; o = align256(o + (fp8 ? (size_t)n_tok * H : 0));
-  s.hq8_scale = o; o = align256(o + (fp8 ? (size_t)n_tok * 4 : 0));
-  s.z = o; o = align256(o + (size_t)R * I * (m->expert_dtype == SPA_BF16 ? 2 : 4));
+  s.z = o; o = align256(o + (size_t)R * I * (ebf ? 2 : 4));
   s.z8 = o; o = align256(o + (fp8 ? (size_t)R * I : 0));
   s.z8_scale = o; o = align256(o + (fp8 ? (size_t)R * 4 : 0));
   s.y = o; o = align256(o + (size_t)R * H * 4);
   s.attn_part = o; o = align256(o + (size_t)n_tok * Hkv * L.max_chunks * G * (D + 2) * 4);
-  s.gemm_part = o; o = align256(o + gemm_part_n * 4);
+  s.gemm_part = o; o = align256(o + gemm_part_floats(m, n_tok) * 4);
   s.bytes = o;
-
   L.err = 0;
   L.slot0 = 256;
   L.slot_bytes = s.bytes;
   L.total = L.slot0 + (size_t)n_micro * s.bytes;
-  L.ctr_begin = 0;
-  L.ctr_end = ctr_bytes;
   return L;
 }
 
@@ -156,11 +148,14 @@ Slot slot_ptrs(const WsLayout& L, void* ws, int slot) {
   const SlotLayout& o = L.s;
   s.base = b;
   s.err = (int*)((char*)ws + L.err);
-  s.ss_x = (float*)(b + o.ss_x);
-  s.ss_h = (float*)(b + o.ss_h);
+  s.xn = b + o.xn;
   s.q = b + o.q;
   s.o = b + o.o;
   s.h = (float*)(b + o.h);
+  s.hn_f32 = (float*)(b + o.hn_f32);
+  s.hn_bf16 = (uint16_t*)(b + o.hn_bf16);
+  s.hn8 = (uint8_t*)(b + o.hn8);
+  s.hn8_scale = (float*)(b + o.hn8_scale);
   s.logits = (float*)(b + o.logits);
   s.route.topk_idx = (int32_t*)(b + o.topk_idx);
   s.route.topk_w = (float*)(b + o.topk_w);
@@ -168,49 +163,32 @@ Slot slot_ptrs(const WsLayout& L, void* ws, int slot) {
   s.route.row_tok = (int32_t*)(b + o.row_tok);
   s.route.row_slot = (int32_t*)(b + o.row_slot);
   s.route.inv = (int32_t*)(b + o.inv);
-  s.hq8 = (uint8_t*)(b + o.hq8);
-  s.hq8_scale = (float*)(b + o.hq8_scale);
   s.z = b + o.z;
   s.z8 = (uint8_t*)(b + o.z8);
   s.z8_scale = (float*)(b + o.z8_scale);
   s.y = (float*)(b + o.y);
   s.attn_part = (float*)(b + o.attn_part);
   s.gemm_part = (float*)(b + o.gemm_part);
-  s.attn_ctr = (int*)(b + o.attn_ctr);
-  s.gemm_ctr = (int*)(b + o.gemm_ctr);
-  s.done_ctr = (int*)(b + o.done_ctr);
   return s;
 }
 
-spa_status clear_counters(const WsLayout& W, void* ws, hipStream_t st) {
-  SPA_HIP(launch_fill_i32((int*)ws, 64, 0, st));   // error word + pad
-  for (int i = 0; i < W.n_slots; ++i) {
-    char* b = (char*)ws + W.slot0 + (size_t)i * W.slot_bytes;
-    SPA_HIP(launch_fill_i32((int*)(b + W.ctr_begin), (long long)((W.ctr_end - W.ctr_begin) / 4), 0, st));
-  }
+spa_status clear_errors(void* ws, hipStream_t st) {
+  SPA_HIP(launch_fill_i32((int*)ws, 64, 0, st));
   return SPA_OK;
 }
 
-static int gemm_ctr_region(int kc) {
-  switch (kc) {
-    case KC_QKV: return 0;
-    case KC_OPROJ: return 1;
-    case KC_ROUTER: return 2;
-    case KC_GATEUP: return 3;
-    default: return 4;
-  }
-}
-
 // ---------------------------------------------------------------------------
-// timing hook
+// timing hook: events around every launch of the timed kernel class
 // ---------------------------------------------------------------------------
 struct HookScope {
   TimingHook* th;
   hipStream_t st;
   bool on;
   HookScope(TimingHook* t, int cls, hipStream_t s) : th(t), st(s), on(t && t->cls == cls && t->evs && t->pool) {
-    if (on) th->evs->push_back(take());
-    if (on) (void)hipEventRecord(th->evs->back(), st);
+    if (on) {
+      th->evs->push_back(take());
+      (void)hipEventRecord(th->evs->back(), st);
+    }
   }
   hipEvent_t take() {
     if (th->pool->empty()) {
@@ -233,7 +211,7 @@ struct HookScope {
 // ---------------------------------------------------------------------------
 // operators (explicit pointers; scratch from slot s)
 // ---------------------------------------------------------------------------
-static GemmArgs gemm_base(const GemmPlan& p, const Slot& s, int kc, int n_tok, const spa_model_desc* m) {
+static GemmArgs gemm_args(const GemmPlan& p, const Slot& s, int n_tok) {
   GemmArgs a;
   memset(&a, 0, sizeof(a));
   a.n_tiles = p.n_tiles;
@@ -242,62 +220,54 @@ static GemmArgs gemm_base(const GemmPlan& p, const Slot& s, int kc, int n_tok, c
   a.rb_stride = p.rb_stride;
   a.n_rows = n_tok;
   a.part = s.gemm_part;
-  size_t region = 0;
-  {
-    // counter region per class: sized by the largest tile count of any class
-    GemmPlan worst{};
-    size_t mx = 0;
-    for (int c : {KC_QKV, KC_OPROJ, KC_ROUTER, KC_GATEUP, KC_DOWN}) {
-      worst = plan_gemm(c, m, n_tok, 1024);
-      mx = std::max(mx, (size_t)worst.n_groups * worst.n_tiles * worst.rb_stride);
-    }
-    region = mx * gemm_ctr_region(kc);
-  }
-  a.ctr = s.gemm_ctr + region;
-  a.err = s.err;
-  a.eps = m->eps;
-  a.inv_h = 1.0f / (float)m->hidden;
   return a;
 }
 
+static PartView view_of(const GemmPlan& p, const Slot& s) {
+  PartView v;
+  v.part = s.gemm_part;
+  v.S = p.S;
+  v.n_tiles = p.n_tiles;
+  v.rb_stride = p.rb_stride;
+  return v;
+}
+
+// Norm + QKV: q and the new K/V (cache append) from xn.
 static spa_status op_qkv(spa_ctx* ctx, const spa_model_desc* m, const spa_layer* l, const spa_batch* b, int tok0,
-                         int n_tok, const float* ss_x, int ss_ld, void* q_out, const Slot& s, hipStream_t st,
-                         TimingHook* th) {
-  GemmPlan p = plan_gemm(KC_QKV, m, n_tok, ctx->n_cus);
-  GemmArgs a = gemm_base(p, s, KC_QKV, n_tok, m);
+                         int n_tok, const void* xn, void* q_out, const Slot& s, hipStream_t st, TimingHook* th) {
+  const GemmPlan p = plan_gemm(KC_QKV, m, n_tok, ctx->n_cus);
+  GemmArgs a = gemm_args(p, s, n_tok);
   a.W = l->wqkv;
   a.K = m->hidden;
   a.N = (m->n_q_heads + 2 * m->n_kv_heads) * m->head_dim;
-  a.X = b->x + (size_t)tok0 * m->hidden;
+  a.X = xn;
   a.x_ld = m->hidden;
-  a.ss = ss_x;
-  a.ss_tiles = m->hidden / 64;
-  a.ss_ld = ss_ld;
-  a.gamma = l->gamma1;
-  a.out = q_out;
-  a.out_ld = m->n_q_heads * m->head_dim;
-  a.out_dtype = m->kv_dtype;
-  a.n_q_heads = m->n_q_heads;
-  a.n_kv_heads = m->n_kv_heads;
-  a.head_dim = m->head_dim;
-  a.kv_dtype = m->kv_dtype;
-  a.kv_kind = l->kind == SPA_FULL ? KV_PACKED : KV_RING;
-  a.k_cache = l->k_cache;
-  a.v_cache = l->v_cache;
-  a.kv_len = b->kv_len;
-  a.kv_off = (const long long*)b->kv_off;
-  a.kv_cap = b->kv_cap;
-  a.window = m->window;
-  a.tok0 = tok0;
+  QkvFinishArgs f;
+  memset(&f, 0, sizeof(f));
+  f.pv = view_of(p, s);
+  f.n_tok = n_tok;
+  f.n_q_heads = m->n_q_heads;
+  f.n_kv_heads = m->n_kv_heads;
+  f.head_dim = m->head_dim;
+  f.q_out = q_out;
+  f.kv_dtype = m->kv_dtype;
+  f.kv_kind = l->kind == SPA_FULL ? KV_PACKED : KV_RING;
+  f.k_cache = l->k_cache;
+  f.v_cache = l->v_cache;
+  f.kv_len = b->kv_len;
+  f.kv_off = (const long long*)b->kv_off;
+  f.kv_cap = b->kv_cap;
+  f.window = m->window;
+  f.tok0 = tok0;
+  f.err = s.err;
   HookScope hs(th, KC_QKV, st);
-  SPA_HIP(launch_gemm(m->dense_dtype, XM_NORM, EPI_QKV, a, st));
+  SPA_HIP(launch_gemm(m->dense_dtype, EPI_PARTIAL, a, st));
+  SPA_HIP(launch_qkv_finish(f, st));
   return SPA_OK;
 }
 
-static spa_status op_attn(spa_ctx* ctx, const spa_model_desc* m, const spa_layer* l, const spa_batch* b, int tok0,
-                          int n_tok, const void* q, void* o, const WsLayout& W, const Slot& s, hipStream_t st,
-                          TimingHook* th) {
-  (void)ctx;
+static AttnArgs attn_args(const spa_model_desc* m, const spa_layer* l, const spa_batch* b, int tok0, int n_tok,
+                          const void* q, void* o, const WsLayout& W, const Slot& s) {
   AttnArgs a;
   memset(&a, 0, sizeof(a));
   a.q = q;
@@ -319,93 +289,93 @@ static spa_status op_attn(spa_ctx* ctx, const spa_model_desc* m, const spa_layer
   a.chunk = kAttnChunk;
   a.max_chunks = l->kind == SPA_FULL ? W.max_chunks : (m->window + kAttnChunk - 1) / kAttnChunk;
   a.part = s.attn_part;
-  a.ctr = s.attn_ctr;
   a.o = o;
   a.err = s.err;
   a.stream_kv = 1;
+  return a;
+}
+
+static spa_status op_attn(const spa_model_desc* m, const spa_layer* l, const spa_batch* b, int tok0, int n_tok,
+                          const void* q, void* o, const WsLayout& W, const Slot& s, hipStream_t st, TimingHook* th) {
+  AttnArgs a = attn_args(m, l, b, tok0, n_tok, q, o, W, s);
   HookScope hs(th, l->kind == SPA_FULL ? KC_ATTN_FULL : KC_ATTN_SLIDING, st);
   SPA_HIP(launch_attn(a, st));
+  if (a.max_chunks > 1) SPA_HIP(launch_attn_merge(a, st));
   return SPA_OK;
 }
 
+// Output proj + Add + Norm: h = x + o Wo^T, hn = RMSNorm(h) gamma2 (fp32, and
+// the expert input format when hn_bf16 / hn8 are given).
 static spa_status op_oproj(spa_ctx* ctx, const spa_model_desc* m, const spa_layer* l, const float* x, const void* o,
-                           int n_tok, float* h, float* ss_h, int ss_ld, const Slot& s, hipStream_t st,
-                           TimingHook* th) {
-  GemmPlan p = plan_gemm(KC_OPROJ, m, n_tok, ctx->n_cus);
-  GemmArgs a = gemm_base(p, s, KC_OPROJ, n_tok, m);
+                           int n_tok, float* h, float* hn, uint16_t* hn_bf16, uint8_t* hn8, float* hn8_scale,
+                           const Slot& s, hipStream_t st, TimingHook* th) {
+  const GemmPlan p = plan_gemm(KC_OPROJ, m, n_tok, ctx->n_cus);
+  GemmArgs a = gemm_args(p, s, n_tok);
   a.W = l->wo;
   a.K = m->n_q_heads * m->head_dim;
   a.N = m->hidden;
   a.X = o;
   a.x_ld = m->n_q_heads * m->head_dim;
-  a.out = h;
-  a.out_ld = m->hidden;
-  a.resid = x;
-  a.resid_ld = m->hidden;
-  a.ss_out = ss_h;
-  a.ss_out_ld = ss_ld;
+  OprojFinishArgs f;
+  memset(&f, 0, sizeof(f));
+  f.pv = view_of(p, s);
+  f.n_tok = n_tok;
+  f.H = m->hidden;
+  f.x = x;
+  f.h_out = h;
+  f.gamma = l->gamma2;
+  f.eps = m->eps;
+  f.hn_f32 = hn;
+  f.hn_bf16 = hn_bf16;
+  f.hn_e4m3 = hn8;
+  f.hn_scale = hn8_scale;
   HookScope hs(th, KC_OPROJ, st);
-  SPA_HIP(launch_gemm(m->dense_dtype, XM_RAW, EPI_RESID_SS, a, st));
+  SPA_HIP(launch_gemm(m->dense_dtype, EPI_PARTIAL, a, st));
+  SPA_HIP(launch_oproj_finish(f, st));
   return SPA_OK;
 }
 
-static spa_status op_route(spa_ctx* ctx, const spa_model_desc* m, const spa_layer* l, const float* h,
-                           const float* ss_h, int ss_ld, int n_tok, float* logits, const spa_route_bufs& r,
-                           int32_t* topk_rec, const Slot& s, hipStream_t st, TimingHook* th) {
-  GemmPlan p = plan_gemm(KC_ROUTER, m, n_tok, ctx->n_cus);
-  GemmArgs a = gemm_base(p, s, KC_ROUTER, n_tok, m);
+static spa_status op_route(spa_ctx* ctx, const spa_model_desc* m, const spa_layer* l, const float* hn, int n_tok,
+                           float* logits, const spa_route_bufs& r, int32_t* topk_rec, const Slot& s, hipStream_t st,
+                           TimingHook* th) {
+  const GemmPlan p = plan_gemm(KC_ROUTER, m, n_tok, ctx->n_cus);
+  GemmArgs a = gemm_args(p, s, n_tok);
   a.W = l->wr;
   a.K = m->hidden;
   a.N = m->n_experts;
-  a.X = h;
+  a.X = hn;
   a.x_ld = m->hidden;
-  a.ss = ss_h;
-  a.ss_tiles = m->hidden / 64;
-  a.ss_ld = ss_ld;
-  a.gamma = l->gamma2;
-  a.out = logits;
-  a.out_ld = m->n_experts;
-  a.done_ctr = s.done_ctr;
-  a.top_k = m->top_k;
-  a.n_resident = m->n_resident;
-  a.topk_idx = r.topk_idx;
-  a.topk_w = r.topk_w;
-  a.topk_rec = topk_rec;
-  a.route_off = r.offsets;
-  a.row_tok = r.row_tok;
-  a.row_slot = r.row_slot;
-  a.inv = r.inv;
+  RouteArgs ra;
+  memset(&ra, 0, sizeof(ra));
+  ra.pv = view_of(p, s);
+  ra.n_tok = n_tok;
+  ra.E = m->n_experts;
+  ra.k = m->top_k;
+  ra.E_res = m->n_resident;
+  ra.logits = logits;
+  ra.topk_idx = r.topk_idx;
+  ra.topk_w = r.topk_w;
+  ra.topk_rec = topk_rec;
+  ra.offsets = r.offsets;
+  ra.row_tok = r.row_tok;
+  ra.row_slot = r.row_slot;
+  ra.inv = r.inv;
   HookScope hs(th, KC_ROUTER, st);
-  SPA_HIP(launch_gemm(DT_F32, XM_NORM, EPI_ROUTER, a, st));
+  SPA_HIP(launch_gemm(DT_F32, EPI_PARTIAL, a, st));
+  SPA_HIP(launch_route(ra, st));
   return SPA_OK;
 }
 
-static spa_status op_expert(spa_ctx* ctx, const spa_model_desc* m, const spa_layer* l, const float* h,
-                            const float* ss_h, int ss_ld, int n_tok, const spa_route_bufs& r, float* y, const Slot& s,
-                            hipStream_t st, TimingHook* th) {
+// Experts: gate/up + SwiGLU, then down. xe: the expert input rows per token
+// (bf16 / fp32 / E4M3 with xe_scale). Leaves y plain (S = 1) or as partials.
+static spa_status op_expert(spa_ctx* ctx, const spa_model_desc* m, const spa_layer* l, const void* xe,
+                            const float* xe_scale, int n_tok, const spa_route_bufs& r, float* y_plain, const Slot& s,
+                            hipStream_t st, TimingHook* th, GemmPlan* down_plan) {
   const int H = m->hidden, I = m->inter, R = n_tok * m->top_k;
   const bool fp8 = m->expert_dtype == SPA_E4M3;
-  if (fp8) {
-    QuantArgs qa;
-    memset(&qa, 0, sizeof(qa));
-    qa.x = h;
-    qa.x_ld = H;
-    qa.n_rows = n_tok;
-    qa.n_cols = H;
-    qa.ss = ss_h;
-    qa.ss_tiles = H / 64;
-    qa.ss_ld = ss_ld;
-    qa.gamma = l->gamma2;
-    qa.eps = m->eps;
-    qa.inv_h = 1.0f / (float)H;
-    qa.codes = s.hq8;
-    qa.scales = s.hq8_scale;
-    HookScope hs(th, KC_GATEUP, st);
-    SPA_HIP(launch_quant_e4m3(qa, st));
-  }
   {
-    GemmPlan p = plan_gemm(KC_GATEUP, m, n_tok, ctx->n_cus);
-    GemmArgs a = gemm_base(p, s, KC_GATEUP, n_tok, m);
+    const GemmPlan p = plan_gemm(KC_GATEUP, m, n_tok, ctx->n_cus);
+    GemmArgs a = gemm_args(p, s, n_tok);
     a.W = l->wgu;
     a.w_gstride = (long long)2 * I * H;
     a.w_scale = l->wgu_scale;
@@ -415,39 +385,18 @@ static spa_status op_expert(spa_ctx* ctx, const spa_model_desc* m, const spa_lay
     a.inter = I;
     a.group_off = r.offsets;
     a.row_src = r.row_tok;
+    a.X = xe;
+    a.x_ld = H;
+    a.x_scale = xe_scale;
     a.out = s.z;
     a.out_ld = I;
     a.out_dtype = m->expert_dtype == SPA_BF16 ? DT_BF16 : DT_F32;
-    if (fp8) {
-      a.X = s.hq8;
-      a.x_ld = H;
-      a.x_scale = s.hq8_scale;
-    } else {
-      a.X = h;
-      a.x_ld = H;
-      a.ss = ss_h;
-      a.ss_tiles = H / 64;
-      a.ss_ld = ss_ld;
-      a.gamma = l->gamma2;
-    }
     HookScope hs(th, KC_GATEUP, st);
-    SPA_HIP(launch_gemm(m->expert_dtype, fp8 ? XM_RAW : XM_NORM, EPI_SWIGLU, a, st));
-  }
-  if (fp8) {
-    QuantArgs qa;
-    memset(&qa, 0, sizeof(qa));
-    qa.x = (const float*)s.z;
-    qa.x_ld = I;
-    qa.n_rows = R;
-    qa.n_cols = I;
-    qa.codes = s.z8;
-    qa.scales = s.z8_scale;
-    HookScope hs(th, KC_DOWN, st);
-    SPA_HIP(launch_quant_e4m3(qa, st));
+    SPA_HIP(launch_gemm(m->expert_dtype, EPI_SWIGLU, a, st));
   }
   {
-    GemmPlan p = plan_gemm(KC_DOWN, m, n_tok, ctx->n_cus);
-    GemmArgs a = gemm_base(p, s, KC_DOWN, n_tok, m);
+    const GemmPlan p = plan_gemm(KC_DOWN, m, n_tok, ctx->n_cus);
+    GemmArgs a = gemm_args(p, s, n_tok);
     a.W = l->wd;
     a.w_gstride = (long long)H * I;
     a.w_scale = l->wd_scale;
@@ -455,92 +404,123 @@ static spa_status op_expert(spa_ctx* ctx, const spa_model_desc* m, const spa_lay
     a.K = I;
     a.N = H;
     a.group_off = r.offsets;
-    a.out = y;
+    a.out = y_plain;
     a.out_ld = H;
+    HookScope hs(th, KC_DOWN, st);
     if (fp8) {
+      CvtArgs c;
+      c.x = (const float*)s.z;
+      c.n_rows = R;
+      c.n_cols = I;
+      c.dtype = DT_E4M3;
+      c.out = s.z8;
+      c.scales = s.z8_scale;
+      SPA_HIP(launch_cvt_rows(c, st));
       a.X = s.z8;
-      a.x_ld = I;
       a.x_scale = s.z8_scale;
     } else {
       a.X = s.z;
-      a.x_ld = I;
     }
-    HookScope hs(th, KC_DOWN, st);
-    SPA_HIP(launch_gemm(m->expert_dtype, XM_RAW, EPI_STORE, a, st));
+    a.x_ld = I;
+    SPA_HIP(launch_gemm(m->expert_dtype, p.epi, a, st));
+    if (down_plan) *down_plan = p;
   }
   return SPA_OK;
 }
 
-static spa_status op_combine(const spa_model_desc* m, const float* h, const float* y, const spa_route_bufs& r,
-                             int n_tok, float* x_out, float* ss_out, int ss_ld, int k, hipStream_t st,
-                             TimingHook* th) {
+static CombineArgs combine_args(const spa_model_desc* m, const float* h, const float* y, const GemmPlan* ypart,
+                                const Slot* s, const spa_route_bufs& r, int n_tok, float* x_out,
+                                const float* gamma_next, void* xn_out) {
   CombineArgs a;
+  memset(&a, 0, sizeof(a));
   a.h = h;
   a.y = y;
+  if (!y && ypart && s) {
+    a.ypv = view_of(*ypart, *s);
+    a.y_group_off = r.offsets;
+    a.y_n_groups = m->n_resident;
+  }
   a.w = r.topk_w;
   a.inv = r.inv;
-  a.k = k;
+  a.k = (y || ypart) ? m->top_k : 0;
   a.n_tok = n_tok;
   a.H = m->hidden;
   a.x_out = x_out;
-  a.ss_out = ss_out;
-  a.ss_ld = ss_ld;
+  a.gamma_next = gamma_next;
+  a.eps = m->eps;
+  a.xn_out = xn_out;
+  a.xn_dtype = m->dense_dtype;
+  return a;
+}
+
+static spa_status op_combine(const spa_model_desc* m, const float* h, const float* y, const GemmPlan* ypart,
+                             const Slot* s, const spa_route_bufs& r, int n_tok, float* x_out, const float* gamma_next,
+                             void* xn_out, hipStream_t st, TimingHook* th) {
+  CombineArgs a = combine_args(m, h, y, ypart, s, r, n_tok, x_out, gamma_next, xn_out);
   HookScope hs(th, KC_COMBINE, st);
   SPA_HIP(launch_combine(a, st));
   return SPA_OK;
 }
 
 // ---------------------------------------------------------------------------
-// segments
+// segments of one layer on one microbatch slot
 // ---------------------------------------------------------------------------
 spa_status run_segment_a(spa_ctx* ctx, const spa_model_desc* m, const spa_layer* l, int layer_index,
-                         const spa_batch* b, int tok0, int n_tok, const WsLayout& W, const Slot& s, bool with_router,
-                         bool first_layer, hipStream_t st, TimingHook* th) {
+                         const spa_layer* next, const spa_batch* b, int tok0, int n_tok, const WsLayout& W,
+                         const Slot& s, bool with_router, bool first_layer, hipStream_t st, TimingHook* th) {
+  (void)next;
   spa_status rc;
   float* x = b->x + (size_t)tok0 * m->hidden;
-  if (first_layer) {
+  if (first_layer) {   // RMSNorm of the incoming residual rows
     spa_route_bufs none{};
-    rc = op_combine(m, x, nullptr, none, n_tok, x, s.ss_x, n_tok, 0, st, nullptr);
-    if (rc) return rc;
+    if ((rc = op_combine(m, x, nullptr, nullptr, nullptr, none, n_tok, x, l->gamma1, s.xn, st, nullptr))) return rc;
   }
-  if ((rc = op_qkv(ctx, m, l, b, tok0, n_tok, s.ss_x, n_tok, s.q, s, st, th))) return rc;
-  if ((rc = op_attn(ctx, m, l, b, tok0, n_tok, s.q, s.o, W, s, st, th))) return rc;
-  if ((rc = op_oproj(ctx, m, l, x, s.o, n_tok, s.h, s.ss_h, n_tok, s, st, th))) return rc;
+  if ((rc = op_qkv(ctx, m, l, b, tok0, n_tok, s.xn, s.q, s, st, th))) return rc;
+  if ((rc = op_attn(m, l, b, tok0, n_tok, s.q, s.o, W, s, st, th))) return rc;
+  const bool fp8 = m->expert_dtype == SPA_E4M3, ebf = m->expert_dtype == SPA_BF16;
+  if ((rc = op_oproj(ctx, m, l, x, s.o, n_tok, s.h, s.hn_f32, ebf ? s.hn_bf16 : nullptr, fp8 ? s.hn8 : nullptr,
+                     fp8 ? s.hn8_scale : nullptr, s, st, th)))
+    return rc;
   if (with_router) {
     int32_t* rec = b->topk_out ? b->topk_out + ((size_t)layer_index * b->batch + tok0) * m->top_k : nullptr;
-    if ((rc = op_route(ctx, m, l, s.h, s.ss_h, n_tok, n_tok, s.logits, s.route, rec, s, st, th))) return rc;
+    if ((rc = op_route(ctx, m, l, s.hn_f32, n_tok, s.logits, s.route, rec, s, st, th))) return rc;
   }
   return SPA_OK;
 }
 
 spa_status run_segment_b(spa_ctx* ctx, const spa_model_desc* m, const spa_layer* l, int layer_index,
-                         const spa_batch* b, int tok0, int n_tok, const WsLayout& W, const Slot& s, bool with_router,
-                         hipStream_t st, TimingHook* th) {
+                         const spa_layer* next, const spa_batch* b, int tok0, int n_tok, const WsLayout& W,
+                         const Slot& s, bool with_router, hipStream_t st, TimingHook* th) {
   (void)W;
   spa_status rc;
   float* x = b->x + (size_t)tok0 * m->hidden;
   if (!with_router) {
     int32_t* rec = b->topk_out ? b->topk_out + ((size_t)layer_index * b->batch + tok0) * m->top_k : nullptr;
-    if ((rc = op_route(ctx, m, l, s.h, s.ss_h, n_tok, n_tok, s.logits, s.route, rec, s, st, th))) return rc;
+    if ((rc = op_route(ctx, m, l, s.hn_f32, n_tok, s.logits, s.route, rec, s, st, th))) return rc;
   }
-  if ((rc = op_expert(ctx, m, l, s.h, s.ss_h, n_tok, n_tok, s.route, s.y, s, st, th))) return rc;
-  return op_combine(m, s.h, s.y, s.route, n_tok, x, s.ss_x, n_tok, m->top_k, st, th);
+  const void* xe = m->expert_dtype == SPA_BF16   ? (const void*)s.hn_bf16
+                   : m->expert_dtype == SPA_E4M3 ? (const void*)s.hn8
+                                                 : (const void*)s.hn_f32;
+  GemmPlan dp{};
+  if ((rc = op_expert(ctx, m, l, xe, s.hn8_scale, n_tok, s.route, s.y, s, st, th, &dp))) return rc;
+  const bool plain = dp.epi == EPI_STORE;
+  return op_combine(m, s.h, plain ? s.y : nullptr, plain ? nullptr : &dp, &s, s.route, n_tok, x,
+                    next ? next->gamma1 : nullptr, s.xn, st, th);
 }
 
 // ---------------------------------------------------------------------------
 // argument checks
 // ---------------------------------------------------------------------------
-static spa_status check_batch(const spa_model_desc* m, const spa_batch* b) {
+static spa_status check_batch(const spa_batch* b) {
   if (!b) return fail(SPA_EINVAL, "batch is NULL");
   if (b->batch < 1) return fail(SPA_EINVAL, "batch must be >= 1");
   if (b->max_kv_len < 1) return fail(SPA_EINVAL, "max_kv_len must be >= 1");
   if (!b->kv_len || !b->kv_off || !b->kv_cap || !b->x) return fail(SPA_EINVAL, "batch pointer is NULL");
   if (((uintptr_t)b->x) & 15) return fail(SPA_EINVAL, "x must be 16-byte aligned");
-  if (b->batch * m->top_k > 4096) return fail(SPA_EUNSUPPORTED, "batch * top_k above 4096 per call");
   return SPA_OK;
 }
 
-static spa_status check_layer(const spa_model_desc* m, const spa_layer* l) {
+spa_status check_layer(const spa_model_desc* m, const spa_layer* l) {
   if (!l) return fail(SPA_EINVAL, "layer is NULL");
   if (l->kind != SPA_FULL && l->kind != SPA_SLIDING) return fail(SPA_EINVAL, "bad layer kind");
   const void* ps[] = {l->wqkv, l->wo, l->wr, l->wgu, l->wd, l->gamma1, l->gamma2, l->sinks, l->k_cache, l->v_cache};
@@ -550,6 +530,12 @@ static spa_status check_layer(const spa_model_desc* m, const spa_layer* l) {
   }
   if (m->expert_dtype == SPA_E4M3 && (!l->wgu_scale || !l->wd_scale))
     return fail(SPA_EINVAL, "E4M3 experts need wgu_scale and wd_scale");
+  return SPA_OK;
+}
+
+spa_status check_tokens(const spa_model_desc* m, int n_tok) {
+  if (n_tok < 1) return fail(SPA_EINVAL, "n_tok must be >= 1");
+  if ((long long)n_tok * m->top_k > 4096) return fail(SPA_EUNSUPPORTED, "tokens * top_k above 4096 per microbatch");
   return SPA_OK;
 }
 
@@ -563,6 +549,8 @@ static spa_status check_ws(const spa_model_desc* m, int n_tok, int max_kv_len, i
   *out = L;
   return SPA_OK;
 }
+
+static bool misaligned(const void* p) { return ((uintptr_t)p) & 15; }
 
 }  // namespace spa
 
@@ -616,6 +604,7 @@ spa_status spa_workspace_query(const spa_model_desc* m, int32_t batch, int32_t m
   if (rc) return rc;
   if (!bytes) return fail(SPA_EINVAL, "bytes is NULL");
   if (batch < 1 || n_micro < 1 || batch % n_micro) return fail(SPA_EINVAL, "n_micro must divide batch");
+  if ((rc = check_tokens(m, batch / n_micro))) return rc;
   if (max_kv_len < 1) return fail(SPA_EINVAL, "max_kv_len must be >= 1");
   *bytes = ws_layout(m, batch / n_micro, max_kv_len, n_micro).total;
   return SPA_OK;
@@ -629,7 +618,7 @@ spa_status spa_workspace_init(spa_ctx* ctx, const spa_model_desc* m, int32_t bat
   if (batch < 1 || n_micro < 1 || batch % n_micro) return fail(SPA_EINVAL, "n_micro must divide batch");
   WsLayout L;
   if ((rc = check_ws(m, batch / n_micro, max_kv_len, n_micro, ws, ws_bytes, &L))) return rc;
-  return clear_counters(L, ws, (hipStream_t)stream);
+  return clear_errors(ws, (hipStream_t)stream);
 }
 
 spa_status spa_workspace_errors(spa_ctx* ctx, const void* ws, size_t ws_bytes, void* stream, int32_t* bits) {
@@ -658,8 +647,8 @@ spa_status spa_kv_io(spa_ctx* ctx, const spa_model_desc* m, int32_t kind, void* 
   a.v_cache = v_cache;
   a.kv_dtype = m->kv_dtype;
   a.kv_kind = kind == SPA_FULL ? KV_PACKED : KV_RING;
-  a.kv_off = b ? (const long long*)b->kv_off : nullptr;
-  a.kv_cap = b ? b->kv_cap : nullptr;
+  a.kv_off = (const long long*)b->kv_off;
+  a.kv_cap = b->kv_cap;
   a.window = m->window;
   a.n_kv_heads = m->n_kv_heads;
   a.head_dim = m->head_dim;
@@ -674,122 +663,134 @@ spa_status spa_kv_io(spa_ctx* ctx, const spa_model_desc* m, int32_t kind, void* 
   return SPA_OK;
 }
 
-spa_status spa_row_sumsq(spa_ctx* ctx, const spa_model_desc* m, const float* x, int32_t n_tok, float* ss,
-                         void* stream) {
+spa_status spa_rms_norm(spa_ctx* ctx, const spa_model_desc* m, const float* x, const float* gamma, int32_t n_tok,
+                        void* xn_out, void* stream) {
   if (!ctx) return fail(SPA_EINVAL, "ctx is NULL");
   spa_status rc = validate_model(m);
   if (rc) return rc;
-  if (!x || !ss || n_tok < 1) return fail(SPA_EINVAL, "bad argument");
-  CombineArgs a;
-  memset(&a, 0, sizeof(a));
-  a.h = x;
-  a.k = 0;
-  a.n_tok = n_tok;
-  a.H = m->hidden;
-  a.x_out = const_cast<float*>(x);   // k == 0: rewrites each element with itself
-  a.ss_out = ss;
-  a.ss_ld = n_tok;
-  SPA_HIP(launch_combine(a, (hipStream_t)stream));
-  return SPA_OK;
+  if (!x || !gamma || !xn_out || n_tok < 1) return fail(SPA_EINVAL, "bad argument");
+  spa_route_bufs none{};
+  // combine with no expert terms: x is rewritten with itself, xn = RMSNorm(x) gamma
+  return op_combine(m, x, nullptr, nullptr, nullptr, none, n_tok, const_cast<float*>(x), gamma, xn_out,
+                    (hipStream_t)stream, nullptr);
 }
 
-#define SPA_OP_PROLOGUE(n_tok_expr)                                                      \
-  if (!ctx) return fail(SPA_EINVAL, "ctx is NULL");                                      \
-  spa_status rc = validate_model(m);                                                     \
-  if (rc) return rc;                                                                     \
-  WsLayout W;                                                                            \
-  if ((rc = check_ws(m, (n_tok_expr), max_kv, 1, ws, ws_bytes, &W))) return rc;          \
-  Slot s = slot_ptrs(W, ws, 0);                                                          \
-  hipStream_t st = (hipStream_t)stream;                                                  \
-  if ((rc = clear_counters(W, ws, st))) return rc;
+#define SPA_OP_PROLOGUE(n_tok_expr)                                             \
+  if (!ctx) return fail(SPA_EINVAL, "ctx is NULL");                             \
+  spa_status rc = validate_model(m);                                            \
+  if (rc) return rc;                                                            \
+  if ((rc = check_tokens(m, (n_tok_expr)))) return rc;                          \
+  WsLayout W;                                                                   \
+  if ((rc = check_ws(m, (n_tok_expr), max_kv, 1, ws, ws_bytes, &W))) return rc; \
+  Slot s = slot_ptrs(W, ws, 0);                                                 \
+  hipStream_t st = (hipStream_t)stream;                                         \
+  if ((rc = clear_errors(ws, st))) return rc;
 
 spa_status spa_qkv_append(spa_ctx* ctx, const spa_model_desc* m, const spa_layer* l, const spa_batch* b, int32_t tok0,
-                          int32_t n_tok, const float* ss_x, void* q_out, void* ws, size_t ws_bytes, void* stream) {
+                          int32_t n_tok, const void* xn, void* q_out, void* ws, size_t ws_bytes, void* stream) {
   if (!m) return fail(SPA_EINVAL, "model is NULL");
-  spa_status rc0 = check_batch(m, b);
+  spa_status rc0 = check_batch(b);
   if (rc0) return rc0;
   if ((rc0 = check_layer(m, l))) return rc0;
   if (tok0 < 0 || n_tok < 1 || tok0 + n_tok > b->batch) return fail(SPA_EINVAL, "token range outside the batch");
-  if (!ss_x || !q_out) return fail(SPA_EINVAL, "NULL pointer");
+  if (!xn || !q_out || misaligned(xn) || misaligned(q_out)) return fail(SPA_EINVAL, "xn / q_out NULL or misaligned");
   const int max_kv = b->max_kv_len;
   SPA_OP_PROLOGUE(n_tok)
-  return op_qkv(ctx, m, l, b, tok0, n_tok, ss_x, n_tok, q_out, s, st, nullptr);
+  return op_qkv(ctx, m, l, b, tok0, n_tok, xn, q_out, s, st, nullptr);
 }
 
 spa_status spa_decode_attn(spa_ctx* ctx, const spa_model_desc* m, const spa_layer* l, const spa_batch* b, int32_t tok0,
                            int32_t n_tok, const void* q, void* o_out, void* ws, size_t ws_bytes, void* stream) {
   if (!m) return fail(SPA_EINVAL, "model is NULL");
-  spa_status rc0 = check_batch(m, b);
+  spa_status rc0 = check_batch(b);
   if (rc0) return rc0;
   if ((rc0 = check_layer(m, l))) return rc0;
   if (tok0 < 0 || n_tok < 1 || tok0 + n_tok > b->batch) return fail(SPA_EINVAL, "token range outside the batch");
-  if (!q || !o_out || (((uintptr_t)q) & 15)) return fail(SPA_EINVAL, "q / o_out NULL or misaligned");
+  if (!q || !o_out || misaligned(q)) return fail(SPA_EINVAL, "q / o_out NULL or misaligned");
   const int max_kv = b->max_kv_len;
   SPA_OP_PROLOGUE(n_tok)
-  return op_attn(ctx, m, l, b, tok0, n_tok, q, o_out, W, s, st, nullptr);
+  return op_attn(m, l, b, tok0, n_tok, q, o_out, W, s, st, nullptr);
 }
 
 spa_status spa_out_proj(spa_ctx* ctx, const spa_model_desc* m, const spa_layer* l, const float* x, const void* o,
-                        int32_t n_tok, float* h_out, float* ss_h, void* ws, size_t ws_bytes, void* stream) {
+                        int32_t n_tok, float* h_out, float* hn_out, void* ws, size_t ws_bytes, void* stream) {
   if (!m) return fail(SPA_EINVAL, "model is NULL");
   spa_status rc0 = check_layer(m, l);
   if (rc0) return rc0;
-  if (!x || !o || !h_out || !ss_h || n_tok < 1) return fail(SPA_EINVAL, "bad argument");
-  if ((((uintptr_t)x) | ((uintptr_t)o) | ((uintptr_t)h_out)) & 15) return fail(SPA_EINVAL, "misaligned tensor");
+  if (!x || !o || !h_out || !hn_out) return fail(SPA_EINVAL, "NULL pointer");
+  if (misaligned(x) || misaligned(o) || misaligned(h_out) || misaligned(hn_out)) return fail(SPA_EINVAL, "misaligned tensor");
   const int max_kv = 1;
   SPA_OP_PROLOGUE(n_tok)
-  return op_oproj(ctx, m, l, x, o, n_tok, h_out, ss_h, n_tok, s, st, nullptr);
+  return op_oproj(ctx, m, l, x, o, n_tok, h_out, hn_out, nullptr, nullptr, nullptr, s, st, nullptr);
 }
 
-spa_status spa_moe_route(spa_ctx* ctx, const spa_model_desc* m, const spa_layer* l, const float* h, const float* ss_h,
-                         int32_t n_tok, float* logits_out, const spa_route_bufs* r, int32_t* topk_rec, void* ws,
-                         size_t ws_bytes, void* stream) {
+spa_status spa_moe_route(spa_ctx* ctx, const spa_model_desc* m, const spa_layer* l, const float* hn, int32_t n_tok,
+                         float* logits_out, const spa_route_bufs* r, int32_t* topk_rec, void* ws, size_t ws_bytes,
+                         void* stream) {
   if (!m) return fail(SPA_EINVAL, "model is NULL");
   spa_status rc0 = check_layer(m, l);
   if (rc0) return rc0;
-  if (!h || !ss_h || !logits_out || !r || n_tok < 1) return fail(SPA_EINVAL, "bad argument");
+  if (!hn || !logits_out || !r || misaligned(hn)) return fail(SPA_EINVAL, "bad argument");
   if (!r->topk_idx || !r->topk_w || !r->offsets || !r->row_tok || !r->row_slot || !r->inv)
     return fail(SPA_EINVAL, "route buffer is NULL");
-  if (n_tok * m->top_k > 4096) return fail(SPA_EUNSUPPORTED, "n_tok * top_k above 4096");
   const int max_kv = 1;
   SPA_OP_PROLOGUE(n_tok)
-  return op_route(ctx, m, l, h, ss_h, n_tok, n_tok, logits_out, *r, topk_rec, s, st, nullptr);
+  return op_route(ctx, m, l, hn, n_tok, logits_out, *r, topk_rec, s, st, nullptr);
 }
 
-spa_status spa_moe_expert(spa_ctx* ctx, const spa_model_desc* m, const spa_layer* l, const float* h, const float* ss_h,
-                          int32_t n_tok, const spa_route_bufs* r, float* y_out, void* ws, size_t ws_bytes,
-                          void* stream) {
+spa_status spa_moe_expert(spa_ctx* ctx, const spa_model_desc* m, const spa_layer* l, const float* hn, int32_t n_tok,
+                          const spa_route_bufs* r, float* y_out, void* ws, size_t ws_bytes, void* stream) {
   if (!m) return fail(SPA_EINVAL, "model is NULL");
   spa_status rc0 = check_layer(m, l);
   if (rc0) return rc0;
-  if (!h || !ss_h || !r || !y_out || n_tok < 1) return fail(SPA_EINVAL, "bad argument");
+  if (!hn || !r || !y_out || misaligned(hn) || !r->offsets || !r->row_tok) return fail(SPA_EINVAL, "bad argument");
   const int max_kv = 1;
   SPA_OP_PROLOGUE(n_tok)
-  return op_expert(ctx, m, l, h, ss_h, n_tok, n_tok, *r, y_out, s, st, nullptr);
+  const void* xe = hn;
+  if (m->expert_dtype != SPA_F32) {   // the expert input format of hn
+    CvtArgs c;
+    c.x = hn;
+    c.n_rows = n_tok;
+    c.n_cols = m->hidden;
+    c.dtype = m->expert_dtype == SPA_BF16 ? DT_BF16 : DT_E4M3;
+    c.out = m->expert_dtype == SPA_BF16 ? (void*)s.hn_bf16 : (void*)s.hn8;
+    c.scales = s.hn8_scale;
+    SPA_HIP(launch_cvt_rows(c, st));
+    xe = c.out;
+  }
+  GemmPlan dp{};
+  if ((rc = op_expert(ctx, m, l, xe, s.hn8_scale, n_tok, *r, y_out, s, st, nullptr, &dp))) return rc;
+  if (dp.epi == EPI_PARTIAL) {
+    CombineArgs a = combine_args(m, nullptr, nullptr, &dp, &s, *r, n_tok, y_out, nullptr, nullptr);
+    SPA_HIP(launch_part_rows(a, n_tok * m->top_k, st));
+  }
+  return SPA_OK;
 }
 
 spa_status spa_moe_combine(spa_ctx* ctx, const spa_model_desc* m, const float* h, const float* y,
-                           const spa_route_bufs* r, int32_t n_tok, float* x_out, float* ss_out, void* stream) {
+                           const spa_route_bufs* r, int32_t n_tok, float* x_out, const float* gamma_next, void* xn_out,
+                           void* stream) {
   if (!ctx) return fail(SPA_EINVAL, "ctx is NULL");
   spa_status rc = validate_model(m);
   if (rc) return rc;
-  if (!h || !y || !r || !x_out || !ss_out || n_tok < 1) return fail(SPA_EINVAL, "bad argument");
-  return op_combine(m, h, y, *r, n_tok, x_out, ss_out, n_tok, m->top_k, (hipStream_t)stream, nullptr);
+  if (!h || !y || !r || !x_out || n_tok < 1) return fail(SPA_EINVAL, "bad argument");
+  if (gamma_next && !xn_out) return fail(SPA_EINVAL, "xn_out needed with gamma_next");
+  return op_combine(m, h, y, nullptr, nullptr, *r, n_tok, x_out, gamma_next, xn_out, (hipStream_t)stream, nullptr);
 }
 
 spa_status spa_layer_forward(spa_ctx* ctx, const spa_model_desc* m, const spa_layer* l, int32_t layer_index,
                              const spa_batch* b, int32_t tok0, int32_t n_tok, void* ws, size_t ws_bytes,
                              void* stream) {
   if (!m) return fail(SPA_EINVAL, "model is NULL");
-  spa_status rc0 = check_batch(m, b);
+  spa_status rc0 = check_batch(b);
   if (rc0) return rc0;
   if ((rc0 = check_layer(m, l))) return rc0;
   if (tok0 < 0 || n_tok < 1 || tok0 + n_tok > b->batch) return fail(SPA_EINVAL, "token range outside the batch");
   if (layer_index < 0 || layer_index >= m->n_layers) return fail(SPA_EINVAL, "layer_index out of range");
   const int max_kv = b->max_kv_len;
   SPA_OP_PROLOGUE(n_tok)
-  if ((rc = run_segment_a(ctx, m, l, layer_index, b, tok0, n_tok, W, s, false, true, st, nullptr))) return rc;
-  return run_segment_b(ctx, m, l, layer_index, b, tok0, n_tok, W, s, false, st, nullptr);
+  if ((rc = run_segment_a(ctx, m, l, layer_index, nullptr, b, tok0, n_tok, W, s, false, true, st, nullptr))) return rc;
+  return run_segment_b(ctx, m, l, layer_index, nullptr, b, tok0, n_tok, W, s, false, st, nullptr);
 }
 
 spa_status spa_temporal_run(spa_ctx* ctx, const spa_model_desc* m, const spa_layer* layers, const spa_batch* b,
@@ -797,22 +798,25 @@ spa_status spa_temporal_run(spa_ctx* ctx, const spa_model_desc* m, const spa_lay
   if (!ctx) return fail(SPA_EINVAL, "ctx is NULL");
   spa_status rc = validate_model(m);
   if (rc) return rc;
-  if ((rc = check_batch(m, b))) return rc;
+  if ((rc = check_batch(b))) return rc;
   if (!layers) return fail(SPA_EINVAL, "layers is NULL");
   for (int i = 0; i < m->n_layers; ++i)
     if ((rc = check_layer(m, &layers[i]))) return rc;
   if (n_micro < 1 || b->batch % n_micro) return fail(SPA_EINVAL, "n_micro must divide the batch");
   const int bm = b->batch / n_micro;
+  if ((rc = check_tokens(m, bm))) return rc;
   WsLayout W;
   if ((rc = check_ws(m, bm, b->max_kv_len, n_micro, ws, ws_bytes, &W))) return rc;
   hipStream_t st = (hipStream_t)stream;
-  if ((rc = clear_counters(W, ws, st))) return rc;
+  if ((rc = clear_errors(ws, st))) return rc;
   // the pipeline's dispatch order (layer, then microbatch), serialised on one stream
   for (int li = 0; li < m->n_layers; ++li) {
+    const spa_layer* next = li + 1 < m->n_layers ? &layers[li + 1] : nullptr;
     for (int mu = 0; mu < n_micro; ++mu) {
       Slot s = slot_ptrs(W, ws, mu);
-      if ((rc = run_segment_a(ctx, m, &layers[li], li, b, mu * bm, bm, W, s, false, li == 0, st, nullptr))) return rc;
-      if ((rc = run_segment_b(ctx, m, &layers[li], li, b, mu * bm, bm, W, s, false, st, nullptr))) return rc;
+      if ((rc = run_segment_a(ctx, m, &layers[li], li, next, b, mu * bm, bm, W, s, false, li == 0, st, nullptr)))
+        return rc;
+      if ((rc = run_segment_b(ctx, m, &layers[li], li, next, b, mu * bm, bm, W, s, false, st, nullptr))) return rc;
     }
   }
   return SPA_OK;

@@ -34,14 +34,13 @@ enum KClass : int {
   KC_ROUTER = 4, KC_GATEUP = 5, KC_DOWN = 6, KC_COMBINE = 7, KC_COUNT = 8
 };
 
-constexpr int kAttnChunk = 256;
+constexpr int kAttnChunk = 512;
 
 // Byte layout of one microbatch slot of the workspace.
 struct SlotLayout {
-  size_t ss_x, ss_h, q, o, h, logits;
+  size_t xn, q, o, h, hn_f32, hn_bf16, hn8, hn8_scale, logits;
   size_t topk_idx, topk_w, offsets, row_tok, row_slot, inv;
-  size_t hq8, hq8_scale, z, z8, z8_scale, y;
-  size_t attn_part, gemm_part, attn_ctr, gemm_ctr, done_ctr;
+  size_t z, z8, z8_scale, y, attn_part, gemm_part;
   size_t bytes;
 };
 
@@ -54,12 +53,10 @@ struct WsLayout {
   int max_chunks;
   size_t total;
   SlotLayout s;
-  // counters region of a slot (relative), cleared on init
-  size_t ctr_begin, ctr_end;
 };
 
 struct GemmPlan {
-  int n_tiles, n_groups, S, rb_stride, ks;
+  int n_tiles, n_groups, S, rb_stride, ks, epi;
 };
 
 spa_status validate_model(const spa_model_desc* m);
@@ -71,24 +68,22 @@ GemmPlan plan_gemm(int kclass, const spa_model_desc* m, int n_tok, int n_cus);
 struct Slot {
   char* base;
   int* err;
-  float* ss_x;
-  float* ss_h;
+  void* xn;
   void* q;
   void* o;
   float* h;
+  float* hn_f32;
+  uint16_t* hn_bf16;
+  uint8_t* hn8;
+  float* hn8_scale;
   float* logits;
   spa_route_bufs route;
-  uint8_t* hq8;
-  float* hq8_scale;
   void* z;
   uint8_t* z8;
   float* z8_scale;
   float* y;
   float* attn_part;
   float* gemm_part;
-  int* attn_ctr;
-  int* gemm_ctr;
-  int* done_ctr;
 };
 
 Slot slot_ptrs(const WsLayout& L, void* ws, int slot);
@@ -102,11 +97,11 @@ struct TimingHook {
 
 // The layer's pieces on one slot (tokens [tok0, tok0+n_tok)); enqueue on st.
 spa_status run_segment_a(spa_ctx* ctx, const spa_model_desc* m, const spa_layer* l, int layer_index,
-                         const spa_batch* b, int tok0, int n_tok, const WsLayout& W, const Slot& s, bool with_router,
-                         bool first_layer, hipStream_t st, TimingHook* th);
+                         const spa_layer* next, const spa_batch* b, int tok0, int n_tok, const WsLayout& W,
+                         const Slot& s, bool with_router, bool first_layer, hipStream_t st, TimingHook* th);
 spa_status run_segment_b(spa_ctx* ctx, const spa_model_desc* m, const spa_layer* l, int layer_index,
-                         const spa_batch* b, int tok0, int n_tok, const WsLayout& W, const Slot& s, bool with_router,
-                         hipStream_t st, TimingHook* th);
-spa_status clear_counters(const WsLayout& W, void* ws, hipStream_t st);
+                         const spa_layer* next, const spa_batch* b, int tok0, int n_tok, const WsLayout& W,
+                         const Slot& s, bool with_router, hipStream_t st, TimingHook* th);
+spa_status clear_errors(void* ws, hipStream_t st);
 
 }  // namespace spa

@@ -8,54 +8,55 @@ namespace spa {
 // Storage type codes shared with the C ABI (spa_dtype).
 enum : int { DT_F32 = 0, DT_BF16 = 1, DT_E4M3 = 2 };
 
-enum XMode : int { XM_RAW = 0, XM_NORM = 1 };
-enum Epi : int { EPI_QKV = 0, EPI_RESID_SS = 1, EPI_SWIGLU = 2, EPI_STORE = 3, EPI_ROUTER = 4 };
+enum Epi : int { EPI_PARTIAL = 0, EPI_SWIGLU = 1, EPI_STORE = 2 };
 enum KvKind : int { KV_RING = 0, KV_PACKED = 1 };
 
 // device-side error bits (workspace error word)
-enum : int { ERR_KV_LEN = 1, ERR_ROUTE = 2 };
+enum : int { ERR_KV_LEN = 1 };
+
+// Split-K partial tiles: fp32 [tile][split][64 rows][64 cols], tile =
+// (group * n_tiles + column tile) * rb_stride + row block.
+struct PartView {
+  const float* part;
+  int S;
+  int n_tiles;
+  int rb_stride;
+};
 
 struct GemmArgs {
-  // weights: group g's matrix starts at W + g * w_gstride elements, rows of K
-  const void* W;
+  const void* W;            // group g's matrix at W + g * w_gstride elements, [rows][K]
   long long w_gstride;
   int K;
   int N;                    // output columns (SwiGLU: inter)
   const float* w_scale;     // E4M3: per W row scale, group stride ws_gstride
   long long ws_gstride;
-  int n_tiles;              // 64-wide output column tiles
+  int n_tiles;              // 64-wide output column tiles (SwiGLU: 32 gate + 32 up)
   int n_groups;
   const int* group_off;     // [n_groups+1] or null (one group of n_rows)
   int n_rows;
   int S;                    // split-K factor
-  // X
-  const void* X;
+  const void* X;            // [rows][x_ld] in the weight's MFMA input type
   int x_ld;
   const int* row_src;       // X row of each output row (null: identity)
-  const float* ss;          // row sum-of-squares partials [ss_tiles][ss_ld]
-  int ss_tiles;
-  int ss_ld;
-  const float* gamma;
-  float eps;
-  float inv_h;
   const float* x_scale;     // E4M3 X: per X row scale
-  // split-K workspace
-  float* part;
-  int* ctr;
+  float* part;              // EPI_PARTIAL output
   int rb_stride;
-  // outputs
-  void* out;
+  void* out;                // EPI_SWIGLU / EPI_STORE output
   int out_ld;
   int out_dtype;
-  const float* resid;
-  int resid_ld;
-  float* ss_out;
-  int ss_out_ld;
   int inter;
-  // QKV epilogue
+};
+
+hipError_t launch_gemm(int wt, int epi, const GemmArgs& a, hipStream_t st);
+
+// q + KV append from the QKV partials, one workgroup per token row.
+struct QkvFinishArgs {
+  PartView pv;
+  int n_tok;
   int n_q_heads;
   int n_kv_heads;
   int head_dim;
+  void* q_out;              // [n_tok][Hq*D], kv dtype
   int kv_dtype;
   int kv_kind;
   void* k_cache;
@@ -66,23 +67,70 @@ struct GemmArgs {
   int window;
   int tok0;
   int* err;
-  // router epilogue
-  int* done_ctr;
-  int top_k;
-  int n_resident;
+};
+hipError_t launch_qkv_finish(const QkvFinishArgs& a, hipStream_t st);
+
+// h = x + o Wo^T (from partials); hn = RMSNorm(h) * gamma in fp32, bf16 and
+// optionally per-row power-of-two-scaled E4M3.
+struct OprojFinishArgs {
+  PartView pv;
+  int n_tok;
+  int H;
+  const float* x;
+  float* h_out;
+  const float* gamma;
+  float eps;
+  float* hn_f32;
+  uint16_t* hn_bf16;        // optional
+  uint8_t* hn_e4m3;         // optional
+  float* hn_scale;
+};
+hipError_t launch_oproj_finish(const OprojFinishArgs& a, hipStream_t st);
+
+// Router logits (from partials) -> top-k -> softmax weights -> permutation. One workgroup.
+struct RouteArgs {
+  PartView pv;
+  int n_tok;
+  int E;
+  int k;
+  int E_res;
+  float* logits;            // [n_tok][E]
   int* topk_idx;
   float* topk_w;
-  int* topk_rec;
-  int* route_off;
+  int* topk_rec;            // optional
+  int* offsets;
   int* row_tok;
   int* row_slot;
   int* inv;
 };
+hipError_t launch_route(const RouteArgs& a, hipStream_t st);
 
-hipError_t launch_gemm(int wt, int xm, int epi, const GemmArgs& a, hipStream_t st);
+// x_out = h + sum_s w[s] * y[inv[s]]; optionally xn = RMSNorm(x_out) * gamma
+// for the next projection. y is plain [R][H] or split partials of the
+// expert-down product (rows grouped by expert with group offsets).
+struct CombineArgs {
+  const float* h;
+  const float* y;           // plain y (or null)
+  PartView ypv;             // partial y when y == null
+  const int* y_group_off;
+  int y_n_groups;
+  const float* w;
+  const int* inv;
+  int k;
+  int n_tok;
+  int H;
+  float* x_out;
+  const float* gamma_next;  // null: no normalised output
+  float eps;
+  void* xn_out;
+  int xn_dtype;
+};
+hipError_t launch_combine(const CombineArgs& a, hipStream_t st);
+// out (a.x_out)[r] = split sum of dispatch row r of the grouped partial y (a.ypv)
+hipError_t launch_part_rows(const CombineArgs& a, int max_rows, hipStream_t st);
 
 struct AttnArgs {
-  const void* q;            // [n_tok][Hq][D] (bf16 or f32 = kv dtype)
+  const void* q;            // [n_tok][Hq][D] (kv dtype)
   const void* k_cache;
   const void* v_cache;
   int kv_dtype;
@@ -101,48 +149,24 @@ struct AttnArgs {
   int chunk;                // positions per workgroup (multiple of 128)
   int max_chunks;
   float* part;              // [n_tok][Hkv][max_chunks][G][D+2]
-  int* ctr;                 // [n_tok][Hkv]
-  void* o;                  // [n_tok][Hq*D] (bf16 or f32 = kv dtype)
+  void* o;                  // [n_tok][Hq*D] (kv dtype)
   int* err;
   int stream_kv;            // non-temporal KV loads
 };
-
 hipError_t launch_attn(const AttnArgs& a, hipStream_t st);
+// merge of the chunk partials of multi-chunk sequences (single-chunk ones are final already)
+hipError_t launch_attn_merge(const AttnArgs& a, hipStream_t st);
 
-struct CombineArgs {
-  const float* h;           // [n_tok][H]
-  const float* y;           // [R][H] expert outputs (rows in dispatch order)
-  const float* w;           // [n_tok][k]
-  const int* inv;           // [n_tok][k]
-  int k;
-  int n_tok;
-  int H;
-  float* x_out;             // [n_tok][H]
-  float* ss_out;            // [H/64][ss_ld]
-  int ss_ld;
-};
-
-hipError_t launch_combine(const CombineArgs& a, hipStream_t st);
-
-// rows of an fp32 matrix -> (x * rstd * gamma) quantised to per-row power-of-two-scaled E4M3
-struct QuantArgs {
+// fp32 rows -> bf16 rows or per-row power-of-two-scaled E4M3 (expert inputs)
+struct CvtArgs {
   const float* x;
-  int x_ld;
   int n_rows;
   int n_cols;
-  const int* row_src;       // optional gather
-  const int* n_rows_dev;    // optional device row count (<= n_rows)
-  const float* ss;          // optional RMSNorm (with gamma); null: plain rows
-  int ss_tiles;
-  int ss_ld;
-  const float* gamma;
-  float eps;
-  float inv_h;
-  uint8_t* codes;           // [n_rows][n_cols]
-  float* scales;            // [n_rows]
+  int dtype;                // DT_BF16 or DT_E4M3
+  void* out;
+  float* scales;            // E4M3
 };
-
-hipError_t launch_quant_e4m3(const QuantArgs& a, hipStream_t st);
+hipError_t launch_cvt_rows(const CvtArgs& a, hipStream_t st);
 
 hipError_t launch_fill_i32(int* p, long long n, int v, hipStream_t st);
 
@@ -164,7 +188,6 @@ struct KvIoArgs {
   void* v_rows;
   int write;                // 1: rows -> cache, 0: cache -> rows
 };
-
 hipError_t launch_kv_io(const KvIoArgs& a, hipStream_t st);
 
 // hardware placement probe: each workgroup records its XCC / SE / CU ids

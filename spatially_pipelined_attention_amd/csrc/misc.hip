@@ -1,88 +1,397 @@
-// Small kernels of the decode layer on gfx950: the MoE combine + residual
-// (Figure 3 "Combine" of the SubGPU Pipelining paper) with the row
-// sum-of-squares the next RMSNorm needs, per-row fp8 activation quantisation,
-// KV cache row I/O, counter clears and a CU placement probe.
+// Row-wise kernels of the decode layer on gfx950 (Figure 3 of the SubGPU
+// Pipelining paper): they finish the split products, one workgroup per token
+// row, and fuse the light operators that need whole rows:
+//   k_qkv_finish   - sum of the QKV splits -> q, and the new K/V written into
+//                    the cache slot of position L-1 ("KV proj" + append);
+//   k_oproj_finish - residual add of the output projection ("Add+Norm"), the
+//                    RMSNorm statistic, and the normalised row in fp32 (router
+//                    input), bf16 and power-of-two-scaled E4M3 (expert input);
+//   k_route_topk   - router logits, top-k in logit order (ties to the lower
+//                    index) and softmax over the picks, one wave per token;
+//   k_route_permute- the dispatch permutation (counts, offsets, rows grouped
+//                    by expert with (token, pick) ascending inside, inverse);
+//   k_combine      - "Combine": weighted sum of the expert outputs in pick
+//                    order plus residual, and the next layer's RMSNorm;
+// plus row conversion, KV row I/O, counter fill and a CU placement probe.
+// Every reduction runs in a fixed order, so results never depend on timing.
 #include "common.h"
 #include "kernels.h"
 
 namespace spa {
 
-// x_out[t] = h[t] + sum_{s < k} w[t][s] * y[inv[t][s]] (pick order, fp32);
-// ss_out[tile][t] = sum over the tile's 64 columns of x_out^2.
-// One wave per (token, 64-column tile); lane = column.
-__global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int n_tiles = a.H >> 6;
-  const int tile = blockIdx.x * 4 + wave;
-  const int t = blockIdx.y;
-  if (tile >= n_tiles) return;
-  const int col = tile * 64 + lane;
-  float v = a.h[(long long)t * a.H + col];
-  for (int s = 0; s < a.k; ++s) {
-    const float w = a.w[t * a.k + s];
-    const int row = a.inv[t * a.k + s];
-    v += w * a.y[(long long)row * a.H + col];
+constexpr int kRowThreads = 1024;   // row kernels: one workgroup per token row
+constexpr int kRowCols = 4;         // columns per thread: rows up to 4096 wide
+
+// Deterministic sum / max over a kRowThreads workgroup (fixed tree order).
+__device__ __forceinline__ float block_sum(float v, float* red) {
+  v = wave_sum(v);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  float t = 0.f;
+#pragma unroll
+  for (int w = 0; w < kRowThreads / 64; ++w) t += red[w];
+  return t;
+}
+
+__device__ __forceinline__ float block_max(float v, float* red) {
+  v = wave_max(v);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  float t = red[0];
+#pragma unroll
+  for (int w = 1; w < kRowThreads / 64; ++w) t = fmaxf(t, red[w]);
+  return t;
+}
+
+constexpr int kMaxSplits = 16;   // plan_gemm never splits k more than this
+
+// Element (row r, column c) of a split product, summed over the splits in
+// split order. All loads are issued before the first add (clamped index,
+// masked value: adding +0 leaves every partial sum unchanged).
+__device__ __forceinline__ float part_sum(const PartView& pv, int grp, int r, int c) {
+  const long long tile = ((long long)grp * pv.n_tiles + (c >> 6)) * pv.rb_stride + (r >> 6);
+  const float* p = pv.part + tile * pv.S * 4096 + (r & 63) * 64 + (c & 63);
+  float v[kMaxSplits];
+#pragma unroll
+  for (int s = 0; s < kMaxSplits; ++s) v[s] = p[min(s, pv.S - 1) * 4096];
+  float acc = v[0];
+#pragma unroll
+  for (int s = 1; s < kMaxSplits; ++s) acc += s < pv.S ? v[s] : 0.f;
+  return acc;
+}
+
+// smallest power of two s with amax <= 448 s (1 for amax == 0)
+__device__ __forceinline__ float pow2_scale_448(float amax) {
+  if (!(amax > 0.f)) return 1.f;
+  int e;
+  frexpf(amax / 448.0f, &e);   // amax/448 in [2^(e-1), 2^e)
+  float s = ldexpf(1.f, e);
+  if (amax <= 448.0f * ldexpf(1.f, e - 1)) s = ldexpf(1.f, e - 1);
+  if (amax > 448.0f * s) s *= 2.f;
+  return s;
+}
+
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_qkv_finish(QkvFinishArgs a) {
+  const int r = blockIdx.x;
+  const int c = blockIdx.y * 256 + threadIdx.x;
+  const int seq = a.tok0 + r;
+  const int D = a.head_dim, Hq = a.n_q_heads, Hkv = a.n_kv_heads;
+  const int QD = Hq * D, N = (Hq + 2 * Hkv) * D;
+  if (c >= N) return;
+  const int L = a.kv_len[seq];
+  const int pos = L - 1;
+  const bool ok = (L >= 1) && (a.kv_kind == KV_RING || L <= a.kv_cap[seq]);
+  if (!ok && c == 0 && a.err) atomicOr(a.err, ERR_KV_LEN);
+  const float v = part_sum(a.pv, 0, r, c);
+  if (c < QD) {
+    if (a.kv_dtype == DT_BF16) ((uint16_t*)a.q_out)[(long long)r * QD + c] = f32_to_bf16(v);
+    else ((float*)a.q_out)[(long long)r * QD + c] = v;
+    return;
   }
-  a.x_out[(long long)t * a.H + col] = v;
-  const float ss = wave_sum(v * v);
-  if (lane == 0) a.ss_out[(long long)tile * a.ss_ld + t] = ss;
+  if (!ok) return;
+  const bool is_k = c < QD + Hkv * D;
+  const int g = (is_k ? c - QD : c - QD - Hkv * D) / D, d = c % D;
+  long long base;
+  int slot;
+  if (a.kv_kind == KV_RING) {
+    base = ((long long)seq * Hkv + g) * a.window * D;
+    slot = pos % a.window;
+  } else {
+    base = (a.kv_off[seq] * Hkv + (long long)g * a.kv_cap[seq]) * D;
+    slot = pos;
+  }
+  const long long off = is_k ? base + (long long)slot * D + d
+                             : base + (long long)(slot >> 5) * 32 * D + (long long)d * 32 + v_slot(slot & 31);
+  void* cache = is_k ? a.k_cache : a.v_cache;
+  if (a.kv_dtype == DT_BF16) ((uint16_t*)cache)[off] = f32_to_bf16(v);
+  else ((float*)cache)[off] = v;
+}
+
+hipError_t launch_qkv_finish(const QkvFinishArgs& a, hipStream_t st) {
+  const int N = (a.n_q_heads + 2 * a.n_kv_heads) * a.head_dim;
+  hipLaunchKernelGGL(k_qkv_finish, dim3(a.n_tok, (N + 255) / 256), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kRowThreads) void k_oproj_finish(OprojFinishArgs a) {
+  __shared__ float red[kRowThreads / 64];
+  const int r = blockIdx.x;
+  const long long row = (long long)r * a.H;
+  float h[kRowCols];
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < kRowCols; ++i) {
+    const int c = threadIdx.x + kRowThreads * i;
+    h[i] = 0.f;
+    if (c < a.H) {
+      h[i] = a.x[row + c] + part_sum(a.pv, 0, r, c);
+      a.h_out[row + c] = h[i];
+    }
+    ss += h[i] * h[i];
+  }
+  ss = block_sum(ss, red);
+  const float rstd = 1.0f / sqrtf(ss / (float)a.H + a.eps);
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < kRowCols; ++i) {
+    const int c = threadIdx.x + kRowThreads * i;
+    if (c < a.H) {
+      h[i] = h[i] * rstd * a.gamma[c];
+      a.hn_f32[row + c] = h[i];
+      if (a.hn_bf16) a.hn_bf16[row + c] = f32_to_bf16(h[i]);
+      amax = fmaxf(amax, fabsf(h[i]));
+    }
+  }
+  if (a.hn_e4m3) {
+    amax = block_max(amax, red);
+    const float s = pow2_scale_448(amax);
+    const float inv_s = 1.0f / s;   // exact: power of two
+    if (threadIdx.x == 0) a.hn_scale[r] = s;
+#pragma unroll
+    for (int i = 0; i < kRowCols; ++i) {
+      const int c = threadIdx.x + kRowThreads * i;
+      if (c < a.H) a.hn_e4m3[row + c] = f32_to_e4m3(h[i] * inv_s);
+    }
+  }
+}
+
+hipError_t launch_oproj_finish(const OprojFinishArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL(k_oproj_finish, dim3(a.n_tok), dim3(kRowThreads), 0, st, a);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Router top-k: one wave per token. Lanes hold the logits of experts
+// lane + 64 j (summed over the splits in split order); k rounds of a wave
+// argmax on (value, index) - larger value wins, equal values go to the lower
+// index - then the softmax over the k picked logits.
+__global__ __launch_bounds__(256) void k_route_topk(RouteArgs a) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + wave;
+  if (t >= a.n_tok) return;
+  const int E = a.E, k = a.k;
+  float v[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int e = lane + 64 * j;
+    v[j] = -INFINITY;
+    if (e < E) {
+      v[j] = part_sum(a.pv, 0, t, e);
+      a.logits[(long long)t * E + e] = v[j];
+    }
+  }
+  float pv[8];
+  int pi[8];
+  for (int p = 0; p < k; ++p) {
+    float bv = v[0];
+    int bi = lane;
+#pragma unroll
+    for (int j = 1; j < 4; ++j)
+      if (v[j] > bv) {
+        bv = v[j];
+        bi = lane + 64 * j;
+      }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const float ov = __shfl_xor(bv, o, 64);
+      const int oi = __shfl_xor(bi, o, 64);
+      if (ov > bv || (ov == bv && oi < bi)) {
+        bv = ov;
+        bi = oi;
+      }
+    }
+    pv[p] = bv;
+    pi[p] = bi;
+    if ((bi & 63) == lane) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (j == (bi >> 6)) v[j] = -INFINITY;
+    }
+  }
+  if (lane == 0) {
+    float den = 0.f;
+    for (int p = 0; p < k; ++p) den += __expf(pv[p] - pv[0]);
+    for (int p = 0; p < k; ++p) {
+      a.topk_idx[t * k + p] = pi[p];
+      a.topk_w[t * k + p] = __expf(pv[p] - pv[0]) / den;
+      if (a.topk_rec) a.topk_rec[t * k + p] = pi[p];
+    }
+  }
+}
+
+// Dispatch permutation of the picks (pick p = token * k + slot runs on
+// resident expert topk_idx[p] % E_res): counts, exclusive offsets, rows grouped
+// by expert with (token, slot) ascending inside, and the inverse map. Ranks
+// come from per-expert bitmasks over the picks, so no order depends on timing.
+__global__ __launch_bounds__(256) void k_route_permute(RouteArgs a) {
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  const int tid = threadIdx.x;
+  const int k = a.k, P = a.n_tok * k, E_res = a.E_res;
+  int* grp = (int*)lds;                         // [P]
+  int* counts = grp + P;                        // [E_res]
+  int* offs = counts + E_res;                   // [E_res + 1]
+  const int W64 = (P + 63) >> 6;
+  unsigned long long* masks = (unsigned long long*)(((uintptr_t)(offs + E_res + 1) + 7) & ~(uintptr_t)7);
+  for (int p = tid; p < P; p += 256) grp[p] = a.topk_idx[p] % E_res;
+  for (int i = tid; i < E_res; i += 256) counts[i] = 0;
+  for (int i = tid; i < E_res * W64; i += 256) masks[i] = 0ull;
+  __syncthreads();
+  for (int p = tid; p < P; p += 256) {
+    const int g = grp[p];
+    atomicAdd(&counts[g], 1);
+    atomicOr(&masks[g * W64 + (p >> 6)], 1ull << (p & 63));
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int s = 0;
+    for (int g = 0; g < E_res; ++g) {
+      offs[g] = s;
+      s += counts[g];
+    }
+    offs[E_res] = s;
+  }
+  __syncthreads();
+  for (int i = tid; i <= E_res; i += 256) a.offsets[i] = offs[i];
+  for (int p = tid; p < P; p += 256) {
+    const int g = grp[p];
+    const unsigned long long* mk = masks + g * W64;
+    int rank = 0;
+    for (int w = 0; w < (p >> 6); ++w) rank += __popcll(mk[w]);
+    rank += __popcll(mk[p >> 6] & ((1ull << (p & 63)) - 1ull));
+    const int row = offs[g] + rank;
+    a.row_tok[row] = p / k;
+    a.row_slot[row] = p % k;
+    a.inv[p] = row;
+  }
+}
+
+int route_lds_bytes(int n_tok, int k, int E_res) {
+  const int P = n_tok * k;
+  return (P + 2 * E_res + 1) * 4 + 16 + E_res * ((P + 63) / 64) * 8;
+}
+
+hipError_t launch_route(const RouteArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL(k_route_topk, dim3((a.n_tok + 3) / 4), dim3(256), 0, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_route_permute, dim3(1), dim3(256), route_lds_bytes(a.n_tok, a.k, a.E_res), st, a);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// expert group of dispatch row `row` (largest g with group_off[g] <= row)
+__device__ __forceinline__ int group_of(const int* off, int n_groups, int row) {
+  int lo = 0, hi = n_groups - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (off[mid] <= row) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
+}
+
+__device__ __forceinline__ float y_elem(const CombineArgs& a, int row, int c) {
+  if (a.y) return a.y[(long long)row * a.H + c];
+  const int g = group_of(a.y_group_off, a.y_n_groups, row);
+  return part_sum(a.ypv, g, row - a.y_group_off[g], c);
+}
+
+__global__ __launch_bounds__(kRowThreads) void k_combine(CombineArgs a) {
+  __shared__ float red[kRowThreads / 64];
+  __shared__ float s_w[8];
+  __shared__ int s_row[8], s_grp[8];
+  const int t = blockIdx.x;
+  const long long row = (long long)t * a.H;
+  if (threadIdx.x < a.k) {
+    const int r = a.inv[t * a.k + threadIdx.x];
+    s_w[threadIdx.x] = a.w[t * a.k + threadIdx.x];
+    s_row[threadIdx.x] = r;
+    s_grp[threadIdx.x] = a.y ? 0 : group_of(a.y_group_off, a.y_n_groups, r);
+  }
+  __syncthreads();
+  float v[kRowCols];
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < kRowCols; ++i) {
+    const int c = threadIdx.x + kRowThreads * i;
+    v[i] = 0.f;
+    if (c < a.H) {
+      float x = a.h[row + c];
+      for (int s = 0; s < a.k; ++s) {
+        const int r = s_row[s];
+        const float y = a.y ? a.y[(long long)r * a.H + c]
+                            : part_sum(a.ypv, s_grp[s], r - a.y_group_off[s_grp[s]], c);
+        x += s_w[s] * y;
+      }
+      v[i] = x;
+      a.x_out[row + c] = x;
+    }
+    ss += v[i] * v[i];
+  }
+  if (!a.gamma_next) return;
+  ss = block_sum(ss, red);
+  const float rstd = 1.0f / sqrtf(ss / (float)a.H + a.eps);
+#pragma unroll
+  for (int i = 0; i < kRowCols; ++i) {
+    const int c = threadIdx.x + kRowThreads * i;
+    if (c < a.H) {
+      const float xn = v[i] * rstd * a.gamma_next[c];
+      if (a.xn_dtype == DT_BF16) ((uint16_t*)a.xn_out)[row + c] = f32_to_bf16(xn);
+      else ((float*)a.xn_out)[row + c] = xn;
+    }
+  }
 }
 
 hipError_t launch_combine(const CombineArgs& a, hipStream_t st) {
-  const int n_tiles = a.H / 64;
-  dim3 grid((n_tiles + 3) / 4, a.n_tok);
-  hipLaunchKernelGGL(k_combine, grid, dim3(256), 0, st, a);
+  hipLaunchKernelGGL(k_combine, dim3(a.n_tok), dim3(kRowThreads), 0, st, a);
   return hipGetLastError();
 }
 
-// One workgroup per row: v = x * rstd * gamma (or x), s = smallest power of
-// two with max|v| <= 448 s, codes = E4M3(v / s).
-__global__ __launch_bounds__(256) void k_quant_e4m3(QuantArgs a) {
-  __shared__ float red[4];
+// Rows of a grouped split product summed over the splits: out[r][c] for
+// dispatch rows r (grouped by expert through group offsets).
+__global__ __launch_bounds__(256) void k_part_rows(CombineArgs a) {
   const int r = blockIdx.x;
-  if (a.n_rows_dev && r >= *a.n_rows_dev) return;
-  const int src = a.row_src ? a.row_src[r] : r;
-  const float* x = a.x + (long long)src * a.x_ld;
-  float rstd = 1.f;
-  if (a.ss) {
-    float ssum = 0.f;
-    for (int t = 0; t < a.ss_tiles; ++t) ssum += a.ss[(long long)t * a.ss_ld + src];
-    rstd = 1.0f / sqrtf(ssum * a.inv_h + a.eps);
+  if (r >= a.y_group_off[a.y_n_groups]) return;
+  for (int c = threadIdx.x; c < a.H; c += 256) a.x_out[(long long)r * a.H + c] = y_elem(a, r, c);
+}
+
+hipError_t launch_part_rows(const CombineArgs& a, int max_rows, hipStream_t st) {
+  if (max_rows <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_part_rows, dim3(max_rows), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kRowThreads) void k_cvt_rows(CvtArgs a) {
+  __shared__ float red[kRowThreads / 64];
+  const int r = blockIdx.x;
+  const float* x = a.x + (long long)r * a.n_cols;
+  if (a.dtype == DT_BF16) {
+    for (int c = threadIdx.x; c < a.n_cols; c += kRowThreads)
+      ((uint16_t*)a.out)[(long long)r * a.n_cols + c] = f32_to_bf16(x[c]);
+    return;
   }
   float amax = 0.f;
-  for (int c = threadIdx.x; c < a.n_cols; c += 256) {
-    float v = x[c] * rstd;
-    if (a.gamma) v *= a.gamma[c];
-    amax = fmaxf(amax, fabsf(v));
-  }
-  amax = wave_max(amax);
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = amax;
-  __syncthreads();
-  amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  // smallest power of two s with amax <= 448 * s
-  float s = 1.f;
-  if (amax > 0.f) {
-    int e;
-    frexpf(amax / 448.0f, &e);            // amax/448 in [2^(e-1), 2^e)
-    s = ldexpf(1.f, e);
-    if (amax <= 448.0f * ldexpf(1.f, e - 1)) s = ldexpf(1.f, e - 1);
-  }
+  for (int c = threadIdx.x; c < a.n_cols; c += kRowThreads) amax = fmaxf(amax, fabsf(x[c]));
+  amax = block_max(amax, red);
+  const float s = pow2_scale_448(amax);
+  const float inv_s = 1.0f / s;
   if (threadIdx.x == 0) a.scales[r] = s;
-  const float inv_s = 1.0f / s;           // exact: power of two
-  uint8_t* o = a.codes + (long long)r * a.n_cols;
-  for (int c = threadIdx.x; c < a.n_cols; c += 256) {
-    float v = x[c] * rstd;
-    if (a.gamma) v *= a.gamma[c];
-    o[c] = f32_to_e4m3(v * inv_s);
-  }
+  for (int c = threadIdx.x; c < a.n_cols; c += kRowThreads)
+    ((uint8_t*)a.out)[(long long)r * a.n_cols + c] = f32_to_e4m3(x[c] * inv_s);
 }
 
-hipError_t launch_quant_e4m3(const QuantArgs& a, hipStream_t st) {
+hipError_t launch_cvt_rows(const CvtArgs& a, hipStream_t st) {
   if (a.n_rows <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_quant_e4m3, dim3(a.n_rows), dim3(256), 0, st, a);
+  hipLaunchKernelGGL(k_cvt_rows, dim3(a.n_rows), dim3(kRowThreads), 0, st, a);
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
 __global__ void k_fill_i32(int* p, long long n, int v) {
   for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (long long)gridDim.x * blockDim.x)
     p[i] = v;
@@ -97,7 +406,6 @@ hipError_t launch_fill_i32(int* p, long long n, int v, hipStream_t st) {
 }
 
 // KV cache rows <-> [n][Hkv][D] (one (sequence, position) per row, all KV heads).
-// Thread -> (row, head, d).
 __global__ void k_kv_io(KvIoArgs a) {
   const long long total = (long long)a.n * a.n_kv_heads * a.head_dim;
   const int D = a.head_dim;
@@ -115,7 +423,7 @@ __global__ void k_kv_io(KvIoArgs a) {
       base = ((long long)seq * a.n_kv_heads + g) * a.window * D;
       slot = pos % a.window;
     } else {
-      if (pos < 0 || pos >= a.kv_cap[seq]) continue;
+      if (pos >= a.kv_cap[seq]) continue;
       base = (a.kv_off[seq] * a.n_kv_heads + (long long)g * a.kv_cap[seq]) * D;
       slot = pos;
     }
@@ -152,9 +460,9 @@ hipError_t launch_kv_io(const KvIoArgs& a, hipStream_t st) {
 // records the hardware ids of the CU it ran on: XCC_ID and HW_ID (SE/SH/CU).
 __global__ void k_probe(unsigned* out, int spin) {
   if (threadIdx.x != 0) return;
-  unsigned xcc = __builtin_amdgcn_s_getreg((20) | (0 << 6) | (15 << 11));   // HW_REG_XCC_ID bits [3:0]
-  unsigned hw = __builtin_amdgcn_s_getreg((4) | (0 << 6) | (31 << 11));     // HW_REG_HW_ID
-  long long t0 = clock64();
+  const unsigned xcc = __builtin_amdgcn_s_getreg((20) | (0 << 6) | (15 << 11));   // HW_REG_XCC_ID
+  const unsigned hw = __builtin_amdgcn_s_getreg((4) | (0 << 6) | (31 << 11));     // HW_REG_HW_ID
+  const long long t0 = clock64();
   while (clock64() - t0 < spin) {
   }
   out[2 * blockIdx.x + 0] = xcc;

@@ -46,12 +46,21 @@ static spa_status make_pool(spa_ctx* ctx, const std::vector<uint32_t>& mask, spa
     }
   }
   if (nbits == 0) return fail(SPA_EMASK, "CU mask is empty");
+  // runtime mask bit i runs on XCD i % n_xcd; the runtime refuses a mask that
+  // leaves an XCD without CUs, so refuse it here before touching HIP
+  for (int x = 0; x < ctx->n_xcd; ++x) {
+    bool any = false;
+    for (int bit = x; bit < ctx->n_cus && !any; bit += ctx->n_xcd)
+      any = (size_t)(bit / 32) < mask.size() && (mask[bit / 32] >> (bit % 32) & 1u);
+    if (!any) return fail(SPA_EMASK, "CU mask leaves XCD " + std::to_string(x) + " without CUs");
+  }
   spa_pool* p = new spa_pool();
   p->ctx = ctx;
   p->mask = mask;
   hipError_t e = hipSetDevice(ctx->device);
   if (e == hipSuccess) e = hipExtStreamCreateWithCUMask(&p->stream, (uint32_t)mask.size(), mask.data());
   if (e != hipSuccess) {
+    (void)hipGetLastError();
     delete p;
     return hip_fail(e, "hipExtStreamCreateWithCUMask");
   }
@@ -192,7 +201,7 @@ spa_status spa_pipeline_run(spa_pipeline* p, const spa_layer* layers, const spa_
   const int n_micro = p->cfg.n_micro;
   if (b->batch < 1 || b->batch % n_micro) return fail(SPA_EINVAL, "n_micro must divide the batch");
   if (!b->x || !b->kv_len || !b->kv_off || !b->kv_cap || b->max_kv_len < 1) return fail(SPA_EINVAL, "bad batch");
-  if (b->batch * m->top_k > 4096 * n_micro) return fail(SPA_EUNSUPPORTED, "microbatch * top_k above 4096");
+  if ((long long)(b->batch / n_micro) * m->top_k > 4096) return fail(SPA_EUNSUPPORTED, "microbatch * top_k above 4096");
   for (int i = 0; i < m->n_layers; ++i) {
     const spa_layer* l = &layers[i];
     if (!l->wqkv || !l->wo || !l->wr || !l->wgu || !l->wd || !l->gamma1 || !l->gamma2 || !l->sinks || !l->k_cache ||
@@ -207,14 +216,13 @@ spa_status spa_pipeline_run(spa_pipeline* p, const spa_layer* layers, const spa_
   if (ws_bytes < W.total) return fail(SPA_EWORKSPACE, "workspace too small: need " + std::to_string(W.total));
 
   hipStream_t cs = (hipStream_t)caller_stream;
-  if (!p->tevs.empty()) harvest_timing(p);
   TimingHook th;
   th.cls = p->timed_cls;
   th.evs = &p->tevs;
   th.pool = &p->tpool;
   TimingHook* thp = p->timed_cls >= 0 ? &th : nullptr;
 
-  spa_status rc = clear_counters(W, ws, cs);
+  spa_status rc = clear_errors(ws, cs);
   if (rc) return rc;
   const bool temporal = p->a == nullptr;
   const bool router_in_a = p->cfg.cut == 1;
@@ -230,13 +238,14 @@ spa_status spa_pipeline_run(spa_pipeline* p, const spa_layer* layers, const spa_
       Slot s = slot_ptrs(W, ws, mu);
       const size_t ei = (size_t)l * n_micro + mu;
       if (!temporal && l > 0) SPA_HIP(hipStreamWaitEvent(sa, p->evB[ei - n_micro], 0));
-      rc = run_segment_a(p->ctx, m, &layers[l], l, b, mu * bm, bm, W, s, router_in_a, l == 0, sa, thp);
+      const spa_layer* next = l + 1 < m->n_layers ? &layers[l + 1] : nullptr;
+      rc = run_segment_a(p->ctx, m, &layers[l], l, next, b, mu * bm, bm, W, s, router_in_a, l == 0, sa, thp);
       if (rc) return rc;
       if (!temporal) {
         SPA_HIP(hipEventRecord(p->evA[ei], sa));
         SPA_HIP(hipStreamWaitEvent(sb, p->evA[ei], 0));
       }
-      rc = run_segment_b(p->ctx, m, &layers[l], l, b, mu * bm, bm, W, s, router_in_a, sb, thp);
+      rc = run_segment_b(p->ctx, m, &layers[l], l, next, b, mu * bm, bm, W, s, router_in_a, sb, thp);
       if (rc) return rc;
       if (!temporal) SPA_HIP(hipEventRecord(p->evB[ei], sb));
     }

@@ -86,3 +86,13 @@ def assert_close_rms(got, ref, tol: float, what: str):
     err = float(np.max(np.abs(got - ref)))
     assert err <= tol * rms, f"{what}: max|err| {err:.3e} > {tol} * RMS {rms:.3e}"
     return err / max(rms, 1e-300)
+
+
+def load_resample(name: str) -> Dict[int, int]:
+    """Re-draw map stored by tests/golden/make_resample.py (empty if absent)."""
+    import json
+    import os
+    p = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", f"resample_{name}.json")
+    if not os.path.exists(p):
+        return {}
+    return {int(k): int(v) for k, v in json.load(open(p))["resample"].items()}

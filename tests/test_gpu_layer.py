@@ -44,9 +44,10 @@ def _bufs(s, n):
     dev = dw.dev
     kvt = torch.bfloat16 if wl.kv_dtype == "bf16" else torch.float32
     H, QD, k = wl.hidden, wl.n_q_heads * wl.head_dim, wl.top_k
+    dnt = torch.bfloat16 if wl.w_dtype == "bf16" else torch.float32
     return dict(
-        ss_x=torch.zeros((H // 64, n), dtype=torch.float32, device=dev),
-        ss_h=torch.zeros((H // 64, n), dtype=torch.float32, device=dev),
+        xn=torch.zeros((n, H), dtype=dnt, device=dev),
+        hn=torch.zeros((n, H), dtype=torch.float32, device=dev),
         q=torch.zeros((n, QD), dtype=kvt, device=dev),
         o=torch.zeros((n, QD), dtype=kvt, device=dev),
         h=torch.zeros((n, H), dtype=torch.float32, device=dev),
@@ -59,7 +60,6 @@ def _bufs(s, n):
         inv=torch.zeros((n, k), dtype=torch.int32, device=dev),
         y=torch.zeros((n * k, H), dtype=torch.float32, device=dev),
         xo=torch.zeros((n, H), dtype=torch.float32, device=dev),
-        ss_o=torch.zeros((H // 64, n), dtype=torch.float32, device=dev),
     )
 
 
@@ -78,9 +78,12 @@ def test_steps_chained_and_isolated(setup):
     bf = _bufs(s, n)
     ws = dw.workspace(n_tok=n)
     dw.reset_x()
-    print(f"[{s['name']}] qkv", flush=True)
-    B.spa_row_sumsq(ctx, m, dw.x, n, bf["ss_x"])
-    B.spa_qkv_append(ctx, m, lay, dw.batch, 0, n, bf["ss_x"], bf["q"], ws)
+    print(f"[{s['name']}] norm + qkv", flush=True)
+    t0 = dw.layers_t[0]
+    B.spa_rms_norm(ctx, m, dw.x, t0["gamma1"], n, bf["xn"])
+    torch.cuda.synchronize()
+    hz.assert_close_rms(_f(bf["xn"])[toks], rec.xn, tol, "xn")
+    B.spa_qkv_append(ctx, m, lay, dw.batch, 0, n, bf["xn"], bf["q"], ws)
     torch.cuda.synchronize()
     q = _f(bf["q"]).reshape(n, wl.n_q_heads, wl.head_dim)
     hz.assert_close_rms(q[toks], rec.q, tol, "q")
@@ -96,7 +99,6 @@ def test_steps_chained_and_isolated(setup):
     qi[toks] = torch.as_tensor(rec.q, dtype=torch.float32, device=dw.dev).to(kvt)
     kr = torch.as_tensor(rec.k_new, dtype=torch.float32, device=dw.dev).to(kvt).contiguous()
     vr = torch.as_tensor(rec.v_new, dtype=torch.float32, device=dw.dev).to(kvt).contiguous()
-    t0 = dw.layers_t[0]
     B.spa_kv_io(ctx, m, t0["kind"], t0["k_cache"], t0["v_cache"], dw._io_batch(),
                 torch.as_tensor(np.array(toks, np.int32), device=dw.dev),
                 torch.as_tensor(np.array([int(L[b]) - 1 for b in toks], np.int32), device=dw.dev), len(toks), kr, vr, 1)
@@ -107,25 +109,27 @@ def test_steps_chained_and_isolated(setup):
 
     # output projection + residual (GPU o of every token)
     print(f"[{s['name']}] out proj", flush=True)
-    B.spa_out_proj(ctx, m, lay, dw.x, bf["o"], n, bf["h"], bf["ss_h"], ws)
+    B.spa_out_proj(ctx, m, lay, dw.x, bf["o"], n, bf["h"], bf["hn"], ws)
     torch.cuda.synchronize()
-    h = _f(bf["h"])
-    hz.assert_close_rms(h[toks], rec.h, tol, "h")
-    ss = _f(bf["ss_h"]).sum(axis=0)
-    np.testing.assert_allclose(ss[toks], (rec.h ** 2).sum(axis=1), rtol=5e-2 if tol > 1e-3 else 1e-4)
+    hz.assert_close_rms(_f(bf["h"])[toks], rec.h, tol, "h")
+    hz.assert_close_rms(_f(bf["hn"])[toks], rec.hn, tol, "hn")
 
-    # router, isolated: oracle h injected
+    # router, isolated: oracle h and hn injected
     print(f"[{s['name']}] route", flush=True)
     bf["h"][toks] = torch.as_tensor(rec.h, dtype=torch.float32, device=dw.dev)
-    B.spa_row_sumsq(ctx, m, bf["h"], n, bf["ss_h"])
+    bf["hn"][toks] = torch.as_tensor(rec.hn, dtype=torch.float32, device=dw.dev)
     route = _route(B, bf)
-    B.spa_moe_route(ctx, m, lay, bf["h"], bf["ss_h"], n, bf["logits"], route, None, ws)
+    B.spa_moe_route(ctx, m, lay, bf["hn"], n, bf["logits"], route, None, ws)
     torch.cuda.synchronize()
     lg = _f(bf["logits"])
     np.testing.assert_allclose(lg[toks], rec.logits, rtol=1e-4, atol=1e-4 * np.abs(rec.logits).max())
     idx = bf["topk_idx"].cpu().numpy()
-    np.testing.assert_array_equal(idx[toks], rec.topk)
-    np.testing.assert_allclose(bf["topk_w"].cpu().numpy()[toks], rec.weights, rtol=1e-4, atol=1e-6)
+    np.testing.assert_array_equal(np.sort(idx[toks], axis=1), np.sort(rec.topk, axis=1))
+    # the order of near-equal picks is not fixed: compare pick-aligned, sorted by expert
+    og = np.argsort(idx[toks], axis=1, kind="stable")
+    orf = np.argsort(rec.topk, axis=1, kind="stable")
+    wg = np.take_along_axis(bf["topk_w"].cpu().numpy()[toks], og, 1)
+    np.testing.assert_allclose(wg, np.take_along_axis(rec.weights, orf, 1), rtol=1e-4, atol=1e-6)
     # permutation invariants over all tokens (bit-exact integer work)
     from oracle.layer import permutation
     grp = idx.astype(np.int64) % wl.n_resident
@@ -137,16 +141,16 @@ def test_steps_chained_and_isolated(setup):
 
     # experts, isolated on the injected h
     print(f"[{s['name']}] experts", flush=True)
-    B.spa_moe_expert(ctx, m, lay, bf["h"], bf["ss_h"], n, route, bf["y"], ws)
+    B.spa_moe_expert(ctx, m, lay, bf["hn"], n, route, bf["y"], ws)
     torch.cuda.synchronize()
     y = _f(bf["y"])
     invn = bf["inv"].cpu().numpy()
-    ysel = np.stack([y[invn[b]] for b in toks])       # [tokens][k][H]
-    hz.assert_close_rms(ysel, rec.y, tol, "expert y")
+    ysel = np.stack([y[invn[b][og[i]]] for i, b in enumerate(toks)])   # [tokens][k][H], expert order
+    hz.assert_close_rms(ysel, np.stack([rec.y[i][orf[i]] for i in range(len(toks))]), tol, "expert y")
 
     # combine
     print(f"[{s['name']}] combine", flush=True)
-    B.spa_moe_combine(ctx, m, bf["h"], bf["y"], route, n, bf["xo"], bf["ss_o"])
+    B.spa_moe_combine(ctx, m, bf["h"], bf["y"], route, n, bf["xo"])
     torch.cuda.synchronize()
     hz.assert_close_rms(_f(bf["xo"])[toks], rec.x_next, tol, "x_next (combine)")
     assert B.spa_workspace_errors(ctx, ws) == 0

@@ -1,0 +1,120 @@
+"""CU pools and the two-stage spatial pipeline on the GPU.
+
+* pools built from CU masks land on the CUs the mask names: disjoint, and
+  spread evenly over the XCDs;
+* the pipeline changes only when each task runs, never what it computes: the
+  spatial schedule gives the same bits as the temporal schedule with the same
+  microbatches, for every cut and CU split;
+* one microbatch (T1) and several (Tm) agree within the bf16 bar and pick
+  the same experts.
+Runs on the first four layers (sliding, full, sliding, full) of the 36-layer
+one-GPU workload.
+"""
+import collections
+
+import numpy as np
+import pytest
+import torch
+
+from tests import harness as hz
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def env():
+    from spatially_pipelined_attention_amd import binding as B, synth
+    from spatially_pipelined_attention_amd.workload import DeviceWorkload
+    wl0 = synth.WORKLOADS["gptoss_36l_b64"]
+    wl = wl0.with_(n_layers=4, layer_kinds=wl0.layer_kinds[:4])
+    print("\n[setup] 4-layer slice of gptoss_36l_b64", flush=True)
+    dw = DeviceWorkload(wl, hz.load_resample("gptoss_36l_b64"))
+    ctx = B.spa_init(0)
+    return dict(B=B, wl=wl, dw=dw, ctx=ctx, n_cus=B.spa_device_cus(ctx))
+
+
+def _run(env, cut, n_micro, cu_a):
+    B, dw, ctx, n_cus = env["B"], env["dw"], env["ctx"], env["n_cus"]
+    pools = []
+    if cu_a is None:
+        pipe = B.spa_pipeline_create(ctx, dw.m, B.spa_pipeline_cfg(cut, n_micro), None, None)
+    else:
+        pa = B.spa_pool_create_split(ctx, 0, cu_a)
+        pb = B.spa_pool_create_split(ctx, cu_a // 8, n_cus - cu_a)
+        pools = [pa, pb]
+        pipe = B.spa_pipeline_create(ctx, dw.m, B.spa_pipeline_cfg(cut, n_micro), pa, pb)
+    ws = dw.workspace(n_micro=n_micro)
+    dw.reset_x()
+    dw.topk.zero_()
+    B.spa_pipeline_run(pipe, dw.layers_c, dw.batch, ws, torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    err = B.spa_workspace_errors(ctx, ws)
+    B.spa_pipeline_destroy(pipe)
+    for p in pools:
+        B.spa_pool_destroy(p)
+    assert err == 0
+    L = dw.L
+    full = [l for l, k in enumerate(dw.wl.layer_kinds) if k == "full"][0]
+    kk, vv = dw.read_kv(full, list(range(dw.wl.batch)), [int(x) - 1 for x in L])
+    return dw.x.clone(), dw.topk.clone(), kk, vv
+
+
+def test_pools_are_disjoint_and_xcd_balanced(env):
+    B, ctx = env["B"], env["ctx"]
+    pa = B.spa_pool_create_split(ctx, 0, 64)
+    pb = B.spa_pool_create_split(ctx, 8, 192)
+    try:
+        ia, na = B.spa_pool_probe(pa, 8192)
+        ib, nb = B.spa_pool_probe(pb, 8192)
+    finally:
+        B.spa_pool_destroy(pa)
+        B.spa_pool_destroy(pb)
+    assert na == 64 and nb == 192
+    assert not set(ia) & set(ib)
+    assert set(collections.Counter(i >> 16 for i in ia).values()) == {8}
+    assert set(collections.Counter(i >> 16 for i in ib).values()) == {24}
+
+
+def test_masks_rejected_before_launch(env):
+    B, ctx = env["B"], env["ctx"]
+    with pytest.raises(B.SpaError) as ei:
+        B.spa_pool_create_mask(ctx, [0x01010101] + [0] * 7)   # bits 0, 8, 16, 24: all on XCD 0
+    assert ei.value.status == B.SPA_EMASK
+    with pytest.raises(B.SpaError) as ei:
+        B.spa_pool_create_mask(ctx, [0] * 8)
+    assert ei.value.status == B.SPA_EMASK
+    pa = B.spa_pool_create_split(ctx, 0, 128)
+    pb = B.spa_pool_create_split(ctx, 8, 128)   # overlaps pa
+    try:
+        with pytest.raises(B.SpaError) as ei:
+            B.spa_pipeline_create(ctx, env["dw"].m, B.spa_pipeline_cfg(0, 2), pa, pb)
+        assert ei.value.status == B.SPA_EMASK
+    finally:
+        B.spa_pool_destroy(pa)
+        B.spa_pool_destroy(pb)
+
+
+@pytest.mark.parametrize("cut,n_micro,cu_a", [(0, 2, 128), (1, 2, 64), (0, 4, 192), (1, 4, 96), (0, 1, 128)])
+def test_spatial_equals_temporal_bitwise(env, cut, n_micro, cu_a):
+    print(f"[case] cut={cut} m={n_micro} cu_a={cu_a}", flush=True)
+    xt, tt, kt, vt = _run(env, cut, n_micro, None)
+    xs, ts, ks, vs = _run(env, cut, n_micro, cu_a)
+    assert torch.equal(xt, xs)
+    assert torch.equal(tt, ts)
+    np.testing.assert_array_equal(kt, ks)
+    np.testing.assert_array_equal(vt, vs)
+
+
+def test_repeat_runs_are_bitwise_identical(env):
+    a = _run(env, 0, 2, 128)
+    b = _run(env, 0, 2, 128)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+def test_one_microbatch_close_to_four(env):
+    x1, t1, _, _ = _run(env, 0, 1, None)
+    x4, t4, _, _ = _run(env, 0, 4, None)
+    x1 = x1.double().cpu().numpy()
+    x4 = x4.double().cpu().numpy()
+    hz.assert_close_rms(x4, x1, 1e-3, "T4 vs T1")
+    assert torch.equal(t1, t4)
