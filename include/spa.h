@@ -34,15 +34,24 @@
  *     bits.
  *   - Objects are not thread-safe; use one per thread or serialise.
  *
- * Tensor layouts (row-major; all offsets in elements)
- *   x         [B][H] fp32 residual stream, updated in place by a layer.
+ * Weight layout. Every projection weight is a stack of matrices W[N][K]
+ * (N output rows, K inputs) stored in the panel layout that
+ * spa_pack_weights() produces from row-major matrices: rows are grouped in
+ * panels of 16 (the last one zero-padded) and a panel is stored k-step by
+ * k-step, where a k-step is 64 bytes of a row (32 bf16, 16 fp32 or 64 E4M3
+ * values); byte b of row n, k-step t of matrix i sits at
+ *   ((i * ceil(N/16) + n/16) * (K*esz/64) + t) * 1024 + (n%16) * 64 + b.
+ * One k-step of 16 rows is then 1 KB of contiguous memory. As matrices:
  *   wqkv      [(Hq + 2 Hkv) D][H]    rows: q heads, then k heads, then v heads.
  *   wo        [H][Hq D]
  *   wr        [E][H] fp32 (router)
  *   wgu       [E_res][2I][H]  rows 0..I-1 gate, I..2I-1 up (per expert).
  *   wd        [E_res][H][I]
- *   wgu_scale [E_res][2I], wd_scale [E_res][H] fp32 (E4M3 experts only):
- *             dequantised weight = code value * scale of its row.
+ *   wgu_scale [E_res][2I], wd_scale [E_res][H] fp32 (E4M3 experts only,
+ *             plain arrays): dequantised weight = code value * scale of its row.
+ *
+ * Other tensors (row-major; all offsets in elements)
+ *   x         [B][H] fp32 residual stream, updated in place by a layer.
  *   sinks     [Hq] fp32 attention sink logits; gamma1, gamma2 [H] fp32.
  *   KV cache, per layer, D = 64, dtype kv_dtype:
  *     full layers (packed): the region of (sequence s, KV head g) starts at
@@ -53,7 +62,7 @@
  *       position p in slot p % W (W a multiple of 32);
  *     K of slot t at region + t*D + d; V at region + (t/32)*32*D + d*32 +
  *     vslot(t%32), vslot(p) = 8*((p%16)/4) + 4*(p/16) + p%4 (d-major 32-slot
- *     blocks). Use spa_kv_write / spa_kv_read instead of computing offsets.
+ *     blocks). Use spa_kv_io instead of computing offsets.
  *   A decode step of sequence s attends positions [0, L) (full) or
  *   [max(0, L-W), L) (sliding), L = kv_len[s], and writes its own K/V at L-1.
  */
@@ -81,7 +90,7 @@ typedef enum { SPA_SLIDING = 0, SPA_FULL = 1 } spa_layer_kind;
 /* Model shapes. Constraints: head_dim == 64; Hq % Hkv == 0, Hq/Hkv <= 16;
  * H % 64 == 0; inter % 32 == 0; window % 32 == 0; H, inter, Hq*D multiples
  * of the weight k-step (32 bf16 / 16 fp32 / 64 e4m3 elements);
- * E <= 256; 1 <= top_k <= min(E, 8); 1 <= n_resident <= E.
+ * E <= 256; 1 <= top_k <= min(E, 8); 1 <= n_resident <= min(E, 128).
  * dense_dtype: F32 or BF16 (wqkv, wo); expert_dtype: F32, BF16 or E4M3;
  * kv_dtype: F32 or BF16 and equal to dense_dtype. */
 typedef struct spa_model_desc {
@@ -168,6 +177,18 @@ spa_status spa_workspace_errors(spa_ctx* ctx, const void* ws, size_t ws_bytes, v
 spa_status spa_kv_io(spa_ctx* ctx, const spa_model_desc* m, int32_t kind, void* k_cache, void* v_cache,
                      const spa_batch* b, const int32_t* seq, const int32_t* pos, int32_t n, void* k_rows,
                      void* v_rows, int32_t write, void* stream);
+
+/* Bytes of n_mats packed N x K matrices (the panel layout above): n_mats *
+ * ceil(N/16)*16 * K * element size. 0 if the shape is not packable (K *
+ * element size must be a multiple of 64 bytes). */
+size_t spa_packed_bytes(int32_t dtype, int32_t n_mats, int32_t n_rows, int32_t k);
+
+/* Pack n_mats row-major matrices src [n_mats][n_rows][k] (dtype) into the
+ * panel layout at dst (spa_packed_bytes() bytes, caller-owned, must not
+ * overlap src). Both pointers 16-byte aligned device memory. Asynchronous
+ * on `stream`. SPA_EINVAL for a bad dtype, shape, pointer or overlap. */
+spa_status spa_pack_weights(spa_ctx* ctx, int32_t dtype, int32_t n_mats, int32_t n_rows, int32_t k, const void* src,
+                            void* dst, void* stream);
 
 /* -------------------------------------------------------- single operators
  * Each acts on tokens [tok0, tok0 + n_tok) of the batch and uses `ws`

@@ -73,6 +73,7 @@ _PROTOS = {
     "spa_workspace_init": [_P, C.POINTER(spa_model_desc), _I, _I, _I, _P, C.c_size_t, _P],
     "spa_workspace_errors": [_P, _P, C.c_size_t, _P, C.POINTER(C.c_int32)],
     "spa_kv_io": [_P, C.POINTER(spa_model_desc), _I, _P, _P, C.POINTER(spa_batch), _P, _P, _I, _P, _P, _I, _P],
+    "spa_pack_weights": [_P, _I, _I, _I, _I, _P, _P, _P],
     "spa_rms_norm": [_P, C.POINTER(spa_model_desc), _P, _P, _I, _P, _P],
     "spa_qkv_append": [_P, C.POINTER(spa_model_desc), C.POINTER(spa_layer), C.POINTER(spa_batch), _I, _I, _P, _P,
                        _P, C.c_size_t, _P],
@@ -107,7 +108,7 @@ _PROTOS = {
                               C.POINTER(C.c_int32)],
 }
 
-EXPORTED = sorted(list(_PROTOS) + ["spa_last_error", "spa_sched_binding"])
+EXPORTED = sorted(list(_PROTOS) + ["spa_last_error", "spa_sched_binding", "spa_packed_bytes"])
 
 _lib = None
 
@@ -127,6 +128,8 @@ def lib():
         L.spa_last_error.argtypes = []
         L.spa_sched_binding.restype = C.c_int32
         L.spa_sched_binding.argtypes = [_I, _I, _I]
+        L.spa_packed_bytes.restype = C.c_size_t
+        L.spa_packed_bytes.argtypes = [_I, _I, _I, _I]
         _lib = L
     return _lib
 
@@ -190,6 +193,14 @@ def spa_workspace_errors(ctx, ws, stream=None) -> int:
 def spa_kv_io(ctx, m, kind, k_cache, v_cache, batch: spa_batch | None, seq, pos, n, k_rows, v_rows, write, stream=None):
     _check(lib().spa_kv_io(ctx, C.byref(m), kind, ptr(k_cache), ptr(v_cache), C.byref(batch) if batch else None,
                            ptr(seq), ptr(pos), n, ptr(k_rows), ptr(v_rows), write, stream_handle(stream)))
+
+
+def spa_packed_bytes(dtype: int, n_mats: int, n_rows: int, k: int) -> int:
+    return int(lib().spa_packed_bytes(dtype, n_mats, n_rows, k))
+
+
+def spa_pack_weights(ctx, dtype: int, n_mats: int, n_rows: int, k: int, src, dst, stream=None):
+    _check(lib().spa_pack_weights(ctx, dtype, n_mats, n_rows, k, ptr(src), ptr(dst), stream_handle(stream)))
 
 
 # ----------------------------------------------------------------------- operators

@@ -4,37 +4,34 @@
 // Q/KV projection, output projection, router gating, expert up, expert down)
 // is Y[r][n] = sum_k X[r][k] * W[n][k] with few rows r (the decoded tokens of
 // a microbatch, or the rows routed to one expert) and a large W read once
-// from HBM. The kernel is built for that:
-//   * a workgroup of 4 waves owns 64 output columns (16 per wave) of one
-//     64-row block; each lane streams 16 bytes of its W row per k-step
-//     straight from HBM into registers;
-//   * X (small, L2-resident) is staged through LDS, 8 k-steps per group,
-//     double-buffered, and shared by the 4 waves (optionally gathered by a
-//     row map, e.g. tokens routed to an expert);
-//   * the hot loop has no data-dependent branches: k-steps beyond the range
-//     are masked to zero and addresses clamped, the next group's X and W
-//     loads are issued (X first) before the current group is multiplied, so
-//     the W stream stays in flight across the LDS barriers;
-//   * the k dimension may be split over S workgroups; each writes its fp32
-//     partial tile to workspace and a row-wise finish kernel sums the splits
-//     in split order (no cross-workgroup fences, fixed summation order);
-//   * with S = 1 the epilogue runs here on the finished tile in LDS: SwiGLU
-//     (gate and up columns paired inside the tile) or a plain store, with
-//     E4M3 per-row and per-channel scales applied first.
-// MFMA operand layout: A = W tile (16 output columns x k), B = X^T tile
-// (k x 16 rows); lane l holds C[4(l/16)+i][l%16] = Y[row l%16][col 4(l/16)+i].
+// from HBM. The kernel is a weight stream:
+//   * a workgroup owns 64 output columns of one block of up to 16*MT rows
+//     (one W read serves all rows of the block); its 4 waves take the
+//     k-steps of the workgroup's K range round-robin (wave w: steps w, w+4,
+//     ...), so together they walk each W row front to back;
+//   * each wave keeps a ring of P k-steps of W and X fragments in flight in
+//     registers (W straight from HBM, X from L2) and multiplies the oldest;
+//     the hot loop has no barriers and no data-dependent branches (steps past
+//     the end load a clamped address and are masked to zero);
+//   * at the end the 4 wave tiles are summed in wave order through LDS, one
+//     16-row tile at a time, and wave 0 writes the result: an fp32 partial
+//     tile for a split-K finish kernel (the k range may be split over S
+//     workgroups, summed later in split order), or the finished rows, with
+//     E4M3 per-row and per-channel scales applied, either stored plainly or
+//     through SwiGLU (a tile's columns 0-31 are gate rows and 32-63 the
+//     matching up rows, so gate and up of one output sit in the same lane).
+// MFMA operand layout: A = W fragment (16 output columns x k), B = X
+// fragment (k x 16 rows); lane l holds C[4(l/16)+i][l%16], i.e. output
+// column 4(l/16)+i of the fragment for row l%16. Both operands take the k
+// elements of a 64-byte k-step in the same lane order, so the product is the
+// plain dot product.
 #include "common.h"
 #include "kernels.h"
 
 namespace spa {
 
-constexpr int kStepBytes = 64;                       // one k-step of one row
-constexpr int kGroup = 8;                            // k-steps per pipeline group
-constexpr int kGroupBytes = kStepBytes * kGroup;     // 512
-constexpr int kRowPitch = kGroupBytes + 16;          // LDS row pitch (bank spread)
-constexpr int kBufBytes = 64 * kRowPitch;            // one X group buffer
-constexpr int kTilePitch = 68;                       // fp32 epilogue tile pitch
-constexpr int kGemmLds = 2 * kBufBytes;
+constexpr int kStepBytes = 64;     // one k-step of one row
+constexpr int kRedBytes = 3 * 4 * 64 * 16;     // LDS for the wave reduction (one 16-row tile, <= 4 fragments)
 
 template <int WT> struct WTraits;
 template <> struct WTraits<DT_BF16> { static constexpr int ks = 32; static constexpr int esz = 2; };
@@ -60,11 +57,13 @@ __device__ __forceinline__ f32x4 mma_step(u32x4 w, u32x4 x, f32x4 acc) {
   }
 }
 
-// W row feeding tile column c (0..63) of column tile nb.
-template <int EPI>
+// W row feeding tile column c (0..16*CT-1) of column tile nb; a SwiGLU tile
+// pairs 8*CT gate rows with the 8*CT up rows of the same outputs.
+template <int EPI, int CT>
 __device__ __forceinline__ int w_row_of(const GemmArgs& a, int nb, int c) {
-  if constexpr (EPI == EPI_SWIGLU) return c < 32 ? nb * 32 + c : a.inter + nb * 32 + (c - 32);
-  else return nb * 64 + c;
+  constexpr int HC = 8 * CT;
+  if constexpr (EPI == EPI_SWIGLU) return c < HC ? nb * HC + c : a.inter + nb * HC + (c - HC);
+  else return nb * 16 * CT + c;
 }
 
 template <int EPI>
@@ -73,210 +72,272 @@ __device__ __forceinline__ int w_rows_total(const GemmArgs& a) {
   else return a.N;
 }
 
-// One row block: acc[mt] += X[rows] W^T over this workgroup's k-steps.
-// Thread t stages LDS row t/4, k-steps 2(t%4) and 2(t%4)+1 of a group.
-template <int WT, int MT>
-__device__ __forceinline__ void mainloop(const GemmArgs& a, const char* wp, bool wvalid, int ks0, int nks,
-                                         const char* xsrc, char* buf0, char* buf1, f32x4 (&acc)[4]) {
+// ring depth: keeps the register budget of two workgroups per CU
+template <int CT, int MT> struct Ring { static constexpr int P = CT * MT > 16 ? 2 : (CT * MT > 8 ? 3 : 4); };
+
+template <int WT, int EPI, int CT, int MT>
+__global__ __launch_bounds__(256, 2) void k_gemm(GemmArgs a) {
+  __shared__ __attribute__((aligned(16))) char red[kRedBytes];
+  constexpr int P = Ring<CT, MT>::P;
+  constexpr int BR = 16 * MT;
+  constexpr int TC = 16 * CT;
   const int tid = threadIdx.x, lane = tid & 63;
-  const int m_st = tid >> 2, kq = (tid & 3) * 2;
-  const int ngroups = (nks + kGroup - 1) / kGroup;
-  const int kl = nks - 1;                       // last local k-step (clamp target)
-  u32x4 WA[kGroup], WB[kGroup], XS[8];
-  const u32x4 zero = {0u, 0u, 0u, 0u};
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
-  auto xload = [&](int g) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int kk = min(g * kGroup + kq + i, kl);
-      const char* p = xsrc + (long long)(ks0 + kk) * kStepBytes;
-#pragma unroll
-      for (int u = 0; u < 4; ++u) XS[4 * i + u] = ld16(p + 16 * u);
-    }
-  };
-  auto xstore = [&](char* buf) {
-    char* dst = buf + m_st * kRowPitch + kq * kStepBytes;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) st16(dst + 16 * i, XS[i]);
-  };
-  auto wload = [&](int g, u32x4 (&W)[kGroup]) {
-#pragma unroll
-    for (int j = 0; j < kGroup; ++j) W[j] = ld16(wp + (long long)min(g * kGroup + j, kl) * kStepBytes);
-  };
-  auto compute = [&](int g, const u32x4 (&W)[kGroup], const char* buf) {
-    const char* xb = buf + (lane & 15) * kRowPitch + (lane >> 4) * 16;
-#pragma unroll
-    for (int j = 0; j < kGroup; ++j) {
-      const bool live = wvalid && (g * kGroup + j < nks);
-      const u32x4 wf = live ? W[j] : zero;
-      u32x4 xf[MT];
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) xf[mt] = ld16(xb + mt * 16 * kRowPitch + j * kStepBytes);
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) acc[mt] = mma_step<WT>(wf, xf[mt], acc[mt]);
-      // keep the fragment reads of one k-step together: bounds register pressure
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  };
-
-  // The loop body is one straight-line block: the loads of the next group are
-  // issued before the current group's MFMAs and cannot be sunk next to their
-  // use. A group past the end (odd count) loads clamped addresses and is
-  // fully masked.
-  xload(0);
-  wload(0, WA);
-  xstore(buf0);
-  lds_barrier();
-  for (int g = 0; g < ngroups; g += 2) {
-    xload(g + 1);
-    wload(g + 1, WB);
-    compute(g, WA, buf0);
-    xstore(buf1);
-    lds_barrier();
-    xload(g + 2);
-    wload(g + 2, WA);
-    compute(g + 1, WB, buf1);
-    xstore(buf0);
-    lds_barrier();
-  }
-}
-
-template <int WT, int EPI>
-__global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
-  extern __shared__ __attribute__((aligned(16))) char lds[];
-  char* buf0 = lds;
-  char* buf1 = lds + kBufBytes;
-  __shared__ int xrow_l[64];
-
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  // block -> (split, column tile, row block, group); one 64-row block per
-  // workgroup, so the workgroups of a tile stream its W concurrently
+  // block -> (split, column tile, row block); grouped products number the
+  // non-empty row blocks of all groups in group order
   int bid = blockIdx.x;
   const int s = bid % a.S;
   bid /= a.S;
   const int nb = bid % a.n_tiles;
-  bid /= a.n_tiles;
-  const int rb = bid % a.rb_stride;
-  const int grp = bid / a.rb_stride;
-
-  int r0 = 0, nrows = a.n_rows;
+  const int blk = bid / a.n_tiles;
+  int grp = 0, rb = blk, r0 = 0, nrows = a.n_rows;
   if (a.group_off) {
+    // wave-parallel scan of the per-group block counts (two groups per lane)
+    const int g0 = 2 * lane, g1 = 2 * lane + 1;
+    const int n0 = g0 < a.n_groups ? a.group_off[g0 + 1] - a.group_off[g0] : 0;
+    const int n1 = g1 < a.n_groups ? a.group_off[g1 + 1] - a.group_off[g1] : 0;
+    const int c0 = (n0 + BR - 1) / BR, c1 = (n1 + BR - 1) / BR;
+    int incl = c0 + c1;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int t = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += t;
+    }
+    const int excl = incl - c0 - c1;
+    const unsigned long long hit = __ballot(blk >= excl && blk < incl);
+    if (hit == 0ull) return;                       // past the last non-empty block
+    const int hl = __builtin_ctzll(hit);
+    const int e = __shfl(excl, hl, 64), cc0 = __shfl(c0, hl, 64);
+    grp = blk - e < cc0 ? 2 * hl : 2 * hl + 1;
+    rb = blk - e < cc0 ? blk - e : blk - e - cc0;
+    grp = __builtin_amdgcn_readfirstlane(grp);
+    rb = __builtin_amdgcn_readfirstlane(rb);
     r0 = a.group_off[grp];
     nrows = a.group_off[grp + 1] - r0;
   }
-  if (nrows <= rb * 64) return;
+  if (nrows <= rb * BR) return;
+  const int rows_here = min(BR, nrows - rb * BR);
 
   constexpr int KS = WTraits<WT>::ks;
+  constexpr int esz = WTraits<WT>::esz;
   const int nks_total = a.K / KS;
   const int ks0 = (int)((long long)s * nks_total / a.S);
-  const int ks1 = (int)((long long)(s + 1) * nks_total / a.S);
-  const int nks = ks1 - ks0;
+  const int nks = (int)((long long)(s + 1) * nks_total / a.S) - ks0;
 
-  const int c_lane = wave * 16 + (lane & 15);
-  const int wrow = w_row_of<EPI>(a, nb, c_lane);
-  const bool wvalid = wrow < w_rows_total<EPI>(a);
-  const char* wp = (const char*)a.W +
-                   ((long long)grp * a.w_gstride + (long long)(wvalid ? wrow : 0) * a.K) * WTraits<WT>::esz +
-                   (long long)ks0 * kStepBytes + (lane >> 4) * 16;   // this split's first k-step
+  // per-lane fragment base pointers. W is stored in 16-row panels: panel p
+  // holds rows 16p..16p+15 as [k-step][16 rows][64 bytes], so the fragment of
+  // one k-step is 1 KB of contiguous memory
+  const int lo16 = lane & 15, kq = (lane >> 4) * 16;
+  const long long panel_bytes = (long long)nks_total * 1024;
+  const char* wp[CT];
+  bool wvalid[CT];
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct) {
+    const int wrow0 = w_row_of<EPI, CT>(a, nb, ct * 16);            // first row of the fragment (16-aligned)
+    wvalid[ct] = wrow0 + lo16 < w_rows_total<EPI>(a);
+    wp[ct] = (const char*)a.W + (long long)grp * a.w_gstride * esz + (long long)((wvalid[ct] ? wrow0 : 0) >> 4) * panel_bytes +
+             (long long)ks0 * 1024 + lo16 * 64 + kq;
+  }
+  // X fragment of row-tile mt: 16 rows of one k-step; rows sit x_rstride
+  // bytes apart and k-steps x_kstride bytes apart (row-major or k-step-major)
+  const char* xp[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const int orow = r0 + rb * BR + min(mt * 16 + lo16, rows_here - 1);   // padding rows repeat a real row
+    const int src = a.row_src ? a.row_src[orow] : orow;
+    xp[mt] = (const char*)a.X + (long long)src * a.x_rstride + (long long)ks0 * a.x_kstride + kq;
+  }
 
-  {
-    const int rows_here = min(64, nrows - rb * 64);
-    const int mtiles = (rows_here + 15) >> 4;
-    if (tid < 64) {
-      const int orow = r0 + rb * 64 + min(tid, rows_here - 1);   // clamp padding rows to a real row
-      xrow_l[tid] = a.row_src ? a.row_src[orow] : orow;
+  f32x4 acc[MT][CT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) acc[mt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  if (nks > 0) {
+    u32x4 Wr[P][CT], Xr[P][MT];
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+    // Wave w takes k-steps w + 4g of this split; the workgroups of a product
+    // start at different groups g (a rotation fixed by the tile), so they do
+    // not all read the same X lines at once. Summation order stays fixed.
+    const int kl = nks - 1;
+    const int ng = (nks + 3) / 4;                  // groups of 4 k-steps
+    const int rot = (int)(((unsigned)nb * 7u + (unsigned)blk * 13u) % (unsigned)ng);
+    auto kstep = [&](int j) {
+      int g = j + rot;
+      g = g >= ng ? g - ng : g;
+      return j < ng ? min(wave + 4 * g, kl) : kl;
+    };
+    auto load = [&](int slot, int j) {
+      const long long kk = kstep(j);
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) Wr[slot][ct] = ld16_stream(wp[ct] + kk * 1024);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) Xr[slot][mt] = ld16(xp[mt] + kk * a.x_kstride);
+    };
+    auto compute = [&](int slot, int j) {
+      int g = j + rot;
+      g = g >= ng ? g - ng : g;
+      const bool live = j < ng && wave + 4 * g < nks;   // wave-uniform
+      u32x4 w[CT];
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) w[ct] = (live && wvalid[ct]) ? Wr[slot][ct] : zero;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) acc[mt][ct] = mma_step<WT>(w[ct], Xr[slot][mt], acc[mt][ct]);
+    };
+    // groups rounded up to the ring depth
+    const int J = (ng + P - 1) / P * P;
+#pragma unroll
+    for (int p = 0; p < P; ++p) load(p, p);
+    // straight-line rounds: multiply slot p, then refill it P steps ahead; the
+    // scheduling barriers keep each refill right behind its multiply so the
+    // wave always has P-1 k-steps of loads in flight
+    for (int j0 = 0; j0 + P < J; j0 += P) {
+#pragma unroll
+      for (int p = 0; p < P; ++p) {
+        compute(p, j0 + p);
+        __builtin_amdgcn_sched_barrier(0);
+        load(p, j0 + P + p);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+#pragma unroll
+    for (int p = 0; p < P; ++p) compute(p, J - P + p);
+  }
+
+  // sum the wave tiles in wave order: 16 rows at a time through LDS
+  f32x4* rd = reinterpret_cast<f32x4*>(red);
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    if (wave > 0) {
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) rd[((wave - 1) * CT + ct) * 64 + lane] = acc[mt][ct];
     }
     __syncthreads();
-    const char* xsrc = (const char*)a.X + (long long)xrow_l[tid >> 2] * a.x_ld * WTraits<WT>::esz;
-
-    f32x4 acc[4];
+    if (wave == 0) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (nks > 0) {
-      if (mtiles == 1) mainloop<WT, 1>(a, wp, wvalid, ks0, nks, xsrc, buf0, buf1, acc);
-      else if (mtiles == 2) mainloop<WT, 2>(a, wp, wvalid, ks0, nks, xsrc, buf0, buf1, acc);
-      else mainloop<WT, 4>(a, wp, wvalid, ks0, nks, xsrc, buf0, buf1, acc);
+      for (int w = 0; w < 3; ++w)
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) acc[mt][ct] += rd[(w * CT + ct) * 64 + lane];
     }
+    __syncthreads();
+  }
+  if (wave != 0) return;
 
-    if constexpr (EPI == EPI_PARTIAL) {
-      // row-major fp32 partial tile [64][64] of split s
-      const long long tile_id = ((long long)grp * a.n_tiles + nb) * a.rb_stride + rb;
-      float* pt = a.part + (tile_id * a.S + s) * 4096;
+  // wave 0 holds the tile: row mt*16 + lo16, columns ct*16 + c4 + i
+  const int c4 = (lane >> 4) * 4;
+  if constexpr (EPI == EPI_PARTIAL) {
+    // split s, row (dispatch or token row), padded column: [S][part_rows][part_ld]
+    float* pt = a.part + ((long long)s * a.part_rows + r0 + rb * BR) * a.part_ld + nb * TC + c4;
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        const int m = mt * 16 + (lane & 15);
-        if (m < rows_here)
-          *reinterpret_cast<f32x4*>(pt + m * 64 + wave * 16 + (lane >> 4) * 4) = acc[mt];
+    for (int mt = 0; mt < MT; ++mt) {
+      const int m = mt * 16 + lo16;
+      if (m < rows_here) {
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) *reinterpret_cast<f32x4*>(pt + (long long)m * a.part_ld + ct * 16) = acc[mt][ct];
       }
-    } else {
-      // finished tile -> LDS (reuses the X buffers: the last barrier ended all reads)
-      float* T = (float*)lds;
-      float wsc[4] = {1.f, 1.f, 1.f, 1.f};
-      if constexpr (WT == DT_E4M3) {
+    }
+  } else {
+    float wsc[CT][4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int wr = w_row_of<EPI>(a, nb, wave * 16 + (lane >> 4) * 4 + r);
-          wsc[r] = wr < w_rows_total<EPI>(a) ? a.w_scale[(long long)grp * a.ws_gstride + wr] : 0.f;
+    for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) wsc[ct][i] = 1.f;
+    if constexpr (WT == DT_E4M3) {
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int wr = w_row_of<EPI, CT>(a, nb, ct * 16 + c4 + i);
+          wsc[ct][i] = wr < w_rows_total<EPI>(a) ? a.w_scale[(long long)grp * a.ws_gstride + wr] : 0.f;
         }
-      }
+    }
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        const int m = mt * 16 + (lane & 15);
-        float xs = 1.f;
-        if constexpr (WT == DT_E4M3) xs = a.x_scale[xrow_l[m]];
+    for (int mt = 0; mt < MT; ++mt) {
+      const int m = mt * 16 + lo16;
+      if (m >= rows_here) continue;
+      const long long orow = r0 + rb * BR + m;
+      float xs = 1.f;
+      if constexpr (WT == DT_E4M3) xs = a.x_scale[a.row_src ? a.row_src[orow] : orow];
+      float v[CT][4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) T[m * kTilePitch + wave * 16 + (lane >> 4) * 4 + r] = acc[mt][r] * wsc[r] * xs;
-      }
-      __syncthreads();
-      const int m = tid >> 2, cq = (tid & 3) * 16;
-      const bool rvalid = m < rows_here;
-      const long long orow = r0 + rb * 64 + m;
-      const float* trow = T + m * kTilePitch;
+      for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[ct][i] = acc[mt][ct][i] * wsc[ct][i] * xs;
       if constexpr (EPI == EPI_STORE) {
-        if (rvalid) {
-          float* o = (float*)a.out + orow * a.out_ld + nb * 64 + cq;
+        float* o = (float*)a.out + orow * a.out_ld;
 #pragma unroll
-          for (int i = 0; i < 16; ++i)
-            if (nb * 64 + cq + i < a.N) o[i] = trow[cq + i];
+        for (int ct = 0; ct < CT; ++ct) {
+          const int c = nb * TC + ct * 16 + c4;
+          if (c + 3 < a.N) {
+            *reinterpret_cast<f32x4*>(o + c) = f32x4{v[ct][0], v[ct][1], v[ct][2], v[ct][3]};
+          } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if (c + i < a.N) o[c + i] = v[ct][i];
+          }
         }
-      } else if constexpr (EPI == EPI_SWIGLU) {
-        if (rvalid && cq < 32) {
-          const int j0 = nb * 32 + cq;
-          float z[16];
+      } else {   // SwiGLU: fragments ct < CT/2 are gate columns, ct + CT/2 the matching up columns
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const float g = trow[cq + i], u = trow[32 + cq + i];
+        for (int ct = 0; ct < CT / 2; ++ct) {
+          const int j0 = nb * 8 * CT + ct * 16 + c4;
+          if (j0 >= a.inter) continue;
+          float z[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float g = v[ct][i], u = v[ct + CT / 2][i];
             z[i] = g / (1.0f + __expf(-g)) * u;
           }
-          if (a.out_dtype == DT_BF16) {
-            uint16_t* o = (uint16_t*)a.out + orow * a.out_ld + j0;
-#pragma unroll
-            for (int i = 0; i < 16; i += 8) {
-              u32x4 pk = {pack_bf16x2(z[i], z[i + 1]), pack_bf16x2(z[i + 2], z[i + 3]),
-                          pack_bf16x2(z[i + 4], z[i + 5]), pack_bf16x2(z[i + 6], z[i + 7])};
-              st16(o + i, pk);
-            }
-          } else {
-            float* o = (float*)a.out + orow * a.out_ld + j0;
-#pragma unroll
-            for (int i = 0; i < 16; i += 4) *reinterpret_cast<f32x4*>(o + i) = f32x4{z[i], z[i + 1], z[i + 2], z[i + 3]};
+          const long long zr = a.out_kmajor_rows;
+          if (a.out_dtype == DT_BF16) {   // k-step-major: 32 bf16 per k-step
+            uint16_t* o = (uint16_t*)a.out + (zr ? ((long long)(j0 >> 5) * zr + orow) * 32 + (j0 & 31) : orow * a.out_ld + j0);
+            *reinterpret_cast<uint2*>(o) = uint2{pack_bf16x2(z[0], z[1]), pack_bf16x2(z[2], z[3])};
+          } else {                        // k-step-major: 16 fp32 per k-step
+            float* o = (float*)a.out + (zr ? ((long long)(j0 >> 4) * zr + orow) * 16 + (j0 & 15) : orow * a.out_ld + j0);
+            *reinterpret_cast<f32x4*>(o) = f32x4{z[0], z[1], z[2], z[3]};
           }
         }
       }
     }
+  }
+}
+
+template <int WT, int EPI, int CT, int MT>
+static hipError_t launch_t(const GemmArgs& a, hipStream_t st) {
+  const int grid = a.n_tiles * a.rb_stride * a.S;
+  hipLaunchKernelGGL((k_gemm<WT, EPI, CT, MT>), dim3(grid), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+template <int WT, int EPI, int CT>
+static hipError_t launch_mt(const GemmArgs& a, hipStream_t st) {
+  switch (a.blk_rows) {
+    case 16: return launch_t<WT, EPI, CT, 1>(a, st);
+    case 32: return launch_t<WT, EPI, CT, 2>(a, st);
+    case 48: return launch_t<WT, EPI, CT, 3>(a, st);
+    case 64: return launch_t<WT, EPI, CT, 4>(a, st);
+    case 80: return launch_t<WT, EPI, CT, 5>(a, st);
+    case 128: return launch_t<WT, EPI, CT, 8>(a, st);
+    default: return hipErrorInvalidValue;
   }
 }
 
 template <int WT, int EPI>
-static hipError_t launch_t(const GemmArgs& a, hipStream_t st) {
-  const int grid = a.n_tiles * a.n_groups * a.rb_stride * a.S;
-  hipLaunchKernelGGL((k_gemm<WT, EPI>), dim3(grid), dim3(256), kGemmLds, st, a);
-  return hipGetLastError();
+static hipError_t launch_ct(const GemmArgs& a, hipStream_t st) {
+  if (a.tile_cols == 64) return launch_mt<WT, EPI, 4>(a, st);
+  if constexpr (WT != DT_F32) {
+    if (a.tile_cols == 32) return launch_mt<WT, EPI, 2>(a, st);
+  }
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_gemm(int wt, int epi, const GemmArgs& a, hipStream_t st) {
+  if (a.group_off && a.n_groups > 128) return hipErrorInvalidValue;   // the block scan holds 2 groups per lane
 #define SPA_CASE(W, E) \
-  if (wt == W && epi == E) return launch_t<W, E>(a, st);
+  if (wt == W && epi == E) return launch_ct<W, E>(a, st);
   SPA_CASE(DT_BF16, EPI_PARTIAL)
   SPA_CASE(DT_F32, EPI_PARTIAL)
   SPA_CASE(DT_E4M3, EPI_PARTIAL)
@@ -290,6 +351,6 @@ hipError_t launch_gemm(int wt, int epi, const GemmArgs& a, hipStream_t st) {
   return hipErrorInvalidValue;
 }
 
-int gemm_lds_bytes() { return kGemmLds; }
+bool gemm_blk_rows_ok(int r) { return r == 16 || r == 32 || r == 48 || r == 64 || r == 80 || r == 128; }
 
 }  // namespace spa

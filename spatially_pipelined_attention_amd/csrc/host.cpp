@@ -39,6 +39,7 @@ spa_status validate_model(const spa_model_desc* m) {
   if (m->n_experts < 1 || m->n_experts > 256) return fail(SPA_EUNSUPPORTED, "n_experts must be in [1, 256]");
   if (m->top_k < 1 || m->top_k > 8 || m->top_k > m->n_experts) return fail(SPA_EINVAL, "top_k must be in [1, min(E, 8)]");
   if (m->n_resident < 1 || m->n_resident > m->n_experts) return fail(SPA_EINVAL, "n_resident must be in [1, E]");
+  if (m->n_resident > 128) return fail(SPA_EUNSUPPORTED, "more than 128 resident experts");
   if (m->n_layers < 1) return fail(SPA_EINVAL, "n_layers must be >= 1");
   if (!(m->eps >= 0.f)) return fail(SPA_EINVAL, "eps must be >= 0");
   if (m->dense_dtype != SPA_F32 && m->dense_dtype != SPA_BF16) return fail(SPA_EUNSUPPORTED, "dense_dtype must be F32 or BF16");
@@ -64,39 +65,69 @@ int max_chunks_for(int max_kv_len, const spa_model_desc* m) {
 
 // Launch shapes depend only on tensor shapes (never on the CU pool), so a
 // microbatch computes the same bits in every schedule.
+static int pick_blk_rows(int need) {
+  for (int r : {16, 32, 48, 64, 80}) if (need <= r) return r;
+  return 128;
+}
+
+// Shape of one projection: rows per block (one W read serves them all), 64
+// output columns per tile, and the split-K factor that gives the chip enough
+// workgroups. Grouped (expert) products size the row block for the expected
+// rows per expert plus three standard deviations of uniform routing, so an
+// expert's W is streamed once with high probability.
 GemmPlan plan_gemm(int kc, const spa_model_desc* m, int n_tok, int n_cus) {
   GemmPlan p{};
-  int K = 0, groups = 1, rows = n_tok;
+  int K = 0, N = 0, groups = 0;
   p.epi = EPI_PARTIAL;
+  p.tile_cols = 64;
   switch (kc) {
-    case KC_QKV: K = m->hidden; p.ks = ks_of(m->dense_dtype);
-      p.n_tiles = (m->n_q_heads + 2 * m->n_kv_heads) * m->head_dim / 64; break;
-    case KC_OPROJ: K = m->n_q_heads * m->head_dim; p.ks = ks_of(m->dense_dtype); p.n_tiles = m->hidden / 64; break;
-    case KC_ROUTER: K = m->hidden; p.ks = 16; p.n_tiles = (m->n_experts + 63) / 64; break;
-    case KC_GATEUP: K = m->hidden; p.ks = ks_of(m->expert_dtype); p.n_tiles = m->inter / 32;
-      groups = m->n_resident; rows = n_tok * m->top_k; p.epi = EPI_SWIGLU; break;
-    case KC_DOWN: K = m->inter; p.ks = ks_of(m->expert_dtype); p.n_tiles = m->hidden / 64;
-      groups = m->n_resident; rows = n_tok * m->top_k; break;
+    case KC_QKV: K = m->hidden; p.ks = ks_of(m->dense_dtype); N = (m->n_q_heads + 2 * m->n_kv_heads) * m->head_dim; break;
+    case KC_OPROJ: K = m->n_q_heads * m->head_dim; p.ks = ks_of(m->dense_dtype); N = m->hidden; break;
+    case KC_ROUTER: K = m->hidden; p.ks = 16; N = m->n_experts; break;
+    case KC_GATEUP: K = m->hidden; p.ks = ks_of(m->expert_dtype); N = 2 * m->inter; groups = m->n_resident;
+      p.epi = EPI_SWIGLU; break;
+    case KC_DOWN: K = m->inter; p.ks = ks_of(m->expert_dtype); N = m->hidden; groups = m->n_resident; break;
     default: break;
   }
-  p.n_groups = groups;
-  p.rb_stride = std::max(1, (rows + 63) / 64);
+  p.n_groups = std::max(groups, 1);
+  p.n_tiles = (N + p.tile_cols - 1) / p.tile_cols;
+  p.part_ld = p.n_tiles * p.tile_cols;
+  int busy_blocks;   // row blocks expected to hold rows
+  if (groups == 0) {
+    p.blk_rows = pick_blk_rows(std::min(n_tok, 128));
+    p.rb_stride = (n_tok + p.blk_rows - 1) / p.blk_rows;
+    p.part_rows = n_tok;
+    busy_blocks = p.rb_stride;
+  } else {
+    const int R = n_tok * m->top_k;
+    const double mean = (double)R / groups;
+    p.blk_rows = pick_blk_rows(std::max(1, (int)std::ceil(mean + 3.0 * std::sqrt(mean))));
+    const int rb_all = (R + p.blk_rows - 1) / p.blk_rows;   // every row in one group
+    p.rb_stride = std::min(groups * rb_all, rb_all + groups);
+    p.part_rows = R;
+    busy_blocks = std::min(p.rb_stride, std::max(1, std::min(groups, R)));
+  }
   const int nks = K / p.ks;
   const int target = std::max(256, (n_cus * 5) / 4);
-  int S = (target + p.n_tiles * groups - 1) / (p.n_tiles * groups);
-  S = std::min(S, std::max(1, nks / 16));
-  S = std::min(S, 16);   // the finish kernels sum at most 16 splits
+  int S = (target + p.n_tiles * busy_blocks - 1) / (p.n_tiles * busy_blocks);
+  S = std::min(S, std::max(1, nks / 8));   // two k-steps per wave at least
+  S = std::min(S, 16);                     // the finish kernels sum at most 16 splits
   if (p.epi == EPI_SWIGLU) S = 1;
   p.S = std::max(1, S);
   if (kc == KC_DOWN && p.S == 1) p.epi = EPI_STORE;
   return p;
 }
 
+// Partial space for any call of up to n_tok tokens: the largest split any
+// plan may choose (16, and at most an eighth of the k-steps) times the rows
+// and padded columns of the product.
 static size_t gemm_part_floats(const spa_model_desc* m, int n_tok) {
   size_t mx = 0;
-  for (int kc : {KC_QKV, KC_OPROJ, KC_ROUTER, KC_GATEUP, KC_DOWN}) {
-    GemmPlan p = plan_gemm(kc, m, n_tok, 1024);   // S never exceeds this device-independent bound
-    if (p.epi == EPI_PARTIAL) mx = std::max(mx, (size_t)p.n_groups * p.n_tiles * p.rb_stride * p.S * 4096);
+  for (int kc : {KC_QKV, KC_OPROJ, KC_ROUTER, KC_DOWN}) {
+    const GemmPlan p = plan_gemm(kc, m, n_tok, 1);
+    int K = kc == KC_QKV || kc == KC_ROUTER ? m->hidden : (kc == KC_OPROJ ? m->n_q_heads * m->head_dim : m->inter);
+    const size_t s_max = (size_t)std::min(16, std::max(1, K / p.ks / 8));
+    mx = std::max(mx, s_max * p.part_rows * p.part_ld);
   }
   return mx;
 }
@@ -128,6 +159,8 @@ WsLayout ws_layout(const spa_model_desc* m, int n_tok, int max_kv_len, int n_mic
   s.row_tok = o; o = align256(o + (size_t)R * 4);
   s.row_slot = o; o = align256(o + (size_t)R * 4);
   s.inv = o; o = align256(o + (size_t)R * 4);
+  s.xe_perm = o; o = align256(o + (size_t)R * H * esz_of(m->expert_dtype));
+  s.xe_perm_scale = o; o = align256(o + (fp8 ? (size_t)R * 4 : 0));
   s.z = o; o = align256(o + (size_t)R * I * (ebf ? 2 : 4));
   s.z8 = o; o = align256(o + (fp8 ? (size_t)R * I : 0));
   s.z8_scale = o; o = align256(o + (fp8 ? (size_t)R * 4 : 0));
@@ -166,6 +199,8 @@ Slot slot_ptrs(const WsLayout& L, void* ws, int slot) {
   s.z = b + o.z;
   s.z8 = (uint8_t*)(b + o.z8);
   s.z8_scale = (float*)(b + o.z8_scale);
+  s.xe_perm = b + o.xe_perm;
+  s.xe_perm_scale = (float*)(b + o.xe_perm_scale);
   s.y = (float*)(b + o.y);
   s.attn_part = (float*)(b + o.attn_part);
   s.gemm_part = (float*)(b + o.gemm_part);
@@ -215,11 +250,15 @@ static GemmArgs gemm_args(const GemmPlan& p, const Slot& s, int n_tok) {
   GemmArgs a;
   memset(&a, 0, sizeof(a));
   a.n_tiles = p.n_tiles;
+  a.tile_cols = p.tile_cols;
+  a.blk_rows = p.blk_rows;
   a.n_groups = p.n_groups;
   a.S = p.S;
   a.rb_stride = p.rb_stride;
   a.n_rows = n_tok;
   a.part = s.gemm_part;
+  a.part_rows = p.part_rows;
+  a.part_ld = p.part_ld;
   return a;
 }
 
@@ -227,8 +266,8 @@ static PartView view_of(const GemmPlan& p, const Slot& s) {
   PartView v;
   v.part = s.gemm_part;
   v.S = p.S;
-  v.n_tiles = p.n_tiles;
-  v.rb_stride = p.rb_stride;
+  v.rows = p.part_rows;
+  v.ld = p.part_ld;
   return v;
 }
 
@@ -241,7 +280,8 @@ static spa_status op_qkv(spa_ctx* ctx, const spa_model_desc* m, const spa_layer*
   a.K = m->hidden;
   a.N = (m->n_q_heads + 2 * m->n_kv_heads) * m->head_dim;
   a.X = xn;
-  a.x_ld = m->hidden;
+  a.x_rstride = (long long)m->hidden * esz_of(m->dense_dtype);
+  a.x_kstride = 64;
   QkvFinishArgs f;
   memset(&f, 0, sizeof(f));
   f.pv = view_of(p, s);
@@ -315,7 +355,8 @@ static spa_status op_oproj(spa_ctx* ctx, const spa_model_desc* m, const spa_laye
   a.K = m->n_q_heads * m->head_dim;
   a.N = m->hidden;
   a.X = o;
-  a.x_ld = m->n_q_heads * m->head_dim;
+  a.x_rstride = (long long)m->n_q_heads * m->head_dim * esz_of(m->dense_dtype);
+  a.x_kstride = 64;
   OprojFinishArgs f;
   memset(&f, 0, sizeof(f));
   f.pv = view_of(p, s);
@@ -344,7 +385,8 @@ static spa_status op_route(spa_ctx* ctx, const spa_model_desc* m, const spa_laye
   a.K = m->hidden;
   a.N = m->n_experts;
   a.X = hn;
-  a.x_ld = m->hidden;
+  a.x_rstride = (long long)m->hidden * 4;
+  a.x_kstride = 64;
   RouteArgs ra;
   memset(&ra, 0, sizeof(ra));
   ra.pv = view_of(p, s);
@@ -384,14 +426,19 @@ static spa_status op_expert(spa_ctx* ctx, const spa_model_desc* m, const spa_lay
     a.N = I;
     a.inter = I;
     a.group_off = r.offsets;
-    a.row_src = r.row_tok;
-    a.X = xe;
-    a.x_ld = H;
-    a.x_scale = xe_scale;
+    // expert rows gathered in dispatch order, k-step-major: one 16-row X
+    // fragment of a k-step is 1 KB of contiguous memory
+    a.X = s.xe_perm;
+    a.x_rstride = 64;
+    a.x_kstride = (long long)R * 64;
+    a.x_scale = fp8 ? s.xe_perm_scale : nullptr;
     a.out = s.z;
     a.out_ld = I;
+    a.out_kmajor_rows = R;
     a.out_dtype = m->expert_dtype == SPA_BF16 ? DT_BF16 : DT_F32;
     HookScope hs(th, KC_GATEUP, st);
+    SPA_HIP(launch_gather_kmajor(xe, r.row_tok, R, H, esz_of(m->expert_dtype), s.xe_perm, fp8 ? xe_scale : nullptr,
+                                 fp8 ? s.xe_perm_scale : nullptr, st));
     SPA_HIP(launch_gemm(m->expert_dtype, EPI_SWIGLU, a, st));
   }
   {
@@ -409,19 +456,22 @@ static spa_status op_expert(spa_ctx* ctx, const spa_model_desc* m, const spa_lay
     HookScope hs(th, KC_DOWN, st);
     if (fp8) {
       CvtArgs c;
+      memset(&c, 0, sizeof(c));
       c.x = (const float*)s.z;
       c.n_rows = R;
       c.n_cols = I;
       c.dtype = DT_E4M3;
       c.out = s.z8;
       c.scales = s.z8_scale;
+      c.kmajor_rows = R;
       SPA_HIP(launch_cvt_rows(c, st));
       a.X = s.z8;
       a.x_scale = s.z8_scale;
     } else {
       a.X = s.z;
     }
-    a.x_ld = I;
+    a.x_rstride = 64;                       // z is k-step-major over the R dispatch rows
+    a.x_kstride = (long long)R * 64;
     SPA_HIP(launch_gemm(m->expert_dtype, p.epi, a, st));
     if (down_plan) *down_plan = p;
   }
@@ -663,6 +713,27 @@ spa_status spa_kv_io(spa_ctx* ctx, const spa_model_desc* m, int32_t kind, void* 
   return SPA_OK;
 }
 
+size_t spa_packed_bytes(int32_t dtype, int32_t n_mats, int32_t n_rows, int32_t k) {
+  if (dtype != SPA_F32 && dtype != SPA_BF16 && dtype != SPA_E4M3) return 0;
+  if (n_mats < 1 || n_rows < 1 || k < 1 || ((size_t)k * esz_of(dtype)) % 64) return 0;
+  return (size_t)n_mats * ((size_t)(n_rows + 15) / 16 * 16) * k * esz_of(dtype);
+}
+
+spa_status spa_pack_weights(spa_ctx* ctx, int32_t dtype, int32_t n_mats, int32_t n_rows, int32_t k, const void* src,
+                            void* dst, void* stream) {
+  if (!ctx) return fail(SPA_EINVAL, "ctx is NULL");
+  if (dtype != SPA_F32 && dtype != SPA_BF16 && dtype != SPA_E4M3) return fail(SPA_EINVAL, "bad dtype");
+  if (n_mats < 1 || n_rows < 1 || k < 1) return fail(SPA_EINVAL, "n_mats, n_rows and k must be >= 1");
+  if (((size_t)k * esz_of(dtype)) % 64) return fail(SPA_EINVAL, "a row must be a whole number of 64-byte k-steps");
+  if (!src || !dst || misaligned(src) || misaligned(dst)) return fail(SPA_EINVAL, "src/dst NULL or not 16-byte aligned");
+  const size_t nb = spa_packed_bytes(dtype, n_mats, n_rows, k);
+  const char *s0 = (const char*)src, *d0 = (const char*)dst;
+  if (s0 < d0 + nb && d0 < s0 + (size_t)n_mats * n_rows * k * esz_of(dtype))
+    return fail(SPA_EINVAL, "src and dst overlap");
+  SPA_HIP(launch_pack_panels(src, dst, n_mats, n_rows, k, esz_of(dtype), (hipStream_t)stream));
+  return SPA_OK;
+}
+
 spa_status spa_rms_norm(spa_ctx* ctx, const spa_model_desc* m, const float* x, const float* gamma, int32_t n_tok,
                         void* xn_out, void* stream) {
   if (!ctx) return fail(SPA_EINVAL, "ctx is NULL");
@@ -749,6 +820,7 @@ spa_status spa_moe_expert(spa_ctx* ctx, const spa_model_desc* m, const spa_layer
   const void* xe = hn;
   if (m->expert_dtype != SPA_F32) {   // the expert input format of hn
     CvtArgs c;
+    memset(&c, 0, sizeof(c));
     c.x = hn;
     c.n_rows = n_tok;
     c.n_cols = m->hidden;

@@ -40,7 +40,7 @@ constexpr int kAttnChunk = 512;
 struct SlotLayout {
   size_t xn, q, o, h, hn_f32, hn_bf16, hn8, hn8_scale, logits;
   size_t topk_idx, topk_w, offsets, row_tok, row_slot, inv;
-  size_t z, z8, z8_scale, y, attn_part, gemm_part;
+  size_t xe_perm, xe_perm_scale, z, z8, z8_scale, y, attn_part, gemm_part;
   size_t bytes;
 };
 
@@ -57,6 +57,7 @@ struct WsLayout {
 
 struct GemmPlan {
   int n_tiles, n_groups, S, rb_stride, ks, epi;
+  int tile_cols, blk_rows, part_rows, part_ld;
 };
 
 spa_status validate_model(const spa_model_desc* m);
@@ -81,6 +82,8 @@ struct Slot {
   void* z;
   uint8_t* z8;
   float* z8_scale;
+  void* xe_perm;
+  float* xe_perm_scale;
   float* y;
   float* attn_part;
   float* gemm_part;

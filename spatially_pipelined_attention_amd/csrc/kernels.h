@@ -14,13 +14,13 @@ enum KvKind : int { KV_RING = 0, KV_PACKED = 1 };
 // device-side error bits (workspace error word)
 enum : int { ERR_KV_LEN = 1 };
 
-// Split-K partial tiles: fp32 [tile][split][64 rows][64 cols], tile =
-// (group * n_tiles + column tile) * rb_stride + row block.
+// Split-K partial products: fp32 [split][rows][ld]; rows are token rows of a
+// dense product or dispatch rows of a grouped one, ld the padded column count.
 struct PartView {
   const float* part;
   int S;
-  int n_tiles;
-  int rb_stride;
+  int rows;
+  int ld;
 };
 
 struct GemmArgs {
@@ -30,19 +30,25 @@ struct GemmArgs {
   int N;                    // output columns (SwiGLU: inter)
   const float* w_scale;     // E4M3: per W row scale, group stride ws_gstride
   long long ws_gstride;
-  int n_tiles;              // 64-wide output column tiles (SwiGLU: 32 gate + 32 up)
+  int n_tiles;              // output column tiles of tile_cols (SwiGLU: half gate, half up)
+  int tile_cols;            // 32 or 64
+  int blk_rows;             // rows per row block (16, 32, 48, 64, 80 or 128)
   int n_groups;
   const int* group_off;     // [n_groups+1] or null (one group of n_rows)
   int n_rows;
   int S;                    // split-K factor
-  const void* X;            // [rows][x_ld] in the weight's MFMA input type
-  int x_ld;
+  const void* X;            // rows of K elements in the weight's MFMA input type
+  long long x_rstride;      // bytes between rows (row-major: K * esz; k-step-major: 64)
+  long long x_kstride;      // bytes between 64-byte k-steps (row-major: 64; k-step-major: rows * 64)
   const int* row_src;       // X row of each output row (null: identity)
   const float* x_scale;     // E4M3 X: per X row scale
-  float* part;              // EPI_PARTIAL output
-  int rb_stride;
+  float* part;              // EPI_PARTIAL output [S][part_rows][part_ld]
+  int part_rows;
+  int part_ld;
+  int rb_stride;            // row-block slots in the grid (grouped: upper bound on non-empty blocks)
   void* out;                // EPI_SWIGLU / EPI_STORE output
   int out_ld;
+  int out_kmajor_rows;      // SwiGLU: > 0 writes z k-step-major over this many rows (else row-major, out_ld)
   int out_dtype;
   int inter;
 };
@@ -111,8 +117,8 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t st);
 struct CombineArgs {
   const float* h;
   const float* y;           // plain y (or null)
-  PartView ypv;             // partial y when y == null
-  const int* y_group_off;
+  PartView ypv;             // partial y (dispatch rows) when y == null
+  const int* y_group_off;   // [y_n_groups + 1]: dispatch rows in use = y_group_off[y_n_groups]
   int y_n_groups;
   const float* w;
   const int* inv;
@@ -157,7 +163,9 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t st);
 // merge of the chunk partials of multi-chunk sequences (single-chunk ones are final already)
 hipError_t launch_attn_merge(const AttnArgs& a, hipStream_t st);
 
-// fp32 rows -> bf16 rows or per-row power-of-two-scaled E4M3 (expert inputs)
+// fp32 rows -> bf16 rows or per-row power-of-two-scaled E4M3 (expert inputs).
+// kmajor_rows > 0: input and output are k-step-major over that many rows
+// (element (r, c) of a 64-byte k-step layout sits at ((c / ks) * rows + r) * ks + c % ks).
 struct CvtArgs {
   const float* x;
   int n_rows;
@@ -165,10 +173,20 @@ struct CvtArgs {
   int dtype;                // DT_BF16 or DT_E4M3
   void* out;
   float* scales;            // E4M3
+  int kmajor_rows;
 };
 hipError_t launch_cvt_rows(const CvtArgs& a, hipStream_t st);
 
 hipError_t launch_fill_i32(int* p, long long n, int v, hipStream_t st);
+
+// Row-major [n_mats][N][K] (element size esz, K * esz a multiple of 64) ->
+// panels [n_mats][ceil(N/16)][K*esz/64][16 rows][64 bytes]; rows past N are zero.
+hipError_t launch_pack_panels(const void* src, void* dst, int n_mats, int N, int K, int esz, hipStream_t st);
+
+// dst k-step-major [K*esz/64][R][64 bytes] <- rows src[row_src[r]] of a
+// row-major [*][K] source; optional per-row scales gathered alongside.
+hipError_t launch_gather_kmajor(const void* src, const int* row_src, int R, int K, int esz, void* dst,
+                                const float* src_scale, float* dst_scale, hipStream_t st);
 
 struct KvIoArgs {
   void* k_cache;
@@ -193,6 +211,6 @@ hipError_t launch_kv_io(const KvIoArgs& a, hipStream_t st);
 // hardware placement probe: each workgroup records its XCC / SE / CU ids
 hipError_t launch_probe(unsigned* out, int n_blocks, int spin, hipStream_t st);
 
-int gemm_lds_bytes();
+bool gemm_blk_rows_ok(int rows);
 
 }  // namespace spa

@@ -50,12 +50,12 @@ constexpr int kMaxSplits = 16;   // plan_gemm never splits k more than this
 // Element (row r, column c) of a split product, summed over the splits in
 // split order. All loads are issued before the first add (clamped index,
 // masked value: adding +0 leaves every partial sum unchanged).
-__device__ __forceinline__ float part_sum(const PartView& pv, int grp, int r, int c) {
-  const long long tile = ((long long)grp * pv.n_tiles + (c >> 6)) * pv.rb_stride + (r >> 6);
-  const float* p = pv.part + tile * pv.S * 4096 + (r & 63) * 64 + (c & 63);
+__device__ __forceinline__ float part_sum(const PartView& pv, int r, int c) {
+  const float* p = pv.part + (long long)r * pv.ld + c;
+  const long long sstride = (long long)pv.rows * pv.ld;
   float v[kMaxSplits];
 #pragma unroll
-  for (int s = 0; s < kMaxSplits; ++s) v[s] = p[min(s, pv.S - 1) * 4096];
+  for (int s = 0; s < kMaxSplits; ++s) v[s] = p[min(s, pv.S - 1) * sstride];
   float acc = v[0];
 #pragma unroll
   for (int s = 1; s < kMaxSplits; ++s) acc += s < pv.S ? v[s] : 0.f;
@@ -85,7 +85,7 @@ __global__ __launch_bounds__(256) void k_qkv_finish(QkvFinishArgs a) {
   const int pos = L - 1;
   const bool ok = (L >= 1) && (a.kv_kind == KV_RING || L <= a.kv_cap[seq]);
   if (!ok && c == 0 && a.err) atomicOr(a.err, ERR_KV_LEN);
-  const float v = part_sum(a.pv, 0, r, c);
+  const float v = part_sum(a.pv, r, c);
   if (c < QD) {
     if (a.kv_dtype == DT_BF16) ((uint16_t*)a.q_out)[(long long)r * QD + c] = f32_to_bf16(v);
     else ((float*)a.q_out)[(long long)r * QD + c] = v;
@@ -128,7 +128,7 @@ __global__ __launch_bounds__(kRowThreads) void k_oproj_finish(OprojFinishArgs a)
     const int c = threadIdx.x + kRowThreads * i;
     h[i] = 0.f;
     if (c < a.H) {
-      h[i] = a.x[row + c] + part_sum(a.pv, 0, r, c);
+      h[i] = a.x[row + c] + part_sum(a.pv, r, c);
       a.h_out[row + c] = h[i];
     }
     ss += h[i] * h[i];
@@ -180,7 +180,7 @@ __global__ __launch_bounds__(256) void k_route_topk(RouteArgs a) {
     const int e = lane + 64 * j;
     v[j] = -INFINITY;
     if (e < E) {
-      v[j] = part_sum(a.pv, 0, t, e);
+      v[j] = part_sum(a.pv, t, e);
       a.logits[(long long)t * E + e] = v[j];
     }
   }
@@ -283,34 +283,20 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t st) {
 }
 
 // ---------------------------------------------------------------------------
-// expert group of dispatch row `row` (largest g with group_off[g] <= row)
-__device__ __forceinline__ int group_of(const int* off, int n_groups, int row) {
-  int lo = 0, hi = n_groups - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (off[mid] <= row) lo = mid;
-    else hi = mid - 1;
-  }
-  return lo;
-}
-
 __device__ __forceinline__ float y_elem(const CombineArgs& a, int row, int c) {
-  if (a.y) return a.y[(long long)row * a.H + c];
-  const int g = group_of(a.y_group_off, a.y_n_groups, row);
-  return part_sum(a.ypv, g, row - a.y_group_off[g], c);
+  return a.y ? a.y[(long long)row * a.H + c] : part_sum(a.ypv, row, c);
 }
 
 __global__ __launch_bounds__(kRowThreads) void k_combine(CombineArgs a) {
   __shared__ float red[kRowThreads / 64];
   __shared__ float s_w[8];
-  __shared__ int s_row[8], s_grp[8];
+  __shared__ int s_row[8];
   const int t = blockIdx.x;
   const long long row = (long long)t * a.H;
   if (threadIdx.x < a.k) {
     const int r = a.inv[t * a.k + threadIdx.x];
     s_w[threadIdx.x] = a.w[t * a.k + threadIdx.x];
     s_row[threadIdx.x] = r;
-    s_grp[threadIdx.x] = a.y ? 0 : group_of(a.y_group_off, a.y_n_groups, r);
   }
   __syncthreads();
   float v[kRowCols];
@@ -322,10 +308,7 @@ __global__ __launch_bounds__(kRowThreads) void k_combine(CombineArgs a) {
     if (c < a.H) {
       float x = a.h[row + c];
       for (int s = 0; s < a.k; ++s) {
-        const int r = s_row[s];
-        const float y = a.y ? a.y[(long long)r * a.H + c]
-                            : part_sum(a.ypv, s_grp[s], r - a.y_group_off[s_grp[s]], c);
-        x += s_w[s] * y;
+        x += s_w[s] * y_elem(a, s_row[s], c);
       }
       v[i] = x;
       a.x_out[row + c] = x;
@@ -369,25 +352,92 @@ hipError_t launch_part_rows(const CombineArgs& a, int max_rows, hipStream_t st) 
 __global__ __launch_bounds__(kRowThreads) void k_cvt_rows(CvtArgs a) {
   __shared__ float red[kRowThreads / 64];
   const int r = blockIdx.x;
-  const float* x = a.x + (long long)r * a.n_cols;
+  const long long R = a.kmajor_rows;
+  // element c of row r: row-major, or k-step-major with 16 fp32 per k-step
+  auto in_at = [&](int c) -> float {
+    return R ? a.x[((long long)(c >> 4) * R + r) * 16 + (c & 15)] : a.x[(long long)r * a.n_cols + c];
+  };
   if (a.dtype == DT_BF16) {
-    for (int c = threadIdx.x; c < a.n_cols; c += kRowThreads)
-      ((uint16_t*)a.out)[(long long)r * a.n_cols + c] = f32_to_bf16(x[c]);
+    for (int c = threadIdx.x; c < a.n_cols; c += kRowThreads) {
+      const long long o = R ? ((long long)(c >> 5) * R + r) * 32 + (c & 31) : (long long)r * a.n_cols + c;
+      ((uint16_t*)a.out)[o] = f32_to_bf16(in_at(c));
+    }
     return;
   }
   float amax = 0.f;
-  for (int c = threadIdx.x; c < a.n_cols; c += kRowThreads) amax = fmaxf(amax, fabsf(x[c]));
+  for (int c = threadIdx.x; c < a.n_cols; c += kRowThreads) amax = fmaxf(amax, fabsf(in_at(c)));
   amax = block_max(amax, red);
   const float s = pow2_scale_448(amax);
   const float inv_s = 1.0f / s;
   if (threadIdx.x == 0) a.scales[r] = s;
-  for (int c = threadIdx.x; c < a.n_cols; c += kRowThreads)
-    ((uint8_t*)a.out)[(long long)r * a.n_cols + c] = f32_to_e4m3(x[c] * inv_s);
+  for (int c = threadIdx.x; c < a.n_cols; c += kRowThreads) {
+    const long long o = R ? ((long long)(c >> 6) * R + r) * 64 + (c & 63) : (long long)r * a.n_cols + c;
+    ((uint8_t*)a.out)[o] = f32_to_e4m3(in_at(c) * inv_s);
+  }
 }
 
 hipError_t launch_cvt_rows(const CvtArgs& a, hipStream_t st) {
   if (a.n_rows <= 0) return hipSuccess;
   hipLaunchKernelGGL(k_cvt_rows, dim3(a.n_rows), dim3(kRowThreads), 0, st, a);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// 16-byte chunk i of the panel layout <- its source chunk (or zero past row N).
+__global__ void k_pack_panels(const u32x4* __restrict__ src, u32x4* __restrict__ dst, int N, int ksteps, int n_panels,
+                              long long total) {
+  for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+       i += (long long)gridDim.x * blockDim.x) {
+    const int q = (int)(i & 3);                      // 16-byte quarter of the 64-byte k-step
+    const int row16 = (int)((i >> 2) & 15);
+    long long t = i >> 6;                            // (mat, panel, kstep)
+    const int ks = (int)(t % ksteps);
+    t /= ksteps;
+    const int panel = (int)(t % n_panels);
+    const long long mat = t / n_panels;
+    const int n = panel * 16 + row16;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (n < N) v = src[((mat * N + n) * ksteps + ks) * 4 + q];
+    dst[i] = v;
+  }
+}
+
+hipError_t launch_pack_panels(const void* src, void* dst, int n_mats, int N, int K, int esz, hipStream_t st) {
+  const int ksteps = K * esz / 64, n_panels = (N + 15) / 16;
+  const long long total = (long long)n_mats * n_panels * ksteps * 64;
+  if (total <= 0) return hipSuccess;
+  long long g = (total + 255) / 256;
+  if (g > 65536) g = 65536;
+  hipLaunchKernelGGL(k_pack_panels, dim3((int)g), dim3(256), 0, st, (const u32x4*)src, (u32x4*)dst, N, ksteps, n_panels,
+                     total);
+  return hipGetLastError();
+}
+
+// 16-byte chunk i of the k-step-major destination [kstep][r][4 quarters].
+__global__ void k_gather_kmajor(const u32x4* __restrict__ src, const int* __restrict__ row_src, int R, int ksteps,
+                                u32x4* __restrict__ dst, const float* __restrict__ src_scale, float* __restrict__ dst_scale) {
+  const long long total = (long long)ksteps * R * 4;
+  for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+       i += (long long)gridDim.x * blockDim.x) {
+    const int q = (int)(i & 3);
+    const long long t = i >> 2;
+    const int r = (int)(t % R);
+    const int ks = (int)(t / R);
+    const long long srow = row_src[r];
+    dst[i] = src[(srow * ksteps + ks) * 4 + q];
+    if (dst_scale && ks == 0 && q == 0) dst_scale[r] = src_scale[srow];
+  }
+}
+
+hipError_t launch_gather_kmajor(const void* src, const int* row_src, int R, int K, int esz, void* dst,
+                                const float* src_scale, float* dst_scale, hipStream_t st) {
+  const int ksteps = K * esz / 64;
+  const long long total = (long long)ksteps * R * 4;
+  if (total <= 0) return hipSuccess;
+  long long g = (total + 255) / 256;
+  if (g > 8192) g = 8192;
+  hipLaunchKernelGGL(k_gather_kmajor, dim3((int)g), dim3(256), 0, st, (const u32x4*)src, row_src, R, ksteps,
+                     (u32x4*)dst, src_scale, dst_scale);
   return hipGetLastError();
 }
 

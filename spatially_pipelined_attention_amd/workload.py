@@ -57,6 +57,7 @@ class DeviceWorkload:
         self._keep = []
         for l in range(wl.n_layers):
             self._build_layer(l, fill_history)
+        torch.cuda.synchronize()
         self.batch = B.spa_batch(wl.batch, self.max_kv_len, self.kv_len_d.data_ptr(), self.kv_off_d.data_ptr(),
                                  self.kv_cap_d.data_ptr(), self.x.data_ptr(),
                                  self.topk.data_ptr() if self.topk is not None else None)
@@ -67,14 +68,22 @@ class DeviceWorkload:
         synth.dev_fill_normal(t, synth.stream_key(self.wl.seed, tag, layer, sub), 0, std)
         return t
 
+    def _pack(self, t: torch.Tensor, dtype: str, n_mats: int, n_rows: int, k: int) -> torch.Tensor:
+        """Row-major weight matrices -> the library's panel layout (a byte tensor)."""
+        code = _DT[dtype]
+        dst = torch.empty(B.spa_packed_bytes(code, n_mats, n_rows, k), dtype=torch.uint8, device=self.dev)
+        B.spa_pack_weights(self.ctx_for_io(), code, n_mats, n_rows, k, t, dst, torch.cuda.current_stream())
+        return dst
+
     def _build_layer(self, l: int, fill_history: bool):
         wl = self.wl
         H, I, E, Er = wl.hidden, wl.inter, wl.n_experts, wl.n_resident
         D, Hkv, Hq = wl.head_dim, wl.n_kv_heads, wl.n_q_heads
         t: dict = {}
-        t["wqkv"] = self._fill((wl.qkv_rows, H), wl.w_dtype, synth.TAG_WQKV, l, 0, wl.w_std)
-        t["wo"] = self._fill((H, Hq * D), wl.w_dtype, synth.TAG_WO, l, 0, wl.w_std)
-        t["wr"] = self._fill((E, H), "f32", synth.TAG_WR, l, 0, wl.router_sigma)
+        t["wqkv"] = self._pack(self._fill((wl.qkv_rows, H), wl.w_dtype, synth.TAG_WQKV, l, 0, wl.w_std),
+                               wl.w_dtype, 1, wl.qkv_rows, H)
+        t["wo"] = self._pack(self._fill((H, Hq * D), wl.w_dtype, synth.TAG_WO, l, 0, wl.w_std), wl.w_dtype, 1, H, Hq * D)
+        t["wr"] = self._pack(self._fill((E, H), "f32", synth.TAG_WR, l, 0, wl.router_sigma), "f32", 1, E, H)
         t["sinks"] = self._fill((Hq,), "f32", synth.TAG_SINK, l, 0, 1.0)
         t["gamma1"] = torch.ones(H, dtype=torch.float32, device=self.dev)
         t["gamma2"] = torch.ones(H, dtype=torch.float32, device=self.dev)
@@ -89,14 +98,16 @@ class DeviceWorkload:
                 d_c[e].copy_(torch.from_numpy(ew["wd_codes"]))
                 gu_s[e].copy_(torch.from_numpy(ew["wgu_scale"]))
                 d_s[e].copy_(torch.from_numpy(ew["wd_scale"]))
-            t.update(wgu=gu_c, wd=d_c, wgu_scale=gu_s, wd_scale=d_s)
+            t.update(wgu=self._pack(gu_c, "e4m3", Er, 2 * I, H), wd=self._pack(d_c, "e4m3", Er, H, I),
+                     wgu_scale=gu_s, wd_scale=d_s)
         else:
             wgu = torch.empty((Er, 2 * I, H), dtype=_TORCH[wl.expert_dtype], device=self.dev)
             wd = torch.empty((Er, H, I), dtype=_TORCH[wl.expert_dtype], device=self.dev)
             for e in range(Er):
                 synth.dev_fill_normal(wgu[e], synth.stream_key(wl.seed, synth.TAG_WGU, l, e), 0, wl.w_std)
                 synth.dev_fill_normal(wd[e], synth.stream_key(wl.seed, synth.TAG_WD, l, e), 0, wl.w_std)
-            t.update(wgu=wgu, wd=wd, wgu_scale=None, wd_scale=None)
+            t.update(wgu=self._pack(wgu, wl.expert_dtype, Er, 2 * I, H), wd=self._pack(wd, wl.expert_dtype, Er, H, I),
+                     wgu_scale=None, wd_scale=None)
         kind = wl.layer_kinds[l]
         kvt = _TORCH[wl.kv_dtype]
         if kind == "full":
