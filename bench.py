@@ -65,17 +65,6 @@ def algorithmic_bytes(dw):
     return wl.n_layers * per_layer_w + kv, wl.n_layers * per_layer_w, kv
 
 
-def time_steps(run, steps, warmup, torch):
-    for _ in range(warmup):
-        run()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        run()
-    torch.cuda.synchronize()
-    return (time.perf_counter() - t0) / steps * 1e3
-
-
 def cpu_baseline(name, n_tok_sample=None):
     """The CPU oracle on a bounded sample of the iteration: one sliding and one
     full layer for every sequence, inputs pre-generated, scaled to 36 layers."""
@@ -174,10 +163,12 @@ def main():
         if timed_cls is not None:
             B.spa_pipeline_time_kernel(pipe, timed_cls, True)
         torch.cuda.synchronize()
+        # a decode step needs the previous step's outputs, so steps are not
+        # overlapped: each one is enqueued after the previous one completed
         t0 = time.perf_counter()
         for _ in range(steps):
             run()
-        torch.cuda.synchronize()
+            torch.cuda.synchronize()
         ms = (time.perf_counter() - t0) / steps * 1e3
         kt = B.spa_pipeline_timing(pipe) if timed_cls is not None else (None, 0)
         B.spa_pipeline_destroy(pipe)

@@ -27,8 +27,15 @@ struct spa_pipeline {
   spa_pipeline_cfg cfg{};
   spa_pool* a = nullptr;   // null: temporal (everything on the caller stream)
   spa_pool* b = nullptr;
-  std::vector<hipEvent_t> evA, evB;   // [layer][micro]
+  std::vector<hipEvent_t> evA, evB;   // [layer][micro] (hand-offs when stream value waits are unavailable)
   hipEvent_t ev_start = nullptr, ev_end_a = nullptr, ev_end_b = nullptr;
+  // Hand-off counters in device memory: done_a[micro], done_b[micro]. The
+  // stage that finishes (layer l, microbatch j) of run r writes r*n_layers +
+  // l + 1 from its stream, the other stage's stream waits until the counter
+  // reaches it; values only grow, so nothing is ever reset.
+  uint64_t* flags = nullptr;
+  uint64_t runs = 0;
+  bool value_sync = false;
   int timed_cls = -1;
   std::vector<hipEvent_t> tevs, tpool;
   double t_sum_ms = 0.0;
@@ -169,6 +176,19 @@ spa_status spa_pipeline_create(spa_ctx* ctx, const spa_model_desc* m, const spa_
     e = hipEventCreateWithFlags(&p->evA[i], hipEventDisableTiming);
     if (e == hipSuccess) e = hipEventCreateWithFlags(&p->evB[i], hipEventDisableTiming);
   }
+  if (e == hipSuccess && stage_a) {
+    e = hipMalloc(&p->flags, sizeof(uint64_t) * 2 * cfg->n_micro);
+    if (e == hipSuccess) e = hipMemset(p->flags, 0, sizeof(uint64_t) * 2 * cfg->n_micro);
+    if (e == hipSuccess) e = hipDeviceSynchronize();
+    if (e == hipSuccess) {
+      // use stream value writes/waits when the runtime supports them on this memory
+      hipError_t t = hipStreamWriteValue64(stage_a->stream, p->flags, 0, 0);
+      if (t == hipSuccess) t = hipStreamWaitValue64(stage_b->stream, p->flags, 0, hipStreamWaitValueGte, ~0ull);
+      if (t == hipSuccess) t = hipDeviceSynchronize();
+      p->value_sync = t == hipSuccess;
+      if (t != hipSuccess) (void)hipGetLastError();
+    }
+  }
   if (e == hipSuccess) e = hipEventCreateWithFlags(&p->ev_start, hipEventDisableTiming);
   if (e == hipSuccess) e = hipEventCreateWithFlags(&p->ev_end_a, hipEventDisableTiming);
   if (e == hipSuccess) e = hipEventCreateWithFlags(&p->ev_end_b, hipEventDisableTiming);
@@ -233,21 +253,35 @@ spa_status spa_pipeline_run(spa_pipeline* p, const spa_layer* layers, const spa_
     SPA_HIP(hipStreamWaitEvent(sa, p->ev_start, 0));
     SPA_HIP(hipStreamWaitEvent(sb, p->ev_start, 0));
   }
+  const bool vs = !temporal && p->value_sync;
+  uint64_t* done_a = p->flags;
+  uint64_t* done_b = p->flags ? p->flags + n_micro : nullptr;
+  // a run that fails midway still consumes its values: the next run never
+  // mistakes one of its writes for its own
+  const uint64_t base = p->runs++ * (uint64_t)m->n_layers;
   for (int l = 0; l < m->n_layers; ++l) {
     for (int mu = 0; mu < n_micro; ++mu) {
       Slot s = slot_ptrs(W, ws, mu);
       const size_t ei = (size_t)l * n_micro + mu;
-      if (!temporal && l > 0) SPA_HIP(hipStreamWaitEvent(sa, p->evB[ei - n_micro], 0));
+      const uint64_t tick = base + (uint64_t)l + 1;   // hand-off value of (l, mu) in this run
+      if (!temporal && l > 0) {
+        if (vs) SPA_HIP(hipStreamWaitValue64(sa, done_b + mu, tick - 1, hipStreamWaitValueGte, ~0ull));
+        else SPA_HIP(hipStreamWaitEvent(sa, p->evB[ei - n_micro], 0));
+      }
       const spa_layer* next = l + 1 < m->n_layers ? &layers[l + 1] : nullptr;
       rc = run_segment_a(p->ctx, m, &layers[l], l, next, b, mu * bm, bm, W, s, router_in_a, l == 0, sa, thp);
       if (rc) return rc;
-      if (!temporal) {
+      if (vs) {
+        SPA_HIP(hipStreamWriteValue64(sa, done_a + mu, tick, 0));
+        SPA_HIP(hipStreamWaitValue64(sb, done_a + mu, tick, hipStreamWaitValueGte, ~0ull));
+      } else if (!temporal) {
         SPA_HIP(hipEventRecord(p->evA[ei], sa));
         SPA_HIP(hipStreamWaitEvent(sb, p->evA[ei], 0));
       }
       rc = run_segment_b(p->ctx, m, &layers[l], l, next, b, mu * bm, bm, W, s, router_in_a, sb, thp);
       if (rc) return rc;
-      if (!temporal) SPA_HIP(hipEventRecord(p->evB[ei], sb));
+      if (vs) SPA_HIP(hipStreamWriteValue64(sb, done_b + mu, tick, 0));
+      else if (!temporal) SPA_HIP(hipEventRecord(p->evB[ei], sb));
     }
   }
   if (!temporal) {
@@ -289,6 +323,7 @@ spa_status spa_pipeline_destroy(spa_pipeline* p) {
     if (e) (void)hipEventDestroy(e);
   for (hipEvent_t e : p->tevs) (void)hipEventDestroy(e);
   for (hipEvent_t e : p->tpool) (void)hipEventDestroy(e);
+  if (p->flags) (void)hipFree(p->flags);
   if (p->ev_start) (void)hipEventDestroy(p->ev_start);
   if (p->ev_end_a) (void)hipEventDestroy(p->ev_end_a);
   if (p->ev_end_b) (void)hipEventDestroy(p->ev_end_b);
