@@ -60,9 +60,12 @@
  *       different sequences must not overlap);
  *     sliding layers (ring): region (s * Hkv + g) * W * D holds W slots,
  *       position p in slot p % W (W a multiple of 32);
- *     K of slot t at region + t*D + d; V at region + (t/32)*32*D + d*32 +
- *     vslot(t%32), vslot(p) = 8*((p%16)/4) + 4*(p/16) + p%4 (d-major 32-slot
- *     blocks). Use spa_kv_io instead of computing offsets.
+ *     slots form 32-slot blocks of 32*D elements. K of slot t, dim d at
+ *     region + (t/32)*32*D + (d/c)*32*c + (t%32)*c + d%c, c = 64 bytes /
+ *     element size (column groups of 64 bytes, slot-major inside a group);
+ *     V at region + (t/32)*32*D + d*32 + vslot(t%32), vslot(p) =
+ *     8*((p%16)/4) + 4*(p/16) + p%4 (d-major). Use spa_kv_io instead of
+ *     computing offsets.
  *   A decode step of sequence s attends positions [0, L) (full) or
  *   [max(0, L-W), L) (sliding), L = kv_len[s], and writes its own K/V at L-1.
  */

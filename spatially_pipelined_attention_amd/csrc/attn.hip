@@ -23,7 +23,8 @@
 // Cache layouts (element offsets, D = 64):
 //   packed (full layers):  region(seq, g) = (kv_off[seq] * Hkv + g * cap[seq]) * D
 //   ring (sliding layers): region(seq, g) = (seq * Hkv + g) * W * D, slot = pos % W
-//   K at region + slot * D + d
+//   K at region + k_offset(slot, d, 64 / element size) (32-slot blocks of
+//     64-byte column groups, slot-major inside a group)
 //   V at region + (slot / 32) * 32 * D + d * 32 + v_slot(slot % 32)
 #include "common.h"
 #include "kernels.h"
@@ -80,7 +81,7 @@ __device__ __forceinline__ void load_block(BlockRegs<KVT>& br, const char* kreg,
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        const char* p = kb + ((16 * t + p16) * kD + 32 * h + 8 * q4) * 2;
+        const char* p = kb + (32 * 32 * h + (16 * t + p16) * 32 + 8 * q4) * 2;
         br.k[t][h] = stream ? ld16_stream(p) : ld16(p);
       }
 #pragma unroll
@@ -95,7 +96,7 @@ __device__ __forceinline__ void load_block(BlockRegs<KVT>& br, const char* kreg,
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int cc = 0; cc < 4; ++cc) {
-        const char* p = kb + ((16 * t + p16) * kD + 16 * cc + 4 * q4) * 4;
+        const char* p = kb + (32 * 16 * cc + (16 * t + p16) * 16 + 4 * q4) * 4;
         br.k[t][cc] = stream ? ld16_stream(p) : ld16(p);
       }
 #pragma unroll
@@ -207,8 +208,13 @@ __device__ __forceinline__ void attend_block(const BlockRegs<KVT>& br, const QRe
   }
 }
 
+#ifndef SPA_ATTN_RING
+#define SPA_ATTN_RING 2
+#endif
+constexpr int kRing = SPA_ATTN_RING;   // 32-position blocks in registers per wave
+
 template <int KVT>
-__global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
+__global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
   __shared__ float s_m[4][16];
   __shared__ float s_l[4][16];
   __shared__ float s_o[4][kD][17];
@@ -257,25 +263,33 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const bool stream = a.stream_kv != 0;
+#ifndef SPA_ATTN_NT
+#define SPA_ATTN_NT 1
+#endif
+  constexpr bool stream = SPA_ATTN_NT != 0;   // KV is read once: non-temporal loads
   if (nbw > 0) {
-    // Two register sets; the older one is always consumed first so the
-    // other's loads stay in flight while it is used. The steady-state body is
-    // straight-line; a block index past this wave's last block is clamped for
-    // the load (a re-read of data it just loaded) and fully masked by position.
+    // A ring of kRing register sets: a set is consumed, then refilled with
+    // the block kRing steps ahead, so kRing - 1 blocks of loads stay in flight
+    // while one is multiplied. The rounds are straight-line (scheduling
+    // barriers keep each refill behind its consumer); a block index past this
+    // wave's last block is clamped for the load and never attended.
     const int last = blk0 + 4 * (nbw - 1);
-    BlockRegs<KVT> A, B;
-    load_block<KVT>(A, kreg, vreg, blk0, lane, stream);
-    load_block<KVT>(B, kreg, vreg, min(blk0 + 4, last), lane, stream);
+    BlockRegs<KVT> rb[kRing];
+#pragma unroll
+    for (int r = 0; r < kRing; ++r) load_block<KVT>(rb[r], kreg, vreg, min(blk0 + 4 * r, last), lane, stream);
     int i = 0;
-    for (; i + 2 < nbw; i += 2) {
-      attend_block<KVT>(A, qr, blk0 + 4 * i, loc.n_valid, a.scale_log2, m_run, l_run, acc, lane);
-      load_block<KVT>(A, kreg, vreg, blk0 + 4 * (i + 2), lane, stream);
-      attend_block<KVT>(B, qr, blk0 + 4 * (i + 1), loc.n_valid, a.scale_log2, m_run, l_run, acc, lane);
-      load_block<KVT>(B, kreg, vreg, min(blk0 + 4 * (i + 3), last), lane, stream);
+    for (; i + kRing < nbw; i += kRing) {
+#pragma unroll
+      for (int r = 0; r < kRing; ++r) {
+        attend_block<KVT>(rb[r], qr, blk0 + 4 * (i + r), loc.n_valid, a.scale_log2, m_run, l_run, acc, lane);
+        __builtin_amdgcn_sched_barrier(0);
+        load_block<KVT>(rb[r], kreg, vreg, min(blk0 + 4 * (i + r + kRing), last), lane, stream);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
-    attend_block<KVT>(A, qr, blk0 + 4 * i, loc.n_valid, a.scale_log2, m_run, l_run, acc, lane);
-    if (i + 1 < nbw) attend_block<KVT>(B, qr, blk0 + 4 * (i + 1), loc.n_valid, a.scale_log2, m_run, l_run, acc, lane);
+#pragma unroll
+    for (int r = 0; r < kRing; ++r)
+      if (i + r < nbw) attend_block<KVT>(rb[r], qr, blk0 + 4 * (i + r), loc.n_valid, a.scale_log2, m_run, l_run, acc, lane);
   }
   l_run += __shfl_xor(l_run, 16, 64);
   l_run += __shfl_xor(l_run, 32, 64);

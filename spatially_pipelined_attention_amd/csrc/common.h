@@ -62,6 +62,13 @@ __device__ __forceinline__ T bitcast(S s) {
 // d-major V tile. Two 16-position halves are interleaved in runs of four so
 // that one lane's eight MFMA k-slots (positions 4q..4q+3 of both halves) are
 // one contiguous 16-byte run.
+// K element (slot, d) of a cache region (D = 64): 32-slot blocks, each split
+// into 64-byte column groups of kpe = 64 / element-size dims stored slot by
+// slot, so 16 slots of one column group are 1 KB of contiguous memory.
+__host__ __device__ __forceinline__ long long k_offset(int slot, int d, int kpe) {
+  return (long long)(slot >> 5) * 32 * 64 + (d / kpe) * 32 * kpe + (slot & 31) * kpe + d % kpe;
+}
+
 __host__ __device__ __forceinline__ int v_slot(int p) {
   return 8 * ((p & 15) >> 2) + 4 * (p >> 4) + (p & 3);
 }

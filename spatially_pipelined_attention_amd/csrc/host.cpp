@@ -306,8 +306,20 @@ static spa_status op_qkv(spa_ctx* ctx, const spa_model_desc* m, const spa_layer*
   return SPA_OK;
 }
 
+// Positions per attention workgroup: the largest of 4096 .. 512 that still
+// gives about four workgroups per CU at the batch's longest sequence (long
+// chunks stream longer and leave fewer partials to merge). Depends only on
+// shapes and the device, never on the CU pool.
+static int attn_chunk(const spa_model_desc* m, const spa_batch* b, int n_tok, int n_cus) {
+  for (int c = 4096; c > kAttnChunk; c >>= 1) {
+    const long long wgs = (long long)n_tok * m->n_kv_heads * ((b->max_kv_len + c - 1) / c);
+    if (wgs >= 4LL * n_cus) return c;
+  }
+  return kAttnChunk;
+}
+
 static AttnArgs attn_args(const spa_model_desc* m, const spa_layer* l, const spa_batch* b, int tok0, int n_tok,
-                          const void* q, void* o, const WsLayout& W, const Slot& s) {
+                          const void* q, void* o, const WsLayout& W, const Slot& s, int n_cus) {
   AttnArgs a;
   memset(&a, 0, sizeof(a));
   a.q = q;
@@ -326,8 +338,10 @@ static AttnArgs attn_args(const spa_model_desc* m, const spa_layer* l, const spa
   a.head_dim = m->head_dim;
   a.sinks = l->sinks;
   a.scale_log2 = (float)(1.0 / std::sqrt((double)m->head_dim) * 1.4426950408889634);
-  a.chunk = kAttnChunk;
-  a.max_chunks = l->kind == SPA_FULL ? W.max_chunks : (m->window + kAttnChunk - 1) / kAttnChunk;
+  a.chunk = l->kind == SPA_FULL ? attn_chunk(m, b, n_tok, n_cus) : kAttnChunk;
+  // the workspace holds max_chunks_for() partials at the smallest chunk
+  a.max_chunks = l->kind == SPA_FULL ? std::min(W.max_chunks, (b->max_kv_len + a.chunk - 1) / a.chunk)
+                                     : (m->window + kAttnChunk - 1) / kAttnChunk;
   a.part = s.attn_part;
   a.o = o;
   a.err = s.err;
@@ -335,9 +349,9 @@ static AttnArgs attn_args(const spa_model_desc* m, const spa_layer* l, const spa
   return a;
 }
 
-static spa_status op_attn(const spa_model_desc* m, const spa_layer* l, const spa_batch* b, int tok0, int n_tok,
+static spa_status op_attn(spa_ctx* ctx, const spa_model_desc* m, const spa_layer* l, const spa_batch* b, int tok0, int n_tok,
                           const void* q, void* o, const WsLayout& W, const Slot& s, hipStream_t st, TimingHook* th) {
-  AttnArgs a = attn_args(m, l, b, tok0, n_tok, q, o, W, s);
+  AttnArgs a = attn_args(m, l, b, tok0, n_tok, q, o, W, s, ctx->n_cus);
   HookScope hs(th, l->kind == SPA_FULL ? KC_ATTN_FULL : KC_ATTN_SLIDING, st);
   SPA_HIP(launch_attn(a, st));
   if (a.max_chunks > 1) SPA_HIP(launch_attn_merge(a, st));
@@ -526,7 +540,7 @@ spa_status run_segment_a(spa_ctx* ctx, const spa_model_desc* m, const spa_layer*
     if ((rc = op_combine(m, x, nullptr, nullptr, nullptr, none, n_tok, x, l->gamma1, s.xn, st, nullptr))) return rc;
   }
   if ((rc = op_qkv(ctx, m, l, b, tok0, n_tok, s.xn, s.q, s, st, th))) return rc;
-  if ((rc = op_attn(m, l, b, tok0, n_tok, s.q, s.o, W, s, st, th))) return rc;
+  if ((rc = op_attn(ctx, m, l, b, tok0, n_tok, s.q, s.o, W, s, st, th))) return rc;
   const bool fp8 = m->expert_dtype == SPA_E4M3, ebf = m->expert_dtype == SPA_BF16;
   if ((rc = op_oproj(ctx, m, l, x, s.o, n_tok, s.h, s.hn_f32, ebf ? s.hn_bf16 : nullptr, fp8 ? s.hn8 : nullptr,
                      fp8 ? s.hn8_scale : nullptr, s, st, th)))
@@ -780,7 +794,7 @@ spa_status spa_decode_attn(spa_ctx* ctx, const spa_model_desc* m, const spa_laye
   if (!q || !o_out || misaligned(q)) return fail(SPA_EINVAL, "q / o_out NULL or misaligned");
   const int max_kv = b->max_kv_len;
   SPA_OP_PROLOGUE(n_tok)
-  return op_attn(m, l, b, tok0, n_tok, q, o_out, W, s, st, nullptr);
+  return op_attn(ctx, m, l, b, tok0, n_tok, q, o_out, W, s, st, nullptr);
 }
 
 spa_status spa_out_proj(spa_ctx* ctx, const spa_model_desc* m, const spa_layer* l, const float* x, const void* o,

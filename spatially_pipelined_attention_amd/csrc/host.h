@@ -34,7 +34,10 @@ enum KClass : int {
   KC_ROUTER = 4, KC_GATEUP = 5, KC_DOWN = 6, KC_COMBINE = 7, KC_COUNT = 8
 };
 
-constexpr int kAttnChunk = 512;
+#ifndef SPA_ATTN_CHUNK
+#define SPA_ATTN_CHUNK 512
+#endif
+constexpr int kAttnChunk = SPA_ATTN_CHUNK;   // cached positions per attention workgroup (multiple of 128)
 
 // Byte layout of one microbatch slot of the workspace.
 struct SlotLayout {

@@ -103,7 +103,7 @@ __global__ __launch_bounds__(256) void k_qkv_finish(QkvFinishArgs a) {
     base = (a.kv_off[seq] * Hkv + (long long)g * a.kv_cap[seq]) * D;
     slot = pos;
   }
-  const long long off = is_k ? base + (long long)slot * D + d
+  const long long off = is_k ? base + k_offset(slot, d, a.kv_dtype == DT_BF16 ? 32 : 16)
                              : base + (long long)(slot >> 5) * 32 * D + (long long)d * 32 + v_slot(slot & 31);
   void* cache = is_k ? a.k_cache : a.v_cache;
   if (a.kv_dtype == DT_BF16) ((uint16_t*)cache)[off] = f32_to_bf16(v);
@@ -477,7 +477,7 @@ __global__ void k_kv_io(KvIoArgs a) {
       base = (a.kv_off[seq] * a.n_kv_heads + (long long)g * a.kv_cap[seq]) * D;
       slot = pos;
     }
-    const long long ko = base + (long long)slot * D + d;
+    const long long ko = base + k_offset(slot, d, a.kv_dtype == DT_BF16 ? 32 : 16);
     const long long vo = base + (long long)(slot >> 5) * 32 * D + (long long)d * 32 + v_slot(slot & 31);
     if (a.kv_dtype == DT_BF16) {
       uint16_t* kc = (uint16_t*)a.k_cache;
