@@ -283,7 +283,10 @@ spa_status spa_pool_destroy(spa_pool* p);
  * Microbatch mu is the contiguous token slice [mu*B/m, (mu+1)*B/m). Tasks are
  * dispatched region-major, then microbatch (a topological order of the data
  * edges, section 3.2); each stage runs its tasks in that order (stage FIFO);
- * A(l, mu) waits for B(l-1, mu) and B(l, mu) for A(l, mu) through events. */
+ * A(l, mu) waits for B(l-1, mu) and B(l, mu) for A(l, mu): the finishing
+ * stream writes a per-microbatch counter in device memory and the other
+ * stream waits for it (stream value write/wait; events where the runtime
+ * lacks them). */
 typedef struct spa_pipeline_cfg {
   int32_t cut;        /* 0 or 1 */
   int32_t n_micro;    /* m, divides the batch */
@@ -304,6 +307,44 @@ spa_status spa_pipeline_run(spa_pipeline* p, const spa_layer* layers, const spa_
 spa_status spa_pipeline_time_kernel(spa_pipeline* p, int32_t cls, int32_t enable);
 spa_status spa_pipeline_timing(spa_pipeline* p, double* mean_ms, int32_t* count);
 spa_status spa_pipeline_destroy(spa_pipeline* p);
+
+/* ---------------------------------------------------------------- tuner
+ * Section 4 (offline search, online selection): measure the iteration time
+ * T(theta) of every point of a small grid - cut x stage A's CU count x
+ * microbatch count - on the caller's own layers and batch, then refine the
+ * CU split of the best point with Algorithm 2 (spa_refine_allocation) using
+ * measured times as the objective. Temporal runs (cu_a = 0) of every
+ * microbatch count are measured too, for reference. Each point runs
+ * `warmup` untimed and `reps` timed iterations, each timed one after the
+ * other (the previous one complete); the median is kept.
+ * The runs update x and the KV caches like any iteration (restore them if
+ * they matter). The workspace must fit every point (the largest of
+ * spa_workspace_query() over the microbatch counts). */
+typedef struct spa_tune_space {
+  int32_t n_cuts;        /* 1 or 2 entries of cuts */
+  int32_t cuts[2];
+  int32_t n_micros;      /* 1..4 entries of micros, each dividing the batch */
+  int32_t micros[4];
+  int32_t cu_step;       /* grid spacing of stage A's CU count: a multiple of the XCD count */
+  int32_t cu_min;        /* smallest pool, a multiple of the XCD count */
+  int32_t warmup;
+  int32_t reps;
+  int32_t refine;        /* 1: Algorithm 2 on the best grid point's split */
+} spa_tune_space;
+
+typedef struct spa_tune_point {
+  int32_t cut;           /* -1 for temporal points */
+  int32_t n_micro;
+  int32_t cu_a;          /* 0 for temporal points */
+  double ms;             /* median iteration time */
+} spa_tune_point;
+
+/* best_out: the fastest spatial point. points_out (optional, max_points
+ * entries): every measured point in measurement order; n_points gets the
+ * total count (may exceed max_points). */
+spa_status spa_pipeline_tune(spa_ctx* ctx, const spa_model_desc* m, const spa_layer* layers, const spa_batch* b,
+                             void* ws, size_t ws_bytes, const spa_tune_space* space, spa_tune_point* best_out,
+                             spa_tune_point* points_out, int32_t max_points, int32_t* n_points, void* stream);
 
 /* ------------------------------------------------- schedule model (host)
  * Equations 1, 4 and 5 of the paper: binding of segment k (1-based) of K

@@ -61,6 +61,16 @@ class spa_pipeline_cfg(C.Structure):
     _fields_ = [("cut", C.c_int32), ("n_micro", C.c_int32)]
 
 
+class spa_tune_space(C.Structure):
+    _fields_ = [("n_cuts", C.c_int32), ("cuts", C.c_int32 * 2), ("n_micros", C.c_int32), ("micros", C.c_int32 * 4),
+                ("cu_step", C.c_int32), ("cu_min", C.c_int32), ("warmup", C.c_int32), ("reps", C.c_int32),
+                ("refine", C.c_int32)]
+
+
+class spa_tune_point(C.Structure):
+    _fields_ = [("cut", C.c_int32), ("n_micro", C.c_int32), ("cu_a", C.c_int32), ("ms", C.c_double)]
+
+
 OBJECTIVE_FN = C.CFUNCTYPE(C.c_double, C.POINTER(C.c_int32), C.c_int32, C.c_void_p)
 
 _P = C.c_void_p
@@ -101,6 +111,9 @@ _PROTOS = {
     "spa_pipeline_time_kernel": [_P, _I, _I],
     "spa_pipeline_timing": [_P, C.POINTER(C.c_double), C.POINTER(C.c_int32)],
     "spa_pipeline_destroy": [_P],
+    "spa_pipeline_tune": [_P, C.POINTER(spa_model_desc), C.POINTER(spa_layer), C.POINTER(spa_batch), _P, C.c_size_t,
+                          C.POINTER(spa_tune_space), C.POINTER(spa_tune_point), C.POINTER(spa_tune_point), _I,
+                          C.POINTER(C.c_int32), _P],
     "spa_sched_makespan": [_I, _I, _I, _I, C.POINTER(C.c_double), C.POINTER(C.c_double), C.POINTER(C.c_double),
                            C.POINTER(C.c_double)],
     "spa_sched_counts": [_I, _I, _I, _I, C.POINTER(C.c_int64), C.POINTER(C.c_int64)],
@@ -311,6 +324,15 @@ def spa_pipeline_timing(pipe):
 
 def spa_pipeline_destroy(pipe):
     _check(lib().spa_pipeline_destroy(pipe))
+
+
+def spa_pipeline_tune(ctx, m, layers, batch, ws, space: spa_tune_space, stream=None, max_points: int = 512):
+    best = spa_tune_point()
+    pts = (spa_tune_point * max_points)()
+    n = C.c_int32()
+    _check(lib().spa_pipeline_tune(ctx, C.byref(m), layers, C.byref(batch), *_ws(ws), C.byref(space), C.byref(best),
+                                   pts, max_points, C.byref(n), stream_handle(stream)))
+    return best, [pts[i] for i in range(min(n.value, max_points))]
 
 
 # ----------------------------------------------------------------------- schedule model

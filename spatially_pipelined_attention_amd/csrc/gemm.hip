@@ -73,7 +73,15 @@ __device__ __forceinline__ int w_rows_total(const GemmArgs& a) {
 }
 
 // ring depth: keeps the register budget of two workgroups per CU
-template <int CT, int MT> struct Ring { static constexpr int P = CT * MT > 16 ? 2 : (CT * MT > 8 ? 3 : 4); };
+#ifndef SPA_GEMM_RING_BIG
+#define SPA_GEMM_RING_BIG 2
+#endif
+#ifndef SPA_GEMM_RING_MID
+#define SPA_GEMM_RING_MID 3
+#endif
+template <int CT, int MT> struct Ring {
+  static constexpr int P = CT * MT > 16 ? SPA_GEMM_RING_BIG : (CT * MT > 8 ? SPA_GEMM_RING_MID : 4);
+};
 
 template <int WT, int EPI, int CT, int MT>
 __global__ __launch_bounds__(256, 2) void k_gemm(GemmArgs a) {
@@ -158,6 +166,11 @@ __global__ __launch_bounds__(256, 2) void k_gemm(GemmArgs a) {
   if (nks > 0) {
     u32x4 Wr[P][CT], Xr[P][MT];
     const u32x4 zero = {0u, 0u, 0u, 0u};
+    const int mt_live = __builtin_amdgcn_readfirstlane((rows_here + 15) >> 4);
+#pragma unroll
+    for (int p = 0; p < P; ++p)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) Xr[p][mt] = zero;
     // Wave w takes k-steps w + 4g of this split; the workgroups of a product
     // start at different groups g (a rotation fixed by the tile), so they do
     // not all read the same X lines at once. Summation order stays fixed.
@@ -174,7 +187,8 @@ __global__ __launch_bounds__(256, 2) void k_gemm(GemmArgs a) {
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct) Wr[slot][ct] = ld16_stream(wp[ct] + kk * 1024);
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) Xr[slot][mt] = ld16(xp[mt] + kk * a.x_kstride);
+      for (int mt = 0; mt < MT; ++mt)
+        if (mt < mt_live) Xr[slot][mt] = ld16(xp[mt] + kk * a.x_kstride);
     };
     auto compute = [&](int slot, int j) {
       int g = j + rot;
@@ -185,8 +199,10 @@ __global__ __launch_bounds__(256, 2) void k_gemm(GemmArgs a) {
       for (int ct = 0; ct < CT; ++ct) w[ct] = (live && wvalid[ct]) ? Wr[slot][ct] : zero;
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
+        if (mt < mt_live) {   // row tiles past the block's rows hold only padding
 #pragma unroll
-        for (int ct = 0; ct < CT; ++ct) acc[mt][ct] = mma_step<WT>(w[ct], Xr[slot][mt], acc[mt][ct]);
+          for (int ct = 0; ct < CT; ++ct) acc[mt][ct] = mma_step<WT>(w[ct], Xr[slot][mt], acc[mt][ct]);
+        }
     };
     // groups rounded up to the ring depth
     const int J = (ng + P - 1) / P * P;

@@ -73,7 +73,7 @@ static int pick_blk_rows(int need) {
 // Shape of one projection: rows per block (one W read serves them all), 64
 // output columns per tile, and the split-K factor that gives the chip enough
 // workgroups. Grouped (expert) products size the row block for the expected
-// rows per expert plus three standard deviations of uniform routing, so an
+// rows per expert plus two standard deviations of uniform routing, so an
 // expert's W is streamed once with high probability.
 GemmPlan plan_gemm(int kc, const spa_model_desc* m, int n_tok, int n_cus) {
   GemmPlan p{};
@@ -101,7 +101,7 @@ GemmPlan plan_gemm(int kc, const spa_model_desc* m, int n_tok, int n_cus) {
   } else {
     const int R = n_tok * m->top_k;
     const double mean = (double)R / groups;
-    p.blk_rows = pick_blk_rows(std::max(1, (int)std::ceil(mean + 3.0 * std::sqrt(mean))));
+    p.blk_rows = pick_blk_rows(std::max(1, (int)std::ceil(mean + 2.0 * std::sqrt(mean))));
     const int rb_all = (R + p.blk_rows - 1) / p.blk_rows;   // every row in one group
     p.rb_stride = std::min(groups * rb_all, rb_all + groups);
     p.part_rows = R;
@@ -352,8 +352,10 @@ static AttnArgs attn_args(const spa_model_desc* m, const spa_layer* l, const spa
 static spa_status op_attn(spa_ctx* ctx, const spa_model_desc* m, const spa_layer* l, const spa_batch* b, int tok0, int n_tok,
                           const void* q, void* o, const WsLayout& W, const Slot& s, hipStream_t st, TimingHook* th) {
   AttnArgs a = attn_args(m, l, b, tok0, n_tok, q, o, W, s, ctx->n_cus);
-  HookScope hs(th, l->kind == SPA_FULL ? KC_ATTN_FULL : KC_ATTN_SLIDING, st);
-  SPA_HIP(launch_attn(a, st));
+  {
+    HookScope hs(th, l->kind == SPA_FULL ? KC_ATTN_FULL : KC_ATTN_SLIDING, st);   // the attention kernel alone
+    SPA_HIP(launch_attn(a, st));
+  }
   if (a.max_chunks > 1) SPA_HIP(launch_attn_merge(a, st));
   return SPA_OK;
 }

@@ -332,3 +332,124 @@ spa_status spa_pipeline_destroy(spa_pipeline* p) {
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------------------
+// tuner
+namespace {
+
+struct TuneCtx {
+  spa_ctx* ctx;
+  const spa_model_desc* m;
+  const spa_layer* layers;
+  const spa_batch* b;
+  void* ws;
+  size_t ws_bytes;
+  const spa_tune_space* sp;
+  hipStream_t st;
+  hipEvent_t e0, e1;
+  std::vector<spa_tune_point> points;
+  spa_status err = SPA_OK;
+  int cut = 0, n_micro = 1;
+};
+
+// median time of reps iterations of one configuration (cu_a = 0: temporal)
+spa_status measure(TuneCtx& t, int cut, int n_micro, int cu_a, double* ms) {
+  spa_pool *pa = nullptr, *pb = nullptr;
+  spa_pipeline* pipe = nullptr;
+  spa_status rc = SPA_OK;
+  if (cu_a > 0) {
+    rc = spa_pool_create_split(t.ctx, 0, cu_a, &pa);
+    if (!rc) rc = spa_pool_create_split(t.ctx, cu_a / t.ctx->n_xcd, t.ctx->n_cus - cu_a, &pb);
+  }
+  spa_pipeline_cfg cfg{cut, n_micro};
+  if (!rc) rc = spa_pipeline_create(t.ctx, t.m, &cfg, pa, pb, &pipe);
+  std::vector<double> v;
+  for (int i = 0; !rc && i < t.sp->warmup + t.sp->reps; ++i) {
+    hipError_t e = hipEventRecord(t.e0, t.st);
+    if (e == hipSuccess) {
+      rc = spa_pipeline_run(pipe, t.layers, t.b, t.ws, t.ws_bytes, t.st);
+      if (!rc) e = hipEventRecord(t.e1, t.st);
+      if (!rc && e == hipSuccess) e = hipEventSynchronize(t.e1);
+    }
+    if (!rc && e != hipSuccess) rc = hip_fail(e, "tuner timing");
+    float f = 0.f;
+    if (!rc && i >= t.sp->warmup) {
+      e = hipEventElapsedTime(&f, t.e0, t.e1);
+      if (e != hipSuccess) rc = hip_fail(e, "tuner timing");
+      v.push_back(f);
+    }
+  }
+  if (pipe) spa_pipeline_destroy(pipe);
+  if (pa) spa_pool_destroy(pa);
+  if (pb) spa_pool_destroy(pb);
+  if (rc) return rc;
+  std::sort(v.begin(), v.end());
+  *ms = v[v.size() / 2];
+  t.points.push_back(spa_tune_point{cu_a > 0 ? cut : -1, n_micro, cu_a, *ms});
+  return SPA_OK;
+}
+
+double refine_objective(const int32_t* p, int32_t, void* user) {
+  TuneCtx& t = *static_cast<TuneCtx*>(user);
+  if (t.err) return 1e30;
+  double ms = 0.0;
+  spa_status rc = measure(t, t.cut, t.n_micro, p[0], &ms);
+  if (rc) {
+    t.err = rc;
+    return 1e30;
+  }
+  return ms;
+}
+
+}  // namespace
+
+extern "C" spa_status spa_pipeline_tune(spa_ctx* ctx, const spa_model_desc* m, const spa_layer* layers,
+                                        const spa_batch* b, void* ws, size_t ws_bytes, const spa_tune_space* sp,
+                                        spa_tune_point* best_out, spa_tune_point* points_out, int32_t max_points,
+                                        int32_t* n_points, void* stream) {
+  if (!ctx || !m || !layers || !b || !ws || !sp || !best_out) return fail(SPA_EINVAL, "bad argument");
+  const int nx = ctx->n_xcd;
+  if (sp->n_cuts < 1 || sp->n_cuts > 2 || sp->n_micros < 1 || sp->n_micros > 4) return fail(SPA_EINVAL, "bad space");
+  if (sp->cu_step < nx || sp->cu_step % nx || sp->cu_min < nx || sp->cu_min % nx || sp->reps < 1 || sp->warmup < 0)
+    return fail(SPA_EINVAL, "cu_step and cu_min must be positive multiples of the XCD count; reps >= 1");
+  for (int i = 0; i < sp->n_cuts; ++i)
+    if (sp->cuts[i] != 0 && sp->cuts[i] != 1) return fail(SPA_EINVAL, "cut must be 0 or 1");
+  for (int i = 0; i < sp->n_micros; ++i)
+    if (sp->micros[i] < 1 || b->batch % sp->micros[i]) return fail(SPA_EINVAL, "each microbatch count must divide the batch");
+  TuneCtx t{ctx, m, layers, b, ws, ws_bytes, sp, (hipStream_t)stream, nullptr, nullptr};
+  SPA_HIP(hipEventCreate(&t.e0));
+  hipError_t he = hipEventCreate(&t.e1);
+  if (he != hipSuccess) {
+    (void)hipEventDestroy(t.e0);
+    return hip_fail(he, "hipEventCreate");
+  }
+  spa_status rc = SPA_OK;
+  spa_tune_point best{0, 0, 0, 1e30};
+  for (int mi = 0; !rc && mi < sp->n_micros; ++mi) {
+    double ms;
+    rc = measure(t, 0, sp->micros[mi], 0, &ms);   // temporal reference
+    for (int ci = 0; !rc && ci < sp->n_cuts; ++ci)
+      for (int cu = sp->cu_min; !rc && cu <= ctx->n_cus - sp->cu_min; cu += sp->cu_step) {
+        rc = measure(t, sp->cuts[ci], sp->micros[mi], cu, &ms);
+        if (!rc && ms < best.ms) best = spa_tune_point{sp->cuts[ci], sp->micros[mi], cu, ms};
+      }
+  }
+  if (!rc && sp->refine && best.cu_a > 0) {
+    t.cut = best.cut;
+    t.n_micro = best.n_micro;
+    int32_t alloc[2] = {best.cu_a, ctx->n_cus - best.cu_a};
+    double v = 0.0;
+    int32_t evals = 0;
+    rc = spa_refine_allocation(2, ctx->n_cus, nx, sp->cu_min, alloc, refine_objective, &t, 0, &v, &evals);
+    if (!rc) rc = t.err;
+    if (!rc && v < best.ms) best = spa_tune_point{best.cut, best.n_micro, alloc[0], v};
+  }
+  (void)hipEventDestroy(t.e0);
+  (void)hipEventDestroy(t.e1);
+  if (rc) return rc;
+  *best_out = best;
+  if (n_points) *n_points = (int32_t)t.points.size();
+  if (points_out)
+    for (size_t i = 0; i < t.points.size() && (int)i < max_points; ++i) points_out[i] = t.points[i];
+  return SPA_OK;
+}

@@ -112,9 +112,49 @@ def test_repeat_runs_are_bitwise_identical(env):
 
 
 def test_one_microbatch_close_to_four(env):
-    x1, t1, _, _ = _run(env, 0, 1, None)
-    x4, t4, _, _ = _run(env, 0, 4, None)
-    x1 = x1.double().cpu().numpy()
-    x4 = x4.double().cpu().numpy()
-    hz.assert_close_rms(x4, x1, 1e-3, "T4 vs T1")
-    assert torch.equal(t1, t4)
+    """T1 and T4 differ only in rounding (the launch shapes change with the
+    microbatch size), so on one layer from the same input they agree within
+    the bf16 bar and pick the same experts (every router margin of the
+    generator's inputs clears 1e-3). Over several layers the rounding
+    differences may flip a pick of a low-margin token, so chains are compared
+    through the spatial == temporal property instead."""
+    B, dw, ctx = env["B"], env["dw"], env["ctx"]
+    m1 = B.spa_model_desc.from_buffer_copy(dw.m)
+    m1.n_layers = 1
+    out = []
+    for n_micro in (1, 4):
+        pipe = B.spa_pipeline_create(ctx, m1, B.spa_pipeline_cfg(0, n_micro), None, None)
+        ws = dw.workspace(n_micro=n_micro)
+        dw.reset_x()
+        dw.topk.zero_()
+        B.spa_pipeline_run(pipe, dw.layers_c, dw.batch, ws, torch.cuda.current_stream())
+        torch.cuda.synchronize()
+        B.spa_pipeline_destroy(pipe)
+        assert B.spa_workspace_errors(ctx, ws) == 0
+        out.append((dw.x.double().cpu().numpy(), dw.topk[0].clone()))
+    hz.assert_close_rms(out[1][0], out[0][0], hz.TOL["bf16"], "T4 vs T1, one layer")
+    assert torch.equal(torch.sort(out[0][1], dim=-1)[0], torch.sort(out[1][1], dim=-1)[0])
+
+
+def test_tuner_returns_a_measured_point_of_the_space(env):
+    B, dw, ctx = env["B"], env["dw"], env["ctx"]
+    sp = B.spa_tune_space(1, (B.C.c_int32 * 2)(0, 0), 1, (B.C.c_int32 * 4)(2, 0, 0, 0), 64, 64, 1, 2, 1)
+    ws = dw.workspace(n_micro=2)
+    best, pts = B.spa_pipeline_tune(ctx, dw.m, dw.layers_c, dw.batch, ws, sp, torch.cuda.current_stream())
+    grid = [p for p in pts if p.cu_a in (64, 128, 192)]
+    assert pts[0].cu_a == 0 and pts[0].cut == -1 and pts[0].ms > 0          # temporal reference first
+    assert len(grid) >= 3
+    assert best.cut == 0 and best.n_micro == 2 and best.cu_a % 8 == 0 and 64 <= best.cu_a <= 192
+    assert best.ms == min(p.ms for p in pts if p.cu_a > 0)
+    assert B.spa_workspace_errors(ctx, ws) == 0
+
+
+def test_tuner_rejects_bad_space(env):
+    B, dw, ctx = env["B"], env["dw"], env["ctx"]
+    ws = dw.workspace(n_micro=2)
+    bad = B.spa_tune_space(1, (B.C.c_int32 * 2)(0, 0), 1, (B.C.c_int32 * 4)(3, 0, 0, 0), 64, 64, 1, 2, 1)
+    with pytest.raises(B.SpaError):
+        B.spa_pipeline_tune(ctx, dw.m, dw.layers_c, dw.batch, ws, bad)   # 3 does not divide 64
+    bad = B.spa_tune_space(1, (B.C.c_int32 * 2)(0, 0), 1, (B.C.c_int32 * 4)(2, 0, 0, 0), 12, 64, 1, 2, 1)
+    with pytest.raises(B.SpaError):
+        B.spa_pipeline_tune(ctx, dw.m, dw.layers_c, dw.batch, ws, bad)   # step not a multiple of 8
