@@ -32,9 +32,12 @@ HBM_PEAK_GBPS = 8000.0
 TUNED = os.path.join(ROOT, "spatially_pipelined_attention_amd", "tuned.json")
 
 
-def traffic_from_profile(name, sched):
+def traffic_from_profile(name, tokens_per_launch):
     """HBM bytes per launch of the full-layer attention kernel from the committed
-    counter summary, or None when the kernel's sources or the schedule changed since."""
+    counter summary, or None when the kernel's sources or its launch shape (the
+    tokens of one microbatch) changed since. The counters are taken on the
+    temporal schedule with the same microbatches: its attention launches are
+    the spatial pipeline's, on one stream."""
     from spatially_pipelined_attention_amd import profiling
     path = os.path.join(ROOT, "profiles", f"k_attn_full_{name}_traffic.md")
     keys = profiling.read_keys(path)
@@ -43,7 +46,7 @@ def traffic_from_profile(name, sched):
     srcs = [os.path.join(ROOT, p.strip()) for p in keys.get("kernel_sources", "").split(",") if p.strip()]
     if not srcs or keys.get("kernel_source_digest") != profiling.source_digest(srcs):
         return None, path
-    if keys.get("schedule") != sched:
+    if keys.get("tokens_per_launch") != str(tokens_per_launch):
         return None, path
     return float(keys["traffic_bytes_per_launch"]), path
 
@@ -82,8 +85,8 @@ def algorithmic_bytes(dw):
 
 
 def cpu_baseline(name, n_tok_sample=None):
-    """The CPU oracle on a bounded sample of the iteration: one sliding and one
-    full layer for every sequence, inputs pre-generated, scaled to 36 layers."""
+    """The CPU oracle on the whole iteration (every layer, every sequence),
+    inputs generated outside the timed region, layer by layer."""
     from threadpoolctl import threadpool_info
     from oracle import layer as ol
     from spatially_pipelined_attention_amd import synth
@@ -93,30 +96,30 @@ def cpu_baseline(name, n_tok_sample=None):
     resample = load_resample(name)
     L = synth.kv_lengths(wl)[toks]
     x = synth.x_rows(wl, toks, resample)
-    layers = [0, 1]
-    params = {l: (synth.dense_weights(wl, l), {e: synth.expert_weights(wl, l, e) for e in range(wl.n_resident)})
-              for l in layers}
-    hist = {}
-    for l in layers:
+    dt = 0.0
+    for l in range(wl.n_layers):
+        dense = synth.dense_weights(wl, l)
+        experts = {e: synth.expert_weights(wl, l, e) for e in range(wl.n_resident)}
+        hist = {}
         for bi, b in enumerate(toks):
             lo, hi = ol.attention_window(wl.layer_kinds[l], int(L[bi]), wl.window)
-            hist[(l, bi)] = (lo, synth.kv_history(wl, l, b, lo, hi - 1))
-    t0 = time.perf_counter()
-    for l in layers:
-        dense, experts = params[l]
-        def history(bi, lo, hi, _l=l):
-            lo0, (K, V) = hist[(_l, bi)]
+            hist[bi] = (lo, synth.kv_history(wl, l, b, lo, hi - 1))
+
+        def history(bi, lo, hi):
+            lo0, (K, V) = hist[bi]
             return K[:, lo - lo0: hi - lo0], V[:, lo - lo0: hi - lo0]
+        t0 = time.perf_counter()
         rec = ol.layer_forward(hz.dims(wl), hz.numerics(wl), wl.layer_kinds[l], x, dense, experts.__getitem__, L,
                                history)
+        dt += time.perf_counter() - t0
         x = rec.x_next
-    dt = time.perf_counter() - t0
-    per_iter_s = dt * (wl.n_layers / len(layers)) * (wl.batch / len(toks))
+        del hist
+    scale = wl.batch / len(toks)
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    return {"value": per_iter_s * 1e6, "unit": "us", "cores": int(threads), "kind": "oracle",
-            "sample": f"layers 0-1 (one sliding + one full) of the {wl.n_layers}-layer iteration for "
-                      f"{len(toks)} of {wl.batch} sequences, measured {dt:.1f} s, scaled x{wl.n_layers // 2}"
-                      + ("" if len(toks) == wl.batch else f" and x{wl.batch / len(toks):.1f}")}
+    return {"value": dt * scale * 1e6, "unit": "us", "cores": int(threads), "kind": "oracle",
+            "sample": f"the whole {wl.n_layers}-layer iteration for {len(toks)} of {wl.batch} sequences "
+                      f"(layer compute timed, input generation excluded), {dt:.1f} s"
+                      + ("" if len(toks) == wl.batch else f", scaled x{scale:.1f}")}
 
 
 def main():
@@ -206,9 +209,9 @@ def main():
     if args.schedule == "spatial":
         ms, (k_ms, k_n) = run_schedule("reported", cfg["cut"], m, cfg["cu_a"], ws, timed_cls=B.KC_ATTN_FULL)
         sched = f"spatial cut={cfg['cut']} m={m} cu_a={cfg['cu_a']}/{n_cus}"
-    else:
-        ms, (k_ms, k_n) = run_schedule("reported", 0, 1, None, ws1, timed_cls=B.KC_ATTN_FULL)
-        sched = "temporal T1"
+    else:   # temporal with the configured microbatch count (--micro 1 for T1)
+        ms, (k_ms, k_n) = run_schedule("reported", cfg["cut"], m, None, ws, timed_cls=B.KC_ATTN_FULL)
+        sched = f"temporal m={m}"
     errs = B.spa_workspace_errors(ctx, ws)
     if args.copy_calibration > 0:
         src = torch.empty(args.copy_calibration, dtype=torch.uint8, device="cuda")
@@ -220,11 +223,11 @@ def main():
 
     total_b, w_b, kv_b = algorithmic_bytes(dw)
     full_layers = [l for l in range(wl.n_layers) if wl.layer_kinds[l] == "full"]
-    n_micro_rep = m if args.schedule == "spatial" else 1
+    n_micro_rep = m
     kv_full = sum(dw.algorithmic_kv_bytes(l) for l in full_layers)
     bytes_per_launch = kv_full / len(full_layers) / n_micro_rep
     achieved = bytes_per_launch / (k_ms * 1e-3) / 1e9 if k_ms else None
-    traffic, traffic_src = traffic_from_profile(name, sched)
+    traffic, traffic_src = traffic_from_profile(name, wl.batch // m)
     us = ms * 1e3
     gbps = total_b / (ms * 1e-3) / 1e9
     out = {
@@ -241,7 +244,7 @@ def main():
         "algorithmic_GB_per_iter": round(total_b / 1e9, 3),
         "tokens_per_s": round(wl.batch / (ms * 1e-3), 1), "per_user_tokens_per_s": round(1 / (ms * 1e-3), 2),
         "schedules_ms": {k: round(v["ms"], 4) for k, v in results.items()},
-        "roofline": {"bound": "hbm", "kernel": "decode attention, full layers (k_attn<bf16>)",
+        "roofline": {"bound": "hbm", "kernel": "spa::k_attn<1, 1> (full-layer decode attention, bf16 KV)",
                      "achieved": round(achieved, 1) if achieved else None, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4) if achieved else None,
                      "traffic": int(traffic) if traffic else None,

@@ -39,10 +39,10 @@ struct KvLoc {
   bool ok;
 };
 
-__device__ __forceinline__ KvLoc kv_locate(const AttnArgs& a, int seq, int g) {
+__device__ __forceinline__ KvLoc kv_locate(const AttnArgs& a, int seq, int g, int kind) {
   KvLoc r;
   const int L = a.kv_len[seq];
-  if (a.kv_kind == KV_RING) {
+  if (kind == KV_RING) {
     r.base = ((long long)seq * a.n_kv_heads + g) * a.window * kD;
     r.n_valid = min(L, a.window);
     r.ok = L >= 1;
@@ -213,7 +213,9 @@ __device__ __forceinline__ void attend_block(const BlockRegs<KVT>& br, const QRe
 #endif
 constexpr int kRing = SPA_ATTN_RING;   // 32-position blocks in registers per wave
 
-template <int KVT>
+// KIND (ring or packed cache) is a template parameter so that sliding and
+// full layers are distinct kernels in profiles.
+template <int KVT, int KIND>
 __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
   __shared__ float s_m[4][16];
   __shared__ float s_l[4][16];
@@ -224,7 +226,7 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
   const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int seq = a.tok0 + b;
   const int G = a.n_q_heads / a.n_kv_heads;
-  const KvLoc loc = kv_locate(a, seq, g);
+  const KvLoc loc = kv_locate(a, seq, g, KIND);
   if (!loc.ok) {
     if (c == 0 && tid == 0 && a.err) atomicOr(a.err, ERR_KV_LEN);
     return;
@@ -353,7 +355,7 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
   const int g = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   const int seq = a.tok0 + b;
   const int G = a.n_q_heads / a.n_kv_heads;
-  const KvLoc loc = kv_locate(a, seq, g);
+  const KvLoc loc = kv_locate(a, seq, g, a.kv_kind);
   if (!loc.ok) return;
   const int n_chunks = (loc.n_valid + a.chunk - 1) / a.chunk;
   if (n_chunks <= 1 || n_chunks > a.max_chunks) return;
@@ -400,8 +402,13 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
 
 hipError_t launch_attn(const AttnArgs& a, hipStream_t st) {
   dim3 grid(a.max_chunks, a.n_kv_heads, a.n_tok);
-  if (a.kv_dtype == DT_BF16) hipLaunchKernelGGL(k_attn<DT_BF16>, grid, dim3(256), 0, st, a);
-  else hipLaunchKernelGGL(k_attn<DT_F32>, grid, dim3(256), 0, st, a);
+  if (a.kv_dtype == DT_BF16) {
+    if (a.kv_kind == KV_PACKED) hipLaunchKernelGGL((k_attn<DT_BF16, KV_PACKED>), grid, dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((k_attn<DT_BF16, KV_RING>), grid, dim3(256), 0, st, a);
+  } else {
+    if (a.kv_kind == KV_PACKED) hipLaunchKernelGGL((k_attn<DT_F32, KV_PACKED>), grid, dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((k_attn<DT_F32, KV_RING>), grid, dim3(256), 0, st, a);
+  }
   return hipGetLastError();
 }
 
