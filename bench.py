@@ -67,10 +67,11 @@ def tuned_config(name):
     return {"cut": 0, "n_micro": 2, "cu_a": 128}
 
 
-def algorithmic_bytes(dw):
-    """Bytes one T1 iteration must move: every layer's dense + router weights,
-    the experts that receive rows (all resident experts here), the attended KV
-    window of every sequence, and the new K/V rows written."""
+def algorithmic_bytes(dw, n_micro=1):
+    """Bytes one iteration of a schedule with n_micro microbatches must move:
+    every layer's dense and router weights and the experts that receive rows
+    (all resident experts here), once per microbatch; the attended KV window
+    of every sequence; and the new K/V rows written."""
     wl = dw.wl
     wb = 2 if wl.w_dtype == "bf16" else 4
     eb = {"bf16": 2, "f32": 4, "e4m3": 1}[wl.expert_dtype]
@@ -81,7 +82,7 @@ def algorithmic_bytes(dw):
         experts += wl.n_resident * (2 * I + H) * 4
     per_layer_w = dense + experts
     kv = sum(dw.algorithmic_kv_bytes(l) for l in range(wl.n_layers))
-    return wl.n_layers * per_layer_w + kv, wl.n_layers * per_layer_w, kv
+    return wl.n_layers * per_layer_w * n_micro + kv, wl.n_layers * per_layer_w * n_micro, kv
 
 
 def cpu_baseline(name, n_tok_sample=None):
@@ -221,7 +222,8 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    total_b, w_b, kv_b = algorithmic_bytes(dw)
+    total_b, w_b, kv_b = algorithmic_bytes(dw, m)
+    min_b = algorithmic_bytes(dw, 1)[0]
     full_layers = [l for l in range(wl.n_layers) if wl.layer_kinds[l] == "full"]
     n_micro_rep = m
     kv_full = sum(dw.algorithmic_kv_bytes(l) for l in full_layers)
@@ -242,6 +244,8 @@ def main():
                    "schedule": sched},
         "hbm_GBps": round(gbps, 1), "hbm_pct_peak": round(100 * gbps / HBM_PEAK_GBPS, 1),
         "algorithmic_GB_per_iter": round(total_b / 1e9, 3),
+        "hbm_GBps_min_bytes": round(min_b / (ms * 1e-3) / 1e9, 1),   # the iteration's bytes with weights read once
+        "min_GB_per_iter": round(min_b / 1e9, 3),
         "tokens_per_s": round(wl.batch / (ms * 1e-3), 1), "per_user_tokens_per_s": round(1 / (ms * 1e-3), 2),
         "schedules_ms": {k: round(v["ms"], 4) for k, v in results.items()},
         "roofline": {"bound": "hbm", "kernel": "spa::k_attn<1, 1> (full-layer decode attention, bf16 KV)",

@@ -26,6 +26,8 @@
 //   K at region + k_offset(slot, d, 64 / element size) (32-slot blocks of
 //     64-byte column groups, slot-major inside a group)
 //   V at region + (slot / 32) * 32 * D + d * 32 + v_slot(slot % 32)
+#include <hip/hip_ext.h>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -400,14 +402,22 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
   }
 }
 
-hipError_t launch_attn(const AttnArgs& a, hipStream_t st) {
+template <int KVT, int KIND>
+static void launch_attn_t(const AttnArgs& a, dim3 grid, hipStream_t st, hipEvent_t start, hipEvent_t stop) {
+  if (start || stop)
+    hipExtLaunchKernelGGL((k_attn<KVT, KIND>), grid, dim3(256), 0, st, start, stop, 0, a);
+  else
+    hipLaunchKernelGGL((k_attn<KVT, KIND>), grid, dim3(256), 0, st, a);
+}
+
+hipError_t launch_attn(const AttnArgs& a, hipStream_t st, hipEvent_t start, hipEvent_t stop) {
   dim3 grid(a.max_chunks, a.n_kv_heads, a.n_tok);
   if (a.kv_dtype == DT_BF16) {
-    if (a.kv_kind == KV_PACKED) hipLaunchKernelGGL((k_attn<DT_BF16, KV_PACKED>), grid, dim3(256), 0, st, a);
-    else hipLaunchKernelGGL((k_attn<DT_BF16, KV_RING>), grid, dim3(256), 0, st, a);
+    if (a.kv_kind == KV_PACKED) launch_attn_t<DT_BF16, KV_PACKED>(a, grid, st, start, stop);
+    else launch_attn_t<DT_BF16, KV_RING>(a, grid, st, start, stop);
   } else {
-    if (a.kv_kind == KV_PACKED) hipLaunchKernelGGL((k_attn<DT_F32, KV_PACKED>), grid, dim3(256), 0, st, a);
-    else hipLaunchKernelGGL((k_attn<DT_F32, KV_RING>), grid, dim3(256), 0, st, a);
+    if (a.kv_kind == KV_PACKED) launch_attn_t<DT_F32, KV_PACKED>(a, grid, st, start, stop);
+    else launch_attn_t<DT_F32, KV_RING>(a, grid, st, start, stop);
   }
   return hipGetLastError();
 }

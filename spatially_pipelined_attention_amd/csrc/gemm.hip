@@ -245,32 +245,46 @@ __global__ __launch_bounds__(256, 2) void k_gemm(GemmArgs a) {
 
   // wave 0 holds the tile: row mt*16 + lo16, columns ct*16 + c4 + i
   const int c4 = (lane >> 4) * 4;
+  // E4M3: per-output-channel weight scales and per-row activation scales
+  float wsc[CT][4];
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) wsc[ct][i] = 1.f;
+  if constexpr (WT == DT_E4M3) {
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int wr = w_row_of<EPI, CT>(a, nb, ct * 16 + c4 + i);
+        wsc[ct][i] = wr < w_rows_total<EPI>(a) ? a.w_scale[(long long)grp * a.ws_gstride + wr] : 0.f;
+      }
+  }
   if constexpr (EPI == EPI_PARTIAL) {
-    // split s, row (dispatch or token row), padded column: [S][part_rows][part_ld]
+    // split s, row (dispatch or token row), padded column: [S][part_rows][part_ld];
+    // every split is scaled, so the splits' sum is the scaled product
     float* pt = a.part + ((long long)s * a.part_rows + r0 + rb * BR) * a.part_ld + nb * TC + c4;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       const int m = mt * 16 + lo16;
       if (m < rows_here) {
+        float xs = 1.f;
+        if constexpr (WT == DT_E4M3) {
+          const long long orow = r0 + rb * BR + m;
+          xs = a.x_scale[a.row_src ? a.row_src[orow] : orow];
+        }
 #pragma unroll
-        for (int ct = 0; ct < CT; ++ct) *reinterpret_cast<f32x4*>(pt + (long long)m * a.part_ld + ct * 16) = acc[mt][ct];
+        for (int ct = 0; ct < CT; ++ct) {
+          f32x4 v = acc[mt][ct];
+          if constexpr (WT == DT_E4M3) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v[i] *= wsc[ct][i] * xs;
+          }
+          *reinterpret_cast<f32x4*>(pt + (long long)m * a.part_ld + ct * 16) = v;
+        }
       }
     }
   } else {
-    float wsc[CT][4];
-#pragma unroll
-    for (int ct = 0; ct < CT; ++ct)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) wsc[ct][i] = 1.f;
-    if constexpr (WT == DT_E4M3) {
-#pragma unroll
-      for (int ct = 0; ct < CT; ++ct)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int wr = w_row_of<EPI, CT>(a, nb, ct * 16 + c4 + i);
-          wsc[ct][i] = wr < w_rows_total<EPI>(a) ? a.w_scale[(long long)grp * a.ws_gstride + wr] : 0.f;
-        }
-    }
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       const int m = mt * 16 + lo16;

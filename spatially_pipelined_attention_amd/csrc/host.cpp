@@ -219,12 +219,19 @@ struct HookScope {
   TimingHook* th;
   hipStream_t st;
   bool on;
-  HookScope(TimingHook* t, int cls, hipStream_t s) : th(t), st(s), on(t && t->cls == cls && t->evs && t->pool) {
-    if (on) {
-      th->evs->push_back(take());
-      (void)hipEventRecord(th->evs->back(), st);
-    }
+  bool ext;          // the launch itself records the pair (hipExtLaunchKernel timestamps)
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  HookScope(TimingHook* t, int cls, hipStream_t s, bool in_launch = false)
+      : th(t), st(s), on(t && t->cls == cls && t->evs && t->pool), ext(in_launch) {
+    if (!on) return;
+    e0 = take();
+    e1 = take();
+    th->evs->push_back(e0);
+    th->evs->push_back(e1);
+    if (!ext) (void)hipEventRecord(e0, st);
   }
+  hipEvent_t start() const { return on && ext ? e0 : nullptr; }
+  hipEvent_t stop() const { return on && ext ? e1 : nullptr; }
   hipEvent_t take() {
     if (th->pool->empty()) {
       hipEvent_t e;
@@ -236,10 +243,7 @@ struct HookScope {
     return e;
   }
   ~HookScope() {
-    if (on) {
-      th->evs->push_back(take());
-      (void)hipEventRecord(th->evs->back(), st);
-    }
+    if (on && !ext) (void)hipEventRecord(e1, st);
   }
 };
 
@@ -353,8 +357,9 @@ static spa_status op_attn(spa_ctx* ctx, const spa_model_desc* m, const spa_layer
                           const void* q, void* o, const WsLayout& W, const Slot& s, hipStream_t st, TimingHook* th) {
   AttnArgs a = attn_args(m, l, b, tok0, n_tok, q, o, W, s, ctx->n_cus);
   {
-    HookScope hs(th, l->kind == SPA_FULL ? KC_ATTN_FULL : KC_ATTN_SLIDING, st);   // the attention kernel alone
-    SPA_HIP(launch_attn(a, st));
+    // the attention kernel alone, timed by its own dispatch (start/stop events of the launch)
+    HookScope hs(th, l->kind == SPA_FULL ? KC_ATTN_FULL : KC_ATTN_SLIDING, st, true);
+    SPA_HIP(launch_attn(a, st, hs.start(), hs.stop()));
   }
   if (a.max_chunks > 1) SPA_HIP(launch_attn_merge(a, st));
   return SPA_OK;

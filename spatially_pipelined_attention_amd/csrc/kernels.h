@@ -159,7 +159,8 @@ struct AttnArgs {
   int* err;
   int stream_kv;            // non-temporal KV loads
 };
-hipError_t launch_attn(const AttnArgs& a, hipStream_t st);
+// start/stop (optional): events the runtime records at the kernel's own start and end
+hipError_t launch_attn(const AttnArgs& a, hipStream_t st, hipEvent_t start = nullptr, hipEvent_t stop = nullptr);
 // merge of the chunk partials of multi-chunk sequences (single-chunk ones are final already)
 hipError_t launch_attn_merge(const AttnArgs& a, hipStream_t st);
 
