@@ -26,51 +26,17 @@
 // elements of a 64-byte k-step in the same lane order, so the product is the
 // plain dot product.
 #include "common.h"
+#include "gemm_common.h"
 #include "kernels.h"
 
 namespace spa {
 
 constexpr int kStepBytes = 64;     // one k-step of one row
+#ifndef SPA_GEMM_W_NT
+#define SPA_GEMM_W_NT 1
+#endif
+constexpr bool kWStream = SPA_GEMM_W_NT != 0;   // weights are read once per launch: non-temporal loads
 constexpr int kRedBytes = 3 * 4 * 64 * 16;     // LDS for the wave reduction (one 16-row tile, <= 4 fragments)
-
-template <int WT> struct WTraits;
-template <> struct WTraits<DT_BF16> { static constexpr int ks = 32; static constexpr int esz = 2; };
-template <> struct WTraits<DT_F32> { static constexpr int ks = 16; static constexpr int esz = 4; };
-template <> struct WTraits<DT_E4M3> { static constexpr int ks = 64; static constexpr int esz = 1; };
-
-template <int WT>
-__device__ __forceinline__ f32x4 mma_step(u32x4 w, u32x4 x, f32x4 acc) {
-  if constexpr (WT == DT_BF16) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(bitcast<bf16x8>(w), bitcast<bf16x8>(x), acc, 0, 0, 0);
-  } else if constexpr (WT == DT_F32) {
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(w[u]), __uint_as_float(x[u]), acc, 0, 0, 0);
-    return acc;
-  } else {
-    long w0 = (long)((uint64_t)w[0] | ((uint64_t)w[1] << 32));
-    long w1 = (long)((uint64_t)w[2] | ((uint64_t)w[3] << 32));
-    long x0 = (long)((uint64_t)x[0] | ((uint64_t)x[1] << 32));
-    long x1 = (long)((uint64_t)x[2] | ((uint64_t)x[3] << 32));
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(w0, x0, acc, 0, 0, 0);
-    return __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(w1, x1, acc, 0, 0, 0);
-  }
-}
-
-// W row feeding tile column c (0..16*CT-1) of column tile nb; a SwiGLU tile
-// pairs 8*CT gate rows with the 8*CT up rows of the same outputs.
-template <int EPI, int CT>
-__device__ __forceinline__ int w_row_of(const GemmArgs& a, int nb, int c) {
-  constexpr int HC = 8 * CT;
-  if constexpr (EPI == EPI_SWIGLU) return c < HC ? nb * HC + c : a.inter + nb * HC + (c - HC);
-  else return nb * 16 * CT + c;
-}
-
-template <int EPI>
-__device__ __forceinline__ int w_rows_total(const GemmArgs& a) {
-  if constexpr (EPI == EPI_SWIGLU) return 2 * a.inter;
-  else return a.N;
-}
 
 // ring depth: keeps the register budget of two workgroups per CU
 #ifndef SPA_GEMM_RING_BIG
@@ -92,39 +58,9 @@ __global__ __launch_bounds__(256, 2) void k_gemm(GemmArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
-  // block -> (split, column tile, row block); grouped products number the
-  // non-empty row blocks of all groups in group order
-  int bid = blockIdx.x;
-  const int s = bid % a.S;
-  bid /= a.S;
-  const int nb = bid % a.n_tiles;
-  const int blk = bid / a.n_tiles;
-  int grp = 0, rb = blk, r0 = 0, nrows = a.n_rows;
-  if (a.group_off) {
-    // wave-parallel scan of the per-group block counts (two groups per lane)
-    const int g0 = 2 * lane, g1 = 2 * lane + 1;
-    const int n0 = g0 < a.n_groups ? a.group_off[g0 + 1] - a.group_off[g0] : 0;
-    const int n1 = g1 < a.n_groups ? a.group_off[g1 + 1] - a.group_off[g1] : 0;
-    const int c0 = (n0 + BR - 1) / BR, c1 = (n1 + BR - 1) / BR;
-    int incl = c0 + c1;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int t = __shfl_up(incl, o, 64);
-      if (lane >= o) incl += t;
-    }
-    const int excl = incl - c0 - c1;
-    const unsigned long long hit = __ballot(blk >= excl && blk < incl);
-    if (hit == 0ull) return;                       // past the last non-empty block
-    const int hl = __builtin_ctzll(hit);
-    const int e = __shfl(excl, hl, 64), cc0 = __shfl(c0, hl, 64);
-    grp = blk - e < cc0 ? 2 * hl : 2 * hl + 1;
-    rb = blk - e < cc0 ? blk - e : blk - e - cc0;
-    grp = __builtin_amdgcn_readfirstlane(grp);
-    rb = __builtin_amdgcn_readfirstlane(rb);
-    r0 = a.group_off[grp];
-    nrows = a.group_off[grp + 1] - r0;
-  }
-  if (nrows <= rb * BR) return;
+  int s, nb, grp, rb, r0, nrows;
+  if (!gemm_block(a, BR, lane, &s, &nb, &grp, &rb, &r0, &nrows)) return;
+  const int blk = rb;   // rotation seed
   const int rows_here = min(BR, nrows - rb * BR);
 
   constexpr int KS = WTraits<WT>::ks;
@@ -185,7 +121,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm(GemmArgs a) {
     auto load = [&](int slot, int j) {
       const long long kk = kstep(j);
 #pragma unroll
-      for (int ct = 0; ct < CT; ++ct) Wr[slot][ct] = ld16_stream(wp[ct] + kk * 1024);
+      for (int ct = 0; ct < CT; ++ct) Wr[slot][ct] = kWStream ? ld16_stream(wp[ct] + kk * 1024) : ld16(wp[ct] + kk * 1024);
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
         if (mt < mt_live) Xr[slot][mt] = ld16(xp[mt] + kk * a.x_kstride);

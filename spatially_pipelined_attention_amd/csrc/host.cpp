@@ -397,9 +397,18 @@ static spa_status op_oproj(spa_ctx* ctx, const spa_model_desc* m, const spa_laye
   return SPA_OK;
 }
 
+// The expert input rows (bf16 / E4M3 / fp32, by expert dtype) of a slot.
+static const void* expert_input(const spa_model_desc* m, const Slot& s) {
+  return m->expert_dtype == SPA_BF16 ? (const void*)s.hn_bf16
+         : m->expert_dtype == SPA_E4M3 ? (const void*)s.hn8
+                                       : (const void*)s.hn_f32;
+}
+
+// Router GEMV, top-k and the dispatch permutation. gather: also gather the
+// slot's expert input rows into dispatch order (s.xe_perm) in the same kernel.
 static spa_status op_route(spa_ctx* ctx, const spa_model_desc* m, const spa_layer* l, const float* hn, int n_tok,
                            float* logits, const spa_route_bufs& r, int32_t* topk_rec, const Slot& s, hipStream_t st,
-                           TimingHook* th) {
+                           TimingHook* th, bool gather = false) {
   const GemmPlan p = plan_gemm(KC_ROUTER, m, n_tok, ctx->n_cus);
   GemmArgs a = gemm_args(p, s, n_tok);
   a.W = l->wr;
@@ -423,6 +432,15 @@ static spa_status op_route(spa_ctx* ctx, const spa_model_desc* m, const spa_laye
   ra.row_tok = r.row_tok;
   ra.row_slot = r.row_slot;
   ra.inv = r.inv;
+  if (gather) {
+    const bool fp8 = m->expert_dtype == SPA_E4M3;
+    ra.gsrc = expert_input(m, s);
+    ra.gK = m->hidden;
+    ra.gesz = esz_of(m->expert_dtype);
+    ra.gdst = s.xe_perm;
+    ra.gsrc_scale = fp8 ? s.hn8_scale : nullptr;
+    ra.gdst_scale = fp8 ? s.xe_perm_scale : nullptr;
+  }
   HookScope hs(th, KC_ROUTER, st);
   SPA_HIP(launch_gemm(DT_F32, EPI_PARTIAL, a, st));
   SPA_HIP(launch_route(ra, st));
@@ -433,7 +451,7 @@ static spa_status op_route(spa_ctx* ctx, const spa_model_desc* m, const spa_laye
 // (bf16 / fp32 / E4M3 with xe_scale). Leaves y plain (S = 1) or as partials.
 static spa_status op_expert(spa_ctx* ctx, const spa_model_desc* m, const spa_layer* l, const void* xe,
                             const float* xe_scale, int n_tok, const spa_route_bufs& r, float* y_plain, const Slot& s,
-                            hipStream_t st, TimingHook* th, GemmPlan* down_plan) {
+                            hipStream_t st, TimingHook* th, GemmPlan* down_plan, bool gathered = false) {
   const int H = m->hidden, I = m->inter, R = n_tok * m->top_k;
   const bool fp8 = m->expert_dtype == SPA_E4M3;
   {
@@ -458,8 +476,9 @@ static spa_status op_expert(spa_ctx* ctx, const spa_model_desc* m, const spa_lay
     a.out_kmajor_rows = R;
     a.out_dtype = m->expert_dtype == SPA_BF16 ? DT_BF16 : DT_F32;
     HookScope hs(th, KC_GATEUP, st);
-    SPA_HIP(launch_gather_kmajor(xe, r.row_tok, R, H, esz_of(m->expert_dtype), s.xe_perm, fp8 ? xe_scale : nullptr,
-                                 fp8 ? s.xe_perm_scale : nullptr, st));
+    if (!gathered)
+      SPA_HIP(launch_gather_kmajor(xe, r.row_tok, R, H, esz_of(m->expert_dtype), s.xe_perm, fp8 ? xe_scale : nullptr,
+                                   fp8 ? s.xe_perm_scale : nullptr, st));
     SPA_HIP(launch_gemm(m->expert_dtype, EPI_SWIGLU, a, st));
   }
   {
@@ -554,7 +573,7 @@ spa_status run_segment_a(spa_ctx* ctx, const spa_model_desc* m, const spa_layer*
     return rc;
   if (with_router) {
     int32_t* rec = b->topk_out ? b->topk_out + ((size_t)layer_index * b->batch + tok0) * m->top_k : nullptr;
-    if ((rc = op_route(ctx, m, l, s.hn_f32, n_tok, s.logits, s.route, rec, s, st, th))) return rc;
+    if ((rc = op_route(ctx, m, l, s.hn_f32, n_tok, s.logits, s.route, rec, s, st, th, true))) return rc;
   }
   return SPA_OK;
 }
@@ -567,13 +586,12 @@ spa_status run_segment_b(spa_ctx* ctx, const spa_model_desc* m, const spa_layer*
   float* x = b->x + (size_t)tok0 * m->hidden;
   if (!with_router) {
     int32_t* rec = b->topk_out ? b->topk_out + ((size_t)layer_index * b->batch + tok0) * m->top_k : nullptr;
-    if ((rc = op_route(ctx, m, l, s.hn_f32, n_tok, s.logits, s.route, rec, s, st, th))) return rc;
+    if ((rc = op_route(ctx, m, l, s.hn_f32, n_tok, s.logits, s.route, rec, s, st, th, true))) return rc;
   }
-  const void* xe = m->expert_dtype == SPA_BF16   ? (const void*)s.hn_bf16
-                   : m->expert_dtype == SPA_E4M3 ? (const void*)s.hn8
-                                                 : (const void*)s.hn_f32;
+  // the router's permutation kernel already gathered the expert rows
   GemmPlan dp{};
-  if ((rc = op_expert(ctx, m, l, xe, s.hn8_scale, n_tok, s.route, s.y, s, st, th, &dp))) return rc;
+  if ((rc = op_expert(ctx, m, l, expert_input(m, s), s.hn8_scale, n_tok, s.route, s.y, s, st, th, &dp, true)))
+    return rc;
   const bool plain = dp.epi == EPI_STORE;
   return op_combine(m, s.h, plain ? s.y : nullptr, plain ? nullptr : &dp, &s, s.route, n_tok, x,
                     next ? next->gamma1 : nullptr, s.xn, st, th);

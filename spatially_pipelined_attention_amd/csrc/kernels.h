@@ -108,6 +108,13 @@ struct RouteArgs {
   int* row_tok;
   int* row_slot;
   int* inv;
+  // optional gather of the expert input rows into dispatch order (k-step-major)
+  const void* gsrc;         // [n_tok][gK] row-major, element size gesz
+  int gK;
+  int gesz;
+  void* gdst;               // [gK*gesz/64][n_tok*k][64 bytes]
+  const float* gsrc_scale;  // E4M3: per source row
+  float* gdst_scale;        // E4M3: per dispatch row
 };
 hipError_t launch_route(const RouteArgs& a, hipStream_t st);
 

@@ -14,6 +14,8 @@
 //                    order plus residual, and the next layer's RMSNorm;
 // plus row conversion, KV row I/O, counter fill and a CU placement probe.
 // Every reduction runs in a fixed order, so results never depend on timing.
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -48,19 +50,32 @@ __device__ __forceinline__ float block_max(float v, float* red) {
 constexpr int kMaxSplits = 16;   // plan_gemm never splits k more than this
 
 // Element (row r, column c) of a split product, summed over the splits in
-// split order. All loads are issued before the first add (clamped index,
-// masked value: adding +0 leaves every partial sum unchanged).
+// split order. SM is a compile-time bound on the split count: all SM loads
+// are issued before the first add (clamped index, masked value: adding +0
+// leaves every partial sum unchanged), so the kernels are instantiated for
+// SM = 1, 2, 4, 8, 16 and launched with the smallest bound that holds.
+template <int SM>
 __device__ __forceinline__ float part_sum(const PartView& pv, int r, int c) {
   const float* p = pv.part + (long long)r * pv.ld + c;
   const long long sstride = (long long)pv.rows * pv.ld;
-  float v[kMaxSplits];
+  float v[SM];
 #pragma unroll
-  for (int s = 0; s < kMaxSplits; ++s) v[s] = p[min(s, pv.S - 1) * sstride];
+  for (int s = 0; s < SM; ++s) v[s] = p[min(s, pv.S - 1) * sstride];
   float acc = v[0];
 #pragma unroll
-  for (int s = 1; s < kMaxSplits; ++s) acc += s < pv.S ? v[s] : 0.f;
+  for (int s = 1; s < SM; ++s) acc += s < pv.S ? v[s] : 0.f;
   return acc;
 }
+
+// launch KERNEL<SM> with the smallest SM >= S
+#define SPA_LAUNCH_SPLITS(S, KERNEL, GRID, BLOCK, LDS, ST, ...)                      \
+  do {                                                                               \
+    if ((S) <= 1) hipLaunchKernelGGL((KERNEL<1>), GRID, BLOCK, LDS, ST, __VA_ARGS__);      \
+    else if ((S) <= 2) hipLaunchKernelGGL((KERNEL<2>), GRID, BLOCK, LDS, ST, __VA_ARGS__); \
+    else if ((S) <= 4) hipLaunchKernelGGL((KERNEL<4>), GRID, BLOCK, LDS, ST, __VA_ARGS__); \
+    else if ((S) <= 8) hipLaunchKernelGGL((KERNEL<8>), GRID, BLOCK, LDS, ST, __VA_ARGS__); \
+    else hipLaunchKernelGGL((KERNEL<16>), GRID, BLOCK, LDS, ST, __VA_ARGS__);              \
+  } while (0)
 
 // smallest power of two s with amax <= 448 s (1 for amax == 0)
 __device__ __forceinline__ float pow2_scale_448(float amax) {
@@ -74,6 +89,7 @@ __device__ __forceinline__ float pow2_scale_448(float amax) {
 }
 
 // ---------------------------------------------------------------------------
+template <int SM>
 __global__ __launch_bounds__(256) void k_qkv_finish(QkvFinishArgs a) {
   const int r = blockIdx.x;
   const int c = blockIdx.y * 256 + threadIdx.x;
@@ -85,7 +101,7 @@ __global__ __launch_bounds__(256) void k_qkv_finish(QkvFinishArgs a) {
   const int pos = L - 1;
   const bool ok = (L >= 1) && (a.kv_kind == KV_RING || L <= a.kv_cap[seq]);
   if (!ok && c == 0 && a.err) atomicOr(a.err, ERR_KV_LEN);
-  const float v = part_sum(a.pv, r, c);
+  const float v = part_sum<SM>(a.pv, r, c);
   if (c < QD) {
     if (a.kv_dtype == DT_BF16) ((uint16_t*)a.q_out)[(long long)r * QD + c] = f32_to_bf16(v);
     else ((float*)a.q_out)[(long long)r * QD + c] = v;
@@ -112,11 +128,12 @@ __global__ __launch_bounds__(256) void k_qkv_finish(QkvFinishArgs a) {
 
 hipError_t launch_qkv_finish(const QkvFinishArgs& a, hipStream_t st) {
   const int N = (a.n_q_heads + 2 * a.n_kv_heads) * a.head_dim;
-  hipLaunchKernelGGL(k_qkv_finish, dim3(a.n_tok, (N + 255) / 256), dim3(256), 0, st, a);
+  SPA_LAUNCH_SPLITS(a.pv.S, k_qkv_finish, dim3(a.n_tok, (N + 255) / 256), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
+template <int SM>
 __global__ __launch_bounds__(kRowThreads) void k_oproj_finish(OprojFinishArgs a) {
   __shared__ float red[kRowThreads / 64];
   const int r = blockIdx.x;
@@ -128,7 +145,7 @@ __global__ __launch_bounds__(kRowThreads) void k_oproj_finish(OprojFinishArgs a)
     const int c = threadIdx.x + kRowThreads * i;
     h[i] = 0.f;
     if (c < a.H) {
-      h[i] = a.x[row + c] + part_sum(a.pv, r, c);
+      h[i] = a.x[row + c] + part_sum<SM>(a.pv, r, c);
       a.h_out[row + c] = h[i];
     }
     ss += h[i] * h[i];
@@ -160,7 +177,7 @@ __global__ __launch_bounds__(kRowThreads) void k_oproj_finish(OprojFinishArgs a)
 }
 
 hipError_t launch_oproj_finish(const OprojFinishArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL(k_oproj_finish, dim3(a.n_tok), dim3(kRowThreads), 0, st, a);
+  SPA_LAUNCH_SPLITS(a.pv.S, k_oproj_finish, dim3(a.n_tok), dim3(kRowThreads), 0, st, a);
   return hipGetLastError();
 }
 
@@ -169,6 +186,7 @@ hipError_t launch_oproj_finish(const OprojFinishArgs& a, hipStream_t st) {
 // lane + 64 j (summed over the splits in split order); k rounds of a wave
 // argmax on (value, index) - larger value wins, equal values go to the lower
 // index - then the softmax over the k picked logits.
+template <int SM>
 __global__ __launch_bounds__(256) void k_route_topk(RouteArgs a) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + wave;
@@ -180,7 +198,7 @@ __global__ __launch_bounds__(256) void k_route_topk(RouteArgs a) {
     const int e = lane + 64 * j;
     v[j] = -INFINITY;
     if (e < E) {
-      v[j] = part_sum(a.pv, t, e);
+      v[j] = part_sum<SM>(a.pv, t, e);
       a.logits[(long long)t * E + e] = v[j];
     }
   }
@@ -232,10 +250,13 @@ __global__ __launch_bounds__(256) void k_route_permute(RouteArgs a) {
   const int tid = threadIdx.x;
   const int k = a.k, P = a.n_tok * k, E_res = a.E_res;
   int* grp = (int*)lds;                         // [P]
-  int* counts = grp + P;                        // [E_res]
+  int* rtok = grp + P;                          // [P] token of each dispatch row
+  int* counts = rtok + P;                       // [E_res]
   int* offs = counts + E_res;                   // [E_res + 1]
   const int W64 = (P + 63) >> 6;
   unsigned long long* masks = (unsigned long long*)(((uintptr_t)(offs + E_res + 1) + 7) & ~(uintptr_t)7);
+  // every workgroup computes the whole (small) permutation; workgroup 0 stores it
+  const bool store = blockIdx.x == 0;
   for (int p = tid; p < P; p += 256) grp[p] = a.topk_idx[p] % E_res;
   for (int i = tid; i < E_res; i += 256) counts[i] = 0;
   for (int i = tid; i < E_res * W64; i += 256) masks[i] = 0ull;
@@ -255,7 +276,8 @@ __global__ __launch_bounds__(256) void k_route_permute(RouteArgs a) {
     offs[E_res] = s;
   }
   __syncthreads();
-  for (int i = tid; i <= E_res; i += 256) a.offsets[i] = offs[i];
+  if (store)
+    for (int i = tid; i <= E_res; i += 256) a.offsets[i] = offs[i];
   for (int p = tid; p < P; p += 256) {
     const int g = grp[p];
     const unsigned long long* mk = masks + g * W64;
@@ -263,30 +285,62 @@ __global__ __launch_bounds__(256) void k_route_permute(RouteArgs a) {
     for (int w = 0; w < (p >> 6); ++w) rank += __popcll(mk[w]);
     rank += __popcll(mk[p >> 6] & ((1ull << (p & 63)) - 1ull));
     const int row = offs[g] + rank;
-    a.row_tok[row] = p / k;
-    a.row_slot[row] = p % k;
-    a.inv[p] = row;
+    rtok[row] = p / k;
+    if (store) {
+      a.row_tok[row] = p / k;
+      a.row_slot[row] = p % k;
+      a.inv[p] = row;
+    }
+  }
+  if (!a.gsrc) return;
+  __syncthreads();
+  // expert input rows in dispatch order, k-step-major: 16-byte chunk i of
+  // [kstep][row][4] <- its source chunk, the chunks dealt over the workgroups
+  const int ksteps = a.gK * a.gesz / 64;
+  const long long total = (long long)ksteps * P * 4;
+  const u32x4* src = (const u32x4*)a.gsrc;
+  u32x4* dst = (u32x4*)a.gdst;
+  for (long long i = (long long)blockIdx.x * 256 + tid; i < total; i += (long long)gridDim.x * 256) {
+    const int q = (int)(i & 3);
+    const long long t = i >> 2;
+    const int r = (int)(t % P);
+    const int ks = (int)(t / P);
+    const long long srow = rtok[r];
+    dst[i] = src[(srow * ksteps + ks) * 4 + q];
+    if (a.gdst_scale && ks == 0 && q == 0) a.gdst_scale[r] = a.gsrc_scale[srow];
   }
 }
 
 int route_lds_bytes(int n_tok, int k, int E_res) {
   const int P = n_tok * k;
-  return (P + 2 * E_res + 1) * 4 + 16 + E_res * ((P + 63) / 64) * 8;
+  return (2 * P + 2 * E_res + 1) * 4 + 16 + E_res * ((P + 63) / 64) * 8;
 }
 
 hipError_t launch_route(const RouteArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL(k_route_topk, dim3((a.n_tok + 3) / 4), dim3(256), 0, st, a);
+  SPA_LAUNCH_SPLITS(a.pv.S, k_route_topk, dim3((a.n_tok + 3) / 4), dim3(256), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_route_permute, dim3(1), dim3(256), route_lds_bytes(a.n_tok, a.k, a.E_res), st, a);
+  static bool lds_raised = false;   // the permutation may need more than the default 64 KB of LDS
+  if (!lds_raised) {
+    (void)hipFuncSetAttribute((const void*)k_route_permute, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    lds_raised = true;
+  }
+  int wgs = 1;
+  if (a.gsrc) {   // enough workgroups for the gather: ~8 chunks per thread, at most 64
+    const long long chunks = (long long)a.gK * a.gesz / 16 * a.n_tok * a.k;
+    wgs = (int)std::min<long long>(64, std::max<long long>(1, chunks / (256 * 8)));
+  }
+  hipLaunchKernelGGL(k_route_permute, dim3(wgs), dim3(256), route_lds_bytes(a.n_tok, a.k, a.E_res), st, a);
   return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
+template <int SM>
 __device__ __forceinline__ float y_elem(const CombineArgs& a, int row, int c) {
-  return a.y ? a.y[(long long)row * a.H + c] : part_sum(a.ypv, row, c);
+  return a.y ? a.y[(long long)row * a.H + c] : part_sum<SM>(a.ypv, row, c);
 }
 
+template <int SM>
 __global__ __launch_bounds__(kRowThreads) void k_combine(CombineArgs a) {
   __shared__ float red[kRowThreads / 64];
   __shared__ float s_w[8];
@@ -308,7 +362,7 @@ __global__ __launch_bounds__(kRowThreads) void k_combine(CombineArgs a) {
     if (c < a.H) {
       float x = a.h[row + c];
       for (int s = 0; s < a.k; ++s) {
-        x += s_w[s] * y_elem(a, s_row[s], c);
+        x += s_w[s] * y_elem<SM>(a, s_row[s], c);
       }
       v[i] = x;
       a.x_out[row + c] = x;
@@ -330,21 +384,22 @@ __global__ __launch_bounds__(kRowThreads) void k_combine(CombineArgs a) {
 }
 
 hipError_t launch_combine(const CombineArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL(k_combine, dim3(a.n_tok), dim3(kRowThreads), 0, st, a);
+  SPA_LAUNCH_SPLITS(a.y ? 1 : a.ypv.S, k_combine, dim3(a.n_tok), dim3(kRowThreads), 0, st, a);
   return hipGetLastError();
 }
 
 // Rows of a grouped split product summed over the splits: out[r][c] for
 // dispatch rows r (grouped by expert through group offsets).
+template <int SM>
 __global__ __launch_bounds__(256) void k_part_rows(CombineArgs a) {
   const int r = blockIdx.x;
   if (r >= a.y_group_off[a.y_n_groups]) return;
-  for (int c = threadIdx.x; c < a.H; c += 256) a.x_out[(long long)r * a.H + c] = y_elem(a, r, c);
+  for (int c = threadIdx.x; c < a.H; c += 256) a.x_out[(long long)r * a.H + c] = y_elem<SM>(a, r, c);
 }
 
 hipError_t launch_part_rows(const CombineArgs& a, int max_rows, hipStream_t st) {
   if (max_rows <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_part_rows, dim3(max_rows), dim3(256), 0, st, a);
+  SPA_LAUNCH_SPLITS(a.y ? 1 : a.ypv.S, k_part_rows, dim3(max_rows), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
