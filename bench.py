@@ -133,6 +133,7 @@ def main():
     ap.add_argument("--cut", type=int, default=None)
     ap.add_argument("--micro", type=int, default=None)
     ap.add_argument("--cu-a", type=int, default=None, help="CUs of stage A (multiple of 8)")
+    ap.add_argument("--cu-a-sliding", type=int, default=None, help="CUs of stage A in sliding layers")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--quick", action="store_true", help="skip the comparison schedules")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
@@ -144,7 +145,7 @@ def main():
 
     import torch
     from spatially_pipelined_attention_amd import binding as B, synth
-    from spatially_pipelined_attention_amd.workload import DeviceWorkload
+    from spatially_pipelined_attention_amd.workload import DeviceWorkload, Pipeline
 
     name = args.workload
     wl = synth.WORKLOADS[name]
@@ -155,6 +156,9 @@ def main():
         cfg["n_micro"] = args.micro
     if args.cu_a is not None:
         cfg["cu_a"] = args.cu_a
+        cfg["cu_a_sliding"] = args.cu_a
+    if args.cu_a_sliding is not None:
+        cfg["cu_a_sliding"] = args.cu_a_sliding
     m = cfg["n_micro"]
 
     t_setup = time.perf_counter()
@@ -167,23 +171,19 @@ def main():
     ws1 = dw.workspace(n_micro=1)
     stream = torch.cuda.current_stream()
 
-    def make_pipe(cut, n_micro, cu_a):
-        if cu_a is None:
-            return B.spa_pipeline_create(ctx, dw.m, B.spa_pipeline_cfg(cut, n_micro), None, None), []
-        pa = B.spa_pool_create_split(ctx, 0, cu_a)
-        pb = B.spa_pool_create_split(ctx, cu_a // 8, n_cus - cu_a)
-        return B.spa_pipeline_create(ctx, dw.m, B.spa_pipeline_cfg(cut, n_micro), pa, pb), [pa, pb]
+    def make_pipe(cut, n_micro, cu_a, cu_s=None):
+        return Pipeline(ctx, dw.m, {"cut": cut, "n_micro": n_micro, "cu_a": cu_a or 0, "cu_a_sliding": cu_s})
 
     results = {}
 
-    def run_schedule(label, cut, n_micro, cu_a, wsx, timed_cls=None, steps=args.steps, warmup=args.warmup):
-        pipe, pools = make_pipe(cut, n_micro, cu_a)
-        run = lambda: B.spa_pipeline_run(pipe, dw.layers_c, dw.batch, wsx, stream)
+    def run_schedule(label, cut, n_micro, cu_a, wsx, timed_cls=None, steps=args.steps, warmup=args.warmup, cu_s=None):
+        pipe = make_pipe(cut, n_micro, cu_a, cu_s)
+        run = lambda: B.spa_pipeline_run(pipe.h, dw.layers_c, dw.batch, wsx, stream)
         for _ in range(warmup):
             run()
         torch.cuda.synchronize()
         if timed_cls is not None:
-            B.spa_pipeline_time_kernel(pipe, timed_cls, True)
+            B.spa_pipeline_time_kernel(pipe.h, timed_cls, True)
         torch.cuda.synchronize()
         # a decode step needs the previous step's outputs, so steps are not
         # overlapped: each one is enqueued after the previous one completed
@@ -192,10 +192,8 @@ def main():
             run()
             torch.cuda.synchronize()
         ms = (time.perf_counter() - t0) / steps * 1e3
-        kt = B.spa_pipeline_timing(pipe) if timed_cls is not None else (None, 0)
-        B.spa_pipeline_destroy(pipe)
-        for p in pools:
-            B.spa_pool_destroy(p)
+        kt = B.spa_pipeline_timing(pipe.h) if timed_cls is not None else (None, 0)
+        pipe.close()
         results[label] = {"ms": ms, "kernel_ms": kt[0], "kernel_n": kt[1]}
         return ms, kt
 
@@ -206,10 +204,13 @@ def main():
         if m > 1:
             run_schedule(f"temporal_T{m}", cfg["cut"], m, None, ws)
         if args.schedule == "temporal":
-            run_schedule("spatial", cfg["cut"], m, cfg["cu_a"], ws)
+            run_schedule("spatial", cfg["cut"], m, cfg["cu_a"], ws, cu_s=cfg.get("cu_a_sliding"))
     if args.schedule == "spatial":
-        ms, (k_ms, k_n) = run_schedule("reported", cfg["cut"], m, cfg["cu_a"], ws, timed_cls=B.KC_ATTN_FULL)
-        sched = f"spatial cut={cfg['cut']} m={m} cu_a={cfg['cu_a']}/{n_cus}"
+        ms, (k_ms, k_n) = run_schedule("reported", cfg["cut"], m, cfg["cu_a"], ws, timed_cls=B.KC_ATTN_FULL,
+                                       cu_s=cfg.get("cu_a_sliding"))
+        cu_s = cfg.get("cu_a_sliding") or cfg["cu_a"]
+        sched = (f"spatial cut={cfg['cut']} m={m} cu_a={cfg['cu_a']}/{n_cus}"
+                 + ("" if cu_s == cfg["cu_a"] else f" (sliding layers {cu_s}/{n_cus})"))
     else:   # temporal with the configured microbatch count (--micro 1 for T1)
         ms, (k_ms, k_n) = run_schedule("reported", cfg["cut"], m, None, ws, timed_cls=B.KC_ATTN_FULL)
         sched = f"temporal m={m}"

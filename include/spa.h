@@ -294,6 +294,15 @@ typedef struct spa_pipeline_cfg {
 
 spa_status spa_pipeline_create(spa_ctx* ctx, const spa_model_desc* m, const spa_pipeline_cfg* cfg, spa_pool* stage_a,
                                spa_pool* stage_b, spa_pipeline** out);
+/* The same pipeline with a CU split per layer kind: full layers run stage A
+ * on a_full and stage B on b_full, sliding layers on a_sliding / b_sliding
+ * (full layers are attention-heavy, sliding layers MoE-heavy). The pools of
+ * one kind must be disjoint; pools of different kinds may overlap (tasks of
+ * adjacent layers then share CUs). spa_pipeline_create(a, b) is the case
+ * a_full = a_sliding = a, b_full = b_sliding = b. */
+spa_status spa_pipeline_create_kinds(spa_ctx* ctx, const spa_model_desc* m, const spa_pipeline_cfg* cfg,
+                                     spa_pool* a_full, spa_pool* b_full, spa_pool* a_sliding, spa_pool* b_sliding,
+                                     spa_pipeline** out);
 /* Run one decode iteration; joins `caller_stream` at both ends (the pipeline
  * starts after work already queued there, and work queued there afterwards
  * starts after the iteration). */
@@ -310,10 +319,10 @@ spa_status spa_pipeline_destroy(spa_pipeline* p);
 
 /* ---------------------------------------------------------------- tuner
  * Section 4 (offline search, online selection): measure the iteration time
- * T(theta) of every point of a small grid - cut x stage A's CU count x
- * microbatch count - on the caller's own layers and batch, then refine the
- * CU split of the best point with Algorithm 2 (spa_refine_allocation) using
- * measured times as the objective. Temporal runs (cu_a = 0) of every
+ * T(theta) of every point of a small grid - cut x stage A's CU count (per
+ * layer kind with per_kind) x microbatch count - on the caller's own layers
+ * and batch, then refine the CU split(s) of the best point with Algorithm 2
+ * (spa_refine_allocation) using measured times as the objective. Temporal runs (cu_a = 0) of every
  * microbatch count are measured too, for reference. Each point runs
  * `warmup` untimed and `reps` timed iterations, each timed one after the
  * other (the previous one complete); the median is kept.
@@ -329,13 +338,15 @@ typedef struct spa_tune_space {
   int32_t cu_min;        /* smallest pool, a multiple of the XCD count */
   int32_t warmup;
   int32_t reps;
-  int32_t refine;        /* 1: Algorithm 2 on the best grid point's split */
+  int32_t refine;        /* 1: Algorithm 2 on the best grid point's split(s) */
+  int32_t per_kind;      /* 1: search stage A's CUs for full and sliding layers separately */
 } spa_tune_space;
 
 typedef struct spa_tune_point {
   int32_t cut;           /* -1 for temporal points */
   int32_t n_micro;
-  int32_t cu_a;          /* 0 for temporal points */
+  int32_t cu_a;          /* stage A's CUs (full layers); 0 for temporal points */
+  int32_t cu_a_sliding;  /* stage A's CUs for sliding layers (= cu_a without per_kind) */
   double ms;             /* median iteration time */
 } spa_tune_point;
 

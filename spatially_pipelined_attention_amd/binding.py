@@ -64,11 +64,12 @@ class spa_pipeline_cfg(C.Structure):
 class spa_tune_space(C.Structure):
     _fields_ = [("n_cuts", C.c_int32), ("cuts", C.c_int32 * 2), ("n_micros", C.c_int32), ("micros", C.c_int32 * 4),
                 ("cu_step", C.c_int32), ("cu_min", C.c_int32), ("warmup", C.c_int32), ("reps", C.c_int32),
-                ("refine", C.c_int32)]
+                ("refine", C.c_int32), ("per_kind", C.c_int32)]
 
 
 class spa_tune_point(C.Structure):
-    _fields_ = [("cut", C.c_int32), ("n_micro", C.c_int32), ("cu_a", C.c_int32), ("ms", C.c_double)]
+    _fields_ = [("cut", C.c_int32), ("n_micro", C.c_int32), ("cu_a", C.c_int32), ("cu_a_sliding", C.c_int32),
+                ("ms", C.c_double)]
 
 
 OBJECTIVE_FN = C.CFUNCTYPE(C.c_double, C.POINTER(C.c_int32), C.c_int32, C.c_void_p)
@@ -107,6 +108,8 @@ _PROTOS = {
     "spa_pool_destroy": [_P],
     "spa_pipeline_create": [_P, C.POINTER(spa_model_desc), C.POINTER(spa_pipeline_cfg), _P, _P,
                             C.POINTER(C.c_void_p)],
+    "spa_pipeline_create_kinds": [_P, C.POINTER(spa_model_desc), C.POINTER(spa_pipeline_cfg), _P, _P, _P, _P,
+                                  C.POINTER(C.c_void_p)],
     "spa_pipeline_run": [_P, C.POINTER(spa_layer), C.POINTER(spa_batch), _P, C.c_size_t, _P],
     "spa_pipeline_time_kernel": [_P, _I, _I],
     "spa_pipeline_timing": [_P, C.POINTER(C.c_double), C.POINTER(C.c_int32)],
@@ -304,6 +307,13 @@ def spa_pool_destroy(pool):
 def spa_pipeline_create(ctx, m, cfg: spa_pipeline_cfg, pool_a, pool_b) -> int:
     h = C.c_void_p()
     _check(lib().spa_pipeline_create(ctx, C.byref(m), C.byref(cfg), pool_a, pool_b, C.byref(h)))
+    return h.value
+
+
+def spa_pipeline_create_kinds(ctx, m, cfg: spa_pipeline_cfg, a_full, b_full, a_sliding, b_sliding) -> int:
+    h = C.c_void_p()
+    _check(lib().spa_pipeline_create_kinds(ctx, C.byref(m), C.byref(cfg), a_full, b_full, a_sliding, b_sliding,
+                                           C.byref(h)))
     return h.value
 
 

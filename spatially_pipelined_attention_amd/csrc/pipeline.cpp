@@ -27,6 +27,9 @@ struct spa_pipeline {
   spa_pipeline_cfg cfg{};
   spa_pool* a = nullptr;   // null: temporal (everything on the caller stream)
   spa_pool* b = nullptr;
+  spa_pool* ak[2] = {nullptr, nullptr};   // stage pools per layer kind (spa_layer_kind)
+  spa_pool* bk[2] = {nullptr, nullptr};
+  std::vector<hipEvent_t> ev_end;         // one per distinct pool stream
   std::vector<hipEvent_t> evA, evB;   // [layer][micro] (hand-offs when stream value waits are unavailable)
   hipEvent_t ev_start = nullptr, ev_end_a = nullptr, ev_end_b = nullptr;
   // Hand-off counters in device memory: done_a[micro], done_b[micro]. The
@@ -145,29 +148,40 @@ spa_status spa_pool_destroy(spa_pool* p) {
   return SPA_OK;
 }
 
-spa_status spa_pipeline_create(spa_ctx* ctx, const spa_model_desc* m, const spa_pipeline_cfg* cfg, spa_pool* stage_a,
-                               spa_pool* stage_b, spa_pipeline** out) {
+static bool pools_overlap(const spa_pool* x, const spa_pool* y) {
+  const size_t nw = std::max(x->mask.size(), y->mask.size());
+  for (size_t w = 0; w < nw; ++w) {
+    const uint32_t mx = w < x->mask.size() ? x->mask[w] : 0u;
+    const uint32_t my = w < y->mask.size() ? y->mask[w] : 0u;
+    if (mx & my) return true;
+  }
+  return false;
+}
+
+static spa_status create_impl(spa_ctx* ctx, const spa_model_desc* m, const spa_pipeline_cfg* cfg, spa_pool* a_full,
+                              spa_pool* b_full, spa_pool* a_slide, spa_pool* b_slide, spa_pipeline** out) {
   if (!ctx || !cfg || !out) return fail(SPA_EINVAL, "bad argument");
   spa_status rc = validate_model(m);
   if (rc) return rc;
   if (cfg->cut != 0 && cfg->cut != 1) return fail(SPA_EINVAL, "cut must be 0 or 1");
   if (cfg->n_micro < 1) return fail(SPA_EINVAL, "n_micro must be >= 1");
-  if ((stage_a == nullptr) != (stage_b == nullptr)) return fail(SPA_EINVAL, "give both pools or neither");
-  if (stage_a) {
-    if (stage_a == stage_b) return fail(SPA_EMASK, "the two stages need distinct pools");
-    size_t nw = std::max(stage_a->mask.size(), stage_b->mask.size());
-    for (size_t w = 0; w < nw; ++w) {
-      uint32_t ma = w < stage_a->mask.size() ? stage_a->mask[w] : 0u;
-      uint32_t mb = w < stage_b->mask.size() ? stage_b->mask[w] : 0u;
-      if (ma & mb) return fail(SPA_EMASK, "stage CU pools overlap");
-    }
+  const bool any = a_full || b_full || a_slide || b_slide;
+  const bool all = a_full && b_full && a_slide && b_slide;
+  if (any && !all) return fail(SPA_EINVAL, "give both pools of every layer kind, or none");
+  if (all) {
+    if (a_full == b_full || a_slide == b_slide) return fail(SPA_EMASK, "the two stages need distinct pools");
+    if (pools_overlap(a_full, b_full) || pools_overlap(a_slide, b_slide)) return fail(SPA_EMASK, "stage CU pools overlap");
   }
   spa_pipeline* p = new spa_pipeline();
   p->ctx = ctx;
   p->m = *m;
   p->cfg = *cfg;
-  p->a = stage_a;
-  p->b = stage_b;
+  p->a = a_full;
+  p->b = b_full;
+  p->ak[SPA_FULL] = a_full;
+  p->bk[SPA_FULL] = b_full;
+  p->ak[SPA_SLIDING] = a_slide;
+  p->bk[SPA_SLIDING] = b_slide;
   const size_t n_ev = (size_t)m->n_layers * cfg->n_micro;
   p->evA.resize(n_ev, nullptr);
   p->evB.resize(n_ev, nullptr);
@@ -176,18 +190,25 @@ spa_status spa_pipeline_create(spa_ctx* ctx, const spa_model_desc* m, const spa_
     e = hipEventCreateWithFlags(&p->evA[i], hipEventDisableTiming);
     if (e == hipSuccess) e = hipEventCreateWithFlags(&p->evB[i], hipEventDisableTiming);
   }
-  if (e == hipSuccess && stage_a) {
+  if (e == hipSuccess && all) {
     e = hipMalloc(&p->flags, sizeof(uint64_t) * 2 * cfg->n_micro);
     if (e == hipSuccess) e = hipMemset(p->flags, 0, sizeof(uint64_t) * 2 * cfg->n_micro);
     if (e == hipSuccess) e = hipDeviceSynchronize();
     if (e == hipSuccess) {
       // use stream value writes/waits when the runtime supports them on this memory
-      hipError_t t = hipStreamWriteValue64(stage_a->stream, p->flags, 0, 0);
-      if (t == hipSuccess) t = hipStreamWaitValue64(stage_b->stream, p->flags, 0, hipStreamWaitValueGte, ~0ull);
+      hipError_t t = hipStreamWriteValue64(a_full->stream, p->flags, 0, 0);
+      if (t == hipSuccess) t = hipStreamWaitValue64(b_full->stream, p->flags, 0, hipStreamWaitValueGte, ~0ull);
       if (t == hipSuccess) t = hipDeviceSynchronize();
       p->value_sync = t == hipSuccess;
       if (t != hipSuccess) (void)hipGetLastError();
     }
+    // one join event per distinct stream
+    std::vector<hipStream_t> seen;
+    for (spa_pool* q : {a_full, b_full, a_slide, b_slide})
+      if (std::find(seen.begin(), seen.end(), q->stream) == seen.end()) seen.push_back(q->stream);
+    p->ev_end.resize(seen.size(), nullptr);
+    for (size_t i = 0; i < seen.size() && e == hipSuccess; ++i)
+      e = hipEventCreateWithFlags(&p->ev_end[i], hipEventDisableTiming);
   }
   if (e == hipSuccess) e = hipEventCreateWithFlags(&p->ev_start, hipEventDisableTiming);
   if (e == hipSuccess) e = hipEventCreateWithFlags(&p->ev_end_a, hipEventDisableTiming);
@@ -198,6 +219,18 @@ spa_status spa_pipeline_create(spa_ctx* ctx, const spa_model_desc* m, const spa_
   }
   *out = p;
   return SPA_OK;
+}
+
+spa_status spa_pipeline_create(spa_ctx* ctx, const spa_model_desc* m, const spa_pipeline_cfg* cfg, spa_pool* stage_a,
+                               spa_pool* stage_b, spa_pipeline** out) {
+  if ((stage_a == nullptr) != (stage_b == nullptr)) return fail(SPA_EINVAL, "give both pools or neither");
+  return create_impl(ctx, m, cfg, stage_a, stage_b, stage_a, stage_b, out);
+}
+
+spa_status spa_pipeline_create_kinds(spa_ctx* ctx, const spa_model_desc* m, const spa_pipeline_cfg* cfg,
+                                     spa_pool* a_full, spa_pool* b_full, spa_pool* a_sliding, spa_pool* b_sliding,
+                                     spa_pipeline** out) {
+  return create_impl(ctx, m, cfg, a_full, b_full, a_sliding, b_sliding, out);
 }
 
 static void harvest_timing(spa_pipeline* p) {
@@ -246,12 +279,16 @@ spa_status spa_pipeline_run(spa_pipeline* p, const spa_layer* layers, const spa_
   if (rc) return rc;
   const bool temporal = p->a == nullptr;
   const bool router_in_a = p->cfg.cut == 1;
-  hipStream_t sa = temporal ? cs : p->a->stream;
-  hipStream_t sb = temporal ? cs : p->b->stream;
+  // stage streams of a layer (its kind's pools); the distinct streams for the joins
+  auto stream_a = [&](const spa_layer* l) { return temporal ? cs : p->ak[l->kind == SPA_FULL ? SPA_FULL : SPA_SLIDING]->stream; };
+  auto stream_b = [&](const spa_layer* l) { return temporal ? cs : p->bk[l->kind == SPA_FULL ? SPA_FULL : SPA_SLIDING]->stream; };
+  std::vector<hipStream_t> streams;
+  if (!temporal)
+    for (spa_pool* q : {p->ak[SPA_FULL], p->bk[SPA_FULL], p->ak[SPA_SLIDING], p->bk[SPA_SLIDING]})
+      if (std::find(streams.begin(), streams.end(), q->stream) == streams.end()) streams.push_back(q->stream);
   if (!temporal) {
     SPA_HIP(hipEventRecord(p->ev_start, cs));
-    SPA_HIP(hipStreamWaitEvent(sa, p->ev_start, 0));
-    SPA_HIP(hipStreamWaitEvent(sb, p->ev_start, 0));
+    for (hipStream_t q : streams) SPA_HIP(hipStreamWaitEvent(q, p->ev_start, 0));
   }
   const bool vs = !temporal && p->value_sync;
   uint64_t* done_a = p->flags;
@@ -260,6 +297,7 @@ spa_status spa_pipeline_run(spa_pipeline* p, const spa_layer* layers, const spa_
   // mistakes one of its writes for its own
   const uint64_t base = p->runs++ * (uint64_t)m->n_layers;
   for (int l = 0; l < m->n_layers; ++l) {
+    const hipStream_t sa = stream_a(&layers[l]), sb = stream_b(&layers[l]);
     for (int mu = 0; mu < n_micro; ++mu) {
       Slot s = slot_ptrs(W, ws, mu);
       const size_t ei = (size_t)l * n_micro + mu;
@@ -285,10 +323,10 @@ spa_status spa_pipeline_run(spa_pipeline* p, const spa_layer* layers, const spa_
     }
   }
   if (!temporal) {
-    SPA_HIP(hipEventRecord(p->ev_end_a, sa));
-    SPA_HIP(hipEventRecord(p->ev_end_b, sb));
-    SPA_HIP(hipStreamWaitEvent(cs, p->ev_end_a, 0));
-    SPA_HIP(hipStreamWaitEvent(cs, p->ev_end_b, 0));
+    for (size_t i = 0; i < streams.size(); ++i) {
+      SPA_HIP(hipEventRecord(p->ev_end[i], streams[i]));
+      SPA_HIP(hipStreamWaitEvent(cs, p->ev_end[i], 0));
+    }
   }
   return SPA_OK;
 }
@@ -324,6 +362,8 @@ spa_status spa_pipeline_destroy(spa_pipeline* p) {
   for (hipEvent_t e : p->tevs) (void)hipEventDestroy(e);
   for (hipEvent_t e : p->tpool) (void)hipEventDestroy(e);
   if (p->flags) (void)hipFree(p->flags);
+  for (hipEvent_t e : p->ev_end)
+    if (e) (void)hipEventDestroy(e);
   if (p->ev_start) (void)hipEventDestroy(p->ev_start);
   if (p->ev_end_a) (void)hipEventDestroy(p->ev_end_a);
   if (p->ev_end_b) (void)hipEventDestroy(p->ev_end_b);
@@ -350,19 +390,33 @@ struct TuneCtx {
   std::vector<spa_tune_point> points;
   spa_status err = SPA_OK;
   int cut = 0, n_micro = 1;
+  int refine_kind = SPA_FULL, fixed_full = 0, fixed_slide = 0;
+  bool per_kind = false;
 };
 
 // median time of reps iterations of one configuration (cu_a = 0: temporal)
-spa_status measure(TuneCtx& t, int cut, int n_micro, int cu_a, double* ms) {
-  spa_pool *pa = nullptr, *pb = nullptr;
+spa_status measure(TuneCtx& t, int cut, int n_micro, int cu_full, int cu_slide, double* ms) {
+  std::vector<spa_pool*> pools;
   spa_pipeline* pipe = nullptr;
   spa_status rc = SPA_OK;
-  if (cu_a > 0) {
-    rc = spa_pool_create_split(t.ctx, 0, cu_a, &pa);
+  auto split = [&](int cu_a) {
+    spa_pool *pa = nullptr, *pb = nullptr;
+    if (!rc) rc = spa_pool_create_split(t.ctx, 0, cu_a, &pa);
+    if (pa) pools.push_back(pa);
     if (!rc) rc = spa_pool_create_split(t.ctx, cu_a / t.ctx->n_xcd, t.ctx->n_cus - cu_a, &pb);
-  }
+    if (pb) pools.push_back(pb);
+  };
   spa_pipeline_cfg cfg{cut, n_micro};
-  if (!rc) rc = spa_pipeline_create(t.ctx, t.m, &cfg, pa, pb, &pipe);
+  if (cu_full > 0) {
+    split(cu_full);
+    if (cu_slide != cu_full) split(cu_slide);
+    if (!rc) {
+      if (pools.size() == 2) rc = spa_pipeline_create(t.ctx, t.m, &cfg, pools[0], pools[1], &pipe);
+      else rc = spa_pipeline_create_kinds(t.ctx, t.m, &cfg, pools[0], pools[1], pools[2], pools[3], &pipe);
+    }
+  } else {
+    rc = spa_pipeline_create(t.ctx, t.m, &cfg, nullptr, nullptr, &pipe);
+  }
   std::vector<double> v;
   for (int i = 0; !rc && i < t.sp->warmup + t.sp->reps; ++i) {
     hipError_t e = hipEventRecord(t.e0, t.st);
@@ -380,20 +434,22 @@ spa_status measure(TuneCtx& t, int cut, int n_micro, int cu_a, double* ms) {
     }
   }
   if (pipe) spa_pipeline_destroy(pipe);
-  if (pa) spa_pool_destroy(pa);
-  if (pb) spa_pool_destroy(pb);
+  for (spa_pool* q : pools) spa_pool_destroy(q);
   if (rc) return rc;
   std::sort(v.begin(), v.end());
   *ms = v[v.size() / 2];
-  t.points.push_back(spa_tune_point{cu_a > 0 ? cut : -1, n_micro, cu_a, *ms});
+  t.points.push_back(spa_tune_point{cu_full > 0 ? cut : -1, n_micro, cu_full, cu_slide, *ms});
   return SPA_OK;
 }
 
+// Algorithm 2 objective: the split of one layer kind, the other held fixed
 double refine_objective(const int32_t* p, int32_t, void* user) {
   TuneCtx& t = *static_cast<TuneCtx*>(user);
   if (t.err) return 1e30;
   double ms = 0.0;
-  spa_status rc = measure(t, t.cut, t.n_micro, p[0], &ms);
+  const int full = t.refine_kind == SPA_FULL ? p[0] : t.fixed_full;
+  const int slide = t.refine_kind == SPA_FULL ? (t.per_kind ? t.fixed_slide : p[0]) : p[0];
+  spa_status rc = measure(t, t.cut, t.n_micro, full, t.per_kind ? slide : full, &ms);
   if (rc) {
     t.err = rc;
     return 1e30;
@@ -424,25 +480,44 @@ extern "C" spa_status spa_pipeline_tune(spa_ctx* ctx, const spa_model_desc* m, c
     return hip_fail(he, "hipEventCreate");
   }
   spa_status rc = SPA_OK;
-  spa_tune_point best{0, 0, 0, 1e30};
+  spa_tune_point best{0, 0, 0, 0, 1e30};
+  t.per_kind = sp->per_kind != 0;
   for (int mi = 0; !rc && mi < sp->n_micros; ++mi) {
     double ms;
-    rc = measure(t, 0, sp->micros[mi], 0, &ms);   // temporal reference
+    rc = measure(t, 0, sp->micros[mi], 0, 0, &ms);   // temporal reference
     for (int ci = 0; !rc && ci < sp->n_cuts; ++ci)
-      for (int cu = sp->cu_min; !rc && cu <= ctx->n_cus - sp->cu_min; cu += sp->cu_step) {
-        rc = measure(t, sp->cuts[ci], sp->micros[mi], cu, &ms);
-        if (!rc && ms < best.ms) best = spa_tune_point{sp->cuts[ci], sp->micros[mi], cu, ms};
-      }
+      for (int cf = sp->cu_min; !rc && cf <= ctx->n_cus - sp->cu_min; cf += sp->cu_step)
+        for (int cs = t.per_kind ? sp->cu_min : cf; !rc && cs <= (t.per_kind ? ctx->n_cus - sp->cu_min : cf);
+             cs += sp->cu_step) {
+          rc = measure(t, sp->cuts[ci], sp->micros[mi], cf, cs, &ms);
+          if (!rc && ms < best.ms) best = spa_tune_point{sp->cuts[ci], sp->micros[mi], cf, cs, ms};
+        }
   }
   if (!rc && sp->refine && best.cu_a > 0) {
     t.cut = best.cut;
     t.n_micro = best.n_micro;
-    int32_t alloc[2] = {best.cu_a, ctx->n_cus - best.cu_a};
-    double v = 0.0;
-    int32_t evals = 0;
-    rc = spa_refine_allocation(2, ctx->n_cus, nx, sp->cu_min, alloc, refine_objective, &t, 0, &v, &evals);
-    if (!rc) rc = t.err;
-    if (!rc && v < best.ms) best = spa_tune_point{best.cut, best.n_micro, alloc[0], v};
+    for (int kind : {SPA_FULL, SPA_SLIDING}) {   // one line search per layer kind (one without per_kind)
+      if (!t.per_kind && kind == SPA_SLIDING) break;
+      t.refine_kind = kind;
+      t.fixed_full = best.cu_a;
+      t.fixed_slide = best.cu_a_sliding;
+      const int start = kind == SPA_FULL ? best.cu_a : best.cu_a_sliding;
+      int32_t alloc[2] = {start, ctx->n_cus - start};
+      double v = 0.0;
+      int32_t evals = 0;
+      rc = spa_refine_allocation(2, ctx->n_cus, nx, sp->cu_min, alloc, refine_objective, &t, 0, &v, &evals);
+      if (!rc) rc = t.err;
+      if (rc) break;
+      if (v < best.ms) {
+        if (kind == SPA_FULL) {
+          best.cu_a = alloc[0];
+          if (!t.per_kind) best.cu_a_sliding = alloc[0];
+        } else {
+          best.cu_a_sliding = alloc[0];
+        }
+        best.ms = v;
+      }
+    }
   }
   (void)hipEventDestroy(t.e0);
   (void)hipEventDestroy(t.e1);

@@ -24,6 +24,7 @@ def main(argv=None):
     ap.add_argument("--cu-min", type=int, default=32)
     ap.add_argument("--reps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--per-kind", type=int, default=1, help="separate CU splits for full and sliding layers")
     a = ap.parse_args(argv)
 
     import torch
@@ -38,16 +39,17 @@ def main(argv=None):
     ws = max((dw.workspace(n_micro=mm) for mm in micros), key=lambda t: t.numel())
     sp = B.spa_tune_space(len(cuts), (B.C.c_int32 * 2)(*(cuts + [0] * (2 - len(cuts)))),
                           len(micros), (B.C.c_int32 * 4)(*(micros + [0] * (4 - len(micros)))),
-                          a.cu_step, a.cu_min, a.warmup, a.reps, 1)
+                          a.cu_step, a.cu_min, a.warmup, a.reps, 1, a.per_kind)
     t0 = time.time()
     best, pts = B.spa_pipeline_tune(ctx, dw.m, dw.layers_c, dw.batch, ws, sp, torch.cuda.current_stream())
     dt = time.time() - t0
     temporal = {p.n_micro: p.ms for p in pts if p.cu_a == 0}
-    entry = {"cut": best.cut, "n_micro": best.n_micro, "cu_a": best.cu_a, "ms": round(best.ms, 4),
+    entry = {"cut": best.cut, "n_micro": best.n_micro, "cu_a": best.cu_a, "cu_a_sliding": best.cu_a_sliding,
+             "ms": round(best.ms, 4),
              "temporal_ms": {str(k): round(v, 4) for k, v in sorted(temporal.items())},
              "points": len(pts), "tune_seconds": round(dt, 1), "n_cus": B.spa_device_cus(ctx)}
     for p in pts:
-        print(f"cut={p.cut:2d} m={p.n_micro} cu_a={p.cu_a:3d}: {p.ms:.3f} ms", flush=True)
+        print(f"cut={p.cut:2d} m={p.n_micro} cu_a={p.cu_a:3d}/{p.cu_a_sliding:3d}: {p.ms:.3f} ms", flush=True)
     print(json.dumps({a.workload: entry}), flush=True)
     d = json.load(open(a.out)) if os.path.exists(a.out) else {}
     d[a.workload] = entry

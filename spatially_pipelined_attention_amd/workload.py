@@ -211,3 +211,42 @@ class DeviceWorkload:
             n = min(int(self.L[b]), wl.window) if wl.layer_kinds[l] == "sliding" else int(self.L[b])
             tot += n * wl.n_kv_heads * wl.head_dim * esz * 2
         return tot
+
+
+class Pipeline:
+    """A pipeline (and the CU pools it owns) from a configuration dict:
+    {"cut", "n_micro", "cu_a"[, "cu_a_sliding"]}; cu_a = None or 0 gives the
+    temporal schedule with the same microbatches. Stage A takes the first
+    cu_a CUs of every XCD's share, stage B the rest."""
+
+    def __init__(self, ctx, m: B.spa_model_desc, cfg: dict):
+        self.pools = []
+        n_cus = B.spa_device_cus(ctx)
+        c = B.spa_pipeline_cfg(int(cfg["cut"]), int(cfg["n_micro"]))
+        cu_a = cfg.get("cu_a") or 0
+        if cu_a <= 0:
+            self.h = B.spa_pipeline_create(ctx, m, c, None, None)
+            return
+
+        def split(cu):
+            pa = B.spa_pool_create_split(ctx, 0, cu)
+            self.pools.append(pa)
+            pb = B.spa_pool_create_split(ctx, cu // 8, n_cus - cu)
+            self.pools.append(pb)
+            return pa, pb
+        cu_s = cfg.get("cu_a_sliding") or cu_a
+        af, bf = split(cu_a)
+        if cu_s == cu_a:
+            self.h = B.spa_pipeline_create(ctx, m, c, af, bf)
+        else:
+            asl, bsl = split(cu_s)
+            self.h = B.spa_pipeline_create_kinds(ctx, m, c, af, bf, asl, bsl)
+
+    def run(self, layers, batch, ws, stream=None):
+        B.spa_pipeline_run(self.h, layers, batch, ws, stream if stream is not None else torch.cuda.current_stream())
+
+    def close(self):
+        B.spa_pipeline_destroy(self.h)
+        for p in self.pools:
+            B.spa_pool_destroy(p)
+        self.pools = []

@@ -39,23 +39,19 @@ def tuned(name, batch):
 
 class Pipe:
     def __init__(self, B, ctx, m, cfg, spatial=True):
-        self.B = B
-        self.pools = []
-        if spatial:
-            n_cus = B.spa_device_cus(ctx)
-            self.pools = [B.spa_pool_create_split(ctx, 0, cfg["cu_a"]),
-                          B.spa_pool_create_split(ctx, cfg["cu_a"] // 8, n_cus - cfg["cu_a"])]
-        pa, pb = (self.pools + [None, None])[:2]
-        self.h = B.spa_pipeline_create(ctx, m, B.spa_pipeline_cfg(cfg["cut"], cfg["n_micro"]), pa, pb)
+        from spatially_pipelined_attention_amd.workload import Pipeline
+        c = dict(cfg)
+        if not spatial:
+            c["cu_a"] = 0
+        self.p = Pipeline(ctx, m, c)
+        self.h = self.p.h
 
     def run(self, layers, batch, ws):
-        self.B.spa_pipeline_run(self.h, layers, batch, ws, torch.cuda.current_stream())
+        self.p.run(layers, batch, ws)
         torch.cuda.synchronize()
 
     def close(self):
-        self.B.spa_pipeline_destroy(self.h)
-        for p in self.pools:
-            self.B.spa_pool_destroy(p)
+        self.p.close()
 
 
 def same_picks(got, ref):

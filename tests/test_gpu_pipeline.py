@@ -33,25 +33,17 @@ def env():
     return dict(B=B, wl=wl, dw=dw, ctx=ctx, n_cus=B.spa_device_cus(ctx))
 
 
-def _run(env, cut, n_micro, cu_a):
-    B, dw, ctx, n_cus = env["B"], env["dw"], env["ctx"], env["n_cus"]
-    pools = []
-    if cu_a is None:
-        pipe = B.spa_pipeline_create(ctx, dw.m, B.spa_pipeline_cfg(cut, n_micro), None, None)
-    else:
-        pa = B.spa_pool_create_split(ctx, 0, cu_a)
-        pb = B.spa_pool_create_split(ctx, cu_a // 8, n_cus - cu_a)
-        pools = [pa, pb]
-        pipe = B.spa_pipeline_create(ctx, dw.m, B.spa_pipeline_cfg(cut, n_micro), pa, pb)
+def _run(env, cut, n_micro, cu_a, cu_s=None):
+    from spatially_pipelined_attention_amd.workload import Pipeline
+    B, dw, ctx = env["B"], env["dw"], env["ctx"]
+    pipe = Pipeline(ctx, dw.m, {"cut": cut, "n_micro": n_micro, "cu_a": cu_a or 0, "cu_a_sliding": cu_s})
     ws = dw.workspace(n_micro=n_micro)
     dw.reset_x()
     dw.topk.zero_()
-    B.spa_pipeline_run(pipe, dw.layers_c, dw.batch, ws, torch.cuda.current_stream())
+    pipe.run(dw.layers_c, dw.batch, ws)
     torch.cuda.synchronize()
     err = B.spa_workspace_errors(ctx, ws)
-    B.spa_pipeline_destroy(pipe)
-    for p in pools:
-        B.spa_pool_destroy(p)
+    pipe.close()
     assert err == 0
     L = dw.L
     full = [l for l, k in enumerate(dw.wl.layer_kinds) if k == "full"][0]
@@ -94,11 +86,14 @@ def test_masks_rejected_before_launch(env):
         B.spa_pool_destroy(pb)
 
 
-@pytest.mark.parametrize("cut,n_micro,cu_a", [(0, 2, 128), (1, 2, 64), (0, 4, 192), (1, 4, 96), (0, 1, 128)])
-def test_spatial_equals_temporal_bitwise(env, cut, n_micro, cu_a):
-    print(f"[case] cut={cut} m={n_micro} cu_a={cu_a}", flush=True)
+@pytest.mark.parametrize("cut,n_micro,cu_a,cu_s", [(0, 2, 128, None), (1, 2, 64, None), (0, 4, 192, None),
+                                                    (1, 4, 96, None), (0, 1, 128, None),
+                                                    (1, 2, 160, 96), (0, 4, 64, 192)])
+def test_spatial_equals_temporal_bitwise(env, cut, n_micro, cu_a, cu_s):
+    """cu_s: a different split for sliding layers (pools per layer kind)."""
+    print(f"[case] cut={cut} m={n_micro} cu_a={cu_a} cu_s={cu_s}", flush=True)
     xt, tt, kt, vt = _run(env, cut, n_micro, None)
-    xs, ts, ks, vs = _run(env, cut, n_micro, cu_a)
+    xs, ts, ks, vs = _run(env, cut, n_micro, cu_a, cu_s)
     assert torch.equal(xt, xs)
     assert torch.equal(tt, ts)
     np.testing.assert_array_equal(kt, ks)
@@ -138,7 +133,7 @@ def test_one_microbatch_close_to_four(env):
 
 def test_tuner_returns_a_measured_point_of_the_space(env):
     B, dw, ctx = env["B"], env["dw"], env["ctx"]
-    sp = B.spa_tune_space(1, (B.C.c_int32 * 2)(0, 0), 1, (B.C.c_int32 * 4)(2, 0, 0, 0), 64, 64, 1, 2, 1)
+    sp = B.spa_tune_space(1, (B.C.c_int32 * 2)(0, 0), 1, (B.C.c_int32 * 4)(2, 0, 0, 0), 64, 64, 1, 2, 1, 0)
     ws = dw.workspace(n_micro=2)
     best, pts = B.spa_pipeline_tune(ctx, dw.m, dw.layers_c, dw.batch, ws, sp, torch.cuda.current_stream())
     grid = [p for p in pts if p.cu_a in (64, 128, 192)]
@@ -152,9 +147,35 @@ def test_tuner_returns_a_measured_point_of_the_space(env):
 def test_tuner_rejects_bad_space(env):
     B, dw, ctx = env["B"], env["dw"], env["ctx"]
     ws = dw.workspace(n_micro=2)
-    bad = B.spa_tune_space(1, (B.C.c_int32 * 2)(0, 0), 1, (B.C.c_int32 * 4)(3, 0, 0, 0), 64, 64, 1, 2, 1)
+    bad = B.spa_tune_space(1, (B.C.c_int32 * 2)(0, 0), 1, (B.C.c_int32 * 4)(3, 0, 0, 0), 64, 64, 1, 2, 1, 0)
     with pytest.raises(B.SpaError):
         B.spa_pipeline_tune(ctx, dw.m, dw.layers_c, dw.batch, ws, bad)   # 3 does not divide 64
-    bad = B.spa_tune_space(1, (B.C.c_int32 * 2)(0, 0), 1, (B.C.c_int32 * 4)(2, 0, 0, 0), 12, 64, 1, 2, 1)
+    bad = B.spa_tune_space(1, (B.C.c_int32 * 2)(0, 0), 1, (B.C.c_int32 * 4)(2, 0, 0, 0), 12, 64, 1, 2, 1, 0)
     with pytest.raises(B.SpaError):
         B.spa_pipeline_tune(ctx, dw.m, dw.layers_c, dw.batch, ws, bad)   # step not a multiple of 8
+
+
+def test_tuner_per_kind_points(env):
+    B, dw, ctx = env["B"], env["dw"], env["ctx"]
+    sp = B.spa_tune_space(1, (B.C.c_int32 * 2)(1, 0), 1, (B.C.c_int32 * 4)(2, 0, 0, 0), 96, 64, 1, 1, 0, 1)
+    ws = dw.workspace(n_micro=2)
+    best, pts = B.spa_pipeline_tune(ctx, dw.m, dw.layers_c, dw.batch, ws, sp, torch.cuda.current_stream())
+    spatial = [(p.cu_a, p.cu_a_sliding) for p in pts if p.cu_a > 0]
+    assert sorted(spatial) == [(a, s) for a in (64, 160) for s in (64, 160)]
+    assert (best.cu_a, best.cu_a_sliding) in spatial
+
+
+def test_per_kind_pools_must_be_disjoint_within_a_kind(env):
+    B, ctx = env["B"], env["ctx"]
+    a = B.spa_pool_create_split(ctx, 0, 128)
+    b = B.spa_pool_create_split(ctx, 16, 128)
+    c = B.spa_pool_create_split(ctx, 8, 64)      # overlaps a (CUs 8..15 of every XCD)
+    try:
+        with pytest.raises(B.SpaError) as ei:
+            B.spa_pipeline_create_kinds(ctx, env["dw"].m, B.spa_pipeline_cfg(0, 2), a, b, a, c)
+        assert ei.value.status == B.SPA_EMASK
+        p = B.spa_pipeline_create_kinds(ctx, env["dw"].m, B.spa_pipeline_cfg(0, 2), a, b, c, b)   # c, b disjoint
+        B.spa_pipeline_destroy(p)
+    finally:
+        for q in (a, b, c):
+            B.spa_pool_destroy(q)
