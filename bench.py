@@ -123,6 +123,12 @@ def cpu_baseline(name, n_tok_sample=None):
                       + ("" if len(toks) == wl.batch else f", scaled x{scale:.1f}")}
 
 
+TIMER_NOTE = {
+    "clock": "device wall clock: first dispatched workgroup's start to the latest workgroup end, recorded by the kernel",
+    "events": "HIP events recorded around each launch on its stream",
+}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -136,11 +142,14 @@ def main():
     ap.add_argument("--cu-a-sliding", type=int, default=None, help="CUs of stage A in sliding layers")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--quick", action="store_true", help="skip the comparison schedules")
+    ap.add_argument("--kernel-timer", choices=["clock", "events"], default="clock",
+                    help="attention launch duration: the kernel's own span on the device wall clock, or HIP "
+                         "events around each launch (these also hold the start marker's dispatch latency)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="after timing, copy BYTES device bytes three times (a known-size kernel for counter scaling)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; use --gpus 1"}))
+        print(json.dumps({"error": "one GPU only: the pipeline partitions the CUs of a single device; use --gpus 1"}))
         sys.exit(2)
 
     import torch
@@ -183,7 +192,7 @@ def main():
             run()
         torch.cuda.synchronize()
         if timed_cls is not None:
-            B.spa_pipeline_time_kernel(pipe.h, timed_cls, True)
+            B.spa_pipeline_time_kernel(pipe.h, timed_cls, 1 if args.kernel_timer == "clock" else 2)
         torch.cuda.synchronize()
         # a decode step needs the previous step's outputs, so steps are not
         # overlapped: each one is enqueued after the previous one completed
@@ -253,7 +262,8 @@ def main():
                      "achieved": round(achieved, 1) if achieved else None, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4) if achieved else None,
                      "traffic": int(traffic) if traffic else None,
-                     "bytes_per_launch": int(bytes_per_launch), "mean_launch_ms": k_ms, "launches": k_n},
+                     "bytes_per_launch": int(bytes_per_launch), "mean_launch_ms": k_ms, "launches": k_n,
+                     "timer": TIMER_NOTE[args.kernel_timer]},
         "device_error_bits": errs,
         "setup_s": round(t_setup, 1),
     }

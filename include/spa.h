@@ -308,11 +308,23 @@ spa_status spa_pipeline_create_kinds(spa_ctx* ctx, const spa_model_desc* m, cons
  * starts after the iteration). */
 spa_status spa_pipeline_run(spa_pipeline* p, const spa_layer* layers, const spa_batch* b, void* ws, size_t ws_bytes,
                             void* caller_stream);
-/* Per-kernel timing: when enabled, every launch of kernel class `cls`
- * (0 = full-layer attention, 1 = sliding attention, 2 = QKV, 3 = output
- * projection, 4 = router, 5 = expert gate/up, 6 = expert down, 7 = combine)
- * is bracketed by events; spa_pipeline_timing returns the mean duration (ms)
- * over the launches since enabling, and the count. */
+/* Per-kernel timing of every launch of kernel class `cls` (0 = full-layer
+ * attention, 1 = sliding attention, 2 = QKV, 3 = output projection, 4 =
+ * router, 5 = expert gate/up, 6 = expert down, 7 = combine).
+ * enable = 0: off.
+ * enable = 1: for the attention classes the kernel itself records its span on
+ *   the device wall clock (start of the first dispatched workgroup to the
+ *   latest workgroup end; one atomic per workgroup, no extra packets in
+ *   the queue); the other
+ *   classes fall back to mode 2. Spans of up to 8192 launches are kept
+ *   between two harvests (spa_pipeline_timing or a new enable); later
+ *   launches run untimed.
+ * enable = 2: HIP events recorded around each launch on its stream. Their
+ *   interval also holds the start marker's dispatch latency, and the
+ *   markers delay the launch they bracket.
+ * spa_pipeline_timing synchronises the device and returns the mean duration
+ * (ms) over the launches timed since enabling, and their count. SPA_EINVAL
+ * for a bad class or mode. */
 spa_status spa_pipeline_time_kernel(spa_pipeline* p, int32_t cls, int32_t enable);
 spa_status spa_pipeline_timing(spa_pipeline* p, double* mean_ms, int32_t* count);
 spa_status spa_pipeline_destroy(spa_pipeline* p);

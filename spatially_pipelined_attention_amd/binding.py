@@ -321,8 +321,9 @@ def spa_pipeline_run(pipe, layers, batch, ws, stream=None):
     _check(lib().spa_pipeline_run(pipe, layers, C.byref(batch), *_ws(ws), stream_handle(stream)))
 
 
-def spa_pipeline_time_kernel(pipe, cls: int, enable: bool):
-    _check(lib().spa_pipeline_time_kernel(pipe, cls, 1 if enable else 0))
+def spa_pipeline_time_kernel(pipe, cls: int, enable: int):
+    """enable: 0 off, 1 device-clock spans (attention; events otherwise), 2 events."""
+    _check(lib().spa_pipeline_time_kernel(pipe, cls, int(enable)))
 
 
 def spa_pipeline_timing(pipe):

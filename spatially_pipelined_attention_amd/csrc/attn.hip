@@ -228,6 +228,7 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
   const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int seq = a.tok0 + b;
   const int G = a.n_q_heads / a.n_kv_heads;
+  if (a.tspan && tid == 0 && c == 0 && g == 0 && b == 0) a.tspan[0] = wall_clock64();   // first dispatched
   const KvLoc loc = kv_locate(a, seq, g, KIND);
   if (!loc.ok) {
     if (c == 0 && tid == 0 && a.err) atomicOr(a.err, ERR_KV_LEN);
@@ -347,6 +348,11 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
         pp[kD + 1] = l;
       }
     }
+  }
+  if (a.tspan) {   // uniform branch: every wave of the workgroup reaches it
+    __syncthreads();
+    const int j = (c + (g + b * gridDim.y) * gridDim.x) & 15;
+    if (tid == 0) atomicMax(a.tspan + 8 * (j + 1), (unsigned long long)wall_clock64());
   }
 }
 

@@ -215,15 +215,27 @@ spa_status clear_errors(void* ws, hipStream_t st) {
 // ---------------------------------------------------------------------------
 // timing hook: events around every launch of the timed kernel class
 // ---------------------------------------------------------------------------
+// Timing events need no system-scope release: they only order against work
+// on the same device, and the release would flush L2 between kernels.
+#ifndef SPA_TIMING_EVENT_FLAGS
+#define SPA_TIMING_EVENT_FLAGS hipEventDisableSystemFence
+#endif
+
 struct HookScope {
   TimingHook* th;
   hipStream_t st;
   bool on;
   bool ext;          // the launch itself records the pair (hipExtLaunchKernel timestamps)
   hipEvent_t e0 = nullptr, e1 = nullptr;
+  unsigned long long* span_slot = nullptr;   // device-clock span of this launch
   HookScope(TimingHook* t, int cls, hipStream_t s, bool in_launch = false)
       : th(t), st(s), on(t && t->cls == cls && t->evs && t->pool), ext(in_launch) {
     if (!on) return;
+    if (ext && th->span) {   // the kernel records its own span: no events
+      on = false;
+      if (*th->span_used < th->span_cap) span_slot = th->span + (size_t)kSpanWords * (*th->span_used)++;
+      return;
+    }
     e0 = take();
     e1 = take();
     th->evs->push_back(e0);
@@ -235,7 +247,7 @@ struct HookScope {
   hipEvent_t take() {
     if (th->pool->empty()) {
       hipEvent_t e;
-      (void)hipEventCreate(&e);
+      (void)hipEventCreateWithFlags(&e, SPA_TIMING_EVENT_FLAGS);
       return e;
     }
     hipEvent_t e = th->pool->back();
@@ -359,6 +371,7 @@ static spa_status op_attn(spa_ctx* ctx, const spa_model_desc* m, const spa_layer
   {
     // the attention kernel alone, timed by its own dispatch (start/stop events of the launch)
     HookScope hs(th, l->kind == SPA_FULL ? KC_ATTN_FULL : KC_ATTN_SLIDING, st, true);
+    a.tspan = hs.span_slot;
     SPA_HIP(launch_attn(a, st, hs.start(), hs.stop()));
   }
   if (a.max_chunks > 1) SPA_HIP(launch_attn_merge(a, st));

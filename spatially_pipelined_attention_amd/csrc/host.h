@@ -99,6 +99,12 @@ struct TimingHook {
   int cls = -1;
   std::vector<hipEvent_t>* evs = nullptr;   // pairs (start, stop)
   std::vector<hipEvent_t>* pool = nullptr;  // free events
+  // device-clock spans (attention kernels): launch i owns
+  // span[i * kSpanWords, (i + 1) * kSpanWords); null when the launches are
+  // timed by events instead
+  unsigned long long* span = nullptr;
+  int* span_used = nullptr;
+  int span_cap = 0;
 };
 
 // The layer's pieces on one slot (tokens [tok0, tok0+n_tok)); enqueue on st.

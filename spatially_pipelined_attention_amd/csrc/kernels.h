@@ -165,8 +165,15 @@ struct AttnArgs {
   void* o;                  // [n_tok][Hq*D] (kv dtype)
   int* err;
   int stream_kv;            // non-temporal KV loads
+  // optional [kSpanWords]: this launch's span on the device wall clock. The
+  // first workgroup stores its start in word 0; every workgroup takes the
+  // atomic max of its end into word 8 (j + 1), j = its linear index mod 16
+  // (spread over 16 lines, so the atomics do not queue on one address).
+  // The caller presets the words to zero.
+  unsigned long long* tspan;
 };
-// start/stop (optional): events the runtime records at the kernel's own start and end
+constexpr int kSpanWords = 136;
+// start/stop (optional): events recorded around the launch
 hipError_t launch_attn(const AttnArgs& a, hipStream_t st, hipEvent_t start = nullptr, hipEvent_t stop = nullptr);
 // merge of the chunk partials of multi-chunk sequences (single-chunk ones are final already)
 hipError_t launch_attn_merge(const AttnArgs& a, hipStream_t st);

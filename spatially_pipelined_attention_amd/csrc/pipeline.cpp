@@ -40,10 +40,16 @@ struct spa_pipeline {
   uint64_t runs = 0;
   bool value_sync = false;
   int timed_cls = -1;
+  int timed_mode = 0;                 // 1: device-clock spans for attention, 2: events
   std::vector<hipEvent_t> tevs, tpool;
+  unsigned long long* tspan = nullptr;   // [kSpanCap][kSpanWords] device-clock spans
+  unsigned long long* tspan_host = nullptr;   // pinned copy for the harvest
+  int tspan_used = 0;
   double t_sum_ms = 0.0;
   int t_count = 0;
 };
+
+static constexpr int kSpanCap = 8192;   // timed launches between two harvests
 
 static spa_status make_pool(spa_ctx* ctx, const std::vector<uint32_t>& mask, spa_pool** out) {
   int nbits = 0;
@@ -233,7 +239,32 @@ spa_status spa_pipeline_create_kinds(spa_ctx* ctx, const spa_model_desc* m, cons
   return create_impl(ctx, m, cfg, a_full, b_full, a_sliding, b_sliding, out);
 }
 
-static void harvest_timing(spa_pipeline* p) {
+// Clears span slots [0, n) (zero: no start stored, identity of the atomic max).
+static hipError_t reset_spans(spa_pipeline* p, int n) {
+  if (n <= 0) return hipSuccess;
+  hipError_t e = launch_fill_i32((int*)p->tspan, (long long)n * kSpanWords * 2, 0, nullptr);
+  return e == hipSuccess ? hipDeviceSynchronize() : e;
+}
+
+static spa_status harvest_timing(spa_pipeline* p) {
+  if (p->tspan_used > 0) {
+    // spans: first workgroup start to last workgroup end, in wall-clock ticks
+    int khz = 0;
+    SPA_HIP(hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, p->ctx->device));
+    if (khz <= 0) return fail(SPA_EHIP, "device wall clock rate unknown");
+    SPA_HIP(hipMemcpy(p->tspan_host, p->tspan, (size_t)kSpanWords * p->tspan_used * sizeof(unsigned long long),
+                      hipMemcpyDeviceToHost));
+    for (int i = 0; i < p->tspan_used; ++i) {
+      const unsigned long long* w = p->tspan_host + (size_t)kSpanWords * i;
+      unsigned long long end = 0;
+      for (int j = 1; j <= 16; ++j) end = std::max(end, w[8 * j]);
+      if (w[0] == 0 || end < w[0]) continue;   // a launch that did no timed work
+      p->t_sum_ms += (double)(end - w[0]) / khz;
+      p->t_count += 1;
+    }
+    SPA_HIP(reset_spans(p, p->tspan_used));
+    p->tspan_used = 0;
+  }
   // pairs (start, stop) in launch order; all complete once the caller synchronised
   for (size_t i = 0; i + 1 < p->tevs.size(); i += 2) {
     float ms = 0.f;
@@ -245,6 +276,7 @@ static void harvest_timing(spa_pipeline* p) {
     p->tpool.push_back(p->tevs[i + 1]);
   }
   p->tevs.clear();
+  return SPA_OK;
 }
 
 spa_status spa_pipeline_run(spa_pipeline* p, const spa_layer* layers, const spa_batch* b, void* ws, size_t ws_bytes,
@@ -273,6 +305,11 @@ spa_status spa_pipeline_run(spa_pipeline* p, const spa_layer* layers, const spa_
   th.cls = p->timed_cls;
   th.evs = &p->tevs;
   th.pool = &p->tpool;
+  if (p->timed_mode == 1) {
+    th.span = p->tspan;
+    th.span_used = &p->tspan_used;
+    th.span_cap = kSpanCap;
+  }
   TimingHook* thp = p->timed_cls >= 0 ? &th : nullptr;
 
   spa_status rc = clear_errors(ws, cs);
@@ -332,12 +369,29 @@ spa_status spa_pipeline_run(spa_pipeline* p, const spa_layer* layers, const spa_
 }
 
 spa_status spa_pipeline_time_kernel(spa_pipeline* p, int32_t cls, int32_t enable) {
-  if (!p || cls < 0 || cls >= KC_COUNT) return fail(SPA_EINVAL, "bad argument");
-  if (!p->tevs.empty()) {
+  if (!p || cls < 0 || cls >= KC_COUNT || enable < 0 || enable > 2) return fail(SPA_EINVAL, "bad argument");
+  if (!p->tevs.empty() || p->tspan_used > 0) {
     SPA_HIP(hipDeviceSynchronize());
-    harvest_timing(p);
+    spa_status rc = harvest_timing(p);
+    if (rc) return rc;
+  }
+  const bool clock = enable == 1 && (cls == KC_ATTN_FULL || cls == KC_ATTN_SLIDING);
+  if (clock && !p->tspan) {
+    SPA_HIP(hipSetDevice(p->ctx->device));
+    const size_t bytes = (size_t)kSpanCap * kSpanWords * sizeof(unsigned long long);
+    hipError_t e = hipMalloc(&p->tspan, bytes);
+    if (e == hipSuccess) e = hipHostMalloc(&p->tspan_host, bytes, hipHostMallocDefault);
+    if (e == hipSuccess) e = reset_spans(p, kSpanCap);
+    if (e != hipSuccess) {
+      if (p->tspan) (void)hipFree(p->tspan);
+      if (p->tspan_host) (void)hipHostFree(p->tspan_host);
+      p->tspan = nullptr;
+      p->tspan_host = nullptr;
+      return hip_fail(e, "timing buffer");
+    }
   }
   p->timed_cls = enable ? cls : -1;
+  p->timed_mode = !enable ? 0 : clock ? 1 : 2;
   p->t_sum_ms = 0.0;
   p->t_count = 0;
   return SPA_OK;
@@ -346,7 +400,8 @@ spa_status spa_pipeline_time_kernel(spa_pipeline* p, int32_t cls, int32_t enable
 spa_status spa_pipeline_timing(spa_pipeline* p, double* mean_ms, int32_t* count) {
   if (!p || !mean_ms || !count) return fail(SPA_EINVAL, "bad argument");
   SPA_HIP(hipDeviceSynchronize());
-  harvest_timing(p);
+  spa_status rc = harvest_timing(p);
+  if (rc) return rc;
   *count = p->t_count;
   *mean_ms = p->t_count ? p->t_sum_ms / p->t_count : 0.0;
   return SPA_OK;
@@ -361,6 +416,8 @@ spa_status spa_pipeline_destroy(spa_pipeline* p) {
     if (e) (void)hipEventDestroy(e);
   for (hipEvent_t e : p->tevs) (void)hipEventDestroy(e);
   for (hipEvent_t e : p->tpool) (void)hipEventDestroy(e);
+  if (p->tspan) (void)hipFree(p->tspan);
+  if (p->tspan_host) (void)hipHostFree(p->tspan_host);
   if (p->flags) (void)hipFree(p->flags);
   for (hipEvent_t e : p->ev_end)
     if (e) (void)hipEventDestroy(e);

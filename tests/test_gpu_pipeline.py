@@ -179,3 +179,39 @@ def test_per_kind_pools_must_be_disjoint_within_a_kind(env):
     finally:
         for q in (a, b, c):
             B.spa_pool_destroy(q)
+
+
+@pytest.mark.parametrize("cu_a", [None, 128])
+def test_kernel_timers(env, cu_a):
+    """Both per-launch timers count every full-layer attention launch; the
+    event interval brackets the kernel, so it is never shorter than the
+    kernel's own device-clock span; timing leaves the outputs unchanged."""
+    from spatially_pipelined_attention_amd.workload import Pipeline
+    B, dw, ctx = env["B"], env["dw"], env["ctx"]
+    m = 2
+    ref = _run(env, 0, m, cu_a)
+    n_full = sum(1 for k in dw.wl.layer_kinds if k == "full")
+    ws = dw.workspace(n_micro=m)
+    means = {}
+    for mode in (1, 2):
+        pipe = Pipeline(ctx, dw.m, {"cut": 0, "n_micro": m, "cu_a": cu_a or 0})
+        B.spa_pipeline_time_kernel(pipe.h, B.KC_ATTN_FULL, mode)
+        runs = 3
+        for _ in range(runs):
+            dw.reset_x()
+            dw.topk.zero_()
+            pipe.run(dw.layers_c, dw.batch, ws)
+        ms, n = B.spa_pipeline_timing(pipe.h)
+        pipe.close()
+        assert n == runs * n_full * m, (mode, n)
+        assert 0.0 < ms < 100.0, (mode, ms)
+        means[mode] = ms
+        assert torch.equal(dw.x, ref[0]) and torch.equal(dw.topk, ref[1])
+    print(f"[timers] cu_a={cu_a} clock {means[1] * 1e3:.1f} us, events {means[2] * 1e3:.1f} us", flush=True)
+    assert means[2] >= 0.98 * means[1], means
+    with pytest.raises(B.SpaError):
+        pipe = Pipeline(ctx, dw.m, {"cut": 0, "n_micro": m, "cu_a": 0})
+        try:
+            B.spa_pipeline_time_kernel(pipe.h, B.KC_ATTN_FULL, 3)
+        finally:
+            pipe.close()
