@@ -9,6 +9,16 @@
         runs, scaled by what the same counters read for a plain copy of N bytes in the same
         run (the copy reads N and writes N bytes)
 
+    python -m spatially_pipelined_attention_amd.profiling traffic-table --fetch CSV --write CSV \\
+            --kernel PREFIX --copy-bytes N --command CMD
+        the same per launch shape of every kernel whose name starts with PREFIX, as a table
+
+    python -m spatially_pipelined_attention_amd.profiling mfma CSV --kernel PREFIX --dtype bf16|f8 \\
+            --command CMD
+        MFMA work and utilisation per launch of the kernels whose name starts with PREFIX, from a
+        `--pmc MfmaUtil SQ_INSTS_VALU_MFMA_MOPS_<DT>` run (MfmaUtil: busy MFMA cycles summed over
+        SIMDs over the active cycles of one XCC times the SIMD count)
+
 Each summary is markdown with `key: value` lines that bench.py reads back.
 """
 from __future__ import annotations
@@ -119,6 +129,65 @@ def cmd_traffic(a):
         print(f"- {k}: {v}")
 
 
+def cmd_traffic_table(a):
+    fetch, write = _per_dispatch(a.fetch), _per_dispatch(a.write)
+    f_scale = a.copy_bytes / (_copy_kib(fetch) * 1024.0)
+    w_scale = a.copy_bytes / (_copy_kib(write) * 1024.0)
+
+    def groups(disp, sc):
+        g = defaultdict(list)
+        for d in disp:
+            name = d["name"].split("(")[0].replace("void ", "")
+            if name.startswith(a.kernel):
+                g[(name, d["grid"])].append(d["kib"] * 1024.0 * sc)
+        return g
+
+    gf, gw = groups(fetch, f_scale), groups(write, w_scale)
+    print(f"# HBM traffic per launch of `{a.kernel}*`\n\ncommand: `{a.command}`\n")
+    print(f"Counter scale from a plain copy of {a.copy_bytes} bytes: fetch x{f_scale:.4f}, write x{w_scale:.4f}.\n")
+    print("| kernel | grid | launches | fetch MB | write MB |")
+    print("|---|---:|---:|---:|---:|")
+    for key in sorted(gf, key=lambda k: -sum(gf[k])):
+        f = gf[key]
+        w = gw.get(key, [0.0])
+        print(f"| `{key[0]}` | {key[1]} | {len(f)} | {sum(f) / len(f) / 1e6:.2f} | {sum(w) / len(w) / 1e6:.2f} |")
+
+
+PEAK_TFLOPS = {"bf16": 2500.0, "f8": 5000.0}   # dense MFMA peaks of the device
+
+
+def cmd_mfma(a):
+    rows = list(csv.DictReader(open(a.csv)))
+    per = defaultdict(dict)
+    meta = {}
+    for r in rows:
+        d = int(r["Dispatch_Id"])
+        per[d][r["Counter_Name"]] = per[d].get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+        meta[d] = (r["Kernel_Name"].split("(")[0].replace("void ", ""), int(r["Grid_Size"]),
+                   (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9)
+    mops = f"SQ_INSTS_VALU_MFMA_MOPS_{a.dtype.upper()}"
+    groups = defaultdict(list)
+    for d, c in per.items():
+        name, grid, dur = meta[d]
+        if name.startswith(a.kernel) and mops in c and "MfmaUtil" in c:
+            groups[(name, grid)].append((c[mops] * 512.0, c["MfmaUtil"], dur))
+    if not groups:
+        raise SystemExit(f"no launch of {a.kernel} with {mops} and MfmaUtil")
+    print(f"# MFMA work of `{a.kernel}*` ({a.dtype})\n\ncommand: `{a.command}`\n")
+    print(f"Dense {a.dtype} MFMA peak: {PEAK_TFLOPS[a.dtype]:.0f} TFLOP/s. Durations are those of the counter run "
+          "(launches serialised by the profiler).\n")
+    print("| kernel | grid | launches | mean us | GFLOP per launch | TFLOP/s | % of peak | MfmaUtil % |")
+    print("|---|---:|---:|---:|---:|---:|---:|---:|")
+    for (name, grid), v in sorted(groups.items(), key=lambda kv: -sum(x[0] for x in kv[1])):
+        n = len(v)
+        fl = sum(x[0] for x in v) / n
+        ut = sum(x[1] for x in v) / n
+        du = sum(x[2] for x in v) / n
+        tf = fl / du / 1e12
+        print(f"| `{name}` | {grid} | {n} | {du * 1e6:.2f} | {fl / 1e9:.3f} | {tf:.1f} | "
+              f"{100 * tf / PEAK_TFLOPS[a.dtype]:.1f} | {ut:.1f} |")
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -134,8 +203,19 @@ def main(argv=None):
     t.add_argument("--command", required=True)
     t.add_argument("--sources", nargs="*")
     t.add_argument("--set", action="append", metavar="KEY=VALUE", help="extra key recorded in the summary")
+    tt = sub.add_parser("traffic-table")
+    tt.add_argument("--fetch", required=True)
+    tt.add_argument("--write", required=True)
+    tt.add_argument("--kernel", required=True)
+    tt.add_argument("--copy-bytes", type=int, required=True)
+    tt.add_argument("--command", required=True)
+    mf = sub.add_parser("mfma")
+    mf.add_argument("csv")
+    mf.add_argument("--kernel", required=True)
+    mf.add_argument("--dtype", choices=["bf16", "f8"], required=True)
+    mf.add_argument("--command", required=True)
     a = ap.parse_args(argv)
-    {"stats": cmd_stats, "traffic": cmd_traffic}[a.cmd](a)
+    {"stats": cmd_stats, "traffic": cmd_traffic, "traffic-table": cmd_traffic_table, "mfma": cmd_mfma}[a.cmd](a)
 
 
 if __name__ == "__main__":
