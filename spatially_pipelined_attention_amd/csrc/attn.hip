@@ -119,7 +119,10 @@ template <>
 struct QRegs<DT_F32> { u32x4 q[4]; };
 
 // One 32-position block: scores, online softmax update, PV accumulation.
-template <int KVT>
+// MASK: the block holds positions at or past n_valid (the sequence's last
+// block); only then are scores and V rows masked. exp2 is the hardware
+// instruction: its arguments are <= 0 here, and -inf gives 0.
+template <int KVT, bool MASK>
 __device__ __forceinline__ void attend_block(const BlockRegs<KVT>& br, const QRegs<KVT>& qr, int blk, int n_valid,
                                              float scale_log2, float& m_run, float& l_run, f32x4 (&acc)[4],
                                              int lane) {
@@ -142,23 +145,22 @@ __device__ __forceinline__ void attend_block(const BlockRegs<KVT>& br, const QRe
                                                      s[t], 0, 0, 0);
     }
   }
-  // scale + mask; this lane holds positions 16t + 4q4 + r of head (lane & 15)
+  // scale (+ mask); this lane holds positions 16t + 4q4 + r of head (lane & 15)
   const int pos0 = blk * 32;
   float bmax = -INFINITY;
 #pragma unroll
   for (int t = 0; t < 2; ++t)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int pos = pos0 + 16 * t + 4 * q4 + r;
       float v = s[t][r] * scale_log2;
-      v = pos < n_valid ? v : -INFINITY;
+      if constexpr (MASK) v = pos0 + 16 * t + 4 * q4 + r < n_valid ? v : -INFINITY;
       s[t][r] = v;
       bmax = fmaxf(bmax, v);
     }
   bmax = fmaxf(bmax, __shfl_xor(bmax, 16, 64));
   bmax = fmaxf(bmax, __shfl_xor(bmax, 32, 64));
   const float m_new = fmaxf(m_run, bmax);
-  const float alpha = exp2f(m_run - m_new);   // m_run = -inf on the first block -> 0
+  const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);   // m_run = -inf on the first block -> 0
   m_run = m_new;
   float p[2][4];
   float psum = 0.f;
@@ -166,22 +168,20 @@ __device__ __forceinline__ void attend_block(const BlockRegs<KVT>& br, const QRe
   for (int t = 0; t < 2; ++t)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      p[t][r] = exp2f(s[t][r] - m_new);
+      p[t][r] = __builtin_amdgcn_exp2f(s[t][r] - m_new);
       psum += p[t][r];
     }
   l_run = l_run * alpha + psum;
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) acc[dt] *= alpha;
 
-  // zero V of masked positions in a partial last block
-  const bool partial = pos0 + 32 > n_valid;
   if constexpr (KVT == DT_BF16) {
     u32x4 pf = {pack_bf16x2(p[0][0], p[0][1]), pack_bf16x2(p[0][2], p[0][3]), pack_bf16x2(p[1][0], p[1][1]),
                 pack_bf16x2(p[1][2], p[1][3])};
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) {
       u32x4 vv = br.v[dt];
-      if (partial) {
+      if constexpr (MASK) {   // zero V of the masked positions (their cache rows may hold anything)
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
           // word w holds slots 8q4 + 2w, 8q4 + 2w + 1
@@ -201,7 +201,7 @@ __device__ __forceinline__ void attend_block(const BlockRegs<KVT>& br, const QRe
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         float vv = __uint_as_float(br.v[dt][u >> 2][u & 3]);
-        if (partial) {
+        if constexpr (MASK) {
           int pp = pos0 + (u < 4 ? 4 * q4 + u : 16 + 4 * q4 + u - 4);
           vv = pp < n_valid ? vv : 0.f;
         }
@@ -210,6 +210,21 @@ __device__ __forceinline__ void attend_block(const BlockRegs<KVT>& br, const QRe
   }
 }
 
+// The block's positions reach past n_valid only in the sequence's last block
+// (a wave-uniform test): that one takes the masked variant.
+template <int KVT>
+__device__ __forceinline__ void attend(const BlockRegs<KVT>& br, const QRegs<KVT>& qr, int blk, int n_valid,
+                                       float scale_log2, float& m_run, float& l_run, f32x4 (&acc)[4], int lane) {
+  if (blk * 32 + 32 > n_valid)
+    attend_block<KVT, true>(br, qr, blk, n_valid, scale_log2, m_run, l_run, acc, lane);
+  else
+    attend_block<KVT, false>(br, qr, blk, n_valid, scale_log2, m_run, l_run, acc, lane);
+}
+
+// minimum resident workgroups per CU (caps the registers per lane)
+#ifndef SPA_ATTN_MINB
+#define SPA_ATTN_MINB 2
+#endif
 #ifndef SPA_ATTN_RING
 #define SPA_ATTN_RING 2
 #endif
@@ -218,7 +233,7 @@ constexpr int kRing = SPA_ATTN_RING;   // 32-position blocks in registers per wa
 // KIND (ring or packed cache) is a template parameter so that sliding and
 // full layers are distinct kernels in profiles.
 template <int KVT, int KIND>
-__global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
+__global__ __launch_bounds__(256, SPA_ATTN_MINB) void k_attn(AttnArgs a) {
   __shared__ float s_m[4][16];
   __shared__ float s_l[4][16];
   __shared__ float s_o[4][kD][17];
@@ -286,7 +301,7 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
     for (; i + kRing < nbw; i += kRing) {
 #pragma unroll
       for (int r = 0; r < kRing; ++r) {
-        attend_block<KVT>(rb[r], qr, blk0 + 4 * (i + r), loc.n_valid, a.scale_log2, m_run, l_run, acc, lane);
+        attend<KVT>(rb[r], qr, blk0 + 4 * (i + r), loc.n_valid, a.scale_log2, m_run, l_run, acc, lane);
         __builtin_amdgcn_sched_barrier(0);
         load_block<KVT>(rb[r], kreg, vreg, min(blk0 + 4 * (i + r + kRing), last), lane, stream);
         __builtin_amdgcn_sched_barrier(0);
@@ -294,7 +309,7 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
     }
 #pragma unroll
     for (int r = 0; r < kRing; ++r)
-      if (i + r < nbw) attend_block<KVT>(rb[r], qr, blk0 + 4 * (i + r), loc.n_valid, a.scale_log2, m_run, l_run, acc, lane);
+      if (i + r < nbw) attend<KVT>(rb[r], qr, blk0 + 4 * (i + r), loc.n_valid, a.scale_log2, m_run, l_run, acc, lane);
   }
   l_run += __shfl_xor(l_run, 16, 64);
   l_run += __shfl_xor(l_run, 32, 64);

@@ -326,10 +326,13 @@ static spa_status op_qkv(spa_ctx* ctx, const spa_model_desc* m, const spa_layer*
 // gives about four workgroups per CU at the batch's longest sequence (long
 // chunks stream longer and leave fewer partials to merge). Depends only on
 // shapes and the device, never on the CU pool.
+#ifndef SPA_ATTN_WGS_PER_CU
+#define SPA_ATTN_WGS_PER_CU 4
+#endif
 static int attn_chunk(const spa_model_desc* m, const spa_batch* b, int n_tok, int n_cus) {
   for (int c = 4096; c > kAttnChunk; c >>= 1) {
     const long long wgs = (long long)n_tok * m->n_kv_heads * ((b->max_kv_len + c - 1) / c);
-    if (wgs >= 4LL * n_cus) return c;
+    if (wgs >= (long long)SPA_ATTN_WGS_PER_CU * n_cus) return c;
   }
   return kAttnChunk;
 }
