@@ -2,8 +2,9 @@
 // Figure 3 of the SubGPU Pipelining paper; full and sliding-window layers as
 // in its section 5.1).
 //
-// Work item = (sequence, KV head, chunk of `chunk` cached positions). The 4
-// waves of a workgroup take 32-position blocks of the chunk round-robin:
+// Work item = (sequence, KV head, chunk): a window of L positions is cut into
+// ceil(L / chunk) chunks of equal numbers of 32-position blocks. The 4 waves
+// of a workgroup take the blocks of their chunk round-robin:
 //   * S^T[pos][head] = K Q^T on MFMA: the K block streams from HBM straight
 //     into A-operand registers (16 B per lane per 16x32 tile half), all query
 //     heads of the KV group ride in the 16 B-operand columns;
@@ -274,9 +275,11 @@ __global__ __launch_bounds__(256, SPA_ATTN_MINB) void k_attn(AttnArgs a) {
   }
 
   // this wave's blocks: blk0 + wave + 4i, i < nbw
-  const int bpc = a.chunk / 32;
-  const int blk0 = c * bpc + wave;
-  const int blk_end = min(c * bpc + bpc, (loc.n_valid + 31) / 32);
+  // chunk c of n_chunks: an equal share of the window's blocks (at most
+  // chunk / 32 of them), so no chunk is a short remainder
+  const int nblk = (loc.n_valid + 31) / 32;
+  const int blk0 = c * nblk / n_chunks + wave;
+  const int blk_end = (c + 1) * nblk / n_chunks;
   const int nbw = blk_end > blk0 ? (blk_end - blk0 + 3) / 4 : 0;
   float m_run = -INFINITY, l_run = 0.f;
   f32x4 acc[4];

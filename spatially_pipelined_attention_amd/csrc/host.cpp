@@ -322,12 +322,13 @@ static spa_status op_qkv(spa_ctx* ctx, const spa_model_desc* m, const spa_layer*
   return SPA_OK;
 }
 
-// Positions per attention workgroup: the largest of 4096 .. 512 that still
-// gives about four workgroups per CU at the batch's longest sequence (long
-// chunks stream longer and leave fewer partials to merge). Depends only on
-// shapes and the device, never on the CU pool.
+// Chunk cap for attention: the largest of 4096 .. 512 that still gives at
+// least two workgroups per CU at the batch's longest sequence (long chunks
+// stream longer and leave fewer partials to merge; a window is then cut into
+// equal chunks below the cap). Depends only on shapes and the device, never
+// on the CU pool, so every schedule computes the same partials.
 #ifndef SPA_ATTN_WGS_PER_CU
-#define SPA_ATTN_WGS_PER_CU 4
+#define SPA_ATTN_WGS_PER_CU 2
 #endif
 static int attn_chunk(const spa_model_desc* m, const spa_batch* b, int n_tok, int n_cus) {
   for (int c = 4096; c > kAttnChunk; c >>= 1) {
