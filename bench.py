@@ -7,12 +7,15 @@ batch of the GPT-OSS-shaped one-GPU workload, inputs already in HBM.
 Schedules timed (same kernels, same work):
   temporal  T1 : every kernel on all CUs, one microbatch;
   temporal  Tm : the pipeline's microbatches, one after another, all CUs;
-  spatial      : two-stage pipeline on disjoint CU pools (cut, CU split, m).
-The reported `value` is the spatial pipeline's iteration time unless
---schedule says otherwise; the others are reported beside it.
+  spatial      : two-stage pipeline on disjoint CU pools (cut, CU split, m),
+                 as tuned offline (spatially_pipelined_attention_amd/tuned.json).
+With --schedule auto (the default) the three are timed and the fastest is
+the one run for the reported `value`, as an engine would select among its
+stored configurations; all three times are reported beside it. --quick runs
+only the stored selection. --schedule spatial / temporal force one.
 
-Prints one JSON line (see the keys below). --gpus N > 1 exits: this build is
-one GPU.
+Prints one JSON line (see the keys below). --gpus N > 1 exits: the pipeline
+partitions the CUs of one device.
 """
 from __future__ import annotations
 
@@ -135,7 +138,7 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="gptoss_36l_b64")
-    ap.add_argument("--schedule", choices=["spatial", "temporal"], default="spatial")
+    ap.add_argument("--schedule", choices=["auto", "spatial", "temporal"], default="auto")
     ap.add_argument("--cut", type=int, default=None)
     ap.add_argument("--micro", type=int, default=None)
     ap.add_argument("--cu-a", type=int, default=None, help="CUs of stage A (multiple of 8)")
@@ -207,22 +210,42 @@ def main():
         return ms, kt
 
     # comparison schedules first (clean timing), then the reported one with the
-    # attention-kernel events live inside its timed region
-    if not args.quick:
+    # attention-kernel timer live inside its timed region
+    cu_s = cfg.get("cu_a_sliding") or cfg["cu_a"]
+    sp_label = (f"spatial cut={cfg['cut']} m={m} cu_a={cfg['cu_a']}/{n_cus}"
+                + ("" if cu_s == cfg["cu_a"] else f" (sliding layers {cu_s}/{n_cus})"))
+    schedule = args.schedule
+    if schedule == "auto":
+        if args.quick:
+            sel = cfg.get("selected", {"schedule": "spatial"})
+            schedule = sel["schedule"]
+            if schedule == "temporal":
+                m = int(sel.get("n_micro", 1))
+        else:
+            t1 = run_schedule("temporal_T1", 0, 1, None, ws1)[0]
+            tm = run_schedule(f"temporal_T{m}", cfg["cut"], m, None, ws)[0] if m > 1 else t1
+            tsp = run_schedule("spatial", cfg["cut"], m, cfg["cu_a"], ws, cu_s=cfg.get("cu_a_sliding"))[0]
+            best = min((t1, "temporal", 1), (tm, "temporal", m), (tsp, "spatial", m))
+            schedule = best[1]
+            m = best[2]
+    elif not args.quick:
         run_schedule("temporal_T1", 0, 1, None, ws1)
         if m > 1:
             run_schedule(f"temporal_T{m}", cfg["cut"], m, None, ws)
-        if args.schedule == "temporal":
+        if schedule == "temporal":
             run_schedule("spatial", cfg["cut"], m, cfg["cu_a"], ws, cu_s=cfg.get("cu_a_sliding"))
-    if args.schedule == "spatial":
-        ms, (k_ms, k_n) = run_schedule("reported", cfg["cut"], m, cfg["cu_a"], ws, timed_cls=B.KC_ATTN_FULL,
+    wsr = ws1 if m == 1 else (ws if m == cfg["n_micro"] else dw.workspace(n_micro=m))
+    if schedule == "spatial":
+        ms, (k_ms, k_n) = run_schedule("reported", cfg["cut"], m, cfg["cu_a"], wsr, timed_cls=B.KC_ATTN_FULL,
                                        cu_s=cfg.get("cu_a_sliding"))
-        cu_s = cfg.get("cu_a_sliding") or cfg["cu_a"]
-        sched = (f"spatial cut={cfg['cut']} m={m} cu_a={cfg['cu_a']}/{n_cus}"
-                 + ("" if cu_s == cfg["cu_a"] else f" (sliding layers {cu_s}/{n_cus})"))
-    else:   # temporal with the configured microbatch count (--micro 1 for T1)
-        ms, (k_ms, k_n) = run_schedule("reported", cfg["cut"], m, None, ws, timed_cls=B.KC_ATTN_FULL)
+        sched = sp_label
+    else:   # temporal with the selected (or configured) microbatch count
+        ms, (k_ms, k_n) = run_schedule("reported", cfg["cut"], m, None, wsr, timed_cls=B.KC_ATTN_FULL)
         sched = f"temporal m={m}"
+    if args.schedule == "auto":
+        sched += " (the fastest of " + ", ".join(k for k in results if k != "reported") + ")" if not args.quick \
+            else " (the stored selection)"
+    ws = wsr
     errs = B.spa_workspace_errors(ctx, ws)
     if args.copy_calibration > 0:
         src = torch.empty(args.copy_calibration, dtype=torch.uint8, device="cuda")

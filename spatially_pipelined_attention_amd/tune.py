@@ -1,7 +1,8 @@
 """Offline tuning of the spatial pipeline for one workload (section 4 of the
 SubGPU Pipelining paper: search offline, select the stored configuration at
 run time). Runs spa_pipeline_tune on the GPU with the workload's own inputs
-and writes the best point to a JSON file, merged with what is there:
+and writes the best spatial point, the temporal times and the selection (the
+faster of the two kinds) to a JSON file, merged with what is there:
 
     python -m spatially_pipelined_attention_amd.tune --workload gptoss_36l_b64 --out tuned.json
 """
@@ -44,9 +45,15 @@ def main(argv=None):
     best, pts = B.spa_pipeline_tune(ctx, dw.m, dw.layers_c, dw.batch, ws, sp, torch.cuda.current_stream())
     dt = time.time() - t0
     temporal = {p.n_micro: p.ms for p in pts if p.cu_a == 0}
+    # run-time selection among the stored configurations: the best spatial
+    # point, or a temporal schedule when one is faster
+    t_m, t_ms = min(temporal.items(), key=lambda kv: kv[1])
+    selected = {"schedule": "spatial", "n_micro": best.n_micro} if best.ms <= t_ms else \
+        {"schedule": "temporal", "n_micro": t_m}
     entry = {"cut": best.cut, "n_micro": best.n_micro, "cu_a": best.cu_a, "cu_a_sliding": best.cu_a_sliding,
              "ms": round(best.ms, 4),
              "temporal_ms": {str(k): round(v, 4) for k, v in sorted(temporal.items())},
+             "selected": selected,
              "points": len(pts), "tune_seconds": round(dt, 1), "n_cus": B.spa_device_cus(ctx)}
     for p in pts:
         print(f"cut={p.cut:2d} m={p.n_micro} cu_a={p.cu_a:3d}/{p.cu_a_sliding:3d}: {p.ms:.3f} ms", flush=True)
