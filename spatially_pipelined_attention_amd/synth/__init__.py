@@ -110,6 +110,10 @@ WORKLOADS: Dict[str, Workload] = {
     # the same with fp8 e4m3 experts (per-output-channel fp32 scale)
     "gptoss_36l_fp8": Workload("gptoss_36l_fp8", 1005, 2880, 64, 8, 64, 128, 4, 4, 2880, 128, 36,
                                64, 1024, 8192, _alternating(36), "bf16", "e4m3", "bf16"),
+    # the SubGPU Pipelining paper's own shape (section 5.1: KV history 32,768):
+    # every sequence at 32,768 positions, otherwise the 36-layer share above
+    "gptoss_36l_kv32k": Workload("gptoss_36l_kv32k", 1006, 2880, 64, 8, 64, 128, 4, 4, 2880, 128, 36,
+                                 64, 32768, 32768, _alternating(36), "bf16", "bf16", "bf16"),
 }
 
 
