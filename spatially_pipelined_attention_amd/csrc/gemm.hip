@@ -102,7 +102,10 @@ __global__ __launch_bounds__(256, 2) void k_gemm(GemmArgs a) {
   if (nks > 0) {
     u32x4 Wr[P][CT], Xr[P][MT];
     const u32x4 zero = {0u, 0u, 0u, 0u};
-    const int mt_live = __builtin_amdgcn_readfirstlane((rows_here + 15) >> 4);
+#ifndef SPA_GEMM_ALL_TILES
+#define SPA_GEMM_ALL_TILES 0
+#endif
+    const int mt_live = SPA_GEMM_ALL_TILES ? MT : __builtin_amdgcn_readfirstlane((rows_here + 15) >> 4);
 #pragma unroll
     for (int p = 0; p < P; ++p)
 #pragma unroll
@@ -296,6 +299,8 @@ static hipError_t launch_ct(const GemmArgs& a, hipStream_t st) {
   if (a.tile_cols == 64) return launch_mt<WT, EPI, 4>(a, st);
   if constexpr (WT != DT_F32) {
     if (a.tile_cols == 32) return launch_mt<WT, EPI, 2>(a, st);
+  } else if constexpr (EPI == EPI_PARTIAL) {
+    if (a.tile_cols == 16) return launch_mt<WT, EPI, 1>(a, st);   // the router: few outputs, many workgroups
   }
   return hipErrorInvalidValue;
 }

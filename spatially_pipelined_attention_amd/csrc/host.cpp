@@ -83,9 +83,13 @@ GemmPlan plan_gemm(int kc, const spa_model_desc* m, int n_tok, int n_cus) {
   switch (kc) {
     case KC_QKV: K = m->hidden; p.ks = ks_of(m->dense_dtype); N = (m->n_q_heads + 2 * m->n_kv_heads) * m->head_dim; break;
     case KC_OPROJ: K = m->n_q_heads * m->head_dim; p.ks = ks_of(m->dense_dtype); N = m->hidden; break;
-    case KC_ROUTER: K = m->hidden; p.ks = 16; N = m->n_experts; break;
+    case KC_ROUTER: K = m->hidden; p.ks = 16; N = m->n_experts; p.tile_cols = 16; break;
     case KC_GATEUP: K = m->hidden; p.ks = ks_of(m->expert_dtype); N = 2 * m->inter; groups = m->n_resident;
-      p.epi = EPI_SWIGLU; break;
+      p.epi = EPI_SWIGLU;
+#ifdef SPA_GEMM_GU_TC
+      if (m->expert_dtype != SPA_F32) p.tile_cols = SPA_GEMM_GU_TC;
+#endif
+      break;
     case KC_DOWN: K = m->inter; p.ks = ks_of(m->expert_dtype); N = m->hidden; groups = m->n_resident; break;
     default: break;
   }
@@ -108,7 +112,10 @@ GemmPlan plan_gemm(int kc, const spa_model_desc* m, int n_tok, int n_cus) {
     busy_blocks = std::min(p.rb_stride, std::max(1, std::min(groups, R)));
   }
   const int nks = K / p.ks;
-  const int target = std::max(256, (n_cus * 5) / 4);
+#ifndef SPA_GEMM_TARGET_X4
+#define SPA_GEMM_TARGET_X4 5
+#endif
+  const int target = std::max(256, (n_cus * SPA_GEMM_TARGET_X4) / 4);
   int S = (target + p.n_tiles * busy_blocks - 1) / (p.n_tiles * busy_blocks);
   S = std::min(S, std::max(1, nks / 8));   // two k-steps per wave at least
   S = std::min(S, 16);                     // the finish kernels sum at most 16 splits
