@@ -276,10 +276,17 @@ spa_status spa_pool_probe(spa_pool* p, int32_t n_blocks, uint32_t* ids_out, int3
 spa_status spa_pool_destroy(spa_pool* p);
 
 /* --------------------------------------------------------- the pipeline
- * theta = (D = 2 stages, w = 0, cut, CU split, microbatch count) of section
- * 3.1. Stage A holds the segment up to the cut, stage B the rest:
+ * theta = (D = 2 stages, w, cut, CU split, microbatch count) of section
+ * 3.1. Cuts 0 and 1 (w = 0): stage A holds the segment up to the cut, stage
+ * B the rest:
  *   cut 0: A = Norm+QKV, attention, output projection (+ residual) | B = router ... combine
  *   cut 1: A = Norm+QKV, attention, output projection, router       | B = experts, combine
+ * Cut 2, the "Macro" design of section 5.3.2 (w = 1 over a two-layer
+ * period): stage A runs only the attention of full layers; stage B runs
+ * everything else - per full layer F and microbatch mu, the rest of the
+ * previous full layer (output projection .. combine), the sliding layers
+ * in between, and F's Norm+QKV - so B(F, mu) -> A(F, mu) -> B(next, mu).
+ * Sliding-layer pools are not used by cut 2.
  * Microbatch mu is the contiguous token slice [mu*B/m, (mu+1)*B/m). Tasks are
  * dispatched region-major, then microbatch (a topological order of the data
  * edges, section 3.2); each stage runs its tasks in that order (stage FIFO);
@@ -288,7 +295,7 @@ spa_status spa_pool_destroy(spa_pool* p);
  * stream waits for it (stream value write/wait; events where the runtime
  * lacks them). */
 typedef struct spa_pipeline_cfg {
-  int32_t cut;        /* 0 or 1 */
+  int32_t cut;        /* 0, 1 or 2 (Macro) */
   int32_t n_micro;    /* m, divides the batch */
 } spa_pipeline_cfg;
 
@@ -342,8 +349,8 @@ spa_status spa_pipeline_destroy(spa_pipeline* p);
  * they matter). The workspace must fit every point (the largest of
  * spa_workspace_query() over the microbatch counts). */
 typedef struct spa_tune_space {
-  int32_t n_cuts;        /* 1 or 2 entries of cuts */
-  int32_t cuts[2];
+  int32_t n_cuts;        /* 1 to 3 entries of cuts (each 0, 1 or 2) */
+  int32_t cuts[3];
   int32_t n_micros;      /* 1..4 entries of micros, each dividing the batch */
   int32_t micros[4];
   int32_t cu_step;       /* grid spacing of stage A's CU count: a multiple of the XCD count */

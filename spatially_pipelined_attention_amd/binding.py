@@ -62,7 +62,7 @@ class spa_pipeline_cfg(C.Structure):
 
 
 class spa_tune_space(C.Structure):
-    _fields_ = [("n_cuts", C.c_int32), ("cuts", C.c_int32 * 2), ("n_micros", C.c_int32), ("micros", C.c_int32 * 4),
+    _fields_ = [("n_cuts", C.c_int32), ("cuts", C.c_int32 * 3), ("n_micros", C.c_int32), ("micros", C.c_int32 * 4),
                 ("cu_step", C.c_int32), ("cu_min", C.c_int32), ("warmup", C.c_int32), ("reps", C.c_int32),
                 ("refine", C.c_int32), ("per_kind", C.c_int32)]
 

@@ -602,6 +602,38 @@ spa_status run_segment_a(spa_ctx* ctx, const spa_model_desc* m, const spa_layer*
   return SPA_OK;
 }
 
+// The layer in three pieces around its attention (the Macro cut):
+// before = [first layer: RMSNorm of x] + QKV and KV append; attention;
+// after = output projection, router, experts, combine.
+spa_status run_layer_before_attn(spa_ctx* ctx, const spa_model_desc* m, const spa_layer* l, const spa_batch* b,
+                                 int tok0, int n_tok, const Slot& s, bool first_layer, hipStream_t st,
+                                 TimingHook* th) {
+  spa_status rc;
+  float* x = b->x + (size_t)tok0 * m->hidden;
+  if (first_layer) {
+    spa_route_bufs none{};
+    if ((rc = op_combine(m, x, nullptr, nullptr, nullptr, none, n_tok, x, l->gamma1, s.xn, st, nullptr))) return rc;
+  }
+  return op_qkv(ctx, m, l, b, tok0, n_tok, s.xn, s.q, s, st, th);
+}
+
+spa_status run_layer_attn(spa_ctx* ctx, const spa_model_desc* m, const spa_layer* l, const spa_batch* b, int tok0,
+                          int n_tok, const WsLayout& W, const Slot& s, hipStream_t st, TimingHook* th) {
+  return op_attn(ctx, m, l, b, tok0, n_tok, s.q, s.o, W, s, st, th);
+}
+
+spa_status run_layer_after_attn(spa_ctx* ctx, const spa_model_desc* m, const spa_layer* l, int layer_index,
+                                const spa_layer* next, const spa_batch* b, int tok0, int n_tok, const WsLayout& W,
+                                const Slot& s, hipStream_t st, TimingHook* th) {
+  spa_status rc;
+  float* x = b->x + (size_t)tok0 * m->hidden;
+  const bool fp8 = m->expert_dtype == SPA_E4M3, ebf = m->expert_dtype == SPA_BF16;
+  if ((rc = op_oproj(ctx, m, l, x, s.o, n_tok, s.h, s.hn_f32, ebf ? s.hn_bf16 : nullptr, fp8 ? s.hn8 : nullptr,
+                     fp8 ? s.hn8_scale : nullptr, s, st, th)))
+    return rc;
+  return run_segment_b(ctx, m, l, layer_index, next, b, tok0, n_tok, W, s, false, st, th);
+}
+
 spa_status run_segment_b(spa_ctx* ctx, const spa_model_desc* m, const spa_layer* l, int layer_index,
                          const spa_layer* next, const spa_batch* b, int tok0, int n_tok, const WsLayout& W,
                          const Slot& s, bool with_router, hipStream_t st, TimingHook* th) {

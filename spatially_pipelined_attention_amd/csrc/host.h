@@ -114,6 +114,16 @@ spa_status run_segment_a(spa_ctx* ctx, const spa_model_desc* m, const spa_layer*
 spa_status run_segment_b(spa_ctx* ctx, const spa_model_desc* m, const spa_layer* l, int layer_index,
                          const spa_layer* next, const spa_batch* b, int tok0, int n_tok, const WsLayout& W,
                          const Slot& s, bool with_router, hipStream_t st, TimingHook* th);
+// The layer around its attention (for the Macro cut): before (first layer:
+// RMSNorm of x; QKV, KV append), the attention, after (output projection to
+// combine).
+spa_status run_layer_before_attn(spa_ctx* ctx, const spa_model_desc* m, const spa_layer* l, const spa_batch* b,
+                                 int tok0, int n_tok, const Slot& s, bool first_layer, hipStream_t st, TimingHook* th);
+spa_status run_layer_attn(spa_ctx* ctx, const spa_model_desc* m, const spa_layer* l, const spa_batch* b, int tok0,
+                          int n_tok, const WsLayout& W, const Slot& s, hipStream_t st, TimingHook* th);
+spa_status run_layer_after_attn(spa_ctx* ctx, const spa_model_desc* m, const spa_layer* l, int layer_index,
+                                const spa_layer* next, const spa_batch* b, int tok0, int n_tok, const WsLayout& W,
+                                const Slot& s, hipStream_t st, TimingHook* th);
 spa_status clear_errors(void* ws, hipStream_t st);
 
 }  // namespace spa

@@ -169,7 +169,7 @@ static spa_status create_impl(spa_ctx* ctx, const spa_model_desc* m, const spa_p
   if (!ctx || !cfg || !out) return fail(SPA_EINVAL, "bad argument");
   spa_status rc = validate_model(m);
   if (rc) return rc;
-  if (cfg->cut != 0 && cfg->cut != 1) return fail(SPA_EINVAL, "cut must be 0 or 1");
+  if (cfg->cut < 0 || cfg->cut > 2) return fail(SPA_EINVAL, "cut must be 0, 1 or 2");
   if (cfg->n_micro < 1) return fail(SPA_EINVAL, "n_micro must be >= 1");
   const bool any = a_full || b_full || a_slide || b_slide;
   const bool all = a_full && b_full && a_slide && b_slide;
@@ -279,6 +279,59 @@ static spa_status harvest_timing(spa_pipeline* p) {
   return SPA_OK;
 }
 
+// The Macro cut (P1 section 5.3.2): stage A runs only the full-attention
+// launches; stage B runs everything else. For each full layer F, microbatch
+// mu's stage-B segment is: what follows the previous full layer's attention
+// (output projection .. combine), every sliding layer in between, and F's
+// Norm+QKV; A(F, mu) waits for that segment, the next segment of mu waits for
+// A(F, mu). Hand-off values: base + F + 1 for full layer F.
+static spa_status run_macro(spa_pipeline* p, const spa_layer* layers, const spa_batch* b, void* ws,
+                            const WsLayout& W, int bm, TimingHook* thp, uint64_t base) {
+  const spa_model_desc* m = &p->m;
+  const int n_micro = p->cfg.n_micro, L = m->n_layers;
+  const hipStream_t sa = p->ak[SPA_FULL]->stream, sb = p->bk[SPA_FULL]->stream;
+  const bool vs = p->value_sync;
+  uint64_t* done_a = p->flags;
+  uint64_t* done_b = p->flags ? p->flags + n_micro : nullptr;
+  auto next_of = [&](int l) { return l + 1 < L ? &layers[l + 1] : nullptr; };
+  spa_status rc;
+  int prev = -1;   // the previous full layer
+  for (int F = 0; F <= L; ++F) {
+    const bool end = F == L;
+    if (!end && layers[F].kind != SPA_FULL) continue;
+    for (int mu = 0; mu < n_micro; ++mu) {
+      const Slot s = slot_ptrs(W, ws, mu);
+      const int tok0 = mu * bm;
+      if (prev >= 0) {
+        if (vs) SPA_HIP(hipStreamWaitValue64(sb, done_a + mu, base + (uint64_t)prev + 1, hipStreamWaitValueGte, ~0ull));
+        else SPA_HIP(hipStreamWaitEvent(sb, p->evA[(size_t)prev * n_micro + mu], 0));
+        if ((rc = run_layer_after_attn(p->ctx, m, &layers[prev], prev, next_of(prev), b, tok0, bm, W, s, sb, thp)))
+          return rc;
+      }
+      for (int l = prev + 1; l < F; ++l) {   // the layers in between run whole on stage B
+        if ((rc = run_layer_before_attn(p->ctx, m, &layers[l], b, tok0, bm, s, l == 0, sb, thp))) return rc;
+        if ((rc = run_layer_attn(p->ctx, m, &layers[l], b, tok0, bm, W, s, sb, thp))) return rc;
+        if ((rc = run_layer_after_attn(p->ctx, m, &layers[l], l, next_of(l), b, tok0, bm, W, s, sb, thp))) return rc;
+      }
+      if (end) continue;
+      if ((rc = run_layer_before_attn(p->ctx, m, &layers[F], b, tok0, bm, s, F == 0, sb, thp))) return rc;
+      if (vs) SPA_HIP(hipStreamWriteValue64(sb, done_b + mu, base + (uint64_t)F + 1, 0));
+      else SPA_HIP(hipEventRecord(p->evB[(size_t)F * n_micro + mu], sb));
+    }
+    if (end) break;
+    for (int mu = 0; mu < n_micro; ++mu) {
+      const Slot s = slot_ptrs(W, ws, mu);
+      if (vs) SPA_HIP(hipStreamWaitValue64(sa, done_b + mu, base + (uint64_t)F + 1, hipStreamWaitValueGte, ~0ull));
+      else SPA_HIP(hipStreamWaitEvent(sa, p->evB[(size_t)F * n_micro + mu], 0));
+      if ((rc = run_layer_attn(p->ctx, m, &layers[F], b, mu * bm, bm, W, s, sa, thp))) return rc;
+      if (vs) SPA_HIP(hipStreamWriteValue64(sa, done_a + mu, base + (uint64_t)F + 1, 0));
+      else SPA_HIP(hipEventRecord(p->evA[(size_t)F * n_micro + mu], sa));
+    }
+    prev = F;
+  }
+  return SPA_OK;
+}
+
 spa_status spa_pipeline_run(spa_pipeline* p, const spa_layer* layers, const spa_batch* b, void* ws, size_t ws_bytes,
                             void* caller_stream) {
   if (!p || !layers || !b) return fail(SPA_EINVAL, "bad argument");
@@ -333,6 +386,15 @@ spa_status spa_pipeline_run(spa_pipeline* p, const spa_layer* layers, const spa_
   // a run that fails midway still consumes its values: the next run never
   // mistakes one of its writes for its own
   const uint64_t base = p->runs++ * (uint64_t)m->n_layers;
+  if (!temporal && p->cfg.cut == 2) {
+    rc = run_macro(p, layers, b, ws, W, bm, thp, base);
+    if (rc) return rc;
+    for (size_t i = 0; i < streams.size(); ++i) {
+      SPA_HIP(hipEventRecord(p->ev_end[i], streams[i]));
+      SPA_HIP(hipStreamWaitEvent(cs, p->ev_end[i], 0));
+    }
+    return SPA_OK;
+  }
   for (int l = 0; l < m->n_layers; ++l) {
     const hipStream_t sa = stream_a(&layers[l]), sb = stream_b(&layers[l]);
     for (int mu = 0; mu < n_micro; ++mu) {
@@ -522,11 +584,11 @@ extern "C" spa_status spa_pipeline_tune(spa_ctx* ctx, const spa_model_desc* m, c
                                         int32_t* n_points, void* stream) {
   if (!ctx || !m || !layers || !b || !ws || !sp || !best_out) return fail(SPA_EINVAL, "bad argument");
   const int nx = ctx->n_xcd;
-  if (sp->n_cuts < 1 || sp->n_cuts > 2 || sp->n_micros < 1 || sp->n_micros > 4) return fail(SPA_EINVAL, "bad space");
+  if (sp->n_cuts < 1 || sp->n_cuts > 3 || sp->n_micros < 1 || sp->n_micros > 4) return fail(SPA_EINVAL, "bad space");
   if (sp->cu_step < nx || sp->cu_step % nx || sp->cu_min < nx || sp->cu_min % nx || sp->reps < 1 || sp->warmup < 0)
     return fail(SPA_EINVAL, "cu_step and cu_min must be positive multiples of the XCD count; reps >= 1");
   for (int i = 0; i < sp->n_cuts; ++i)
-    if (sp->cuts[i] != 0 && sp->cuts[i] != 1) return fail(SPA_EINVAL, "cut must be 0 or 1");
+    if (sp->cuts[i] < 0 || sp->cuts[i] > 2) return fail(SPA_EINVAL, "cut must be 0, 1 or 2");
   for (int i = 0; i < sp->n_micros; ++i)
     if (sp->micros[i] < 1 || b->batch % sp->micros[i]) return fail(SPA_EINVAL, "each microbatch count must divide the batch");
   TuneCtx t{ctx, m, layers, b, ws, ws_bytes, sp, (hipStream_t)stream, nullptr, nullptr};
@@ -542,19 +604,20 @@ extern "C" spa_status spa_pipeline_tune(spa_ctx* ctx, const spa_model_desc* m, c
   for (int mi = 0; !rc && mi < sp->n_micros; ++mi) {
     double ms;
     rc = measure(t, 0, sp->micros[mi], 0, 0, &ms);   // temporal reference
-    for (int ci = 0; !rc && ci < sp->n_cuts; ++ci)
+    for (int ci = 0; !rc && ci < sp->n_cuts; ++ci) {
+      const bool pk = t.per_kind && sp->cuts[ci] != 2;   // the Macro cut has one split
       for (int cf = sp->cu_min; !rc && cf <= ctx->n_cus - sp->cu_min; cf += sp->cu_step)
-        for (int cs = t.per_kind ? sp->cu_min : cf; !rc && cs <= (t.per_kind ? ctx->n_cus - sp->cu_min : cf);
-             cs += sp->cu_step) {
+        for (int cs = pk ? sp->cu_min : cf; !rc && cs <= (pk ? ctx->n_cus - sp->cu_min : cf); cs += sp->cu_step) {
           rc = measure(t, sp->cuts[ci], sp->micros[mi], cf, cs, &ms);
           if (!rc && ms < best.ms) best = spa_tune_point{sp->cuts[ci], sp->micros[mi], cf, cs, ms};
         }
+    }
   }
   if (!rc && sp->refine && best.cu_a > 0) {
     t.cut = best.cut;
     t.n_micro = best.n_micro;
     for (int kind : {SPA_FULL, SPA_SLIDING}) {   // one line search per layer kind (one without per_kind)
-      if (!t.per_kind && kind == SPA_SLIDING) break;
+      if ((!t.per_kind || best.cut == 2) && kind == SPA_SLIDING) break;
       t.refine_kind = kind;
       t.fixed_full = best.cu_a;
       t.fixed_slide = best.cu_a_sliding;
@@ -568,7 +631,7 @@ extern "C" spa_status spa_pipeline_tune(spa_ctx* ctx, const spa_model_desc* m, c
       if (v < best.ms) {
         if (kind == SPA_FULL) {
           best.cu_a = alloc[0];
-          if (!t.per_kind) best.cu_a_sliding = alloc[0];
+          if (!t.per_kind || best.cut == 2) best.cu_a_sliding = alloc[0];
         } else {
           best.cu_a_sliding = alloc[0];
         }

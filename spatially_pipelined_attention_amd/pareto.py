@@ -37,7 +37,7 @@ def main(argv=None):
     ap.add_argument("--workload", default="gptoss_36l_fp8")
     ap.add_argument("--batches", default="16,64,256,1024")
     ap.add_argument("--micros", default="1,2,4,8")
-    ap.add_argument("--cuts", default="0,1")
+    ap.add_argument("--cuts", default="0,1,2")
     ap.add_argument("--cu-step", type=int, default=32)
     ap.add_argument("--cu-min", type=int, default=32)
     ap.add_argument("--reps", type=int, default=3)
@@ -51,7 +51,7 @@ def main(argv=None):
 
     base = synth.WORKLOADS[a.workload]
     ctx = B.spa_init(0)
-    cuts = [int(x) for x in a.cuts.split(",")][:2]
+    cuts = [int(x) for x in a.cuts.split(",")][:3]
     result = {"workload": a.workload, "n_cus": B.spa_device_cus(ctx), "batches": {}}
     points = []
     for bsz in [int(x) for x in a.batches.split(",")]:
@@ -62,7 +62,7 @@ def main(argv=None):
         torch.cuda.synchronize()
         setup = time.time() - t0
         ws = max((dw.workspace(n_micro=mm) for mm in micros), key=lambda t: t.numel())
-        sp = B.spa_tune_space(len(cuts), (B.C.c_int32 * 2)(*(cuts + [0] * (2 - len(cuts)))),
+        sp = B.spa_tune_space(len(cuts), (B.C.c_int32 * 3)(*(cuts + [0] * (3 - len(cuts)))),
                               len(micros), (B.C.c_int32 * 4)(*(micros + [0] * (4 - len(micros)))),
                               a.cu_step, a.cu_min, a.warmup, a.reps, 1, 0)
         t0 = time.time()

@@ -20,7 +20,7 @@ def main(argv=None):
     ap.add_argument("--workload", default="gptoss_36l_b64")
     ap.add_argument("--out", required=True)
     ap.add_argument("--micros", default="1,2,4")
-    ap.add_argument("--cuts", default="0,1")
+    ap.add_argument("--cuts", default="0,1,2")
     ap.add_argument("--cu-step", type=int, default=32)
     ap.add_argument("--cu-min", type=int, default=32)
     ap.add_argument("--reps", type=int, default=5)
@@ -34,11 +34,11 @@ def main(argv=None):
 
     wl = synth.WORKLOADS[a.workload]
     micros = [int(x) for x in a.micros.split(",") if wl.batch % int(x) == 0][:4]
-    cuts = [int(x) for x in a.cuts.split(",")][:2]
+    cuts = [int(x) for x in a.cuts.split(",")][:3]
     dw = DeviceWorkload(wl)
     ctx = B.spa_init(0)
     ws = max((dw.workspace(n_micro=mm) for mm in micros), key=lambda t: t.numel())
-    sp = B.spa_tune_space(len(cuts), (B.C.c_int32 * 2)(*(cuts + [0] * (2 - len(cuts)))),
+    sp = B.spa_tune_space(len(cuts), (B.C.c_int32 * 3)(*(cuts + [0] * (3 - len(cuts)))),
                           len(micros), (B.C.c_int32 * 4)(*(micros + [0] * (4 - len(micros)))),
                           a.cu_step, a.cu_min, a.warmup, a.reps, 1, a.per_kind)
     t0 = time.time()

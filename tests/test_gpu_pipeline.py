@@ -88,7 +88,8 @@ def test_masks_rejected_before_launch(env):
 
 @pytest.mark.parametrize("cut,n_micro,cu_a,cu_s", [(0, 2, 128, None), (1, 2, 64, None), (0, 4, 192, None),
                                                     (1, 4, 96, None), (0, 1, 128, None),
-                                                    (1, 2, 160, 96), (0, 4, 64, 192)])
+                                                    (1, 2, 160, 96), (0, 4, 64, 192),
+                                                    (2, 2, 96, None), (2, 4, 160, None), (2, 1, 64, None)])
 def test_spatial_equals_temporal_bitwise(env, cut, n_micro, cu_a, cu_s):
     """cu_s: a different split for sliding layers (pools per layer kind)."""
     print(f"[case] cut={cut} m={n_micro} cu_a={cu_a} cu_s={cu_s}", flush=True)
@@ -104,6 +105,9 @@ def test_repeat_runs_are_bitwise_identical(env):
     a = _run(env, 0, 2, 128)
     b = _run(env, 0, 2, 128)
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+    c = _run(env, 2, 2, 128)   # the Macro cut: its hand-off values keep growing over runs
+    d = _run(env, 2, 2, 128)
+    assert torch.equal(c[0], d[0]) and torch.equal(c[1], d[1]) and torch.equal(a[0], c[0])
 
 
 def test_one_microbatch_close_to_four(env):
@@ -133,7 +137,7 @@ def test_one_microbatch_close_to_four(env):
 
 def test_tuner_returns_a_measured_point_of_the_space(env):
     B, dw, ctx = env["B"], env["dw"], env["ctx"]
-    sp = B.spa_tune_space(1, (B.C.c_int32 * 2)(0, 0), 1, (B.C.c_int32 * 4)(2, 0, 0, 0), 64, 64, 1, 2, 1, 0)
+    sp = B.spa_tune_space(1, (B.C.c_int32 * 3)(0, 0, 0), 1, (B.C.c_int32 * 4)(2, 0, 0, 0), 64, 64, 1, 2, 1, 0)
     ws = dw.workspace(n_micro=2)
     best, pts = B.spa_pipeline_tune(ctx, dw.m, dw.layers_c, dw.batch, ws, sp, torch.cuda.current_stream())
     grid = [p for p in pts if p.cu_a in (64, 128, 192)]
@@ -147,22 +151,33 @@ def test_tuner_returns_a_measured_point_of_the_space(env):
 def test_tuner_rejects_bad_space(env):
     B, dw, ctx = env["B"], env["dw"], env["ctx"]
     ws = dw.workspace(n_micro=2)
-    bad = B.spa_tune_space(1, (B.C.c_int32 * 2)(0, 0), 1, (B.C.c_int32 * 4)(3, 0, 0, 0), 64, 64, 1, 2, 1, 0)
+    bad = B.spa_tune_space(1, (B.C.c_int32 * 3)(0, 0, 0), 1, (B.C.c_int32 * 4)(3, 0, 0, 0), 64, 64, 1, 2, 1, 0)
     with pytest.raises(B.SpaError):
         B.spa_pipeline_tune(ctx, dw.m, dw.layers_c, dw.batch, ws, bad)   # 3 does not divide 64
-    bad = B.spa_tune_space(1, (B.C.c_int32 * 2)(0, 0), 1, (B.C.c_int32 * 4)(2, 0, 0, 0), 12, 64, 1, 2, 1, 0)
+    bad = B.spa_tune_space(1, (B.C.c_int32 * 3)(0, 0, 0), 1, (B.C.c_int32 * 4)(2, 0, 0, 0), 12, 64, 1, 2, 1, 0)
     with pytest.raises(B.SpaError):
         B.spa_pipeline_tune(ctx, dw.m, dw.layers_c, dw.batch, ws, bad)   # step not a multiple of 8
 
 
 def test_tuner_per_kind_points(env):
     B, dw, ctx = env["B"], env["dw"], env["ctx"]
-    sp = B.spa_tune_space(1, (B.C.c_int32 * 2)(1, 0), 1, (B.C.c_int32 * 4)(2, 0, 0, 0), 96, 64, 1, 1, 0, 1)
+    sp = B.spa_tune_space(1, (B.C.c_int32 * 3)(1, 0, 0), 1, (B.C.c_int32 * 4)(2, 0, 0, 0), 96, 64, 1, 1, 0, 1)
     ws = dw.workspace(n_micro=2)
     best, pts = B.spa_pipeline_tune(ctx, dw.m, dw.layers_c, dw.batch, ws, sp, torch.cuda.current_stream())
     spatial = [(p.cu_a, p.cu_a_sliding) for p in pts if p.cu_a > 0]
     assert sorted(spatial) == [(a, s) for a in (64, 160) for s in (64, 160)]
     assert (best.cu_a, best.cu_a_sliding) in spatial
+
+
+def test_tuner_macro_cut_has_one_split(env):
+    B, dw, ctx = env["B"], env["dw"], env["ctx"]
+    sp = B.spa_tune_space(2, (B.C.c_int32 * 3)(0, 2, 0), 1, (B.C.c_int32 * 4)(2, 0, 0, 0), 96, 64, 1, 1, 0, 1)
+    ws = dw.workspace(n_micro=2)
+    best, pts = B.spa_pipeline_tune(ctx, dw.m, dw.layers_c, dw.batch, ws, sp, torch.cuda.current_stream())
+    macro = [(p.cu_a, p.cu_a_sliding) for p in pts if p.cut == 2]
+    assert sorted(macro) == [(64, 64), (160, 160)]
+    assert len([p for p in pts if p.cut == 0]) == 4   # per-kind grid for cut 0
+    assert best.ms == min(p.ms for p in pts if p.cu_a > 0)
 
 
 def test_per_kind_pools_must_be_disjoint_within_a_kind(env):
