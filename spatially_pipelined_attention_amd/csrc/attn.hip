@@ -58,6 +58,17 @@ __device__ __forceinline__ KvLoc kv_locate(const AttnArgs& a, int seq, int g, in
   return r;
 }
 
+// Element offset of o[token b][head hq][d]: row-major [n_tok][Hq * D], or
+// k-step-major over o_kmajor_rows rows (64-byte k-steps of 32 bf16 / 16 fp32)
+__device__ __forceinline__ long long o_index(const AttnArgs& a, int b, int hq, int d) {
+  const int c = hq * kD + d;
+  if (a.o_kmajor_rows > 0) {
+    const int ks = a.kv_dtype == DT_BF16 ? 32 : 16;
+    return ((long long)(c / ks) * a.o_kmajor_rows + b) * ks + c % ks;
+  }
+  return (long long)b * a.n_q_heads * kD + c;
+}
+
 template <int KVT>
 struct BlockRegs;
 
@@ -355,7 +366,7 @@ __global__ __launch_bounds__(256, SPA_ATTN_MINB) void k_attn(AttnArgs a) {
       const float f = M == -INFINITY ? 0.f : exp2f(M - MM);
       const float Z = exp2f(sink - MM) + f * l;
       const float out = f * o / Z;
-      const long long oi = ((long long)b * a.n_q_heads + hq) * kD + d;
+      const long long oi = o_index(a, b, hq, d);
       if constexpr (KVT == DT_BF16) ((uint16_t*)a.o)[oi] = f32_to_bf16(out);
       else ((float*)a.o)[oi] = out;
     } else {
@@ -420,7 +431,7 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
       }
     }
     const float out = o / Z;
-    const long long oi = ((long long)b * a.n_q_heads + hq) * kD + d;
+    const long long oi = o_index(a, b, hq, d);
     if constexpr (KVT == DT_BF16) ((uint16_t*)a.o)[oi] = f32_to_bf16(out);
     else ((float*)a.o)[oi] = out;
   }

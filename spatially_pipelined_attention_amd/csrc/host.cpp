@@ -295,16 +295,20 @@ static PartView view_of(const GemmPlan& p, const Slot& s) {
 }
 
 // Norm + QKV: q and the new K/V (cache append) from xn.
+// kmajor: the activation input (xn / o) is k-step-major over the call's rows,
+// as the pipeline's own slot buffers are; the single-operator entry points
+// take and return row-major tensors.
 static spa_status op_qkv(spa_ctx* ctx, const spa_model_desc* m, const spa_layer* l, const spa_batch* b, int tok0,
-                         int n_tok, const void* xn, void* q_out, const Slot& s, hipStream_t st, TimingHook* th) {
+                         int n_tok, const void* xn, void* q_out, const Slot& s, hipStream_t st, TimingHook* th,
+                         bool kmajor = false) {
   const GemmPlan p = plan_gemm(KC_QKV, m, n_tok, ctx->n_cus);
   GemmArgs a = gemm_args(p, s, n_tok);
   a.W = l->wqkv;
   a.K = m->hidden;
   a.N = (m->n_q_heads + 2 * m->n_kv_heads) * m->head_dim;
   a.X = xn;
-  a.x_rstride = (long long)m->hidden * esz_of(m->dense_dtype);
-  a.x_kstride = 64;
+  a.x_rstride = kmajor ? 64 : (long long)m->hidden * esz_of(m->dense_dtype);
+  a.x_kstride = kmajor ? (long long)n_tok * 64 : 64;
   QkvFinishArgs f;
   memset(&f, 0, sizeof(f));
   f.pv = view_of(p, s);
@@ -377,8 +381,10 @@ static AttnArgs attn_args(const spa_model_desc* m, const spa_layer* l, const spa
 }
 
 static spa_status op_attn(spa_ctx* ctx, const spa_model_desc* m, const spa_layer* l, const spa_batch* b, int tok0, int n_tok,
-                          const void* q, void* o, const WsLayout& W, const Slot& s, hipStream_t st, TimingHook* th) {
+                          const void* q, void* o, const WsLayout& W, const Slot& s, hipStream_t st, TimingHook* th,
+                          bool kmajor = false) {
   AttnArgs a = attn_args(m, l, b, tok0, n_tok, q, o, W, s, ctx->n_cus);
+  a.o_kmajor_rows = kmajor ? n_tok : 0;
   {
     // the attention kernel alone, timed by its own dispatch (start/stop events of the launch)
     HookScope hs(th, l->kind == SPA_FULL ? KC_ATTN_FULL : KC_ATTN_SLIDING, st, true);
@@ -393,15 +399,15 @@ static spa_status op_attn(spa_ctx* ctx, const spa_model_desc* m, const spa_layer
 // the expert input format when hn_bf16 / hn8 are given).
 static spa_status op_oproj(spa_ctx* ctx, const spa_model_desc* m, const spa_layer* l, const float* x, const void* o,
                            int n_tok, float* h, float* hn, uint16_t* hn_bf16, uint8_t* hn8, float* hn8_scale,
-                           const Slot& s, hipStream_t st, TimingHook* th) {
+                           const Slot& s, hipStream_t st, TimingHook* th, bool kmajor = false) {
   const GemmPlan p = plan_gemm(KC_OPROJ, m, n_tok, ctx->n_cus);
   GemmArgs a = gemm_args(p, s, n_tok);
   a.W = l->wo;
   a.K = m->n_q_heads * m->head_dim;
   a.N = m->hidden;
   a.X = o;
-  a.x_rstride = (long long)m->n_q_heads * m->head_dim * esz_of(m->dense_dtype);
-  a.x_kstride = 64;
+  a.x_rstride = kmajor ? 64 : (long long)m->n_q_heads * m->head_dim * esz_of(m->dense_dtype);
+  a.x_kstride = kmajor ? (long long)n_tok * 64 : 64;
   OprojFinishArgs f;
   memset(&f, 0, sizeof(f));
   f.pv = view_of(p, s);
@@ -569,8 +575,9 @@ static CombineArgs combine_args(const spa_model_desc* m, const float* h, const f
 
 static spa_status op_combine(const spa_model_desc* m, const float* h, const float* y, const GemmPlan* ypart,
                              const Slot* s, const spa_route_bufs& r, int n_tok, float* x_out, const float* gamma_next,
-                             void* xn_out, hipStream_t st, TimingHook* th) {
+                             void* xn_out, hipStream_t st, TimingHook* th, bool kmajor = false) {
   CombineArgs a = combine_args(m, h, y, ypart, s, r, n_tok, x_out, gamma_next, xn_out);
+  a.xn_kmajor_rows = kmajor ? n_tok : 0;
   HookScope hs(th, KC_COMBINE, st);
   SPA_HIP(launch_combine(a, st));
   return SPA_OK;
@@ -587,13 +594,13 @@ spa_status run_segment_a(spa_ctx* ctx, const spa_model_desc* m, const spa_layer*
   float* x = b->x + (size_t)tok0 * m->hidden;
   if (first_layer) {   // RMSNorm of the incoming residual rows
     spa_route_bufs none{};
-    if ((rc = op_combine(m, x, nullptr, nullptr, nullptr, none, n_tok, x, l->gamma1, s.xn, st, nullptr))) return rc;
+    if ((rc = op_combine(m, x, nullptr, nullptr, nullptr, none, n_tok, x, l->gamma1, s.xn, st, nullptr, true))) return rc;
   }
-  if ((rc = op_qkv(ctx, m, l, b, tok0, n_tok, s.xn, s.q, s, st, th))) return rc;
-  if ((rc = op_attn(ctx, m, l, b, tok0, n_tok, s.q, s.o, W, s, st, th))) return rc;
+  if ((rc = op_qkv(ctx, m, l, b, tok0, n_tok, s.xn, s.q, s, st, th, true))) return rc;
+  if ((rc = op_attn(ctx, m, l, b, tok0, n_tok, s.q, s.o, W, s, st, th, true))) return rc;
   const bool fp8 = m->expert_dtype == SPA_E4M3, ebf = m->expert_dtype == SPA_BF16;
   if ((rc = op_oproj(ctx, m, l, x, s.o, n_tok, s.h, s.hn_f32, ebf ? s.hn_bf16 : nullptr, fp8 ? s.hn8 : nullptr,
-                     fp8 ? s.hn8_scale : nullptr, s, st, th)))
+                     fp8 ? s.hn8_scale : nullptr, s, st, th, true)))
     return rc;
   if (with_router) {
     int32_t* rec = b->topk_out ? b->topk_out + ((size_t)layer_index * b->batch + tok0) * m->top_k : nullptr;
@@ -612,14 +619,14 @@ spa_status run_layer_before_attn(spa_ctx* ctx, const spa_model_desc* m, const sp
   float* x = b->x + (size_t)tok0 * m->hidden;
   if (first_layer) {
     spa_route_bufs none{};
-    if ((rc = op_combine(m, x, nullptr, nullptr, nullptr, none, n_tok, x, l->gamma1, s.xn, st, nullptr))) return rc;
+    if ((rc = op_combine(m, x, nullptr, nullptr, nullptr, none, n_tok, x, l->gamma1, s.xn, st, nullptr, true))) return rc;
   }
-  return op_qkv(ctx, m, l, b, tok0, n_tok, s.xn, s.q, s, st, th);
+  return op_qkv(ctx, m, l, b, tok0, n_tok, s.xn, s.q, s, st, th, true);
 }
 
 spa_status run_layer_attn(spa_ctx* ctx, const spa_model_desc* m, const spa_layer* l, const spa_batch* b, int tok0,
                           int n_tok, const WsLayout& W, const Slot& s, hipStream_t st, TimingHook* th) {
-  return op_attn(ctx, m, l, b, tok0, n_tok, s.q, s.o, W, s, st, th);
+  return op_attn(ctx, m, l, b, tok0, n_tok, s.q, s.o, W, s, st, th, true);
 }
 
 spa_status run_layer_after_attn(spa_ctx* ctx, const spa_model_desc* m, const spa_layer* l, int layer_index,
@@ -629,7 +636,7 @@ spa_status run_layer_after_attn(spa_ctx* ctx, const spa_model_desc* m, const spa
   float* x = b->x + (size_t)tok0 * m->hidden;
   const bool fp8 = m->expert_dtype == SPA_E4M3, ebf = m->expert_dtype == SPA_BF16;
   if ((rc = op_oproj(ctx, m, l, x, s.o, n_tok, s.h, s.hn_f32, ebf ? s.hn_bf16 : nullptr, fp8 ? s.hn8 : nullptr,
-                     fp8 ? s.hn8_scale : nullptr, s, st, th)))
+                     fp8 ? s.hn8_scale : nullptr, s, st, th, true)))
     return rc;
   return run_segment_b(ctx, m, l, layer_index, next, b, tok0, n_tok, W, s, false, st, th);
 }
@@ -650,7 +657,7 @@ spa_status run_segment_b(spa_ctx* ctx, const spa_model_desc* m, const spa_layer*
     return rc;
   const bool plain = dp.epi == EPI_STORE;
   return op_combine(m, s.h, plain ? s.y : nullptr, plain ? nullptr : &dp, &s, s.route, n_tok, x,
-                    next ? next->gamma1 : nullptr, s.xn, st, th);
+                    next ? next->gamma1 : nullptr, s.xn, st, th, true);
 }
 
 // ---------------------------------------------------------------------------

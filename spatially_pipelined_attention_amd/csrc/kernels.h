@@ -137,6 +137,7 @@ struct CombineArgs {
   float eps;
   void* xn_out;
   int xn_dtype;
+  int xn_kmajor_rows;       // > 0: xn is k-step-major over this many rows (64-byte k-steps)
 };
 hipError_t launch_combine(const CombineArgs& a, hipStream_t st);
 // out (a.x_out)[r] = split sum of dispatch row r of the grouped partial y (a.ypv)
@@ -165,6 +166,7 @@ struct AttnArgs {
   void* o;                  // [n_tok][Hq*D] (kv dtype)
   int* err;
   int stream_kv;            // non-temporal KV loads
+  int o_kmajor_rows;        // > 0: o is k-step-major over this many rows (64-byte k-steps)
   // optional [kSpanWords]: this launch's span on the device wall clock. The
   // first workgroup stores its start in word 0; every workgroup takes the
   // atomic max of its end into word 8 (j + 1), j = its linear index mod 16

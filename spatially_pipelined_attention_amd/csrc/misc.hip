@@ -377,8 +377,10 @@ __global__ __launch_bounds__(kRowThreads) void k_combine(CombineArgs a) {
     const int c = threadIdx.x + kRowThreads * i;
     if (c < a.H) {
       const float xn = v[i] * rstd * a.gamma_next[c];
-      if (a.xn_dtype == DT_BF16) ((uint16_t*)a.xn_out)[row + c] = f32_to_bf16(xn);
-      else ((float*)a.xn_out)[row + c] = xn;
+      const int ks = a.xn_dtype == DT_BF16 ? 32 : 16;   // elements per 64-byte k-step
+      const long long xi = a.xn_kmajor_rows > 0 ? ((long long)(c / ks) * a.xn_kmajor_rows + t) * ks + c % ks : row + c;
+      if (a.xn_dtype == DT_BF16) ((uint16_t*)a.xn_out)[xi] = f32_to_bf16(xn);
+      else ((float*)a.xn_out)[xi] = xn;
     }
   }
 }
