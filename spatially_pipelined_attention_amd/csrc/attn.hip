@@ -244,30 +244,24 @@ constexpr int kRing = SPA_ATTN_RING;   // 32-position blocks in registers per wa
 
 // KIND (ring or packed cache) is a template parameter so that sliding and
 // full layers are distinct kernels in profiles.
+struct AttnLds {
+  float m[4][16];
+  float l[4][16];
+  float o[4][kD][17];
+};
+
+#ifndef SPA_ATTN_NT
+#define SPA_ATTN_NT 1
+#endif
+constexpr bool kStreamKV = SPA_ATTN_NT != 0;   // KV is read once: non-temporal loads
+
+// Chunk c of n_chunks of (token b, KV group g): the 4 waves stream their
+// blocks, merge their states in wave order through LDS and write the output
+// (single chunk) or the chunk's partial. Every thread of the workgroup calls
+// it; it ends with a barrier, so the LDS may be reused at once.
 template <int KVT, int KIND>
-__global__ __launch_bounds__(256, SPA_ATTN_MINB) void k_attn(AttnArgs a) {
-  __shared__ float s_m[4][16];
-  __shared__ float s_l[4][16];
-  __shared__ float s_o[4][kD][17];
-
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: scalar control flow
-  const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-  const int seq = a.tok0 + b;
-  const int G = a.n_q_heads / a.n_kv_heads;
-  if (a.tspan && tid == 0 && c == 0 && g == 0 && b == 0) a.tspan[0] = wall_clock64();   // first dispatched
-  const KvLoc loc = kv_locate(a, seq, g, KIND);
-  if (!loc.ok) {
-    if (c == 0 && tid == 0 && a.err) atomicOr(a.err, ERR_KV_LEN);
-    return;
-  }
-  const int n_chunks = (loc.n_valid + a.chunk - 1) / a.chunk;
-  if (n_chunks > a.max_chunks) {   // kv_len above the planned maximum: refuse, never read past the plan
-    if (c == 0 && tid == 0 && a.err) atomicOr(a.err, ERR_KV_LEN);
-    return;
-  }
-  if (c >= n_chunks) return;
-
+__device__ __forceinline__ void attn_chunk_body(const AttnArgs& a, AttnLds& s, const KvLoc& loc, int b, int g, int c,
+                                                int n_chunks, int G, int tid, int lane, int wave) {
   constexpr int esz = KVT == DT_BF16 ? 2 : 4;
   const char* kreg = (const char*)a.k_cache + loc.base * esz;
   const char* vreg = (const char*)a.v_cache + loc.base * esz;
@@ -285,9 +279,9 @@ __global__ __launch_bounds__(256, SPA_ATTN_MINB) void k_attn(AttnArgs a) {
     for (int cc = 0; cc < 4; ++cc) qr.q[cc] = hvalid ? ld16(qrow + (16 * cc + 4 * q4) * 4) : u32x4{0u, 0u, 0u, 0u};
   }
 
-  // this wave's blocks: blk0 + wave + 4i, i < nbw
   // chunk c of n_chunks: an equal share of the window's blocks (at most
-  // chunk / 32 of them), so no chunk is a short remainder
+  // chunk / 32 of them), so no chunk is a short remainder; this wave's
+  // blocks are blk0 + 4i, i < nbw
   const int nblk = (loc.n_valid + 31) / 32;
   const int blk0 = c * nblk / n_chunks + wave;
   const int blk_end = (c + 1) * nblk / n_chunks;
@@ -297,10 +291,6 @@ __global__ __launch_bounds__(256, SPA_ATTN_MINB) void k_attn(AttnArgs a) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-#ifndef SPA_ATTN_NT
-#define SPA_ATTN_NT 1
-#endif
-  constexpr bool stream = SPA_ATTN_NT != 0;   // KV is read once: non-temporal loads
   if (nbw > 0) {
     // A ring of kRing register sets: a set is consumed, then refilled with
     // the block kRing steps ahead, so kRing - 1 blocks of loads stay in flight
@@ -310,14 +300,14 @@ __global__ __launch_bounds__(256, SPA_ATTN_MINB) void k_attn(AttnArgs a) {
     const int last = blk0 + 4 * (nbw - 1);
     BlockRegs<KVT> rb[kRing];
 #pragma unroll
-    for (int r = 0; r < kRing; ++r) load_block<KVT>(rb[r], kreg, vreg, min(blk0 + 4 * r, last), lane, stream);
+    for (int r = 0; r < kRing; ++r) load_block<KVT>(rb[r], kreg, vreg, min(blk0 + 4 * r, last), lane, kStreamKV);
     int i = 0;
     for (; i + kRing < nbw; i += kRing) {
 #pragma unroll
       for (int r = 0; r < kRing; ++r) {
         attend<KVT>(rb[r], qr, blk0 + 4 * (i + r), loc.n_valid, a.scale_log2, m_run, l_run, acc, lane);
         __builtin_amdgcn_sched_barrier(0);
-        load_block<KVT>(rb[r], kreg, vreg, min(blk0 + 4 * (i + r + kRing), last), lane, stream);
+        load_block<KVT>(rb[r], kreg, vreg, min(blk0 + 4 * (i + r + kRing), last), lane, kStreamKV);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -332,10 +322,10 @@ __global__ __launch_bounds__(256, SPA_ATTN_MINB) void k_attn(AttnArgs a) {
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) s_o[wave][16 * dt + 4 * q4 + r][hl] = acc[dt][r];
+    for (int r = 0; r < 4; ++r) s.o[wave][16 * dt + 4 * q4 + r][hl] = acc[dt][r];
   if (q4 == 0) {
-    s_m[wave][hl] = m_run;
-    s_l[wave][hl] = l_run;
+    s.m[wave][hl] = m_run;
+    s.l[wave][hl] = l_run;
   }
   __syncthreads();
 
@@ -349,14 +339,14 @@ __global__ __launch_bounds__(256, SPA_ATTN_MINB) void k_attn(AttnArgs a) {
     const int h = idx >> 6, d = idx & 63;
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) M = fmaxf(M, s_m[w][h]);
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, s.m[w][h]);
     float l = 0.f, o = 0.f;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      const float mw = s_m[w][h];
+      const float mw = s.m[w][h];
       const float f = mw == -INFINITY ? 0.f : exp2f(mw - M);
-      l += f * s_l[w][h];
-      o += f * s_o[w][d][h];
+      l += f * s.l[w][h];
+      o += f * s.o[w][d][h];
     }
     if (n_chunks == 1) {
       // the whole window was in this chunk: finish with the sink here
@@ -378,11 +368,106 @@ __global__ __launch_bounds__(256, SPA_ATTN_MINB) void k_attn(AttnArgs a) {
       }
     }
   }
+  __syncthreads();
+}
+
+// Workgroup = (chunk c, KV group g, token b).
+template <int KVT, int KIND>
+__global__ __launch_bounds__(256, SPA_ATTN_MINB) void k_attn(AttnArgs a) {
+  __shared__ AttnLds s;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: scalar control flow
+  const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int seq = a.tok0 + b;
+  const int G = a.n_q_heads / a.n_kv_heads;
+  if (a.tspan && tid == 0 && c == 0 && g == 0 && b == 0) a.tspan[0] = wall_clock64();   // first dispatched
+  const KvLoc loc = kv_locate(a, seq, g, KIND);
+  if (!loc.ok) {
+    if (c == 0 && tid == 0 && a.err) atomicOr(a.err, ERR_KV_LEN);
+    return;
+  }
+  const int n_chunks = (loc.n_valid + a.chunk - 1) / a.chunk;
+  if (n_chunks > a.max_chunks) {   // kv_len above the planned maximum: refuse, never read past the plan
+    if (c == 0 && tid == 0 && a.err) atomicOr(a.err, ERR_KV_LEN);
+    return;
+  }
+  if (c >= n_chunks) return;
+  attn_chunk_body<KVT, KIND>(a, s, loc, b, g, c, n_chunks, G, tid, lane, wave);
   if (a.tspan) {   // uniform branch: every wave of the workgroup reaches it
-    __syncthreads();
     const int j = (c + (g + b * gridDim.y) * gridDim.x) & 15;
     if (tid == 0) atomicMax(a.tspan + 8 * (j + 1), (unsigned long long)wall_clock64());
   }
+}
+
+// The same chunks, dealt to a fixed number of resident workgroups so that
+// every CU streams about the same number of bytes. Tokens are ranked by
+// their chunk length (longest first, ties by index) and their chunks listed
+// in that order, (token, KV group, chunk); item i goes to workgroup i mod W
+// in even rounds and W - 1 - (i mod W) in odd ones (a snake), each
+// workgroup working through its items one after the other. What each chunk
+// computes is exactly k_attn's, whatever W: results do not depend on the
+// grid, so the CU pool may set it.
+template <int KVT>
+__global__ __launch_bounds__(256, SPA_ATTN_MINB) void k_attn_dealt(AttnArgs a) {
+  __shared__ AttnLds s;
+  __shared__ int s_len[kDealMaxTok];     // chunk length (blocks) per token
+  __shared__ int s_nc[kDealMaxTok];      // chunks per KV group
+  __shared__ int s_first[kDealMaxTok + 1];   // first item of the rank-r token
+  __shared__ int s_tok[kDealMaxTok];     // token of rank r
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int G = a.n_q_heads / a.n_kv_heads;
+  const int n = a.n_tok;
+  if (a.tspan && tid == 0 && blockIdx.x == 0) a.tspan[0] = wall_clock64();   // first dispatched
+  for (int t = tid; t < n; t += 256) {
+    const KvLoc loc = kv_locate(a, a.tok0 + t, 0, KV_PACKED);
+    int nc = (loc.n_valid + a.chunk - 1) / a.chunk;
+    if (!loc.ok || nc > a.max_chunks) {   // refused: no items, reported once
+      if (blockIdx.x == 0 && a.err) atomicOr(a.err, ERR_KV_LEN);
+      nc = 0;
+    }
+    s_nc[t] = nc;
+    s_len[t] = nc > 0 ? ((loc.n_valid + 31) / 32 + nc - 1) / nc : 0;
+  }
+  __syncthreads();
+  for (int t = tid; t < n; t += 256) {   // rank: longer chunks first, ties by token index
+    const int lt = s_len[t];
+    int r = 0;
+    for (int u = 0; u < n; ++u) {
+      const int lu = s_len[u];
+      r += (lu > lt || (lu == lt && u < t)) ? 1 : 0;
+    }
+    s_tok[r] = t;
+  }
+  __syncthreads();
+  if (tid == 0) {   // items per rank: KV groups x chunks
+    int acc = 0;
+    for (int r = 0; r < n; ++r) {
+      s_first[r] = acc;
+      acc += a.n_kv_heads * s_nc[s_tok[r]];
+    }
+    s_first[n] = acc;
+  }
+  __syncthreads();
+  const int total = s_first[n];
+  const int W = gridDim.x, w = blockIdx.x;
+  for (int round = 0;; ++round) {
+    const int i = round * W + ((round & 1) ? W - 1 - w : w);
+    if (i >= total) break;
+    int lo = 0, hi = n - 1;   // rank of item i: the largest r with s_first[r] <= i
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_first[mid] <= i) lo = mid;
+      else hi = mid - 1;
+    }
+    const int b = s_tok[lo];
+    const int nc = s_nc[b];
+    const int rel = i - s_first[lo];
+    const int g = rel / nc, c = rel - g * nc;
+    const KvLoc loc = kv_locate(a, a.tok0 + b, g, KV_PACKED);
+    attn_chunk_body<KVT, KV_PACKED>(a, s, loc, b, g, c, nc, G, tid, lane, wave);
+  }
+  if (a.tspan && tid == 0) atomicMax(a.tspan + 8 * ((w & 15) + 1), (unsigned long long)wall_clock64());
 }
 
 // Merge the chunk partials of one (sequence, KV head) in chunk order with the
@@ -445,7 +530,21 @@ static void launch_attn_t(const AttnArgs& a, dim3 grid, hipStream_t st, hipEvent
     hipLaunchKernelGGL((k_attn<KVT, KIND>), grid, dim3(256), 0, st, a);
 }
 
+template <int KVT>
+static void launch_dealt_t(const AttnArgs& a, hipStream_t st, hipEvent_t start, hipEvent_t stop) {
+  if (start || stop)
+    hipExtLaunchKernelGGL(k_attn_dealt<KVT>, dim3(a.deal_wgs), dim3(256), 0, st, start, stop, 0, a);
+  else
+    hipLaunchKernelGGL(k_attn_dealt<KVT>, dim3(a.deal_wgs), dim3(256), 0, st, a);
+}
+
 hipError_t launch_attn(const AttnArgs& a, hipStream_t st, hipEvent_t start, hipEvent_t stop) {
+  if (a.deal_wgs > 0 && a.kv_kind == KV_PACKED) {
+    if (a.n_tok < 1 || a.n_tok > kDealMaxTok) return hipErrorInvalidValue;
+    if (a.kv_dtype == DT_BF16) launch_dealt_t<DT_BF16>(a, st, start, stop);
+    else launch_dealt_t<DT_F32>(a, st, start, stop);
+    return hipGetLastError();
+  }
   dim3 grid(a.max_chunks, a.n_kv_heads, a.n_tok);
   if (a.kv_dtype == DT_BF16) {
     if (a.kv_kind == KV_PACKED) launch_attn_t<DT_BF16, KV_PACKED>(a, grid, st, start, stop);

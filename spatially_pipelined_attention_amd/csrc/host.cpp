@@ -5,7 +5,9 @@
 
 #include <algorithm>
 #include <cmath>
+#include <mutex>
 #include <string>
+#include <unordered_map>
 
 #include "host.h"
 
@@ -214,6 +216,25 @@ Slot slot_ptrs(const WsLayout& L, void* ws, int slot) {
   return s;
 }
 
+static std::mutex g_cus_mu;
+static std::unordered_map<hipStream_t, int> g_stream_cus;
+
+void register_stream_cus(hipStream_t st, int n_cus) {
+  std::lock_guard<std::mutex> lk(g_cus_mu);
+  g_stream_cus[st] = n_cus;
+}
+
+void unregister_stream_cus(hipStream_t st) {
+  std::lock_guard<std::mutex> lk(g_cus_mu);
+  g_stream_cus.erase(st);
+}
+
+int stream_cus(hipStream_t st, int fallback) {
+  std::lock_guard<std::mutex> lk(g_cus_mu);
+  const auto it = g_stream_cus.find(st);
+  return it == g_stream_cus.end() ? fallback : it->second;
+}
+
 spa_status clear_errors(void* ws, hipStream_t st) {
   SPA_HIP(launch_fill_i32((int*)ws, 64, 0, st));
   return SPA_OK;
@@ -385,6 +406,9 @@ static spa_status op_attn(spa_ctx* ctx, const spa_model_desc* m, const spa_layer
                           bool kmajor = false) {
   AttnArgs a = attn_args(m, l, b, tok0, n_tok, q, o, W, s, ctx->n_cus);
   a.o_kmajor_rows = kmajor ? n_tok : 0;
+  // full layers: the chunks dealt to two resident workgroups per CU of the
+  // stream's pool (the chunks, and so the results, are the same either way)
+  if (l->kind == SPA_FULL && n_tok <= kDealMaxTok) a.deal_wgs = kDealWgsPerCu * stream_cus(st, ctx->n_cus);
   {
     // the attention kernel alone, timed by its own dispatch (start/stop events of the launch)
     HookScope hs(th, l->kind == SPA_FULL ? KC_ATTN_FULL : KC_ATTN_SLIDING, st, true);

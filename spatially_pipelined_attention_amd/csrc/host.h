@@ -68,6 +68,12 @@ WsLayout ws_layout(const spa_model_desc* m, int n_tok, int max_kv_len, int n_mic
 int max_chunks_for(int max_kv_len, const spa_model_desc* m);
 GemmPlan plan_gemm(int kclass, const spa_model_desc* m, int n_tok, int n_cus);
 
+// CUs a stream's kernels run on: the pool's count for a CU-masked pool
+// stream (registered by the pool), `fallback` for any other stream.
+void register_stream_cus(hipStream_t st, int n_cus);
+void unregister_stream_cus(hipStream_t st);
+int stream_cus(hipStream_t st, int fallback);
+
 // Per-slot device pointers resolved from a workspace base.
 struct Slot {
   char* base;

@@ -173,8 +173,16 @@ struct AttnArgs {
   // (spread over 16 lines, so the atomics do not queue on one address).
   // The caller presets the words to zero.
   unsigned long long* tspan;
+  // > 0: full-layer chunks dealt to this many resident workgroups
+  // (k_attn_dealt); 0: one workgroup per chunk (k_attn)
+  int deal_wgs;
 };
 constexpr int kSpanWords = 136;
+constexpr int kDealMaxTok = 256;   // tokens per launch the dealt kernel ranks in LDS
+#ifndef SPA_DEAL_WGS_PER_CU
+#define SPA_DEAL_WGS_PER_CU 2
+#endif
+constexpr int kDealWgsPerCu = SPA_DEAL_WGS_PER_CU;   // resident workgroups per CU it deals to
 // start/stop (optional): events recorded around the launch
 hipError_t launch_attn(const AttnArgs& a, hipStream_t st, hipEvent_t start = nullptr, hipEvent_t stop = nullptr);
 // merge of the chunk partials of multi-chunk sequences (single-chunk ones are final already)

@@ -80,6 +80,7 @@ static spa_status make_pool(spa_ctx* ctx, const std::vector<uint32_t>& mask, spa
     delete p;
     return hip_fail(e, "hipExtStreamCreateWithCUMask");
   }
+  register_stream_cus(p->stream, nbits);
   *out = p;
   return SPA_OK;
 }
@@ -149,7 +150,10 @@ spa_status spa_pool_probe(spa_pool* p, int32_t n_blocks, uint32_t* ids_out, int3
 
 spa_status spa_pool_destroy(spa_pool* p) {
   if (!p) return SPA_OK;
-  if (p->stream) (void)hipStreamDestroy(p->stream);
+  if (p->stream) {
+    unregister_stream_cus(p->stream);
+    (void)hipStreamDestroy(p->stream);
+  }
   delete p;
   return SPA_OK;
 }
