@@ -84,3 +84,40 @@ def test_largest_microbatch_sampled():
     x1, t1 = _run(B, ctx, dw, {"cut": 0, "n_micro": 1, "cu_a": 0})
     hz.assert_close_rms(x1.double().cpu().numpy()[toks], x_ref, hz.tol_of(wl), "1024 tokens")
     assert _same_picks(t1.cpu().numpy()[:, toks], picks)
+
+
+def test_kv_length_beyond_capacity_is_refused():
+    """A cached length above the sequence's capacity (or zero) sets the
+    error bit and is skipped before any KV read; every other token's
+    attention output is unchanged, bit for bit. Each call clears the error
+    word first, so each reading belongs to one launch."""
+    from spatially_pipelined_attention_amd import binding as B, synth
+    from spatially_pipelined_attention_amd.workload import DeviceWorkload
+    base = synth.WORKLOADS["gptoss_36l_b64"]
+    wl = base.with_(name="edge_refuse", seed=2005, n_layers=2, layer_kinds=("sliding", "full"), batch=16,
+                    kv_len_lo=200, kv_len_hi=600)
+    print("\n[case] kv length beyond capacity, 16 tokens", flush=True)
+    dw = DeviceWorkload(wl)
+    ctx = B.spa_init(0)
+    n = wl.batch
+    g = torch.Generator(device="cpu").manual_seed(7)
+    q = (torch.randn(n, wl.n_q_heads * wl.head_dim, generator=g) * 0.5).to(torch.bfloat16).to("cuda")
+    ws = dw.workspace(n_micro=1)
+    outs, errs = [], []
+    for bad in (False, True):
+        saved = dw.kv_len_d.clone()
+        if bad:
+            dw.kv_len_d[3] = dw.kv_cap_d[3] + 1
+            dw.kv_len_d[9] = 0
+        for layer in (1, 0):   # full (packed cache), then sliding (ring)
+            o = torch.zeros_like(q)
+            B.spa_decode_attn(ctx, dw.m, dw.layers_c[layer], dw.batch, 0, n, q, o, ws)
+            torch.cuda.synchronize()
+            outs.append(o.clone())
+            errs.append(B.spa_workspace_errors(ctx, ws))
+        dw.kv_len_d.copy_(saved)
+    assert errs[0] == 0 and errs[1] == 0
+    assert errs[2] & 1 and errs[3] & 1
+    keep = [t for t in range(n) if t not in (3, 9)]
+    assert torch.equal(outs[0][keep], outs[2][keep])   # full layer
+    assert torch.equal(outs[1][keep], outs[3][keep])   # sliding layer
