@@ -54,6 +54,14 @@ def traffic_from_profile(name, tokens_per_launch):
     return float(keys["traffic_bytes_per_launch"]), path
 
 
+DEAL_MAX_TOKENS = 256   # launches of up to this many tokens deal their chunks (kDealMaxTok)
+
+
+def attn_kernel_name(tokens_per_launch):
+    """The full-layer attention kernel a launch of this many tokens runs."""
+    return "spa::k_attn_dealt<1>" if tokens_per_launch <= DEAL_MAX_TOKENS else "spa::k_attn<1, 1>"
+
+
 def load_resample(name):
     p = os.path.join(ROOT, "tests", "golden", f"resample_{name}.json")
     if not os.path.exists(p):
@@ -138,6 +146,9 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="gptoss_36l_b64")
+    ap.add_argument("--batch", type=int, default=None,
+                    help="resident sequences (the workload's own by default; other batches skip the CPU baseline "
+                         "and the stored router re-draws)")
     ap.add_argument("--schedule", choices=["auto", "spatial", "temporal"], default="auto")
     ap.add_argument("--cut", type=int, default=None)
     ap.add_argument("--micro", type=int, default=None)
@@ -161,6 +172,9 @@ def main():
 
     name = args.workload
     wl = synth.WORKLOADS[name]
+    if args.batch is not None and args.batch != wl.batch:
+        wl = wl.with_(batch=args.batch)
+        args.no_cpu_baseline = True
     cfg = dict(tuned_config(name))
     if args.cut is not None:
         cfg["cut"] = args.cut
@@ -174,7 +188,7 @@ def main():
     m = cfg["n_micro"]
 
     t_setup = time.perf_counter()
-    dw = DeviceWorkload(wl, load_resample(name))
+    dw = DeviceWorkload(wl, load_resample(name) if wl.batch == synth.WORKLOADS[name].batch else None)
     torch.cuda.synchronize()
     t_setup = time.perf_counter() - t_setup
     ctx = B.spa_init(0)
@@ -281,7 +295,7 @@ def main():
         "min_GB_per_iter": round(min_b / 1e9, 3),
         "tokens_per_s": round(wl.batch / (ms * 1e-3), 1), "per_user_tokens_per_s": round(1 / (ms * 1e-3), 2),
         "schedules_ms": {k: round(v["ms"], 4) for k, v in results.items()},
-        "roofline": {"bound": "hbm", "kernel": "spa::k_attn<1, 1> (full-layer decode attention, bf16 KV)",
+        "roofline": {"bound": "hbm", "kernel": f"{attn_kernel_name(wl.batch // m)} (full-layer decode attention, bf16 KV)",
                      "achieved": round(achieved, 1) if achieved else None, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4) if achieved else None,
                      "traffic": int(traffic) if traffic else None,
