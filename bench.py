@@ -14,6 +14,12 @@ the one run for the reported `value`, as an engine would select among its
 stored configurations; all three times are reported beside it. --quick runs
 only the stored selection. --schedule spatial / temporal force one.
 
+--virtual-comm LATENCY_US,GBPS adds one rank's communication endpoints to
+every layer (attention all-reduce, MoE dispatch, MoE combine; each a kernel
+lasting latency + payload / bandwidth, as in the single-GPU emulation of a
+32-GPU deployment in section 5.3.1 of the SubGPU Pipelining paper) and uses
+the configuration tuned with them ("<workload>+comm").
+
 Prints one JSON line (see the keys below). --gpus N > 1 exits: the pipeline
 partitions the CUs of one device.
 """
@@ -70,11 +76,12 @@ def load_resample(name):
     return {int(k): int(v) for k, v in d["resample"].items()}
 
 
-def tuned_config(name):
+def tuned_config(name, comm=False):
     if os.path.exists(TUNED):
         d = json.load(open(TUNED))
-        if name in d:
-            return d[name]
+        for key in ([name + "+comm"] if comm else []) + [name]:
+            if key in d:
+                return d[key]
     return {"cut": 0, "n_micro": 2, "cu_a": 128}
 
 
@@ -159,6 +166,8 @@ def main():
     ap.add_argument("--kernel-timer", choices=["clock", "events"], default="clock",
                     help="attention launch duration: the kernel's own span on the device wall clock, or HIP "
                          "events around each launch (these also hold the start marker's dispatch latency)")
+    ap.add_argument("--virtual-comm", default="", metavar="LATENCY_US,GBPS",
+                    help="add one rank's communication endpoints to every layer (e.g. 3,900)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="after timing, copy BYTES device bytes three times (a known-size kernel for counter scaling)")
     args = ap.parse_args()
@@ -168,14 +177,15 @@ def main():
 
     import torch
     from spatially_pipelined_attention_amd import binding as B, synth
-    from spatially_pipelined_attention_amd.workload import DeviceWorkload, Pipeline
+    from spatially_pipelined_attention_amd.workload import DeviceWorkload, Pipeline, parse_comm, set_comm
 
     name = args.workload
     wl = synth.WORKLOADS[name]
     if args.batch is not None and args.batch != wl.batch:
         wl = wl.with_(batch=args.batch)
         args.no_cpu_baseline = True
-    cfg = dict(tuned_config(name))
+    comm = parse_comm(args.virtual_comm)
+    cfg = dict(tuned_config(name, comm is not None))
     if args.cut is not None:
         cfg["cut"] = args.cut
     if args.micro is not None:
@@ -191,6 +201,8 @@ def main():
     dw = DeviceWorkload(wl, load_resample(name) if wl.batch == synth.WORKLOADS[name].batch else None)
     torch.cuda.synchronize()
     t_setup = time.perf_counter() - t_setup
+    if comm:
+        set_comm(dw.m, *comm)
     ctx = B.spa_init(0)
     n_cus = B.spa_device_cus(ctx)
     ws = dw.workspace(n_micro=m)
@@ -288,7 +300,10 @@ def main():
                                f"{wl.batch} sequences, KV U[{wl.kv_len_lo},{wl.kv_len_hi}], H {wl.hidden}, "
                                f"{wl.n_q_heads}q/{wl.n_kv_heads}kv x {wl.head_dim}, {wl.n_resident} resident "
                                f"experts of {wl.n_experts} (top-{wl.top_k}), I {wl.inter}",
-                   "schedule": sched},
+                   "schedule": sched,
+                   "virtual_comm": ({"latency_us": comm[0], "gbps": comm[1],
+                                     "endpoints": "attention all-reduce, MoE dispatch, MoE combine per layer"}
+                                    if comm else None)},
         "hbm_GBps": round(gbps, 1), "hbm_pct_peak": round(100 * gbps / HBM_PEAK_GBPS, 1),
         "algorithmic_GB_per_iter": round(total_b / 1e9, 3),
         "hbm_GBps_min_bytes": round(min_b / (ms * 1e-3) / 1e9, 1),   # the iteration's bytes with weights read once

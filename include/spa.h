@@ -111,6 +111,20 @@ typedef struct spa_model_desc {
   int32_t dense_dtype;
   int32_t expert_dtype;
   int32_t kv_dtype;
+  /* Virtual communication endpoints of one rank of a multi-GPU deployment
+   * (the single-GPU emulation of section 5.3.1 of the SubGPU Pipelining
+   * paper): with comm_gbps > 0, every layer also runs the attention
+   * all-reduce after the output projection, the MoE dispatch after the
+   * router and the MoE combine after the expert down projection, each as a
+   * spa_virtual_comm() launch on its stage's stream whose payload is the
+   * tensor that collective would carry (B x H dense_dtype values for the
+   * all-reduce, B*k x H expert-input values (+ E4M3 row scales) for
+   * dispatch, B*k x H dense_dtype values for combine; B = tokens of the
+   * call). Results do not change; only time does. comm_gbps = 0 (the
+   * zero-initialised default) leaves them out. 0 <= comm_latency_us <= 1000,
+   * 0 <= comm_gbps <= 100000. */
+  float comm_latency_us;
+  float comm_gbps;
 } spa_model_desc;
 
 /* One layer's parameters and KV cache (device pointers). */
@@ -244,6 +258,18 @@ spa_status spa_moe_combine(spa_ctx* ctx, const spa_model_desc* m, const float* h
                            const spa_route_bufs* r, int32_t n_tok, float* x_out, const float* gamma_next, void* xn_out,
                            void* stream);
 
+/* A virtual communication endpoint (section 5.3.1 of the paper: a collective
+ * of a multi-GPU rank replaced by a kernel that does the endpoint's local
+ * work and lasts the modelled time). Copies `bytes` bytes from src to dst
+ * (device memory, 16-byte aligned, not overlapping; the endpoint's read of
+ * the send buffer and write of the receive buffer) and keeps the launch
+ * running until latency_us + bytes / (gbps * 1e3) microseconds after each
+ * workgroup started, on the device wall clock. bytes <= 2^32; the modelled
+ * time must stay below 100 ms; SPA_EINVAL otherwise. bytes = 0 is a pure
+ * delay (src, dst may be NULL). */
+spa_status spa_virtual_comm(spa_ctx* ctx, const void* src, void* dst, size_t bytes, float latency_us, float gbps,
+                            void* stream);
+
 /* One whole layer, temporal, on tokens [tok0, tok0 + n_tok): updates x in
  * place, appends K/V, optionally records the router picks. */
 spa_status spa_layer_forward(spa_ctx* ctx, const spa_model_desc* m, const spa_layer* l, int32_t layer_index,
@@ -317,7 +343,8 @@ spa_status spa_pipeline_run(spa_pipeline* p, const spa_layer* layers, const spa_
                             void* caller_stream);
 /* Per-kernel timing of every launch of kernel class `cls` (0 = full-layer
  * attention, 1 = sliding attention, 2 = QKV, 3 = output projection, 4 =
- * router, 5 = expert gate/up, 6 = expert down, 7 = combine).
+ * router, 5 = expert gate/up, 6 = expert down, 7 = combine, 8 = virtual
+ * communication endpoints).
  * enable = 0: off.
  * enable = 1: for the attention classes the kernel itself records its span on
  *   the device wall clock (start of the first dispatched workgroup to the

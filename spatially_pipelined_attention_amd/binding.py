@@ -23,7 +23,7 @@ SPA_EMASK = -5
 SPA_F32, SPA_BF16, SPA_E4M3 = 0, 1, 2
 SPA_SLIDING, SPA_FULL = 0, 1
 
-KC_ATTN_FULL, KC_ATTN_SLIDING, KC_QKV, KC_OPROJ, KC_ROUTER, KC_GATEUP, KC_DOWN, KC_COMBINE = range(8)
+KC_ATTN_FULL, KC_ATTN_SLIDING, KC_QKV, KC_OPROJ, KC_ROUTER, KC_GATEUP, KC_DOWN, KC_COMBINE, KC_COMM = range(9)
 
 
 class SpaError(RuntimeError):
@@ -37,7 +37,7 @@ class spa_model_desc(C.Structure):
                 ("head_dim", C.c_int32), ("n_experts", C.c_int32), ("n_resident", C.c_int32),
                 ("top_k", C.c_int32), ("inter", C.c_int32), ("window", C.c_int32), ("n_layers", C.c_int32),
                 ("eps", C.c_float), ("dense_dtype", C.c_int32), ("expert_dtype", C.c_int32),
-                ("kv_dtype", C.c_int32)]
+                ("kv_dtype", C.c_int32), ("comm_latency_us", C.c_float), ("comm_gbps", C.c_float)]
 
 
 class spa_layer(C.Structure):
@@ -96,6 +96,7 @@ _PROTOS = {
     "spa_moe_expert": [_P, C.POINTER(spa_model_desc), C.POINTER(spa_layer), _P, _I, C.POINTER(spa_route_bufs),
                        _P, _P, C.c_size_t, _P],
     "spa_moe_combine": [_P, C.POINTER(spa_model_desc), _P, _P, C.POINTER(spa_route_bufs), _I, _P, _P, _P, _P],
+    "spa_virtual_comm": [_P, _P, _P, C.c_size_t, C.c_float, C.c_float, _P],
     "spa_layer_forward": [_P, C.POINTER(spa_model_desc), C.POINTER(spa_layer), _I, C.POINTER(spa_batch), _I, _I, _P,
                           C.c_size_t, _P],
     "spa_temporal_run": [_P, C.POINTER(spa_model_desc), C.POINTER(spa_layer), C.POINTER(spa_batch), _I, _P,
@@ -256,6 +257,10 @@ def spa_moe_expert(ctx, m, layer, hn, n_tok, route: spa_route_bufs, y_out, ws, s
 def spa_moe_combine(ctx, m, h, y, route: spa_route_bufs, n_tok, x_out, gamma_next=None, xn_out=None, stream=None):
     _check(lib().spa_moe_combine(ctx, C.byref(m), ptr(h), ptr(y), C.byref(route), n_tok, ptr(x_out), ptr(gamma_next),
                                  ptr(xn_out), stream_handle(stream)))
+
+
+def spa_virtual_comm(ctx, src, dst, nbytes: int, latency_us: float, gbps: float, stream=None):
+    _check(lib().spa_virtual_comm(ctx, ptr(src), ptr(dst), nbytes, latency_us, gbps, stream_handle(stream)))
 
 
 def spa_layer_forward(ctx, m, layer, layer_index, batch, tok0, n_tok, ws, stream=None):

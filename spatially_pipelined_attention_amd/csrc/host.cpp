@@ -57,6 +57,34 @@ spa_status validate_model(const spa_model_desc* m) {
     return fail(SPA_EUNSUPPORTED, "hidden and inter must be multiples of the expert k-step");
   if (m->hidden % 16) return fail(SPA_EUNSUPPORTED, "hidden must be a multiple of 16 (router)");
   if (m->hidden > 4096) return fail(SPA_EUNSUPPORTED, "hidden above 4096 (row kernels hold 4 columns per thread)");
+  if (!(m->comm_latency_us >= 0.f && m->comm_latency_us <= 1000.f))
+    return fail(SPA_EINVAL, "comm_latency_us must be in [0, 1000]");
+  if (!(m->comm_gbps >= 0.f && m->comm_gbps <= 100000.f)) return fail(SPA_EINVAL, "comm_gbps must be in [0, 100000]");
+  return SPA_OK;
+}
+
+bool comm_enabled(const spa_model_desc* m) { return m->comm_gbps > 0.f; }
+
+// Payload bytes of the three collectives of one layer for n_tok tokens: the
+// attention all-reduce carries the output projection's rows, dispatch the
+// expert input rows (and their E4M3 scales), combine the expert output rows.
+static size_t comm_bytes_allreduce(const spa_model_desc* m, int n_tok) {
+  return (size_t)n_tok * m->hidden * esz_of(m->dense_dtype);
+}
+static size_t comm_bytes_dispatch(const spa_model_desc* m, int n_tok) {
+  const size_t R = (size_t)n_tok * m->top_k;
+  return R * m->hidden * esz_of(m->expert_dtype) + (m->expert_dtype == SPA_E4M3 ? R * 4 : 0);
+}
+static size_t comm_bytes_combine(const spa_model_desc* m, int n_tok) {
+  return (size_t)n_tok * m->top_k * m->hidden * esz_of(m->dense_dtype);
+}
+
+spa_status launch_comm(spa_ctx* ctx, const void* src, void* dst, size_t copy_bytes, size_t bytes, double latency_us,
+                       double gbps, hipStream_t st) {
+  const double us = latency_us + (gbps > 0.0 ? (double)bytes / (gbps * 1e3) : 0.0);
+  if (!(us >= 0.0 && us < 1e5)) return fail(SPA_EINVAL, "modelled communication time must be below 100 ms");
+  const unsigned long long ticks = (unsigned long long)std::llround(us * ctx->wall_khz / 1000.0);
+  SPA_HIP(launch_virtual_comm(src, dst, (long long)(copy_bytes / 16), ticks, st));
   return SPA_OK;
 }
 
@@ -176,6 +204,10 @@ WsLayout ws_layout(const spa_model_desc* m, int n_tok, int max_kv_len, int n_mic
   s.y = o; o = align256(o + (size_t)R * H * 4);
   s.attn_part = o; o = align256(o + (size_t)n_tok * Hkv * L.max_chunks * G * (D + 2) * 4);
   s.gemm_part = o; o = align256(o + gemm_part_floats(m, n_tok) * 4);
+  s.comm = o;
+  if (comm_enabled(m))
+    o = align256(o + std::max({comm_bytes_allreduce(m, n_tok), comm_bytes_dispatch(m, n_tok),
+                               comm_bytes_combine(m, n_tok)}));
   s.bytes = o;
   L.err = 0;
   L.slot0 = 256;
@@ -213,6 +245,7 @@ Slot slot_ptrs(const WsLayout& L, void* ws, int slot) {
   s.y = (float*)(b + o.y);
   s.attn_part = (float*)(b + o.attn_part);
   s.gemm_part = (float*)(b + o.gemm_part);
+  s.comm = b + o.comm;
   return s;
 }
 
@@ -607,6 +640,16 @@ static spa_status op_combine(const spa_model_desc* m, const float* h, const floa
   return SPA_OK;
 }
 
+// The virtual endpoint of one collective of the layer (nothing when the
+// model has no communication): copies the payload's 16-byte words from src
+// (a slot buffer at least that long) and lasts the payload's modelled time.
+static spa_status op_comm(spa_ctx* ctx, const spa_model_desc* m, const void* src, size_t copy_bytes, size_t bytes,
+                          const Slot& s, hipStream_t st, TimingHook* th) {
+  if (!comm_enabled(m)) return SPA_OK;
+  HookScope hs(th, KC_COMM, st);
+  return launch_comm(ctx, src, s.comm, copy_bytes & ~(size_t)15, bytes, m->comm_latency_us, m->comm_gbps, st);
+}
+
 // ---------------------------------------------------------------------------
 // segments of one layer on one microbatch slot
 // ---------------------------------------------------------------------------
@@ -626,6 +669,8 @@ spa_status run_segment_a(spa_ctx* ctx, const spa_model_desc* m, const spa_layer*
   if ((rc = op_oproj(ctx, m, l, x, s.o, n_tok, s.h, s.hn_f32, ebf ? s.hn_bf16 : nullptr, fp8 ? s.hn8 : nullptr,
                      fp8 ? s.hn8_scale : nullptr, s, st, th, true)))
     return rc;
+  const size_t ar = comm_bytes_allreduce(m, n_tok);
+  if ((rc = op_comm(ctx, m, s.h, ar, ar, s, st, th))) return rc;   // attention all-reduce
   if (with_router) {
     int32_t* rec = b->topk_out ? b->topk_out + ((size_t)layer_index * b->batch + tok0) * m->top_k : nullptr;
     if ((rc = op_route(ctx, m, l, s.hn_f32, n_tok, s.logits, s.route, rec, s, st, th, true))) return rc;
@@ -662,6 +707,8 @@ spa_status run_layer_after_attn(spa_ctx* ctx, const spa_model_desc* m, const spa
   if ((rc = op_oproj(ctx, m, l, x, s.o, n_tok, s.h, s.hn_f32, ebf ? s.hn_bf16 : nullptr, fp8 ? s.hn8 : nullptr,
                      fp8 ? s.hn8_scale : nullptr, s, st, th, true)))
     return rc;
+  const size_t ar = comm_bytes_allreduce(m, n_tok);
+  if ((rc = op_comm(ctx, m, s.h, ar, ar, s, st, th))) return rc;   // attention all-reduce
   return run_segment_b(ctx, m, l, layer_index, next, b, tok0, n_tok, W, s, false, st, th);
 }
 
@@ -676,9 +723,13 @@ spa_status run_segment_b(spa_ctx* ctx, const spa_model_desc* m, const spa_layer*
     if ((rc = op_route(ctx, m, l, s.hn_f32, n_tok, s.logits, s.route, rec, s, st, th, true))) return rc;
   }
   // the router's permutation kernel already gathered the expert rows
+  if ((rc = op_comm(ctx, m, s.xe_perm, (size_t)n_tok * m->top_k * m->hidden * esz_of(m->expert_dtype),
+                     comm_bytes_dispatch(m, n_tok), s, st, th))) return rc;   // MoE dispatch
   GemmPlan dp{};
   if ((rc = op_expert(ctx, m, l, expert_input(m, s), s.hn8_scale, n_tok, s.route, s.y, s, st, th, &dp, true)))
     return rc;
+  const size_t cb = comm_bytes_combine(m, n_tok);
+  if ((rc = op_comm(ctx, m, s.y, cb, cb, s, st, th))) return rc;   // MoE combine
   const bool plain = dp.epi == EPI_STORE;
   return op_combine(m, s.h, plain ? s.y : nullptr, plain ? nullptr : &dp, &s, s.route, n_tok, x,
                     next ? next->gamma1 : nullptr, s.xn, st, th, true);
@@ -759,6 +810,9 @@ spa_status spa_init(int hip_device, spa_ctx** out) {
     return fail(SPA_EUNSUPPORTED, "this library is built for gfx950, device is " + arch);
   }
   c->n_xcd = 8;
+  int khz = 0;
+  if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, hip_device) == hipSuccess && khz > 0)
+    c->wall_khz = khz;
   *out = c;
   return SPA_OK;
 }
@@ -974,6 +1028,19 @@ spa_status spa_moe_combine(spa_ctx* ctx, const spa_model_desc* m, const float* h
   if (!h || !y || !r || !x_out || n_tok < 1) return fail(SPA_EINVAL, "bad argument");
   if (gamma_next && !xn_out) return fail(SPA_EINVAL, "xn_out needed with gamma_next");
   return op_combine(m, h, y, nullptr, nullptr, *r, n_tok, x_out, gamma_next, xn_out, (hipStream_t)stream, nullptr);
+}
+
+spa_status spa_virtual_comm(spa_ctx* ctx, const void* src, void* dst, size_t bytes, float latency_us, float gbps,
+                            void* stream) {
+  if (!ctx) return fail(SPA_EINVAL, "ctx is NULL");
+  if (bytes % 16 || bytes > ((size_t)1 << 32)) return fail(SPA_EINVAL, "bytes must be a multiple of 16, at most 2^32");
+  if (bytes && (!src || !dst || misaligned(src) || misaligned(dst)))
+    return fail(SPA_EINVAL, "src and dst must be 16-byte aligned device pointers");
+  if (bytes && (const char*)src < (const char*)dst + bytes && (const char*)dst < (const char*)src + bytes)
+    return fail(SPA_EINVAL, "src and dst overlap");
+  if (!(latency_us >= 0.f) || !(gbps >= 0.f) || (bytes && gbps == 0.f))
+    return fail(SPA_EINVAL, "latency_us must be >= 0 and gbps > 0");
+  return launch_comm(ctx, src, dst, bytes, bytes, latency_us, gbps, (hipStream_t)stream);
 }
 
 spa_status spa_layer_forward(spa_ctx* ctx, const spa_model_desc* m, const spa_layer* l, int32_t layer_index,

@@ -13,6 +13,7 @@ struct spa_ctx {
   int device = 0;
   int n_cus = 0;
   int n_xcd = 8;
+  int wall_khz = 100000;   // device wall clock (wall_clock64) rate
   hipDeviceProp_t prop{};
 };
 
@@ -31,7 +32,7 @@ spa_status hip_fail(hipError_t e, const char* what);
 // Kernel classes (timing hooks and split heuristics).
 enum KClass : int {
   KC_ATTN_FULL = 0, KC_ATTN_SLIDING = 1, KC_QKV = 2, KC_OPROJ = 3,
-  KC_ROUTER = 4, KC_GATEUP = 5, KC_DOWN = 6, KC_COMBINE = 7, KC_COUNT = 8
+  KC_ROUTER = 4, KC_GATEUP = 5, KC_DOWN = 6, KC_COMBINE = 7, KC_COMM = 8, KC_COUNT = 9
 };
 
 #ifndef SPA_ATTN_CHUNK
@@ -44,6 +45,7 @@ struct SlotLayout {
   size_t xn, q, o, h, hn_f32, hn_bf16, hn8, hn8_scale, logits;
   size_t topk_idx, topk_w, offsets, row_tok, row_slot, inv;
   size_t xe_perm, xe_perm_scale, z, z8, z8_scale, y, attn_part, gemm_part;
+  size_t comm;          // receive buffer of the virtual communication endpoints
   size_t bytes;
 };
 
@@ -64,6 +66,11 @@ struct GemmPlan {
 };
 
 spa_status validate_model(const spa_model_desc* m);
+bool comm_enabled(const spa_model_desc* m);
+// Launch one virtual communication endpoint: copy copy_bytes (a multiple of
+// 16) src -> dst; the launch lasts latency_us + bytes / gbps.
+spa_status launch_comm(spa_ctx* ctx, const void* src, void* dst, size_t copy_bytes, size_t bytes, double latency_us,
+                       double gbps, hipStream_t st);
 WsLayout ws_layout(const spa_model_desc* m, int n_tok, int max_kv_len, int n_micro);
 int max_chunks_for(int max_kv_len, const spa_model_desc* m);
 GemmPlan plan_gemm(int kclass, const spa_model_desc* m, int n_tok, int n_cus);
@@ -96,6 +103,7 @@ struct Slot {
   float* y;
   float* attn_part;
   float* gemm_part;
+  void* comm;
 };
 
 Slot slot_ptrs(const WsLayout& L, void* ws, int slot);

@@ -204,6 +204,11 @@ hipError_t launch_cvt_rows(const CvtArgs& a, hipStream_t st);
 
 hipError_t launch_fill_i32(int* p, long long n, int v, hipStream_t st);
 
+// Virtual communication endpoint: copy n16 16-byte words src -> dst, then
+// keep every workgroup resident until `ticks` device wall-clock ticks after
+// it started (a collective's modelled duration).
+hipError_t launch_virtual_comm(const void* src, void* dst, long long n16, unsigned long long ticks, hipStream_t st);
+
 // Row-major [n_mats][N][K] (element size esz, K * esz a multiple of 64) ->
 // panels [n_mats][ceil(N/16)][K*esz/64][16 rows][64 bytes]; rows past N are zero.
 hipError_t launch_pack_panels(const void* src, void* dst, int n_mats, int N, int K, int esz, hipStream_t st);

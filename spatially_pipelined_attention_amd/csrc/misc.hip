@@ -512,6 +512,30 @@ hipError_t launch_fill_i32(int* p, long long n, int v, hipStream_t st) {
   return hipGetLastError();
 }
 
+// Virtual communication endpoint. The copy stands for the endpoint's local
+// traffic (send buffer read, receive buffer written); the wait makes the
+// launch last the collective's modelled time. Wave 0 of each workgroup polls
+// the wall clock with short sleeps; the iteration cap (each iteration sleeps
+// for more than one clock tick) ends the wait even if the clock stalled.
+__global__ __launch_bounds__(256) void k_virtual_comm(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
+                                                      long long n16, unsigned long long ticks) {
+  const unsigned long long t0 = wall_clock64();
+  for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += (long long)gridDim.x * blockDim.x)
+    dst[i] = src[i];
+  if (threadIdx.x < 64) {
+    const unsigned long long cap = ticks + 1024;
+    for (unsigned long long it = 0; it < cap && wall_clock64() - t0 < ticks; ++it) __builtin_amdgcn_s_sleep(2);
+  }
+  __syncthreads();
+}
+
+hipError_t launch_virtual_comm(const void* src, void* dst, long long n16, unsigned long long ticks, hipStream_t st) {
+  long long g = (n16 + 2047) / 2048;   // 32 KB per workgroup
+  g = g < 1 ? 1 : (g > 128 ? 128 : g);
+  hipLaunchKernelGGL(k_virtual_comm, dim3((int)g), dim3(256), 0, st, (const u32x4*)src, (u32x4*)dst, n16, ticks);
+  return hipGetLastError();
+}
+
 // KV cache rows <-> [n][Hkv][D] (one (sequence, position) per row, all KV heads).
 __global__ void k_kv_io(KvIoArgs a) {
   const long long total = (long long)a.n * a.n_kv_heads * a.head_dim;

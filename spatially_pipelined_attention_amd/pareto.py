@@ -43,22 +43,28 @@ def main(argv=None):
     ap.add_argument("--reps", type=int, default=3)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--out", required=True)
+    ap.add_argument("--virtual-comm", default="", metavar="LATENCY_US,GBPS",
+                    help="add the rank's communication endpoints to every layer")
     a = ap.parse_args(argv)
 
     import torch
     from . import binding as B, synth
-    from .workload import DeviceWorkload
+    from .workload import DeviceWorkload, parse_comm, set_comm
 
     base = synth.WORKLOADS[a.workload]
     ctx = B.spa_init(0)
     cuts = [int(x) for x in a.cuts.split(",")][:3]
-    result = {"workload": a.workload, "n_cus": B.spa_device_cus(ctx), "batches": {}}
+    comm = parse_comm(a.virtual_comm)
+    result = {"workload": a.workload, "n_cus": B.spa_device_cus(ctx), "batches": {},
+              "virtual_comm": {"latency_us": comm[0], "gbps": comm[1]} if comm else None}
     points = []
     for bsz in [int(x) for x in a.batches.split(",")]:
         wl = base.with_(batch=bsz)
         micros = [int(x) for x in a.micros.split(",") if bsz % int(x) == 0 and bsz // int(x) * wl.top_k <= 4096][:4]
         t0 = time.time()
         dw = DeviceWorkload(wl)
+        if comm:
+            set_comm(dw.m, *comm)
         torch.cuda.synchronize()
         setup = time.time() - t0
         ws = max((dw.workspace(n_micro=mm) for mm in micros), key=lambda t: t.numel())

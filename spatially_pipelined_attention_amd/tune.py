@@ -5,6 +5,10 @@ and writes the best spatial point, the temporal times and the selection (the
 faster of the two kinds) to a JSON file, merged with what is there:
 
     python -m spatially_pipelined_attention_amd.tune --workload gptoss_36l_b64 --out tuned.json
+
+With --virtual-comm LATENCY_US,GBPS every layer also runs the rank's
+communication endpoints (spa_model_desc.comm_*), and the entry is stored
+under "<workload>+comm".
 """
 from __future__ import annotations
 
@@ -26,16 +30,21 @@ def main(argv=None):
     ap.add_argument("--reps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--per-kind", type=int, default=1, help="separate CU splits for full and sliding layers")
+    ap.add_argument("--virtual-comm", default="", metavar="LATENCY_US,GBPS")
     a = ap.parse_args(argv)
 
     import torch
     from . import binding as B, synth
-    from .workload import DeviceWorkload
+    from .workload import DeviceWorkload, parse_comm, set_comm
 
     wl = synth.WORKLOADS[a.workload]
     micros = [int(x) for x in a.micros.split(",") if wl.batch % int(x) == 0][:4]
     cuts = [int(x) for x in a.cuts.split(",")][:3]
     dw = DeviceWorkload(wl)
+    comm = parse_comm(a.virtual_comm)
+    if comm:
+        set_comm(dw.m, *comm)
+    key = a.workload + ("+comm" if comm else "")
     ctx = B.spa_init(0)
     ws = max((dw.workspace(n_micro=mm) for mm in micros), key=lambda t: t.numel())
     sp = B.spa_tune_space(len(cuts), (B.C.c_int32 * 3)(*(cuts + [0] * (3 - len(cuts)))),
@@ -55,11 +64,13 @@ def main(argv=None):
              "temporal_ms": {str(k): round(v, 4) for k, v in sorted(temporal.items())},
              "selected": selected,
              "points": len(pts), "tune_seconds": round(dt, 1), "n_cus": B.spa_device_cus(ctx)}
+    if comm:
+        entry["virtual_comm"] = {"latency_us": comm[0], "gbps": comm[1]}
     for p in pts:
         print(f"cut={p.cut:2d} m={p.n_micro} cu_a={p.cu_a:3d}/{p.cu_a_sliding:3d}: {p.ms:.3f} ms", flush=True)
-    print(json.dumps({a.workload: entry}), flush=True)
+    print(json.dumps({key: entry}), flush=True)
     d = json.load(open(a.out)) if os.path.exists(a.out) else {}
-    d[a.workload] = entry
+    d[key] = entry
     with open(a.out, "w") as f:
         json.dump(d, f, indent=1, sort_keys=True)
     return 0

@@ -27,6 +27,24 @@ def model_desc(wl: synth.Workload) -> B.spa_model_desc:
                             _DT[wl.expert_dtype], _DT[wl.kv_dtype])
 
 
+def set_comm(m: B.spa_model_desc, latency_us: float, gbps: float) -> B.spa_model_desc:
+    """Give the model the virtual communication endpoints of one rank (the
+    all-reduce after the output projection, MoE dispatch and combine), each
+    lasting latency_us + payload bytes / gbps; gbps = 0 removes them. Set it
+    before sizing a workspace or creating a pipeline: both copy the model."""
+    m.comm_latency_us = float(latency_us)
+    m.comm_gbps = float(gbps)
+    return m
+
+
+def parse_comm(spec: str):
+    """'LATENCY_US,GBPS' -> (latency_us, gbps); '' or None -> None."""
+    if not spec:
+        return None
+    lat, gbps = (float(v) for v in spec.split(","))
+    return lat, gbps
+
+
 def round_up(v, a):
     return (v + a - 1) // a * a
 

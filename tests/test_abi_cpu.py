@@ -83,6 +83,36 @@ def test_model_validation_errors(field, value, status):
     assert ei.value.status == status
 
 
+@pytest.mark.parametrize("latency,gbps", [(-1.0, 900.0), (2000.0, 900.0), (float("nan"), 900.0), (3.0, -1.0),
+                                           (3.0, 2e5), (3.0, float("nan"))])
+def test_comm_model_validation(latency, gbps):
+    m = model_desc(synth.WORKLOADS["gptoss_36l_b64"])
+    m.comm_latency_us, m.comm_gbps = latency, gbps
+    with pytest.raises(B.SpaError) as ei:
+        B.spa_workspace_query(m, 64, 8192, 1)
+    assert ei.value.status == B.SPA_EINVAL
+
+
+@pytest.mark.parametrize("name,n_micro", [("gptoss_36l_b64", 1), ("gptoss_36l_b64", 4), ("gptoss_36l_fp8", 2),
+                                          ("tiny_fp32", 1)])
+def test_comm_receive_buffer_is_the_largest_payload(name, n_micro):
+    """With endpoints, every microbatch slot holds one receive buffer as large
+    as the largest of the layer's three payloads: b*H dense values (all-reduce),
+    b*k*H expert-input values plus E4M3 row scales (dispatch), b*k*H dense
+    values (combine), b = tokens per microbatch; rounded up to 256 bytes."""
+    wl = synth.WORKLOADS[name]
+    m = model_desc(wl)
+    base = B.spa_workspace_query(m, wl.batch, wl.kv_len_hi, n_micro)
+    m.comm_latency_us, m.comm_gbps = 3.0, 900.0
+    with_comm = B.spa_workspace_query(m, wl.batch, wl.kv_len_hi, n_micro)
+    esz = {"f32": 4, "bf16": 2, "e4m3": 1}
+    b = wl.batch // n_micro
+    dn, ex = esz[wl.w_dtype], esz[wl.expert_dtype]
+    payload = max(b * wl.hidden * dn, b * wl.top_k * wl.hidden * ex + (b * wl.top_k * 4 if ex == 1 else 0),
+                  b * wl.top_k * wl.hidden * dn)
+    assert with_comm - base == n_micro * ((payload + 255) // 256 * 256)
+
+
 def test_microbatch_must_divide_batch():
     m = model_desc(synth.WORKLOADS["gptoss_36l_b64"])
     with pytest.raises(B.SpaError) as ei:

@@ -1,0 +1,140 @@
+"""Virtual communication endpoints on the GPU (the single-GPU emulation of a
+multi-GPU rank in section 5.3.1 of the SubGPU Pipelining paper: each
+collective becomes a kernel lasting latency + payload / bandwidth).
+
+* spa_virtual_comm copies its payload exactly and lasts at least the
+  modelled time, and not much longer;
+* with endpoints in every layer the iteration computes the same bits as
+  without them, temporally and in the spatial pipeline (they change only
+  time), and the spatial schedule still equals the temporal one with the same
+  microbatches;
+* every layer runs three endpoints per microbatch, and the temporal iteration
+  grows by about their modelled time.
+Runs on a two-layer (sliding, full) slice of the 36-layer one-GPU workload.
+"""
+import statistics
+
+import pytest
+import torch
+
+from tests import harness as hz
+
+pytestmark = pytest.mark.gpu
+
+LAT_US, GBPS = 3.0, 900.0
+
+
+@pytest.fixture(scope="module")
+def env():
+    from spatially_pipelined_attention_amd import binding as B, synth
+    from spatially_pipelined_attention_amd.workload import DeviceWorkload
+    wl0 = synth.WORKLOADS["gptoss_36l_b64"]
+    wl = wl0.with_(n_layers=2, layer_kinds=wl0.layer_kinds[:2])
+    print("\n[setup] 2-layer slice of gptoss_36l_b64 for the communication endpoints", flush=True)
+    dw = DeviceWorkload(wl, hz.load_resample("gptoss_36l_b64"))
+    ctx = B.spa_init(0)
+    return dict(B=B, wl=wl, dw=dw, ctx=ctx)
+
+
+def _elapsed_us(fn, reps=5):
+    out = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn()
+        e1.record()
+        torch.cuda.synchronize()
+        out.append(e0.elapsed_time(e1) * 1e3)
+    return statistics.median(out)
+
+
+def test_endpoint_copies_payload_and_lasts_modelled_time(env):
+    B, ctx = env["B"], env["ctx"]
+    nbytes = 4 << 20
+    g = torch.Generator(device="cpu").manual_seed(11)
+    src = torch.randint(0, 256, (nbytes,), dtype=torch.uint8, generator=g).to("cuda")
+    dst = torch.zeros_like(src)
+    st = torch.cuda.current_stream()
+    print("[case] 4 MiB endpoint, 200 us + bytes / 900 GB/s", flush=True)
+    B.spa_virtual_comm(ctx, src, dst, nbytes, 200.0, GBPS, st)
+    torch.cuda.synchronize()
+    assert torch.equal(src, dst)
+    model = 200.0 + nbytes / (GBPS * 1e3)
+    t = _elapsed_us(lambda: B.spa_virtual_comm(ctx, src, dst, nbytes, 200.0, GBPS, st))
+    assert model <= t <= model + 40.0, (t, model)
+    # a pure delay
+    t0 = _elapsed_us(lambda: B.spa_virtual_comm(ctx, None, None, 0, 50.0, 0.0, st))
+    assert 50.0 <= t0 <= 90.0, t0
+
+
+def test_endpoint_rejects_bad_arguments(env):
+    B, ctx = env["B"], env["ctx"]
+    buf = torch.zeros(4096, dtype=torch.uint8, device="cuda")
+    for args in [(buf, buf[2048:], 100, 3.0, GBPS),        # not a multiple of 16
+                 (buf, buf[16:], 2048, 3.0, GBPS),         # overlapping
+                 (buf, buf[2048:], 2048, -1.0, GBPS),      # negative latency
+                 (buf, buf[2048:], 2048, 3.0, 0.0),        # payload without bandwidth
+                 (buf, buf[2048:], 2048, 2e5, GBPS)]:      # above 100 ms
+        with pytest.raises(B.SpaError) as ei:
+            B.spa_virtual_comm(ctx, args[0], args[1], args[2], args[3], args[4])
+        assert ei.value.status == B.SPA_EINVAL
+
+
+def _iterate(env, comm, cut, n_micro, cu_a, timed=False, reps=0):
+    from spatially_pipelined_attention_amd.workload import Pipeline, set_comm
+    B, dw, ctx = env["B"], env["dw"], env["ctx"]
+    set_comm(dw.m, LAT_US if comm else 0.0, GBPS if comm else 0.0)
+    pipe = Pipeline(ctx, dw.m, {"cut": cut, "n_micro": n_micro, "cu_a": cu_a})
+    ws = dw.workspace(n_micro=n_micro)
+    try:
+        if timed:
+            B.spa_pipeline_time_kernel(pipe.h, B.KC_COMM, 2)
+        dw.reset_x()
+        dw.topk.zero_()
+        pipe.run(dw.layers_c, dw.batch, ws)
+        torch.cuda.synchronize()
+        assert B.spa_workspace_errors(ctx, ws) == 0
+        x, topk = dw.x.clone(), dw.topk.clone()
+        timing = B.spa_pipeline_timing(pipe.h) if timed else None
+        t_us = None
+        if reps:
+            t_us = _elapsed_us(lambda: pipe.run(dw.layers_c, dw.batch, ws), reps)
+    finally:
+        pipe.close()
+        set_comm(dw.m, 0.0, 0.0)
+    return x, topk, timing, t_us
+
+
+def test_endpoints_change_time_not_bits(env):
+    print("[case] T1 / T2 / spatial cut 0 and 1 with and without endpoints", flush=True)
+    x1, k1, _, _ = _iterate(env, False, 0, 1, 0)
+    x1c, k1c, _, _ = _iterate(env, True, 0, 1, 0)
+    assert torch.equal(x1, x1c) and torch.equal(k1, k1c)
+    x2, k2, _, _ = _iterate(env, False, 0, 2, 0)
+    for cut in (0, 1):
+        xs, ks, _, _ = _iterate(env, True, cut, 2, 128)
+        assert torch.equal(xs, x2) and torch.equal(ks, k2), cut
+
+
+def test_three_endpoints_per_layer_and_microbatch(env):
+    dw = env["dw"]
+    wl = env["wl"]
+    print("[case] endpoint count and time in T2", flush=True)
+    _, _, (mean_ms, count), _ = _iterate(env, True, 0, 2, 0, timed=True)
+    assert count == 3 * wl.n_layers * 2
+    b = wl.batch // 2
+    payloads = [b * wl.hidden * 2, b * wl.top_k * wl.hidden * 2, b * wl.top_k * wl.hidden * 2]
+    model_us = statistics.mean(LAT_US + p / (GBPS * 1e3) for p in payloads)
+    # events bracket each launch: the mean holds the launch and marker latency too
+    assert model_us <= mean_ms * 1e3 <= model_us + 25.0, (mean_ms * 1e3, model_us)
+    del dw
+
+
+def test_temporal_iteration_grows_by_the_modelled_time(env):
+    wl = env["wl"]
+    print("[case] T1 iteration time with and without endpoints", flush=True)
+    _, _, _, t0 = _iterate(env, False, 0, 1, 0, reps=7)
+    _, _, _, t1 = _iterate(env, True, 0, 1, 0, reps=7)
+    payloads = [wl.batch * wl.hidden * 2, wl.batch * wl.top_k * wl.hidden * 2, wl.batch * wl.top_k * wl.hidden * 2]
+    model = wl.n_layers * sum(LAT_US + p / (GBPS * 1e3) for p in payloads)
+    assert 0.9 * model <= t1 - t0 <= model + 3 * wl.n_layers * 10.0, (t1 - t0, model)
