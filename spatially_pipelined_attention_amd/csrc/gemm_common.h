@@ -1,4 +1,5 @@
-// Helpers shared by the two skinny-GEMM kernels (gemm.hip, gemm_x.hip).
+// Helpers of the skinny-GEMM kernel (gemm.hip): MFMA steps per weight type,
+// the weight row of a tile column, and the workgroup -> tile mapping.
 #pragma once
 #include "common.h"
 #include "kernels.h"

@@ -182,15 +182,14 @@ hipError_t launch_oproj_finish(const OprojFinishArgs& a, hipStream_t st) {
 }
 
 // ---------------------------------------------------------------------------
-// Router top-k: one wave per token. Lanes hold the logits of experts
+// Router top-k of token t by one wave. Lanes hold the logits of experts
 // lane + 64 j (summed over the splits in split order); k rounds of a wave
 // argmax on (value, index) - larger value wins, equal values go to the lower
-// index - then the softmax over the k picked logits.
+// index - leave the picks in pick order in pv/pi on every lane. With
+// store_logits the summed logits are written to a.logits.
 template <int SM>
-__global__ __launch_bounds__(256) void k_route_topk(RouteArgs a) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + wave;
-  if (t >= a.n_tok) return;
+__device__ __forceinline__ void route_token(const RouteArgs& a, int t, int lane, bool store_logits, float (&pv)[8],
+                                            int (&pi)[8]) {
   const int E = a.E, k = a.k;
   float v[4];
 #pragma unroll
@@ -199,11 +198,9 @@ __global__ __launch_bounds__(256) void k_route_topk(RouteArgs a) {
     v[j] = -INFINITY;
     if (e < E) {
       v[j] = part_sum<SM>(a.pv, t, e);
-      a.logits[(long long)t * E + e] = v[j];
+      if (store_logits) a.logits[(long long)t * E + e] = v[j];
     }
   }
-  float pv[8];
-  int pi[8];
   for (int p = 0; p < k; ++p) {
     float bv = v[0];
     int bi = lane;
@@ -230,24 +227,43 @@ __global__ __launch_bounds__(256) void k_route_topk(RouteArgs a) {
         if (j == (bi >> 6)) v[j] = -INFINITY;
     }
   }
-  if (lane == 0) {
-    float den = 0.f;
-    for (int p = 0; p < k; ++p) den += __expf(pv[p] - pv[0]);
-    for (int p = 0; p < k; ++p) {
-      a.topk_idx[t * k + p] = pi[p];
-      a.topk_w[t * k + p] = __expf(pv[p] - pv[0]) / den;
-      if (a.topk_rec) a.topk_rec[t * k + p] = pi[p];
-    }
+}
+
+// The picks of token t and their softmax weights (lane 0 writes).
+__device__ __forceinline__ void store_picks(const RouteArgs& a, int t, int lane, const float (&pv)[8],
+                                            const int (&pi)[8]) {
+  if (lane != 0) return;
+  const int k = a.k;
+  float den = 0.f;
+  for (int p = 0; p < k; ++p) den += __expf(pv[p] - pv[0]);
+  for (int p = 0; p < k; ++p) {
+    a.topk_idx[t * k + p] = pi[p];
+    a.topk_w[t * k + p] = __expf(pv[p] - pv[0]) / den;
+    if (a.topk_rec) a.topk_rec[t * k + p] = pi[p];
   }
 }
 
+// Router top-k and softmax over the picks: one wave per token.
+template <int SM>
+__global__ __launch_bounds__(256) void k_route_topk(RouteArgs a) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + wave;
+  if (t >= a.n_tok) return;
+  float pv[8];
+  int pi[8];
+  route_token<SM>(a, t, lane, true, pv, pi);
+  store_picks(a, t, lane, pv, pi);
+}
+
 // Dispatch permutation of the picks (pick p = token * k + slot runs on
-// resident expert topk_idx[p] % E_res): counts, exclusive offsets, rows grouped
-// by expert with (token, slot) ascending inside, and the inverse map. Ranks
+// resident expert grp[p] = topk_idx[p] % E_res, grp in LDS on entry): counts,
+// exclusive offsets, rows grouped by expert with (token, slot) ascending
+// inside, and the inverse map; then the gather of the expert input rows. Ranks
 // come from per-expert bitmasks over the picks, so no order depends on timing.
-__global__ __launch_bounds__(256) void k_route_permute(RouteArgs a) {
-  extern __shared__ __attribute__((aligned(16))) char lds[];
-  const int tid = threadIdx.x;
+// Every workgroup computes the whole (small) permutation; workgroup 0 stores
+// it, and the gather is dealt over the workgroups.
+__device__ __forceinline__ void permute_body(const RouteArgs& a, char* lds) {
+  const int tid = threadIdx.x, nthr = blockDim.x;
   const int k = a.k, P = a.n_tok * k, E_res = a.E_res;
   int* grp = (int*)lds;                         // [P]
   int* rtok = grp + P;                          // [P] token of each dispatch row
@@ -255,13 +271,11 @@ __global__ __launch_bounds__(256) void k_route_permute(RouteArgs a) {
   int* offs = counts + E_res;                   // [E_res + 1]
   const int W64 = (P + 63) >> 6;
   unsigned long long* masks = (unsigned long long*)(((uintptr_t)(offs + E_res + 1) + 7) & ~(uintptr_t)7);
-  // every workgroup computes the whole (small) permutation; workgroup 0 stores it
   const bool store = blockIdx.x == 0;
-  for (int p = tid; p < P; p += 256) grp[p] = a.topk_idx[p] % E_res;
-  for (int i = tid; i < E_res; i += 256) counts[i] = 0;
-  for (int i = tid; i < E_res * W64; i += 256) masks[i] = 0ull;
+  for (int i = tid; i < E_res; i += nthr) counts[i] = 0;
+  for (int i = tid; i < E_res * W64; i += nthr) masks[i] = 0ull;
   __syncthreads();
-  for (int p = tid; p < P; p += 256) {
+  for (int p = tid; p < P; p += nthr) {
     const int g = grp[p];
     atomicAdd(&counts[g], 1);
     atomicOr(&masks[g * W64 + (p >> 6)], 1ull << (p & 63));
@@ -277,8 +291,8 @@ __global__ __launch_bounds__(256) void k_route_permute(RouteArgs a) {
   }
   __syncthreads();
   if (store)
-    for (int i = tid; i <= E_res; i += 256) a.offsets[i] = offs[i];
-  for (int p = tid; p < P; p += 256) {
+    for (int i = tid; i <= E_res; i += nthr) a.offsets[i] = offs[i];
+  for (int p = tid; p < P; p += nthr) {
     const int g = grp[p];
     const unsigned long long* mk = masks + g * W64;
     int rank = 0;
@@ -300,7 +314,7 @@ __global__ __launch_bounds__(256) void k_route_permute(RouteArgs a) {
   const long long total = (long long)ksteps * P * 4;
   const u32x4* src = (const u32x4*)a.gsrc;
   u32x4* dst = (u32x4*)a.gdst;
-  for (long long i = (long long)blockIdx.x * 256 + tid; i < total; i += (long long)gridDim.x * 256) {
+  for (long long i = (long long)blockIdx.x * nthr + tid; i < total; i += (long long)gridDim.x * nthr) {
     const int q = (int)(i & 3);
     const long long t = i >> 2;
     const int r = (int)(t % P);
@@ -311,15 +325,21 @@ __global__ __launch_bounds__(256) void k_route_permute(RouteArgs a) {
   }
 }
 
+__global__ __launch_bounds__(256) void k_route_permute(RouteArgs a) {
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  int* grp = (int*)lds;
+  const int P = a.n_tok * a.k;
+  for (int p = threadIdx.x; p < P; p += blockDim.x) grp[p] = a.topk_idx[p] % a.E_res;
+  __syncthreads();
+  permute_body(a, lds);
+}
+
 int route_lds_bytes(int n_tok, int k, int E_res) {
   const int P = n_tok * k;
   return (2 * P + 2 * E_res + 1) * 4 + 16 + E_res * ((P + 63) / 64) * 8;
 }
 
 hipError_t launch_route(const RouteArgs& a, hipStream_t st) {
-  SPA_LAUNCH_SPLITS(a.pv.S, k_route_topk, dim3((a.n_tok + 3) / 4), dim3(256), 0, st, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
   static bool lds_raised = false;   // the permutation may need more than the default 64 KB of LDS
   if (!lds_raised) {
     (void)hipFuncSetAttribute((const void*)k_route_permute, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
@@ -330,7 +350,11 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t st) {
     const long long chunks = (long long)a.gK * a.gesz / 16 * a.n_tok * a.k;
     wgs = (int)std::min<long long>(64, std::max<long long>(1, chunks / (256 * 8)));
   }
-  hipLaunchKernelGGL(k_route_permute, dim3(wgs), dim3(256), route_lds_bytes(a.n_tok, a.k, a.E_res), st, a);
+  const int lds = route_lds_bytes(a.n_tok, a.k, a.E_res);
+  SPA_LAUNCH_SPLITS(a.pv.S, k_route_topk, dim3((a.n_tok + 3) / 4), dim3(256), 0, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_route_permute, dim3(wgs), dim3(256), lds, st, a);
   return hipGetLastError();
 }
 
