@@ -142,13 +142,35 @@ GemmPlan plan_gemm(int kc, const spa_model_desc* m, int n_tok, int n_cus) {
     busy_blocks = std::min(p.rb_stride, std::max(1, std::min(groups, R)));
   }
   const int nks = K / p.ks;
+  const int s_max = std::min(16, std::max(1, nks / 8));   // two k-steps per wave; the finish kernels sum <= 16
 #ifndef SPA_GEMM_TARGET_X4
 #define SPA_GEMM_TARGET_X4 5
 #endif
   const int target = std::max(256, (n_cus * SPA_GEMM_TARGET_X4) / 4);
   int S = (target + p.n_tiles * busy_blocks - 1) / (p.n_tiles * busy_blocks);
-  S = std::min(S, std::max(1, nks / 8));   // two k-steps per wave at least
-  S = std::min(S, 16);                     // the finish kernels sum at most 16 splits
+  const int T = p.n_tiles * busy_blocks;
+  if (groups == 0 && T < n_cus) {
+    // Dense products with fewer tiles than CUs: a workgroup streams its k
+    // range at about one CU's share of the bandwidth, so a grid a little
+    // larger than the CU count leaves the CUs holding two workgroups to
+    // finish alone. Take the smallest split whose grid fills between 3/4 of
+    // the CUs and all of them (one workgroup each), else the split with the
+    // least work on the busiest CU.
+    S = 0;
+    for (int c = 1; c <= s_max && !S; ++c)
+      if (4 * T * c >= 3 * n_cus && T * c <= n_cus) S = c;
+    if (!S) {
+      double best = 1e30;
+      for (int c = 1; c <= s_max; ++c) {
+        const double per_cu = (double)((T * c + n_cus - 1) / n_cus) / c;   // splits' work on the busiest CU
+        if (per_cu < best - 1e-9) {
+          best = per_cu;
+          S = c;
+        }
+      }
+    }
+  }
+  S = std::min(S, s_max);
   if (p.epi == EPI_SWIGLU) S = 1;
   p.S = std::max(1, S);
   if (kc == KC_DOWN && p.S == 1) p.epi = EPI_STORE;
