@@ -36,7 +36,6 @@ constexpr int kStepBytes = 64;     // one k-step of one row
 #define SPA_GEMM_W_NT 1
 #endif
 constexpr bool kWStream = SPA_GEMM_W_NT != 0;   // weights are read once per launch: non-temporal loads
-constexpr int kRedBytes = 3 * 4 * 64 * 16;     // LDS for the wave reduction (one 16-row tile, <= 4 fragments)
 
 // ring depth: keeps the register budget of two workgroups per CU
 #ifndef SPA_GEMM_RING_BIG
@@ -51,7 +50,7 @@ template <int CT, int MT> struct Ring {
 
 template <int WT, int EPI, int CT, int MT>
 __global__ __launch_bounds__(256, 2) void k_gemm(GemmArgs a) {
-  __shared__ __attribute__((aligned(16))) char red[kRedBytes];
+  __shared__ __attribute__((aligned(16))) char red[3 * CT * 64 * 16];   // wave reduction of one 16-row tile
   constexpr int P = Ring<CT, MT>::P;
   constexpr int BR = 16 * MT;
   constexpr int TC = 16 * CT;
@@ -299,6 +298,9 @@ static hipError_t launch_ct(const GemmArgs& a, hipStream_t st) {
   if (a.tile_cols == 64) return launch_mt<WT, EPI, 4>(a, st);
   if constexpr (WT != DT_F32) {
     if (a.tile_cols == 32) return launch_mt<WT, EPI, 2>(a, st);
+    if (a.tile_cols == 96) return launch_mt<WT, EPI, 6>(a, st);
+    if constexpr (EPI != EPI_SWIGLU)   // SwiGLU tiles pair gate and up halves: an even fragment count
+      if (a.tile_cols == 48) return launch_mt<WT, EPI, 3>(a, st);
   } else if constexpr (EPI == EPI_PARTIAL) {
     if (a.tile_cols == 16) return launch_mt<WT, EPI, 1>(a, st);   // the router: few outputs, many workgroups
   }

@@ -100,7 +100,7 @@ static int pick_blk_rows(int need) {
   return 128;
 }
 
-// Shape of one projection: rows per block (one W read serves them all), 64
+// Shape of one projection: rows per block (one W read serves them all),
 // output columns per tile, and the split-K factor that gives the chip enough
 // workgroups. Grouped (expert) products size the row block for the expected
 // rows per expert plus two standard deviations of uniform routing, so an
@@ -116,9 +116,6 @@ GemmPlan plan_gemm(int kc, const spa_model_desc* m, int n_tok, int n_cus) {
     case KC_ROUTER: K = m->hidden; p.ks = 16; N = m->n_experts; p.tile_cols = 16; break;
     case KC_GATEUP: K = m->hidden; p.ks = ks_of(m->expert_dtype); N = 2 * m->inter; groups = m->n_resident;
       p.epi = EPI_SWIGLU;
-#ifdef SPA_GEMM_GU_TC
-      if (m->expert_dtype != SPA_F32) p.tile_cols = SPA_GEMM_GU_TC;
-#endif
       break;
     case KC_DOWN: K = m->inter; p.ks = ks_of(m->expert_dtype); N = m->hidden; groups = m->n_resident; break;
     default: break;
@@ -139,7 +136,9 @@ GemmPlan plan_gemm(int kc, const spa_model_desc* m, int n_tok, int n_cus) {
     const int rb_all = (R + p.blk_rows - 1) / p.blk_rows;   // every row in one group
     p.rb_stride = std::min(groups * rb_all, rb_all + groups);
     p.part_rows = R;
-    busy_blocks = std::min(p.rb_stride, std::max(1, std::min(groups, R)));
+    // groups expected to hold rows, times the blocks such a group needs
+    const int per_group = std::max(1, (int)std::ceil(mean / p.blk_rows));
+    busy_blocks = std::min(p.rb_stride, std::max(1, std::min(groups, R)) * per_group);
   }
   const int nks = K / p.ks;
   const int s_max = std::min(16, std::max(1, nks / 8));   // two k-steps per wave; the finish kernels sum <= 16
@@ -148,25 +147,43 @@ GemmPlan plan_gemm(int kc, const spa_model_desc* m, int n_tok, int n_cus) {
 #endif
   const int target = std::max(256, (n_cus * SPA_GEMM_TARGET_X4) / 4);
   int S = (target + p.n_tiles * busy_blocks - 1) / (p.n_tiles * busy_blocks);
+  // A workgroup streams its k range at about one CU's share of the
+  // bandwidth, so a grid a little larger than the CU count leaves the CUs
+  // holding two workgroups to finish alone. Fill rule: the first (tile width,
+  // split) whose grid fills between 3/4 of the CUs and all of them, one
+  // workgroup each. Expert products try wider tiles first (fewer activation
+  // loads per weight byte: 96-column tiles hold at most 80 rows in
+  // registers; SwiGLU needs an even number of 16-column fragments and takes
+  // no split), dense products 64 columns; fewer splits first (less partial
+  // traffic). Without such a grid: 64 columns and the split with the least
+  // work on the busiest CU (dense products only while their tiles are fewer
+  // than the CUs; larger ones keep the target above).
   const int T = p.n_tiles * busy_blocks;
-  if (groups == 0 && T < n_cus) {
-    // Dense products with fewer tiles than CUs: a workgroup streams its k
-    // range at about one CU's share of the bandwidth, so a grid a little
-    // larger than the CU count leaves the CUs holding two workgroups to
-    // finish alone. Take the smallest split whose grid fills between 3/4 of
-    // the CUs and all of them (one workgroup each), else the split with the
-    // least work on the busiest CU.
-    S = 0;
-    for (int c = 1; c <= s_max && !S; ++c)
-      if (4 * T * c >= 3 * n_cus && T * c <= n_cus) S = c;
-    if (!S) {
-      double best = 1e30;
-      for (int c = 1; c <= s_max; ++c) {
-        const double per_cu = (double)((T * c + n_cus - 1) / n_cus) / c;   // splits' work on the busiest CU
-        if (per_cu < best - 1e-9) {
-          best = per_cu;
-          S = c;
-        }
+  const int s_lim = p.epi == EPI_SWIGLU ? 1 : s_max;
+  bool found = kc == KC_ROUTER;   // the router keeps its 16-column fp32 tiles
+  for (int tc : {96, 64, 48}) {
+    if (found) break;
+    if (groups == 0 ? tc != 64 : (m->expert_dtype == SPA_F32 && tc != 64)) continue;
+    if ((tc == 96 && p.blk_rows > 80) || (tc == 48 && p.epi == EPI_SWIGLU)) continue;
+    const int tiles = (N + tc - 1) / tc;
+    for (int c = 1; c <= s_lim && !found; ++c) {
+      const int w = tiles * busy_blocks * c;
+      if (4 * w >= 3 * n_cus && w <= n_cus) {
+        found = true;
+        p.tile_cols = tc;
+        p.n_tiles = tiles;
+        p.part_ld = tiles * tc;
+        S = c;
+      }
+    }
+  }
+  if (!found && (groups > 0 || T < n_cus)) {
+    double best = 1e30;
+    for (int c = 1; c <= s_lim; ++c) {
+      const double per_cu = (double)((T * c + n_cus - 1) / n_cus) / c;   // splits' work on the busiest CU
+      if (per_cu < best - 1e-9) {
+        best = per_cu;
+        S = c;
       }
     }
   }
@@ -177,6 +194,10 @@ GemmPlan plan_gemm(int kc, const spa_model_desc* m, int n_tok, int n_cus) {
   return p;
 }
 
+// Columns of the partial buffer of an N-column product: any tile width the
+// plans use (16, 48, 64, 96) pads N to at most this.
+static size_t part_ld_bound(int N) { return (size_t)(N + 191) / 192 * 192; }
+
 // Partial space for any call of up to n_tok tokens: the largest split any
 // plan may choose (16, and at most an eighth of the k-steps) times the rows
 // and padded columns of the product.
@@ -185,8 +206,10 @@ static size_t gemm_part_floats(const spa_model_desc* m, int n_tok) {
   for (int kc : {KC_QKV, KC_OPROJ, KC_ROUTER, KC_DOWN}) {
     const GemmPlan p = plan_gemm(kc, m, n_tok, 1);
     int K = kc == KC_QKV || kc == KC_ROUTER ? m->hidden : (kc == KC_OPROJ ? m->n_q_heads * m->head_dim : m->inter);
+    const int N = kc == KC_QKV ? (m->n_q_heads + 2 * m->n_kv_heads) * m->head_dim
+                               : (kc == KC_ROUTER ? m->n_experts : m->hidden);
     const size_t s_max = (size_t)std::min(16, std::max(1, K / p.ks / 8));
-    mx = std::max(mx, s_max * p.part_rows * p.part_ld);
+    mx = std::max(mx, s_max * p.part_rows * std::max((size_t)p.part_ld, part_ld_bound(N)));
   }
   return mx;
 }

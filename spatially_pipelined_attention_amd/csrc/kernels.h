@@ -31,7 +31,7 @@ struct GemmArgs {
   const float* w_scale;     // E4M3: per W row scale, group stride ws_gstride
   long long ws_gstride;
   int n_tiles;              // output column tiles of tile_cols (SwiGLU: half gate, half up)
-  int tile_cols;            // 32 or 64
+  int tile_cols;            // 16 (fp32 router), 32, 48, 64 or 96
   int blk_rows;             // rows per row block (16, 32, 48, 64, 80 or 128)
   int n_groups;
   const int* group_off;     // [n_groups+1] or null (one group of n_rows)
