@@ -149,41 +149,39 @@ GemmPlan plan_gemm(int kc, const spa_model_desc* m, int n_tok, int n_cus) {
   int S = (target + p.n_tiles * busy_blocks - 1) / (p.n_tiles * busy_blocks);
   // A workgroup streams its k range at about one CU's share of the
   // bandwidth, so a grid a little larger than the CU count leaves the CUs
-  // holding two workgroups to finish alone. Fill rule: the first (tile width,
-  // split) whose grid fills between 3/4 of the CUs and all of them, one
-  // workgroup each. Expert products try wider tiles first (fewer activation
-  // loads per weight byte: 96-column tiles hold at most 80 rows in
-  // registers; SwiGLU needs an even number of 16-column fragments and takes
-  // no split), dense products 64 columns; fewer splits first (less partial
-  // traffic). Without such a grid: 64 columns and the split with the least
-  // work on the busiest CU (dense products only while their tiles are fewer
-  // than the CUs; larger ones keep the target above).
-  const int T = p.n_tiles * busy_blocks;
-  const int s_lim = p.epi == EPI_SWIGLU ? 1 : s_max;
-  bool found = kc == KC_ROUTER;   // the router keeps its 16-column fp32 tiles
-  for (int tc : {96, 64, 48}) {
-    if (found) break;
-    if (groups == 0 ? tc != 64 : (m->expert_dtype == SPA_F32 && tc != 64)) continue;
-    if ((tc == 96 && p.blk_rows > 80) || (tc == 48 && p.epi == EPI_SWIGLU)) continue;
-    const int tiles = (N + tc - 1) / tc;
-    for (int c = 1; c <= s_lim && !found; ++c) {
-      const int w = tiles * busy_blocks * c;
-      if (4 * w >= 3 * n_cus && w <= n_cus) {
-        found = true;
-        p.tile_cols = tc;
-        p.n_tiles = tiles;
-        p.part_ld = tiles * tc;
-        S = c;
-      }
-    }
-  }
-  if (!found && (groups > 0 || T < n_cus)) {
+  // holding two workgroups to finish alone, and a smaller one leaves CUs
+  // idle. The (tile width, split) pair is the one of least modelled time,
+  // in units of the weight stream at full fill:
+  //   ceil(w / n_cus) * n_cus / w          the busiest CU's share (w workgroups)
+  //   * (1 + 0.6 * block rows / tile cols)  activation loads per weight byte
+  //   + 4 * splits * rows per group / (K * weight element size)
+  //                                         the fp32 split partials, written and
+  //                                         read once (about half of it served
+  //                                         by the last-level cache)
+  // Dense products use 64-column tiles; expert products also 96 (at most 80
+  // rows in registers) and 48 (not SwiGLU, whose tiles pair gate and up
+  // halves). SwiGLU takes no split. Ties keep the wider tile, then the
+  // smaller split. The router keeps its 16-column fp32 tiles and the target.
+  if (kc != KC_ROUTER) {
+    const double rows_per_group = groups == 0 ? (double)n_tok : (double)n_tok * m->top_k / groups;
+    const double wbytes_per_k = (double)K * esz_of(groups == 0 ? m->dense_dtype : m->expert_dtype);
+    const int s_lim = p.epi == EPI_SWIGLU ? 1 : s_max;
     double best = 1e30;
-    for (int c = 1; c <= s_lim; ++c) {
-      const double per_cu = (double)((T * c + n_cus - 1) / n_cus) / c;   // splits' work on the busiest CU
-      if (per_cu < best - 1e-9) {
-        best = per_cu;
-        S = c;
+    for (int tc : {96, 64, 48}) {
+      if ((groups == 0 || m->expert_dtype == SPA_F32) && tc != 64) continue;
+      if ((tc == 96 && p.blk_rows > 80) || (tc == 48 && p.epi == EPI_SWIGLU)) continue;
+      const int tiles = (N + tc - 1) / tc;
+      for (int c = 1; c <= s_lim; ++c) {
+        const double w = (double)tiles * busy_blocks * c;
+        const double fill = std::ceil(w / n_cus) * n_cus / w;
+        const double cost = fill * (1.0 + 0.6 * p.blk_rows / tc) + 4.0 * c * rows_per_group / wbytes_per_k;
+        if (cost < best - 1e-9) {
+          best = cost;
+          p.tile_cols = tc;
+          p.n_tiles = tiles;
+          p.part_ld = tiles * tc;
+          S = c;
+        }
       }
     }
   }
