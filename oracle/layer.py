@@ -11,8 +11,13 @@ operator names but not their formulas; the readings taken here are:
 
   * pre-norm residual block: xn = RMSNorm(x); h = x + Attn(xn) Wo^T;
     hn = RMSNorm(h); x' = h + MoE(hn); RMSNorm(v) = v * gamma / sqrt(mean(v^2) + eps);
-  * RoPE (listed in Figure 3) is left out: the KV history is synthetic, so
-    positions carry no meaning;
+  * RoPE (listed in Figure 3) is optional (Dims.rope_theta > 0): the
+    rotary embedding of the original RoFormer formulation, adjacent pairs
+    (2i, 2i+1) of a head turned by pos * theta^(-2i/D), applied to q and to
+    the new k at the decoded position L-1 before they are stored; the cache
+    holds keys already rotated at their own positions, which for the
+    synthetic history means the generated values are taken as rotated keys.
+    rope_theta = 0 leaves it out;
   * grouped-query attention with contiguous groups: query head h reads KV
     head h // (Hq / Hkv); scores scaled by 1/sqrt(D);
   * one learned sink logit per query head joins the softmax denominator and
@@ -55,6 +60,7 @@ class Dims:
     inter: int
     window: int
     eps: float = 1e-5
+    rope_theta: float = 0.0    # 0: no rotary embedding
 
 
 @dataclasses.dataclass(frozen=True)
@@ -87,6 +93,22 @@ def rmsnorm(x, gamma, eps: float) -> np.ndarray:
 def linear(x, w) -> np.ndarray:
     """y = x W^T with W stored [out][in] (Figure 3 "Q proj", "KV proj", "Output proj")."""
     return np.asarray(x, np.float64) @ np.asarray(w, np.float64).T
+
+
+def rope(x, pos: int, theta: float) -> np.ndarray:
+    """Figure 3 "RoPE" on the last axis of x (length D, even): the pair
+    (x[2i], x[2i+1]) is turned by the angle pos * theta^(-2i/D):
+      out[2i]   = x[2i] cos(a) - x[2i+1] sin(a)
+      out[2i+1] = x[2i] sin(a) + x[2i+1] cos(a)."""
+    x = np.asarray(x, np.float64)
+    D = x.shape[-1]
+    i = np.arange(D // 2, dtype=np.float64)
+    a = float(pos) * np.power(float(theta), -2.0 * i / D)
+    c, s = np.cos(a), np.sin(a)
+    out = np.empty_like(x)
+    out[..., 0::2] = x[..., 0::2] * c - x[..., 1::2] * s
+    out[..., 1::2] = x[..., 0::2] * s + x[..., 1::2] * c
+    return out
 
 
 def attention_window(kind: str, L: int, window: int) -> Tuple[int, int]:
@@ -237,11 +259,16 @@ def layer_forward(dims: Dims, num: Numerics, kind: str, x, dense: Dict[str, np.n
     x = np.asarray(x, np.float64)
     B = x.shape[0]
 
-    # Norm + QKV (RMSNorm, Q proj, KV proj)
+    # Norm + QKV (RMSNorm, Q proj, KV proj) [+ RoPE of q and the new k at L-1]
     xn = rmsnorm(x, dense["gamma1"], dims.eps)
     qkv = linear(_q(xn, num.act), dense["wqkv"])
-    q = _q(qkv[:, : Hq * D], num.act).reshape(B, Hq, D)
-    k_new = _q(qkv[:, Hq * D: (Hq + Hkv) * D], num.kv).reshape(B, Hkv, D)
+    q = qkv[:, : Hq * D].reshape(B, Hq, D)
+    k_new = qkv[:, Hq * D: (Hq + Hkv) * D].reshape(B, Hkv, D)
+    if dims.rope_theta > 0:
+        q = np.stack([rope(q[b], int(L[b]) - 1, dims.rope_theta) for b in range(B)])
+        k_new = np.stack([rope(k_new[b], int(L[b]) - 1, dims.rope_theta) for b in range(B)])
+    q = _q(q, num.act)
+    k_new = _q(k_new, num.kv)
     v_new = _q(qkv[:, (Hq + Hkv) * D:], num.kv).reshape(B, Hkv, D)
 
     # Attention (FMHA over the window, the new token appended at L-1)

@@ -1,5 +1,6 @@
 """Pins of the oracle's decode layer (CPU): library routines, closed forms,
 invariants and a pure-Python brute force on tiny shapes."""
+import dataclasses
 import math
 
 import numpy as np
@@ -219,7 +220,9 @@ def test_zero_gate_gives_identity_moe_and_doubling_down_doubles_term():
 
 # ----------------------------------------------------------------------------- whole layer
 def brute_layer(dims, kind, x, dense, experts, L, Kh, Vh):
-    """Pure-Python loops over every index of the layer (float64)."""
+    """Pure-Python loops over every index of the layer (float64). With
+    dims.rope_theta > 0 the q heads and the new k heads are turned pair by
+    pair at position L - 1 (RoFormer's rotary embedding)."""
     H, Hq, Hkv, D, I = dims.hidden, dims.n_q_heads, dims.n_kv_heads, dims.head_dim, dims.inter
     G = Hq // Hkv
     out = []
@@ -228,6 +231,13 @@ def brute_layer(dims, kind, x, dense, experts, L, Kh, Vh):
         ms = sum(v * v for v in xb) / H
         xn = [xb[i] * dense["gamma1"][i] / math.sqrt(ms + dims.eps) for i in range(H)]
         qkv = [sum(xn[i] * dense["wqkv"][r][i] for i in range(H)) for r in range((Hq + 2 * Hkv) * D)]
+        if dims.rope_theta > 0:
+            for head in range(Hq + Hkv):          # q heads, then k heads
+                for i in range(D // 2):
+                    ang = (L[b] - 1) / dims.rope_theta ** (2 * i / D)
+                    u, v = qkv[head * D + 2 * i], qkv[head * D + 2 * i + 1]
+                    qkv[head * D + 2 * i] = u * math.cos(ang) - v * math.sin(ang)
+                    qkv[head * D + 2 * i + 1] = u * math.sin(ang) + v * math.cos(ang)
         lo = 0 if kind == "full" else max(0, L[b] - dims.window)
         att = []
         for hq in range(Hq):
@@ -269,9 +279,10 @@ def brute_layer(dims, kind, x, dense, experts, L, Kh, Vh):
     return np.array(out)
 
 
-@pytest.mark.parametrize("kind,E_res", [("full", 8), ("sliding", 8), ("sliding", 3)])
-def test_layer_matches_brute_force(kind, E_res):
-    dims = _tiny(E_res=E_res)
+@pytest.mark.parametrize("kind,E_res,theta", [("full", 8, 0.0), ("sliding", 8, 0.0), ("sliding", 3, 0.0),
+                                                ("full", 8, 10000.0), ("sliding", 3, 500.0)])
+def test_layer_matches_brute_force(kind, E_res, theta):
+    dims = dataclasses.replace(_tiny(E_res=E_res), rope_theta=theta)
     rng = np.random.default_rng(12)
     dense, experts = _params(dims, rng)
     B, L = 3, [9, 4, 6]
