@@ -299,7 +299,8 @@ def main():
         "config": {"workload": f"{name}: {wl.n_layers} layers alternating sliding({wl.window})/full, "
                                f"{wl.batch} sequences, KV U[{wl.kv_len_lo},{wl.kv_len_hi}], H {wl.hidden}, "
                                f"{wl.n_q_heads}q/{wl.n_kv_heads}kv x {wl.head_dim}, {wl.n_resident} resident "
-                               f"experts of {wl.n_experts} (top-{wl.top_k}), I {wl.inter}",
+                               f"experts of {wl.n_experts} (top-{wl.top_k}), I {wl.inter}"
+                               + (f", RoPE base {wl.rope_theta:g}" if wl.rope_theta > 0 else ""),
                    "schedule": sched,
                    "virtual_comm": ({"latency_us": comm[0], "gbps": comm[1],
                                      "endpoints": "attention all-reduce, MoE dispatch, MoE combine per layer"}

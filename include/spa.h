@@ -125,6 +125,13 @@ typedef struct spa_model_desc {
    * 0 <= comm_gbps <= 100000. */
   float comm_latency_us;
   float comm_gbps;
+  /* Figure 3 "RoPE": with rope_theta > 0, q and the new k are turned at the
+   * decoded position p = L-1 before they are stored (q as the attention
+   * input, k into the cache), pair by pair: (v[2i], v[2i+1]) of a head by
+   * the angle p * rope_theta^(-2i/D) (RoFormer's rotary embedding; cached
+   * keys are taken as already rotated at their own positions). 0 (the
+   * zero-initialised default) leaves it out. Finite, >= 0. */
+  float rope_theta;
 } spa_model_desc;
 
 /* One layer's parameters and KV cache (device pointers). */
@@ -217,9 +224,10 @@ spa_status spa_pack_weights(spa_ctx* ctx, int32_t dtype, int32_t n_mats, int32_t
 spa_status spa_rms_norm(spa_ctx* ctx, const spa_model_desc* m, const float* x, const float* gamma, int32_t n_tok,
                         void* xn_out, void* stream);
 
-/* Figure 3 "Q proj, KV proj": [q | k | v] = xn Wqkv^T from the normalised
- * rows xn [n_tok][H] (dense_dtype); q -> q_out [n_tok][Hq*D] (kv_dtype), k and
- * v -> the layer's cache at position kv_len[s] - 1 of sequence s = tok0 + row. */
+/* Figure 3 "Q proj, KV proj" (+ "RoPE" when the model's rope_theta > 0):
+ * [q | k | v] = xn Wqkv^T from the normalised rows xn [n_tok][H]
+ * (dense_dtype); q -> q_out [n_tok][Hq*D] (kv_dtype), k and v -> the layer's
+ * cache at position kv_len[s] - 1 of sequence s = tok0 + row. */
 spa_status spa_qkv_append(spa_ctx* ctx, const spa_model_desc* m, const spa_layer* l, const spa_batch* b,
                           int32_t tok0, int32_t n_tok, const void* xn, void* q_out, void* ws, size_t ws_bytes,
                           void* stream);

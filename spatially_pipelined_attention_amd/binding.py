@@ -37,7 +37,8 @@ class spa_model_desc(C.Structure):
                 ("head_dim", C.c_int32), ("n_experts", C.c_int32), ("n_resident", C.c_int32),
                 ("top_k", C.c_int32), ("inter", C.c_int32), ("window", C.c_int32), ("n_layers", C.c_int32),
                 ("eps", C.c_float), ("dense_dtype", C.c_int32), ("expert_dtype", C.c_int32),
-                ("kv_dtype", C.c_int32), ("comm_latency_us", C.c_float), ("comm_gbps", C.c_float)]
+                ("kv_dtype", C.c_int32), ("comm_latency_us", C.c_float), ("comm_gbps", C.c_float),
+                ("rope_theta", C.c_float)]
 
 
 class spa_layer(C.Structure):

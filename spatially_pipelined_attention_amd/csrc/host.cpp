@@ -60,6 +60,7 @@ spa_status validate_model(const spa_model_desc* m) {
   if (!(m->comm_latency_us >= 0.f && m->comm_latency_us <= 1000.f))
     return fail(SPA_EINVAL, "comm_latency_us must be in [0, 1000]");
   if (!(m->comm_gbps >= 0.f && m->comm_gbps <= 100000.f)) return fail(SPA_EINVAL, "comm_gbps must be in [0, 100000]");
+  if (!(m->rope_theta >= 0.f && m->rope_theta <= 3.0e38f)) return fail(SPA_EINVAL, "rope_theta must be finite and >= 0");
   return SPA_OK;
 }
 
@@ -424,6 +425,7 @@ static spa_status op_qkv(spa_ctx* ctx, const spa_model_desc* m, const spa_layer*
   f.window = m->window;
   f.tok0 = tok0;
   f.err = s.err;
+  f.rope_theta = m->rope_theta;
   HookScope hs(th, KC_QKV, st);
   SPA_HIP(launch_gemm(m->dense_dtype, EPI_PARTIAL, a, st));
   SPA_HIP(launch_qkv_finish(f, st));

@@ -73,6 +73,7 @@ struct QkvFinishArgs {
   int window;
   int tok0;
   int* err;
+  float rope_theta;         // > 0: rotary embedding of q and k at position L-1
 };
 hipError_t launch_qkv_finish(const QkvFinishArgs& a, hipStream_t st);
 

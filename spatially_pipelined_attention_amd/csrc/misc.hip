@@ -2,7 +2,8 @@
 // Pipelining paper): they finish the split products, one workgroup per token
 // row, and fuse the light operators that need whole rows:
 //   k_qkv_finish   - sum of the QKV splits -> q, and the new K/V written into
-//                    the cache slot of position L-1 ("KV proj" + append);
+//                    the cache slot of position L-1 ("KV proj" + append),
+//                    with the rotary embedding of q and k ("RoPE") when set;
 //   k_oproj_finish - residual add of the output projection ("Add+Norm"), the
 //                    RMSNorm statistic, and the normalised row in fp32 (router
 //                    input), bf16 and power-of-two-scaled E4M3 (expert input);
@@ -101,7 +102,16 @@ __global__ __launch_bounds__(256) void k_qkv_finish(QkvFinishArgs a) {
   const int pos = L - 1;
   const bool ok = (L >= 1) && (a.kv_kind == KV_RING || L <= a.kv_cap[seq]);
   if (!ok && c == 0 && a.err) atomicOr(a.err, ERR_KV_LEN);
-  const float v = part_sum<SM>(a.pv, r, c);
+  float v = part_sum<SM>(a.pv, r, c);
+  if (a.rope_theta > 0.f && c < QD + Hkv * D) {
+    // RoPE: the pair (2i, 2i+1) of the head turned by pos * theta^(-2i/D);
+    // the angle and its sine and cosine in double, the rotation in fp32
+    const int d = c % D, i = d >> 1;
+    const float w = part_sum<SM>(a.pv, r, c ^ 1);
+    const double ang = (double)pos * exp2(-(2.0 * i / D) * log2((double)a.rope_theta));
+    const float cs = (float)cos(ang), sn = (float)sin(ang);
+    v = (d & 1) ? w * sn + v * cs : v * cs - w * sn;
+  }
   if (c < QD) {
     if (a.kv_dtype == DT_BF16) ((uint16_t*)a.q_out)[(long long)r * QD + c] = f32_to_bf16(v);
     else ((float*)a.q_out)[(long long)r * QD + c] = v;

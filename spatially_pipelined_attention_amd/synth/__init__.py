@@ -75,6 +75,7 @@ class Workload:
     w_std: float = 0.02
     router_std: Optional[float] = None   # None: 1/sqrt(hidden)
     eps: float = 1e-5
+    rope_theta: float = 0.0              # rotary embedding base (0: none)
 
     @property
     def qkv_rows(self) -> int:
@@ -114,6 +115,9 @@ WORKLOADS: Dict[str, Workload] = {
     # every sequence at 32,768 positions, otherwise the 36-layer share above
     "gptoss_36l_kv32k": Workload("gptoss_36l_kv32k", 1006, 2880, 64, 8, 64, 128, 4, 4, 2880, 128, 36,
                                  64, 32768, 32768, _alternating(36), "bf16", "bf16", "bf16"),
+    # the 36-layer one-GPU share with the rotary embedding of Figure 3 (base 10000)
+    "gptoss_36l_b64_rope": Workload("gptoss_36l_b64_rope", 1007, 2880, 64, 8, 64, 128, 4, 4, 2880, 128, 36,
+                                    64, 1024, 8192, _alternating(36), "bf16", "bf16", "bf16", rope_theta=10000.0),
 }
 
 

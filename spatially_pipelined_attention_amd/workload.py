@@ -22,9 +22,11 @@ _TORCH = {"f32": torch.float32, "bf16": torch.bfloat16}
 
 
 def model_desc(wl: synth.Workload) -> B.spa_model_desc:
-    return B.spa_model_desc(wl.hidden, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.n_experts, wl.n_resident,
-                            wl.top_k, wl.inter, wl.window, wl.n_layers, wl.eps, _DT[wl.w_dtype],
-                            _DT[wl.expert_dtype], _DT[wl.kv_dtype])
+    m = B.spa_model_desc(wl.hidden, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.n_experts, wl.n_resident,
+                         wl.top_k, wl.inter, wl.window, wl.n_layers, wl.eps, _DT[wl.w_dtype],
+                         _DT[wl.expert_dtype], _DT[wl.kv_dtype])
+    m.rope_theta = float(wl.rope_theta)
+    return m
 
 
 def set_comm(m: B.spa_model_desc, latency_us: float, gbps: float) -> B.spa_model_desc:

@@ -19,7 +19,7 @@ TOL = {"bf16": 2e-2, "e4m3": 6e-2, "f32": 2.5e-4}
 
 def dims(wl: synth.Workload) -> ol.Dims:
     return ol.Dims(wl.hidden, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.n_experts, wl.n_resident, wl.top_k,
-                   wl.inter, wl.window, wl.eps)
+                   wl.inter, wl.window, wl.eps, wl.rope_theta)
 
 
 def numerics(wl: synth.Workload) -> ol.Numerics:
