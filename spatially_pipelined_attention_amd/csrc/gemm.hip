@@ -309,6 +309,7 @@ static hipError_t launch_ct(const GemmArgs& a, hipStream_t st) {
 
 hipError_t launch_gemm(int wt, int epi, const GemmArgs& a, hipStream_t st) {
   if (a.group_off && a.n_groups > 128) return hipErrorInvalidValue;   // the block scan holds 2 groups per lane
+  if (a.tile_cols == 128) return launch_gemm_big(wt, epi, a, st);    // 128-row blocks: the LDS-tiled kernel
 #define SPA_CASE(W, E) \
   if (wt == W && epi == E) return launch_ct<W, E>(a, st);
   SPA_CASE(DT_BF16, EPI_PARTIAL)

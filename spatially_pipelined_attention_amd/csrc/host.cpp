@@ -187,6 +187,20 @@ GemmPlan plan_gemm(int kc, const spa_model_desc* m, int n_tok, int n_cus) {
     }
   }
   S = std::min(S, s_max);
+  // Full 128-row blocks (hundreds of rows per expert, or 256 and more dense
+  // rows): the LDS-tiled kernel, 128 weight rows per workgroup, its split
+  // chosen for about two workgroups per CU (at most 6; SwiGLU takes none).
+  const int wdt = groups == 0 ? m->dense_dtype : m->expert_dtype;
+#ifndef SPA_GEMM_BIG
+#define SPA_GEMM_BIG 1
+#endif
+  if (SPA_GEMM_BIG && kc != KC_ROUTER && wdt != SPA_F32 && p.blk_rows == 128 && (groups > 0 || n_tok >= 256)) {
+    p.tile_cols = 128;
+    p.n_tiles = (N + 127) / 128;
+    p.part_ld = p.n_tiles * 128;
+    const int tb = p.n_tiles * busy_blocks;
+    S = std::min({6, s_max, std::max(1, (2 * n_cus + tb - 1) / tb)});
+  }
   if (p.epi == EPI_SWIGLU) S = 1;
   p.S = std::max(1, S);
   if (kc == KC_DOWN && p.S == 1) p.epi = EPI_STORE;
@@ -194,8 +208,8 @@ GemmPlan plan_gemm(int kc, const spa_model_desc* m, int n_tok, int n_cus) {
 }
 
 // Columns of the partial buffer of an N-column product: any tile width the
-// plans use (16, 48, 64, 96) pads N to at most this.
-static size_t part_ld_bound(int N) { return (size_t)(N + 191) / 192 * 192; }
+// plans use (16, 48, 64, 96, 128; all divide 384) pads N to at most this.
+static size_t part_ld_bound(int N) { return (size_t)(N + 383) / 384 * 384; }
 
 // Partial space for any call of up to n_tok tokens: the largest split any
 // plan may choose (16, and at most an eighth of the k-steps) times the rows

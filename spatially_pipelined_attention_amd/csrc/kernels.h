@@ -31,7 +31,7 @@ struct GemmArgs {
   const float* w_scale;     // E4M3: per W row scale, group stride ws_gstride
   long long ws_gstride;
   int n_tiles;              // output column tiles of tile_cols (SwiGLU: half gate, half up)
-  int tile_cols;            // 16 (fp32 router), 32, 48, 64 or 96
+  int tile_cols;            // 16 (fp32 router), 32, 48, 64, 96, or 128 (the LDS-tiled kernel)
   int blk_rows;             // rows per row block (16, 32, 48, 64, 80 or 128)
   int n_groups;
   const int* group_off;     // [n_groups+1] or null (one group of n_rows)
@@ -54,6 +54,9 @@ struct GemmArgs {
 };
 
 hipError_t launch_gemm(int wt, int epi, const GemmArgs& a, hipStream_t st);
+// The 128-row x 128-column LDS-tiled variant (gemm_big.hip): blk_rows 128,
+// tile_cols 128 (SwiGLU: 64 outputs), split-K for partials only.
+hipError_t launch_gemm_big(int wt, int epi, const GemmArgs& a, hipStream_t st);
 
 // q + KV append from the QKV partials, one workgroup per token row.
 struct QkvFinishArgs {
