@@ -133,8 +133,13 @@ def test_three_endpoints_per_layer_and_microbatch(env):
 def test_temporal_iteration_grows_by_the_modelled_time(env):
     wl = env["wl"]
     print("[case] T1 iteration time with and without endpoints", flush=True)
-    _, _, _, t0 = _iterate(env, False, 0, 1, 0, reps=7)
-    _, _, _, t1 = _iterate(env, True, 0, 1, 0, reps=7)
+    _, _, _, t0 = _iterate(env, False, 0, 1, 0, reps=15)
+    _, _, _, t1 = _iterate(env, True, 0, 1, 0, reps=15)
     payloads = [wl.batch * wl.hidden * 2, wl.batch * wl.top_k * wl.hidden * 2, wl.batch * wl.top_k * wl.hidden * 2]
     model = wl.n_layers * sum(LAT_US + p / (GBPS * 1e3) for p in payloads)
-    assert 0.9 * model <= t1 - t0 <= model + 3 * wl.n_layers * 10.0, (t1 - t0, model)
+    n_end = 3 * wl.n_layers
+    # each endpoint lasts at least its modelled time (checked per launch
+    # above), but while it waits the command processor readies the next
+    # dispatch, so up to about a microsecond of that kernel's launch cost per
+    # endpoint leaves the critical path
+    assert model - 1.0 * n_end <= t1 - t0 <= model + 10.0 * n_end, (t1 - t0, model)
