@@ -389,14 +389,35 @@ __global__ __launch_bounds__(kRowThreads) void k_combine(CombineArgs a) {
   __syncthreads();
   float v[kRowCols];
   float ss = 0.f;
+  const int k = a.k;
+  // x = h + sum over the picks in pick order of w * y. With up to 4 picks
+  // and 4 splits all of the thread's loads are issued before the first add
+  // (a clamped pick stands in for a missing one); the sums are the same.
+  constexpr int KB = 4;
+  float yv[kRowCols][KB];
+  const bool batched = SM <= 4 && k >= 1 && k <= KB;
+  if (batched) {
+    // plain expert rows are a product of one split: no branch between loads
+    const PartView pv = a.y ? PartView{a.y, 1, 0, a.H} : a.ypv;
+#pragma unroll
+    for (int i = 0; i < kRowCols; ++i) {
+      const int c = min(threadIdx.x + kRowThreads * i, a.H - 1);
+#pragma unroll
+      for (int s = 0; s < KB; ++s) yv[i][s] = part_sum<SM>(pv, s_row[min(s, k - 1)], c);
+    }
+  }
 #pragma unroll
   for (int i = 0; i < kRowCols; ++i) {
     const int c = threadIdx.x + kRowThreads * i;
     v[i] = 0.f;
     if (c < a.H) {
       float x = a.h[row + c];
-      for (int s = 0; s < a.k; ++s) {
-        x += s_w[s] * y_elem<SM>(a, s_row[s], c);
+      if (batched) {
+#pragma unroll
+        for (int s = 0; s < KB; ++s)
+          if (s < k) x += s_w[s] * yv[i][s];
+      } else {
+        for (int s = 0; s < k; ++s) x += s_w[s] * y_elem<SM>(a, s_row[s], c);
       }
       v[i] = x;
       a.x_out[row + c] = x;
