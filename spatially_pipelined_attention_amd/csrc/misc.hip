@@ -98,9 +98,12 @@ __global__ __launch_bounds__(256) void k_qkv_finish(QkvFinishArgs a) {
   const int D = a.head_dim, Hq = a.n_q_heads, Hkv = a.n_kv_heads;
   const int QD = Hq * D, N = (Hq + 2 * Hkv) * D;
   if (c >= N) return;
+  // the sequence's length, capacity and offset first, all together
   const int L = a.kv_len[seq];
+  const int cap = a.kv_kind == KV_RING ? 0 : a.kv_cap[seq];
+  const long long kv_off = a.kv_kind == KV_RING ? 0 : a.kv_off[seq];
   const int pos = L - 1;
-  const bool ok = (L >= 1) && (a.kv_kind == KV_RING || L <= a.kv_cap[seq]);
+  const bool ok = (L >= 1) && (a.kv_kind == KV_RING || L <= cap);
   if (!ok && c == 0 && a.err) atomicOr(a.err, ERR_KV_LEN);
   float v = part_sum<SM>(a.pv, r, c);
   if (a.rope_theta > 0.f && c < QD + Hkv * D) {
@@ -126,7 +129,7 @@ __global__ __launch_bounds__(256) void k_qkv_finish(QkvFinishArgs a) {
     base = ((long long)seq * Hkv + g) * a.window * D;
     slot = pos % a.window;
   } else {
-    base = (a.kv_off[seq] * Hkv + (long long)g * a.kv_cap[seq]) * D;
+    base = (kv_off * Hkv + (long long)g * cap) * D;
     slot = pos;
   }
   const long long off = is_k ? base + k_offset(slot, d, a.kv_dtype == DT_BF16 ? 32 : 16)
@@ -150,12 +153,21 @@ __global__ __launch_bounds__(kRowThreads) void k_oproj_finish(OprojFinishArgs a)
   const long long row = (long long)r * a.H;
   float h[kRowCols];
   float ss = 0.f;
+  // every load of the thread first (columns past the row clamped to its
+  // last), then the sums
+  float xv[kRowCols], yv[kRowCols];
+#pragma unroll
+  for (int i = 0; i < kRowCols; ++i) {
+    const int c = min(threadIdx.x + kRowThreads * i, a.H - 1);
+    xv[i] = a.x[row + c];
+    yv[i] = part_sum<SM>(a.pv, r, c);
+  }
 #pragma unroll
   for (int i = 0; i < kRowCols; ++i) {
     const int c = threadIdx.x + kRowThreads * i;
     h[i] = 0.f;
     if (c < a.H) {
-      h[i] = a.x[row + c] + part_sum<SM>(a.pv, r, c);
+      h[i] = xv[i] + yv[i];
       a.h_out[row + c] = h[i];
     }
     ss += h[i] * h[i];
@@ -202,13 +214,23 @@ __device__ __forceinline__ void route_token(const RouteArgs& a, int t, int lane,
                                             int (&pi)[8]) {
   const int E = a.E, k = a.k;
   float v[4];
+  // every logit's split loads first (experts past E clamped to the last),
+  // for the 2 or 4 experts a lane holds
+  if (E <= 128) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) v[j] = part_sum<SM>(a.pv, t, min(lane + 64 * j, E - 1));
+    v[2] = v[3] = 0.f;
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[j] = part_sum<SM>(a.pv, t, min(lane + 64 * j, E - 1));
+  }
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int e = lane + 64 * j;
-    v[j] = -INFINITY;
     if (e < E) {
-      v[j] = part_sum<SM>(a.pv, t, e);
       if (store_logits) a.logits[(long long)t * E + e] = v[j];
+    } else {
+      v[j] = -INFINITY;
     }
   }
   for (int p = 0; p < k; ++p) {
