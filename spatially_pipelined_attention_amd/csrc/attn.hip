@@ -483,6 +483,47 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
   if (n_chunks <= 1 || n_chunks > a.max_chunks) return;
   const long long pbase = (((long long)b * a.n_kv_heads + g) * a.max_chunks) * G * (kD + 2);
   const long long cstride = (long long)G * (kD + 2);
+  constexpr int UF = 8;   // up to UF chunks and 2 (head, d) pairs per thread: one pass, every load first
+  if (n_chunks <= UF && G * kD <= 512) {
+    float mv[2][UF], lv[2][UF], ov[2][UF], sk[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int idx = min(tid + 256 * j, G * kD - 1);
+      const int h = idx >> 6, d = idx & 63;
+      sk[j] = a.sinks[g * G + h];
+      const float* pp = a.part + pbase + (long long)h * (kD + 2);
+#pragma unroll
+      for (int i = 0; i < UF; ++i) {
+        const float* q = pp + min(i, n_chunks - 1) * cstride;
+        mv[j][i] = q[kD];
+        lv[j][i] = q[kD + 1];
+        ov[j][i] = q[d];
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int idx = tid + 256 * j;
+      if (idx >= G * kD) continue;
+      const int h = idx >> 6, d = idx & 63;
+      const float sink = sk[j] * kLog2e;
+      float M = sink;
+#pragma unroll
+      for (int i = 0; i < UF; ++i) M = fmaxf(M, mv[j][i]);   // clamped repeats do not change a max
+      float Z = exp2f(sink - M), o = 0.f;
+#pragma unroll
+      for (int i = 0; i < UF; ++i) {
+        if (i >= n_chunks) break;
+        const float f = mv[j][i] == -INFINITY ? 0.f : exp2f(mv[j][i] - M);
+        Z += f * lv[j][i];
+        o += f * ov[j][i];
+      }
+      const float out = o / Z;
+      const long long oi = o_index(a, b, g * G + h, d);
+      if constexpr (KVT == DT_BF16) ((uint16_t*)a.o)[oi] = f32_to_bf16(out);
+      else ((float*)a.o)[oi] = out;
+    }
+    return;
+  }
   constexpr int U = 16;   // chunk states loaded together (clamped, masked)
   for (int idx = tid; idx < G * kD; idx += 256) {
     const int h = idx >> 6, d = idx & 63;
