@@ -346,15 +346,25 @@ __device__ __forceinline__ void permute_body(const RouteArgs& a, char* lds) {
   const long long total = (long long)ksteps * P * 4;
   const u32x4* src = (const u32x4*)a.gsrc;
   u32x4* dst = (u32x4*)a.gdst;
-  for (long long i = (long long)blockIdx.x * nthr + tid; i < total; i += (long long)gridDim.x * nthr) {
-    const int q = (int)(i & 3);
-    const long long t = i >> 2;
-    const int r = (int)(t % P);
-    const int ks = (int)(t / P);
-    const long long srow = rtok[r];
-    dst[i] = src[(srow * ksteps + ks) * 4 + q];
-    if (a.gdst_scale && ks == 0 && q == 0) a.gdst_scale[r] = a.gsrc_scale[srow];
+  // GU chunks per thread in flight: all loads of a round, then its stores
+  constexpr int GU = 8;
+  const long long stride = (long long)gridDim.x * nthr;
+  for (long long i0 = (long long)blockIdx.x * nthr + tid; i0 < total; i0 += GU * stride) {
+    u32x4 v[GU];
+#pragma unroll
+    for (int u = 0; u < GU; ++u) {
+      const long long i = min(i0 + u * stride, total - 1);   // past the end: a repeat, not stored
+      const long long t = i >> 2;
+      v[u] = src[((long long)rtok[(int)(t % P)] * ksteps + t / P) * 4 + (i & 3)];
+    }
+#pragma unroll
+    for (int u = 0; u < GU; ++u) {
+      const long long i = i0 + u * stride;
+      if (i < total) dst[i] = v[u];
+    }
   }
+  if (a.gdst_scale)   // one scale per dispatch row
+    for (int r = blockIdx.x * nthr + tid; r < P; r += (int)stride) a.gdst_scale[r] = a.gsrc_scale[rtok[r]];
 }
 
 __global__ __launch_bounds__(256) void k_route_permute(RouteArgs a) {
