@@ -4,6 +4,7 @@
   window, on and off 32-position block boundaries), many resident experts
   (about one row each), an odd batch split into 3 microbatches, spatial equal
   to temporal;
+* 256 router experts with top-8 picks, temporal and spatial;
 * the first decode step of a single sequence (KV length 1: only the new token
   and the sink), one token through the whole path;
 * the largest microbatch the library takes (tokens * top_k = 4096), sampled;
@@ -62,6 +63,25 @@ def test_ragged_short_lengths_many_experts_odd_batch():
     xs, ts = _run(B, ctx, dw, {"cut": 1, "n_micro": 3, "cu_a": 96})
     assert torch.equal(xt, xs) and torch.equal(tt, ts)
     hz.assert_close_rms(xs.double().cpu().numpy(), x_ref, hz.tol_of(wl), "T3 spatial vs oracle")
+
+
+def test_wide_router_and_eight_picks():
+    """256 router experts (each lane of the top-k wave holds four logits) and
+    top-8 (the combine's general pick loop; at most 4 picks take its batched
+    form), temporal and spatial."""
+    from spatially_pipelined_attention_amd import synth
+    wl = synth.WORKLOADS["gptoss_layer_full"].with_(
+        name="edge_wide", seed=2007, batch=6, n_experts=256, top_k=8, n_resident=16, kv_len_lo=40,
+        kv_len_hi=400, n_layers=2, layer_kinds=("sliding", "full"))
+    toks = list(range(wl.batch))
+    print("\n[edge_wide] E 256, top-8, 16 resident experts", flush=True)
+    B, dw, ctx, x_ref, picks = _setup(wl, toks)
+    x1, t1 = _run(B, ctx, dw, {"cut": 0, "n_micro": 1, "cu_a": 0})
+    hz.assert_close_rms(x1.double().cpu().numpy(), x_ref, hz.tol_of(wl), "E 256, top-8")
+    assert _same_picks(t1.cpu().numpy(), picks)
+    xt, tt = _run(B, ctx, dw, {"cut": 0, "n_micro": 2, "cu_a": 0})
+    xs, ts = _run(B, ctx, dw, {"cut": 0, "n_micro": 2, "cu_a": 128})
+    assert torch.equal(xt, xs) and torch.equal(tt, ts)
 
 
 def test_first_step_of_a_single_sequence():
