@@ -6,7 +6,8 @@ Follows section 3 of the SubGPU Pipelining paper: the segment-to-stage
 binding (equation 1), the augmented task DAG of section 3.2 and its max-plus
 recurrence (equations 4-5), the configuration count of section 3.3
 (equation 7), and the pairwise-line SM-allocation refinement of section 4.2
-(Algorithm 2), each written from the text, not from a listing.
+(Algorithm 2); the refinement follows the section's prose description of
+the method, in this module's own structure.
 """
 from __future__ import annotations
 
@@ -123,56 +124,73 @@ def allocations(n_units: int, n_stages: int, quantum: int, p_min: Optional[int] 
 
 
 # --------------------------------------------------------------------------
-# pairwise-line allocation refinement (section 4.2, Algorithm 2)
+# pairwise-line allocation refinement (section 4.2)
 # --------------------------------------------------------------------------
+def _shift(p: Tuple[int, ...], donor: int, receiver: int, amount: int) -> Tuple[int, ...]:
+    """p with `amount` CUs taken from the donor stage and given to the receiver."""
+    y = list(p)
+    y[donor] -= amount
+    y[receiver] += amount
+    return tuple(y)
+
+
+def _gallop(value_at: Callable[[int], Optional[float]], z: int, best: float) -> Tuple[int, float]:
+    """One-dimensional search over a transfer size z >= 1 (in quanta), starting
+    from a size already known to give `best`. A trial at z + step that
+    improves is taken and the step doubles; any other trial (worse, or
+    illegal: value_at returns None) halves the step; the search ends when the
+    step reaches zero."""
+    step = 1
+    while step:
+        v = value_at(z + step)
+        if v is not None and v < best:
+            z, best, step = z + step, v, step * 2
+        else:
+            step //= 2
+    return z, best
+
+
 def pairwise_line(f: Callable[[Tuple[int, ...]], float], feasible: Callable[[Tuple[int, ...]], bool],
                   p0: Sequence[int], quantum: int, pass_limit: Optional[int] = None):
-    """Refine an allocation by moving quanta between one donor and one receiver stage.
+    """Section 4.2's allocation refinement: local search over CU allocations by
+    pairwise transfers between stages.
 
-    Each pass: among all legal one-quantum moves (donor d -> receiver r) take
-    the one with the smallest objective (ties: lowest (d, r)). Stop if it does
-    not improve on the current value. Otherwise search along that line: keep a
-    step h (starting at 1) and the best move size z; try z + h, doubling h on
-    improvement and halving it (integer) otherwise, until h reaches zero; apply
-    the best z. Repeat until no improving move or the pass limit.
-    Returns (p, f(p), number of objective evaluations).
+    A pass looks at every ordered (donor, receiver) pair whose one-quantum
+    transfer stays legal and ranks the pairs by the objective after that
+    transfer (ties to the lowest pair). If the best of them is no better than
+    the current allocation, the search has converged. Otherwise the pass
+    follows that pair's line: larger transfers along the same direction are
+    tried with a doubling/halving step (_gallop) and the best one is applied.
+    The search stops when no legal pairwise move improves the objective or
+    after pass_limit passes. Returns (p, f(p), objective evaluations).
     """
-    p = tuple(p0)
-    evals = 0
+    n_eval = 0
 
-    def F(x):
-        nonlocal evals
-        evals += 1
+    def cost(x):
+        nonlocal n_eval
+        n_eval += 1
         return f(x)
 
-    def move(x, d, r, z):
-        y = list(x)
-        y[d] -= z * quantum
-        y[r] += z * quantum
-        return tuple(y)
-
-    t = F(p)
-    n = len(p)
+    p = tuple(p0)
+    current = cost(p)
     passes = 0
     while pass_limit is None or passes < pass_limit:
         passes += 1
-        cands = [(d, r) for d in range(n) for r in range(n) if d != r and feasible(move(p, d, r, 1))]
-        if not cands:
-            return p, t, evals
-        vals = [(F(move(p, d, r, 1)), d, r) for d, r in cands]
-        best = min(vals)
-        t_line, d, r = best
-        if t_line >= t:
-            return p, t, evals
-        z, h = 1, 1
-        while h > 0:
-            zz = z + h
-            cand = move(p, d, r, zz)
-            if feasible(cand):
-                v = F(cand)
-                if v < t_line:
-                    z, t_line, h = zz, v, 2 * h
-                    continue
-            h //= 2
-        p, t = move(p, d, r, z), t_line
-    return p, t, evals
+        probes = []
+        for d in range(len(p)):
+            for r in range(len(p)):
+                if d != r and feasible(_shift(p, d, r, quantum)):
+                    probes.append((cost(_shift(p, d, r, quantum)), d, r))
+        if not probes:
+            break
+        v1, d, r = min(probes)
+        if v1 >= current:
+            break
+
+        def along(z, _d=d, _r=r):
+            cand = _shift(p, _d, _r, z * quantum)
+            return cost(cand) if feasible(cand) else None
+
+        z, current = _gallop(along, 1, v1)
+        p = _shift(p, d, r, z * quantum)
+    return p, current, n_eval

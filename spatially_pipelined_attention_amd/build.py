@@ -8,6 +8,7 @@ Run `python -m spatially_pipelined_attention_amd.build`.
 """
 from __future__ import annotations
 
+import concurrent.futures
 import os
 import shutil
 import subprocess
@@ -23,9 +24,11 @@ LIB = os.path.join(PKG, "libspa.so")
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # Packed fp32 ALU ops are kept out of generated code.
-HIP_FLAGS = ["-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC", "-shared",
-             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-             "-Wno-unused-result", "-munsafe-fp-atomics"]
+HIP_CFLAGS = ["-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC",
+              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+              "-Wno-unused-result", "-munsafe-fp-atomics"]
+HIP_FLAGS = HIP_CFLAGS + ["-shared"]
+OBJ = os.path.join(ROOT, "_build")
 
 
 def _run(cmd):
@@ -56,11 +59,19 @@ def product_sources():
 
 
 def build_product():
+    """Every translation unit compiled on its own (in parallel), then linked."""
     srcs = product_sources()
     if not srcs:
         return
-    _run([HIPCC] + HIP_FLAGS + ["-I", INCLUDE, "-I", CSRC] + srcs +
-         ["-o", _atomic_out(LIB), "-lpthread"])
+    os.makedirs(OBJ, exist_ok=True)
+    objs = [os.path.join(OBJ, os.path.basename(s) + ".o") for s in srcs]
+    jobs = max(1, min(len(srcs), os.cpu_count() or 1, 16))
+    with concurrent.futures.ThreadPoolExecutor(jobs) as ex:
+        futs = [ex.submit(_run, [HIPCC] + HIP_CFLAGS + ["-I", INCLUDE, "-I", CSRC, "-c", s, "-o", o])
+                for s, o in zip(srcs, objs)]
+        for f in futs:
+            f.result()
+    _run([HIPCC] + HIP_FLAGS + objs + ["-o", _atomic_out(LIB), "-lpthread"])
     os.replace(_atomic_out(LIB), LIB)
 
 

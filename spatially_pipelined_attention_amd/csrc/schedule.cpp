@@ -25,6 +25,81 @@ static int64_t binom(int64_t n, int64_t k) {
   return (int64_t)r;
 }
 
+// Section 4.2's allocation refinement: a local search over CU allocations in
+// which each pass picks the best one-quantum transfer between an ordered
+// (donor, receiver) pair of stages, and, if it improves on the current
+// allocation, follows that direction with a doubling/halving step to the best
+// transfer size. It ends when no legal pairwise move improves, or after the
+// pass limit.
+namespace {
+
+struct Probe {
+  int donor = -1, receiver = -1;
+  double value = 0.0;
+};
+
+struct AllocSearch {
+  int n, total, quantum, p_min;
+  spa_objective_fn fn;
+  void* user;
+  int evals = 0;
+  double last_line_value = 0.0;
+
+  bool legal(const std::vector<int32_t>& x) const {
+    long long sum = 0;
+    for (int32_t v : x) {
+      if (v < p_min || v < quantum || v % quantum) return false;
+      sum += v;
+    }
+    return sum == total;
+  }
+  double cost(const std::vector<int32_t>& x) {
+    ++evals;
+    return fn(x.data(), n, user);
+  }
+  std::vector<int32_t> shifted(const std::vector<int32_t>& x, int d, int r, int quanta) const {
+    std::vector<int32_t> y = x;
+    y[d] -= quanta * quantum;
+    y[r] += quanta * quantum;
+    return y;
+  }
+  // the best legal one-quantum transfer (ties to the lowest donor, then receiver)
+  Probe best_probe(const std::vector<int32_t>& x) {
+    Probe b;
+    for (int d = 0; d < n; ++d)
+      for (int r = 0; r < n; ++r) {
+        if (d == r) continue;
+        const std::vector<int32_t> c = shifted(x, d, r, 1);
+        if (!legal(c)) continue;
+        const double v = cost(c);
+        if (b.donor < 0 || v < b.value) b = Probe{d, r, v};
+      }
+    return b;
+  }
+  // transfer size along the probe's direction: a trial at z + step that
+  // improves is taken and the step doubles; otherwise the step halves
+  int gallop(const std::vector<int32_t>& x, const Probe& pr) {
+    int z = 1;
+    double v_best = pr.value;
+    for (int step = 1; step > 0;) {
+      const std::vector<int32_t> c = shifted(x, pr.donor, pr.receiver, z + step);
+      double v = 0.0;
+      const bool better = legal(c) && (v = cost(c)) < v_best;
+      if (better) {
+        z += step;
+        v_best = v;
+        step *= 2;
+      } else {
+        step /= 2;
+      }
+    }
+    last_line_value = v_best;
+    return z;
+  }
+};
+
+}  // namespace
+
 extern "C" {
 
 int32_t spa_sched_binding(int32_t k, int32_t K, int32_t w) { return (w == 1 && k == K) ? 1 : k; }
@@ -73,68 +148,20 @@ spa_status spa_refine_allocation(int32_t n_stages, int32_t total, int32_t quantu
                                  spa_objective_fn objective, void* user, int32_t pass_limit, double* best,
                                  int32_t* n_evals) {
   if (n_stages < 1 || total < 1 || quantum < 1 || !p || !objective) return fail(SPA_EINVAL, "bad argument");
-  auto feasible = [&](const std::vector<int32_t>& x) {
-    long long s = 0;
-    for (int32_t v : x) {
-      if (v < p_min || v < quantum || v % quantum) return false;
-      s += v;
-    }
-    return s == total;
-  };
+  AllocSearch S{n_stages, total, quantum, p_min, objective, user};
   std::vector<int32_t> cur(p, p + n_stages);
-  if (!feasible(cur)) return fail(SPA_EINVAL, "initial allocation is infeasible");
-  int evals = 0;
-  auto F = [&](const std::vector<int32_t>& x) {
-    ++evals;
-    return objective(x.data(), n_stages, user);
-  };
-  auto move = [&](const std::vector<int32_t>& x, int d, int r, int z) {
-    std::vector<int32_t> y = x;
-    y[d] -= z * quantum;
-    y[r] += z * quantum;
-    return y;
-  };
-  double t = F(cur);
+  if (!S.legal(cur)) return fail(SPA_EINVAL, "initial allocation is infeasible");
+  double value = S.cost(cur);
   for (int pass = 0; pass_limit <= 0 || pass < pass_limit; ++pass) {
-    // best legal one-quantum transfer (ties: lowest donor, then receiver)
-    bool any = false;
-    double t_line = 0.0;
-    int bd = -1, br = -1;
-    for (int d = 0; d < n_stages; ++d)
-      for (int r = 0; r < n_stages; ++r) {
-        if (d == r) continue;
-        std::vector<int32_t> c = move(cur, d, r, 1);
-        if (!feasible(c)) continue;
-        double v = F(c);
-        if (!any || v < t_line) {
-          any = true;
-          t_line = v;
-          bd = d;
-          br = r;
-        }
-      }
-    if (!any || t_line >= t) break;
-    // line search along donor -> receiver: grow the step on improvement, halve otherwise
-    int z = 1, h = 1;
-    while (h > 0) {
-      std::vector<int32_t> c = move(cur, bd, br, z + h);
-      if (feasible(c)) {
-        double v = F(c);
-        if (v < t_line) {
-          z += h;
-          t_line = v;
-          h *= 2;
-          continue;
-        }
-      }
-      h /= 2;
-    }
-    cur = move(cur, bd, br, z);
-    t = t_line;
+    const Probe pr = S.best_probe(cur);
+    if (pr.donor < 0 || !(pr.value < value)) break;   // converged: no improving pairwise move
+    const int z = S.gallop(cur, pr);
+    cur = S.shifted(cur, pr.donor, pr.receiver, z);
+    value = S.last_line_value;
   }
   memcpy(p, cur.data(), sizeof(int32_t) * n_stages);
-  if (best) *best = t;
-  if (n_evals) *n_evals = evals;
+  if (best) *best = value;
+  if (n_evals) *n_evals = S.evals;
   return SPA_OK;
 }
 

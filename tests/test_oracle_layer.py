@@ -219,17 +219,95 @@ def test_zero_gate_gives_identity_moe_and_doubling_down_doubles_term():
 
 
 # ----------------------------------------------------------------------------- whole layer
-def brute_layer(dims, kind, x, dense, experts, L, Kh, Vh):
+# Pure-Python roundings of the stored formats, written from the format
+# definitions (not from oracle.numerics): a value's significand is taken from
+# math.frexp and rounded with Python's round(), which breaks ties to even.
+def py_bf16(v):
+    """bfloat16: 8 significant bits, fp32's exponent range (normal inputs)."""
+    if v == 0.0:
+        return 0.0
+    m, e = math.frexp(v)                 # v = m * 2^e, 0.5 <= |m| < 1
+    return round(m * 256.0) * 2.0 ** (e - 8)
+
+
+def py_e4m3(v):
+    """OCP E4M3 (|v| <= 448): 4 significant bits for normals (leading-bit
+    exponent >= -6), a fixed quantum of 2^-9 below that."""
+    if v == 0.0:
+        return 0.0
+    _, e = math.frexp(abs(v))
+    lead = max(e - 1, -6)                # exponent of the leading bit, clamped at the subnormal range
+    q = 2.0 ** (lead - 3)
+    return math.copysign(round(abs(v) / q) * q, v)
+
+
+def py_pow2_scale(amax):
+    """Smallest power of two s with amax <= 448 s (1 for an all-zero row)."""
+    if amax == 0.0:
+        return 1.0
+    s = 1.0
+    while amax > 448.0 * s:
+        s *= 2.0
+    while amax <= 448.0 * s / 2.0:
+        s /= 2.0
+    return s
+
+
+def py_e4m3_row(row):
+    """A row stored as E4M3 codes times one power-of-two scale."""
+    s = py_pow2_scale(max(abs(v) for v in row))
+    return [py_e4m3(v / s) * s for v in row]
+
+
+def py_e4m3_decode(code):
+    """Value of an OCP E4M3 byte: sign, 4 exponent bits (bias 7), 3 mantissa bits."""
+    sign = -1.0 if code & 0x80 else 1.0
+    ex, man = (code >> 3) & 15, code & 7
+    if ex == 0:
+        return sign * man * 2.0 ** -9
+    return sign * (1.0 + man / 8.0) * 2.0 ** (ex - 7)
+
+
+IDENT = lambda row: list(row)
+QUANT = {
+    "pure": {"act": IDENT, "kv": IDENT, "ex": IDENT},
+    "bf16": {"act": lambda r: [py_bf16(v) for v in r], "kv": lambda r: [py_bf16(v) for v in r],
+             "ex": lambda r: [py_bf16(v) for v in r]},
+    "e4m3": {"act": lambda r: [py_bf16(v) for v in r], "kv": lambda r: [py_bf16(v) for v in r],
+             "ex": py_e4m3_row},
+}
+NUMERICS = {"pure": ol.Numerics(), "bf16": ol.Numerics("bf16", "bf16", "bf16"),
+            "e4m3": ol.Numerics("bf16", "bf16", "e4m3")}
+
+
+def brute_expert(ew, I, H):
+    """An expert's (wgu, wd) as nested lists: given values, or E4M3 codes times
+    the scale of their output channel (the matrix row)."""
+    if "wgu_codes" in ew:
+        return ([[py_e4m3_decode(int(ew["wgu_codes"][j][i])) * float(ew["wgu_scale"][j]) for i in range(H)]
+                 for j in range(2 * I)],
+                [[py_e4m3_decode(int(ew["wd_codes"][i][j])) * float(ew["wd_scale"][i]) for j in range(I)]
+                 for i in range(H)])
+    return [list(map(float, r)) for r in ew["wgu"]], [list(map(float, r)) for r in ew["wd"]]
+
+
+def brute_layer(dims, kind, x, dense, experts, L, Kh, Vh, quant="pure"):
     """Pure-Python loops over every index of the layer (float64). With
     dims.rope_theta > 0 the q heads and the new k heads are turned pair by
-    pair at position L - 1 (RoFormer's rotary embedding)."""
+    pair at position L - 1 (RoFormer's rotary embedding). `quant` names the
+    stored formats: "pure" (none), "bf16" (xn, q, the new K/V, o, the expert
+    input hn and z rounded to bf16) or "e4m3" (as bf16, but hn and z stored as
+    per-row power-of-two-scaled E4M3; experts given as E4M3 codes and
+    per-output-channel scales)."""
+    qa, qk, qe = QUANT[quant]["act"], QUANT[quant]["kv"], QUANT[quant]["ex"]
     H, Hq, Hkv, D, I = dims.hidden, dims.n_q_heads, dims.n_kv_heads, dims.head_dim, dims.inter
     G = Hq // Hkv
+    ex_w = {e: brute_expert(experts[e], I, H) for e in experts}
     out = []
     for b in range(len(x)):
         xb = [float(v) for v in x[b]]
         ms = sum(v * v for v in xb) / H
-        xn = [xb[i] * dense["gamma1"][i] / math.sqrt(ms + dims.eps) for i in range(H)]
+        xn = qa([xb[i] * dense["gamma1"][i] / math.sqrt(ms + dims.eps) for i in range(H)])
         qkv = [sum(xn[i] * dense["wqkv"][r][i] for i in range(H)) for r in range((Hq + 2 * Hkv) * D)]
         if dims.rope_theta > 0:
             for head in range(Hq + Hkv):          # q heads, then k heads
@@ -238,6 +316,7 @@ def brute_layer(dims, kind, x, dense, experts, L, Kh, Vh):
                     u, v = qkv[head * D + 2 * i], qkv[head * D + 2 * i + 1]
                     qkv[head * D + 2 * i] = u * math.cos(ang) - v * math.sin(ang)
                     qkv[head * D + 2 * i + 1] = u * math.sin(ang) + v * math.cos(ang)
+        qkv = qa(qkv[:Hq * D]) + qk(qkv[Hq * D:])   # q as the attention input, new K/V as stored
         lo = 0 if kind == "full" else max(0, L[b] - dims.window)
         att = []
         for hq in range(Hq):
@@ -256,6 +335,7 @@ def brute_layer(dims, kind, x, dense, experts, L, Kh, Vh):
             ex = [math.exp(s - M) for s in sc]
             Z = math.exp(dense["sinks"][hq] - M) + sum(ex)
             att += [sum(ex[j] * vals[j][d] for j in range(len(vals))) / Z for d in range(D)]
+        att = qa(att)
         hb = [xb[i] + sum(att[j] * dense["wo"][i][j] for j in range(Hq * D)) for i in range(H)]
         ms2 = sum(v * v for v in hb) / H
         hn = [hb[i] * dense["gamma2"][i] / math.sqrt(ms2 + dims.eps) for i in range(H)]
@@ -263,15 +343,16 @@ def brute_layer(dims, kind, x, dense, experts, L, Kh, Vh):
         ranked = sorted(range(dims.n_experts), key=lambda e: (-np.float32(logits[e]), e))[:dims.top_k]
         mx = max(logits[t] for t in ranked)
         wsum = sum(math.exp(logits[t] - mx) for t in ranked)
+        hx = qe(hn)                               # the experts' input row
         res = list(hb)
         for t in ranked:
-            e = t % dims.n_resident
-            wgu, wd = experts[e]["wgu"], experts[e]["wd"]
+            wgu, wd = ex_w[t % dims.n_resident]
             z = []
             for j in range(I):
-                gte = sum(hn[i] * wgu[j][i] for i in range(H))
-                up = sum(hn[i] * wgu[I + j][i] for i in range(H))
+                gte = sum(hx[i] * wgu[j][i] for i in range(H))
+                up = sum(hx[i] * wgu[I + j][i] for i in range(H))
                 z.append(gte / (1 + math.exp(-gte)) * up)
+            z = qe(z)
             wt = math.exp(logits[t] - mx) / wsum
             for i in range(H):
                 res[i] += wt * sum(z[j] * wd[i][j] for j in range(I))
@@ -291,6 +372,112 @@ def test_layer_matches_brute_force(kind, E_res, theta):
     rec = ol.layer_forward(dims, ol.Numerics(), kind, x, dense, experts.__getitem__, L, hist)
     np.testing.assert_allclose(rec.x_next, brute_layer(dims, kind, x, dense, experts, L, Kh, Vh),
                                rtol=1e-11, atol=1e-11)
+
+
+def _e4m3_table():
+    """E4M3-exact value -> code, for every non-NaN code (pure-Python decode)."""
+    return {py_e4m3_decode(c): c for c in range(256) if (c & 0x7F) != 0x7F}
+
+
+def _to_e4m3_expert(ew, rng):
+    """Quantise an expert's float matrices per output channel (row): scale =
+    a random positive value near amax / 448, codes of the nearest E4M3 value
+    of w / scale (saturated). Distinct scales per row, so a scale applied
+    along the wrong axis changes the result."""
+    table = _e4m3_table()
+    out = {}
+    for name in ("wgu", "wd"):
+        w = np.asarray(ew[name], np.float64)
+        sc = np.max(np.abs(w), axis=1) / 448.0 * rng.uniform(0.6, 1.0, w.shape[0])
+        codes = np.empty(w.shape, np.uint8)
+        for r in range(w.shape[0]):
+            for c in range(w.shape[1]):
+                v = max(-448.0, min(448.0, w[r, c] / sc[r]))
+                codes[r, c] = table[py_e4m3(v)]
+        out[name + "_codes"] = codes
+        out[name + "_scale"] = sc.astype(np.float32)
+    return out
+
+
+@pytest.mark.parametrize("quant,kind,E_res,theta", [("bf16", "full", 8, 0.0), ("bf16", "sliding", 3, 500.0),
+                                                     ("e4m3", "full", 8, 0.0), ("e4m3", "sliding", 3, 10000.0)])
+def test_quantised_layer_matches_brute_force(quant, kind, E_res, theta):
+    """The mirrored rounding points (bf16 xn, q, new K/V, o, hn, z; or E4M3
+    hn and z with power-of-two row scales and E4M3 expert weights with
+    per-channel scales) against the pure-Python loops with their own
+    roundings."""
+    dims = dataclasses.replace(_tiny(E_res=E_res), rope_theta=theta)
+    rng = np.random.default_rng(21)
+    dense, experts = _params(dims, rng)
+    if quant == "e4m3":
+        experts = {e: _to_e4m3_expert(ew, rng) for e, ew in experts.items()}
+    B, L = 3, [9, 4, 6]
+    Kh, Vh, hist = _history(dims, rng, B, 10)
+    x = rnd(rng, B, dims.hidden)
+    rec = ol.layer_forward(dims, NUMERICS[quant], kind, x, dense, experts.__getitem__, L, hist)
+    ref = brute_layer(dims, kind, x, dense, experts, L, Kh, Vh, quant)
+    np.testing.assert_allclose(rec.x_next, ref, rtol=1e-11, atol=1e-11)
+    # the rounding points matter at this size: without them the layer is measurably different
+    pure = brute_layer(dims, kind, x, dense, experts, L, Kh, Vh, "pure")
+    assert np.max(np.abs(pure - ref)) > 1e-6 * np.max(np.abs(ref))
+
+
+def test_e4m3_expert_dequantisation_uses_the_output_channel_scale():
+    """wgu [2I][H] and wd [H][I] (non-square): element (n, k) is the code's
+    value times the scale of output channel n."""
+    rng = np.random.default_rng(22)
+    I, H = 5, 7
+    ew = {"wgu_codes": rng.integers(0, 0x7F, (2 * I, H)).astype(np.uint8),
+          "wgu_scale": rng.uniform(0.5, 4.0, 2 * I).astype(np.float32),
+          "wd_codes": rng.integers(0x80, 0xFF, (H, I)).astype(np.uint8),
+          "wd_scale": rng.uniform(0.5, 4.0, H).astype(np.float32)}
+    wgu, wd = ol.expert_matrices(ew)
+    bgu, bd = brute_expert(ew, I, H)
+    np.testing.assert_array_equal(wgu, np.array(bgu))
+    np.testing.assert_array_equal(wd, np.array(bd))
+
+
+def test_e4m3_scale_one_equals_plain_weights_and_pow2_down_scale_is_exact():
+    """Codes with scale 1 are the code values themselves: the layer equals the
+    same layer given those values as plain weights, bit for bit. Doubling every
+    down-projection scale doubles the MoE term exactly (z does not depend on it)."""
+    dims = _tiny()
+    rng = np.random.default_rng(23)
+    dense, experts = _params(dims, rng)
+    q = {e: _to_e4m3_expert({k: v / 448.0 for k, v in ew.items()}, rng) for e, ew in experts.items()}
+    one = {e: dict(ew, wgu_scale=np.ones_like(ew["wgu_scale"]), wd_scale=np.ones_like(ew["wd_scale"]))
+           for e, ew in q.items()}
+    plain = {e: {"wgu": np.array([[py_e4m3_decode(int(c)) for c in r] for r in ew["wgu_codes"]]),
+                 "wd": np.array([[py_e4m3_decode(int(c)) for c in r] for r in ew["wd_codes"]])}
+             for e, ew in q.items()}
+    dbl = {e: dict(ew, wd_scale=2 * ew["wd_scale"]) for e, ew in q.items()}
+    _, _, hist = _history(dims, rng, 3, 10)
+    x = rnd(rng, 3, dims.hidden)
+    run = lambda ex: ol.layer_forward(dims, NUMERICS["e4m3"], "full", x, dense, ex.__getitem__, [9, 4, 6], hist)
+    a, b = run(one), run(plain)
+    np.testing.assert_array_equal(a.x_next, b.x_next)
+    c, d = run(q), run(dbl)
+    np.testing.assert_array_equal(d.y, 2 * c.y)
+    np.testing.assert_array_equal(d.weights, c.weights)
+
+
+def test_oracle_roundings_match_pure_python():
+    """oracle.numerics against the pure-Python roundings above, ties included."""
+    from oracle.numerics import quant_rows_pow2_e4m3, round_e4m3
+    rng = np.random.default_rng(24)
+    v = np.concatenate([rng.standard_normal(3000) * 10.0 ** rng.uniform(-6, 2, 3000),
+                        (np.arange(1, 600) + 0.5) * 2.0 ** -16,          # halfway points (bf16 ties)
+                        [1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, -(1.0 + 2.0 ** -8)]])
+    np.testing.assert_array_equal(round_bf16(v), [py_bf16(float(t)) for t in v])
+    w = np.concatenate([rng.uniform(-448, 448, 2000), rng.standard_normal(2000) * 2.0 ** -8,
+                        (np.arange(1, 64) + 0.5) * 2.0 ** -9, [1.0625, 1.1875, 3.0 * 2 ** -10, 416.0 + 16.0]])
+    np.testing.assert_array_equal(round_e4m3(w), [py_e4m3(float(t)) for t in w])
+    rows = rng.standard_normal((40, 33)) * 10.0 ** rng.uniform(-5, 5, (40, 1))
+    rows[3] = 0.0
+    rows[4, 0] = 448.0 * 2.0 ** -7        # amax exactly at a power-of-two boundary
+    got, sc = quant_rows_pow2_e4m3(rows)
+    np.testing.assert_array_equal(got, [py_e4m3_row(list(r)) for r in rows])
+    np.testing.assert_array_equal(sc, [py_pow2_scale(float(np.max(np.abs(r)))) for r in rows])
 
 
 def test_sliding_with_wide_window_equals_full():
