@@ -168,6 +168,9 @@ def main():
                          "events around each launch (these also hold the start marker's dispatch latency)")
     ap.add_argument("--virtual-comm", default="", metavar="LATENCY_US,GBPS",
                     help="add one rank's communication endpoints to every layer (e.g. 3,900)")
+    ap.add_argument("--handoff", choices=["values", "events"], default="values",
+                    help="stage hand-offs of the spatial pipeline: stream value waits (the default) or events "
+                         "(for per-dispatch counter collection, which can hold a value wait's writer back)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="after timing, copy BYTES device bytes three times (a known-size kernel for counter scaling)")
     args = ap.parse_args()
@@ -210,7 +213,8 @@ def main():
     stream = torch.cuda.current_stream()
 
     def make_pipe(cut, n_micro, cu_a, cu_s=None):
-        return Pipeline(ctx, dw.m, {"cut": cut, "n_micro": n_micro, "cu_a": cu_a or 0, "cu_a_sliding": cu_s})
+        return Pipeline(ctx, dw.m, {"cut": cut, "n_micro": n_micro, "cu_a": cu_a or 0, "cu_a_sliding": cu_s,
+                                    "handoff": 1 if args.handoff == "events" else 0})
 
     results = {}
 

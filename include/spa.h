@@ -234,7 +234,10 @@ spa_status spa_qkv_append(spa_ctx* ctx, const spa_model_desc* m, const spa_layer
 
 /* Figure 3 "FMHA" (section 5.1: sliding or full): grouped-query decode
  * attention with sinks over the cached window; q [n_tok][Hq*D] and o_out
- * [n_tok][Hq*D] in kv_dtype. Split-KV over 512-position chunks. */
+ * [n_tok][Hq*D] in kv_dtype. Split-KV: a window is cut into equal chunks of
+ * at most 4096 .. 512 positions (the largest cap that still gives two
+ * workgroups per CU at the batch's longest sequence), whose partial softmax
+ * states are merged with the sink in chunk order. */
 spa_status spa_decode_attn(spa_ctx* ctx, const spa_model_desc* m, const spa_layer* l, const spa_batch* b,
                            int32_t tok0, int32_t n_tok, const void* q, void* o_out, void* ws, size_t ws_bytes,
                            void* stream);
@@ -327,10 +330,19 @@ spa_status spa_pool_destroy(spa_pool* p);
  * A(l, mu) waits for B(l-1, mu) and B(l, mu) for A(l, mu): the finishing
  * stream writes a per-microbatch counter in device memory and the other
  * stream waits for it (stream value write/wait; events where the runtime
- * lacks them). */
+ * lacks them, or when `handoff` asks for them). */
 typedef struct spa_pipeline_cfg {
   int32_t cut;        /* 0, 1 or 2 (Macro) */
   int32_t n_micro;    /* m, divides the batch */
+  /* Stage hand-off mechanism. 0 (the zero-initialised default): stream value
+   * write/wait on device counters where the runtime supports them. 1:
+   * event record/wait always. The runtime executes a value wait as a small
+   * kernel that polls memory; a tool that runs one dispatch at a time (a
+   * per-dispatch hardware-counter collection) can then leave that poller
+   * waiting for a write whose dispatch it holds back. Event waits are
+   * resolved by the command processor and dispatch nothing, so use 1 under
+   * such tools. Results are identical either way. */
+  int32_t handoff;
 } spa_pipeline_cfg;
 
 spa_status spa_pipeline_create(spa_ctx* ctx, const spa_model_desc* m, const spa_pipeline_cfg* cfg, spa_pool* stage_a,

@@ -175,6 +175,7 @@ static spa_status create_impl(spa_ctx* ctx, const spa_model_desc* m, const spa_p
   if (rc) return rc;
   if (cfg->cut < 0 || cfg->cut > 2) return fail(SPA_EINVAL, "cut must be 0, 1 or 2");
   if (cfg->n_micro < 1) return fail(SPA_EINVAL, "n_micro must be >= 1");
+  if (cfg->handoff != 0 && cfg->handoff != 1) return fail(SPA_EINVAL, "handoff must be 0 (value waits) or 1 (events)");
   const bool any = a_full || b_full || a_slide || b_slide;
   const bool all = a_full && b_full && a_slide && b_slide;
   if (any && !all) return fail(SPA_EINVAL, "give both pools of every layer kind, or none");
@@ -204,7 +205,7 @@ static spa_status create_impl(spa_ctx* ctx, const spa_model_desc* m, const spa_p
     e = hipMalloc(&p->flags, sizeof(uint64_t) * 2 * cfg->n_micro);
     if (e == hipSuccess) e = hipMemset(p->flags, 0, sizeof(uint64_t) * 2 * cfg->n_micro);
     if (e == hipSuccess) e = hipDeviceSynchronize();
-    if (e == hipSuccess) {
+    if (e == hipSuccess && cfg->handoff == 0) {
       // use stream value writes/waits when the runtime supports them on this memory
       hipError_t t = hipStreamWriteValue64(a_full->stream, p->flags, 0, 0);
       if (t == hipSuccess) t = hipStreamWaitValue64(b_full->stream, p->flags, 0, hipStreamWaitValueGte, ~0ull);

@@ -13,6 +13,11 @@
             --kernel PREFIX --copy-bytes N --command CMD
         the same per launch shape of every kernel whose name starts with PREFIX, as a table
 
+    python -m spatially_pipelined_attention_amd.profiling iter-traffic --fetch CSV --write CSV \\
+            --copy-bytes N --iterations K --command CMD
+        HBM-side bytes of whole iterations: every dispatch of the two counter runs summed per
+        kernel name, scaled as above, divided by the K iterations the run executed
+
     python -m spatially_pipelined_attention_amd.profiling mfma CSV --kernel PREFIX --dtype bf16|f8 \\
             --command CMD
         MFMA work and utilisation per launch of the kernels whose name starts with PREFIX, from a
@@ -129,6 +134,40 @@ def cmd_traffic(a):
         print(f"- {k}: {v}")
 
 
+def cmd_iter_traffic(a):
+    fetch, write = _per_dispatch(a.fetch), _per_dispatch(a.write)
+    f_scale = a.copy_bytes / (_copy_kib(fetch) * 1024.0)
+    w_scale = a.copy_bytes / (_copy_kib(write) * 1024.0)
+
+    def sums(disp, sc):
+        g = defaultdict(lambda: [0, 0.0])
+        for d in disp:
+            name = d["name"].split("(")[0].replace("void ", "")
+            if "copy" in name.lower() or name.startswith("__amd"):
+                continue
+            g[name][0] += 1
+            g[name][1] += d["kib"] * 1024.0 * sc
+        return g
+
+    gf, gw = sums(fetch, f_scale), sums(write, w_scale)
+    K = a.iterations
+    tf = sum(v[1] for v in gf.values()) / K
+    tw = sum(v[1] for v in gw.values()) / K
+    print(f"# HBM-side traffic per iteration\n\ncommand: `{a.command}`\n")
+    print(f"Counter scale from a plain copy of {a.copy_bytes} bytes: fetch x{f_scale:.4f}, write x{w_scale:.4f}. "
+          f"Every dispatch of the run except the copies and runtime helpers, divided by {K} iterations.\n")
+    print(f"- fetch_GB_per_iter: {tf / 1e9:.3f}")
+    print(f"- write_GB_per_iter: {tw / 1e9:.3f}")
+    print(f"- traffic_GB_per_iter: {(tf + tw) / 1e9:.3f}")
+    for kv in a.set or []:
+        k, v = kv.split("=", 1)
+        print(f"- {k}: {v}")
+    print("\n| kernel | launches per iteration | fetch MB per iteration | write MB per iteration |")
+    print("|---|---:|---:|---:|")
+    for name in sorted(gf, key=lambda n: -gf[n][1]):
+        print(f"| `{name}` | {gf[name][0] / K:.0f} | {gf[name][1] / K / 1e6:.1f} | {gw.get(name, [0, 0.0])[1] / K / 1e6:.1f} |")
+
+
 def cmd_traffic_table(a):
     fetch, write = _per_dispatch(a.fetch), _per_dispatch(a.write)
     f_scale = a.copy_bytes / (_copy_kib(fetch) * 1024.0)
@@ -203,6 +242,13 @@ def main(argv=None):
     t.add_argument("--command", required=True)
     t.add_argument("--sources", nargs="*")
     t.add_argument("--set", action="append", metavar="KEY=VALUE", help="extra key recorded in the summary")
+    it = sub.add_parser("iter-traffic")
+    it.add_argument("--fetch", required=True)
+    it.add_argument("--write", required=True)
+    it.add_argument("--copy-bytes", type=int, required=True)
+    it.add_argument("--iterations", type=int, required=True)
+    it.add_argument("--command", required=True)
+    it.add_argument("--set", action="append")
     tt = sub.add_parser("traffic-table")
     tt.add_argument("--fetch", required=True)
     tt.add_argument("--write", required=True)
@@ -215,7 +261,8 @@ def main(argv=None):
     mf.add_argument("--dtype", choices=["bf16", "f8"], required=True)
     mf.add_argument("--command", required=True)
     a = ap.parse_args(argv)
-    {"stats": cmd_stats, "traffic": cmd_traffic, "traffic-table": cmd_traffic_table, "mfma": cmd_mfma}[a.cmd](a)
+    {"stats": cmd_stats, "traffic": cmd_traffic, "iter-traffic": cmd_iter_traffic, "traffic-table": cmd_traffic_table,
+     "mfma": cmd_mfma}[a.cmd](a)
 
 
 if __name__ == "__main__":

@@ -39,7 +39,7 @@ def layer_params(wl: synth.Workload, l: int):
 
 
 def run_oracle(wl: synth.Workload, tokens: Sequence[int], resample: Optional[Dict[int, int]] = None,
-               n_layers: Optional[int] = None, keep_records: bool = False):
+               n_layers: Optional[int] = None, keep_records: bool = False, progress: bool = True):
     """Oracle decode iteration for the given sequences (any subset: tokens are independent)."""
     tokens = list(tokens)
     L = synth.kv_lengths(wl)[tokens]
@@ -49,8 +49,12 @@ def run_oracle(wl: synth.Workload, tokens: Sequence[int], resample: Optional[Dic
     def history(l, bi, lo, hi):
         return synth.kv_history(wl, l, tokens[bi], lo, hi)
 
-    return ol.iteration_forward(dims(wl), numerics(wl), kinds, x, lambda l: layer_params(wl, l), L, history,
-                                keep_records)
+    def params(l):
+        if progress:
+            print(f"  oracle layer {l} ({len(tokens)} sequences)", flush=True)
+        return layer_params(wl, l)
+
+    return ol.iteration_forward(dims(wl), numerics(wl), kinds, x, params, L, history, keep_records)
 
 
 def resample_for_margins(wl: synth.Workload, tokens: Sequence[int], max_rounds: int = 12,

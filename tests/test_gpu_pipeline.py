@@ -33,10 +33,11 @@ def env():
     return dict(B=B, wl=wl, dw=dw, ctx=ctx, n_cus=B.spa_device_cus(ctx))
 
 
-def _run(env, cut, n_micro, cu_a, cu_s=None):
+def _run(env, cut, n_micro, cu_a, cu_s=None, handoff=0):
     from spatially_pipelined_attention_amd.workload import Pipeline
     B, dw, ctx = env["B"], env["dw"], env["ctx"]
-    pipe = Pipeline(ctx, dw.m, {"cut": cut, "n_micro": n_micro, "cu_a": cu_a or 0, "cu_a_sliding": cu_s})
+    pipe = Pipeline(ctx, dw.m, {"cut": cut, "n_micro": n_micro, "cu_a": cu_a or 0, "cu_a_sliding": cu_s,
+                                "handoff": handoff})
     ws = dw.workspace(n_micro=n_micro)
     dw.reset_x()
     dw.topk.zero_()
@@ -99,6 +100,18 @@ def test_spatial_equals_temporal_bitwise(env, cut, n_micro, cu_a, cu_s):
     assert torch.equal(tt, ts)
     np.testing.assert_array_equal(kt, ks)
     np.testing.assert_array_equal(vt, vs)
+
+
+@pytest.mark.parametrize("cut", [0, 2])
+def test_event_handoffs_give_the_same_bits(env, cut):
+    """Stage hand-offs by event record/wait (the mechanism for per-dispatch
+    counter collection) instead of stream value waits: same bits."""
+    print(f"[case] events, cut={cut}", flush=True)
+    xt, tt, kt, vt = _run(env, cut, 2, None)
+    xe, te, ke, ve = _run(env, cut, 2, 128, handoff=1)
+    assert torch.equal(xt, xe) and torch.equal(tt, te)
+    np.testing.assert_array_equal(kt, ke)
+    np.testing.assert_array_equal(vt, ve)
 
 
 def test_repeat_runs_are_bitwise_identical(env):
