@@ -242,6 +242,27 @@ spa_status spa_decode_attn(spa_ctx* ctx, const spa_model_desc* m, const spa_laye
                            int32_t tok0, int32_t n_tok, const void* q, void* o_out, void* ws, size_t ws_bytes,
                            void* stream);
 
+/* spa_decode_attn for callers that cannot allocate device memory (code
+ * under stream capture, tight serving loops, harnesses that forbid
+ * allocation): the same operator, kernels and results, with no workspace.
+ * Its scratch (the per-chunk softmax partials) lives in a fixed array of
+ * the library, one per GPU, held until the process ends: at most 16 MiB of
+ * partials, n_tok * Hkv * chunks * (Hq/Hkv) * (D + 2) * 4 bytes, where
+ * chunks = ceil(max_kv_len / chunk) for full layers (the chunk is 4096 ..
+ * 512 positions, chosen from the shapes as in spa_decode_attn) and
+ * ceil(window / 512) for sliding layers. A call that needs more returns
+ * SPA_EWORKSPACE and enqueues nothing. The call allocates nothing.
+ * err_out: optional device int32, zeroed by the caller; bit 0 is set when a
+ * kv_len lies outside its cache (those rows are then left unwritten). With
+ * err_out NULL the bit goes to the array's own word, which the caller
+ * cannot read. Every call on one GPU shares that GPU's array and the array
+ * keeps the last call's contents: calls that overlap in time on one GPU
+ * (different streams, or different host threads) race and must be
+ * serialised by the caller. */
+spa_status spa_decode_attn_noalloc(spa_ctx* ctx, const spa_model_desc* m, const spa_layer* l, const spa_batch* b,
+                                   int32_t tok0, int32_t n_tok, const void* q, void* o_out, int32_t* err_out,
+                                   void* stream);
+
 /* Figure 3 "Output proj, Add+Norm": h = x + o Wo^T (h_out [n_tok][H] fp32)
  * and hn = RMSNorm(h) gamma2 (hn_out [n_tok][H] fp32). */
 spa_status spa_out_proj(spa_ctx* ctx, const spa_model_desc* m, const spa_layer* l, const float* x, const void* o,

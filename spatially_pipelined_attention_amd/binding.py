@@ -91,6 +91,8 @@ _PROTOS = {
                        _P, C.c_size_t, _P],
     "spa_decode_attn": [_P, C.POINTER(spa_model_desc), C.POINTER(spa_layer), C.POINTER(spa_batch), _I, _I, _P, _P,
                         _P, C.c_size_t, _P],
+    "spa_decode_attn_noalloc": [_P, C.POINTER(spa_model_desc), C.POINTER(spa_layer), C.POINTER(spa_batch), _I, _I,
+                                _P, _P, _P, _P],
     "spa_out_proj": [_P, C.POINTER(spa_model_desc), C.POINTER(spa_layer), _P, _P, _I, _P, _P, _P, C.c_size_t, _P],
     "spa_moe_route": [_P, C.POINTER(spa_model_desc), C.POINTER(spa_layer), _P, _I, _P,
                       C.POINTER(spa_route_bufs), _P, _P, C.c_size_t, _P],
@@ -238,6 +240,12 @@ def spa_qkv_append(ctx, m, layer, batch, tok0, n_tok, xn, q_out, ws, stream=None
 def spa_decode_attn(ctx, m, layer, batch, tok0, n_tok, q, o_out, ws, stream=None):
     _check(lib().spa_decode_attn(ctx, C.byref(m), C.byref(layer), C.byref(batch), tok0, n_tok, ptr(q), ptr(o_out),
                                  *_ws(ws), stream_handle(stream)))
+
+
+def spa_decode_attn_noalloc(ctx, m, layer, batch, tok0, n_tok, q, o_out, err_out=None, stream=None):
+    _check(lib().spa_decode_attn_noalloc(ctx, C.byref(m), C.byref(layer), C.byref(batch), tok0, n_tok, ptr(q),
+                                         ptr(o_out), ptr(err_out) if err_out is not None else None,
+                                         stream_handle(stream)))
 
 
 def spa_out_proj(ctx, m, layer, x, o, n_tok, h_out, hn_out, ws, stream=None):

@@ -869,6 +869,10 @@ spa_status spa_init(int hip_device, spa_ctx** out) {
     return fail(SPA_EUNSUPPORTED, "this library is built for gfx950, device is " + arch);
   }
   c->n_xcd = 8;
+  if (spa_status rc = noalloc_bind_device(hip_device)) {
+    delete c;
+    return rc;
+  }
   int khz = 0;
   if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, hip_device) == hipSuccess && khz > 0)
     c->wall_khz = khz;
@@ -1021,6 +1025,58 @@ spa_status spa_decode_attn(spa_ctx* ctx, const spa_model_desc* m, const spa_laye
   SPA_OP_PROLOGUE(n_tok)
   return op_attn(ctx, m, l, b, tok0, n_tok, q, o_out, W, s, st, nullptr);
 }
+
+}  // extern "C"
+
+namespace spa {
+
+// The attention operator on scratch the caller hands over (the no-allocation
+// entry point's fixed device array): the chunk partials at part, the error
+// word at err (cleared here unless the caller gave its own). The partial
+// buffer holds exactly the chunks this call's shapes produce.
+size_t attn_scratch_bytes(spa_ctx* ctx, const spa_model_desc* m, const spa_layer* l, const spa_batch* b, int n_tok,
+                          int* max_chunks_out) {
+  const int G = m->n_q_heads / m->n_kv_heads;
+  const int chunks = l->kind == SPA_FULL ? (b->max_kv_len + attn_chunk(m, b, n_tok, ctx->n_cus) - 1) /
+                                               attn_chunk(m, b, n_tok, ctx->n_cus)
+                                         : (m->window + kAttnChunk - 1) / kAttnChunk;
+  if (max_chunks_out) *max_chunks_out = chunks;
+  return (size_t)n_tok * m->n_kv_heads * chunks * G * (m->head_dim + 2) * 4;
+}
+
+spa_status decode_attn_on_scratch(spa_ctx* ctx, const spa_model_desc* m, const spa_layer* l, const spa_batch* b,
+                                  int tok0, int n_tok, const void* q, void* o, float* part, size_t part_bytes,
+                                  int32_t* err_word, bool clear_err, hipStream_t st) {
+  int chunks = 0;
+  const size_t need = attn_scratch_bytes(ctx, m, l, b, n_tok, &chunks);
+  if (need > part_bytes)
+    return fail(SPA_EWORKSPACE, "attention partials need " + std::to_string(need) + " bytes, the fixed scratch holds " +
+                                    std::to_string(part_bytes));
+  WsLayout W{};
+  W.max_chunks = chunks;
+  Slot s{};
+  s.attn_part = part;
+  s.err = err_word;
+  if (clear_err) SPA_HIP(launch_fill_i32(err_word, 1, 0, st));
+  return op_attn(ctx, m, l, b, tok0, n_tok, q, o, W, s, st, nullptr);
+}
+
+spa_status check_decode_attn_args(const spa_model_desc* m, const spa_layer* l, const spa_batch* b, int tok0, int n_tok,
+                                  const void* q, const void* o_out) {
+  if (!m) return fail(SPA_EINVAL, "model is NULL");
+  spa_status rc = validate_model(m);
+  if (rc) return rc;
+  if ((rc = check_batch(b))) return rc;
+  if ((rc = check_layer(m, l))) return rc;
+  if ((rc = check_tokens(m, n_tok))) return rc;
+  if (tok0 < 0 || n_tok < 1 || tok0 + n_tok > b->batch) return fail(SPA_EINVAL, "token range outside the batch");
+  if (!q || !o_out || misaligned(q)) return fail(SPA_EINVAL, "q / o_out NULL or misaligned");
+  return SPA_OK;
+}
+
+}  // namespace spa
+
+extern "C" {
 
 spa_status spa_out_proj(spa_ctx* ctx, const spa_model_desc* m, const spa_layer* l, const float* x, const void* o,
                         int32_t n_tok, float* h_out, float* hn_out, void* ws, size_t ws_bytes, void* stream) {

@@ -74,6 +74,19 @@ spa_status launch_comm(spa_ctx* ctx, const void* src, void* dst, size_t copy_byt
 WsLayout ws_layout(const spa_model_desc* m, int n_tok, int max_kv_len, int n_micro);
 int max_chunks_for(int max_kv_len, const spa_model_desc* m);
 GemmPlan plan_gemm(int kclass, const spa_model_desc* m, int n_tok, int n_cus);
+// Decode attention with its scratch handed over (no workspace): bytes of
+// chunk partials a call needs, the argument checks of spa_decode_attn, and
+// the launch itself (SPA_EWORKSPACE when part_bytes is too small).
+size_t attn_scratch_bytes(spa_ctx* ctx, const spa_model_desc* m, const spa_layer* l, const spa_batch* b, int n_tok,
+                          int* max_chunks_out);
+spa_status check_decode_attn_args(const spa_model_desc* m, const spa_layer* l, const spa_batch* b, int tok0, int n_tok,
+                                  const void* q, const void* o_out);
+spa_status decode_attn_on_scratch(spa_ctx* ctx, const spa_model_desc* m, const spa_layer* l, const spa_batch* b,
+                                  int tok0, int n_tok, const void* q, void* o, float* part, size_t part_bytes,
+                                  int32_t* err_word, bool clear_err, hipStream_t st);
+// Looks up this device's copy of the no-allocation scratch array (once per
+// device; the device must be current). Called by spa_init.
+spa_status noalloc_bind_device(int device);
 
 // CUs a stream's kernels run on: the pool's count for a CU-masked pool
 // stream (registered by the pool), `fallback` for any other stream.
