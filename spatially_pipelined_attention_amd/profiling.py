@@ -32,11 +32,14 @@ import argparse
 import csv
 import hashlib
 import os
+import re
 import sys
 from collections import defaultdict
 from typing import Dict, List
 
 PKG = os.path.dirname(os.path.abspath(__file__))
+# kernels that build a run's inputs rather than run the decode iteration
+SETUP_KERNELS = r"k_gen_|k_pack_panels|k_kv_io|FillFunctor|k_fill_i32"
 
 
 def source_digest(paths: List[str]) -> str:
@@ -139,11 +142,13 @@ def cmd_iter_traffic(a):
     f_scale = a.copy_bytes / (_copy_kib(fetch) * 1024.0)
     w_scale = a.copy_bytes / (_copy_kib(write) * 1024.0)
 
+    skip = re.compile(a.exclude)
+
     def sums(disp, sc):
         g = defaultdict(lambda: [0, 0.0])
         for d in disp:
             name = d["name"].split("(")[0].replace("void ", "")
-            if "copy" in name.lower() or name.startswith("__amd"):
+            if "copy" in name.lower() or name.startswith("__amd") or skip.search(name):
                 continue
             g[name][0] += 1
             g[name][1] += d["kib"] * 1024.0 * sc
@@ -155,7 +160,8 @@ def cmd_iter_traffic(a):
     tw = sum(v[1] for v in gw.values()) / K
     print(f"# HBM-side traffic per iteration\n\ncommand: `{a.command}`\n")
     print(f"Counter scale from a plain copy of {a.copy_bytes} bytes: fetch x{f_scale:.4f}, write x{w_scale:.4f}. "
-          f"Every dispatch of the run except the copies and runtime helpers, divided by {K} iterations.\n")
+          f"Every dispatch of the run except the copies, runtime helpers and the input set-up kernels "
+          f"(`{a.exclude}`), divided by {K} iterations.\n")
     print(f"- fetch_GB_per_iter: {tf / 1e9:.3f}")
     print(f"- write_GB_per_iter: {tw / 1e9:.3f}")
     print(f"- traffic_GB_per_iter: {(tf + tw) / 1e9:.3f}")
@@ -249,6 +255,8 @@ def main(argv=None):
     it.add_argument("--iterations", type=int, required=True)
     it.add_argument("--command", required=True)
     it.add_argument("--set", action="append")
+    it.add_argument("--exclude", default=SETUP_KERNELS,
+                    help="regex of kernel names that build the inputs (generator, weight packing, KV writes, fills)")
     tt = sub.add_parser("traffic-table")
     tt.add_argument("--fetch", required=True)
     tt.add_argument("--write", required=True)
