@@ -11,7 +11,9 @@ import ctypes as C
 import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libspa.so")
+# SPA_LIBRARY names another build of the same library (a build-time variant
+# for a measurement); the default is the in-tree build.
+LIB_PATH = os.environ.get("SPA_LIBRARY") or os.path.join(_HERE, "libspa.so")
 
 SPA_OK = 0
 SPA_EINVAL = -1

@@ -48,8 +48,13 @@ template <int CT, int MT> struct Ring {
   static constexpr int P = CT * MT > 16 ? SPA_GEMM_RING_BIG : (CT * MT > 8 ? SPA_GEMM_RING_MID : 4);
 };
 
+// resident workgroups per CU the register budget is sized for
+#ifndef SPA_GEMM_MINB
+#define SPA_GEMM_MINB 2
+#endif
+
 template <int WT, int EPI, int CT, int MT>
-__global__ __launch_bounds__(256, 2) void k_gemm(GemmArgs a) {
+__global__ __launch_bounds__(256, SPA_GEMM_MINB) void k_gemm(GemmArgs a) {
   __shared__ __attribute__((aligned(16))) char red[3 * CT * 64 * 16];   // wave reduction of one 16-row tile
   constexpr int P = Ring<CT, MT>::P;
   constexpr int BR = 16 * MT;

@@ -9,8 +9,9 @@
 // x 128-column tile and streams K through LDS:
 //   * per 64-byte k-step the 256 threads load the block's 128 activation rows
 //     and 128 weight rows (16 KB, four 16-byte loads per thread) into one of
-//     two LDS buffers, the next k-step's loads in flight while the current
-//     one is multiplied (one barrier per k-step);
+//     two LDS buffers (one barrier per k-step); the loads are issued two
+//     k-steps ahead into two register slots, so each has two k-steps of
+//     multiplication to land before it is stored to LDS;
 //   * the 4 waves form a 2 x 2 grid of 64 x 64 sub-tiles; each reads its 4
 //     activation and 4 weight fragments from LDS and issues 16 MFMA tiles, so
 //     every loaded byte feeds 64 output rows or columns instead of one tile;
@@ -26,6 +27,8 @@
 #include "common.h"
 #include "gemm_common.h"
 #include "kernels.h"
+
+#include <type_traits>
 
 namespace spa {
 
@@ -82,21 +85,27 @@ __global__ __launch_bounds__(256, 2) void k_gemm_big(GemmArgs a) {
               (long long)ks0 * 1024 + (wv & 15) * 64 + part * 16;
     ldsoff[h] = row * kLdsRow + part * 16;
   }
-  u32x4 xr[2], wreg[2];
-  auto load = [&](int kk) {
+  // two register slots of one k-step each: the loads of k-step k + 2 go out
+  // while k is multiplied, so every load has two k-steps of MFMA work to land
+  u32x4 xr[2][2], wreg[2][2];
+  auto load = [&](auto slot_c, int kk) {
+    constexpr int sl = decltype(slot_c)::value;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      xr[h] = ld16(xsrc[h] + (long long)kk * a.x_kstride);
-      wreg[h] = ld16(wsrc[h] + (long long)kk * 1024);
+      xr[sl][h] = ld16(xsrc[h] + (long long)kk * a.x_kstride);
+      wreg[sl][h] = ld16(wsrc[h] + (long long)kk * 1024);
     }
   };
-  auto stash = [&](int buf) {
+  auto stash = [&](auto slot_c) {   // slot sl into LDS buffer sl
+    constexpr int sl = decltype(slot_c)::value;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      *reinterpret_cast<u32x4*>(&xs[buf][ldsoff[h]]) = xr[h];
-      *reinterpret_cast<u32x4*>(&wsm[buf][ldsoff[h]]) = wreg[h];
+      *reinterpret_cast<u32x4*>(&xs[sl][ldsoff[h]]) = xr[sl][h];
+      *reinterpret_cast<u32x4*>(&wsm[sl][ldsoff[h]]) = wreg[sl][h];
     }
   };
+  constexpr std::integral_constant<int, 0> S0{};
+  constexpr std::integral_constant<int, 1> S1{};
 
   f32x4 acc[4][4];
 #pragma unroll
@@ -108,25 +117,34 @@ __global__ __launch_bounds__(256, 2) void k_gemm_big(GemmArgs a) {
   const int wrd = (wc * 64 + lo16) * kLdsRow + kq;
 
   if (nks > 0) {
-    load(0);
-    stash(0);
+    load(S0, 0);
+    stash(S0);
   }
+  if (nks > 1) load(S1, 1);
   __syncthreads();
-  for (int k = 0; k < nks; ++k) {
-    const int buf = k & 1;
-    if (k + 1 < nks) load(k + 1);   // in flight while this k-step is multiplied
+  // k-step k sits in LDS buffer and register slot k & 1
+  auto step = [&](auto slot_c, int k) {
+    constexpr int sl = decltype(slot_c)::value;
+    if (k + 2 < nks) load(slot_c, k + 2);   // this slot's k-step was stashed one step ago
     u32x4 xf[4], wf[4];
 #pragma unroll
     for (int f = 0; f < 4; ++f) {
-      xf[f] = *reinterpret_cast<const u32x4*>(&xs[buf][xrd + f * 16 * kLdsRow]);
-      wf[f] = *reinterpret_cast<const u32x4*>(&wsm[buf][wrd + f * 16 * kLdsRow]);
+      xf[f] = *reinterpret_cast<const u32x4*>(&xs[sl][xrd + f * 16 * kLdsRow]);
+      wf[f] = *reinterpret_cast<const u32x4*>(&wsm[sl][wrd + f * 16 * kLdsRow]);
     }
 #pragma unroll
     for (int mf = 0; mf < 4; ++mf)
 #pragma unroll
       for (int cf = 0; cf < 4; ++cf) acc[mf][cf] = mma_step<WT>(wf[cf], xf[mf], acc[mf][cf]);
-    if (k + 1 < nks) stash(buf ^ 1);
+    if (k + 1 < nks) {   // k-step k + 1 into the other buffer (read one step ago by every wave)
+      if constexpr (sl == 0) stash(S1);
+      else stash(S0);
+    }
     __syncthreads();
+  };
+  for (int k = 0; k < nks; k += 2) {
+    step(S0, k);
+    if (k + 1 < nks) step(S1, k + 1);
   }
 
   // lane: row wr*64 + mf*16 + lo16 of the block; tile column wc*64 + cf*16 + c4 + i
