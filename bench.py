@@ -63,8 +63,10 @@ def traffic_from_profile(name, tokens_per_launch):
 DEAL_MAX_TOKENS = 256   # launches of up to this many tokens deal their chunks (kDealMaxTok)
 
 
-def attn_kernel_name(tokens_per_launch):
-    """The full-layer attention kernel a launch of this many tokens runs."""
+def attn_kernel_name(tokens_per_launch, full=True):
+    """The attention kernel a launch of this many tokens runs (full or sliding layers)."""
+    if not full:
+        return "spa::k_attn<1, 0>"
     return "spa::k_attn_dealt<1>" if tokens_per_launch <= DEAL_MAX_TOKENS else "spa::k_attn<1, 1>"
 
 
@@ -85,6 +87,12 @@ def tuned_config(name, comm=False):
     return {"cut": 0, "n_micro": 2, "cu_a": 128}
 
 
+def dense_weight_bytes(wl):
+    """One layer's dense projection and router weights."""
+    wb = 2 if wl.w_dtype == "bf16" else 4
+    return (wl.qkv_rows * wl.hidden + wl.hidden * wl.n_q_heads * wl.head_dim) * wb + wl.n_experts * wl.hidden * 4
+
+
 def algorithmic_bytes(dw, n_micro=1):
     """Bytes one iteration of a schedule with n_micro microbatches must move:
     every layer's dense and router weights and the experts that receive rows
@@ -94,7 +102,7 @@ def algorithmic_bytes(dw, n_micro=1):
     wb = 2 if wl.w_dtype == "bf16" else 4
     eb = {"bf16": 2, "f32": 4, "e4m3": 1}[wl.expert_dtype]
     H, I, QD = wl.hidden, wl.inter, wl.n_q_heads * wl.head_dim
-    dense = (wl.qkv_rows * H + H * QD) * wb + wl.n_experts * H * 4
+    dense = dense_weight_bytes(wl)
     experts = wl.n_resident * 3 * H * I * eb
     if wl.expert_dtype == "e4m3":
         experts += wl.n_resident * (2 * I + H) * 4
@@ -103,20 +111,28 @@ def algorithmic_bytes(dw, n_micro=1):
     return wl.n_layers * per_layer_w * n_micro + kv, wl.n_layers * per_layer_w * n_micro, kv
 
 
-def cpu_baseline(name, n_tok_sample=None):
-    """The CPU oracle on the whole iteration (every layer, every sequence),
-    inputs generated outside the timed region, layer by layer."""
-    from threadpoolctl import threadpool_info
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.lower().startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _oracle_iteration_s(name, n_layers=None):
+    """Seconds of oracle layer compute for the whole batch over the first
+    n_layers layers (all by default); input generation is not timed."""
     from oracle import layer as ol
     from spatially_pipelined_attention_amd import synth
     from tests import harness as hz
     wl = synth.WORKLOADS[name]
-    toks = list(range(wl.batch if n_tok_sample is None else n_tok_sample))
-    resample = load_resample(name)
+    toks = list(range(wl.batch))
     L = synth.kv_lengths(wl)[toks]
-    x = synth.x_rows(wl, toks, resample)
+    x = synth.x_rows(wl, toks, load_resample(name))
     dt = 0.0
-    for l in range(wl.n_layers):
+    for l in range(n_layers or wl.n_layers):
         dense = synth.dense_weights(wl, l)
         experts = {e: synth.expert_weights(wl, l, e) for e in range(wl.n_resident)}
         hist = {}
@@ -133,12 +149,50 @@ def cpu_baseline(name, n_tok_sample=None):
         dt += time.perf_counter() - t0
         x = rec.x_next
         del hist
-    scale = wl.batch / len(toks)
+    return dt
+
+
+def cpu_baseline(name, single_thread_layers=8):
+    """The CPU oracle (oracle/: float64 numpy, as written for checking, not
+    tuned for speed) on the host cores: the whole iteration for every
+    sequence with the BLAS thread pool at its default size, and the first
+    `single_thread_layers` layers (half sliding, half full) on one thread,
+    scaled to the whole iteration."""
+    from threadpoolctl import threadpool_info, threadpool_limits
+    from spatially_pipelined_attention_amd import synth
+    wl = synth.WORKLOADS[name]
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    return {"value": dt * scale * 1e6, "unit": "us", "cores": int(threads), "kind": "oracle",
-            "sample": f"the whole {wl.n_layers}-layer iteration for {len(toks)} of {wl.batch} sequences "
-                      f"(layer compute timed, input generation excluded), {dt:.1f} s"
-                      + ("" if len(toks) == wl.batch else f", scaled x{scale:.1f}")}
+    dt_all = _oracle_iteration_s(name)
+    n1 = min(single_thread_layers, wl.n_layers)
+    with threadpool_limits(limits=1):
+        dt_one = _oracle_iteration_s(name, n1) * wl.n_layers / n1
+    return {"value": dt_all * 1e6, "unit": "us", "cores": int(threads), "kind": "oracle",
+            "sample": f"the whole {wl.n_layers}-layer iteration for all {wl.batch} sequences (layer compute timed, "
+                      f"input generation excluded), {dt_all:.1f} s with {threads} BLAS threads",
+            "single_thread_us": round(dt_one * 1e6, 0),
+            "single_thread_sample": f"first {n1} of {wl.n_layers} layers on one thread, scaled x{wl.n_layers / n1:g}",
+            "nproc": os.cpu_count(), "cpu_model": _cpu_model(),
+            "impl": "float64 numpy oracle of the tests (not the tuned C++ baseline a production comparison would use)"}
+
+
+def probe_ceiling():
+    """The device's practical HBM read rate from the committed probe summary
+    (spatially_pipelined_attention_amd/hbm_probe.py), or None."""
+    from spatially_pipelined_attention_amd import profiling
+    keys = profiling.read_keys(os.path.join(ROOT, "profiles", "hbm_read_probe.md"))
+    return float(keys["ceiling_GBps"]) if "ceiling_GBps" in keys else None
+
+
+def touched_expert_bytes(dw, n_micro):
+    """Bytes of the resident experts that received rows, per microbatch, from
+    the picks recorded by the last run (pick t runs expert t % E_res)."""
+    wl = dw.wl
+    eb = {"bf16": 2, "f32": 4, "e4m3": 1}[wl.expert_dtype]
+    per_expert = 3 * wl.hidden * wl.inter * eb + ((2 * wl.inter + wl.hidden) * 4 if wl.expert_dtype == "e4m3" else 0)
+    picks = dw.topk.cpu().numpy() % wl.n_resident        # [layers][batch][k]
+    bm = wl.batch // n_micro
+    n = sum(len(np.unique(picks[l, mu * bm:(mu + 1) * bm])) for l in range(wl.n_layers) for mu in range(n_micro))
+    return n * per_expert
 
 
 TIMER_NOTE = {
@@ -264,13 +318,16 @@ def main():
             run_schedule(f"temporal_T{m}", cfg["cut"], m, None, ws)
         if schedule == "temporal":
             run_schedule("spatial", cfg["cut"], m, cfg["cu_a"], ws, cu_s=cfg.get("cu_a_sliding"))
+    # the roofline kernel: full-layer attention (sliding-layer attention when the workload has no full layer)
+    has_full = "full" in wl.layer_kinds
+    attn_cls = B.KC_ATTN_FULL if has_full else B.KC_ATTN_SLIDING
     wsr = ws1 if m == 1 else (ws if m == cfg["n_micro"] else dw.workspace(n_micro=m))
     if schedule == "spatial":
-        ms, (k_ms, k_n) = run_schedule("reported", cfg["cut"], m, cfg["cu_a"], wsr, timed_cls=B.KC_ATTN_FULL,
+        ms, (k_ms, k_n) = run_schedule("reported", cfg["cut"], m, cfg["cu_a"], wsr, timed_cls=attn_cls,
                                        cu_s=cfg.get("cu_a_sliding"))
         sched = sp_label
     else:   # temporal with the selected (or configured) microbatch count
-        ms, (k_ms, k_n) = run_schedule("reported", cfg["cut"], m, None, wsr, timed_cls=B.KC_ATTN_FULL)
+        ms, (k_ms, k_n) = run_schedule("reported", cfg["cut"], m, None, wsr, timed_cls=attn_cls)
         sched = f"temporal m={m}"
     if args.schedule == "auto":
         sched += " (the fastest of " + ", ".join(k for k in results if k != "reported") + ")" if not args.quick \
@@ -287,7 +344,12 @@ def main():
 
     total_b, w_b, kv_b = algorithmic_bytes(dw, m)
     min_b = algorithmic_bytes(dw, 1)[0]
-    full_layers = [l for l in range(wl.n_layers) if wl.layer_kinds[l] == "full"]
+    if wl.n_resident > wl.top_k * wl.batch // m or wl.n_resident > 4:
+        # many resident experts: only those that received rows are read
+        all_e = algorithmic_bytes(dw, 1)[1] - wl.n_layers * dense_weight_bytes(wl)   # every resident expert, once
+        total_b += touched_expert_bytes(dw, m) - all_e * m
+        min_b += touched_expert_bytes(dw, 1) - all_e
+    full_layers = [l for l in range(wl.n_layers) if wl.layer_kinds[l] == ("full" if has_full else "sliding")]
     n_micro_rep = m
     kv_full = sum(dw.algorithmic_kv_bytes(l) for l in full_layers)
     bytes_per_launch = kv_full / len(full_layers) / n_micro_rep
@@ -295,8 +357,11 @@ def main():
     traffic, traffic_src = traffic_from_profile(name, wl.batch // m)
     us = ms * 1e3
     gbps = total_b / (ms * 1e-3) / 1e9
+    ceiling = probe_ceiling()
+    metric = METRIC if wl.n_layers == 36 else METRIC.replace("36-layer decode iteration",
+                                                             f"{wl.n_layers}-layer decode step")
     out = {
-        "metric": METRIC, "value": round(us, 1), "unit": "us", "n_gpus": 1, "steps": args.steps,
+        "metric": metric, "value": round(us, 1), "unit": "us", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": False, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16" if wl.expert_dtype != "e4m3" else "bf16+e4m3",
         "data": "synthetic (seeded generator; GPT-OSS-120B-shaped random weights, no trained checkpoint)",
@@ -310,14 +375,18 @@ def main():
                                      "endpoints": "attention all-reduce, MoE dispatch, MoE combine per layer"}
                                     if comm else None)},
         "hbm_GBps": round(gbps, 1), "hbm_pct_peak": round(100 * gbps / HBM_PEAK_GBPS, 1),
+        "hbm_probe_ceiling_GBps": ceiling,
+        "hbm_pct_probe_ceiling": round(100 * gbps / ceiling, 1) if ceiling else None,
         "algorithmic_GB_per_iter": round(total_b / 1e9, 3),
         "hbm_GBps_min_bytes": round(min_b / (ms * 1e-3) / 1e9, 1),   # the iteration's bytes with weights read once
         "min_GB_per_iter": round(min_b / 1e9, 3),
         "tokens_per_s": round(wl.batch / (ms * 1e-3), 1), "per_user_tokens_per_s": round(1 / (ms * 1e-3), 2),
         "schedules_ms": {k: round(v["ms"], 4) for k, v in results.items()},
-        "roofline": {"bound": "hbm", "kernel": f"{attn_kernel_name(wl.batch // m)} (full-layer decode attention, bf16 KV)",
+        "roofline": {"bound": "hbm", "kernel": f"{attn_kernel_name(wl.batch // m, has_full)} "
+                                               f"({'full' if has_full else 'sliding'}-layer decode attention, bf16 KV)",
                      "achieved": round(achieved, 1) if achieved else None, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4) if achieved else None,
+                     "frac_of_probe_ceiling": round(achieved / ceiling, 4) if achieved and ceiling else None,
                      "traffic": int(traffic) if traffic else None,
                      "bytes_per_launch": int(bytes_per_launch), "mean_launch_ms": k_ms, "launches": k_n,
                      "timer": TIMER_NOTE[args.kernel_timer]},

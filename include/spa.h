@@ -331,7 +331,28 @@ spa_status spa_pool_stream(spa_pool* p, void** hip_stream);
  * report the distinct hardware CUs (XCC, SE, SH, CU ids packed as
  * xcc << 16 | se << 8 | sh << 4 | cu) they ran on, up to max_ids entries. */
 spa_status spa_pool_probe(spa_pool* p, int32_t n_blocks, uint32_t* ids_out, int32_t max_ids, int32_t* n_ids);
+/* Placement check of a pool (the blog on the paper warns that a partition
+ * handle that is not applied silently runs the work on the whole GPU): runs
+ * the probe with 64 workgroups per CU of the mask and compares the CUs they
+ * landed on with the mask. SPA_OK when they fit it - no more distinct CUs
+ * than the mask holds, on as many XCDs, and on no XCD more CUs than the mask
+ * gives that XCD (the counts are compared as sorted lists, since the
+ * hardware's XCD labels need not follow the mask's numbering); SPA_EMASK
+ * otherwise, with the counts in spa_last_error(). observed_out (optional):
+ * the distinct CUs seen. Synchronises the pool's stream. */
+spa_status spa_pool_verify(spa_pool* p, int32_t* observed_out);
 spa_status spa_pool_destroy(spa_pool* p);
+
+/* Read-bandwidth probe (the empirical HBM bandwidth-versus-concurrency curve
+ * that section 4.3 of the paper lists among its calibration inputs): n_wgs
+ * workgroups of 256 threads each stream their share of `bytes` bytes of src
+ * once (non-temporal 16-byte loads, 8 in flight per lane) on `stream`; on a
+ * pool's stream this is the rate that pool can pull. src: device memory,
+ * 16-byte aligned; bytes a non-zero multiple of n_wgs * 1024. One warm-up
+ * launch, then `reps` launches between two events; *ms = mean launch time.
+ * Synchronises the stream. The rate is bytes / ms. */
+spa_status spa_hbm_probe(spa_ctx* ctx, const void* src, size_t bytes, int32_t n_wgs, int32_t reps, void* stream,
+                         double* ms);
 
 /* --------------------------------------------------------- the pipeline
  * theta = (D = 2 stages, w, cut, CU split, microbatch count) of section

@@ -111,6 +111,8 @@ _PROTOS = {
     "spa_pool_mask": [_P, C.POINTER(C.c_uint32), _I],
     "spa_pool_stream": [_P, C.POINTER(C.c_void_p)],
     "spa_pool_probe": [_P, _I, C.POINTER(C.c_uint32), _I, C.POINTER(C.c_int32)],
+    "spa_pool_verify": [_P, C.POINTER(C.c_int32)],
+    "spa_hbm_probe": [_P, _P, C.c_size_t, _I, _I, _P, C.POINTER(C.c_double)],
     "spa_pool_destroy": [_P],
     "spa_pipeline_create": [_P, C.POINTER(spa_model_desc), C.POINTER(spa_pipeline_cfg), _P, _P,
                             C.POINTER(C.c_void_p)],
@@ -314,6 +316,22 @@ def spa_pool_probe(pool, n_blocks: int, max_ids: int = 1024):
     n = C.c_int32()
     _check(lib().spa_pool_probe(pool, n_blocks, arr, max_ids, C.byref(n)))
     return list(arr[: min(n.value, max_ids)]), n.value
+
+
+def spa_pool_verify(pool) -> int:
+    """Raises SpaError (SPA_EMASK) when the pool's kernels land outside its mask;
+    returns the distinct CUs observed."""
+    n = C.c_int32()
+    _check(lib().spa_pool_verify(pool, C.byref(n)))
+    return n.value
+
+
+def spa_hbm_probe(ctx, src, n_wgs: int, reps: int = 10, stream=None, nbytes: int | None = None) -> float:
+    """Mean launch time (ms) of the read probe over src (a torch CUDA tensor)."""
+    ms = C.c_double()
+    nb = nbytes if nbytes is not None else src.numel() * src.element_size()
+    _check(lib().spa_hbm_probe(ctx, ptr(src), nb, n_wgs, reps, stream_handle(stream), C.byref(ms)))
+    return ms.value
 
 
 def spa_pool_destroy(pool):

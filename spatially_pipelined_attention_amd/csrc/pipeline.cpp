@@ -85,6 +85,25 @@ static spa_status make_pool(spa_ctx* ctx, const std::vector<uint32_t>& mask, spa
   return SPA_OK;
 }
 
+// Distinct hardware CUs (packed ids) that n_blocks short workgroups on the
+// pool's stream ran on.
+static spa_status probe_ids(spa_pool* p, int n_blocks, std::set<uint32_t>* ids) {
+  unsigned* buf = nullptr;
+  SPA_HIP(hipMalloc(&buf, sizeof(unsigned) * 2 * n_blocks));
+  std::vector<unsigned> h(2 * (size_t)n_blocks);
+  hipError_t e = launch_probe(buf, n_blocks, 20000, p->stream);
+  if (e == hipSuccess) e = hipMemcpyAsync(h.data(), buf, h.size() * sizeof(unsigned), hipMemcpyDeviceToHost, p->stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(p->stream);
+  (void)hipFree(buf);
+  if (e != hipSuccess) return hip_fail(e, "probe");
+  for (int i = 0; i < n_blocks; ++i) {
+    unsigned xcc = h[2 * i] & 0xF, hw = h[2 * i + 1];
+    unsigned cu = (hw >> 8) & 0xF, sh = (hw >> 12) & 1, se = (hw >> 13) & 7;
+    ids->insert((xcc << 16) | (se << 8) | (sh << 4) | cu);
+  }
+  return SPA_OK;
+}
+
 extern "C" {
 
 spa_status spa_pool_create_mask(spa_ctx* ctx, const uint32_t* cu_mask, int32_t n_words, spa_pool** out) {
@@ -125,26 +144,50 @@ spa_status spa_pool_stream(spa_pool* p, void** s) {
 
 spa_status spa_pool_probe(spa_pool* p, int32_t n_blocks, uint32_t* ids_out, int32_t max_ids, int32_t* n_ids) {
   if (!p || !ids_out || !n_ids || n_blocks < 1 || n_blocks > (1 << 20)) return fail(SPA_EINVAL, "bad argument");
-  unsigned* buf = nullptr;
-  SPA_HIP(hipMalloc(&buf, sizeof(unsigned) * 2 * n_blocks));
-  std::vector<unsigned> h(2 * (size_t)n_blocks);
-  hipError_t e = launch_probe(buf, n_blocks, 20000, p->stream);
-  if (e == hipSuccess) e = hipMemcpyAsync(h.data(), buf, h.size() * sizeof(unsigned), hipMemcpyDeviceToHost, p->stream);
-  if (e == hipSuccess) e = hipStreamSynchronize(p->stream);
-  (void)hipFree(buf);
-  if (e != hipSuccess) return hip_fail(e, "probe");
   std::set<uint32_t> ids;
-  for (int i = 0; i < n_blocks; ++i) {
-    unsigned xcc = h[2 * i] & 0xF, hw = h[2 * i + 1];
-    unsigned cu = (hw >> 8) & 0xF, sh = (hw >> 12) & 1, se = (hw >> 13) & 7;
-    ids.insert((xcc << 16) | (se << 8) | (sh << 4) | cu);
-  }
+  spa_status rc = probe_ids(p, n_blocks, &ids);
+  if (rc) return rc;
   int n = 0;
   for (uint32_t v : ids) {
     if (n < max_ids) ids_out[n] = v;
     ++n;
   }
   *n_ids = n;
+  return SPA_OK;
+}
+
+spa_status spa_pool_verify(spa_pool* p, int32_t* observed_out) {
+  if (!p) return fail(SPA_EINVAL, "bad argument");
+  const int nx = p->ctx->n_xcd;
+  std::vector<int> want(nx, 0);
+  int n_mask = 0;
+  for (size_t w = 0; w < p->mask.size(); ++w)
+    for (int bit = 0; bit < 32; ++bit)
+      if (p->mask[w] >> bit & 1u) {
+        ++want[(w * 32 + bit) % nx];
+        ++n_mask;
+      }
+  std::set<uint32_t> ids;
+  spa_status rc = probe_ids(p, std::min(1 << 16, 64 * n_mask), &ids);
+  if (rc) return rc;
+  std::vector<int> got(16, 0);
+  for (uint32_t v : ids) ++got[(v >> 16) & 0xF];
+  if (observed_out) *observed_out = (int32_t)ids.size();
+  // XCD labels of the hardware ids need not follow the mask's numbering:
+  // compare the per-XCD counts as sorted lists
+  std::vector<int> g(got.begin(), got.end()), wnt(want.begin(), want.end());
+  g.erase(std::remove(g.begin(), g.end(), 0), g.end());
+  wnt.erase(std::remove(wnt.begin(), wnt.end(), 0), wnt.end());
+  std::sort(g.begin(), g.end());
+  std::sort(wnt.begin(), wnt.end());
+  const bool over = (int)ids.size() > n_mask || g.size() > wnt.size();
+  bool per_xcd_over = false;
+  if (!over && g.size() == wnt.size())
+    for (size_t i = 0; i < g.size(); ++i) per_xcd_over |= g[i] > wnt[i];
+  if (over || per_xcd_over || g.size() != wnt.size())
+    return fail(SPA_EMASK, "pool kernels ran on " + std::to_string(ids.size()) + " CUs over " +
+                               std::to_string(g.size()) + " XCDs; the mask holds " + std::to_string(n_mask) +
+                               " CUs over " + std::to_string(wnt.size()) + " XCDs");
   return SPA_OK;
 }
 

@@ -31,6 +31,10 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--per-kind", type=int, default=1, help="separate CU splits for full and sliding layers")
     ap.add_argument("--virtual-comm", default="", metavar="LATENCY_US,GBPS")
+    ap.add_argument("--points-md", default="", metavar="PATH",
+                    help="also write every measured point as a markdown table (with --command as its provenance)")
+    ap.add_argument("--command", default="")
+    ap.add_argument("--no-store", action="store_true", help="do not merge the result into --out")
     a = ap.parse_args(argv)
 
     import torch
@@ -69,11 +73,41 @@ def main(argv=None):
     for p in pts:
         print(f"cut={p.cut:2d} m={p.n_micro} cu_a={p.cu_a:3d}/{p.cu_a_sliding:3d}: {p.ms:.3f} ms", flush=True)
     print(json.dumps({key: entry}), flush=True)
-    d = json.load(open(a.out)) if os.path.exists(a.out) else {}
-    d[key] = entry
-    with open(a.out, "w") as f:
-        json.dump(d, f, indent=1, sort_keys=True)
+    if a.points_md:
+        write_points_md(a.points_md, key, wl, pts, best, temporal, a.command or " ".join(sys.argv),
+                        B.spa_device_cus(ctx))
+    if not a.no_store:
+        d = json.load(open(a.out)) if os.path.exists(a.out) else {}
+        d[key] = entry
+        with open(a.out, "w") as f:
+            json.dump(d, f, indent=1, sort_keys=True)
     return 0
+
+
+def write_points_md(path, key, wl, pts, best, temporal, command, n_cus):
+    """Every measured point of a tuning run: temporal schedules and the
+    spatial grid (cut x stage-A CUs x microbatches), median iteration ms."""
+    t1 = temporal.get(1)
+    cut_name = {0: "attn | MoE", 1: "attn+router | experts", 2: "Macro (full attention | rest)"}
+    with open(path, "w") as f:
+        f.write(f"# Schedule sweep: {key}\n\ncommand: `{command}`\n\n")
+        f.write(f"{wl.n_layers} layer(s) ({', '.join(sorted(set(wl.layer_kinds)))}), batch {wl.batch}, "
+                f"KV U[{wl.kv_len_lo},{wl.kv_len_hi}], {wl.n_resident} resident experts of {wl.n_experts} "
+                f"(top-{wl.top_k}), {wl.expert_dtype} experts. Median of the timed iterations per point.\n\n")
+        f.write(f"- temporal_T1_ms: {t1:.4f}\n" if t1 else "")
+        f.write(f"- best_spatial_ms: {best.ms:.4f}\n")
+        f.write(f"- best_spatial: cut {best.cut}, m {best.n_micro}, stage A {best.cu_a} CUs"
+                + (f" (sliding layers {best.cu_a_sliding})" if best.cu_a_sliding != best.cu_a else "") + "\n")
+        if t1:
+            f.write(f"- best_spatial_vs_T1: {100 * (best.ms / t1 - 1):+.1f}%\n")
+        f.write("\n| schedule | cut | m | stage A CUs | stage B CUs | ms | vs T1 |\n|---|---|---:|---:|---:|---:|---:|\n")
+        for p in pts:
+            kind = "temporal" if p.cu_a == 0 else "spatial"
+            cut = "-" if p.cu_a == 0 else cut_name.get(p.cut, str(p.cut))
+            a_cus = "-" if p.cu_a == 0 else (str(p.cu_a) if p.cu_a_sliding == p.cu_a else f"{p.cu_a}/{p.cu_a_sliding}")
+            b_cus = "-" if p.cu_a == 0 else str(n_cus - p.cu_a)
+            rel = f"{100 * (p.ms / t1 - 1):+.1f}%" if t1 else ""
+            f.write(f"| {kind} | {cut} | {p.n_micro} | {a_cus} | {b_cus} | {p.ms:.3f} | {rel} |\n")
 
 
 if __name__ == "__main__":

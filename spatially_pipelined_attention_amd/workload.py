@@ -239,7 +239,7 @@ class Pipeline:
     temporal schedule with the same microbatches. Stage A takes the first
     cu_a CUs of every XCD's share, stage B the rest."""
 
-    def __init__(self, ctx, m: B.spa_model_desc, cfg: dict):
+    def __init__(self, ctx, m: B.spa_model_desc, cfg: dict, verify: bool = True):
         self.pools = []
         n_cus = B.spa_device_cus(ctx)
         c = B.spa_pipeline_cfg(int(cfg["cut"]), int(cfg["n_micro"]), int(cfg.get("handoff", 0)))
@@ -253,6 +253,9 @@ class Pipeline:
             self.pools.append(pa)
             pb = B.spa_pool_create_split(ctx, cu // 8, n_cus - cu)
             self.pools.append(pb)
+            if verify:   # the kernels must land on the masked CUs, not silently on the whole GPU
+                B.spa_pool_verify(pa)
+                B.spa_pool_verify(pb)
             return pa, pb
         cu_s = cfg.get("cu_a_sliding") or cu_a
         af, bf = split(cu_a)

@@ -64,6 +64,11 @@ def test_pools_are_disjoint_and_xcd_balanced(env):
         B.spa_pool_destroy(pb)
     assert na == 64 and nb == 192
     assert not set(ia) & set(ib)
+    pa = B.spa_pool_create_split(ctx, 0, 64)
+    try:
+        assert B.spa_pool_verify(pa) == 64   # the library's own placement check agrees
+    finally:
+        B.spa_pool_destroy(pa)
     assert set(collections.Counter(i >> 16 for i in ia).values()) == {8}
     assert set(collections.Counter(i >> 16 for i in ib).values()) == {24}
 
