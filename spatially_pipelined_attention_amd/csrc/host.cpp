@@ -869,6 +869,10 @@ spa_status spa_init(int hip_device, spa_ctx** out) {
     return fail(SPA_EUNSUPPORTED, "this library is built for gfx950, device is " + arch);
   }
   c->n_xcd = 8;
+  if (hipError_t ka = init_kernel_attributes()) {
+    delete c;
+    return hip_fail(ka, "kernel attributes");
+  }
   if (spa_status rc = noalloc_bind_device(hip_device)) {
     delete c;
     return rc;

@@ -207,6 +207,13 @@ struct CvtArgs {
 hipError_t launch_cvt_rows(const CvtArgs& a, hipStream_t st);
 
 hipError_t launch_fill_i32(int* p, long long n, int v, hipStream_t st);
+// Folds n recorded launch spans (kSpanWords words each, as the attention
+// kernels write them) into acc[0] += sum of (latest end - start) ticks and
+// acc[1] += the number of spans with a start (one workgroup, in span order),
+// then clears the n spans for the next launches.
+hipError_t launch_span_fold(unsigned long long* spans, int n, unsigned long long* acc, hipStream_t st);
+// Kernel attributes the launches rely on; call before any stream capture.
+hipError_t init_kernel_attributes();
 
 // Virtual communication endpoint: copy n16 16-byte words src -> dst, then
 // keep every workgroup resident until `ticks` device wall-clock ticks after

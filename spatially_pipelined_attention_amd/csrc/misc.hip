@@ -381,12 +381,16 @@ int route_lds_bytes(int n_tok, int k, int E_res) {
   return (2 * P + 2 * E_res + 1) * 4 + 16 + E_res * ((P + 63) / 64) * 8;
 }
 
+// Kernel attributes set once per process before any launch (not inside a
+// stream capture): the permutation may need more than the default 64 KB of LDS.
+hipError_t init_kernel_attributes() {
+  static hipError_t e = hipFuncSetAttribute((const void*)k_route_permute, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                            160 * 1024);
+  return e;
+}
+
 hipError_t launch_route(const RouteArgs& a, hipStream_t st) {
-  static bool lds_raised = false;   // the permutation may need more than the default 64 KB of LDS
-  if (!lds_raised) {
-    (void)hipFuncSetAttribute((const void*)k_route_permute, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-    lds_raised = true;
-  }
+  (void)init_kernel_attributes();
   int wgs = 1;
   if (a.gsrc) {   // enough workgroups for the gather: ~8 chunks per thread, at most 64
     const long long chunks = (long long)a.gK * a.gesz / 16 * a.n_tok * a.k;
@@ -589,6 +593,29 @@ hipError_t launch_gather_kmajor(const void* src, const int* row_src, int R, int 
 __global__ void k_fill_i32(int* p, long long n, int v) {
   for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (long long)gridDim.x * blockDim.x)
     p[i] = v;
+}
+
+__global__ __launch_bounds__(64) void k_span_fold(unsigned long long* spans, int n, unsigned long long* acc) {
+  if (threadIdx.x != 0) return;
+  unsigned long long sum = 0, cnt = 0;
+  for (int i = 0; i < n; ++i) {
+    unsigned long long* w = spans + (long long)i * kSpanWords;
+    unsigned long long end = 0;
+    for (int j = 1; j <= 16; ++j) end = w[8 * j] > end ? w[8 * j] : end;
+    if (w[0] != 0 && end >= w[0]) {   // else a launch that did no timed work
+      sum += end - w[0];
+      cnt += 1;
+    }
+    w[0] = 0;   // cleared for the next iteration's launches
+    for (int j = 1; j <= 16; ++j) w[8 * j] = 0;
+  }
+  acc[0] += sum;
+  acc[1] += cnt;
+}
+
+hipError_t launch_span_fold(unsigned long long* spans, int n, unsigned long long* acc, hipStream_t st) {
+  hipLaunchKernelGGL(k_span_fold, dim3(1), dim3(64), 0, st, spans, n, acc);
+  return hipGetLastError();
 }
 
 hipError_t launch_fill_i32(int* p, long long n, int v, hipStream_t st) {

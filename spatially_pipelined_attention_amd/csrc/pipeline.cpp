@@ -47,6 +47,12 @@ struct spa_pipeline {
   int tspan_used = 0;
   double t_sum_ms = 0.0;
   int t_count = 0;
+  // graph replay of temporal iterations (cfg.graph)
+  hipStream_t gstream = nullptr;
+  hipGraphExec_t gexec = nullptr;
+  std::vector<unsigned char> gkey;      // the arguments the captured launches were built from
+  hipEvent_t gev_in = nullptr, gev_out = nullptr;
+  unsigned long long* gacc = nullptr;   // device: attention span ticks and launch count of replays
 };
 
 static constexpr int kSpanCap = 8192;   // timed launches between two harvests
@@ -219,6 +225,9 @@ static spa_status create_impl(spa_ctx* ctx, const spa_model_desc* m, const spa_p
   if (cfg->cut < 0 || cfg->cut > 2) return fail(SPA_EINVAL, "cut must be 0, 1 or 2");
   if (cfg->n_micro < 1) return fail(SPA_EINVAL, "n_micro must be >= 1");
   if (cfg->handoff != 0 && cfg->handoff != 1) return fail(SPA_EINVAL, "handoff must be 0 (value waits) or 1 (events)");
+  if (cfg->graph != 0 && cfg->graph != 1) return fail(SPA_EINVAL, "graph must be 0 or 1");
+  if (cfg->graph && (a_full || b_full || a_slide || b_slide))
+    return fail(SPA_EUNSUPPORTED, "graph replay needs the temporal schedule: graph kernel nodes do not keep a CU mask");
   const bool any = a_full || b_full || a_slide || b_slide;
   const bool all = a_full && b_full && a_slide && b_slide;
   if (any && !all) return fail(SPA_EINVAL, "give both pools of every layer kind, or none");
@@ -264,6 +273,14 @@ static spa_status create_impl(spa_ctx* ctx, const spa_model_desc* m, const spa_p
     for (size_t i = 0; i < seen.size() && e == hipSuccess; ++i)
       e = hipEventCreateWithFlags(&p->ev_end[i], hipEventDisableTiming);
   }
+  if (e == hipSuccess && cfg->graph) {
+    e = hipStreamCreateWithFlags(&p->gstream, hipStreamNonBlocking);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&p->gev_in, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&p->gev_out, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipMalloc(&p->gacc, 2 * sizeof(unsigned long long));
+    if (e == hipSuccess) e = hipMemset(p->gacc, 0, 2 * sizeof(unsigned long long));
+    if (e == hipSuccess) e = hipDeviceSynchronize();
+  }
   if (e == hipSuccess) e = hipEventCreateWithFlags(&p->ev_start, hipEventDisableTiming);
   if (e == hipSuccess) e = hipEventCreateWithFlags(&p->ev_end_a, hipEventDisableTiming);
   if (e == hipSuccess) e = hipEventCreateWithFlags(&p->ev_end_b, hipEventDisableTiming);
@@ -295,6 +312,19 @@ static hipError_t reset_spans(spa_pipeline* p, int n) {
 }
 
 static spa_status harvest_timing(spa_pipeline* p) {
+  if (p->gacc) {   // graph replays: spans folded on the device by the graph's last kernel
+    unsigned long long acc[2] = {0, 0};
+    SPA_HIP(hipMemcpy(acc, p->gacc, sizeof(acc), hipMemcpyDeviceToHost));
+    if (acc[1] > 0) {
+      int khz = 0;
+      SPA_HIP(hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, p->ctx->device));
+      if (khz <= 0) return fail(SPA_EHIP, "device wall clock rate unknown");
+      p->t_sum_ms += (double)acc[0] / khz;
+      p->t_count += (int)acc[1];
+      SPA_HIP(hipMemset(p->gacc, 0, sizeof(acc)));
+      SPA_HIP(hipDeviceSynchronize());
+    }
+  }
   if (p->tspan_used > 0) {
     // spans: first workgroup start to last workgroup end, in wall-clock ticks
     int khz = 0;
@@ -380,6 +410,11 @@ static spa_status run_macro(spa_pipeline* p, const spa_layer* layers, const spa_
   return SPA_OK;
 }
 
+static spa_status enqueue_run(spa_pipeline* p, const spa_layer* layers, const spa_batch* b, void* ws,
+                              const WsLayout& W, int bm, hipStream_t cs, TimingHook* thp);
+static spa_status run_graph(spa_pipeline* p, const spa_layer* layers, const spa_batch* b, void* ws, size_t ws_bytes,
+                            const WsLayout& W, int bm, hipStream_t cs);
+
 spa_status spa_pipeline_run(spa_pipeline* p, const spa_layer* layers, const spa_batch* b, void* ws, size_t ws_bytes,
                             void* caller_stream) {
   if (!p || !layers || !b) return fail(SPA_EINVAL, "bad argument");
@@ -402,6 +437,7 @@ spa_status spa_pipeline_run(spa_pipeline* p, const spa_layer* layers, const spa_
   if (ws_bytes < W.total) return fail(SPA_EWORKSPACE, "workspace too small: need " + std::to_string(W.total));
 
   hipStream_t cs = (hipStream_t)caller_stream;
+  if (p->a == nullptr && p->cfg.graph && p->timed_mode != 2) return run_graph(p, layers, b, ws, ws_bytes, W, bm, cs);
   TimingHook th;
   th.cls = p->timed_cls;
   th.evs = &p->tevs;
@@ -412,7 +448,15 @@ spa_status spa_pipeline_run(spa_pipeline* p, const spa_layer* layers, const spa_
     th.span_cap = kSpanCap;
   }
   TimingHook* thp = p->timed_cls >= 0 ? &th : nullptr;
+  return enqueue_run(p, layers, b, ws, W, bm, cs, thp);
+}
 
+// One iteration enqueued: temporal on cs, or spatial on the pools' streams
+// joined to cs at both ends.
+static spa_status enqueue_run(spa_pipeline* p, const spa_layer* layers, const spa_batch* b, void* ws,
+                              const WsLayout& W, int bm, hipStream_t cs, TimingHook* thp) {
+  const spa_model_desc* m = &p->m;
+  const int n_micro = p->cfg.n_micro;
   spa_status rc = clear_errors(ws, cs);
   if (rc) return rc;
   const bool temporal = p->a == nullptr;
@@ -478,6 +522,80 @@ spa_status spa_pipeline_run(spa_pipeline* p, const spa_layer* layers, const spa_
   return SPA_OK;
 }
 
+// Everything a captured iteration's launches were built from.
+static std::vector<unsigned char> graph_key(const spa_pipeline* p, const spa_layer* layers, const spa_batch* b,
+                                            void* ws, size_t ws_bytes) {
+  std::vector<unsigned char> k;
+  auto put = [&](const void* x, size_t n) {
+    const unsigned char* c = static_cast<const unsigned char*>(x);
+    k.insert(k.end(), c, c + n);
+  };
+  put(layers, sizeof(spa_layer) * (size_t)p->m.n_layers);
+  put(b, sizeof(*b));
+  put(&ws, sizeof(ws));
+  put(&ws_bytes, sizeof(ws_bytes));
+  put(&p->timed_cls, sizeof(p->timed_cls));
+  put(&p->timed_mode, sizeof(p->timed_mode));
+  return k;
+}
+
+// Temporal iteration from a HIP graph: captured on the pipeline's own stream
+// when the arguments differ from the last capture, then launched there
+// between two event joins with the caller's stream. With the attention timer
+// on (device-clock spans), the captured launches record into fixed slots and
+// the graph's last kernel folds their spans into an accumulator and clears
+// them, so every replay is timed inside the graph itself.
+static spa_status run_graph(spa_pipeline* p, const spa_layer* layers, const spa_batch* b, void* ws, size_t ws_bytes,
+                            const WsLayout& W, int bm, hipStream_t cs) {
+  std::vector<unsigned char> key = graph_key(p, layers, b, ws, ws_bytes);
+  if (!p->gexec || key != p->gkey) {
+    if (p->gexec) {
+      SPA_HIP(hipStreamSynchronize(p->gstream));
+      (void)hipGraphExecDestroy(p->gexec);
+      p->gexec = nullptr;
+    }
+    int n_spans = 0;
+    TimingHook th;
+    th.cls = p->timed_cls;
+    th.evs = &p->tevs;
+    th.pool = &p->tpool;
+    if (p->timed_mode == 1) {
+      th.span = p->tspan;
+      th.span_used = &n_spans;
+      th.span_cap = kSpanCap;
+    }
+    TimingHook* thp = p->timed_cls >= 0 ? &th : nullptr;
+    SPA_HIP(hipStreamBeginCapture(p->gstream, hipStreamCaptureModeThreadLocal));
+    spa_status rc = enqueue_run(p, layers, b, ws, W, bm, p->gstream, thp);
+    if (!rc && n_spans > 0) {
+      hipError_t e = launch_span_fold(p->tspan, n_spans, p->gacc, p->gstream);
+      if (e != hipSuccess) rc = hip_fail(e, "span fold");
+    }
+    hipGraph_t g = nullptr;
+    hipError_t ec = hipStreamEndCapture(p->gstream, &g);   // always end the capture
+    if (!rc && ec != hipSuccess) rc = hip_fail(ec, "hipStreamEndCapture");
+    if (!rc) {
+      hipError_t ei = hipGraphInstantiate(&p->gexec, g, nullptr, nullptr, 0);
+      if (ei != hipSuccess) {
+        p->gexec = nullptr;
+        rc = hip_fail(ei, "hipGraphInstantiate");
+      }
+    }
+    if (g) (void)hipGraphDestroy(g);
+    if (rc) {
+      (void)hipGetLastError();
+      return rc;
+    }
+    p->gkey = std::move(key);
+  }
+  SPA_HIP(hipEventRecord(p->gev_in, cs));
+  SPA_HIP(hipStreamWaitEvent(p->gstream, p->gev_in, 0));
+  SPA_HIP(hipGraphLaunch(p->gexec, p->gstream));
+  SPA_HIP(hipEventRecord(p->gev_out, p->gstream));
+  SPA_HIP(hipStreamWaitEvent(cs, p->gev_out, 0));
+  return SPA_OK;
+}
+
 spa_status spa_pipeline_time_kernel(spa_pipeline* p, int32_t cls, int32_t enable) {
   if (!p || cls < 0 || cls >= KC_COUNT || enable < 0 || enable > 2) return fail(SPA_EINVAL, "bad argument");
   if (!p->tevs.empty() || p->tspan_used > 0) {
@@ -531,6 +649,11 @@ spa_status spa_pipeline_destroy(spa_pipeline* p) {
   if (p->flags) (void)hipFree(p->flags);
   for (hipEvent_t e : p->ev_end)
     if (e) (void)hipEventDestroy(e);
+  if (p->gexec) (void)hipGraphExecDestroy(p->gexec);
+  if (p->gstream) (void)hipStreamDestroy(p->gstream);
+  if (p->gev_in) (void)hipEventDestroy(p->gev_in);
+  if (p->gev_out) (void)hipEventDestroy(p->gev_out);
+  if (p->gacc) (void)hipFree(p->gacc);
   if (p->ev_start) (void)hipEventDestroy(p->ev_start);
   if (p->ev_end_a) (void)hipEventDestroy(p->ev_end_a);
   if (p->ev_end_b) (void)hipEventDestroy(p->ev_end_b);

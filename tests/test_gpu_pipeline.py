@@ -119,6 +119,51 @@ def test_event_handoffs_give_the_same_bits(env, cut):
     np.testing.assert_array_equal(vt, ve)
 
 
+@pytest.mark.parametrize("n_micro", [1, 2])
+def test_graph_replay_equals_direct_launches(env, n_micro):
+    """A temporal iteration replayed from a captured HIP graph gives the bits
+    of direct launches, on every replay, with eager work (input resets)
+    between replays; with the attention timer on, every replayed launch is
+    timed."""
+    from spatially_pipelined_attention_amd.workload import Pipeline
+    B, dw, ctx = env["B"], env["dw"], env["ctx"]
+    print(f"[case] graph replay, T{n_micro}", flush=True)
+    xd, td, kd, vd = _run(env, 0, n_micro, None)
+    pipe = Pipeline(ctx, dw.m, {"cut": 0, "n_micro": n_micro, "cu_a": 0, "graph": 1})
+    ws = dw.workspace(n_micro=n_micro)
+    full = [l for l, k in enumerate(dw.wl.layer_kinds) if k == "full"]
+    try:
+        for rep in range(3):
+            if rep == 2:
+                B.spa_pipeline_time_kernel(pipe.h, B.KC_ATTN_FULL, 1)   # new arguments: captured again, timed
+            dw.reset_x()
+            dw.topk.zero_()
+            pipe.run(dw.layers_c, dw.batch, ws)
+            torch.cuda.synchronize()
+            assert B.spa_workspace_errors(ctx, ws) == 0
+            assert torch.equal(dw.x, xd) and torch.equal(dw.topk, td), f"replay {rep}"
+            kk, vv = dw.read_kv(full[0], list(range(dw.wl.batch)), [int(x) - 1 for x in dw.L])
+            np.testing.assert_array_equal(kk, kd)
+            np.testing.assert_array_equal(vv, vd)
+        ms, n = B.spa_pipeline_timing(pipe.h)
+        assert n == len(full) * n_micro and ms > 0
+    finally:
+        pipe.close()
+
+
+def test_graph_refused_for_spatial_pipelines(env):
+    B, ctx = env["B"], env["ctx"]
+    pa = B.spa_pool_create_split(ctx, 0, 128)
+    pb = B.spa_pool_create_split(ctx, 16, 128)
+    try:
+        with pytest.raises(B.SpaError) as ei:
+            B.spa_pipeline_create(ctx, env["dw"].m, B.spa_pipeline_cfg(0, 2, 0, 1), pa, pb)
+        assert ei.value.status == B.SPA_EUNSUPPORTED
+    finally:
+        B.spa_pool_destroy(pa)
+        B.spa_pool_destroy(pb)
+
+
 def test_repeat_runs_are_bitwise_identical(env):
     a = _run(env, 0, 2, 128)
     b = _run(env, 0, 2, 128)
