@@ -229,6 +229,9 @@ def main():
                     help="temporal schedules replay each iteration from a captured HIP graph (1) or launch "
                          "every kernel directly (0, the faster here: 6.38 against 6.79 ms per 36-layer T1 "
                          "iteration); spatial schedules always launch directly")
+    ap.add_argument("--head", type=int, choices=[0, 1], default=0,
+                    help="the MoE head (output projection finish .. gather) as separate launches (0, the faster "
+                         "here) or as one persistent launch where it applies (1)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="after timing, copy BYTES device bytes three times (a known-size kernel for counter scaling)")
     args = ap.parse_args()
@@ -272,7 +275,8 @@ def main():
 
     def make_pipe(cut, n_micro, cu_a, cu_s=None):
         return Pipeline(ctx, dw.m, {"cut": cut, "n_micro": n_micro, "cu_a": cu_a or 0, "cu_a_sliding": cu_s,
-                                    "handoff": 1 if args.handoff == "events" else 0, "graph": args.graph})
+                                    "handoff": 1 if args.handoff == "events" else 0, "graph": args.graph,
+                                    "head": args.head})
 
     results = {}
 

@@ -191,7 +191,9 @@ spa_status spa_workspace_query(const spa_model_desc* m, int32_t batch, int32_t m
 /* Prepare a fresh workspace (clears its counters); enqueued on `stream`. */
 spa_status spa_workspace_init(spa_ctx* ctx, const spa_model_desc* m, int32_t batch, int32_t max_kv_len,
                               int32_t n_micro, void* ws, size_t ws_bytes, void* stream);
-/* Device error bits found so far (1: a kv_len outside its cache); synchronises `stream`. */
+/* Device error bits found so far (1: a kv_len outside its cache; 2: a
+ * hand-off inside the one-launch MoE head did not complete within its
+ * polling bound, so that launch's results are invalid); synchronises `stream`. */
 spa_status spa_workspace_errors(spa_ctx* ctx, const void* ws, size_t ws_bytes, void* stream, int32_t* bits);
 
 /* -------------------------------------------------------------- KV cache */
@@ -396,6 +398,21 @@ typedef struct spa_pipeline_cfg {
    * Spatial pipelines refuse it (SPA_EUNSUPPORTED): graph kernel nodes do
    * not keep a stream's CU mask. 0 (default): direct launches. */
   int32_t graph;
+  /* 1: the MoE head - output projection finish, router GEMV, top-k, the
+   * dispatch permutation and the gather of the expert rows - as one
+   * persistent launch: up to 64 workgroups (at most one per CU of the
+   * stream's pool, so all are resident) run the four steps with device
+   * hand-offs between them (agent-scope release, an arrival counter,
+   * bounded polling, agent-scope acquire) instead of four dependent
+   * launches (the "persistent kernels" of section 6.1 of the paper). Same
+   * arithmetic as the separate kernels, same bits. Used wherever the output
+   * projection and the router share a stream (temporal schedules, cuts 1
+   * and 2), every stage has one pool, the virtual communication endpoints
+   * are off and the shapes fit its instances; elsewhere the separate
+   * launches run. On the 36-layer batch-64 workload the one launch took
+   * 36 us against 25 us for the four it replaces. 0 (default): the separate
+   * launches. */
+  int32_t head;
 } spa_pipeline_cfg;
 
 spa_status spa_pipeline_create(spa_ctx* ctx, const spa_model_desc* m, const spa_pipeline_cfg* cfg, spa_pool* stage_a,

@@ -61,7 +61,8 @@ class spa_route_bufs(C.Structure):
 
 
 class spa_pipeline_cfg(C.Structure):
-    _fields_ = [("cut", C.c_int32), ("n_micro", C.c_int32), ("handoff", C.c_int32), ("graph", C.c_int32)]
+    _fields_ = [("cut", C.c_int32), ("n_micro", C.c_int32), ("handoff", C.c_int32), ("graph", C.c_int32),
+                ("head", C.c_int32)]
 
 
 class spa_tune_space(C.Structure):

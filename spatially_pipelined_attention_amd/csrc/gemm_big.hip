@@ -56,7 +56,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_big(GemmArgs a) {
   const int wr = wave >> 1, wc = wave & 1;
 
   int s, nb, grp, rb, r0, nrows;
-  if (!gemm_block(a, kBigRows, lane, &s, &nb, &grp, &rb, &r0, &nrows)) return;
+  if (!gemm_block(a, kBigRows, lane, blockIdx.x, &s, &nb, &grp, &rb, &r0, &nrows)) return;
   const int rows_here = min(kBigRows, nrows - rb * kBigRows);
 
   constexpr int KS = WTraits<WT>::ks;

@@ -50,9 +50,8 @@ __device__ __forceinline__ int w_rows_total(const GemmArgs& a) {
 // row blocks of all groups in group order (wave-parallel scan of the per-group
 // block counts, two groups per lane). Returns false when the workgroup has no
 // rows (the whole workgroup returns: the result is wave-uniform).
-__device__ __forceinline__ bool gemm_block(const GemmArgs& a, int BR, int lane, int* s_out, int* nb_out, int* grp_out,
-                                           int* rb_out, int* r0_out, int* nrows_out) {
-  int bid = blockIdx.x;
+__device__ __forceinline__ bool gemm_block(const GemmArgs& a, int BR, int lane, int bid, int* s_out, int* nb_out,
+                                           int* grp_out, int* rb_out, int* r0_out, int* nrows_out) {
   const int s = bid % a.S;
   bid /= a.S;
   const int nb = bid % a.n_tiles;

@@ -280,6 +280,9 @@ Slot slot_ptrs(const WsLayout& L, void* ws, int slot) {
   const SlotLayout& o = L.s;
   s.base = b;
   s.err = (int*)((char*)ws + L.err);
+  // two hand-off counters of the MoE-head launch per slot, in the header
+  // words that every run clears (words 32..63: slots 0..15)
+  s.head_ctr = slot < 16 ? (unsigned*)((char*)ws + L.err) + 32 + 2 * slot : nullptr;
   s.xn = b + o.xn;
   s.q = b + o.q;
   s.o = b + o.o;
@@ -511,11 +514,15 @@ static spa_status op_attn(spa_ctx* ctx, const spa_model_desc* m, const spa_layer
   return SPA_OK;
 }
 
+static spa_status op_comm(spa_ctx* ctx, const spa_model_desc* m, const void* src, size_t copy_bytes, size_t bytes,
+                          const Slot& s, hipStream_t st, TimingHook* th);
+
 // Output proj + Add + Norm: h = x + o Wo^T, hn = RMSNorm(h) gamma2 (fp32, and
-// the expert input format when hn_bf16 / hn8 are given).
-static spa_status op_oproj(spa_ctx* ctx, const spa_model_desc* m, const spa_layer* l, const float* x, const void* o,
-                           int n_tok, float* h, float* hn, uint16_t* hn_bf16, uint8_t* hn8, float* hn8_scale,
-                           const Slot& s, hipStream_t st, TimingHook* th, bool kmajor = false) {
+// the expert input format when hn_bf16 / hn8 are given). The split product's
+// and the finish kernel's arguments.
+static void oproj_args(spa_ctx* ctx, const spa_model_desc* m, const spa_layer* l, const float* x, const void* o,
+                       int n_tok, float* h, float* hn, uint16_t* hn_bf16, uint8_t* hn8, float* hn8_scale,
+                       const Slot& s, bool kmajor, GemmArgs* ga, OprojFinishArgs* fa) {
   const GemmPlan p = plan_gemm(KC_OPROJ, m, n_tok, ctx->n_cus);
   GemmArgs a = gemm_args(p, s, n_tok);
   a.W = l->wo;
@@ -537,6 +544,16 @@ static spa_status op_oproj(spa_ctx* ctx, const spa_model_desc* m, const spa_laye
   f.hn_bf16 = hn_bf16;
   f.hn_e4m3 = hn8;
   f.hn_scale = hn8_scale;
+  *ga = a;
+  *fa = f;
+}
+
+static spa_status op_oproj(spa_ctx* ctx, const spa_model_desc* m, const spa_layer* l, const float* x, const void* o,
+                           int n_tok, float* h, float* hn, uint16_t* hn_bf16, uint8_t* hn8, float* hn8_scale,
+                           const Slot& s, hipStream_t st, TimingHook* th, bool kmajor = false) {
+  GemmArgs a;
+  OprojFinishArgs f;
+  oproj_args(ctx, m, l, x, o, n_tok, h, hn, hn_bf16, hn8, hn8_scale, s, kmajor, &a, &f);
   HookScope hs(th, KC_OPROJ, st);
   SPA_HIP(launch_gemm(m->dense_dtype, EPI_PARTIAL, a, st));
   SPA_HIP(launch_oproj_finish(f, st));
@@ -551,10 +568,11 @@ static const void* expert_input(const spa_model_desc* m, const Slot& s) {
 }
 
 // Router GEMV, top-k and the dispatch permutation. gather: also gather the
-// slot's expert input rows into dispatch order (s.xe_perm) in the same kernel.
-static spa_status op_route(spa_ctx* ctx, const spa_model_desc* m, const spa_layer* l, const float* hn, int n_tok,
-                           float* logits, const spa_route_bufs& r, int32_t* topk_rec, const Slot& s, hipStream_t st,
-                           TimingHook* th, bool gather = false) {
+// slot's expert input rows into dispatch order (s.xe_perm) in the same
+// kernel. The router product's and the routing kernels' arguments.
+static void route_args(spa_ctx* ctx, const spa_model_desc* m, const spa_layer* l, const float* hn, int n_tok,
+                       float* logits, const spa_route_bufs& r, int32_t* topk_rec, const Slot& s, bool gather,
+                       GemmArgs* ga, RouteArgs* ra_out, GemmPlan* plan) {
   const GemmPlan p = plan_gemm(KC_ROUTER, m, n_tok, ctx->n_cus);
   GemmArgs a = gemm_args(p, s, n_tok);
   a.W = l->wr;
@@ -587,9 +605,61 @@ static spa_status op_route(spa_ctx* ctx, const spa_model_desc* m, const spa_laye
     ra.gsrc_scale = fp8 ? s.hn8_scale : nullptr;
     ra.gdst_scale = fp8 ? s.xe_perm_scale : nullptr;
   }
+  *ga = a;
+  *ra_out = ra;
+  if (plan) *plan = p;
+}
+
+static spa_status op_route(spa_ctx* ctx, const spa_model_desc* m, const spa_layer* l, const float* hn, int n_tok,
+                           float* logits, const spa_route_bufs& r, int32_t* topk_rec, const Slot& s, hipStream_t st,
+                           TimingHook* th, bool gather = false) {
+  GemmArgs a;
+  RouteArgs ra;
+  route_args(ctx, m, l, hn, n_tok, logits, r, topk_rec, s, gather, &a, &ra, nullptr);
   HookScope hs(th, KC_ROUTER, st);
   SPA_HIP(launch_gemm(DT_F32, EPI_PARTIAL, a, st));
   SPA_HIP(launch_route(ra, st));
+  return SPA_OK;
+}
+
+// Output projection through the gather of the expert rows, with the MoE head
+// (finish, router, top-k, permutation and gather) as one persistent launch
+// after the output projection's split product: the same bits as the
+// separate launches. Those run instead when the head does not apply: no
+// counter slot, split counts or router rows outside its instances, the
+// virtual communication endpoints on (the all-reduce sits between the
+// projection and the router), or fuse false.
+static spa_status op_oproj_route(spa_ctx* ctx, const spa_model_desc* m, const spa_layer* l, const float* x, int n_tok,
+                                 const Slot& s, int32_t* rec, bool fuse, hipStream_t st, TimingHook* th) {
+  const bool fp8 = m->expert_dtype == SPA_E4M3, ebf = m->expert_dtype == SPA_BF16;
+  MoeHeadArgs h;
+  memset(&h, 0, sizeof(h));
+  GemmArgs oa;
+  GemmPlan rp;
+  oproj_args(ctx, m, l, x, s.o, n_tok, s.h, s.hn_f32, ebf ? s.hn_bf16 : nullptr, fp8 ? s.hn8 : nullptr,
+             fp8 ? s.hn8_scale : nullptr, s, true, &oa, &h.of);
+  route_args(ctx, m, l, s.hn_f32, n_tok, s.logits, s.route, rec, s, true, &h.router, &h.ra, &rp);
+  const bool use = fuse && s.head_ctr && !comm_enabled(m) && moe_head_supported(h.of.pv.S, h.ra.pv.S, rp.blk_rows);
+  if (!use) {
+    spa_status rc = op_oproj(ctx, m, l, x, s.o, n_tok, s.h, s.hn_f32, ebf ? s.hn_bf16 : nullptr, fp8 ? s.hn8 : nullptr,
+                             fp8 ? s.hn8_scale : nullptr, s, st, th, true);
+    if (rc) return rc;
+    const size_t ar = comm_bytes_allreduce(m, n_tok);
+    if ((rc = op_comm(ctx, m, s.h, ar, ar, s, st, th))) return rc;   // attention all-reduce
+    return op_route(ctx, m, l, s.hn_f32, n_tok, s.logits, s.route, rec, s, st, th, true);
+  }
+  h.n_router_tiles = rp.n_tiles * rp.rb_stride * rp.S;
+  h.ctr = s.head_ctr;
+  h.err = s.err;
+  // at most one workgroup per CU of the stream's pool, so every workgroup is
+  // resident while the others wait at a hand-off
+  const int G = std::max(1, std::min(64, stream_cus(st, ctx->n_cus)));
+  {
+    HookScope hs(th, KC_OPROJ, st);
+    SPA_HIP(launch_gemm(m->dense_dtype, EPI_PARTIAL, oa, st));
+  }
+  HookScope hs(th, KC_ROUTER, st);
+  SPA_HIP(launch_moe_head(h, G, st));
   return SPA_OK;
 }
 
@@ -714,7 +784,8 @@ static spa_status op_comm(spa_ctx* ctx, const spa_model_desc* m, const void* src
 // ---------------------------------------------------------------------------
 spa_status run_segment_a(spa_ctx* ctx, const spa_model_desc* m, const spa_layer* l, int layer_index,
                          const spa_layer* next, const spa_batch* b, int tok0, int n_tok, const WsLayout& W,
-                         const Slot& s, bool with_router, bool first_layer, hipStream_t st, TimingHook* th) {
+                         const Slot& s, bool with_router, bool first_layer, hipStream_t st, TimingHook* th,
+                         bool fuse_head) {
   (void)next;
   spa_status rc;
   float* x = b->x + (size_t)tok0 * m->hidden;
@@ -724,17 +795,16 @@ spa_status run_segment_a(spa_ctx* ctx, const spa_model_desc* m, const spa_layer*
   }
   if ((rc = op_qkv(ctx, m, l, b, tok0, n_tok, s.xn, s.q, s, st, th, true))) return rc;
   if ((rc = op_attn(ctx, m, l, b, tok0, n_tok, s.q, s.o, W, s, st, th, true))) return rc;
+  if (with_router) {
+    int32_t* rec = b->topk_out ? b->topk_out + ((size_t)layer_index * b->batch + tok0) * m->top_k : nullptr;
+    return op_oproj_route(ctx, m, l, x, n_tok, s, rec, fuse_head, st, th);
+  }
   const bool fp8 = m->expert_dtype == SPA_E4M3, ebf = m->expert_dtype == SPA_BF16;
   if ((rc = op_oproj(ctx, m, l, x, s.o, n_tok, s.h, s.hn_f32, ebf ? s.hn_bf16 : nullptr, fp8 ? s.hn8 : nullptr,
                      fp8 ? s.hn8_scale : nullptr, s, st, th, true)))
     return rc;
   const size_t ar = comm_bytes_allreduce(m, n_tok);
-  if ((rc = op_comm(ctx, m, s.h, ar, ar, s, st, th))) return rc;   // attention all-reduce
-  if (with_router) {
-    int32_t* rec = b->topk_out ? b->topk_out + ((size_t)layer_index * b->batch + tok0) * m->top_k : nullptr;
-    if ((rc = op_route(ctx, m, l, s.hn_f32, n_tok, s.logits, s.route, rec, s, st, th, true))) return rc;
-  }
-  return SPA_OK;
+  return op_comm(ctx, m, s.h, ar, ar, s, st, th);   // attention all-reduce
 }
 
 // The layer in three pieces around its attention (the Macro cut):
@@ -759,16 +829,12 @@ spa_status run_layer_attn(spa_ctx* ctx, const spa_model_desc* m, const spa_layer
 
 spa_status run_layer_after_attn(spa_ctx* ctx, const spa_model_desc* m, const spa_layer* l, int layer_index,
                                 const spa_layer* next, const spa_batch* b, int tok0, int n_tok, const WsLayout& W,
-                                const Slot& s, hipStream_t st, TimingHook* th) {
+                                const Slot& s, hipStream_t st, TimingHook* th, bool fuse_head) {
   spa_status rc;
   float* x = b->x + (size_t)tok0 * m->hidden;
-  const bool fp8 = m->expert_dtype == SPA_E4M3, ebf = m->expert_dtype == SPA_BF16;
-  if ((rc = op_oproj(ctx, m, l, x, s.o, n_tok, s.h, s.hn_f32, ebf ? s.hn_bf16 : nullptr, fp8 ? s.hn8 : nullptr,
-                     fp8 ? s.hn8_scale : nullptr, s, st, th, true)))
-    return rc;
-  const size_t ar = comm_bytes_allreduce(m, n_tok);
-  if ((rc = op_comm(ctx, m, s.h, ar, ar, s, st, th))) return rc;   // attention all-reduce
-  return run_segment_b(ctx, m, l, layer_index, next, b, tok0, n_tok, W, s, false, st, th);
+  int32_t* rec = b->topk_out ? b->topk_out + ((size_t)layer_index * b->batch + tok0) * m->top_k : nullptr;
+  if ((rc = op_oproj_route(ctx, m, l, x, n_tok, s, rec, fuse_head, st, th))) return rc;
+  return run_segment_b(ctx, m, l, layer_index, next, b, tok0, n_tok, W, s, true, st, th);
 }
 
 spa_status run_segment_b(spa_ctx* ctx, const spa_model_desc* m, const spa_layer* l, int layer_index,
@@ -1173,8 +1239,9 @@ spa_status spa_layer_forward(spa_ctx* ctx, const spa_model_desc* m, const spa_la
   if (layer_index < 0 || layer_index >= m->n_layers) return fail(SPA_EINVAL, "layer_index out of range");
   const int max_kv = b->max_kv_len;
   SPA_OP_PROLOGUE(n_tok)
-  if ((rc = run_segment_a(ctx, m, l, layer_index, nullptr, b, tok0, n_tok, W, s, false, true, st, nullptr))) return rc;
-  return run_segment_b(ctx, m, l, layer_index, nullptr, b, tok0, n_tok, W, s, false, st, nullptr);
+  if ((rc = run_segment_a(ctx, m, l, layer_index, nullptr, b, tok0, n_tok, W, s, true, true, st, nullptr, false)))
+    return rc;
+  return run_segment_b(ctx, m, l, layer_index, nullptr, b, tok0, n_tok, W, s, true, st, nullptr);
 }
 
 spa_status spa_temporal_run(spa_ctx* ctx, const spa_model_desc* m, const spa_layer* layers, const spa_batch* b,
@@ -1198,9 +1265,9 @@ spa_status spa_temporal_run(spa_ctx* ctx, const spa_model_desc* m, const spa_lay
     const spa_layer* next = li + 1 < m->n_layers ? &layers[li + 1] : nullptr;
     for (int mu = 0; mu < n_micro; ++mu) {
       Slot s = slot_ptrs(W, ws, mu);
-      if ((rc = run_segment_a(ctx, m, &layers[li], li, next, b, mu * bm, bm, W, s, false, li == 0, st, nullptr)))
+      if ((rc = run_segment_a(ctx, m, &layers[li], li, next, b, mu * bm, bm, W, s, true, li == 0, st, nullptr, false)))
         return rc;
-      if ((rc = run_segment_b(ctx, m, &layers[li], li, next, b, mu * bm, bm, W, s, false, st, nullptr))) return rc;
+      if ((rc = run_segment_b(ctx, m, &layers[li], li, next, b, mu * bm, bm, W, s, true, st, nullptr))) return rc;
     }
   }
   return SPA_OK;

@@ -98,6 +98,7 @@ int stream_cus(hipStream_t st, int fallback);
 struct Slot {
   char* base;
   int* err;
+  unsigned* head_ctr;   // two zeroed counters for the MoE-head launch's hand-offs (null: none)
   void* xn;
   void* q;
   void* o;
@@ -135,9 +136,12 @@ struct TimingHook {
 };
 
 // The layer's pieces on one slot (tokens [tok0, tok0+n_tok)); enqueue on st.
+// with_router: segment A also routes (output projection through the gather);
+// fuse_head: that part may run as the one-launch MoE head.
 spa_status run_segment_a(spa_ctx* ctx, const spa_model_desc* m, const spa_layer* l, int layer_index,
                          const spa_layer* next, const spa_batch* b, int tok0, int n_tok, const WsLayout& W,
-                         const Slot& s, bool with_router, bool first_layer, hipStream_t st, TimingHook* th);
+                         const Slot& s, bool with_router, bool first_layer, hipStream_t st, TimingHook* th,
+                         bool fuse_head = false);
 spa_status run_segment_b(spa_ctx* ctx, const spa_model_desc* m, const spa_layer* l, int layer_index,
                          const spa_layer* next, const spa_batch* b, int tok0, int n_tok, const WsLayout& W,
                          const Slot& s, bool with_router, hipStream_t st, TimingHook* th);
@@ -150,7 +154,7 @@ spa_status run_layer_attn(spa_ctx* ctx, const spa_model_desc* m, const spa_layer
                           int n_tok, const WsLayout& W, const Slot& s, hipStream_t st, TimingHook* th);
 spa_status run_layer_after_attn(spa_ctx* ctx, const spa_model_desc* m, const spa_layer* l, int layer_index,
                                 const spa_layer* next, const spa_batch* b, int tok0, int n_tok, const WsLayout& W,
-                                const Slot& s, hipStream_t st, TimingHook* th);
+                                const Slot& s, hipStream_t st, TimingHook* th, bool fuse_head = false);
 spa_status clear_errors(void* ws, hipStream_t st);
 
 }  // namespace spa

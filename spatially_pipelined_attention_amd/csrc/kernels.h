@@ -12,7 +12,7 @@ enum Epi : int { EPI_PARTIAL = 0, EPI_SWIGLU = 1, EPI_STORE = 2 };
 enum KvKind : int { KV_RING = 0, KV_PACKED = 1 };
 
 // device-side error bits (workspace error word)
-enum : int { ERR_KV_LEN = 1 };
+enum : int { ERR_KV_LEN = 1, ERR_HANDOFF = 2 };
 
 // Split-K partial products: fp32 [split][rows][ld]; rows are token rows of a
 // dense product or dispatch rows of a grouped one, ld the padded column count.
@@ -121,6 +121,22 @@ struct RouteArgs {
   float* gdst_scale;        // E4M3: per dispatch row
 };
 hipError_t launch_route(const RouteArgs& a, hipStream_t st);
+
+// The MoE head (output projection finish, router GEMV, top-k, permutation and
+// gather) as one persistent launch of G workgroups of 1024 threads with
+// device hand-offs between its phases (misc.hip). ctr: two zeroed counters,
+// cleared again by the launch itself; err: device error word (ERR_HANDOFF).
+struct MoeHeadArgs {
+  OprojFinishArgs of;       // phase 0
+  GemmArgs router;          // phase 1: the router product (fp32 16-column tiles, split partials)
+  int n_router_tiles;       // its tiles: n_tiles * rb_stride * S
+  RouteArgs ra;             // phases 2 and 3 (ra.pv: the router partials)
+  unsigned* ctr;
+  int* err;
+};
+// splits of the output projection and the router, rows per router block
+bool moe_head_supported(int oproj_splits, int router_splits, int router_blk_rows);
+hipError_t launch_moe_head(const MoeHeadArgs& a, int G, hipStream_t st);
 
 // x_out = h + sum_s w[s] * y[inv[s]]; optionally xn = RMSNorm(x_out) * gamma
 // for the next projection. y is plain [R][H] or split partials of the

@@ -18,6 +18,7 @@
 #include <algorithm>
 
 #include "common.h"
+#include "gemm_tile.h"
 #include "kernels.h"
 
 namespace spa {
@@ -146,10 +147,10 @@ hipError_t launch_qkv_finish(const QkvFinishArgs& a, hipStream_t st) {
 }
 
 // ---------------------------------------------------------------------------
+// Output projection finish of token row r by a kRowThreads workgroup (red:
+// kRowThreads / 64 floats of LDS).
 template <int SM>
-__global__ __launch_bounds__(kRowThreads) void k_oproj_finish(OprojFinishArgs a) {
-  __shared__ float red[kRowThreads / 64];
-  const int r = blockIdx.x;
+__device__ __forceinline__ void oproj_finish_row(const OprojFinishArgs& a, int r, float* red) {
   const long long row = (long long)r * a.H;
   float h[kRowCols];
   float ss = 0.f;
@@ -196,6 +197,12 @@ __global__ __launch_bounds__(kRowThreads) void k_oproj_finish(OprojFinishArgs a)
       if (c < a.H) a.hn_e4m3[row + c] = f32_to_e4m3(h[i] * inv_s);
     }
   }
+}
+
+template <int SM>
+__global__ __launch_bounds__(kRowThreads) void k_oproj_finish(OprojFinishArgs a) {
+  __shared__ float red[kRowThreads / 64];
+  oproj_finish_row<SM>(a, blockIdx.x, red);
 }
 
 hipError_t launch_oproj_finish(const OprojFinishArgs& a, hipStream_t st) {
@@ -381,14 +388,6 @@ int route_lds_bytes(int n_tok, int k, int E_res) {
   return (2 * P + 2 * E_res + 1) * 4 + 16 + E_res * ((P + 63) / 64) * 8;
 }
 
-// Kernel attributes set once per process before any launch (not inside a
-// stream capture): the permutation may need more than the default 64 KB of LDS.
-hipError_t init_kernel_attributes() {
-  static hipError_t e = hipFuncSetAttribute((const void*)k_route_permute, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                            160 * 1024);
-  return e;
-}
-
 hipError_t launch_route(const RouteArgs& a, hipStream_t st) {
   (void)init_kernel_attributes();
   int wgs = 1;
@@ -402,6 +401,156 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t st) {
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_route_permute, dim3(wgs), dim3(256), lds, st, a);
   return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// The MoE head as one persistent launch: a stage worker whose G resident
+// workgroups (kRowThreads threads each, G at most one per CU of the stream's
+// pool, so all are resident at once) run four phases with device hand-offs
+// between them, instead of four dependent launches:
+//   0. output projection finish (h, hn and the expert input rows), token rows
+//      dealt over the workgroups;
+//   1. router GEMV tiles: the tiles of the router product, four 256-thread
+//      groups of a workgroup each running one (the same tile arithmetic as
+//      the separate router launch), in lockstep;
+//   2. router top-k and softmax, one wave per token;
+//   3. dispatch permutation and gather of the expert input rows (every
+//      workgroup computes the permutation, workgroup 0 stores it, the gather
+//      is dealt over the workgroups).
+// Every phase reuses the separate kernels' device code, so the results are
+// those of the separate launches bit for bit, whatever G is. Hand-off: each
+// workgroup finishes its stores, releases them at agent scope (the L2s of
+// the XCDs are not coherent with each other) and adds one to an arrival
+// counter; it then polls the counter (relaxed) until every workgroup of the
+// phase has arrived and acquires at agent scope. The polls are bounded: past
+// the limit the kernel sets the error bit and goes on rather than waiting
+// forever. The last workgroup to leave clears the counters for the next
+// launch.
+constexpr unsigned kHeadSpinLimit = 1u << 22;
+
+__device__ __forceinline__ void head_barrier(unsigned* ctr, unsigned target, int* err) {
+  __builtin_amdgcn_s_waitcnt(0);   // this wave's stores have completed
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    unsigned spins = 0;
+    while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+      if (++spins > kHeadSpinLimit) {
+        atomicOr(err, ERR_HANDOFF);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(2);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  }
+  __syncthreads();
+}
+
+template <int MT>
+__device__ __forceinline__ void gemm_tile_idle() {   // the barriers of one gemm_tile<.., MT> call
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    __syncthreads();
+    __syncthreads();
+  }
+}
+
+template <int SM0, int SM2, int MT>
+__global__ __launch_bounds__(kRowThreads) void k_moe_head(MoeHeadArgs a) {
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  const unsigned G = gridDim.x;
+  // 0: output projection finish
+  for (int r = blockIdx.x; r < a.of.n_tok; r += G) oproj_finish_row<SM0>(a.of, r, (float*)lds);
+  head_barrier(a.ctr, G, a.err);
+  // 1: router product tiles, four 256-thread groups per workgroup
+  {
+    const int grp = threadIdx.x >> 8, tid = threadIdx.x & 255;
+    char* red = lds + grp * gemm_red_bytes<1>();
+    // tile t0 + grp * G + blockIdx.x: spread over the workgroups first
+    for (int t0 = 0; t0 < a.n_router_tiles; t0 += 4 * (int)G) {
+      const int t = t0 + grp * (int)G + blockIdx.x;
+      if (t < a.n_router_tiles) gemm_tile<DT_F32, EPI_PARTIAL, 1, MT, 2>(a.router, t, tid, red);   // 2-deep ring: 1024-thread register budget
+      else gemm_tile_idle<MT>();
+    }
+  }
+  head_barrier(a.ctr, 2 * G, a.err);
+  // 2: top-k and softmax weights, one wave per token
+  {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    for (int t = blockIdx.x * (kRowThreads / 64) + wave; t < a.ra.n_tok; t += G * (kRowThreads / 64)) {
+      float pv[8];
+      int pi[8];
+      route_token<SM2>(a.ra, t, lane, true, pv, pi);
+      store_picks(a.ra, t, lane, pv, pi);
+    }
+  }
+  head_barrier(a.ctr, 3 * G, a.err);
+  // 3: permutation and gather
+  {
+    int* grp = (int*)lds;
+    const int P = a.ra.n_tok * a.ra.k;
+    for (int p = threadIdx.x; p < P; p += blockDim.x) grp[p] = a.ra.topk_idx[p] % a.ra.E_res;
+    __syncthreads();
+    permute_body(a.ra, lds);
+  }
+  // the last workgroup out clears the counters (every workgroup is past its polls)
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const unsigned prev = __hip_atomic_fetch_add(a.ctr + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (prev == G - 1) {
+      __hip_atomic_store(a.ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(a.ctr + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
+int moe_head_lds_bytes(int n_tok, int k, int E_res) {
+  return std::max({4 * gemm_red_bytes<1>(), route_lds_bytes(n_tok, k, E_res), (int)(kRowThreads / 64 * sizeof(float))});
+}
+
+template <int SM0, int MT>
+static hipError_t launch_head_t(const MoeHeadArgs& a, int G, int lds, hipStream_t st) {
+  hipLaunchKernelGGL((k_moe_head<SM0, 16, MT>), dim3(G), dim3(kRowThreads), lds, st, a);
+  return hipGetLastError();
+}
+
+bool moe_head_supported(int oproj_splits, int router_splits, int router_blk_rows) {
+  return oproj_splits > 2 && oproj_splits <= 16 && router_splits > 8 && router_splits <= 16 &&
+         (router_blk_rows == 16 || router_blk_rows == 32 || router_blk_rows == 64);
+}
+
+hipError_t launch_moe_head(const MoeHeadArgs& a, int G, hipStream_t st) {
+  if (!moe_head_supported(a.of.pv.S, a.ra.pv.S, a.router.blk_rows) || G < 1) return hipErrorInvalidValue;
+  const int lds = moe_head_lds_bytes(a.ra.n_tok, a.ra.k, a.ra.E_res);
+  const int S0 = a.of.pv.S;
+#define SPA_HEAD(SMV)                                                      \
+  switch (a.router.blk_rows) {                                             \
+    case 16: return launch_head_t<SMV, 1>(a, G, lds, st);                 \
+    case 32: return launch_head_t<SMV, 2>(a, G, lds, st);                 \
+    default: return launch_head_t<SMV, 4>(a, G, lds, st);                 \
+  }
+  if (S0 <= 4) { SPA_HEAD(4) }
+  if (S0 <= 8) { SPA_HEAD(8) }
+  SPA_HEAD(16)
+#undef SPA_HEAD
+}
+
+// Kernel attributes set once per process before any launch (not inside a
+// stream capture): the permutation may need more than the default 64 KB of LDS.
+hipError_t init_kernel_attributes() {
+  static hipError_t e = [] {
+    hipError_t r = hipFuncSetAttribute((const void*)k_route_permute, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       160 * 1024);
+    for (const void* f : {(const void*)k_moe_head<4, 16, 1>, (const void*)k_moe_head<4, 16, 2>,
+                          (const void*)k_moe_head<4, 16, 4>, (const void*)k_moe_head<8, 16, 1>,
+                          (const void*)k_moe_head<8, 16, 2>, (const void*)k_moe_head<8, 16, 4>,
+                          (const void*)k_moe_head<16, 16, 1>, (const void*)k_moe_head<16, 16, 2>,
+                          (const void*)k_moe_head<16, 16, 4>})
+      if (r == hipSuccess) r = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    return r;
+  }();
+  return e;
 }
 
 // ---------------------------------------------------------------------------

@@ -226,6 +226,7 @@ static spa_status create_impl(spa_ctx* ctx, const spa_model_desc* m, const spa_p
   if (cfg->n_micro < 1) return fail(SPA_EINVAL, "n_micro must be >= 1");
   if (cfg->handoff != 0 && cfg->handoff != 1) return fail(SPA_EINVAL, "handoff must be 0 (value waits) or 1 (events)");
   if (cfg->graph != 0 && cfg->graph != 1) return fail(SPA_EINVAL, "graph must be 0 or 1");
+  if (cfg->head != 0 && cfg->head != 1) return fail(SPA_EINVAL, "head must be 0 (separate launches) or 1 (one launch)");
   if (cfg->graph && (a_full || b_full || a_slide || b_slide))
     return fail(SPA_EUNSUPPORTED, "graph replay needs the temporal schedule: graph kernel nodes do not keep a CU mask");
   const bool any = a_full || b_full || a_slide || b_slide;
@@ -357,6 +358,16 @@ static spa_status harvest_timing(spa_pipeline* p) {
   return SPA_OK;
 }
 
+// Whether the MoE head runs as one persistent launch: asked for, and its
+// workgroups wait for each other, so no other such launch may compete for
+// the same CUs - true when every stage has one pool (a stream runs its tasks
+// one at a time and the stages' pools are disjoint) or the schedule is
+// temporal.
+static bool head_fusable(const spa_pipeline* p) {
+  if (p->cfg.head != 1) return false;
+  return p->a == nullptr || (p->ak[SPA_FULL] == p->ak[SPA_SLIDING] && p->bk[SPA_FULL] == p->bk[SPA_SLIDING]);
+}
+
 // The Macro cut (P1 section 5.3.2): stage A runs only the full-attention
 // launches; stage B runs everything else. For each full layer F, microbatch
 // mu's stage-B segment is: what follows the previous full layer's attention
@@ -383,13 +394,16 @@ static spa_status run_macro(spa_pipeline* p, const spa_layer* layers, const spa_
       if (prev >= 0) {
         if (vs) SPA_HIP(hipStreamWaitValue64(sb, done_a + mu, base + (uint64_t)prev + 1, hipStreamWaitValueGte, ~0ull));
         else SPA_HIP(hipStreamWaitEvent(sb, p->evA[(size_t)prev * n_micro + mu], 0));
-        if ((rc = run_layer_after_attn(p->ctx, m, &layers[prev], prev, next_of(prev), b, tok0, bm, W, s, sb, thp)))
+        if ((rc = run_layer_after_attn(p->ctx, m, &layers[prev], prev, next_of(prev), b, tok0, bm, W, s, sb, thp,
+                                       head_fusable(p))))
           return rc;
       }
       for (int l = prev + 1; l < F; ++l) {   // the layers in between run whole on stage B
         if ((rc = run_layer_before_attn(p->ctx, m, &layers[l], b, tok0, bm, s, l == 0, sb, thp))) return rc;
         if ((rc = run_layer_attn(p->ctx, m, &layers[l], b, tok0, bm, W, s, sb, thp))) return rc;
-        if ((rc = run_layer_after_attn(p->ctx, m, &layers[l], l, next_of(l), b, tok0, bm, W, s, sb, thp))) return rc;
+        if ((rc = run_layer_after_attn(p->ctx, m, &layers[l], l, next_of(l), b, tok0, bm, W, s, sb, thp,
+                                       head_fusable(p))))
+          return rc;
       }
       if (end) continue;
       if ((rc = run_layer_before_attn(p->ctx, m, &layers[F], b, tok0, bm, s, F == 0, sb, thp))) return rc;
@@ -460,7 +474,10 @@ static spa_status enqueue_run(spa_pipeline* p, const spa_layer* layers, const sp
   spa_status rc = clear_errors(ws, cs);
   if (rc) return rc;
   const bool temporal = p->a == nullptr;
-  const bool router_in_a = p->cfg.cut == 1;
+  // temporal: both segments share the stream, so the router may run in
+  // segment A (where the output projection is) at no change to the results
+  const bool router_in_a = temporal || p->cfg.cut == 1;
+  const bool fuse = head_fusable(p);
   // stage streams of a layer (its kind's pools); the distinct streams for the joins
   auto stream_a = [&](const spa_layer* l) { return temporal ? cs : p->ak[l->kind == SPA_FULL ? SPA_FULL : SPA_SLIDING]->stream; };
   auto stream_b = [&](const spa_layer* l) { return temporal ? cs : p->bk[l->kind == SPA_FULL ? SPA_FULL : SPA_SLIDING]->stream; };
@@ -498,7 +515,7 @@ static spa_status enqueue_run(spa_pipeline* p, const spa_layer* layers, const sp
         else SPA_HIP(hipStreamWaitEvent(sa, p->evB[ei - n_micro], 0));
       }
       const spa_layer* next = l + 1 < m->n_layers ? &layers[l + 1] : nullptr;
-      rc = run_segment_a(p->ctx, m, &layers[l], l, next, b, mu * bm, bm, W, s, router_in_a, l == 0, sa, thp);
+      rc = run_segment_a(p->ctx, m, &layers[l], l, next, b, mu * bm, bm, W, s, router_in_a, l == 0, sa, thp, fuse);
       if (rc) return rc;
       if (vs) {
         SPA_HIP(hipStreamWriteValue64(sa, done_a + mu, tick, 0));

@@ -235,14 +235,15 @@ class DeviceWorkload:
 
 class Pipeline:
     """A pipeline (and the CU pools it owns) from a configuration dict:
-    {"cut", "n_micro", "cu_a"[, "cu_a_sliding", "handoff", "graph"]}; cu_a = None or 0 gives the
+    {"cut", "n_micro", "cu_a"[, "cu_a_sliding", "handoff", "graph", "head"]}; cu_a = None or 0 gives the
     temporal schedule with the same microbatches. Stage A takes the first
     cu_a CUs of every XCD's share, stage B the rest."""
 
     def __init__(self, ctx, m: B.spa_model_desc, cfg: dict, verify: bool = True):
         self.pools = []
         n_cus = B.spa_device_cus(ctx)
-        c = B.spa_pipeline_cfg(int(cfg["cut"]), int(cfg["n_micro"]), int(cfg.get("handoff", 0)), 0)
+        c = B.spa_pipeline_cfg(int(cfg["cut"]), int(cfg["n_micro"]), int(cfg.get("handoff", 0)), 0,
+                               int(cfg.get("head", 0)))
         cu_a = cfg.get("cu_a") or 0
         if cu_a <= 0:
             c.graph = int(cfg.get("graph", 0))   # graph replay: temporal schedules only

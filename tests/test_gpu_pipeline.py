@@ -164,6 +164,32 @@ def test_graph_refused_for_spatial_pipelines(env):
         B.spa_pool_destroy(pb)
 
 
+@pytest.mark.parametrize("cut,n_micro,cu_a", [(0, 1, None), (0, 2, None), (2, 2, 128), (1, 2, 96)])
+def test_one_launch_moe_head_equals_separate_launches(env, cut, n_micro, cu_a):
+    """The MoE head as one persistent launch (output projection finish,
+    router GEMV, top-k, permutation and gather with device hand-offs) gives
+    the bits of the separate launches; no hand-off runs out of its polling
+    bound (error bit 2)."""
+    from spatially_pipelined_attention_amd.workload import Pipeline
+    B, dw, ctx = env["B"], env["dw"], env["ctx"]
+    print(f"[case] one-launch head: cut={cut} m={n_micro} cu_a={cu_a}", flush=True)
+    out = []
+    for head in (0, 1):
+        pipe = Pipeline(ctx, dw.m, {"cut": cut, "n_micro": n_micro, "cu_a": cu_a or 0, "head": head})
+        ws = dw.workspace(n_micro=n_micro)
+        try:
+            for _ in range(2):   # the counters are left clear for the next launch
+                dw.reset_x()
+                dw.topk.zero_()
+                pipe.run(dw.layers_c, dw.batch, ws)
+                torch.cuda.synchronize()
+                assert B.spa_workspace_errors(ctx, ws) == 0
+        finally:
+            pipe.close()
+        out.append((dw.x.clone(), dw.topk.clone()))
+    assert torch.equal(out[0][0], out[1][0]) and torch.equal(out[0][1], out[1][1])
+
+
 def test_repeat_runs_are_bitwise_identical(env):
     a = _run(env, 0, 2, 128)
     b = _run(env, 0, 2, 128)
