@@ -236,10 +236,14 @@ spa_status spa_qkv_append(spa_ctx* ctx, const spa_model_desc* m, const spa_layer
 
 /* Figure 3 "FMHA" (section 5.1: sliding or full): grouped-query decode
  * attention with sinks over the cached window; q [n_tok][Hq*D] and o_out
- * [n_tok][Hq*D] in kv_dtype. Split-KV: a window is cut into equal chunks of
- * at most 4096 .. 512 positions (the largest cap that still gives two
- * workgroups per CU at the batch's longest sequence), whose partial softmax
- * states are merged with the sink in chunk order. */
+ * [n_tok][Hq*D] in kv_dtype. Split-KV, partial softmax states merged with the
+ * sink in window order. Full layers of up to 256 tokens: the call's windows,
+ * laid end to end as 32-position blocks, are cut into 2 x (device CUs) equal
+ * ranges, so a window may be cut anywhere and a token's last bits depend on
+ * the other tokens' lengths in the call (never on the CU pool). Other calls:
+ * a window is cut into equal chunks of at most 4096 .. 512 positions (the
+ * largest cap that still gives two workgroups per CU at the batch's longest
+ * sequence). */
 spa_status spa_decode_attn(spa_ctx* ctx, const spa_model_desc* m, const spa_layer* l, const spa_batch* b,
                            int32_t tok0, int32_t n_tok, const void* q, void* o_out, void* ws, size_t ws_bytes,
                            void* stream);
@@ -247,9 +251,12 @@ spa_status spa_decode_attn(spa_ctx* ctx, const spa_model_desc* m, const spa_laye
 /* spa_decode_attn for callers that cannot allocate device memory (code
  * under stream capture, tight serving loops, harnesses that forbid
  * allocation): the same operator, kernels and results, with no workspace.
- * Its scratch (the per-chunk softmax partials) lives in a fixed array of
- * the library, one per GPU, held until the process ends: at most 16 MiB of
- * partials, n_tok * Hkv * chunks * (Hq/Hkv) * (D + 2) * 4 bytes, where
+ * Its scratch (the softmax partials of the pieces) lives in a fixed array
+ * of the library, one per GPU, held until the process ends: at most 16 MiB of
+ * partials. A full layer of up to 256 tokens needs
+ * (2 * CUs + n_tok * Hkv) * (Hq/Hkv) * (D + 2) * 4 + n_tok * Hkv * 8 bytes
+ * (5.4 MB at 256 tokens on 256 CUs); other calls need
+ * n_tok * Hkv * chunks * (Hq/Hkv) * (D + 2) * 4 bytes, where
  * chunks = ceil(max_kv_len / chunk) for full layers (the chunk is 4096 ..
  * 512 positions, chosen from the shapes as in spa_decode_attn) and
  * ceil(window / 512) for sliding layers. A call that needs more returns

@@ -2,9 +2,11 @@
 // Figure 3 of the SubGPU Pipelining paper; full and sliding-window layers as
 // in its section 5.1).
 //
-// Work item = (sequence, KV head, chunk): a window of L positions is cut into
-// ceil(L / chunk) chunks of equal numbers of 32-position blocks. The 4 waves
-// of a workgroup take the blocks of their chunk round-robin:
+// Work item = a piece of one (sequence, KV head) window: a range of its
+// 32-position blocks. k_attn cuts a window of L positions into ceil(L / chunk)
+// chunks of equal block counts; k_attn_dealt cuts the launch's blocks into
+// equal ranges (see there). The 4 waves of a workgroup take the blocks of
+// their piece round-robin:
 //   * S^T[pos][head] = K Q^T on MFMA: the K block streams from HBM straight
 //     into A-operand registers (16 B per lane per 16x32 tile half), all query
 //     heads of the KV group ride in the 16 B-operand columns;
@@ -16,10 +18,10 @@
 //     exactly its B operand;
 //   * each wave keeps two blocks of K/V in registers and always consumes the
 //     older one first, so the next block's loads stay in flight;
-//   * the 4 wave states merge through LDS; when the whole window fits one
-//     chunk the sink is applied and o written at once, otherwise the chunk's
-//     (m, l, o) partial goes to workspace and k_attn_merge combines the chunks
-//     in chunk order together with the sink logit:
+//   * the 4 wave states merge through LDS; when the piece is the whole
+//     window the sink is applied and o written at once, otherwise the piece's
+//     (m, l, o) partial goes to workspace and k_attn_merge combines the pieces
+//     in window order together with the sink logit:
 //     M = max(sink, m_c), Z = 2^(sink-M) + sum l_c 2^(m_c-M), o = sum o_c 2^(m_c-M) / Z.
 // Cache layouts (element offsets, D = 64):
 //   packed (full layers):  region(seq, g) = (kv_off[seq] * Hkv + g * cap[seq]) * D
@@ -255,13 +257,14 @@ struct AttnLds {
 #endif
 constexpr bool kStreamKV = SPA_ATTN_NT != 0;   // KV is read once: non-temporal loads
 
-// Chunk c of n_chunks of (token b, KV group g): the 4 waves stream their
-// blocks, merge their states in wave order through LDS and write the output
-// (single chunk) or the chunk's partial. Every thread of the workgroup calls
-// it; it ends with a barrier, so the LDS may be reused at once.
-template <int KVT, int KIND>
-__device__ __forceinline__ void attn_chunk_body(const AttnArgs& a, AttnLds& s, const KvLoc& loc, int b, int g, int c,
-                                                int n_chunks, int G, int tid, int lane, int wave) {
+// Blocks [p0, p1) of the window of (token b, KV group g): the 4 waves stream
+// their blocks, merge their states in wave order through LDS and write the
+// output (pdst null: the piece is the whole window) or the piece's partial,
+// [G][D + 2] floats at pdst. Every thread of the workgroup calls it; it ends
+// with a barrier, so the LDS may be reused at once.
+template <int KVT>
+__device__ __forceinline__ void attn_piece_body(const AttnArgs& a, AttnLds& s, const KvLoc& loc, int b, int g, int p0,
+                                                int p1, float* pdst, int G, int tid, int lane, int wave) {
   constexpr int esz = KVT == DT_BF16 ? 2 : 4;
   const char* kreg = (const char*)a.k_cache + loc.base * esz;
   const char* vreg = (const char*)a.v_cache + loc.base * esz;
@@ -279,13 +282,9 @@ __device__ __forceinline__ void attn_chunk_body(const AttnArgs& a, AttnLds& s, c
     for (int cc = 0; cc < 4; ++cc) qr.q[cc] = hvalid ? ld16(qrow + (16 * cc + 4 * q4) * 4) : u32x4{0u, 0u, 0u, 0u};
   }
 
-  // chunk c of n_chunks: an equal share of the window's blocks (at most
-  // chunk / 32 of them), so no chunk is a short remainder; this wave's
-  // blocks are blk0 + 4i, i < nbw
-  const int nblk = (loc.n_valid + 31) / 32;
-  const int blk0 = c * nblk / n_chunks + wave;
-  const int blk_end = (c + 1) * nblk / n_chunks;
-  const int nbw = blk_end > blk0 ? (blk_end - blk0 + 3) / 4 : 0;
+  // this wave's blocks are blk0 + 4i, i < nbw
+  const int blk0 = p0 + wave;
+  const int nbw = p1 > blk0 ? (p1 - blk0 + 3) / 4 : 0;
   float m_run = -INFINITY, l_run = 0.f;
   f32x4 acc[4];
 #pragma unroll
@@ -331,7 +330,6 @@ __device__ __forceinline__ void attn_chunk_body(const AttnArgs& a, AttnLds& s, c
 
   // merge the 4 waves (fixed order); thread -> (head, d) pairs
   const int GD = G * kD;
-  const long long pbase = (((long long)b * a.n_kv_heads + g) * a.max_chunks) * G * (kD + 2);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int idx = tid + 256 * i;
@@ -348,8 +346,8 @@ __device__ __forceinline__ void attn_chunk_body(const AttnArgs& a, AttnLds& s, c
       l += f * s.l[w][h];
       o += f * s.o[w][d][h];
     }
-    if (n_chunks == 1) {
-      // the whole window was in this chunk: finish with the sink here
+    if (pdst == nullptr) {
+      // the whole window was in this piece: finish with the sink here
       const int hq = g * G + h;
       const float sink = a.sinks[hq] * kLog2e;
       const float MM = fmaxf(M, sink);
@@ -360,7 +358,7 @@ __device__ __forceinline__ void attn_chunk_body(const AttnArgs& a, AttnLds& s, c
       if constexpr (KVT == DT_BF16) ((uint16_t*)a.o)[oi] = f32_to_bf16(out);
       else ((float*)a.o)[oi] = out;
     } else {
-      float* pp = a.part + pbase + ((long long)c * G + h) * (kD + 2);
+      float* pp = pdst + h * (kD + 2);
       pp[d] = o;
       if (d == 0) {
         pp[kD] = M;
@@ -392,96 +390,147 @@ __global__ __launch_bounds__(256, SPA_ATTN_MINB) void k_attn(AttnArgs a) {
     return;
   }
   if (c >= n_chunks) return;
-  attn_chunk_body<KVT, KIND>(a, s, loc, b, g, c, n_chunks, G, tid, lane, wave);
+  // chunk c of n_chunks: an equal share of the window's blocks (at most
+  // chunk / 32 of them), so no chunk is a short remainder
+  const int nblk = (loc.n_valid + 31) / 32;
+  float* pdst = n_chunks == 1 ? nullptr
+                              : a.part + ((((long long)b * a.n_kv_heads + g) * a.max_chunks + c) * G) * (kD + 2);
+  attn_piece_body<KVT>(a, s, loc, b, g, c * nblk / n_chunks, (c + 1) * nblk / n_chunks, pdst, G, tid, lane, wave);
   if (a.tspan) {   // uniform branch: every wave of the workgroup reaches it
     const int j = (c + (g + b * gridDim.y) * gridDim.x) & 15;
     if (tid == 0) atomicMax(a.tspan + 8 * (j + 1), (unsigned long long)wall_clock64());
   }
 }
 
-// The same chunks, dealt to a fixed number of resident workgroups so that
-// every CU streams about the same number of bytes. Tokens are ranked by
-// their chunk length (longest first, ties by index) and their chunks listed
-// in that order, (token, KV group, chunk); item i goes to workgroup i mod W
-// in even rounds and W - 1 - (i mod W) in odd ones (a snake), each
-// workgroup working through its items one after the other. What each chunk
-// computes is exactly k_attn's, whatever W: results do not depend on the
-// grid, so the CU pool may set it.
+// Full layers, launches of up to kDealMaxTok tokens. The launch's windows are
+// laid end to end on one line of 32-position blocks, in (token, KV head)
+// order, T blocks in all, and the line is cut into V equal ranges
+// (v T / V .. (v + 1) T / V; V = a.deal_v, the same for every CU pool of the
+// device, or T when T is smaller). A range's pieces of windows are computed
+// like k_attn's chunks; a window inside one range is finished here, and a
+// piece of a window that a range boundary cuts goes to partial slot
+// (range + window index), which k_attn_merge combines in range order. The
+// resident workgroup w of the stream's pool takes ranges w, w + W, ...: all
+// ranges are the same work, so no CU is left with a long window while others
+// idle. What a range computes depends on the launch's lengths and V only,
+// never on W, so every schedule computes the same bits. Workgroup 0 also
+// writes, per window, its first range and piece count for the merge
+// (deal_tab).
 template <int KVT>
 __global__ __launch_bounds__(256, SPA_ATTN_MINB) void k_attn_dealt(AttnArgs a) {
   __shared__ AttnLds s;
-  __shared__ int s_len[kDealMaxTok];     // chunk length (blocks) per token
-  __shared__ int s_nc[kDealMaxTok];      // chunks per KV group
-  __shared__ int s_first[kDealMaxTok + 1];   // first item of the rank-r token
-  __shared__ int s_tok[kDealMaxTok];     // token of rank r
+  __shared__ long long s_first[kDealMaxTok + 1];   // first block of token t's windows on the line
+  __shared__ long long s_off[kDealMaxTok];
+  __shared__ int s_len[kDealMaxTok], s_cap[kDealMaxTok], s_nb[kDealMaxTok];   // s_nb: blocks per window, 0 if refused
+  __shared__ int s_wsum[4];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int G = a.n_q_heads / a.n_kv_heads;
-  const int n = a.n_tok;
+  const int G = a.n_q_heads / a.n_kv_heads, Hkv = a.n_kv_heads;
+  const int n = a.n_tok;   // 1 .. kDealMaxTok = 256: one token per thread
   if (a.tspan && tid == 0 && blockIdx.x == 0) a.tspan[0] = wall_clock64();   // first dispatched
-  for (int t = tid; t < n; t += 256) {
-    const KvLoc loc = kv_locate(a, a.tok0 + t, 0, KV_PACKED);
-    int nc = (loc.n_valid + a.chunk - 1) / a.chunk;
-    if (!loc.ok || nc > a.max_chunks) {   // refused: no items, reported once
-      if (blockIdx.x == 0 && a.err) atomicOr(a.err, ERR_KV_LEN);
-      nc = 0;
-    }
-    s_nc[t] = nc;
-    s_len[t] = nc > 0 ? ((loc.n_valid + 31) / 32 + nc - 1) / nc : 0;
+  int nb = 0;
+  if (tid < n) {
+    const int seq = a.tok0 + tid;
+    const int L = a.kv_len[seq], cap = a.kv_cap[seq];
+    const long long off = a.kv_off[seq];
+    const bool ok = L >= 1 && L <= cap;
+    if (!ok && blockIdx.x == 0 && a.err) atomicOr(a.err, ERR_KV_LEN);   // refused: no blocks, reported once
+    nb = ok ? (L + 31) / 32 : 0;
+    s_len[tid] = L;
+    s_cap[tid] = cap;
+    s_off[tid] = off;
+    s_nb[tid] = nb;
   }
-  __syncthreads();
-  for (int t = tid; t < n; t += 256) {   // rank: longer chunks first, ties by token index
-    const int lt = s_len[t];
-    int r = 0;
-    for (int u = 0; u < n; ++u) {
-      const int lu = s_len[u];
-      r += (lu > lt || (lu == lt && u < t)) ? 1 : 0;
-    }
-    s_tok[r] = t;
+  // exclusive prefix of the per-token block counts: wave scans, then wave sums
+  int incl = nb;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int t = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += t;
   }
+  if (lane == 63) s_wsum[wave] = incl;
   __syncthreads();
-  if (tid == 0) {   // items per rank: KV groups x chunks
-    int acc = 0;
-    for (int r = 0; r < n; ++r) {
-      s_first[r] = acc;
-      acc += a.n_kv_heads * s_nc[s_tok[r]];
+  int before = 0;
+  for (int w2 = 0; w2 < wave; ++w2) before += s_wsum[w2];
+  if (tid < n) s_first[tid] = (long long)(before + incl - nb) * Hkv;
+  if (tid == 0) s_first[n] = (long long)(s_wsum[0] + s_wsum[1] + s_wsum[2] + s_wsum[3]) * Hkv;
+  __syncthreads();
+  const long long T = s_first[n];
+  const int V = (int)min((long long)a.deal_v, T);
+  // range holding block x: the largest v with v T / V <= x
+  auto range_of = [&](long long x) { return (int)(((x + 1) * V - 1) / T); };
+  if (blockIdx.x == 0) {
+    for (int j = tid; j < n * Hkv; j += 256) {
+      const int t = j / Hkv, g = j - t * Hkv, nbt = s_nb[t];
+      int first = 0, cnt = 0;
+      if (nbt > 0) {
+        const long long ws = s_first[t] + (long long)g * nbt;
+        first = range_of(ws);
+        cnt = range_of(ws + nbt - 1) - first + 1;
+      }
+      a.deal_tab[2 * j] = first;
+      a.deal_tab[2 * j + 1] = cnt;
     }
-    s_first[n] = acc;
   }
-  __syncthreads();
-  const int total = s_first[n];
   const int W = gridDim.x, w = blockIdx.x;
-  for (int round = 0;; ++round) {
-    const int i = round * W + ((round & 1) ? W - 1 - w : w);
-    if (i >= total) break;
-    int lo = 0, hi = n - 1;   // rank of item i: the largest r with s_first[r] <= i
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (s_first[mid] <= i) lo = mid;
-      else hi = mid - 1;
+  for (int v = w; v < V; v += W) {
+    const long long lo = (long long)v * T / V, hi = (long long)(v + 1) * T / V;
+    int t = 0, t1 = n - 1;   // token holding block lo: the largest t with s_first[t] <= lo (it has blocks)
+    while (t < t1) {
+      const int mid = (t + t1 + 1) >> 1;
+      if (s_first[mid] <= lo) t = mid;
+      else t1 = mid - 1;
     }
-    const int b = s_tok[lo];
-    const int nc = s_nc[b];
-    const int rel = i - s_first[lo];
-    const int g = rel / nc, c = rel - g * nc;
-    const KvLoc loc = kv_locate(a, a.tok0 + b, g, KV_PACKED);
-    attn_chunk_body<KVT, KV_PACKED>(a, s, loc, b, g, c, nc, G, tid, lane, wave);
+    int nbt = s_nb[t];
+    int g = (int)((lo - s_first[t]) / nbt);
+    long long ws = s_first[t] + (long long)g * nbt;   // the window's first block on the line
+    long long x = lo;
+    for (;;) {
+      const int p0 = (int)(x - ws), p1 = (int)(min(hi, ws + nbt) - ws);
+      const int j = t * Hkv + g;
+      KvLoc loc;
+      loc.base = (s_off[t] * Hkv + (long long)g * s_cap[t]) * kD;
+      loc.n_valid = s_len[t];
+      loc.ok = true;
+      float* pdst = (p0 == 0 && p1 == nbt) ? nullptr : a.part + (long long)(v + j) * G * (kD + 2);
+      attn_piece_body<KVT>(a, s, loc, t, g, p0, p1, pdst, G, tid, lane, wave);
+      x = ws + p1;
+      if (x >= hi) break;
+      if (++g == Hkv) {   // the next token with blocks (one exists: x < hi <= T)
+        g = 0;
+        do ++t; while (t < n && s_nb[t] == 0);
+        if (t >= n) break;
+        nbt = s_nb[t];
+      }
+      ws = s_first[t] + (long long)g * nbt;
+    }
   }
   if (a.tspan && tid == 0) atomicMax(a.tspan + 8 * ((w & 15) + 1), (unsigned long long)wall_clock64());
 }
 
-// Merge the chunk partials of one (sequence, KV head) in chunk order with the
+// Merge the piece partials of one (sequence, KV head) in window order with the
 // sink: M = max(sink, m_c), Z = 2^(sink-M) + sum l_c 2^(m_c-M), o = sum o_c 2^(m_c-M) / Z.
+// k_attn's chunks sit at [b][g][chunk]; k_attn_dealt's pieces of window j at
+// the consecutive slots first + j + i, i < count, from deal_tab.
 template <int KVT>
 __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
   const int g = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   const int seq = a.tok0 + b;
   const int G = a.n_q_heads / a.n_kv_heads;
-  const KvLoc loc = kv_locate(a, seq, g, a.kv_kind);
-  if (!loc.ok) return;
-  const int n_chunks = (loc.n_valid + a.chunk - 1) / a.chunk;
-  if (n_chunks <= 1 || n_chunks > a.max_chunks) return;
-  const long long pbase = (((long long)b * a.n_kv_heads + g) * a.max_chunks) * G * (kD + 2);
+  int n_chunks;
+  long long pbase;
+  if (a.deal_v > 0) {
+    const int j = b * a.n_kv_heads + g;
+    n_chunks = a.deal_tab[2 * j + 1];
+    if (n_chunks <= 1) return;
+    pbase = (long long)(a.deal_tab[2 * j] + j) * G * (kD + 2);
+  } else {
+    const KvLoc loc = kv_locate(a, seq, g, a.kv_kind);
+    if (!loc.ok) return;
+    n_chunks = (loc.n_valid + a.chunk - 1) / a.chunk;
+    if (n_chunks <= 1 || n_chunks > a.max_chunks) return;
+    pbase = (((long long)b * a.n_kv_heads + g) * a.max_chunks) * G * (kD + 2);
+  }
   const long long cstride = (long long)G * (kD + 2);
   constexpr int UF = 8;   // up to UF chunks and 2 (head, d) pairs per thread: one pass, every load first
   if (n_chunks <= UF && G * kD <= 512) {
@@ -581,7 +630,8 @@ static void launch_dealt_t(const AttnArgs& a, hipStream_t st, hipEvent_t start, 
 
 hipError_t launch_attn(const AttnArgs& a, hipStream_t st, hipEvent_t start, hipEvent_t stop) {
   if (a.deal_wgs > 0 && a.kv_kind == KV_PACKED) {
-    if (a.n_tok < 1 || a.n_tok > kDealMaxTok) return hipErrorInvalidValue;
+    if (a.n_tok < 1 || a.n_tok > kDealMaxTok || a.deal_v < 1 || a.deal_v > kDealMaxRanges || !a.deal_tab)
+      return hipErrorInvalidValue;
     if (a.kv_dtype == DT_BF16) launch_dealt_t<DT_BF16>(a, st, start, stop);
     else launch_dealt_t<DT_F32>(a, st, start, stop);
     return hipGetLastError();

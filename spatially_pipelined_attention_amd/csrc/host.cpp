@@ -89,6 +89,15 @@ spa_status launch_comm(spa_ctx* ctx, const void* src, void* dst, size_t copy_byt
   return SPA_OK;
 }
 
+// Full layers of up to kDealMaxTok tokens run as an even split of the
+// launch's blocks into deal_ranges() ranges (k_attn_dealt): its partial slots
+// and the per-window merge table.
+static bool dealt_launch(const spa_layer* l, int n_tok) { return l->kind == SPA_FULL && n_tok <= kDealMaxTok; }
+static int deal_ranges(int device_cus) { return kDealWgsPerCu * device_cus; }
+static size_t deal_part_bytes(int ranges, int n_tok, int Hkv, int G, int D) {
+  return ((size_t)ranges + (size_t)n_tok * Hkv) * G * (D + 2) * 4 + (size_t)n_tok * Hkv * 2 * 4;
+}
+
 int max_chunks_for(int max_kv_len, const spa_model_desc* m) {
   int l = std::max(max_kv_len, m->window);
   return (l + kAttnChunk - 1) / kAttnChunk;
@@ -260,7 +269,8 @@ WsLayout ws_layout(const spa_model_desc* m, int n_tok, int max_kv_len, int n_mic
   s.z8 = o; o = align256(o + (fp8 ? (size_t)R * I : 0));
   s.z8_scale = o; o = align256(o + (fp8 ? (size_t)R * 4 : 0));
   s.y = o; o = align256(o + (size_t)R * H * 4);
-  s.attn_part = o; o = align256(o + (size_t)n_tok * Hkv * L.max_chunks * G * (D + 2) * 4);
+  s.attn_part = o; o = align256(o + std::max((size_t)n_tok * Hkv * L.max_chunks * G * (D + 2) * 4,
+                                             deal_part_bytes(kDealMaxRanges, n_tok, Hkv, G, D)));
   s.gemm_part = o; o = align256(o + gemm_part_floats(m, n_tok) * 4);
   s.comm = o;
   if (comm_enabled(m))
@@ -501,16 +511,23 @@ static spa_status op_attn(spa_ctx* ctx, const spa_model_desc* m, const spa_layer
                           bool kmajor = false) {
   AttnArgs a = attn_args(m, l, b, tok0, n_tok, q, o, W, s, ctx->n_cus);
   a.o_kmajor_rows = kmajor ? n_tok : 0;
-  // full layers: the chunks dealt to two resident workgroups per CU of the
-  // stream's pool (the chunks, and so the results, are the same either way)
-  if (l->kind == SPA_FULL && n_tok <= kDealMaxTok) a.deal_wgs = kDealWgsPerCu * stream_cus(st, ctx->n_cus);
+  // full layers: the launch's blocks cut into ranges fixed by the device,
+  // taken by two resident workgroups per CU of the stream's pool (the ranges,
+  // and so the results, are the same for every pool)
+  if (dealt_launch(l, n_tok)) {
+    const int G = m->n_q_heads / m->n_kv_heads;
+    a.deal_wgs = kDealWgsPerCu * stream_cus(st, ctx->n_cus);
+    a.deal_v = deal_ranges(ctx->n_cus);
+    if (a.deal_v > kDealMaxRanges) return fail(SPA_EUNSUPPORTED, "device has more CUs than the attention split supports");
+    a.deal_tab = (int*)(a.part + ((size_t)a.deal_v + (size_t)n_tok * m->n_kv_heads) * G * (m->head_dim + 2));
+  }
   {
     // the attention kernel alone, timed by its own dispatch (start/stop events of the launch)
     HookScope hs(th, l->kind == SPA_FULL ? KC_ATTN_FULL : KC_ATTN_SLIDING, st, true);
     a.tspan = hs.span_slot;
     SPA_HIP(launch_attn(a, st, hs.start(), hs.stop()));
   }
-  if (a.max_chunks > 1) SPA_HIP(launch_attn_merge(a, st));
+  if (a.deal_v > 0 || a.max_chunks > 1) SPA_HIP(launch_attn_merge(a, st));
   return SPA_OK;
 }
 
@@ -1111,6 +1128,7 @@ size_t attn_scratch_bytes(spa_ctx* ctx, const spa_model_desc* m, const spa_layer
                                                attn_chunk(m, b, n_tok, ctx->n_cus)
                                          : (m->window + kAttnChunk - 1) / kAttnChunk;
   if (max_chunks_out) *max_chunks_out = chunks;
+  if (dealt_launch(l, n_tok)) return deal_part_bytes(deal_ranges(ctx->n_cus), n_tok, m->n_kv_heads, G, m->head_dim);
   return (size_t)n_tok * m->n_kv_heads * chunks * G * (m->head_dim + 2) * 4;
 }
 

@@ -182,7 +182,7 @@ struct AttnArgs {
   float scale_log2;         // softmax scale * log2(e)
   int chunk;                // positions per workgroup (multiple of 128)
   int max_chunks;
-  float* part;              // [n_tok][Hkv][max_chunks][G][D+2]
+  float* part;              // k_attn: [n_tok][Hkv][max_chunks][G][D+2]; k_attn_dealt: [deal_v + n_tok*Hkv][G][D+2]
   void* o;                  // [n_tok][Hq*D] (kv dtype)
   int* err;
   int stream_kv;            // non-temporal KV loads
@@ -193,12 +193,16 @@ struct AttnArgs {
   // (spread over 16 lines, so the atomics do not queue on one address).
   // The caller presets the words to zero.
   unsigned long long* tspan;
-  // > 0: full-layer chunks dealt to this many resident workgroups
-  // (k_attn_dealt); 0: one workgroup per chunk (k_attn)
+  // > 0: full layers as an even split of the launch's blocks into deal_v
+  // ranges, taken by this many resident workgroups (k_attn_dealt); 0: one
+  // workgroup per chunk (k_attn)
   int deal_wgs;
+  int deal_v;               // ranges of the even split (the same for every pool of the device)
+  int* deal_tab;            // [n_tok * Hkv][2]: first range and piece count of each window
 };
 constexpr int kSpanWords = 136;
-constexpr int kDealMaxTok = 256;   // tokens per launch the dealt kernel ranks in LDS
+constexpr int kDealMaxTok = 256;   // tokens per launch of the dealt kernel (one per thread of its prologue)
+constexpr int kDealMaxRanges = 1024;   // upper bound of deal_v (workspace sizing)
 #ifndef SPA_DEAL_WGS_PER_CU
 #define SPA_DEAL_WGS_PER_CU 2
 #endif

@@ -1,7 +1,7 @@
 // The no-allocation variant of decode attention: the same kernels as
-// spa_decode_attn, with their scratch (the per-chunk softmax partials and
-// the device error word) in a fixed array of the library instead of a caller
-// workspace, for callers that cannot allocate device memory.
+// spa_decode_attn, with their scratch (the softmax partials of the pieces
+// and the device error word) in a fixed array of the library instead of a
+// caller workspace, for callers that cannot allocate device memory.
 //
 // `scratch` is a file-scope device array; every GPU the library runs on
 // holds its own copy until the process ends. In host code its name is only
@@ -16,7 +16,7 @@
 namespace {
 
 constexpr size_t kScratchErrBytes = 256;                    // the error word (and padding)
-constexpr size_t kScratchPartBytes = (size_t)16 << 20;      // chunk partials: 16 MiB
+constexpr size_t kScratchPartBytes = (size_t)16 << 20;      // piece partials: 16 MiB
 constexpr int kMaxDevices = 64;
 
 __device__ __align__(256) unsigned char scratch[kScratchErrBytes + kScratchPartBytes];

@@ -128,8 +128,10 @@ def test_large_batch_expert_tiles_sampled(name, n_layers):
 def test_kv_length_beyond_capacity_is_refused():
     """A cached length above the sequence's capacity (or zero) sets the
     error bit and is skipped before any KV read; every other token's
-    attention output is unchanged, bit for bit. Each call clears the error
-    word first, so each reading belongs to one launch."""
+    attention output is unchanged (bit for bit on the sliding layer, within
+    rounding on the full layer, whose split follows the launch's lengths).
+    Each call clears the error word first, so each reading belongs to one
+    launch."""
     from spatially_pipelined_attention_amd import binding as B, synth
     from spatially_pipelined_attention_amd.workload import DeviceWorkload
     base = synth.WORKLOADS["gptoss_36l_b64"]
@@ -158,5 +160,9 @@ def test_kv_length_beyond_capacity_is_refused():
     assert errs[0] == 0 and errs[1] == 0
     assert errs[2] & 1 and errs[3] & 1
     keep = [t for t in range(n) if t not in (3, 9)]
-    assert torch.equal(outs[0][keep], outs[2][keep])   # full layer
-    assert torch.equal(outs[1][keep], outs[3][keep])   # sliding layer
+    # full layer: the launch's blocks are split evenly, so a refused token's
+    # missing blocks move the other windows' split points; their outputs stay
+    # within rounding of the clean run
+    hz.assert_close_rms(outs[2][keep].double().cpu().numpy(), outs[0][keep].double().cpu().numpy(), 1e-2,
+                        "full layer, refused tokens left out")
+    assert torch.equal(outs[1][keep], outs[3][keep])   # sliding layer: one workgroup per window, bit for bit
