@@ -36,7 +36,7 @@ namespace spa {
 
 template <int WT, int EPI, int CT, int MT>
 __global__ __launch_bounds__(256, SPA_GEMM_MINB) void k_gemm(GemmArgs a) {
-  __shared__ __attribute__((aligned(16))) char red[gemm_red_bytes<CT>()];
+  __shared__ __attribute__((aligned(16))) char red[gemm_red_bytes<CT, MT>()];
   gemm_tile<WT, EPI, CT, MT>(a, blockIdx.x, threadIdx.x, red);
 }
 

@@ -1,7 +1,7 @@
 // The weight-streaming GEMM tile (the body of k_gemm in gemm.hip) as a device
 // function over an explicit block id, so a persistent kernel can run the same
 // tiles with the same arithmetic: 256 threads (tid 0..255, 4 waves), LDS
-// reduction buffer `red` of gemm_red_bytes<CT>() bytes. Every thread of the
+// reduction buffer `red` of gemm_red_bytes<CT, MT>() bytes. Every thread of the
 // 256 calls it; the block's barriers are those of the calling workgroup.
 #pragma once
 #include "common.h"
@@ -27,8 +27,17 @@ template <int CT, int MT> struct Ring {
   static constexpr int P = CT * MT > 16 ? SPA_GEMM_RING_BIG : (CT * MT > 8 ? SPA_GEMM_RING_MID : 4);
 };
 
-template <int CT>
-constexpr int gemm_red_bytes() { return 3 * CT * 64 * 16; }   // wave reduction of one 16-row tile
+// The tile's finish: small tiles put all their row tiles in LDS at once
+// (4 waves x MT x CT fragments of 1 KB, at most 32 KB), larger ones one row
+// tile at a time through two alternating buffers.
+template <int CT, int MT>
+constexpr bool gemm_finish_at_once() { return 4 * MT * CT * 1024 <= 32 * 1024; }
+template <int CT, int MT>
+constexpr int gemm_red_bytes() { return gemm_finish_at_once<CT, MT>() ? 4 * MT * CT * 1024 : 2 * 4 * CT * 1024; }
+// barriers one gemm_tile<.., CT, MT> call takes (a workgroup whose groups
+// share barriers matches them when it has no tile)
+template <int CT, int MT>
+constexpr int gemm_tile_barriers() { return gemm_finish_at_once<CT, MT>() ? 2 : MT + 1; }
 
 // P: k-steps per wave in the register ring (the order of the products does
 // not depend on it; only the count of zero-weight padding steps at the end).
@@ -144,115 +153,144 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int bid, int tid, c
     for (int p = 0; p < P; ++p) compute(p, J - P + p);
   }
 
-  // sum the wave tiles in wave order: 16 rows at a time through LDS
+  // Finish the tile: every wave puts its partial tiles in LDS, and the
+  // (row tile, fragment) pairs are dealt over the 4 waves, each summed in
+  // wave order (((w0 + w1) + w2) + w3) and finished (SwiGLU: gate fragment f
+  // with its up partner f + CT/2). Small tiles go through LDS at once; larger
+  // ones 16 rows at a time, wave w taking fragments w, w + 4, ..., through
+  // two alternating buffers, so one barrier per row tile suffices: a buffer
+  // is written again two row tiles later, after a barrier every wave reaches
+  // only once its reads are done.
+  constexpr int NF = EPI == EPI_SWIGLU ? CT / 2 : CT;   // fragments (SwiGLU: gate/up pairs) to finish
+  constexpr int NU = (NF + 3) / 4;                      // per wave
+  // at once: [4 waves][MT][CT][64 lanes]; by row tile: [2][4 waves][CT][64 lanes]
   f32x4* rd = reinterpret_cast<f32x4*>(red);
+  const int c4 = (lane >> 4) * 4;                       // a lane holds row lo16, columns c4 .. c4 + 3 of a fragment
+  // E4M3 weight scale of column c4 + i of fragment f (h = 1: its up partner)
+  auto wscale = [&](int f, int h, int i) {
+    const int wr = w_row_of<EPI, CT>(a, nb, (f + h * (CT / 2)) * 16 + c4 + i);
+    return wr < w_rows_total<EPI>(a) ? a.w_scale[(long long)grp * a.ws_gstride + wr] : 0.f;
+  };
+  // the scales of this wave's fragments, read once (row-tile mode)
+  float wsc[NU][2][4];
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    if (wave > 0) {
+  for (int u = 0; u < NU; ++u)
 #pragma unroll
-      for (int ct = 0; ct < CT; ++ct) rd[((wave - 1) * CT + ct) * 64 + lane] = acc[mt][ct];
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) wsc[u][h][i] = 1.f;
+  if constexpr (WT == DT_E4M3 && !gemm_finish_at_once<CT, MT>()) {
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      const int f = wave + 4 * u;
+      if (f >= NF) continue;
+#pragma unroll
+      for (int h = 0; h < (EPI == EPI_SWIGLU ? 2 : 1); ++h)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) wsc[u][h][i] = wscale(f, h, i);
     }
-    __syncthreads();
-    if (wave == 0) {
-#pragma unroll
-      for (int w = 0; w < 3; ++w)
-#pragma unroll
-        for (int ct = 0; ct < CT; ++ct) acc[mt][ct] += rd[(w * CT + ct) * 64 + lane];
-    }
-    __syncthreads();
   }
-  if (wave != 0) return;
-
-  // wave 0 holds the tile: row mt*16 + lo16, columns ct*16 + c4 + i
-  const int c4 = (lane >> 4) * 4;
-  // E4M3: per-output-channel weight scales and per-row activation scales
-  float wsc[CT][4];
+  // finish fragment f (a gate/up pair for SwiGLU) of row tile mt from the 4
+  // waves' copies at buf[(w * wstride + ct) * 64 + lane]; u: its slot in
+  // this wave's scale table, or -1 to read the scales here
+  auto finish = [&](const f32x4* buf, int wstride, int mt, int f, int u) {
+    const int m = mt * 16 + lo16;
+    if (m >= rows_here) return;   // padding rows are not written
+    const long long orow = r0 + rb * BR + m;
+    float xs = 1.f;
+    if constexpr (WT == DT_E4M3) xs = a.x_scale[a.row_src ? a.row_src[orow] : orow];
+    f32x4 v[2];
 #pragma unroll
-  for (int ct = 0; ct < CT; ++ct)
+    for (int h = 0; h < (EPI == EPI_SWIGLU ? 2 : 1); ++h) {
+      const int ct = f + h * (CT / 2);
+      f32x4 t = buf[ct * 64 + lane];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) wsc[ct][i] = 1.f;
-  if constexpr (WT == DT_E4M3) {
+      for (int w = 1; w < 4; ++w) t += buf[(w * wstride + ct) * 64 + lane];
+      v[h] = t;
+    }
+    float sc[2][4];
 #pragma unroll
-    for (int ct = 0; ct < CT; ++ct)
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sc[h][i] = 1.f;
+    if constexpr (WT == DT_E4M3) {
+#pragma unroll
+      for (int h = 0; h < (EPI == EPI_SWIGLU ? 2 : 1); ++h)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sc[h][i] = u >= 0 ? wsc[u][h][i] : wscale(f, h, i);
+    }
+    if constexpr (EPI == EPI_PARTIAL) {
+      // split s, row (dispatch or token row), padded column: [S][part_rows][part_ld];
+      // every split is scaled, so the splits' sum is the scaled product
+      f32x4 t = v[0];
+      if constexpr (WT == DT_E4M3) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) t[i] *= sc[0][i] * xs;
+      }
+      float* pt = a.part + ((long long)s * a.part_rows + orow) * a.part_ld + nb * TC + f * 16 + c4;
+      *reinterpret_cast<f32x4*>(pt) = t;
+    } else if constexpr (EPI == EPI_STORE) {
+      float o4[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o4[i] = v[0][i] * sc[0][i] * xs;
+      float* o = (float*)a.out + orow * a.out_ld;
+      const int c = nb * TC + f * 16 + c4;
+      if (c + 3 < a.N) {
+        *reinterpret_cast<f32x4*>(o + c) = f32x4{o4[0], o4[1], o4[2], o4[3]};
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (c + i < a.N) o[c + i] = o4[i];
+      }
+    } else {   // SwiGLU: fragment f < CT/2 holds gate columns, f + CT/2 the matching up columns
+      const int j0 = nb * 8 * CT + f * 16 + c4;
+      if (j0 >= a.inter) return;
+      float z[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int wr = w_row_of<EPI, CT>(a, nb, ct * 16 + c4 + i);
-        wsc[ct][i] = wr < w_rows_total<EPI>(a) ? a.w_scale[(long long)grp * a.ws_gstride + wr] : 0.f;
+        const float g = v[0][i] * sc[0][i] * xs, up = v[1][i] * sc[1][i] * xs;
+        z[i] = g / (1.0f + __expf(-g)) * up;
       }
-  }
-  if constexpr (EPI == EPI_PARTIAL) {
-    // split s, row (dispatch or token row), padded column: [S][part_rows][part_ld];
-    // every split is scaled, so the splits' sum is the scaled product
-    float* pt = a.part + ((long long)s * a.part_rows + r0 + rb * BR) * a.part_ld + nb * TC + c4;
+      const long long zr = a.out_kmajor_rows;
+      if (a.out_dtype == DT_BF16) {   // k-step-major: 32 bf16 per k-step
+        uint16_t* o = (uint16_t*)a.out + (zr ? ((long long)(j0 >> 5) * zr + orow) * 32 + (j0 & 31) : orow * a.out_ld + j0);
+        *reinterpret_cast<uint2*>(o) = uint2{pack_bf16x2(z[0], z[1]), pack_bf16x2(z[2], z[3])};
+      } else {                        // k-step-major: 16 fp32 per k-step
+        float* o = (float*)a.out + (zr ? ((long long)(j0 >> 4) * zr + orow) * 16 + (j0 & 15) : orow * a.out_ld + j0);
+        *reinterpret_cast<f32x4*>(o) = f32x4{z[0], z[1], z[2], z[3]};
+      }
+    }
+  };
+  if constexpr (gemm_finish_at_once<CT, MT>()) {
+    // [4 waves][MT][CT][64 lanes]; pair i = (mt, f) goes to wave i % 4
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      const int m = mt * 16 + lo16;
-      if (m < rows_here) {
-        float xs = 1.f;
-        if constexpr (WT == DT_E4M3) {
-          const long long orow = r0 + rb * BR + m;
-          xs = a.x_scale[a.row_src ? a.row_src[orow] : orow];
-        }
+    for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int ct = 0; ct < CT; ++ct) {
-          f32x4 v = acc[mt][ct];
-          if constexpr (WT == DT_E4M3) {
+      for (int ct = 0; ct < CT; ++ct) rd[((wave * MT + mt) * CT + ct) * 64 + lane] = acc[mt][ct];
+    __syncthreads();
 #pragma unroll
-            for (int i = 0; i < 4; ++i) v[i] *= wsc[ct][i] * xs;
-          }
-          *reinterpret_cast<f32x4*>(pt + (long long)m * a.part_ld + ct * 16) = v;
-        }
+    for (int i = 0; i < (MT * NF + 3) / 4; ++i) {
+      const int pair = wave + 4 * i;
+      if (pair < MT * NF) {
+        const int mt = pair / NF, f = pair - mt * NF;
+        finish(rd + mt * CT * 64, MT * CT, mt, f, -1);   // wave w's copy of row tile mt: MT * CT fragments apart
       }
     }
   } else {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-      const int m = mt * 16 + lo16;
-      if (m >= rows_here) continue;
-      const long long orow = r0 + rb * BR + m;
-      float xs = 1.f;
-      if constexpr (WT == DT_E4M3) xs = a.x_scale[a.row_src ? a.row_src[orow] : orow];
-      float v[CT][4];
+      f32x4* buf = rd + (mt & 1) * 4 * CT * 64;
 #pragma unroll
-      for (int ct = 0; ct < CT; ++ct)
+      for (int ct = 0; ct < CT; ++ct) buf[(wave * CT + ct) * 64 + lane] = acc[mt][ct];
+      __syncthreads();
 #pragma unroll
-        for (int i = 0; i < 4; ++i) v[ct][i] = acc[mt][ct][i] * wsc[ct][i] * xs;
-      if constexpr (EPI == EPI_STORE) {
-        float* o = (float*)a.out + orow * a.out_ld;
-#pragma unroll
-        for (int ct = 0; ct < CT; ++ct) {
-          const int c = nb * TC + ct * 16 + c4;
-          if (c + 3 < a.N) {
-            *reinterpret_cast<f32x4*>(o + c) = f32x4{v[ct][0], v[ct][1], v[ct][2], v[ct][3]};
-          } else {
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-              if (c + i < a.N) o[c + i] = v[ct][i];
-          }
-        }
-      } else {   // SwiGLU: fragments ct < CT/2 are gate columns, ct + CT/2 the matching up columns
-#pragma unroll
-        for (int ct = 0; ct < CT / 2; ++ct) {
-          const int j0 = nb * 8 * CT + ct * 16 + c4;
-          if (j0 >= a.inter) continue;
-          float z[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float g = v[ct][i], u = v[ct + CT / 2][i];
-            z[i] = g / (1.0f + __expf(-g)) * u;
-          }
-          const long long zr = a.out_kmajor_rows;
-          if (a.out_dtype == DT_BF16) {   // k-step-major: 32 bf16 per k-step
-            uint16_t* o = (uint16_t*)a.out + (zr ? ((long long)(j0 >> 5) * zr + orow) * 32 + (j0 & 31) : orow * a.out_ld + j0);
-            *reinterpret_cast<uint2*>(o) = uint2{pack_bf16x2(z[0], z[1]), pack_bf16x2(z[2], z[3])};
-          } else {                        // k-step-major: 16 fp32 per k-step
-            float* o = (float*)a.out + (zr ? ((long long)(j0 >> 4) * zr + orow) * 16 + (j0 & 15) : orow * a.out_ld + j0);
-            *reinterpret_cast<f32x4*>(o) = f32x4{z[0], z[1], z[2], z[3]};
-          }
-        }
+      for (int u = 0; u < NU; ++u) {
+        const int f = wave + 4 * u;
+        if (f < NF) finish(buf, CT, mt, f, u);
       }
     }
   }
+  __syncthreads();   // the LDS buffers are free again when the call returns
 }
 
 }  // namespace spa

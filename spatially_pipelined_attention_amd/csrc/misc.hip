@@ -450,10 +450,7 @@ __device__ __forceinline__ void head_barrier(unsigned* ctr, unsigned target, int
 template <int MT>
 __device__ __forceinline__ void gemm_tile_idle() {   // the barriers of one gemm_tile<.., MT> call
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    __syncthreads();
-    __syncthreads();
-  }
+  for (int i = 0; i < gemm_tile_barriers<1, MT>(); ++i) __syncthreads();
 }
 
 template <int SM0, int SM2, int MT>
@@ -466,7 +463,7 @@ __global__ __launch_bounds__(kRowThreads) void k_moe_head(MoeHeadArgs a) {
   // 1: router product tiles, four 256-thread groups per workgroup
   {
     const int grp = threadIdx.x >> 8, tid = threadIdx.x & 255;
-    char* red = lds + grp * gemm_red_bytes<1>();
+    char* red = lds + grp * gemm_red_bytes<1, MT>();
     // tile t0 + grp * G + blockIdx.x: spread over the workgroups first
     for (int t0 = 0; t0 < a.n_router_tiles; t0 += 4 * (int)G) {
       const int t = t0 + grp * (int)G + blockIdx.x;
@@ -506,7 +503,7 @@ __global__ __launch_bounds__(kRowThreads) void k_moe_head(MoeHeadArgs a) {
 }
 
 int moe_head_lds_bytes(int n_tok, int k, int E_res) {
-  return std::max({4 * gemm_red_bytes<1>(), route_lds_bytes(n_tok, k, E_res), (int)(kRowThreads / 64 * sizeof(float))});
+  return std::max({4 * gemm_red_bytes<1, 4>(), route_lds_bytes(n_tok, k, E_res), (int)(kRowThreads / 64 * sizeof(float))});
 }
 
 template <int SM0, int MT>
