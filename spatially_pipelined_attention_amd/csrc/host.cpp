@@ -587,6 +587,13 @@ static const void* expert_input(const spa_model_desc* m, const Slot& s) {
 // Router GEMV, top-k and the dispatch permutation. gather: also gather the
 // slot's expert input rows into dispatch order (s.xe_perm) in the same
 // kernel. The router product's and the routing kernels' arguments.
+// Whether the routing gathers the expert input rows into dispatch order: the
+// virtual dispatch endpoint sends the gathered rows; otherwise the gate/up
+// product reads them in place through the row map (measured faster than the
+// gather: the permutation kernel then moves no rows, and the product's
+// row-major activation fragments cost it about 0.5 us).
+static bool route_gathers(const spa_model_desc* m) { return comm_enabled(m); }
+
 static void route_args(spa_ctx* ctx, const spa_model_desc* m, const spa_layer* l, const float* hn, int n_tok,
                        float* logits, const spa_route_bufs& r, int32_t* topk_rec, const Slot& s, bool gather,
                        GemmArgs* ga, RouteArgs* ra_out, GemmPlan* plan) {
@@ -655,7 +662,7 @@ static spa_status op_oproj_route(spa_ctx* ctx, const spa_model_desc* m, const sp
   GemmPlan rp;
   oproj_args(ctx, m, l, x, s.o, n_tok, s.h, s.hn_f32, ebf ? s.hn_bf16 : nullptr, fp8 ? s.hn8 : nullptr,
              fp8 ? s.hn8_scale : nullptr, s, true, &oa, &h.of);
-  route_args(ctx, m, l, s.hn_f32, n_tok, s.logits, s.route, rec, s, true, &h.router, &h.ra, &rp);
+  route_args(ctx, m, l, s.hn_f32, n_tok, s.logits, s.route, rec, s, true, &h.router, &h.ra, &rp);   // the head gathers
   const bool use = fuse && s.head_ctr && !comm_enabled(m) && moe_head_supported(h.of.pv.S, h.ra.pv.S, rp.blk_rows);
   if (!use) {
     spa_status rc = op_oproj(ctx, m, l, x, s.o, n_tok, s.h, s.hn_f32, ebf ? s.hn_bf16 : nullptr, fp8 ? s.hn8 : nullptr,
@@ -663,7 +670,7 @@ static spa_status op_oproj_route(spa_ctx* ctx, const spa_model_desc* m, const sp
     if (rc) return rc;
     const size_t ar = comm_bytes_allreduce(m, n_tok);
     if ((rc = op_comm(ctx, m, s.h, ar, ar, s, st, th))) return rc;   // attention all-reduce
-    return op_route(ctx, m, l, s.hn_f32, n_tok, s.logits, s.route, rec, s, st, th, true);
+    return op_route(ctx, m, l, s.hn_f32, n_tok, s.logits, s.route, rec, s, st, th, route_gathers(m));
   }
   h.n_router_tiles = rp.n_tiles * rp.rb_stride * rp.S;
   h.ctr = s.head_ctr;
@@ -682,9 +689,15 @@ static spa_status op_oproj_route(spa_ctx* ctx, const spa_model_desc* m, const sp
 
 // Experts: gate/up + SwiGLU, then down. xe: the expert input rows per token
 // (bf16 / fp32 / E4M3 with xe_scale). Leaves y plain (S = 1) or as partials.
+// Where the gate/up product finds its expert input rows: gathered into
+// dispatch order (k-step-major) by the routing, to be gathered here, or read
+// in place from the per-token rows through the row map (row_tok).
+enum class ExpertRows { kGather, kGathered, kInPlace };
+
 static spa_status op_expert(spa_ctx* ctx, const spa_model_desc* m, const spa_layer* l, const void* xe,
                             const float* xe_scale, int n_tok, const spa_route_bufs& r, float* y_plain, const Slot& s,
-                            hipStream_t st, TimingHook* th, GemmPlan* down_plan, bool gathered = false) {
+                            hipStream_t st, TimingHook* th, GemmPlan* down_plan,
+                            ExpertRows rows = ExpertRows::kGather) {
   const int H = m->hidden, I = m->inter, R = n_tok * m->top_k;
   const bool fp8 = m->expert_dtype == SPA_E4M3;
   {
@@ -698,18 +711,27 @@ static spa_status op_expert(spa_ctx* ctx, const spa_model_desc* m, const spa_lay
     a.N = I;
     a.inter = I;
     a.group_off = r.offsets;
-    // expert rows gathered in dispatch order, k-step-major: one 16-row X
-    // fragment of a k-step is 1 KB of contiguous memory
-    a.X = s.xe_perm;
-    a.x_rstride = 64;
-    a.x_kstride = (long long)R * 64;
-    a.x_scale = fp8 ? s.xe_perm_scale : nullptr;
+    if (rows == ExpertRows::kInPlace) {
+      // the per-token rows, row-major, through the row map
+      a.X = xe;
+      a.row_src = r.row_tok;
+      a.x_rstride = (long long)H * esz_of(m->expert_dtype);
+      a.x_kstride = 64;
+      a.x_scale = fp8 ? xe_scale : nullptr;
+    } else {
+      // expert rows gathered in dispatch order, k-step-major: one 16-row X
+      // fragment of a k-step is 1 KB of contiguous memory
+      a.X = s.xe_perm;
+      a.x_rstride = 64;
+      a.x_kstride = (long long)R * 64;
+      a.x_scale = fp8 ? s.xe_perm_scale : nullptr;
+    }
     a.out = s.z;
     a.out_ld = I;
     a.out_kmajor_rows = R;
     a.out_dtype = m->expert_dtype == SPA_BF16 ? DT_BF16 : DT_F32;
     HookScope hs(th, KC_GATEUP, st);
-    if (!gathered)
+    if (rows == ExpertRows::kGather)
       SPA_HIP(launch_gather_kmajor(xe, r.row_tok, R, H, esz_of(m->expert_dtype), s.xe_perm, fp8 ? xe_scale : nullptr,
                                    fp8 ? s.xe_perm_scale : nullptr, st));
     SPA_HIP(launch_gemm(m->expert_dtype, EPI_SWIGLU, a, st));
@@ -862,13 +884,15 @@ spa_status run_segment_b(spa_ctx* ctx, const spa_model_desc* m, const spa_layer*
   float* x = b->x + (size_t)tok0 * m->hidden;
   if (!with_router) {
     int32_t* rec = b->topk_out ? b->topk_out + ((size_t)layer_index * b->batch + tok0) * m->top_k : nullptr;
-    if ((rc = op_route(ctx, m, l, s.hn_f32, n_tok, s.logits, s.route, rec, s, st, th, true))) return rc;
+    if ((rc = op_route(ctx, m, l, s.hn_f32, n_tok, s.logits, s.route, rec, s, st, th, route_gathers(m))))
+      return rc;
   }
-  // the router's permutation kernel already gathered the expert rows
+  // the router's permutation kernel gathered the expert rows, or left them in place (route_gathers)
   if ((rc = op_comm(ctx, m, s.xe_perm, (size_t)n_tok * m->top_k * m->hidden * esz_of(m->expert_dtype),
                      comm_bytes_dispatch(m, n_tok), s, st, th))) return rc;   // MoE dispatch
   GemmPlan dp{};
-  if ((rc = op_expert(ctx, m, l, expert_input(m, s), s.hn8_scale, n_tok, s.route, s.y, s, st, th, &dp, true)))
+  if ((rc = op_expert(ctx, m, l, expert_input(m, s), s.hn8_scale, n_tok, s.route, s.y, s, st, th, &dp,
+                      route_gathers(m) ? ExpertRows::kGathered : ExpertRows::kInPlace)))
     return rc;
   const size_t cb = comm_bytes_combine(m, n_tok);
   if ((rc = op_comm(ctx, m, s.y, cb, cb, s, st, th))) return rc;   // MoE combine

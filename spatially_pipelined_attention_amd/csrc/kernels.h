@@ -120,6 +120,7 @@ struct RouteArgs {
   const float* gsrc_scale;  // E4M3: per source row
   float* gdst_scale;        // E4M3: per dispatch row
 };
+// top-k, then the permutation (and the gather when gsrc is set)
 hipError_t launch_route(const RouteArgs& a, hipStream_t st);
 
 // The MoE head (output projection finish, router GEMV, top-k, permutation and
