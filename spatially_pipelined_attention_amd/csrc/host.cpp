@@ -93,7 +93,7 @@ spa_status launch_comm(spa_ctx* ctx, const void* src, void* dst, size_t copy_byt
 // launch's blocks into deal_ranges() ranges (k_attn_dealt): its partial slots
 // and the per-window merge table.
 static bool dealt_launch(const spa_layer* l, int n_tok) { return l->kind == SPA_FULL && n_tok <= kDealMaxTok; }
-static int deal_ranges(int device_cus) { return kDealWgsPerCu * device_cus; }
+static int deal_ranges(int device_cus) { return kDealRangesPerCu * device_cus; }
 static size_t deal_part_bytes(int ranges, int n_tok, int Hkv, int G, int D) {
   return ((size_t)ranges + (size_t)n_tok * Hkv) * G * (D + 2) * 4 + (size_t)n_tok * Hkv * 2 * 4;
 }

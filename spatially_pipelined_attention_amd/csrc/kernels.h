@@ -203,7 +203,11 @@ struct AttnArgs {
 };
 constexpr int kSpanWords = 136;
 constexpr int kDealMaxTok = 256;   // tokens per launch of the dealt kernel (one per thread of its prologue)
-constexpr int kDealMaxRanges = 1024;   // upper bound of deal_v (workspace sizing)
+#ifndef SPA_DEAL_RANGES_PER_CU
+#define SPA_DEAL_RANGES_PER_CU 2
+#endif
+constexpr int kDealRangesPerCu = SPA_DEAL_RANGES_PER_CU;   // ranges of the split per CU of the device
+constexpr int kDealMaxRanges = 2048;   // upper bound of deal_v (workspace sizing)
 #ifndef SPA_DEAL_WGS_PER_CU
 #define SPA_DEAL_WGS_PER_CU 2
 #endif
