@@ -278,7 +278,7 @@ WsLayout ws_layout(const spa_model_desc* m, int n_tok, int max_kv_len, int n_mic
                                comm_bytes_combine(m, n_tok)}));
   s.bytes = o;
   L.err = 0;
-  L.slot0 = 256;
+  L.slot0 = kHeaderWords * 4;
   L.slot_bytes = s.bytes;
   L.total = L.slot0 + (size_t)n_micro * s.bytes;
   return L;
@@ -290,9 +290,11 @@ Slot slot_ptrs(const WsLayout& L, void* ws, int slot) {
   const SlotLayout& o = L.s;
   s.base = b;
   s.err = (int*)((char*)ws + L.err);
-  // two hand-off counters of the MoE-head launch per slot, in the header
-  // words that every run clears (words 32..63: slots 0..15)
+  // two hand-off counters of the MoE-head launch per slot, and one arrival
+  // counter of the routing launch, in the header words that every run clears
+  // (words 32..63: slots 0..15; words 64..127: slots 0..63)
   s.head_ctr = slot < 16 ? (unsigned*)((char*)ws + L.err) + 32 + 2 * slot : nullptr;
+  s.route_ctr = slot < 64 ? (unsigned*)((char*)ws + L.err) + 64 + slot : nullptr;
   s.xn = b + o.xn;
   s.q = b + o.q;
   s.o = b + o.o;
@@ -340,7 +342,7 @@ int stream_cus(hipStream_t st, int fallback) {
 }
 
 spa_status clear_errors(void* ws, hipStream_t st) {
-  SPA_HIP(launch_fill_i32((int*)ws, 64, 0, st));
+  SPA_HIP(launch_fill_i32((int*)ws, kHeaderWords, 0, st));
   return SPA_OK;
 }
 
@@ -620,6 +622,10 @@ static void route_args(spa_ctx* ctx, const spa_model_desc* m, const spa_layer* l
   ra.row_tok = r.row_tok;
   ra.row_slot = r.row_slot;
   ra.inv = r.inv;
+#ifndef SPA_ROUTE_ONE_LAUNCH
+#define SPA_ROUTE_ONE_LAUNCH 1
+#endif
+  ra.arrive = SPA_ROUTE_ONE_LAUNCH && !gather ? s.route_ctr : nullptr;
   if (gather) {
     const bool fp8 = m->expert_dtype == SPA_E4M3;
     ra.gsrc = expert_input(m, s);

@@ -49,6 +49,10 @@ struct SlotLayout {
   size_t bytes;
 };
 
+// Workspace header: the error word and the launch counters, cleared at the
+// start of every run (words 32..63: MoE-head hand-offs, 64..127: routing)
+constexpr int kHeaderWords = 128;
+
 struct WsLayout {
   size_t err;           // int32 error word (shared by all slots)
   size_t slot0;         // first slot
@@ -99,6 +103,7 @@ struct Slot {
   char* base;
   int* err;
   unsigned* head_ctr;   // two zeroed counters for the MoE-head launch's hand-offs (null: none)
+  unsigned* route_ctr;  // zeroed arrival counter of the routing launch (null: none)
   void* xn;
   void* q;
   void* o;

@@ -119,6 +119,9 @@ struct RouteArgs {
   void* gdst;               // [gK*gesz/64][n_tok*k][64 bytes]
   const float* gsrc_scale;  // E4M3: per source row
   float* gdst_scale;        // E4M3: per dispatch row
+  // zeroed arrival counter (no gather only): the last top-k workgroup to
+  // finish runs the permutation and clears it again; null: a second launch
+  unsigned* arrive;
 };
 // top-k, then the permutation (and the gather when gsrc is set)
 hipError_t launch_route(const RouteArgs& a, hipStream_t st);

@@ -268,7 +268,10 @@ __device__ __forceinline__ void route_token(const RouteArgs& a, int t, int lane,
   }
 }
 
-// The picks of token t and their softmax weights (lane 0 writes).
+// The picks of token t and their softmax weights (lane 0 writes). AGENT:
+// the picks are stored at agent scope, through to where the XCDs' caches
+// agree, for a workgroup of the same launch to read.
+template <bool AGENT = false>
 __device__ __forceinline__ void store_picks(const RouteArgs& a, int t, int lane, const float (&pv)[8],
                                             const int (&pi)[8]) {
   if (lane != 0) return;
@@ -276,22 +279,65 @@ __device__ __forceinline__ void store_picks(const RouteArgs& a, int t, int lane,
   float den = 0.f;
   for (int p = 0; p < k; ++p) den += __expf(pv[p] - pv[0]);
   for (int p = 0; p < k; ++p) {
-    a.topk_idx[t * k + p] = pi[p];
+    if constexpr (AGENT) __hip_atomic_store(a.topk_idx + t * k + p, pi[p], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else a.topk_idx[t * k + p] = pi[p];
     a.topk_w[t * k + p] = __expf(pv[p] - pv[0]) / den;
     if (a.topk_rec) a.topk_rec[t * k + p] = pi[p];
   }
 }
 
+// tokens per routing workgroup (one wave each)
+#ifndef SPA_TOPK_TPW
+#define SPA_TOPK_TPW 2
+#endif
+constexpr int kTopkTpw = SPA_TOPK_TPW;
+
 // Router top-k and softmax over the picks: one wave per token.
 template <int SM>
 __global__ __launch_bounds__(256) void k_route_topk(RouteArgs a) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + wave;
-  if (t >= a.n_tok) return;
+  const int t = blockIdx.x * kTopkTpw + wave;
+  if (wave >= kTopkTpw || t >= a.n_tok) return;
   float pv[8];
   int pi[8];
   route_token<SM>(a, t, lane, true, pv, pi);
   store_picks(a, t, lane, pv, pi);
+}
+
+__device__ __forceinline__ void permute_body(const RouteArgs& a, char* lds, bool store);
+
+// Top-k as above, and the permutation run by the workgroup that finishes
+// last, instead of a second launch. Each wave stores its picks at agent scope
+// and waits for the stores to complete; the workgroup then counts itself in
+// on the arrival counter. The workgroup that takes the last count reads every
+// pick at agent scope, computes the permutation and clears the counter for
+// the next launch. No workgroup waits for another, and the permutation is
+// the separate kernel's, bit for bit.
+template <int SM>
+__global__ __launch_bounds__(256) void k_route_topk_perm(RouteArgs a) {
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  __shared__ int s_last;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int t = blockIdx.x * kTopkTpw + wave;
+  if (wave < kTopkTpw && t < a.n_tok) {
+    float pv[8];
+    int pi[8];
+    route_token<SM>(a, t, lane, true, pv, pi);
+    store_picks<true>(a, t, lane, pv, pi);
+  }
+  __builtin_amdgcn_s_waitcnt(0);   // this wave's stores have completed
+  __syncthreads();
+  if (threadIdx.x == 0)
+    s_last = __hip_atomic_fetch_add(a.arrive, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == gridDim.x - 1;
+  __syncthreads();
+  if (!s_last) return;
+  int* grp = (int*)lds;
+  const int P = a.n_tok * a.k;
+  for (int p = threadIdx.x; p < P; p += blockDim.x)
+    grp[p] = __hip_atomic_load(a.topk_idx + p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) % a.E_res;
+  __syncthreads();
+  permute_body(a, lds, true);
+  if (threadIdx.x == 0) __hip_atomic_store(a.arrive, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Dispatch permutation of the picks (pick p = token * k + slot runs on
@@ -299,9 +345,9 @@ __global__ __launch_bounds__(256) void k_route_topk(RouteArgs a) {
 // exclusive offsets, rows grouped by expert with (token, slot) ascending
 // inside, and the inverse map; then the gather of the expert input rows. Ranks
 // come from per-expert bitmasks over the picks, so no order depends on timing.
-// Every workgroup computes the whole (small) permutation; workgroup 0 stores
-// it, and the gather is dealt over the workgroups.
-__device__ __forceinline__ void permute_body(const RouteArgs& a, char* lds) {
+// Every workgroup computes the whole (small) permutation; the one with store
+// set stores it, and the gather is dealt over the workgroups.
+__device__ __forceinline__ void permute_body(const RouteArgs& a, char* lds, bool store) {
   const int tid = threadIdx.x, nthr = blockDim.x;
   const int k = a.k, P = a.n_tok * k, E_res = a.E_res;
   int* grp = (int*)lds;                         // [P]
@@ -310,7 +356,6 @@ __device__ __forceinline__ void permute_body(const RouteArgs& a, char* lds) {
   int* offs = counts + E_res;                   // [E_res + 1]
   const int W64 = (P + 63) >> 6;
   unsigned long long* masks = (unsigned long long*)(((uintptr_t)(offs + E_res + 1) + 7) & ~(uintptr_t)7);
-  const bool store = blockIdx.x == 0;
   for (int i = tid; i < E_res; i += nthr) counts[i] = 0;
   for (int i = tid; i < E_res * W64; i += nthr) masks[i] = 0ull;
   __syncthreads();
@@ -380,7 +425,7 @@ __global__ __launch_bounds__(256) void k_route_permute(RouteArgs a) {
   const int P = a.n_tok * a.k;
   for (int p = threadIdx.x; p < P; p += blockDim.x) grp[p] = a.topk_idx[p] % a.E_res;
   __syncthreads();
-  permute_body(a, lds);
+  permute_body(a, lds, blockIdx.x == 0);
 }
 
 int route_lds_bytes(int n_tok, int k, int E_res) {
@@ -396,7 +441,11 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t st) {
     wgs = (int)std::min<long long>(64, std::max<long long>(1, chunks / (256 * 8)));
   }
   const int lds = route_lds_bytes(a.n_tok, a.k, a.E_res);
-  SPA_LAUNCH_SPLITS(a.pv.S, k_route_topk, dim3((a.n_tok + 3) / 4), dim3(256), 0, st, a);
+  if (a.arrive && !a.gsrc) {   // one launch: the last top-k workgroup permutes
+    SPA_LAUNCH_SPLITS(a.pv.S, k_route_topk_perm, dim3((a.n_tok + kTopkTpw - 1) / kTopkTpw), dim3(256), lds, st, a);
+    return hipGetLastError();
+  }
+  SPA_LAUNCH_SPLITS(a.pv.S, k_route_topk, dim3((a.n_tok + kTopkTpw - 1) / kTopkTpw), dim3(256), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_route_permute, dim3(wgs), dim3(256), lds, st, a);
@@ -489,7 +538,7 @@ __global__ __launch_bounds__(kRowThreads) void k_moe_head(MoeHeadArgs a) {
     const int P = a.ra.n_tok * a.ra.k;
     for (int p = threadIdx.x; p < P; p += blockDim.x) grp[p] = a.ra.topk_idx[p] % a.ra.E_res;
     __syncthreads();
-    permute_body(a.ra, lds);
+    permute_body(a.ra, lds, blockIdx.x == 0);
   }
   // the last workgroup out clears the counters (every workgroup is past its polls)
   __syncthreads();
@@ -545,6 +594,11 @@ hipError_t init_kernel_attributes() {
                           (const void*)k_moe_head<16, 16, 1>, (const void*)k_moe_head<16, 16, 2>,
                           (const void*)k_moe_head<16, 16, 4>})
       if (r == hipSuccess) r = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    for (const void* f : {(const void*)k_route_topk_perm<1>, (const void*)k_route_topk_perm<2>,
+                          (const void*)k_route_topk_perm<4>, (const void*)k_route_topk_perm<8>,
+                          (const void*)k_route_topk_perm<16>})   // beside a little static LDS; the
+      // permutation needs at most ~100 KB (4096 picks, 128 resident experts)
+      if (r == hipSuccess) r = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, 128 * 1024);
     return r;
   }();
   return e;
