@@ -292,13 +292,18 @@ def main():
         # a decode step needs the previous step's outputs, so steps are not
         # overlapped: each one is enqueued after the previous one completed
         t0 = time.perf_counter()
+        marks = []
         for _ in range(steps):
             run()
             torch.cuda.synchronize()
-        ms = (time.perf_counter() - t0) / steps * 1e3
+            marks.append(time.perf_counter())
+        ms = (marks[-1] - t0) / steps * 1e3
+        step_ms = np.diff(np.array([t0] + marks)) * 1e3
         kt = B.spa_pipeline_timing(pipe.h) if timed_cls is not None else (None, 0)
         pipe.close()
-        results[label] = {"ms": ms, "kernel_ms": kt[0], "kernel_n": kt[1]}
+        results[label] = {"ms": ms, "kernel_ms": kt[0], "kernel_n": kt[1],
+                          "step_ms": {"mean": round(float(step_ms.mean()), 4), "std": round(float(step_ms.std()), 4),
+                                      "min": round(float(step_ms.min()), 4), "max": round(float(step_ms.max()), 4)}}
         return ms, kt
 
     # comparison schedules first (clean timing), then the reported one with the
@@ -390,6 +395,7 @@ def main():
         "min_GB_per_iter": round(min_b / 1e9, 3),
         "tokens_per_s": round(wl.batch / (ms * 1e-3), 1), "per_user_tokens_per_s": round(1 / (ms * 1e-3), 2),
         "schedules_ms": {k: round(v["ms"], 4) for k, v in results.items()},
+        "step_ms": results["reported"]["step_ms"],   # per-step spread of the timed steps (host clock)
         "roofline": {"bound": "hbm", "kernel": f"{attn_kernel_name(wl.batch // m, has_full)} "
                                                f"({'full' if has_full else 'sliding'}-layer decode attention, bf16 KV)",
                      "achieved": round(achieved, 1) if achieved else None, "peak": HBM_PEAK_GBPS, "unit": "GB/s",

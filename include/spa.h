@@ -185,7 +185,11 @@ spa_status spa_device_cus(spa_ctx* ctx, int32_t* n_cus);
 
 /* -------------------------------------------------------------- workspace */
 /* Bytes of workspace a call with these shapes needs: n_micro microbatches of
- * batch/n_micro tokens each (n_micro = 1 for the single-op calls). */
+ * batch/n_micro tokens each (n_micro = 1 for the single-op calls). A
+ * workspace serves one call at a time: calls that share one must be ordered
+ * (one stream, or events), since its header holds the error word and the
+ * launch counters (routing arrivals, MoE-head hand-offs) that every call
+ * clears and uses. */
 spa_status spa_workspace_query(const spa_model_desc* m, int32_t batch, int32_t max_kv_len, int32_t n_micro,
                                size_t* bytes);
 /* Prepare a fresh workspace (clears its counters); enqueued on `stream`. */
