@@ -59,8 +59,13 @@ __device__ __forceinline__ bool gemm_block(const GemmArgs& a, int BR, int lane, 
   int grp = 0, rb = blk, r0 = 0, nrows = a.n_rows;
   if (a.group_off) {
     const int g0 = 2 * lane, g1 = 2 * lane + 1;
-    const int n0 = g0 < a.n_groups ? a.group_off[g0 + 1] - a.group_off[g0] : 0;
-    const int n1 = g1 < a.n_groups ? a.group_off[g1 + 1] - a.group_off[g1] : 0;
+    // offsets of this lane's two groups and of the one after them (kept: the
+    // chosen group's first row comes from its lane, not from another load)
+    const int o0 = g0 <= a.n_groups ? a.group_off[g0] : 0;
+    const int o1 = g1 <= a.n_groups ? a.group_off[g1] : 0;
+    const int o2 = g1 + 1 <= a.n_groups ? a.group_off[g1 + 1] : 0;
+    const int n0 = g0 < a.n_groups ? o1 - o0 : 0;
+    const int n1 = g1 < a.n_groups ? o2 - o1 : 0;
     const int c0 = (n0 + BR - 1) / BR, c1 = (n1 + BR - 1) / BR;
     int incl = c0 + c1;
 #pragma unroll
@@ -73,12 +78,15 @@ __device__ __forceinline__ bool gemm_block(const GemmArgs& a, int BR, int lane, 
     if (hit == 0ull) return false;                 // past the last non-empty block
     const int hl = __builtin_ctzll(hit);
     const int e = __shfl(excl, hl, 64), cc0 = __shfl(c0, hl, 64);
-    grp = blk - e < cc0 ? 2 * hl : 2 * hl + 1;
-    rb = blk - e < cc0 ? blk - e : blk - e - cc0;
+    const bool first = blk - e < cc0;   // the lane's first group
+    grp = first ? 2 * hl : 2 * hl + 1;
+    rb = first ? blk - e : blk - e - cc0;
+    r0 = first ? __shfl(o0, hl, 64) : __shfl(o1, hl, 64);
+    nrows = first ? __shfl(n0, hl, 64) : __shfl(n1, hl, 64);
     grp = __builtin_amdgcn_readfirstlane(grp);
     rb = __builtin_amdgcn_readfirstlane(rb);
-    r0 = a.group_off[grp];
-    nrows = a.group_off[grp + 1] - r0;
+    r0 = __builtin_amdgcn_readfirstlane(r0);
+    nrows = __builtin_amdgcn_readfirstlane(nrows);
   }
   if (nrows <= rb * BR) return false;
   *s_out = s;

@@ -155,13 +155,14 @@ __device__ __forceinline__ void oproj_finish_row(const OprojFinishArgs& a, int r
   float h[kRowCols];
   float ss = 0.f;
   // every load of the thread first (columns past the row clamped to its
-  // last), then the sums
-  float xv[kRowCols], yv[kRowCols];
+  // last), the norm weights included, then the sums
+  float xv[kRowCols], yv[kRowCols], gv[kRowCols];
 #pragma unroll
   for (int i = 0; i < kRowCols; ++i) {
     const int c = min(threadIdx.x + kRowThreads * i, a.H - 1);
     xv[i] = a.x[row + c];
     yv[i] = part_sum<SM>(a.pv, r, c);
+    gv[i] = a.gamma[c];
   }
 #pragma unroll
   for (int i = 0; i < kRowCols; ++i) {
@@ -180,7 +181,7 @@ __device__ __forceinline__ void oproj_finish_row(const OprojFinishArgs& a, int r
   for (int i = 0; i < kRowCols; ++i) {
     const int c = threadIdx.x + kRowThreads * i;
     if (c < a.H) {
-      h[i] = h[i] * rstd * a.gamma[c];
+      h[i] = h[i] * rstd * gv[i];
       a.hn_f32[row + c] = h[i];
       if (a.hn_bf16) a.hn_bf16[row + c] = f32_to_bf16(h[i]);
       amax = fmaxf(amax, fabsf(h[i]));
@@ -617,6 +618,15 @@ __global__ __launch_bounds__(kRowThreads) void k_combine(CombineArgs a) {
   __shared__ int s_row[8];
   const int t = blockIdx.x;
   const long long row = (long long)t * a.H;
+  // the residual row and the next norm's weights do not depend on the picks:
+  // loaded with them, ahead of the barrier (columns past the row clamped)
+  float hv[kRowCols], gv[kRowCols];
+#pragma unroll
+  for (int i = 0; i < kRowCols; ++i) {
+    const int c = min(threadIdx.x + kRowThreads * i, a.H - 1);
+    hv[i] = a.h[row + c];
+    gv[i] = a.gamma_next ? a.gamma_next[c] : 0.f;
+  }
   if (threadIdx.x < a.k) {
     const int r = a.inv[t * a.k + threadIdx.x];
     s_w[threadIdx.x] = a.w[t * a.k + threadIdx.x];
@@ -647,7 +657,7 @@ __global__ __launch_bounds__(kRowThreads) void k_combine(CombineArgs a) {
     const int c = threadIdx.x + kRowThreads * i;
     v[i] = 0.f;
     if (c < a.H) {
-      float x = a.h[row + c];
+      float x = hv[i];
       if (batched) {
 #pragma unroll
         for (int s = 0; s < KB; ++s)
@@ -667,7 +677,7 @@ __global__ __launch_bounds__(kRowThreads) void k_combine(CombineArgs a) {
   for (int i = 0; i < kRowCols; ++i) {
     const int c = threadIdx.x + kRowThreads * i;
     if (c < a.H) {
-      const float xn = v[i] * rstd * a.gamma_next[c];
+      const float xn = v[i] * rstd * gv[i];
       const int ks = a.xn_dtype == DT_BF16 ? 32 : 16;   // elements per 64-byte k-step
       const long long xi = a.xn_kmajor_rows > 0 ? ((long long)(c / ks) * a.xn_kmajor_rows + t) * ks + c % ks : row + c;
       if (a.xn_dtype == DT_BF16) ((uint16_t*)a.xn_out)[xi] = f32_to_bf16(xn);
