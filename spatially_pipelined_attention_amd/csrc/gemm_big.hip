@@ -116,6 +116,30 @@ __global__ __launch_bounds__(256, 2) void k_gemm_big(GemmArgs a) {
   const int xrd = (wr * 64 + lo16) * kLdsRow + kq;   // fragment mf at + mf * 16 rows
   const int wrd = (wc * 64 + lo16) * kLdsRow + kq;
 
+  // E4M3: this lane's weight channel scales and activation row scales, loaded
+  // before the k-loop so that the epilogue does not wait for them
+  // (lane: row wr*64 + mf*16 + lo16 of the block; tile column wc*64 + cf*16 + c4 + i)
+  const int c4 = (lane >> 4) * 4;
+  float wsc[4][4], xsc[4];
+#pragma unroll
+  for (int cf = 0; cf < 4; ++cf)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      wsc[cf][i] = 1.f;
+      if constexpr (WT == DT_E4M3) {
+        const int wrow = big_wrow<EPI>(a, nb, wc * 64 + cf * 16 + c4 + i);
+        wsc[cf][i] = wrow < wtotal ? a.w_scale[(long long)grp * a.ws_gstride + wrow] : 0.f;
+      }
+    }
+#pragma unroll
+  for (int mf = 0; mf < 4; ++mf) {
+    xsc[mf] = 1.f;
+    if constexpr (WT == DT_E4M3) {
+      const long long orow = r0 + rb * kBigRows + min(wr * 64 + mf * 16 + lo16, rows_here - 1);
+      xsc[mf] = a.x_scale[a.row_src ? a.row_src[orow] : orow];
+    }
+  }
+
   if (nks > 0) {
     load(S0, 0);
     stash(S0);
@@ -147,26 +171,12 @@ __global__ __launch_bounds__(256, 2) void k_gemm_big(GemmArgs a) {
     if (k + 1 < nks) step(S1, k + 1);
   }
 
-  // lane: row wr*64 + mf*16 + lo16 of the block; tile column wc*64 + cf*16 + c4 + i
-  const int c4 = (lane >> 4) * 4;
-  float wsc[4][4];
-#pragma unroll
-  for (int cf = 0; cf < 4; ++cf)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      wsc[cf][i] = 1.f;
-      if constexpr (WT == DT_E4M3) {
-        const int wrow = big_wrow<EPI>(a, nb, wc * 64 + cf * 16 + c4 + i);
-        wsc[cf][i] = wrow < wtotal ? a.w_scale[(long long)grp * a.ws_gstride + wrow] : 0.f;
-      }
-    }
 #pragma unroll
   for (int mf = 0; mf < 4; ++mf) {
     const int m = wr * 64 + mf * 16 + lo16;
     if (m >= rows_here) continue;
     const long long orow = r0 + rb * kBigRows + m;
-    float xsc = 1.f;
-    if constexpr (WT == DT_E4M3) xsc = a.x_scale[a.row_src ? a.row_src[orow] : orow];
+    const float xs = xsc[mf];
     if constexpr (EPI == EPI_SWIGLU) {
 #pragma unroll
       for (int cf = 0; cf < 2; ++cf) {   // fragments 0, 1 gate; 2, 3 the matching up
@@ -175,7 +185,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_big(GemmArgs a) {
         float z[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float g = acc[mf][cf][i] * wsc[cf][i] * xsc, u = acc[mf][cf + 2][i] * wsc[cf + 2][i] * xsc;
+          const float g = acc[mf][cf][i] * wsc[cf][i] * xs, u = acc[mf][cf + 2][i] * wsc[cf + 2][i] * xs;
           z[i] = g / (1.0f + __expf(-g)) * u;
         }
         const long long zr = a.out_kmajor_rows;
@@ -198,7 +208,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_big(GemmArgs a) {
         const int c = nb * kBigCols + wc * 64 + cf * 16 + c4;
         float v[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) v[i] = acc[mf][cf][i] * wsc[cf][i] * xsc;
+        for (int i = 0; i < 4; ++i) v[i] = acc[mf][cf][i] * wsc[cf][i] * xs;
         if (c + 3 < ncols) {
           *reinterpret_cast<f32x4*>(o + c) = f32x4{v[0], v[1], v[2], v[3]};
         } else {

@@ -76,11 +76,50 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int bid, int tid, c
   // X fragment of row-tile mt: 16 rows of one k-step; rows sit x_rstride
   // bytes apart and k-steps x_kstride bytes apart (row-major or k-step-major)
   const char* xp[MT];
+  float xsc[MT];   // E4M3: the activation scale of this lane's row of each row tile
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
     const int orow = r0 + rb * BR + min(mt * 16 + lo16, rows_here - 1);   // padding rows repeat a real row
     const int src = a.row_src ? a.row_src[orow] : orow;
     xp[mt] = (const char*)a.X + (long long)src * a.x_rstride + (long long)ks0 * a.x_kstride + kq;
+    xsc[mt] = 1.f;
+    if constexpr (WT == DT_E4M3) xsc[mt] = a.x_scale[src];
+  }
+
+  // E4M3 weight channel scales of the fragments this wave will finish, also
+  // loaded before the k-loop: slot u holds fragment f = wave + 4u (finished
+  // a row tile at a time), or the fragment of pair wave + 4u (all row tiles
+  // at once); its columns c4 + i (h = 1: the SwiGLU up partner)
+  constexpr int NF = EPI == EPI_SWIGLU ? CT / 2 : CT;   // fragments (SwiGLU: gate/up pairs) to finish
+  constexpr int NU = (NF + 3) / 4;                      // per wave, a row tile at a time
+  constexpr int NS = gemm_finish_at_once<CT, MT>() ? (MT * NF + 3) / 4 : NU;
+  const int c4 = (lane >> 4) * 4;                       // a lane holds row lo16, columns c4 .. c4 + 3 of a fragment
+  float wsc[NS][2][4];
+#pragma unroll
+  for (int u = 0; u < NS; ++u)
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) wsc[u][h][i] = 1.f;
+  if constexpr (WT == DT_E4M3) {
+#pragma unroll
+    for (int u = 0; u < NS; ++u) {
+      const int pair = wave + 4 * u;
+      int f = pair;
+      if constexpr (gemm_finish_at_once<CT, MT>()) {
+        if (pair >= MT * NF) continue;
+        f = pair % NF;
+      } else if (f >= NF) {
+        continue;
+      }
+#pragma unroll
+      for (int h = 0; h < (EPI == EPI_SWIGLU ? 2 : 1); ++h)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int wr = w_row_of<EPI, CT>(a, nb, (f + h * (CT / 2)) * 16 + c4 + i);
+          wsc[u][h][i] = wr < w_rows_total<EPI>(a) ? a.w_scale[(long long)grp * a.ws_gstride + wr] : 0.f;
+        }
+    }
   }
 
   f32x4 acc[MT][CT];
@@ -161,44 +200,15 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int bid, int tid, c
   // two alternating buffers, so one barrier per row tile suffices: a buffer
   // is written again two row tiles later, after a barrier every wave reaches
   // only once its reads are done.
-  constexpr int NF = EPI == EPI_SWIGLU ? CT / 2 : CT;   // fragments (SwiGLU: gate/up pairs) to finish
-  constexpr int NU = (NF + 3) / 4;                      // per wave
   // at once: [4 waves][MT][CT][64 lanes]; by row tile: [2][4 waves][CT][64 lanes]
   f32x4* rd = reinterpret_cast<f32x4*>(red);
-  const int c4 = (lane >> 4) * 4;                       // a lane holds row lo16, columns c4 .. c4 + 3 of a fragment
-  // E4M3 weight scale of column c4 + i of fragment f (h = 1: its up partner)
-  auto wscale = [&](int f, int h, int i) {
-    const int wr = w_row_of<EPI, CT>(a, nb, (f + h * (CT / 2)) * 16 + c4 + i);
-    return wr < w_rows_total<EPI>(a) ? a.w_scale[(long long)grp * a.ws_gstride + wr] : 0.f;
-  };
-  // the scales of this wave's fragments, read once (row-tile mode)
-  float wsc[NU][2][4];
-#pragma unroll
-  for (int u = 0; u < NU; ++u)
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) wsc[u][h][i] = 1.f;
-  if constexpr (WT == DT_E4M3 && !gemm_finish_at_once<CT, MT>()) {
-#pragma unroll
-    for (int u = 0; u < NU; ++u) {
-      const int f = wave + 4 * u;
-      if (f >= NF) continue;
-#pragma unroll
-      for (int h = 0; h < (EPI == EPI_SWIGLU ? 2 : 1); ++h)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) wsc[u][h][i] = wscale(f, h, i);
-    }
-  }
   // finish fragment f (a gate/up pair for SwiGLU) of row tile mt from the 4
-  // waves' copies at buf[(w * wstride + ct) * 64 + lane]; u: its slot in
-  // this wave's scale table, or -1 to read the scales here
-  auto finish = [&](const f32x4* buf, int wstride, int mt, int f, int u) {
+  // waves' copies at buf[(w * wstride + ct) * 64 + lane], with the scales of
+  // slot u and the activation scale xs
+  auto finish = [&](const f32x4* buf, int wstride, int mt, int f, int u, float xs) {
     const int m = mt * 16 + lo16;
     if (m >= rows_here) return;   // padding rows are not written
     const long long orow = r0 + rb * BR + m;
-    float xs = 1.f;
-    if constexpr (WT == DT_E4M3) xs = a.x_scale[a.row_src ? a.row_src[orow] : orow];
     f32x4 v[2];
 #pragma unroll
     for (int h = 0; h < (EPI == EPI_SWIGLU ? 2 : 1); ++h) {
@@ -208,17 +218,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int bid, int tid, c
       for (int w = 1; w < 4; ++w) t += buf[(w * wstride + ct) * 64 + lane];
       v[h] = t;
     }
-    float sc[2][4];
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) sc[h][i] = 1.f;
-    if constexpr (WT == DT_E4M3) {
-#pragma unroll
-      for (int h = 0; h < (EPI == EPI_SWIGLU ? 2 : 1); ++h)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sc[h][i] = u >= 0 ? wsc[u][h][i] : wscale(f, h, i);
-    }
+    const float (&sc)[2][4] = wsc[u];
     if constexpr (EPI == EPI_PARTIAL) {
       // split s, row (dispatch or token row), padded column: [S][part_rows][part_ld];
       // every split is scaled, so the splits' sum is the scaled product
@@ -273,7 +273,10 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int bid, int tid, c
       const int pair = wave + 4 * i;
       if (pair < MT * NF) {
         const int mt = pair / NF, f = pair - mt * NF;
-        finish(rd + mt * CT * 64, MT * CT, mt, f, -1);   // wave w's copy of row tile mt: MT * CT fragments apart
+        float xs = xsc[0];   // xsc[mt] without a dynamic register index
+#pragma unroll
+        for (int j = 1; j < MT; ++j) xs = mt == j ? xsc[j] : xs;
+        finish(rd + mt * CT * 64, MT * CT, mt, f, i, xs);   // wave w's copy of row tile mt: MT * CT fragments apart
       }
     }
   } else {
@@ -286,7 +289,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int bid, int tid, c
 #pragma unroll
       for (int u = 0; u < NU; ++u) {
         const int f = wave + 4 * u;
-        if (f < NF) finish(buf, CT, mt, f, u);
+        if (f < NF) finish(buf, CT, mt, f, u, xsc[mt]);
       }
     }
   }
