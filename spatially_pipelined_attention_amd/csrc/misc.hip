@@ -10,7 +10,9 @@
 //   k_route_topk   - router logits, top-k in logit order (ties to the lower
 //                    index) and softmax over the picks, one wave per token;
 //   k_route_permute- the dispatch permutation (counts, offsets, rows grouped
-//                    by expert with (token, pick) ascending inside, inverse);
+//                    by expert with (token, pick) ascending inside, inverse),
+//                    run by the last k_route_topk_perm workgroup to finish,
+//                    or as its own launch where it also gathers the rows;
 //   k_combine      - "Combine": weighted sum of the expert outputs in pick
 //                    order plus residual, and the next layer's RMSNorm;
 // plus row conversion, KV row I/O, counter fill and a CU placement probe.
