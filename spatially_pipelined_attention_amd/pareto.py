@@ -42,6 +42,8 @@ def main(argv=None):
     ap.add_argument("--cu-min", type=int, default=32)
     ap.add_argument("--reps", type=int, default=3)
     ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--per-kind", type=int, default=0, choices=(0, 1),
+                    help="1: search stage A's CUs for full and sliding layers separately")
     ap.add_argument("--out", required=True)
     ap.add_argument("--virtual-comm", default="", metavar="LATENCY_US,GBPS",
                     help="add the rank's communication endpoints to every layer")
@@ -70,14 +72,14 @@ def main(argv=None):
         ws = max((dw.workspace(n_micro=mm) for mm in micros), key=lambda t: t.numel())
         sp = B.spa_tune_space(len(cuts), (B.C.c_int32 * 3)(*(cuts + [0] * (3 - len(cuts)))),
                               len(micros), (B.C.c_int32 * 4)(*(micros + [0] * (4 - len(micros)))),
-                              a.cu_step, a.cu_min, a.warmup, a.reps, 1, 0)
+                              a.cu_step, a.cu_min, a.warmup, a.reps, 1, a.per_kind)
         t0 = time.time()
         best, pts = B.spa_pipeline_tune(ctx, dw.m, dw.layers_c, dw.batch, ws, sp, torch.cuda.current_stream())
         tune_s = time.time() - t0
         rows = []
         for p in pts:
             r = {"batch": bsz, "schedule": "temporal" if p.cu_a == 0 else "spatial", "cut": p.cut,
-                 "n_micro": p.n_micro, "cu_a": p.cu_a, "ms": round(p.ms, 4),
+                 "n_micro": p.n_micro, "cu_a": p.cu_a, "cu_a_sliding": p.cu_a_sliding, "ms": round(p.ms, 4),
                  "per_user": round(1000.0 / p.ms, 2), "per_gpu": round(1000.0 * bsz / p.ms, 1)}
             rows.append(r)
         temporal = {r["n_micro"]: r for r in rows if r["schedule"] == "temporal"}
@@ -89,7 +91,8 @@ def main(argv=None):
             "best_temporal": best_t, "best_spatial": best_sp, "points": len(rows),
             "setup_s": round(setup, 1), "tune_s": round(tune_s, 1)}
         print(f"[batch {bsz}] T: " + ", ".join(f"m={k} {v['ms']:.3f}" for k, v in sorted(temporal.items()))
-              + (f"; best spatial cut={best_sp['cut']} m={best_sp['n_micro']} cu_a={best_sp['cu_a']} "
+              + (f"; best spatial cut={best_sp['cut']} m={best_sp['n_micro']} cu_a={best_sp['cu_a']}"
+                 f"/{best_sp['cu_a_sliding']} "
                  f"{best_sp['ms']:.3f} ms" if best_sp else "") + f" ({len(rows)} points, {tune_s:.0f} s)",
               flush=True)
         points += rows
