@@ -60,14 +60,16 @@ def traffic_from_profile(name, tokens_per_launch):
     return float(keys["traffic_bytes_per_launch"]), path
 
 
-DEAL_MAX_TOKENS = 256   # launches of up to this many tokens deal their chunks (kDealMaxTok)
+DEAL_MAX_TOKENS = 1024   # full-layer launches of up to this many tokens split their KV blocks evenly (kDealMaxTok)
 
 
 def attn_kernel_name(tokens_per_launch, full=True):
     """The attention kernel a launch of this many tokens runs (full or sliding layers)."""
     if not full:
         return "spa::k_attn<1, 0>"
-    return "spa::k_attn_dealt<1>" if tokens_per_launch <= DEAL_MAX_TOKENS else "spa::k_attn<1, 1>"
+    if tokens_per_launch <= 256:   # one token per prologue thread
+        return "spa::k_attn_dealt<1, 1>"
+    return "spa::k_attn_dealt<1, 4>" if tokens_per_launch <= DEAL_MAX_TOKENS else "spa::k_attn<1, 1>"
 
 
 def load_resample(name):

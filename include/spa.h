@@ -241,7 +241,7 @@ spa_status spa_qkv_append(spa_ctx* ctx, const spa_model_desc* m, const spa_layer
 /* Figure 3 "FMHA" (section 5.1: sliding or full): grouped-query decode
  * attention with sinks over the cached window; q [n_tok][Hq*D] and o_out
  * [n_tok][Hq*D] in kv_dtype. Split-KV, partial softmax states merged with the
- * sink in window order. Full layers of up to 256 tokens: the call's windows,
+ * sink in window order. Full layers of up to 1024 tokens: the call's windows,
  * laid end to end as 32-position blocks, are cut into 2 x (device CUs) equal
  * ranges, so a window may be cut anywhere and a token's last bits depend on
  * the other tokens' lengths in the call (never on the CU pool). Other calls:
@@ -256,10 +256,11 @@ spa_status spa_decode_attn(spa_ctx* ctx, const spa_model_desc* m, const spa_laye
  * under stream capture, tight serving loops, harnesses that forbid
  * allocation): the same operator, kernels and results, with no workspace.
  * Its scratch (the softmax partials of the pieces) lives in a fixed array
- * of the library, one per GPU, held until the process ends: at most 16 MiB of
- * partials. A full layer of up to 256 tokens needs
+ * of the library, one per GPU, held until the process ends: at most 24 MiB of
+ * partials. A full layer of up to 1024 tokens needs
  * (2 * CUs + n_tok * Hkv) * (Hq/Hkv) * (D + 2) * 4 + n_tok * Hkv * 8 bytes
- * (5.4 MB at 256 tokens on 256 CUs); other calls need
+ * (18.4 MB at 1024 tokens on 256 CUs, 8 KV heads of 8 query heads); other
+ * calls need
  * n_tok * Hkv * chunks * (Hq/Hkv) * (D + 2) * 4 bytes, where
  * chunks = ceil(max_kv_len / chunk) for full layers (the chunk is 4096 ..
  * 512 positions, chosen from the shapes as in spa_decode_attn) and

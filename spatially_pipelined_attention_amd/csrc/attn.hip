@@ -402,7 +402,7 @@ __global__ __launch_bounds__(256, SPA_ATTN_MINB) void k_attn(AttnArgs a) {
   }
 }
 
-// Full layers, launches of up to kDealMaxTok tokens. The launch's windows are
+// Full layers, launches of up to kDealMaxTok (1,024) tokens. The launch's windows are
 // laid end to end on one line of 32-position blocks, in (token, KV head)
 // order, T blocks in all, and the line is cut into V equal ranges
 // (v T / V .. (v + 1) T / V; V = a.deal_v, the same for every CU pool of the
@@ -416,33 +416,43 @@ __global__ __launch_bounds__(256, SPA_ATTN_MINB) void k_attn(AttnArgs a) {
 // never on W, so every schedule computes the same bits. Workgroup 0 also
 // writes, per window, its first range and piece count for the merge
 // (deal_tab).
-template <int KVT>
+// TPT: tokens per thread of the prologue (launches of up to 256 TPT tokens;
+// the per-token tables in LDS are sized for them).
+template <int KVT, int TPT>
 __global__ __launch_bounds__(256, SPA_ATTN_MINB) void k_attn_dealt(AttnArgs a) {
+  constexpr int NT = 256 * TPT;
   __shared__ AttnLds s;
-  __shared__ long long s_first[kDealMaxTok + 1];   // first block of token t's windows on the line
-  __shared__ long long s_off[kDealMaxTok];
-  __shared__ int s_len[kDealMaxTok], s_cap[kDealMaxTok], s_nb[kDealMaxTok];   // s_nb: blocks per window, 0 if refused
+  __shared__ long long s_first[NT + 1];   // first block of token t's windows on the line
+  __shared__ long long s_off[NT];
+  __shared__ int s_len[NT], s_cap[NT], s_nb[NT];   // s_nb: blocks per window, 0 if refused
   __shared__ int s_wsum[4];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int G = a.n_q_heads / a.n_kv_heads, Hkv = a.n_kv_heads;
-  const int n = a.n_tok;   // 1 .. kDealMaxTok = 256: one token per thread
+  const int n = a.n_tok;   // 1 .. NT: tokens TPT tid .. TPT tid + TPT - 1 per thread
   if (a.tspan && tid == 0 && blockIdx.x == 0) a.tspan[0] = wall_clock64();   // first dispatched
-  int nb = 0;
-  if (tid < n) {
-    const int seq = a.tok0 + tid;
-    const int L = a.kv_len[seq], cap = a.kv_cap[seq];
-    const long long off = a.kv_off[seq];
-    const bool ok = L >= 1 && L <= cap;
-    if (!ok && blockIdx.x == 0 && a.err) atomicOr(a.err, ERR_KV_LEN);   // refused: no blocks, reported once
-    nb = ok ? (L + 31) / 32 : 0;
-    s_len[tid] = L;
-    s_cap[tid] = cap;
-    s_off[tid] = off;
-    s_nb[tid] = nb;
+  int nbv[TPT], local = 0;   // the thread's block counts and their sum
+#pragma unroll
+  for (int u = 0; u < TPT; ++u) {
+    const int t = tid * TPT + u;
+    nbv[u] = 0;
+    if (t < n) {
+      const int seq = a.tok0 + t;
+      const int L = a.kv_len[seq], cap = a.kv_cap[seq];
+      const long long off = a.kv_off[seq];
+      const bool ok = L >= 1 && L <= cap;
+      if (!ok && blockIdx.x == 0 && a.err) atomicOr(a.err, ERR_KV_LEN);   // refused: no blocks, reported once
+      nbv[u] = ok ? (L + 31) / 32 : 0;
+      s_len[t] = L;
+      s_cap[t] = cap;
+      s_off[t] = off;
+      s_nb[t] = nbv[u];
+    }
+    local += nbv[u];
   }
-  // exclusive prefix of the per-token block counts: wave scans, then wave sums
-  int incl = nb;
+  // exclusive prefix of the per-token block counts in token order: the
+  // thread's own tokens, a wave scan of the thread sums, then the wave sums
+  int incl = local;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
     const int t = __shfl_up(incl, o, 64);
@@ -452,7 +462,13 @@ __global__ __launch_bounds__(256, SPA_ATTN_MINB) void k_attn_dealt(AttnArgs a) {
   __syncthreads();
   int before = 0;
   for (int w2 = 0; w2 < wave; ++w2) before += s_wsum[w2];
-  if (tid < n) s_first[tid] = (long long)(before + incl - nb) * Hkv;
+  int run = before + incl - local;
+#pragma unroll
+  for (int u = 0; u < TPT; ++u) {
+    const int t = tid * TPT + u;
+    if (t < n) s_first[t] = (long long)run * Hkv;
+    run += nbv[u];
+  }
   if (tid == 0) s_first[n] = (long long)(s_wsum[0] + s_wsum[1] + s_wsum[2] + s_wsum[3]) * Hkv;
   __syncthreads();
   const long long T = s_first[n];
@@ -620,12 +636,20 @@ static void launch_attn_t(const AttnArgs& a, dim3 grid, hipStream_t st, hipEvent
     hipLaunchKernelGGL((k_attn<KVT, KIND>), grid, dim3(256), 0, st, a);
 }
 
+template <int KVT, int TPT>
+static void launch_dealt_tpt(const AttnArgs& a, hipStream_t st, hipEvent_t start, hipEvent_t stop) {
+  if (start || stop)
+    hipExtLaunchKernelGGL((k_attn_dealt<KVT, TPT>), dim3(a.deal_wgs), dim3(256), 0, st, start, stop, 0, a);
+  else
+    hipLaunchKernelGGL((k_attn_dealt<KVT, TPT>), dim3(a.deal_wgs), dim3(256), 0, st, a);
+}
+
+// up to 256 tokens: one token per prologue thread and the smaller tables
 template <int KVT>
 static void launch_dealt_t(const AttnArgs& a, hipStream_t st, hipEvent_t start, hipEvent_t stop) {
-  if (start || stop)
-    hipExtLaunchKernelGGL(k_attn_dealt<KVT>, dim3(a.deal_wgs), dim3(256), 0, st, start, stop, 0, a);
-  else
-    hipLaunchKernelGGL(k_attn_dealt<KVT>, dim3(a.deal_wgs), dim3(256), 0, st, a);
+  static_assert(kDealMaxTok == 4 * 256, "the prologue instances cover 256 and 1024 tokens");
+  if (a.n_tok <= 256) launch_dealt_tpt<KVT, 1>(a, st, start, stop);
+  else launch_dealt_tpt<KVT, 4>(a, st, start, stop);
 }
 
 hipError_t launch_attn(const AttnArgs& a, hipStream_t st, hipEvent_t start, hipEvent_t stop) {

@@ -205,7 +205,7 @@ struct AttnArgs {
   int* deal_tab;            // [n_tok * Hkv][2]: first range and piece count of each window
 };
 constexpr int kSpanWords = 136;
-constexpr int kDealMaxTok = 256;   // tokens per launch of the dealt kernel (one per thread of its prologue)
+constexpr int kDealMaxTok = 1024;   // tokens per launch of the dealt kernel (four per thread of its prologue)
 #ifndef SPA_DEAL_RANGES_PER_CU
 #define SPA_DEAL_RANGES_PER_CU 2
 #endif

@@ -16,7 +16,7 @@
 namespace {
 
 constexpr size_t kScratchErrBytes = 256;                    // the error word (and padding)
-constexpr size_t kScratchPartBytes = (size_t)16 << 20;      // piece partials: 16 MiB
+constexpr size_t kScratchPartBytes = (size_t)24 << 20;      // piece partials: 24 MiB
 constexpr int kMaxDevices = 64;
 
 __device__ __align__(256) unsigned char scratch[kScratchErrBytes + kScratchPartBytes];

@@ -6,9 +6,9 @@ identical bit for bit. Two calls in a row: a full layer over all 64
 sequences (the launch's blocks split evenly over the device's ranges), then
 a smaller call of 16 sequences (another split), which must not see anything
 the first call left in the fixed scratch array; then a sliding layer, and a
-full layer of 264 sequences (above the split kernel's 256 tokens: one
-workgroup per chunk). A call whose partials would not fit the array is
-refused before any launch.
+full layer of 1,040 sequences with top-2 routing (above the split kernel's
+1,024 tokens: one workgroup per chunk). A call whose partials would not fit
+the array is refused before any launch.
 """
 import pytest
 import torch
@@ -40,10 +40,10 @@ def test_noalloc_attention_equals_workspace_attention_twice():
         assert torch.equal(o_ref, o_got), f"layer {layer}, tokens {tok0}+{n_tok}"
         assert int(err.item()) == 0 and B.spa_workspace_errors(ctx, ws) == 0
     del dw
-    # 264 sequences: the per-chunk grid kernel, whose partials grow with the
-    # batch's length bound
-    wl2 = wl.with_(name="noalloc_grid", seed=2017, batch=264, kv_len_lo=16, kv_len_hi=200)
-    print("[no-alloc] layer 1 (full), 264 tokens", flush=True)
+    # 1,040 sequences: the per-chunk grid kernel, whose partials grow with
+    # the batch's length bound
+    wl2 = wl.with_(name="noalloc_grid", seed=2017, top_k=2, batch=1040, kv_len_lo=16, kv_len_hi=200)
+    print("[no-alloc] layer 1 (full), 1040 tokens", flush=True)
     dw2 = DeviceWorkload(wl2)
     q2 = torch.randn(wl2.batch, QD, device="cuda", generator=gen).to(torch.bfloat16)
     ws = dw2.workspace(n_tok=wl2.batch)
@@ -53,7 +53,7 @@ def test_noalloc_attention_equals_workspace_attention_twice():
     B.spa_decode_attn(ctx, dw2.m, dw2.layers_c[1], dw2.batch, 0, wl2.batch, q2, o_ref, ws)
     B.spa_decode_attn_noalloc(ctx, dw2.m, dw2.layers_c[1], dw2.batch, 0, wl2.batch, q2, o_got, err)
     torch.cuda.synchronize()
-    assert torch.equal(o_ref, o_got), "full layer, 264 tokens"
+    assert torch.equal(o_ref, o_got), "full layer, 1040 tokens"
     assert int(err.item()) == 0 and B.spa_workspace_errors(ctx, ws) == 0
     # partials beyond the fixed array: refused on the host, nothing launched
     big = B.spa_batch.from_buffer_copy(dw2.batch)
