@@ -125,19 +125,21 @@ def test_large_batch_expert_tiles_sampled(name, n_layers):
     assert _same_picks(t1.cpu().numpy()[:, toks], picks)
 
 
-def test_kv_length_beyond_capacity_is_refused():
+@pytest.mark.parametrize("batch,refused", [(16, (3, 9)), (300, (3, 9, 257, 299))])
+def test_kv_length_beyond_capacity_is_refused(batch, refused):
     """A cached length above the sequence's capacity (or zero) sets the
     error bit and is skipped before any KV read; every other token's
     attention output is unchanged (bit for bit on the sliding layer, within
     rounding on the full layer, whose split follows the launch's lengths).
     Each call clears the error word first, so each reading belongs to one
-    launch."""
+    launch. 16 tokens run the split's one-token-per-thread prologue, 300
+    tokens its four-token one."""
     from spatially_pipelined_attention_amd import binding as B, synth
     from spatially_pipelined_attention_amd.workload import DeviceWorkload
     base = synth.WORKLOADS["gptoss_36l_b64"]
-    wl = base.with_(name="edge_refuse", seed=2005, n_layers=2, layer_kinds=("sliding", "full"), batch=16,
+    wl = base.with_(name="edge_refuse", seed=2005, n_layers=2, layer_kinds=("sliding", "full"), batch=batch,
                     kv_len_lo=200, kv_len_hi=600)
-    print("\n[case] kv length beyond capacity, 16 tokens", flush=True)
+    print(f"\n[case] kv length beyond capacity, {batch} tokens, refused {refused}", flush=True)
     dw = DeviceWorkload(wl)
     ctx = B.spa_init(0)
     n = wl.batch
@@ -148,8 +150,8 @@ def test_kv_length_beyond_capacity_is_refused():
     for bad in (False, True):
         saved = dw.kv_len_d.clone()
         if bad:
-            dw.kv_len_d[3] = dw.kv_cap_d[3] + 1
-            dw.kv_len_d[9] = 0
+            for i, t in enumerate(refused):   # above capacity, or zero
+                dw.kv_len_d[t] = dw.kv_cap_d[t] + 1 if i % 2 == 0 else 0
         for layer in (1, 0):   # full (packed cache), then sliding (ring)
             o = torch.zeros_like(q)
             B.spa_decode_attn(ctx, dw.m, dw.layers_c[layer], dw.batch, 0, n, q, o, ws)
@@ -159,10 +161,17 @@ def test_kv_length_beyond_capacity_is_refused():
         dw.kv_len_d.copy_(saved)
     assert errs[0] == 0 and errs[1] == 0
     assert errs[2] & 1 and errs[3] & 1
-    keep = [t for t in range(n) if t not in (3, 9)]
+    keep = [t for t in range(n) if t not in refused]
     # full layer: the launch's blocks are split evenly, so a refused token's
-    # missing blocks move the other windows' split points; their outputs stay
-    # within rounding of the clean run
-    hz.assert_close_rms(outs[2][keep].double().cpu().numpy(), outs[0][keep].double().cpu().numpy(), 1e-2,
-                        "full layer, refused tokens left out")
+    # missing blocks move the other windows' split points. The probabilities
+    # enter the PV product in bf16, each relative to its piece's running
+    # maximum, so moving a split changes their rounding (2^-9 of each term)
+    # and the output's by about 2^-9 of the output scale; the output itself
+    # is rounded to bf16 (spacing <= 2^-7 of its magnitude). Bound: 2^-7 of
+    # (|element| + RMS of the outputs)
+    got = outs[2][keep].double().cpu().numpy()
+    ref = outs[0][keep].double().cpu().numpy()
+    bound = 2.0 ** -7 * (np.abs(ref) + np.sqrt(np.mean(ref * ref)))
+    worst = float((np.abs(got - ref) / bound).max())
+    assert worst <= 1.0, f"full layer, refused tokens left out: {worst:.2f} of the rounding bound"
     assert torch.equal(outs[1][keep], outs[3][keep])   # sliding layer: one workgroup per window, bit for bit
