@@ -524,6 +524,88 @@ __global__ __launch_bounds__(256, SPA_ATTN_MINB) void k_attn_dealt(AttnArgs a) {
   if (a.tspan && tid == 0) atomicMax(a.tspan + 8 * ((w & 15) + 1), (unsigned long long)wall_clock64());
 }
 
+// Sliding layers at large batches: one wave per window (token b, KV head g),
+// four windows per workgroup. The wave streams the window's blocks through
+// its register ring and finishes with the sink itself: no piece merge through
+// LDS and no barrier, so the workgroup's fixed costs are shared by four
+// windows. A lane holds head (lane & 15) and dims 16 dt + 4 (lane >> 4) + r,
+// so each lane stores four runs of four outputs.
+template <int KVT>
+__global__ __launch_bounds__(256, SPA_ATTN_MINB) void k_attn_wave(AttnArgs a) {
+  constexpr int esz = KVT == DT_BF16 ? 2 : 4;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int G = a.n_q_heads / a.n_kv_heads, Hkv = a.n_kv_heads;
+  if (a.tspan && tid == 0 && blockIdx.x == 0) a.tspan[0] = wall_clock64();   // first dispatched
+  const int j = blockIdx.x * 4 + wave;   // wave-uniform; the kernel has no workgroup barrier
+  if (j < a.n_tok * Hkv) {
+    const int b = j / Hkv, g = j - b * Hkv;
+    const KvLoc loc = kv_locate(a, a.tok0 + b, g, KV_RING);
+    if (!loc.ok) {
+      if (lane == 0 && g == 0 && a.err) atomicOr(a.err, ERR_KV_LEN);
+    } else {
+      const char* kreg = (const char*)a.k_cache + loc.base * esz;
+      const char* vreg = (const char*)a.v_cache + loc.base * esz;
+      const int hl = lane & 15, q4 = lane >> 4;
+      const bool hvalid = hl < G;
+      const char* qrow = (const char*)a.q + ((long long)b * a.n_q_heads + g * G + (hvalid ? hl : 0)) * kD * esz;
+      QRegs<KVT> qr;
+      if constexpr (KVT == DT_BF16) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) qr.q[h] = hvalid ? ld16(qrow + (32 * h + 8 * q4) * 2) : u32x4{0u, 0u, 0u, 0u};
+      } else {
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc) qr.q[cc] = hvalid ? ld16(qrow + (16 * cc + 4 * q4) * 4) : u32x4{0u, 0u, 0u, 0u};
+      }
+      const float sink = a.sinks[g * G + (hvalid ? hl : 0)] * kLog2e;
+      const int nb = (loc.n_valid + 31) / 32;
+      float m_run = -INFINITY, l_run = 0.f;
+      f32x4 acc[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+      // blocks 0 .. nb-1 through a ring of kRing register sets (a block past
+      // the last is clamped for the load and never attended)
+      BlockRegs<KVT> rb[kRing];
+#pragma unroll
+      for (int r = 0; r < kRing; ++r) load_block<KVT>(rb[r], kreg, vreg, min(r, nb - 1), lane, kStreamKV);
+      int i = 0;
+      for (; i + kRing < nb; i += kRing) {
+#pragma unroll
+        for (int r = 0; r < kRing; ++r) {
+          attend<KVT>(rb[r], qr, i + r, loc.n_valid, a.scale_log2, m_run, l_run, acc, lane);
+          __builtin_amdgcn_sched_barrier(0);
+          load_block<KVT>(rb[r], kreg, vreg, min(i + r + kRing, nb - 1), lane, kStreamKV);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < kRing; ++r)
+        if (i + r < nb) attend<KVT>(rb[r], qr, i + r, loc.n_valid, a.scale_log2, m_run, l_run, acc, lane);
+      l_run += __shfl_xor(l_run, 16, 64);
+      l_run += __shfl_xor(l_run, 32, 64);
+      if (hvalid) {
+        const float MM = fmaxf(m_run, sink);
+        const float f = m_run == -INFINITY ? 0.f : exp2f(m_run - MM);
+        const float Z = exp2f(sink - MM) + f * l_run;
+        const float fz = f / Z;
+        const int hq = g * G + hl;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+          const long long oi = o_index(a, b, hq, 16 * dt + 4 * q4);   // four consecutive outputs
+          if constexpr (KVT == DT_BF16) {
+            *reinterpret_cast<uint2*>((uint16_t*)a.o + oi) =
+                uint2{pack_bf16x2(acc[dt][0] * fz, acc[dt][1] * fz), pack_bf16x2(acc[dt][2] * fz, acc[dt][3] * fz)};
+          } else {
+            *reinterpret_cast<f32x4*>((float*)a.o + oi) =
+                f32x4{acc[dt][0] * fz, acc[dt][1] * fz, acc[dt][2] * fz, acc[dt][3] * fz};
+          }
+        }
+      }
+    }
+  }
+  if (a.tspan && lane == 0) atomicMax(a.tspan + 8 * ((blockIdx.x & 15) + 1), (unsigned long long)wall_clock64());
+}
+
 // Merge the piece partials of one (sequence, KV head) in window order with the
 // sink: M = max(sink, m_c), Z = 2^(sink-M) + sum l_c 2^(m_c-M), o = sum o_c 2^(m_c-M) / Z.
 // k_attn's chunks sit at [b][g][chunk]; k_attn_dealt's pieces of window j at
@@ -652,7 +734,22 @@ static void launch_dealt_t(const AttnArgs& a, hipStream_t st, hipEvent_t start, 
   else launch_dealt_tpt<KVT, 4>(a, st, start, stop);
 }
 
+template <int KVT>
+static void launch_wave_t(const AttnArgs& a, hipStream_t st, hipEvent_t start, hipEvent_t stop) {
+  const dim3 grid((a.n_tok * a.n_kv_heads + 3) / 4);
+  if (start || stop)
+    hipExtLaunchKernelGGL(k_attn_wave<KVT>, grid, dim3(256), 0, st, start, stop, 0, a);
+  else
+    hipLaunchKernelGGL(k_attn_wave<KVT>, grid, dim3(256), 0, st, a);
+}
+
 hipError_t launch_attn(const AttnArgs& a, hipStream_t st, hipEvent_t start, hipEvent_t stop) {
+  if (a.wave_windows) {
+    if (a.kv_kind != KV_RING || a.deal_wgs > 0 || a.n_q_heads / a.n_kv_heads > 16) return hipErrorInvalidValue;
+    if (a.kv_dtype == DT_BF16) launch_wave_t<DT_BF16>(a, st, start, stop);
+    else launch_wave_t<DT_F32>(a, st, start, stop);
+    return hipGetLastError();
+  }
   if (a.deal_wgs > 0 && a.kv_kind == KV_PACKED) {
     if (a.n_tok < 1 || a.n_tok > kDealMaxTok || a.deal_v < 1 || a.deal_v > kDealMaxRanges || !a.deal_tab)
       return hipErrorInvalidValue;

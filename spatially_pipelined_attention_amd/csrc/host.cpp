@@ -525,6 +525,15 @@ static spa_status op_attn(spa_ctx* ctx, const spa_model_desc* m, const spa_layer
   // full layers: the launch's blocks cut into ranges fixed by the device,
   // taken by two resident workgroups per CU of the stream's pool (the ranges,
   // and so the results, are the same for every pool)
+#ifndef SPA_ATTN_WAVE_PER_4CU
+#define SPA_ATTN_WAVE_PER_4CU 4
+#endif
+  // sliding layers with at least SPA_ATTN_WAVE_PER_4CU windows per 4 CUs of
+  // the device (so the choice, and the results, never depend on the pool):
+  // one wave per window
+  if (l->kind == SPA_SLIDING && m->window <= 256 && SPA_ATTN_WAVE_PER_4CU >= 0 &&
+      4LL * n_tok * m->n_kv_heads >= (long long)SPA_ATTN_WAVE_PER_4CU * ctx->n_cus)
+    a.wave_windows = 1;
   if (dealt_launch(l, n_tok)) {
     const int G = m->n_q_heads / m->n_kv_heads;
     a.deal_wgs = kDealWgsPerCu * stream_cus(st, ctx->n_cus);

@@ -203,9 +203,12 @@ struct AttnArgs {
   int deal_wgs;
   int deal_v;               // ranges of the even split (the same for every pool of the device)
   int* deal_tab;            // [n_tok * Hkv][2]: first range and piece count of each window
+  // 1 (sliding layers): one wave per window, four windows per workgroup
+  // (k_attn_wave); 0: a window's blocks spread over the four waves
+  int wave_windows;
 };
 constexpr int kSpanWords = 136;
-constexpr int kDealMaxTok = 1024;   // tokens per launch of the dealt kernel (four per thread of its prologue)
+constexpr int kDealMaxTok = 1024;   // tokens per launch of the dealt kernel (one or four per prologue thread)
 #ifndef SPA_DEAL_RANGES_PER_CU
 #define SPA_DEAL_RANGES_PER_CU 2
 #endif
