@@ -783,6 +783,7 @@ static spa_status op_expert(spa_ctx* ctx, const spa_model_desc* m, const spa_lay
       c.out = s.z8;
       c.scales = s.z8_scale;
       c.kmajor_rows = R;
+      c.n_cus = ctx->n_cus;
       SPA_HIP(launch_cvt_rows(c, st));
       a.X = s.z8;
       a.x_scale = s.z8_scale;
@@ -1258,6 +1259,7 @@ spa_status spa_moe_expert(spa_ctx* ctx, const spa_model_desc* m, const spa_layer
     c.dtype = m->expert_dtype == SPA_BF16 ? DT_BF16 : DT_E4M3;
     c.out = m->expert_dtype == SPA_BF16 ? (void*)s.hn_bf16 : (void*)s.hn8;
     c.scales = s.hn8_scale;
+    c.n_cus = ctx->n_cus;
     SPA_HIP(launch_cvt_rows(c, st));
     xe = c.out;
   }

@@ -234,6 +234,7 @@ struct CvtArgs {
   void* out;
   float* scales;            // E4M3
   int kmajor_rows;
+  int n_cus;                // device CUs: picks the workgroup size
 };
 hipError_t launch_cvt_rows(const CvtArgs& a, hipStream_t st);
 

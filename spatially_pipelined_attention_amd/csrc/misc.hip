@@ -709,36 +709,83 @@ hipError_t launch_part_rows(const CombineArgs& a, int max_rows, hipStream_t st) 
 }
 
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kRowThreads) void k_cvt_rows(CvtArgs a) {
-  __shared__ float red[kRowThreads / 64];
+// Row conversion, one workgroup of T threads per row: rows of up to 4,096
+// columns are read once into registers (4,096 / T per thread, every load
+// issued before the first use), the row's largest magnitude is a block
+// reduction, then the codes are written; longer rows read their columns again
+// for the second pass. Thread t holds columns t + T j. Few rows take T = 1,024
+// (more waves per row while the rows leave CUs idle), many rows T = 256.
+constexpr int kCvtRowCols = 4096;   // longest row held in registers
+
+template <int T>
+__global__ __launch_bounds__(T) void k_cvt_rows(CvtArgs a) {
+  constexpr int kRegCols = kCvtRowCols / T;
+  __shared__ float red[T / 64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r = blockIdx.x;
   const long long R = a.kmajor_rows;
   // element c of row r: row-major, or k-step-major with 16 fp32 per k-step
-  auto in_at = [&](int c) -> float {
-    return R ? a.x[((long long)(c >> 4) * R + r) * 16 + (c & 15)] : a.x[(long long)r * a.n_cols + c];
+  auto in_idx = [&](int c) -> long long {
+    return R ? ((long long)(c >> 4) * R + r) * 16 + (c & 15) : (long long)r * a.n_cols + c;
   };
-  if (a.dtype == DT_BF16) {
-    for (int c = threadIdx.x; c < a.n_cols; c += kRowThreads) {
+  const bool e4m3 = a.dtype != DT_BF16;
+  // output c: bf16 (32 per k-step) or E4M3 (64 per k-step)
+  auto store = [&](int c, float x, float inv_s) {
+    if (!e4m3) {
       const long long o = R ? ((long long)(c >> 5) * R + r) * 32 + (c & 31) : (long long)r * a.n_cols + c;
-      ((uint16_t*)a.out)[o] = f32_to_bf16(in_at(c));
+      ((uint16_t*)a.out)[o] = f32_to_bf16(x);
+    } else {
+      const long long o = R ? ((long long)(c >> 6) * R + r) * 64 + (c & 63) : (long long)r * a.n_cols + c;
+      ((uint8_t*)a.out)[o] = f32_to_e4m3(x * inv_s);
+    }
+  };
+  // the row's scale from this thread's largest magnitude (E4M3)
+  auto row_scale = [&](float amax) {
+    amax = wave_max(amax);
+    if (lane == 0) red[wave] = amax;
+    __syncthreads();
+    float m = red[0];
+#pragma unroll
+    for (int w = 1; w < T / 64; ++w) m = fmaxf(m, red[w]);
+    const float s = pow2_scale_448(m);
+    if (tid == 0) a.scales[r] = s;
+    return 1.0f / s;   // exact: power of two
+  };
+  if (a.n_cols <= kCvtRowCols) {
+    float v[kRegCols];
+#pragma unroll
+    for (int j = 0; j < kRegCols; ++j) {
+      const int c = tid + T * j;
+      const float x = a.x[in_idx(min(c, a.n_cols - 1))];   // clamped: no branch between the loads
+      v[j] = c < a.n_cols ? x : 0.f;
+    }
+    float inv_s = 1.f;
+    if (e4m3) {
+      float amax = 0.f;
+#pragma unroll
+      for (int j = 0; j < kRegCols; ++j) amax = fmaxf(amax, fabsf(v[j]));
+      inv_s = row_scale(amax);
+    }
+#pragma unroll
+    for (int j = 0; j < kRegCols; ++j) {
+      const int c = tid + T * j;
+      if (c < a.n_cols) store(c, v[j], inv_s);
     }
     return;
   }
-  float amax = 0.f;
-  for (int c = threadIdx.x; c < a.n_cols; c += kRowThreads) amax = fmaxf(amax, fabsf(in_at(c)));
-  amax = block_max(amax, red);
-  const float s = pow2_scale_448(amax);
-  const float inv_s = 1.0f / s;
-  if (threadIdx.x == 0) a.scales[r] = s;
-  for (int c = threadIdx.x; c < a.n_cols; c += kRowThreads) {
-    const long long o = R ? ((long long)(c >> 6) * R + r) * 64 + (c & 63) : (long long)r * a.n_cols + c;
-    ((uint8_t*)a.out)[o] = f32_to_e4m3(in_at(c) * inv_s);
+  float inv_s = 1.f;
+  if (e4m3) {
+    float amax = 0.f;
+    for (int c = tid; c < a.n_cols; c += T) amax = fmaxf(amax, fabsf(a.x[in_idx(c)]));
+    inv_s = row_scale(amax);
   }
+  for (int c = tid; c < a.n_cols; c += T) store(c, a.x[in_idx(c)], inv_s);
 }
 
 hipError_t launch_cvt_rows(const CvtArgs& a, hipStream_t st) {
-  if (a.n_rows <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_cvt_rows, dim3(a.n_rows), dim3(kRowThreads), 0, st, a);
+  if (a.n_rows <= 0 || a.n_cols <= 0) return hipSuccess;
+  if (a.n_rows >= 2 * a.n_cus) hipLaunchKernelGGL(k_cvt_rows<256>, dim3(a.n_rows), dim3(256), 0, st, a);
+  else hipLaunchKernelGGL(k_cvt_rows<1024>, dim3(a.n_rows), dim3(1024), 0, st, a);
   return hipGetLastError();
 }
 
