@@ -524,14 +524,51 @@ __global__ __launch_bounds__(256, SPA_ATTN_MINB) void k_attn_dealt(AttnArgs a) {
   if (a.tspan && tid == 0) atomicMax(a.tspan + 8 * ((w & 15) + 1), (unsigned long long)wall_clock64());
 }
 
+// The new token's K row and V column of one window (bf16), patched into the
+// registers of the block that holds its ring slot s32 (slot % 32): lanes with
+// lane % 16 == s32 % 16 hold that slot's K row (tile s32 / 16) as dims
+// 32 h + 8 (lane / 16) .. + 7; lanes with lane / 16 == (s32 % 16) / 4 hold its
+// V entries, bf16 element v_slot(s32) % 8 of each d tile (d = 16 dt + lane % 16).
+__device__ __forceinline__ void patch_new_slot(BlockRegs<DT_BF16>& br, const u32x4 (&kn)[2], const uint32_t (&vn)[4],
+                                               int s32, int lane) {
+  // value selects and masks only: a conditional store to a register array
+  // element would be turned into an indexed store through scratch memory
+  const int p16 = lane & 15, q4 = lane >> 4;
+  const bool krow = p16 == (s32 & 15);
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const bool take = krow && (s32 >> 4) == t;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) br.k[t][h] = take ? kn[h] : br.k[t][h];
+  }
+  const bool vcol = q4 == ((s32 & 15) >> 2);
+  const int e = v_slot(s32) & 7;
+#pragma unroll
+  for (int ww = 0; ww < 4; ++ww) {
+    const uint32_t sel = vcol && (e >> 1) == ww ? ((e & 1) ? 0xffff0000u : 0x0000ffffu) : 0u;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+      const uint32_t ins = (e & 1) ? (vn[dt] << 16) : vn[dt];
+      br.v[dt][ww] = (br.v[dt][ww] & ~sel) | (ins & sel);
+    }
+  }
+}
+
 // Sliding layers at large batches: one wave per window (token b, KV head g),
 // four windows per workgroup. The wave streams the window's blocks through
 // its register ring and finishes with the sink itself: no piece merge through
 // LDS and no barrier, so the workgroup's fixed costs are shared by four
 // windows. A lane holds head (lane & 15) and dims 16 dt + 4 (lane >> 4) + r,
 // so each lane stores four runs of four outputs.
-template <int KVT>
+// QSM > 0 (bf16): the QKV finish is folded in. The wave sums its heads' q and
+// the new K and V of its window from the QKV split partials (part_sum<QSM>,
+// the finish's sums and roundings), appends K and V at ring slot
+// (L - 1) % W, and patches them into the registers of the block holding that
+// slot (the block's load may return the slot's old row): the same values the
+// separate finish would have stored and this kernel would have loaded.
+template <int KVT, int QSM>
 __global__ __launch_bounds__(256, SPA_ATTN_MINB) void k_attn_wave(AttnArgs a) {
+  static_assert(QSM == 0 || KVT == DT_BF16, "the folded finish is bf16 only");
   constexpr int esz = KVT == DT_BF16 ? 2 : 4;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -550,7 +587,64 @@ __global__ __launch_bounds__(256, SPA_ATTN_MINB) void k_attn_wave(AttnArgs a) {
       const bool hvalid = hl < G;
       const char* qrow = (const char*)a.q + ((long long)b * a.n_q_heads + g * G + (hvalid ? hl : 0)) * kD * esz;
       QRegs<KVT> qr;
-      if constexpr (KVT == DT_BF16) {
+      u32x4 kn[2] = {u32x4{0u, 0u, 0u, 0u}, u32x4{0u, 0u, 0u, 0u}};
+      uint32_t vn[4] = {0u, 0u, 0u, 0u};
+      int sblk = -1, s32 = 0;
+      const int nb = (loc.n_valid + 31) / 32;
+      // blocks 0 .. nb-1 through a ring of kRing register sets (a block past
+      // the last is clamped for the load and never attended)
+      BlockRegs<KVT> rb[kRing];
+      if constexpr (QSM > 0) {
+        // the ring's first loads go out before the finish's loads and the
+        // append's stores, which they would otherwise wait behind
+#pragma unroll
+        for (int r = 0; r < kRing; ++r) load_block<KVT>(rb[r], kreg, vreg, min(r, nb - 1), lane, kStreamKV);
+        const int QD = a.n_q_heads * kD;
+        const int L = a.kv_len[a.tok0 + b];   // >= 1 (loc.ok)
+        const int slot = (L - 1) % a.window;
+        sblk = slot >> 5;
+        s32 = slot & 31;
+        // Every partial sum the wave needs, with no branch between the loads
+        // (a branch would hold the later loads behind the earlier sums): q of
+        // the lane's head (the padding heads' lanes read head 0's, unused),
+        // the new K row's dims 32 h + 8 q4 .. + 7 and the new V's dims
+        // 16 dt + lane % 16, in every lane.
+        const int qc = (g * G + (hvalid ? hl : 0)) * kD, kc = QD + g * kD, vc = QD + a.n_kv_heads * kD + g * kD;
+        f32x4 qx[2][2], kx[2][2];
+        float vx[4];
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            qx[h][u] = part_sum4<QSM>(a.qkv, b, qc + 32 * h + 8 * q4 + 4 * u);
+            kx[h][u] = part_sum4<QSM>(a.qkv, b, kc + 32 * h + 8 * q4 + 4 * u);
+          }
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) vx[dt] = part_sum<QSM>(a.qkv, b, vc + 16 * dt + (lane & 15));
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          qr.q[h] = hvalid ? u32x4{pack_bf16x2(qx[h][0][0], qx[h][0][1]), pack_bf16x2(qx[h][0][2], qx[h][0][3]),
+                                   pack_bf16x2(qx[h][1][0], qx[h][1][1]), pack_bf16x2(qx[h][1][2], qx[h][1][3])}
+                           : u32x4{0u, 0u, 0u, 0u};
+          kn[h] = u32x4{pack_bf16x2(kx[h][0][0], kx[h][0][1]), pack_bf16x2(kx[h][0][2], kx[h][0][3]),
+                        pack_bf16x2(kx[h][1][0], kx[h][1][1]), pack_bf16x2(kx[h][1][2], kx[h][1][3])};
+        }
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) vn[dt] = f32_to_bf16(vx[dt]);
+        // the append: the lanes that hold the slot's K row and V entries store
+        // them (the cache is written through the region pointers it is read from)
+        char* kw = const_cast<char*>(kreg);
+        uint16_t* vw = (uint16_t*)const_cast<char*>(vreg);
+        if ((lane & 15) == (s32 & 15)) {
+#pragma unroll
+          for (int h = 0; h < 2; ++h) st16(kw + k_offset(slot, 32 * h + 8 * q4, 32) * 2, kn[h]);
+        }
+        if (q4 == ((s32 & 15) >> 2)) {
+#pragma unroll
+          for (int dt = 0; dt < 4; ++dt)
+            vw[(long long)sblk * 32 * kD + (16 * dt + (lane & 15)) * 32 + v_slot(s32)] = (uint16_t)vn[dt];
+        }
+      } else if constexpr (KVT == DT_BF16) {
 #pragma unroll
         for (int h = 0; h < 2; ++h) qr.q[h] = hvalid ? ld16(qrow + (32 * h + 8 * q4) * 2) : u32x4{0u, 0u, 0u, 0u};
       } else {
@@ -558,20 +652,20 @@ __global__ __launch_bounds__(256, SPA_ATTN_MINB) void k_attn_wave(AttnArgs a) {
         for (int cc = 0; cc < 4; ++cc) qr.q[cc] = hvalid ? ld16(qrow + (16 * cc + 4 * q4) * 4) : u32x4{0u, 0u, 0u, 0u};
       }
       const float sink = a.sinks[g * G + (hvalid ? hl : 0)] * kLog2e;
-      const int nb = (loc.n_valid + 31) / 32;
       float m_run = -INFINITY, l_run = 0.f;
       f32x4 acc[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-      // blocks 0 .. nb-1 through a ring of kRing register sets (a block past
-      // the last is clamped for the load and never attended)
-      BlockRegs<KVT> rb[kRing];
+      if constexpr (QSM == 0) {
 #pragma unroll
-      for (int r = 0; r < kRing; ++r) load_block<KVT>(rb[r], kreg, vreg, min(r, nb - 1), lane, kStreamKV);
+        for (int r = 0; r < kRing; ++r) load_block<KVT>(rb[r], kreg, vreg, min(r, nb - 1), lane, kStreamKV);
+      }
       int i = 0;
       for (; i + kRing < nb; i += kRing) {
 #pragma unroll
         for (int r = 0; r < kRing; ++r) {
+          if constexpr (QSM > 0)
+            if (i + r == sblk) patch_new_slot(rb[r], kn, vn, s32, lane);
           attend<KVT>(rb[r], qr, i + r, loc.n_valid, a.scale_log2, m_run, l_run, acc, lane);
           __builtin_amdgcn_sched_barrier(0);
           load_block<KVT>(rb[r], kreg, vreg, min(i + r + kRing, nb - 1), lane, kStreamKV);
@@ -580,7 +674,11 @@ __global__ __launch_bounds__(256, SPA_ATTN_MINB) void k_attn_wave(AttnArgs a) {
       }
 #pragma unroll
       for (int r = 0; r < kRing; ++r)
-        if (i + r < nb) attend<KVT>(rb[r], qr, i + r, loc.n_valid, a.scale_log2, m_run, l_run, acc, lane);
+        if (i + r < nb) {
+          if constexpr (QSM > 0)
+            if (i + r == sblk) patch_new_slot(rb[r], kn, vn, s32, lane);
+          attend<KVT>(rb[r], qr, i + r, loc.n_valid, a.scale_log2, m_run, l_run, acc, lane);
+        }
       l_run += __shfl_xor(l_run, 16, 64);
       l_run += __shfl_xor(l_run, 32, 64);
       if (hvalid) {
@@ -734,18 +832,40 @@ static void launch_dealt_t(const AttnArgs& a, hipStream_t st, hipEvent_t start, 
   else launch_dealt_tpt<KVT, 4>(a, st, start, stop);
 }
 
-template <int KVT>
-static void launch_wave_t(const AttnArgs& a, hipStream_t st, hipEvent_t start, hipEvent_t stop) {
+template <int KVT, int QSM>
+static void launch_wave_q(const AttnArgs& a, hipStream_t st, hipEvent_t start, hipEvent_t stop) {
   const dim3 grid((a.n_tok * a.n_kv_heads + 3) / 4);
   if (start || stop)
-    hipExtLaunchKernelGGL(k_attn_wave<KVT>, grid, dim3(256), 0, st, start, stop, 0, a);
+    hipExtLaunchKernelGGL((k_attn_wave<KVT, QSM>), grid, dim3(256), 0, st, start, stop, 0, a);
   else
-    hipLaunchKernelGGL(k_attn_wave<KVT>, grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((k_attn_wave<KVT, QSM>), grid, dim3(256), 0, st, a);
+}
+
+// QSM: 0 (q given, K/V appended), else the smallest of 1, 2, 4 that bounds
+// the QKV split count, the bound the finish kernel takes. Every partial is in
+// flight at once, so more than 4 splits would not fit the registers: the
+// folded finish takes at most 4 (kFoldMaxSplits).
+template <int KVT>
+static void launch_wave_t(const AttnArgs& a, hipStream_t st, hipEvent_t start, hipEvent_t stop) {
+  static_assert(kFoldMaxSplits == 4, "instances for 1, 2 and 4 splits");
+  if constexpr (KVT == DT_BF16) {
+    if (a.qkv.part) {
+      const int S = a.qkv.S;
+      if (S <= 1) launch_wave_q<KVT, 1>(a, st, start, stop);
+      else if (S <= 2) launch_wave_q<KVT, 2>(a, st, start, stop);
+      else launch_wave_q<KVT, 4>(a, st, start, stop);
+      return;
+    }
+  }
+  launch_wave_q<KVT, 0>(a, st, start, stop);
 }
 
 hipError_t launch_attn(const AttnArgs& a, hipStream_t st, hipEvent_t start, hipEvent_t stop) {
   if (a.wave_windows) {
     if (a.kv_kind != KV_RING || a.deal_wgs > 0 || a.n_q_heads / a.n_kv_heads > 16) return hipErrorInvalidValue;
+    if (a.qkv.part && (a.kv_dtype != DT_BF16 || a.head_dim != kD || a.qkv.S < 1 || a.qkv.S > kFoldMaxSplits ||
+                       a.qkv.rows < a.n_tok || a.qkv.ld % 4 != 0))
+      return hipErrorInvalidValue;
     if (a.kv_dtype == DT_BF16) launch_wave_t<DT_BF16>(a, st, start, stop);
     else launch_wave_t<DT_F32>(a, st, start, stop);
     return hipGetLastError();

@@ -57,6 +57,36 @@ __device__ __forceinline__ T bitcast(S s) {
   return __builtin_bit_cast(T, s);
 }
 
+// Element (r, c) of a split-K product: its S partials (split stride rows *
+// ld floats) summed in split order; SM >= S is a compile-time bound, and the
+// padding terms add +0. part_sum4 does the same for columns c .. c + 3 (c a
+// multiple of 4, ld too), element by element in the same order.
+template <int SM, class View>
+__device__ __forceinline__ float part_sum(const View& pv, int r, int c) {
+  const float* p = pv.part + (long long)r * pv.ld + c;
+  const long long sstride = (long long)pv.rows * pv.ld;
+  float v[SM];
+#pragma unroll
+  for (int s = 0; s < SM; ++s) v[s] = p[min(s, pv.S - 1) * sstride];
+  float acc = v[0];
+#pragma unroll
+  for (int s = 1; s < SM; ++s) acc += s < pv.S ? v[s] : 0.f;
+  return acc;
+}
+
+template <int SM, class View>
+__device__ __forceinline__ f32x4 part_sum4(const View& pv, int r, int c) {
+  const float* p = pv.part + (long long)r * pv.ld + c;
+  const long long sstride = (long long)pv.rows * pv.ld;
+  f32x4 v[SM];
+#pragma unroll
+  for (int s = 0; s < SM; ++s) v[s] = *reinterpret_cast<const f32x4*>(p + min(s, pv.S - 1) * sstride);
+  f32x4 acc = v[0];
+#pragma unroll
+  for (int s = 1; s < SM; ++s) acc += s < pv.S ? v[s] : f32x4{0.f, 0.f, 0.f, 0.f};
+  return acc;
+}
+
 // Position p of a 32-position KV block -> storage slot inside the block's
 // d-major V tile. Two 16-position halves are interleaved in runs of four so
 // that one lane's eight MFMA k-slots (positions 4q..4q+3 of both halves) are

@@ -434,9 +434,11 @@ static PartView view_of(const GemmPlan& p, const Slot& s) {
 // kmajor: the activation input (xn / o) is k-step-major over the call's rows,
 // as the pipeline's own slot buffers are; the single-operator entry points
 // take and return row-major tensors.
+// fold_finish: the product only; the sliding attention's one-wave-per-window
+// kernel sums its partials and appends K/V itself (qkv_folds).
 static spa_status op_qkv(spa_ctx* ctx, const spa_model_desc* m, const spa_layer* l, const spa_batch* b, int tok0,
                          int n_tok, const void* xn, void* q_out, const Slot& s, hipStream_t st, TimingHook* th,
-                         bool kmajor = false) {
+                         bool kmajor = false, bool fold_finish = false) {
   const GemmPlan p = plan_gemm(KC_QKV, m, n_tok, ctx->n_cus);
   GemmArgs a = gemm_args(p, s, n_tok);
   a.W = l->wqkv;
@@ -466,7 +468,7 @@ static spa_status op_qkv(spa_ctx* ctx, const spa_model_desc* m, const spa_layer*
   f.rope_theta = m->rope_theta;
   HookScope hs(th, KC_QKV, st);
   SPA_HIP(launch_gemm(m->dense_dtype, EPI_PARTIAL, a, st));
-  SPA_HIP(launch_qkv_finish(f, st));
+  if (!fold_finish) SPA_HIP(launch_qkv_finish(f, st));
   return SPA_OK;
 }
 
@@ -517,23 +519,45 @@ static AttnArgs attn_args(const spa_model_desc* m, const spa_layer* l, const spa
   return a;
 }
 
+#ifndef SPA_ATTN_WAVE_PER_4CU
+#define SPA_ATTN_WAVE_PER_4CU 4
+#endif
+// Sliding layers with at least SPA_ATTN_WAVE_PER_4CU windows per 4 CUs of the
+// device (so the choice, and the results, never depend on the pool): one wave
+// per window (k_attn_wave).
+static bool sliding_wave(const spa_ctx* ctx, const spa_model_desc* m, const spa_layer* l, int n_tok) {
+  return l->kind == SPA_SLIDING && m->window <= 256 && SPA_ATTN_WAVE_PER_4CU >= 0 &&
+         4LL * n_tok * m->n_kv_heads >= (long long)SPA_ATTN_WAVE_PER_4CU * ctx->n_cus;
+}
+
+#ifndef SPA_ATTN_FOLD_QKV
+#define SPA_ATTN_FOLD_QKV 1
+#endif
+// Layers whose QKV finish runs inside the one-wave-per-window attention
+// kernel (bf16 KV, no RoPE, at most kFoldMaxSplits QKV splits): the finish
+// kernel's launch is saved, and the attention computes exactly what it would
+// have read.
+static bool qkv_folds(spa_ctx* ctx, const spa_model_desc* m, const spa_layer* l, int n_tok) {
+  return SPA_ATTN_FOLD_QKV && sliding_wave(ctx, m, l, n_tok) && m->kv_dtype == SPA_BF16 && !(m->rope_theta > 0.f) &&
+         m->head_dim == 64 && m->n_q_heads / m->n_kv_heads <= 16 &&
+         plan_gemm(KC_QKV, m, n_tok, ctx->n_cus).S <= kFoldMaxSplits;
+}
+
+// qkv: the QKV split partials when the finish is folded into the attention
+// (qkv_folds), else null.
 static spa_status op_attn(spa_ctx* ctx, const spa_model_desc* m, const spa_layer* l, const spa_batch* b, int tok0, int n_tok,
                           const void* q, void* o, const WsLayout& W, const Slot& s, hipStream_t st, TimingHook* th,
-                          bool kmajor = false) {
+                          bool kmajor = false, const PartView* qkv = nullptr) {
   AttnArgs a = attn_args(m, l, b, tok0, n_tok, q, o, W, s, ctx->n_cus);
   a.o_kmajor_rows = kmajor ? n_tok : 0;
   // full layers: the launch's blocks cut into ranges fixed by the device,
   // taken by two resident workgroups per CU of the stream's pool (the ranges,
   // and so the results, are the same for every pool)
-#ifndef SPA_ATTN_WAVE_PER_4CU
-#define SPA_ATTN_WAVE_PER_4CU 4
-#endif
-  // sliding layers with at least SPA_ATTN_WAVE_PER_4CU windows per 4 CUs of
-  // the device (so the choice, and the results, never depend on the pool):
-  // one wave per window
-  if (l->kind == SPA_SLIDING && m->window <= 256 && SPA_ATTN_WAVE_PER_4CU >= 0 &&
-      4LL * n_tok * m->n_kv_heads >= (long long)SPA_ATTN_WAVE_PER_4CU * ctx->n_cus)
-    a.wave_windows = 1;
+  if (sliding_wave(ctx, m, l, n_tok)) a.wave_windows = 1;
+  if (qkv) {
+    if (!a.wave_windows) return fail(SPA_EINVAL, "the QKV finish folds only into one-wave-per-window attention");
+    a.qkv = *qkv;
+  }
   if (dealt_launch(l, n_tok)) {
     const int G = m->n_q_heads / m->n_kv_heads;
     a.deal_wgs = kDealWgsPerCu * stream_cus(st, ctx->n_cus);
@@ -857,8 +881,10 @@ spa_status run_segment_a(spa_ctx* ctx, const spa_model_desc* m, const spa_layer*
     spa_route_bufs none{};
     if ((rc = op_combine(m, x, nullptr, nullptr, nullptr, none, n_tok, x, l->gamma1, s.xn, st, nullptr, true))) return rc;
   }
-  if ((rc = op_qkv(ctx, m, l, b, tok0, n_tok, s.xn, s.q, s, st, th, true))) return rc;
-  if ((rc = op_attn(ctx, m, l, b, tok0, n_tok, s.q, s.o, W, s, st, th, true))) return rc;
+  const bool fold = qkv_folds(ctx, m, l, n_tok);
+  const PartView qkv_parts = view_of(plan_gemm(KC_QKV, m, n_tok, ctx->n_cus), s);
+  if ((rc = op_qkv(ctx, m, l, b, tok0, n_tok, s.xn, s.q, s, st, th, true, fold))) return rc;
+  if ((rc = op_attn(ctx, m, l, b, tok0, n_tok, s.q, s.o, W, s, st, th, true, fold ? &qkv_parts : nullptr))) return rc;
   if (with_router) {
     int32_t* rec = b->topk_out ? b->topk_out + ((size_t)layer_index * b->batch + tok0) * m->top_k : nullptr;
     return op_oproj_route(ctx, m, l, x, n_tok, s, rec, fuse_head, st, th);
@@ -883,12 +909,16 @@ spa_status run_layer_before_attn(spa_ctx* ctx, const spa_model_desc* m, const sp
     spa_route_bufs none{};
     if ((rc = op_combine(m, x, nullptr, nullptr, nullptr, none, n_tok, x, l->gamma1, s.xn, st, nullptr, true))) return rc;
   }
-  return op_qkv(ctx, m, l, b, tok0, n_tok, s.xn, s.q, s, st, th, true);
+  return op_qkv(ctx, m, l, b, tok0, n_tok, s.xn, s.q, s, st, th, true, qkv_folds(ctx, m, l, n_tok));
 }
 
+// (with the QKV finish folded in, the attention reads the QKV partials, which
+// the slot keeps until its output projection)
 spa_status run_layer_attn(spa_ctx* ctx, const spa_model_desc* m, const spa_layer* l, const spa_batch* b, int tok0,
                           int n_tok, const WsLayout& W, const Slot& s, hipStream_t st, TimingHook* th) {
-  return op_attn(ctx, m, l, b, tok0, n_tok, s.q, s.o, W, s, st, th, true);
+  const PartView qkv_parts = view_of(plan_gemm(KC_QKV, m, n_tok, ctx->n_cus), s);
+  return op_attn(ctx, m, l, b, tok0, n_tok, s.q, s.o, W, s, st, th, true,
+                 qkv_folds(ctx, m, l, n_tok) ? &qkv_parts : nullptr);
 }
 
 spa_status run_layer_after_attn(spa_ctx* ctx, const spa_model_desc* m, const spa_layer* l, int layer_index,

@@ -53,25 +53,10 @@ __device__ __forceinline__ float block_max(float v, float* red) {
 
 constexpr int kMaxSplits = 16;   // plan_gemm never splits k more than this
 
-// Element (row r, column c) of a split product, summed over the splits in
-// split order. SM is a compile-time bound on the split count: all SM loads
-// are issued before the first add (clamped index, masked value: adding +0
-// leaves every partial sum unchanged), so the kernels are instantiated for
-// SM = 1, 2, 4, 8, 16 and launched with the smallest bound that holds.
-template <int SM>
-__device__ __forceinline__ float part_sum(const PartView& pv, int r, int c) {
-  const float* p = pv.part + (long long)r * pv.ld + c;
-  const long long sstride = (long long)pv.rows * pv.ld;
-  float v[SM];
-#pragma unroll
-  for (int s = 0; s < SM; ++s) v[s] = p[min(s, pv.S - 1) * sstride];
-  float acc = v[0];
-#pragma unroll
-  for (int s = 1; s < SM; ++s) acc += s < pv.S ? v[s] : 0.f;
-  return acc;
-}
-
-// launch KERNEL<SM> with the smallest SM >= S
+// Kernels that sum split partials (part_sum) take SM, a compile-time bound on
+// the split count, so that all SM loads are issued before the first add; they
+// are instantiated for SM = 1, 2, 4, 8, 16 and launched with the smallest
+// bound that holds: KERNEL<SM> with the smallest SM >= S.
 #define SPA_LAUNCH_SPLITS(S, KERNEL, GRID, BLOCK, LDS, ST, ...)                      \
   do {                                                                               \
     if ((S) <= 1) hipLaunchKernelGGL((KERNEL<1>), GRID, BLOCK, LDS, ST, __VA_ARGS__);      \
