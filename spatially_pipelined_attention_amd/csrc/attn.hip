@@ -560,7 +560,8 @@ __device__ __forceinline__ void patch_new_slot(BlockRegs<DT_BF16>& br, const u32
 // LDS and no barrier, so the workgroup's fixed costs are shared by four
 // windows. A lane holds head (lane & 15) and dims 16 dt + 4 (lane >> 4) + r,
 // so each lane stores four runs of four outputs.
-// QSM > 0 (bf16): the QKV finish is folded in. The wave sums its heads' q and
+// QSM > 0 (bf16, 8 query heads per KV head): the QKV finish is folded in.
+// The wave sums its heads' q and
 // the new K and V of its window from the QKV split partials (part_sum<QSM>,
 // the finish's sums and roundings), appends K and V at ring slot
 // (L - 1) % W, and patches them into the registers of the block holding that
@@ -604,33 +605,48 @@ __global__ __launch_bounds__(256, SPA_ATTN_MINB) void k_attn_wave(AttnArgs a) {
         const int slot = (L - 1) % a.window;
         sblk = slot >> 5;
         s32 = slot & 31;
-        // Every partial sum the wave needs, with no branch between the loads
-        // (a branch would hold the later loads behind the earlier sums): q of
-        // the lane's head (the padding heads' lanes read head 0's, unused),
-        // the new K row's dims 32 h + 8 q4 .. + 7 and the new V's dims
-        // 16 dt + lane % 16, in every lane.
-        const int qc = (g * G + (hvalid ? hl : 0)) * kD, kc = QD + g * kD, vc = QD + a.n_kv_heads * kD + g * kD;
-        f32x4 qx[2][2], kx[2][2];
-        float vx[4];
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            qx[h][u] = part_sum4<QSM>(a.qkv, b, qc + 32 * h + 8 * q4 + 4 * u);
-            kx[h][u] = part_sum4<QSM>(a.qkv, b, kc + 32 * h + 8 * q4 + 4 * u);
-          }
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt) vx[dt] = part_sum<QSM>(a.qkv, b, vc + 16 * dt + (lane & 15));
+        // The group's partials are read contiguously, 16 bytes per lane and
+        // no branch between the loads (a branch would hold the later loads
+        // behind the earlier sums): q of its 8 heads as two 1 KB rows of the
+        // wave (lane l holds floats 256 i + 4 l .. + 3: head 4 i + l / 16,
+        // dims 4 (l % 16) ..), K and V as one (lanes with bit 4 clear: K dims
+        // 4 (l % 16) ..; set: V). Summed and rounded where loaded, then moved
+        // to the lanes that need them.
+        const int q0 = g * G * kD, kc = QD + g * kD, vc = QD + a.n_kv_heads * kD + g * kD;
+        const f32x4 qs0 = part_sum4<QSM>(a.qkv, b, q0 + 4 * lane);
+        const f32x4 qs1 = part_sum4<QSM>(a.qkv, b, q0 + 256 + 4 * lane);
+        const f32x4 kvs = part_sum4<QSM>(a.qkv, b, ((lane & 16) ? vc : kc) + 4 * (lane & 15));
+        const uint32_t qd00 = pack_bf16x2(qs0[0], qs0[1]), qd01 = pack_bf16x2(qs0[2], qs0[3]);
+        const uint32_t qd10 = pack_bf16x2(qs1[0], qs1[1]), qd11 = pack_bf16x2(qs1[2], qs1[3]);
+        const uint32_t kvd0 = pack_bf16x2(kvs[0], kvs[1]), kvd1 = pack_bf16x2(kvs[2], kvs[3]);
+        // q: lane (hl, q4) takes head hl's dims 32 h + 8 q4 .. + 7, the 4-dim
+        // chunks c = 8 h + 2 q4 + k of row hl / 4, lane 16 (hl % 4) + c
+        // K: every lane takes dims 32 h + 8 q4 .. + 7 (chunks 8 h + 2 q4 + k)
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-          qr.q[h] = hvalid ? u32x4{pack_bf16x2(qx[h][0][0], qx[h][0][1]), pack_bf16x2(qx[h][0][2], qx[h][0][3]),
-                                   pack_bf16x2(qx[h][1][0], qx[h][1][1]), pack_bf16x2(qx[h][1][2], qx[h][1][3])}
-                           : u32x4{0u, 0u, 0u, 0u};
-          kn[h] = u32x4{pack_bf16x2(kx[h][0][0], kx[h][0][1]), pack_bf16x2(kx[h][0][2], kx[h][0][3]),
-                        pack_bf16x2(kx[h][1][0], kx[h][1][1]), pack_bf16x2(kx[h][1][2], kx[h][1][3])};
-        }
+          uint32_t w[4], kw4[4];
 #pragma unroll
-        for (int dt = 0; dt < 4; ++dt) vn[dt] = f32_to_bf16(vx[dt]);
+          for (int k = 0; k < 2; ++k) {
+            const int c = 8 * h + 2 * q4 + k, src = 16 * (hl & 3) + c;
+            const uint32_t a0 = __shfl(qd00, src, 64), a1 = __shfl(qd01, src, 64);
+            const uint32_t b0 = __shfl(qd10, src, 64), b1 = __shfl(qd11, src, 64);
+            w[2 * k] = hl < 4 ? a0 : b0;
+            w[2 * k + 1] = hl < 4 ? a1 : b1;
+            kw4[2 * k] = __shfl(kvd0, c, 64);
+            kw4[2 * k + 1] = __shfl(kvd1, c, 64);
+          }
+          qr.q[h] = hvalid ? u32x4{w[0], w[1], w[2], w[3]} : u32x4{0u, 0u, 0u, 0u};
+          kn[h] = u32x4{kw4[0], kw4[1], kw4[2], kw4[3]};
+        }
+        // V: every lane takes dim d = 16 dt + lane % 16, element d % 4 of
+        // chunk d / 4 held by lane 16 + d / 4
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+          const int d = 16 * dt + (lane & 15), src = 16 + (d >> 2);
+          const uint32_t a0 = __shfl(kvd0, src, 64), a1 = __shfl(kvd1, src, 64);
+          const uint32_t wv = (d & 2) ? a1 : a0;
+          vn[dt] = (d & 1) ? (wv >> 16) : (wv & 0xffffu);
+        }
         // the append: the lanes that hold the slot's K row and V entries store
         // them (the cache is written through the region pointers it is read from)
         char* kw = const_cast<char*>(kreg);
@@ -863,7 +879,8 @@ static void launch_wave_t(const AttnArgs& a, hipStream_t st, hipEvent_t start, h
 hipError_t launch_attn(const AttnArgs& a, hipStream_t st, hipEvent_t start, hipEvent_t stop) {
   if (a.wave_windows) {
     if (a.kv_kind != KV_RING || a.deal_wgs > 0 || a.n_q_heads / a.n_kv_heads > 16) return hipErrorInvalidValue;
-    if (a.qkv.part && (a.kv_dtype != DT_BF16 || a.head_dim != kD || a.qkv.S < 1 || a.qkv.S > kFoldMaxSplits ||
+    if (a.qkv.part && (a.kv_dtype != DT_BF16 || a.head_dim != kD || a.n_q_heads != 8 * a.n_kv_heads ||
+                       a.qkv.S < 1 || a.qkv.S > kFoldMaxSplits ||
                        a.qkv.rows < a.n_tok || a.qkv.ld % 4 != 0))
       return hipErrorInvalidValue;
     if (a.kv_dtype == DT_BF16) launch_wave_t<DT_BF16>(a, st, start, stop);

@@ -534,12 +534,12 @@ static bool sliding_wave(const spa_ctx* ctx, const spa_model_desc* m, const spa_
 #define SPA_ATTN_FOLD_QKV 1
 #endif
 // Layers whose QKV finish runs inside the one-wave-per-window attention
-// kernel (bf16 KV, no RoPE, at most kFoldMaxSplits QKV splits): the finish
-// kernel's launch is saved, and the attention computes exactly what it would
-// have read.
+// kernel (bf16 KV, no RoPE, 8 query heads per KV head, at most kFoldMaxSplits
+// QKV splits): the finish kernel's launch is saved, and the attention
+// computes exactly what it would have read.
 static bool qkv_folds(spa_ctx* ctx, const spa_model_desc* m, const spa_layer* l, int n_tok) {
   return SPA_ATTN_FOLD_QKV && sliding_wave(ctx, m, l, n_tok) && m->kv_dtype == SPA_BF16 && !(m->rope_theta > 0.f) &&
-         m->head_dim == 64 && m->n_q_heads / m->n_kv_heads <= 16 &&
+         m->head_dim == 64 && m->n_q_heads == 8 * m->n_kv_heads &&
          plan_gemm(KC_QKV, m, n_tok, ctx->n_cus).S <= kFoldMaxSplits;
 }
 

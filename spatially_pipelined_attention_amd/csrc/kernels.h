@@ -206,7 +206,8 @@ struct AttnArgs {
   // 1 (sliding layers): one wave per window, four windows per workgroup
   // (k_attn_wave); 0: a window's blocks spread over the four waves
   int wave_windows;
-  // k_attn_wave, bf16 KV: the QKV split partials (at most kFoldMaxSplits) of the launch's tokens (row b
+  // k_attn_wave, bf16 KV, 8 query heads per KV head: the QKV split partials
+  // (at most kFoldMaxSplits) of the launch's tokens (row b
   // = token b; q at columns [0, Hq D), K at Hq D + g D, V at (Hq + Hkv) D + g D).
   // The kernel then sums q and the new K/V itself and appends K/V (the QKV
   // finish folded in); part null: q is given and K/V are already appended.
