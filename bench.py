@@ -66,9 +66,7 @@ DEAL_MAX_TOKENS = 1024   # full-layer launches of up to this many tokens split t
 def attn_kernel_name(tokens_per_launch, full=True, n_kv_heads=8, n_cus=256):
     """The attention kernel a launch of this many tokens runs (full or sliding layers)."""
     if not full:   # one wave per window from one window per CU of the device, the QKV finish folded in
-        return ("spa::k_attn_wave<1, QSM> (QSM: the bound on the QKV splits it sums; it also reads the QKV "
-                "split partials and appends K/V, bytes not counted here)"
-                if tokens_per_launch * n_kv_heads >= n_cus else "spa::k_attn<1, 0>")
+        return "spa::k_attn_wave<1>" if tokens_per_launch * n_kv_heads >= n_cus else "spa::k_attn<1, 0>"
     if tokens_per_launch <= 256:   # one token per prologue thread
         return "spa::k_attn_dealt<1, 1>"
     return "spa::k_attn_dealt<1, 4>" if tokens_per_launch <= DEAL_MAX_TOKENS else "spa::k_attn<1, 1>"
@@ -401,7 +399,9 @@ def main():
         "schedules_ms": {k: round(v["ms"], 4) for k, v in results.items()},
         "step_ms": results["reported"]["step_ms"],   # per-step spread of the timed steps (host clock)
         "roofline": {"bound": "hbm", "kernel": f"{attn_kernel_name(wl.batch // m, has_full, wl.n_kv_heads, n_cus)} "
-                                               f"({'full' if has_full else 'sliding'}-layer decode attention, bf16 KV)",
+                                               f"({'full' if has_full else 'sliding'}-layer decode attention, bf16 KV"
+                                               + ("" if has_full else "; the QKV finish folded in: it also reads the "
+                                                  "QKV split partials, bytes not counted") + ")",
                      "achieved": round(achieved, 1) if achieved else None, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4) if achieved else None,
                      "frac_of_probe_ceiling": round(achieved / ceiling, 4) if achieved and ceiling else None,

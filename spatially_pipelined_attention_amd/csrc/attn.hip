@@ -257,6 +257,140 @@ struct AttnLds {
 #endif
 constexpr bool kStreamKV = SPA_ATTN_NT != 0;   // KV is read once: non-temporal loads
 
+// ---------------------------------------------------------------------------
+// The QKV finish folded into the attention (bf16 KV, 8 query heads per KV
+// head, at most kFoldMaxSplits QKV splits). A wave that attends window
+// (token b, KV group g) sums its group's q and the window's new K and V from
+// the QKV split partials itself, with the finish kernel's arithmetic, and
+// patches the new K/V into the registers of the block that holds the new slot
+// (that block's load may return the slot's old row); the wave that attends
+// that block also appends them to the cache. The values attended are the ones
+// the finish kernel would have stored.
+
+// The group's partials of one split, read contiguously, 16 bytes per lane: q
+// of its 8 heads as two 1 KB rows of the wave (lane l: floats 256 i + 4 l ..
+// + 3, head 4 i + l / 16, dims 4 (l % 16) ..), K and V as one (lanes with bit
+// 4 clear: K dims 4 (l % 16) ..; set: V).
+struct FoldRaw {
+  f32x4 q0[kFoldMaxSplits], q1[kFoldMaxSplits], kv[kFoldMaxSplits];
+};
+
+// Every load issued at once, no branch between them (the sums come later, so
+// the caller can issue its first KV blocks before it waits).
+__device__ __forceinline__ void fold_issue(const AttnArgs& a, int b, int g, int lane, FoldRaw& f) {
+  const PartView& pv = a.qkv;
+  const int QD = a.n_q_heads * kD, G = 8;
+  const int q0 = g * G * kD, kc = QD + g * kD, vc = QD + a.n_kv_heads * kD + g * kD;
+  const float* row = pv.part + (long long)b * pv.ld;
+  const long long ss = (long long)pv.rows * pv.ld;
+  const int ckv = ((lane & 16) ? vc : kc) + 4 * (lane & 15);
+#pragma unroll
+  for (int s = 0; s < kFoldMaxSplits; ++s) {
+    const float* p = row + min(s, pv.S - 1) * ss;
+    f.q0[s] = *reinterpret_cast<const f32x4*>(p + q0 + 4 * lane);
+    f.q1[s] = *reinterpret_cast<const f32x4*>(p + q0 + 256 + 4 * lane);
+    f.kv[s] = *reinterpret_cast<const f32x4*>(p + ckv);
+  }
+}
+
+// The split sum of the finish kernel, which takes a bound of 1, 2 or 4 splits
+// and adds +0 for each split past S: with 3 splits one +0 (it turns a -0 sum
+// into +0), otherwise none.
+__device__ __forceinline__ f32x4 fold_sum(const f32x4 (&v)[kFoldMaxSplits], int S) {
+  static_assert(kFoldMaxSplits == 4, "the finish's bounds for 1 to 4 splits are 1, 2, 4, 4");
+  f32x4 acc = v[0];
+#pragma unroll
+  for (int s = 1; s < kFoldMaxSplits; ++s) acc = s < S ? acc + v[s] : acc;
+  return S == 3 ? acc + f32x4{0.f, 0.f, 0.f, 0.f} : acc;
+}
+
+// Sums, bf16 rounding, and the moves to the lanes that use the values: q to
+// the MFMA layout (lane (hl, q4): head hl's dims 32 h + 8 q4 .. + 7, the
+// 4-dim chunks c = 8 h + 2 q4 + k of row hl / 4 at lane 16 (hl % 4) + c; the
+// padding heads' lanes get 0); K the same dims in every lane; V dim
+// d = 16 dt + lane % 16 in every lane (element d % 4 of chunk d / 4 at lane
+// 16 + d / 4).
+__device__ __forceinline__ void fold_make(const FoldRaw& f, int S, int lane, QRegs<DT_BF16>& qr, u32x4 (&kn)[2],
+                                          uint32_t (&vn)[4]) {
+  const int hl = lane & 15, q4 = lane >> 4;
+  const f32x4 qs0 = fold_sum(f.q0, S), qs1 = fold_sum(f.q1, S), kvs = fold_sum(f.kv, S);
+  const uint32_t qd00 = pack_bf16x2(qs0[0], qs0[1]), qd01 = pack_bf16x2(qs0[2], qs0[3]);
+  const uint32_t qd10 = pack_bf16x2(qs1[0], qs1[1]), qd11 = pack_bf16x2(qs1[2], qs1[3]);
+  const uint32_t kvd0 = pack_bf16x2(kvs[0], kvs[1]), kvd1 = pack_bf16x2(kvs[2], kvs[3]);
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    uint32_t w[4], kw4[4];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int c = 8 * h + 2 * q4 + k, src = 16 * (hl & 3) + c;
+      const uint32_t a0 = __shfl(qd00, src, 64), a1 = __shfl(qd01, src, 64);
+      const uint32_t b0 = __shfl(qd10, src, 64), b1 = __shfl(qd11, src, 64);
+      w[2 * k] = hl < 4 ? a0 : b0;
+      w[2 * k + 1] = hl < 4 ? a1 : b1;
+      kw4[2 * k] = __shfl(kvd0, c, 64);
+      kw4[2 * k + 1] = __shfl(kvd1, c, 64);
+    }
+    qr.q[h] = hl < 8 ? u32x4{w[0], w[1], w[2], w[3]} : u32x4{0u, 0u, 0u, 0u};
+    kn[h] = u32x4{kw4[0], kw4[1], kw4[2], kw4[3]};
+  }
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) {
+    const int d = 16 * dt + (lane & 15), src = 16 + (d >> 2);
+    const uint32_t a0 = __shfl(kvd0, src, 64), a1 = __shfl(kvd1, src, 64);
+    const uint32_t wv = (d & 2) ? a1 : a0;
+    vn[dt] = (d & 1) ? (wv >> 16) : (wv & 0xffffu);
+  }
+}
+
+// The append of the new K row and V column at cache slot `slot` of a region
+// (the cache is written through the region pointers it is read from): the
+// lanes that hold the slot's K row and V entries store them.
+__device__ __forceinline__ void fold_append(const char* kreg, const char* vreg, int slot, const u32x4 (&kn)[2],
+                                            const uint32_t (&vn)[4], int lane) {
+  const int s32 = slot & 31, q4 = lane >> 4;
+  char* kw = const_cast<char*>(kreg);
+  uint16_t* vw = (uint16_t*)const_cast<char*>(vreg);
+  if ((lane & 15) == (s32 & 15)) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) st16(kw + k_offset(slot, 32 * h + 8 * q4, 32) * 2, kn[h]);
+  }
+  if (q4 == ((s32 & 15) >> 2)) {
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+      vw[(long long)(slot >> 5) * 32 * kD + (16 * dt + (lane & 15)) * 32 + v_slot(s32)] = (uint16_t)vn[dt];
+  }
+}
+
+// The new token's K row and V column of one window (bf16), patched into the
+// registers of the block that holds its ring slot s32 (slot % 32): lanes with
+// lane % 16 == s32 % 16 hold that slot's K row (tile s32 / 16) as dims
+// 32 h + 8 (lane / 16) .. + 7; lanes with lane / 16 == (s32 % 16) / 4 hold its
+// V entries, bf16 element v_slot(s32) % 8 of each d tile (d = 16 dt + lane % 16).
+__device__ __forceinline__ void patch_new_slot(BlockRegs<DT_BF16>& br, const u32x4 (&kn)[2], const uint32_t (&vn)[4],
+                                               int s32, int lane) {
+  // value selects and masks only: a conditional store to a register array
+  // element would be turned into an indexed store through scratch memory
+  const int p16 = lane & 15, q4 = lane >> 4;
+  const bool krow = p16 == (s32 & 15);
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const bool take = krow && (s32 >> 4) == t;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) br.k[t][h] = take ? kn[h] : br.k[t][h];
+  }
+  const bool vcol = q4 == ((s32 & 15) >> 2);
+  const int e = v_slot(s32) & 7;
+#pragma unroll
+  for (int ww = 0; ww < 4; ++ww) {
+    const uint32_t sel = vcol && (e >> 1) == ww ? ((e & 1) ? 0xffff0000u : 0x0000ffffu) : 0u;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+      const uint32_t ins = (e & 1) ? (vn[dt] << 16) : vn[dt];
+      br.v[dt][ww] = (br.v[dt][ww] & ~sel) | (ins & sel);
+    }
+  }
+}
+
 // Blocks [p0, p1) of the window of (token b, KV group g): the 4 waves stream
 // their blocks, merge their states in wave order through LDS and write the
 // output (pdst null: the piece is the whole window) or the piece's partial,
@@ -524,52 +658,16 @@ __global__ __launch_bounds__(256, SPA_ATTN_MINB) void k_attn_dealt(AttnArgs a) {
   if (a.tspan && tid == 0) atomicMax(a.tspan + 8 * ((w & 15) + 1), (unsigned long long)wall_clock64());
 }
 
-// The new token's K row and V column of one window (bf16), patched into the
-// registers of the block that holds its ring slot s32 (slot % 32): lanes with
-// lane % 16 == s32 % 16 hold that slot's K row (tile s32 / 16) as dims
-// 32 h + 8 (lane / 16) .. + 7; lanes with lane / 16 == (s32 % 16) / 4 hold its
-// V entries, bf16 element v_slot(s32) % 8 of each d tile (d = 16 dt + lane % 16).
-__device__ __forceinline__ void patch_new_slot(BlockRegs<DT_BF16>& br, const u32x4 (&kn)[2], const uint32_t (&vn)[4],
-                                               int s32, int lane) {
-  // value selects and masks only: a conditional store to a register array
-  // element would be turned into an indexed store through scratch memory
-  const int p16 = lane & 15, q4 = lane >> 4;
-  const bool krow = p16 == (s32 & 15);
-#pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    const bool take = krow && (s32 >> 4) == t;
-#pragma unroll
-    for (int h = 0; h < 2; ++h) br.k[t][h] = take ? kn[h] : br.k[t][h];
-  }
-  const bool vcol = q4 == ((s32 & 15) >> 2);
-  const int e = v_slot(s32) & 7;
-#pragma unroll
-  for (int ww = 0; ww < 4; ++ww) {
-    const uint32_t sel = vcol && (e >> 1) == ww ? ((e & 1) ? 0xffff0000u : 0x0000ffffu) : 0u;
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt) {
-      const uint32_t ins = (e & 1) ? (vn[dt] << 16) : vn[dt];
-      br.v[dt][ww] = (br.v[dt][ww] & ~sel) | (ins & sel);
-    }
-  }
-}
-
 // Sliding layers at large batches: one wave per window (token b, KV head g),
 // four windows per workgroup. The wave streams the window's blocks through
 // its register ring and finishes with the sink itself: no piece merge through
 // LDS and no barrier, so the workgroup's fixed costs are shared by four
 // windows. A lane holds head (lane & 15) and dims 16 dt + 4 (lane >> 4) + r,
 // so each lane stores four runs of four outputs.
-// QSM > 0 (bf16, 8 query heads per KV head): the QKV finish is folded in.
-// The wave sums its heads' q and
-// the new K and V of its window from the QKV split partials (part_sum<QSM>,
-// the finish's sums and roundings), appends K and V at ring slot
-// (L - 1) % W, and patches them into the registers of the block holding that
-// slot (the block's load may return the slot's old row): the same values the
-// separate finish would have stored and this kernel would have loaded.
-template <int KVT, int QSM>
+// With a.qkv set (bf16) the QKV finish is folded in (fold_issue ..
+// fold_append): the new K/V sit at ring slot (L - 1) % W.
+template <int KVT>
 __global__ __launch_bounds__(256, SPA_ATTN_MINB) void k_attn_wave(AttnArgs a) {
-  static_assert(QSM == 0 || KVT == DT_BF16, "the folded finish is bf16 only");
   constexpr int esz = KVT == DT_BF16 ? 2 : 4;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -595,93 +693,44 @@ __global__ __launch_bounds__(256, SPA_ATTN_MINB) void k_attn_wave(AttnArgs a) {
       // blocks 0 .. nb-1 through a ring of kRing register sets (a block past
       // the last is clamped for the load and never attended)
       BlockRegs<KVT> rb[kRing];
-      if constexpr (QSM > 0) {
-        // the ring's first loads go out before the finish's loads and the
-        // append's stores, which they would otherwise wait behind
+      const bool fold = KVT == DT_BF16 && a.qkv.part != nullptr;
+      if (fold) {
+        if constexpr (KVT == DT_BF16) {
+          // the ring's first loads go out with the finish's loads, ahead of
+          // their sums and of the append's stores
+          FoldRaw fr;
+          fold_issue(a, b, g, lane, fr);
+#pragma unroll
+          for (int r = 0; r < kRing; ++r) load_block<KVT>(rb[r], kreg, vreg, min(r, nb - 1), lane, kStreamKV);
+          const int slot = (a.kv_len[a.tok0 + b] - 1) % a.window;   // L >= 1 (loc.ok)
+          sblk = slot >> 5;
+          s32 = slot & 31;
+          fold_make(fr, a.qkv.S, lane, qr, kn, vn);
+          fold_append(kreg, vreg, slot, kn, vn, lane);
+        }
+      } else {
+        if constexpr (KVT == DT_BF16) {
+#pragma unroll
+          for (int h = 0; h < 2; ++h) qr.q[h] = hvalid ? ld16(qrow + (32 * h + 8 * q4) * 2) : u32x4{0u, 0u, 0u, 0u};
+        } else {
+#pragma unroll
+          for (int cc = 0; cc < 4; ++cc)
+            qr.q[cc] = hvalid ? ld16(qrow + (16 * cc + 4 * q4) * 4) : u32x4{0u, 0u, 0u, 0u};
+        }
 #pragma unroll
         for (int r = 0; r < kRing; ++r) load_block<KVT>(rb[r], kreg, vreg, min(r, nb - 1), lane, kStreamKV);
-        const int QD = a.n_q_heads * kD;
-        const int L = a.kv_len[a.tok0 + b];   // >= 1 (loc.ok)
-        const int slot = (L - 1) % a.window;
-        sblk = slot >> 5;
-        s32 = slot & 31;
-        // The group's partials are read contiguously, 16 bytes per lane and
-        // no branch between the loads (a branch would hold the later loads
-        // behind the earlier sums): q of its 8 heads as two 1 KB rows of the
-        // wave (lane l holds floats 256 i + 4 l .. + 3: head 4 i + l / 16,
-        // dims 4 (l % 16) ..), K and V as one (lanes with bit 4 clear: K dims
-        // 4 (l % 16) ..; set: V). Summed and rounded where loaded, then moved
-        // to the lanes that need them.
-        const int q0 = g * G * kD, kc = QD + g * kD, vc = QD + a.n_kv_heads * kD + g * kD;
-        const f32x4 qs0 = part_sum4<QSM>(a.qkv, b, q0 + 4 * lane);
-        const f32x4 qs1 = part_sum4<QSM>(a.qkv, b, q0 + 256 + 4 * lane);
-        const f32x4 kvs = part_sum4<QSM>(a.qkv, b, ((lane & 16) ? vc : kc) + 4 * (lane & 15));
-        const uint32_t qd00 = pack_bf16x2(qs0[0], qs0[1]), qd01 = pack_bf16x2(qs0[2], qs0[3]);
-        const uint32_t qd10 = pack_bf16x2(qs1[0], qs1[1]), qd11 = pack_bf16x2(qs1[2], qs1[3]);
-        const uint32_t kvd0 = pack_bf16x2(kvs[0], kvs[1]), kvd1 = pack_bf16x2(kvs[2], kvs[3]);
-        // q: lane (hl, q4) takes head hl's dims 32 h + 8 q4 .. + 7, the 4-dim
-        // chunks c = 8 h + 2 q4 + k of row hl / 4, lane 16 (hl % 4) + c
-        // K: every lane takes dims 32 h + 8 q4 .. + 7 (chunks 8 h + 2 q4 + k)
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          uint32_t w[4], kw4[4];
-#pragma unroll
-          for (int k = 0; k < 2; ++k) {
-            const int c = 8 * h + 2 * q4 + k, src = 16 * (hl & 3) + c;
-            const uint32_t a0 = __shfl(qd00, src, 64), a1 = __shfl(qd01, src, 64);
-            const uint32_t b0 = __shfl(qd10, src, 64), b1 = __shfl(qd11, src, 64);
-            w[2 * k] = hl < 4 ? a0 : b0;
-            w[2 * k + 1] = hl < 4 ? a1 : b1;
-            kw4[2 * k] = __shfl(kvd0, c, 64);
-            kw4[2 * k + 1] = __shfl(kvd1, c, 64);
-          }
-          qr.q[h] = hvalid ? u32x4{w[0], w[1], w[2], w[3]} : u32x4{0u, 0u, 0u, 0u};
-          kn[h] = u32x4{kw4[0], kw4[1], kw4[2], kw4[3]};
-        }
-        // V: every lane takes dim d = 16 dt + lane % 16, element d % 4 of
-        // chunk d / 4 held by lane 16 + d / 4
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt) {
-          const int d = 16 * dt + (lane & 15), src = 16 + (d >> 2);
-          const uint32_t a0 = __shfl(kvd0, src, 64), a1 = __shfl(kvd1, src, 64);
-          const uint32_t wv = (d & 2) ? a1 : a0;
-          vn[dt] = (d & 1) ? (wv >> 16) : (wv & 0xffffu);
-        }
-        // the append: the lanes that hold the slot's K row and V entries store
-        // them (the cache is written through the region pointers it is read from)
-        char* kw = const_cast<char*>(kreg);
-        uint16_t* vw = (uint16_t*)const_cast<char*>(vreg);
-        if ((lane & 15) == (s32 & 15)) {
-#pragma unroll
-          for (int h = 0; h < 2; ++h) st16(kw + k_offset(slot, 32 * h + 8 * q4, 32) * 2, kn[h]);
-        }
-        if (q4 == ((s32 & 15) >> 2)) {
-#pragma unroll
-          for (int dt = 0; dt < 4; ++dt)
-            vw[(long long)sblk * 32 * kD + (16 * dt + (lane & 15)) * 32 + v_slot(s32)] = (uint16_t)vn[dt];
-        }
-      } else if constexpr (KVT == DT_BF16) {
-#pragma unroll
-        for (int h = 0; h < 2; ++h) qr.q[h] = hvalid ? ld16(qrow + (32 * h + 8 * q4) * 2) : u32x4{0u, 0u, 0u, 0u};
-      } else {
-#pragma unroll
-        for (int cc = 0; cc < 4; ++cc) qr.q[cc] = hvalid ? ld16(qrow + (16 * cc + 4 * q4) * 4) : u32x4{0u, 0u, 0u, 0u};
       }
       const float sink = a.sinks[g * G + (hvalid ? hl : 0)] * kLog2e;
       float m_run = -INFINITY, l_run = 0.f;
       f32x4 acc[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if constexpr (QSM == 0) {
-#pragma unroll
-        for (int r = 0; r < kRing; ++r) load_block<KVT>(rb[r], kreg, vreg, min(r, nb - 1), lane, kStreamKV);
-      }
       int i = 0;
       for (; i + kRing < nb; i += kRing) {
 #pragma unroll
         for (int r = 0; r < kRing; ++r) {
-          if constexpr (QSM > 0)
-            if (i + r == sblk) patch_new_slot(rb[r], kn, vn, s32, lane);
+          if constexpr (KVT == DT_BF16)
+            if (i + r == sblk) patch_new_slot(rb[r], kn, vn, s32, lane);   // sblk = -1 unless folded
           attend<KVT>(rb[r], qr, i + r, loc.n_valid, a.scale_log2, m_run, l_run, acc, lane);
           __builtin_amdgcn_sched_barrier(0);
           load_block<KVT>(rb[r], kreg, vreg, min(i + r + kRing, nb - 1), lane, kStreamKV);
@@ -691,7 +740,7 @@ __global__ __launch_bounds__(256, SPA_ATTN_MINB) void k_attn_wave(AttnArgs a) {
 #pragma unroll
       for (int r = 0; r < kRing; ++r)
         if (i + r < nb) {
-          if constexpr (QSM > 0)
+          if constexpr (KVT == DT_BF16)
             if (i + r == sblk) patch_new_slot(rb[r], kn, vn, s32, lane);
           attend<KVT>(rb[r], qr, i + r, loc.n_valid, a.scale_log2, m_run, l_run, acc, lane);
         }
@@ -848,41 +897,26 @@ static void launch_dealt_t(const AttnArgs& a, hipStream_t st, hipEvent_t start, 
   else launch_dealt_tpt<KVT, 4>(a, st, start, stop);
 }
 
-template <int KVT, int QSM>
-static void launch_wave_q(const AttnArgs& a, hipStream_t st, hipEvent_t start, hipEvent_t stop) {
-  const dim3 grid((a.n_tok * a.n_kv_heads + 3) / 4);
-  if (start || stop)
-    hipExtLaunchKernelGGL((k_attn_wave<KVT, QSM>), grid, dim3(256), 0, st, start, stop, 0, a);
-  else
-    hipLaunchKernelGGL((k_attn_wave<KVT, QSM>), grid, dim3(256), 0, st, a);
-}
-
-// QSM: 0 (q given, K/V appended), else the smallest of 1, 2, 4 that bounds
-// the QKV split count, the bound the finish kernel takes. Every partial is in
-// flight at once, so more than 4 splits would not fit the registers: the
-// folded finish takes at most 4 (kFoldMaxSplits).
 template <int KVT>
 static void launch_wave_t(const AttnArgs& a, hipStream_t st, hipEvent_t start, hipEvent_t stop) {
-  static_assert(kFoldMaxSplits == 4, "instances for 1, 2 and 4 splits");
-  if constexpr (KVT == DT_BF16) {
-    if (a.qkv.part) {
-      const int S = a.qkv.S;
-      if (S <= 1) launch_wave_q<KVT, 1>(a, st, start, stop);
-      else if (S <= 2) launch_wave_q<KVT, 2>(a, st, start, stop);
-      else launch_wave_q<KVT, 4>(a, st, start, stop);
-      return;
-    }
-  }
-  launch_wave_q<KVT, 0>(a, st, start, stop);
+  const dim3 grid((a.n_tok * a.n_kv_heads + 3) / 4);
+  if (start || stop)
+    hipExtLaunchKernelGGL(k_attn_wave<KVT>, grid, dim3(256), 0, st, start, stop, 0, a);
+  else
+    hipLaunchKernelGGL(k_attn_wave<KVT>, grid, dim3(256), 0, st, a);
+}
+
+// The shapes the folded QKV finish handles (fold_issue .. fold_append).
+static bool fold_args_ok(const AttnArgs& a) {
+  return a.kv_dtype == DT_BF16 && a.head_dim == kD && a.n_q_heads == 8 * a.n_kv_heads && a.qkv.S >= 1 &&
+         a.qkv.S <= kFoldMaxSplits && a.qkv.rows >= a.n_tok && a.qkv.ld % 4 == 0 &&
+         a.qkv.ld >= (a.n_q_heads + 2 * a.n_kv_heads) * kD;
 }
 
 hipError_t launch_attn(const AttnArgs& a, hipStream_t st, hipEvent_t start, hipEvent_t stop) {
   if (a.wave_windows) {
     if (a.kv_kind != KV_RING || a.deal_wgs > 0 || a.n_q_heads / a.n_kv_heads > 16) return hipErrorInvalidValue;
-    if (a.qkv.part && (a.kv_dtype != DT_BF16 || a.head_dim != kD || a.n_q_heads != 8 * a.n_kv_heads ||
-                       a.qkv.S < 1 || a.qkv.S > kFoldMaxSplits ||
-                       a.qkv.rows < a.n_tok || a.qkv.ld % 4 != 0))
-      return hipErrorInvalidValue;
+    if (a.qkv.part && !fold_args_ok(a)) return hipErrorInvalidValue;
     if (a.kv_dtype == DT_BF16) launch_wave_t<DT_BF16>(a, st, start, stop);
     else launch_wave_t<DT_F32>(a, st, start, stop);
     return hipGetLastError();
@@ -890,10 +924,12 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t st, hipEvent_t start, hipE
   if (a.deal_wgs > 0 && a.kv_kind == KV_PACKED) {
     if (a.n_tok < 1 || a.n_tok > kDealMaxTok || a.deal_v < 1 || a.deal_v > kDealMaxRanges || !a.deal_tab)
       return hipErrorInvalidValue;
+    if (a.qkv.part) return hipErrorInvalidValue;   // the even split takes q and appended K/V
     if (a.kv_dtype == DT_BF16) launch_dealt_t<DT_BF16>(a, st, start, stop);
     else launch_dealt_t<DT_F32>(a, st, start, stop);
     return hipGetLastError();
   }
+  if (a.qkv.part) return hipErrorInvalidValue;   // the chunk grid takes q and appended K/V
   dim3 grid(a.max_chunks, a.n_kv_heads, a.n_tok);
   if (a.kv_dtype == DT_BF16) {
     if (a.kv_kind == KV_PACKED) launch_attn_t<DT_BF16, KV_PACKED>(a, grid, st, start, stop);

@@ -536,7 +536,9 @@ static bool sliding_wave(const spa_ctx* ctx, const spa_model_desc* m, const spa_
 // Layers whose QKV finish runs inside the one-wave-per-window attention
 // kernel (bf16 KV, no RoPE, 8 query heads per KV head, at most kFoldMaxSplits
 // QKV splits): the finish kernel's launch is saved, and the attention
-// computes exactly what it would have read.
+// computes exactly what it would have read. (Full layers keep the finish
+// kernel: folded into the even split, every piece re-sums its q and the
+// kernel's registers grow, and the iteration was slower.)
 static bool qkv_folds(spa_ctx* ctx, const spa_model_desc* m, const spa_layer* l, int n_tok) {
   return SPA_ATTN_FOLD_QKV && sliding_wave(ctx, m, l, n_tok) && m->kv_dtype == SPA_BF16 && !(m->rope_theta > 0.f) &&
          m->head_dim == 64 && m->n_q_heads == 8 * m->n_kv_heads &&
