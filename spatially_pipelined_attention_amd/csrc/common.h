@@ -39,10 +39,24 @@ __device__ __forceinline__ T wave_sum(T v) {
   return v;
 }
 
+// A lane's partner value inside its 16-lane row by DPP (a VALU operand
+// modifier, no LDS round trip): lane ^ 1, lane ^ 2 (quad permutes), the
+// mirror inside each half row (i <-> 7 - i) and inside the row
+// (i <-> 15 - i). Each is an involution, so after the four steps every lane
+// of a row has combined the same 16 values (exact for max).
+template <int STEP>
+__device__ __forceinline__ int dpp_partner(int x) {
+  constexpr int ctrl = STEP == 0 ? 0xB1 : STEP == 1 ? 0x4E : STEP == 2 ? 0x141 : 0x140;
+  return __builtin_amdgcn_update_dpp(0, x, ctrl, 0xF, 0xF, false);
+}
+
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
+  v = fmaxf(v, __int_as_float(dpp_partner<0>(__float_as_int(v))));
+  v = fmaxf(v, __int_as_float(dpp_partner<1>(__float_as_int(v))));
+  v = fmaxf(v, __int_as_float(dpp_partner<2>(__float_as_int(v))));
+  v = fmaxf(v, __int_as_float(dpp_partner<3>(__float_as_int(v))));
+  v = fmaxf(v, __shfl_xor(v, 16, 64));
+  return fmaxf(v, __shfl_xor(v, 32, 64));
 }
 
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }

@@ -237,15 +237,21 @@ __device__ __forceinline__ void route_token(const RouteArgs& a, int t, int lane,
         bv = v[j];
         bi = lane + 64 * j;
       }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      const float ov = __shfl_xor(bv, o, 64);
-      const int oi = __shfl_xor(bi, o, 64);
+    // the wave's largest (value, index), ties to the lower index: a total
+    // order, so any pairing of the lanes gives the same pick (DPP inside each
+    // row, lane shuffles across rows)
+    auto take = [&](float ov, int oi) {
       if (ov > bv || (ov == bv && oi < bi)) {
         bv = ov;
         bi = oi;
       }
-    }
+    };
+    take(__int_as_float(dpp_partner<0>(__float_as_int(bv))), dpp_partner<0>(bi));
+    take(__int_as_float(dpp_partner<1>(__float_as_int(bv))), dpp_partner<1>(bi));
+    take(__int_as_float(dpp_partner<2>(__float_as_int(bv))), dpp_partner<2>(bi));
+    take(__int_as_float(dpp_partner<3>(__float_as_int(bv))), dpp_partner<3>(bi));
+    take(__shfl_xor(bv, 16, 64), __shfl_xor(bi, 16, 64));
+    take(__shfl_xor(bv, 32, 64), __shfl_xor(bi, 32, 64));
     pv[p] = bv;
     pi[p] = bi;
     if ((bi & 63) == lane) {
