@@ -402,7 +402,7 @@ typedef struct spa_pipeline_cfg {
   /* 1: temporal pipelines (no pools) capture an iteration's launches into a
    * HIP graph on its own stream the first time and replay it while the
    * run's arguments (layers, batch, workspace, kernel timer) are unchanged,
-   * capturing again when they change; the graph replaces about 400 kernel
+   * capturing again when they change; the graph replaces about 360 kernel
    * launches per 36-layer iteration with one. Same kernels, same results
    * (for callers that must submit whole iterations; on the 36-layer batch-64
    * workload it measured 6.79 ms per iteration against 6.38 ms launched
