@@ -2,8 +2,10 @@
 finish kernel on the GPU, bit for bit.
 
 One sliding layer of the 36-layer workload (64 sequences: the attention runs
-one wave per window, and the QKV product takes 3 splits, so the layer path
-folds the finish into that kernel) is run twice from the same KV cache:
+one wave per window, so the layer path folds the finish into that kernel) is
+run twice from the same KV cache, at the model's hidden size 2880 (the QKV
+product takes 3 splits: the finish's bound is 4, one +0 term) and at 512 and
+256 (2 splits and 1: no padding term):
 through the separate entry points (spa_rms_norm, spa_qkv_append with its
 finish kernel, spa_decode_attn with q given, spa_out_proj, spa_moe_route,
 spa_moe_expert, spa_moe_combine) and through spa_layer_forward. The folded
@@ -19,12 +21,13 @@ import torch
 pytestmark = pytest.mark.gpu
 
 
-def test_folded_finish_matches_the_separate_kernels():
+@pytest.mark.parametrize("hidden", [2880, 512, 256])
+def test_folded_finish_matches_the_separate_kernels(hidden):
     from spatially_pipelined_attention_amd import binding as B, synth
     from spatially_pipelined_attention_amd.workload import DeviceWorkload
     wl = synth.WORKLOADS["gptoss_36l_b64"]
-    wl = wl.with_(n_layers=1, layer_kinds=("sliding",))
-    print("\n[fold] building one sliding layer of gptoss_36l_b64", flush=True)
+    wl = wl.with_(n_layers=1, layer_kinds=("sliding",), hidden=hidden, inter=hidden)
+    print(f"\n[fold] building one sliding layer of gptoss_36l_b64, hidden {hidden}", flush=True)
     dw = DeviceWorkload(wl)
     ctx = B.spa_init(0)
     m, lay, t0, dev = dw.m, dw.layers_c[0], dw.layers_t[0], dw.dev
