@@ -65,8 +65,8 @@ DEAL_MAX_TOKENS = 1024   # full-layer launches of up to this many tokens split t
 
 def attn_kernel_name(tokens_per_launch, full=True, n_kv_heads=8, n_cus=256):
     """The attention kernel a launch of this many tokens runs (full or sliding layers)."""
-    if not full:   # one wave per window from one window per CU of the device, the QKV finish folded in
-        return "spa::k_attn_wave<1>" if tokens_per_launch * n_kv_heads >= n_cus else "spa::k_attn<1, 0>"
+    if not full:   # one wave per window from half a window per CU of the device, the QKV finish folded in
+        return "spa::k_attn_wave<1>" if 2 * tokens_per_launch * n_kv_heads >= n_cus else "spa::k_attn<1, 0>"
     if tokens_per_launch <= 256:   # one token per prologue thread
         return "spa::k_attn_dealt<1, 1>"
     return "spa::k_attn_dealt<1, 4>" if tokens_per_launch <= DEAL_MAX_TOKENS else "spa::k_attn<1, 1>"

@@ -520,7 +520,7 @@ static AttnArgs attn_args(const spa_model_desc* m, const spa_layer* l, const spa
 }
 
 #ifndef SPA_ATTN_WAVE_PER_4CU
-#define SPA_ATTN_WAVE_PER_4CU 4
+#define SPA_ATTN_WAVE_PER_4CU 2
 #endif
 // Sliding layers with at least SPA_ATTN_WAVE_PER_4CU windows per 4 CUs of the
 // device (so the choice, and the results, never depend on the pool): one wave
