@@ -5,8 +5,9 @@ One sliding layer of the 36-layer workload (64 sequences: the attention runs
 one wave per window, so the layer path folds the finish into that kernel) is
 run twice from the same KV cache, at the model's hidden size 2880 (the QKV
 product takes 3 splits: the finish's bound is 4, one +0 term), at 512 and 256
-(2 splits and 1: no padding term), and at 16 sequences (half a window per CU
-of a 256-CU device, the smallest launch that takes the kernel there):
+(2 splits and 1: no padding term), at 16 sequences (half a window per CU
+of a 256-CU device, the smallest launch that takes the kernel there), and with
+ragged KV lengths from 1 to 300 (new slots inside rings not yet full):
 through the separate entry points (spa_rms_norm, spa_qkv_append with its
 finish kernel, spa_decode_attn with q given, spa_out_proj, spa_moe_route,
 spa_moe_expert, spa_moe_combine) and through spa_layer_forward. The folded
@@ -22,13 +23,16 @@ import torch
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("hidden,batch", [(2880, 64), (512, 64), (256, 64), (2880, 16)])
-def test_folded_finish_matches_the_separate_kernels(hidden, batch):
+@pytest.mark.parametrize("hidden,batch,kv", [(2880, 64, None), (512, 64, None), (256, 64, None), (2880, 16, None),
+                                             (2880, 64, (1, 300))])
+def test_folded_finish_matches_the_separate_kernels(hidden, batch, kv):
     from spatially_pipelined_attention_amd import binding as B, synth
     from spatially_pipelined_attention_amd.workload import DeviceWorkload
     wl = synth.WORKLOADS["gptoss_36l_b64"]
     wl = wl.with_(n_layers=1, layer_kinds=("sliding",), hidden=hidden, inter=hidden, batch=batch)
-    print(f"\n[fold] building one sliding layer of gptoss_36l_b64, hidden {hidden}, batch {batch}", flush=True)
+    if kv:   # ragged lengths from 1: rings not yet full, and single-position windows
+        wl = wl.with_(kv_len_lo=kv[0], kv_len_hi=kv[1])
+    print(f"\n[fold] one sliding layer of gptoss_36l_b64, hidden {hidden}, batch {batch}, KV {kv}", flush=True)
     dw = DeviceWorkload(wl)
     ctx = B.spa_init(0)
     m, lay, t0, dev = dw.m, dw.layers_c[0], dw.layers_t[0], dw.dev
